@@ -1,0 +1,433 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+* numbers the pages print (parameter and activation counts, token/batch counts);
+* PyTorch library routines (layer_norm, tanh-GELU, causal attention, cross_entropy,
+  autograd, AdamW) -- the pages' own test compares the C model to PyTorch;
+* central finite differences of the oracle's own loss (backward vs forward);
+* brute-force attention from its definition (explicit mask matrix, dense softmax);
+* closed forms and exact special cases (wte = 0 gives ln V; T = 1 attention;
+  constant LayerNorm rows; the first AdamW step);
+* invariants (softmax rows, LayerNorm moments, zero-sum gradients, conservation).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle as O
+from scratch_transformer_lm_amd import synthetic as S
+from tests import torch_gpt2
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+MICRO = S.Workload("micro", S.ModelShape(8, 16, 1, 2, 8), 2, 4)
+PRINTED = json.load(open(os.path.join(HERE, "golden", "pages_printed.json")))
+
+
+def model_124m():
+    c = PRINTED["config"]
+    return S.ModelShape(c["max_seq_len"], c["vocab_size"], c["num_layers"], c["num_heads"],
+                        c["channels"])
+
+
+# ----------------------------------------------------------------- printed numbers
+
+def test_parameter_count_matches_printed():
+    assert O.num_parameters(model_124m()) == PRINTED["num_parameters"]
+
+
+def test_activation_count_matches_printed_run_shape():
+    # The printed batch counts fix B*T = 256 ...
+    bt = PRINTED["train_tokens"] // PRINTED["train_num_batches"]
+    assert bt == 256 and PRINTED["val_tokens"] // PRINTED["val_num_batches"] == 256
+    # ... and among the power-of-two splits only B=4, T=64 gives the printed count.
+    hits = [(B, bt // B) for B in (1, 2, 4, 8, 16, 32, 64, 128, 256)
+            if O.num_activations(model_124m(), B, bt // B) == PRINTED["num_activations"]]
+    assert hits == [(4, 64)]
+
+
+def test_other_model_counts():
+    assert O.num_parameters(S.TINY.model) == 136960
+    assert O.num_parameters(S.GPT2_350M.model) == 354823168
+    assert O.num_parameters(MICRO.model) == 1080
+
+
+def test_layout_agrees_with_generator_shapes():
+    off, ln = O.param_layout(S.GPT2_124M.model)
+    assert ln == list(S.param_sizes(S.GPT2_124M.model))
+    assert off == list(np.concatenate([[0], np.cumsum(ln)[:-1]]))
+
+
+# ----------------------------------------------------------------- layers vs library
+
+def test_layernorm_vs_torch():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((37, 48))
+    w = 1 + 0.1 * rng.standard_normal(48)
+    b = 0.1 * rng.standard_normal(48)
+    dy = rng.standard_normal((37, 48))
+    y, mean, rstd = O.layernorm_forward(x, w, b)
+    xt, wt, bt = (torch.tensor(a, requires_grad=True) for a in (x, w, b))
+    yt = F.layer_norm(xt, (48,), wt, bt, eps=1e-5)
+    yt.backward(torch.tensor(dy))
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(mean, x.mean(1), atol=1e-15)
+    np.testing.assert_allclose(rstd, 1 / np.sqrt(x.var(1) + 1e-5), rtol=1e-14)
+    dx, dw, db = O.layernorm_backward(dy, x, w, mean, rstd)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(db, bt.grad.numpy(), atol=1e-12)
+
+
+def test_layernorm_invariants_and_constant_row():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((16, 64)) * 3 + 1
+    x[3] = 0.25  # constant row
+    ones, zeros = np.ones(64), np.zeros(64)
+    y, mean, rstd = O.layernorm_forward(x, ones, zeros)
+    var = x.var(1)
+    # pre-affine output: mean 0, variance var / (var + eps)
+    np.testing.assert_allclose(y.mean(1), 0, atol=1e-14)
+    np.testing.assert_allclose(y.var(1), var / (var + 1e-5), rtol=1e-12)
+    beta = rng.standard_normal(64)
+    y2, _, r2 = O.layernorm_forward(x, rng.standard_normal(64), beta)
+    assert np.array_equal(y2[3], beta) and r2[3] == 1 / math.sqrt(1e-5)
+    dx, _, _ = O.layernorm_backward(rng.standard_normal(x.shape), x, rng.standard_normal(64), mean, rstd)
+    np.testing.assert_allclose(dx.sum(1), 0, atol=1e-10)
+
+
+def test_gelu_vs_torch_and_special_values():
+    x = np.linspace(-8, 8, 2001)
+    dy = np.cos(x)
+    xt = torch.tensor(x, requires_grad=True)
+    yt = F.gelu(xt, approximate="tanh")
+    yt.backward(torch.tensor(dy))
+    np.testing.assert_allclose(O.gelu_forward(x), yt.detach().numpy(), atol=1e-15)
+    np.testing.assert_allclose(O.gelu_backward(x, dy), xt.grad.numpy(), atol=1e-14)
+    assert O.gelu_forward(np.array([0.0]))[0] == 0.0
+    assert O.gelu_backward(np.array([0.0]), np.array([1.0]))[0] == 0.5
+
+
+def test_matmul_vs_numpy():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((19, 300))
+    w = rng.standard_normal((270, 300))
+    b = rng.standard_normal(270)
+    dy = rng.standard_normal((19, 270))
+    np.testing.assert_allclose(O.matmul_forward(x, w, b), x @ w.T + b, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.matmul_forward(x, w), x @ w.T, rtol=1e-12, atol=1e-12)
+    dx, dw, db = O.matmul_backward(dy, x, w)
+    np.testing.assert_allclose(dx, dy @ w, atol=1e-11)
+    np.testing.assert_allclose(dw, dy.T @ x, atol=1e-11)
+    np.testing.assert_allclose(db, dy.sum(0), atol=1e-12)
+
+
+def brute_attention(qkv, NH):
+    """Attention from its definition with dense matrices and an explicit mask."""
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    hs = C // NH
+    out = np.zeros((B, T, C))
+    att = np.zeros((B, NH, T, T))
+    mask = np.tril(np.ones((T, T), bool))
+    for b in range(B):
+        for h in range(NH):
+            q = qkv[b, :, h * hs:(h + 1) * hs]
+            k = qkv[b, :, C + h * hs:C + (h + 1) * hs]
+            v = qkv[b, :, 2 * C + h * hs:2 * C + (h + 1) * hs]
+            s = (q @ k.T) / math.sqrt(hs)
+            s = np.where(mask, s, -np.inf)
+            p = np.exp(s - s.max(1, keepdims=True))
+            p = p / p.sum(1, keepdims=True)
+            att[b, h] = p
+            out[b, :, h * hs:(h + 1) * hs] = p @ v
+    return out, att
+
+
+@pytest.mark.parametrize("B,T,C,NH", [(2, 7, 12, 3), (1, 16, 32, 2), (3, 5, 16, 4)])
+def test_attention_brute_force(B, T, C, NH):
+    rng = np.random.default_rng(13)
+    qkv = rng.standard_normal((B, T, 3 * C))
+    out, pre, att = O.attention_forward(qkv, NH)
+    ref, ref_att = brute_attention(qkv, NH)
+    np.testing.assert_allclose(out, ref, atol=1e-13)
+    np.testing.assert_allclose(att, ref_att, atol=1e-14)
+    np.testing.assert_allclose(att.sum(-1), 1, atol=1e-14)
+    assert np.all(att[..., np.triu_indices(T, 1)[0], np.triu_indices(T, 1)[1]] == 0)
+
+
+def test_attention_backward_vs_torch():
+    rng = np.random.default_rng(14)
+    B, T, C, NH = 2, 9, 16, 4
+    qkv = rng.standard_normal((B, T, 3 * C))
+    dy = rng.standard_normal((B, T, C))
+    out, pre, att = O.attention_forward(qkv, NH)
+    dqkv, dpre, datt = O.attention_backward(dy, qkv, att, NH)
+    t = torch.tensor(qkv, requires_grad=True)
+    q, k, v = t.split(C, -1)
+    f = lambda z: z.view(B, T, NH, C // NH).transpose(1, 2)
+    y = F.scaled_dot_product_attention(f(q), f(k), f(v), is_causal=True)
+    y = y.transpose(1, 2).reshape(B, T, C)
+    np.testing.assert_allclose(out, y.detach().numpy(), atol=1e-13)
+    y.backward(torch.tensor(dy))
+    np.testing.assert_allclose(dqkv, t.grad.numpy(), atol=1e-12)
+    # softmax backward rows sum to zero
+    np.testing.assert_allclose(dpre.sum(-1), 0, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(15)
+    qkv = rng.standard_normal((2, 1, 3 * 8))
+    out, _, _ = O.attention_forward(qkv, 2)
+    assert np.array_equal(out[:, 0], qkv[:, 0, 16:24])          # T = 1: o = v_0 exactly
+    qkv = rng.standard_normal((1, 6, 3 * 8))
+    qkv[:, :, 8:16] = qkv[:, :1, 8:16]                           # identical keys
+    out, _, _ = O.attention_forward(qkv, 2)
+    v = qkv[0, :, 16:24]
+    np.testing.assert_allclose(out[0], np.cumsum(v, 0) / np.arange(1, 7)[:, None], atol=1e-14)
+
+
+def test_softmax_crossentropy_vs_torch():
+    rng = np.random.default_rng(16)
+    z = rng.standard_normal((11, 37)) * 4
+    tg = rng.integers(0, 37, 11).astype(np.int32)
+    p = O.softmax_forward(z)
+    np.testing.assert_allclose(p.sum(1), 1, atol=1e-15)
+    ls = O.crossentropy_forward(p, tg)
+    zt = torch.tensor(z, requires_grad=True)
+    lt = F.cross_entropy(zt, torch.tensor(tg, dtype=torch.long))
+    assert abs(ls.mean() - float(lt.detach())) < 1e-14
+    lt.backward()
+    d = O.crossentropy_softmax_backward(np.full(11, 1 / 11), p, tg)
+    np.testing.assert_allclose(d, zt.grad.numpy(), atol=1e-16)
+    np.testing.assert_allclose(d.sum(1), 0, atol=1e-16)
+
+
+def test_encoder_vs_scatter_add():
+    rng = np.random.default_rng(17)
+    V, maxT, C, B, T = 13, 9, 6, 3, 7
+    tok = rng.integers(0, 4, (B, T)).astype(np.int32)  # many collisions
+    wte, wpe = rng.standard_normal((V, C)), rng.standard_normal((maxT, C))
+    out = O.encoder_forward(tok, wte, wpe)
+    np.testing.assert_array_equal(out, wte[tok] + wpe[None, :T])
+    d = rng.standard_normal((B, T, C))
+    dwte, dwpe = O.encoder_backward(d, tok, V, maxT)
+    ref = np.zeros((V, C))
+    np.add.at(ref, tok.reshape(-1), d.reshape(-1, C))
+    np.testing.assert_allclose(dwte, ref, atol=1e-14)
+    np.testing.assert_allclose(dwpe[:T], d.sum(0), atol=1e-14)
+    assert np.all(dwpe[T:] == 0)
+    # conservation: both embeddings receive the whole upstream gradient
+    np.testing.assert_allclose(dwte.sum(0), d.sum((0, 1)), atol=1e-13)
+    np.testing.assert_allclose(dwpe.sum(0), d.sum((0, 1)), atol=1e-13)
+
+
+def test_adamw_vs_torch_and_first_step_closed_form():
+    rng = np.random.default_rng(18)
+    n = 1000
+    p0 = rng.standard_normal(n)
+    gs = [rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 0, n) for _ in range(5)]
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.999, 1e-8, 0.1
+    # closed form of step 1: m_hat = g, v_hat = g^2
+    p1, _, _ = O.adamw(p0, gs[0], np.zeros(n), np.zeros(n), lr, b1, b2, eps, wd, 1)
+    np.testing.assert_allclose(p1, p0 - lr * (gs[0] / (np.abs(gs[0]) + eps) + wd * p0), rtol=1e-13)
+    # five steps against torch.optim.AdamW
+    pt = torch.tensor(p0, requires_grad=True)
+    opt = torch.optim.AdamW([pt], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd)
+    p, m, v = p0, np.zeros(n), np.zeros(n)
+    for t, g in enumerate(gs, 1):
+        pt.grad = torch.tensor(g)
+        opt.step()
+        p, m, v = O.adamw(p, g, m, v, lr, b1, b2, eps, wd, t)
+    np.testing.assert_allclose(p, pt.detach().numpy(), rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------- whole model
+
+def test_zero_embeddings_give_log_vocab_exactly():
+    w = S.TINY
+    p = S.init_params(w.model)
+    m = O.OracleGPT2(w.model, w.B, w.T, p)
+    m.tensor(m.params, "wte")[:] = 0
+    x, y = S.tokens(w)
+    loss = m.forward(x, y)
+    assert abs(loss - math.log(512)) < 1e-14
+    m.zero_grad()
+    assert m.backward() == 0
+    d = m.activation("logits", grad=True).reshape(-1, 512)
+    onehot = np.zeros_like(d)
+    onehot[np.arange(64), y.reshape(-1)] = 1
+    np.testing.assert_allclose(d, (1 / 512 - onehot) / 64, atol=1e-18)
+
+
+def micro_inputs(seed=3):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(0, 16, (2, 4)).astype(np.int32)
+    y = rng.integers(0, 16, (2, 4)).astype(np.int32)
+    return x, y
+
+
+def micro_params(seed=4):
+    # larger than the default init so every term of the loss is exercised
+    p = S.init_params(MICRO.model, seed)
+    rng = np.random.default_rng(seed)
+    return (p + 0.3 * rng.standard_normal(p.size)).astype(np.float64)
+
+
+def test_finite_differences_micro_every_coordinate():
+    x, y = micro_inputs()
+    p = micro_params()
+    m = O.OracleGPT2(MICRO.model, 2, 4, p)
+    m.forward(x, y)
+    m.zero_grad()
+    m.backward()
+    g = m.grads.copy()
+    h = 1e-5
+    fd = np.empty_like(g)
+    for i in range(p.size):
+        old = m.params[i]
+        m.params[i] = old + h
+        lp = m.forward(x, y)
+        m.params[i] = old - h
+        lm = m.forward(x, y)
+        m.params[i] = old
+        fd[i] = (lp - lm) / (2 * h)
+    for name, off, n in zip(O.PARAM_NAMES, m.offsets, m.lengths):
+        gt, ft = g[off:off + n], fd[off:off + n]
+        assert np.max(np.abs(gt - ft)) <= 1e-7 * max(np.max(np.abs(gt)), 1e-12), name
+
+
+def test_finite_differences_tiny_model_sampled():
+    w = S.TINY
+    p = S.init_params(w.model).astype(np.float64)
+    rng = np.random.default_rng(5)
+    p = p + 0.05 * rng.standard_normal(p.size)
+    x, y = S.tokens(w)
+    m = O.OracleGPT2(w.model, w.B, w.T, p)
+    m.forward(x, y)
+    m.zero_grad()
+    m.backward()
+    g = m.grads.copy()
+    h = 1e-5
+
+    def loss_at(delta):
+        m.params[:] = p + delta
+        return m.forward(x, y)
+
+    for name, off, n in zip(O.PARAM_NAMES, m.offsets, m.lengths):
+        gt = g[off:off + n]
+        idx = rng.choice(n, size=min(16, n), replace=False)
+        if name == "wte":  # make sure rows that were actually used are sampled
+            idx = np.concatenate([idx, x.reshape(-1)[:8] * w.model.channels])
+        for i in idx:
+            e = np.zeros(p.size)
+            e[off + i] = h
+            fd = (loss_at(e) - loss_at(-e)) / (2 * h)
+            assert abs(fd - gt[i]) <= 1e-6 * np.max(np.abs(gt)), (name, i)
+    for _ in range(5):
+        d = rng.standard_normal(p.size)
+        d /= np.linalg.norm(d)
+        fd = (loss_at(h * d) - loss_at(-h * d)) / (2 * h)
+        assert abs(fd - g @ d) <= 1e-6 * np.abs(g).max()
+    m.params[:] = p
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_ten_steps_vs_pytorch_tiny(wd):
+    w = S.TINY
+    p = S.init_params(w.model)
+    x, y = S.tokens(w)
+    losses_t, g_t, p_t = torch_gpt2.train(w.model, p, x, y, 10, weight_decay=wd)
+    m = O.OracleGPT2(w.model, w.B, w.T, p)
+    losses, g1 = [], None
+    for t in range(1, 11):
+        losses.append(m.forward(x, y))
+        m.zero_grad()
+        m.backward()
+        if g1 is None:
+            g1 = m.grads.copy()
+        m.update(1e-4, 0.9, 0.999, 1e-8, wd, t)
+    np.testing.assert_allclose(losses, losses_t, rtol=1e-13)
+    for name, off, n in zip(O.PARAM_NAMES, m.offsets, m.lengths):
+        sl = slice(off, off + n)
+        scale = np.max(np.abs(g_t[sl]))
+        assert np.max(np.abs(g1[sl] - g_t[sl])) <= 1e-11 * scale, name
+        assert np.max(np.abs(m.params[sl] - p_t[sl])) <= 1e-10 * np.max(np.abs(p_t[sl])), name
+
+
+def test_micro_logits_vs_pytorch_with_large_weights():
+    x, y = micro_inputs(6)
+    p = micro_params(7)
+    P = torch_gpt2.to_tensors(MICRO.model, p)
+    loss_t, logits_t = torch_gpt2.loss_fn(MICRO.model, P, x, y)
+    loss_t.backward()
+    m = O.OracleGPT2(MICRO.model, 2, 4, p)
+    loss = m.forward(x, y)
+    np.testing.assert_allclose(m.activation("logits"), logits_t.detach().numpy().reshape(-1), atol=1e-12)
+    assert abs(loss - float(loss_t)) < 1e-13
+    m.zero_grad()
+    m.backward()
+    np.testing.assert_allclose(m.grads, torch_gpt2.flat(P, "grad"), atol=1e-12)
+
+
+# ----------------------------------------------------------------- precision / threads / ABI
+
+def run_steps(w, precision, steps=3, threads=None):
+    if threads:
+        O.set_threads(threads, precision)
+    p = S.init_params(w.model)
+    x, y = S.tokens(w)
+    m = O.OracleGPT2(w.model, w.B, w.T, p, precision)
+    losses = []
+    for t in range(1, steps + 1):
+        losses.append(m.forward(x, y))
+        m.zero_grad()
+        m.backward()
+        m.update(1e-4, 0.9, 0.999, 1e-8, 0.0, t)
+    return np.array(losses), m.params.copy(), m.grads.copy()
+
+
+def test_float_and_double_builds_agree():
+    l64, p64, g64 = run_steps(S.TINY, "f64")
+    l32, p32, g32 = run_steps(S.TINY, "f32")
+    np.testing.assert_allclose(l32, l64, rtol=1e-6)
+    assert np.max(np.abs(g32 - g64)) <= 1e-4 * np.max(np.abs(g64))
+
+
+def test_thread_count_does_not_change_bits():
+    n = O.load("f64").oracle_get_threads()
+    try:
+        a = run_steps(S.TINY, "f64", threads=1)
+        b = run_steps(S.TINY, "f64", threads=4)
+    finally:
+        O.set_threads(n, "f64")
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_abi_errors_and_accumulation():
+    w = S.TINY
+    p = S.init_params(w.model)
+    x, y = S.tokens(w)
+    m = O.OracleGPT2(w.model, w.B, w.T, p)
+    assert m.backward() == -2                       # no forward yet
+    assert m.update(1e-4, 0.9, 0.999, 1e-8, 0.0, 0) == -2
+    bad = x.copy()
+    bad[0, 0] = 512
+    assert math.isnan(m.forward(bad, y)) and m.last_error() == -1
+    assert math.isnan(m.forward(np.zeros((1, 65), np.int32), None))   # T > maxT
+    assert m.forward(x, None) == -1.0
+    assert m.backward() == -2                       # forward had no targets
+    m.forward(x, y)
+    m.zero_grad()
+    m.backward()
+    g1 = m.grads.copy()
+    m.backward()
+    np.testing.assert_allclose(m.grads, 2 * g1, rtol=0, atol=1e-12 * np.abs(g1).max())
+    with pytest.raises(ValueError):
+        O.OracleGPT2(S.ModelShape(64, 512, 2, 3, 64), 2, 32, np.zeros(10))
