@@ -1,0 +1,181 @@
+/*
+ * gpt2.h -- C ABI of the MI355X (gfx950) GPT-2 fp32 training step.
+ *
+ * The library follows the decomposition the pages give for llm.c's train_gpt2.c
+ * ("llm.c：Andrej Karpathy带你从零复现LLM", section 核心代码解读：train_gpt2.c):
+ * a model config, a flat parameter tensor set, an activation set, and the calls
+ * build, forward (outputs and loss), zero_grad, backward and an AdamW update.  As on
+ * the pages, all memory is laid out once in flat 1-D buffers and never reallocated
+ * ("OpenAI创始大神手搓千行C代码训练GPT", section 手动实现每个层前向 / 反向传播; 新智元
+ * article "千行C代码训完GPT-2", section 纯CUDA也可训).  Checkpoint loading is replaced by
+ * gpt2_build on caller-initialised parameters.
+ *
+ * Conventions for every call:
+ *   - Pointers named as device pointers must point to device memory of the current
+ *     HIP device; the library borrows them and never frees them.  Host pointers are
+ *     only read during the call.
+ *   - float buffers must be 16-byte aligned.
+ *   - Work is enqueued on the hipStream_t passed to gpt2_build (or to the standalone
+ *     calls); NULL means the default stream.  Only gpt2_forward synchronises.
+ *   - A gpt2 handle is not thread-safe; calls on one handle must not overlap.
+ *   - Errors: status codes below; gpt2_forward returns NaN and records the code,
+ *     readable through gpt2_last_error.
+ */
+#ifndef GPT2_MI355X_H
+#define GPT2_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Model shape: the five fields the pages' log prints for GPT2Config (新智元 article,
+ * 快速入门).  channels must be a multiple of num_heads and of 4; head size
+ * channels/num_heads must be 16, 32 or 64. */
+typedef struct gpt2_config {
+    int max_seq_len;
+    int vocab_size;
+    int num_layers;
+    int num_heads;
+    int channels;
+} gpt2_config;
+
+typedef struct gpt2 gpt2; /* opaque model handle */
+
+enum {
+    GPT2_OK = 0,
+    GPT2_EINVAL = -1,  /* bad argument, shape or token id */
+    GPT2_ESTATE = -2,  /* call out of order (backward without a forward with targets, t < 1) */
+    GPT2_EDEVICE = -3, /* a HIP call failed */
+    GPT2_ENOMEM = -4   /* host allocation failed */
+};
+
+#define GPT2_NUM_PARAM_TENSORS 16
+
+/* Number of parameters: V*C + maxT*C + L*(12*C*C + 13*C) + 2*C (124,439,808 for the
+ * 124M shape the pages print).  0 for an invalid config.  Host-only. */
+size_t gpt2_num_parameters(const gpt2_config* cfg);
+
+/* Offsets and lengths (in floats) of the 16 parameter tensors inside the flat buffer,
+ * in this order, each row-major, linear weights stored (out, in):
+ *   wte (V,C), wpe (maxT,C), ln1w (L,C), ln1b (L,C), qkvw (L,3C,C), qkvb (L,3C),
+ *   attprojw (L,C,C), attprojb (L,C), ln2w (L,C), ln2b (L,C), fcw (L,4C,C), fcb (L,4C),
+ *   fcprojw (L,C,4C), fcprojb (L,C), lnfw (C), lnfb (C).
+ * The order is the pages' ParameterTensors listing (huxiu page, 核心代码解读 item 2).
+ * grads, m and v use the same offsets.  Host-only; returns GPT2_OK or GPT2_EINVAL. */
+int gpt2_param_layout(const gpt2_config* cfg, size_t off[GPT2_NUM_PARAM_TENSORS],
+                      size_t len[GPT2_NUM_PARAM_TENSORS]);
+
+/* Sizes (in floats) of the two arenas a model of batch shape (B, T) needs: the
+ * activation arena and the gradient scratch arena.  Host-only. */
+int gpt2_arena_sizes(const gpt2_config* cfg, int B, int T, size_t* n_acts, size_t* n_grad_scratch);
+
+/* The six caller-owned device buffers.  params, grads, m, v hold
+ * gpt2_num_parameters floats each; acts and grad_scratch the sizes gpt2_arena_sizes
+ * returns.  They must outlive the handle. */
+typedef struct gpt2_buffers {
+    float* params;
+    float* grads;
+    float* m;
+    float* v;
+    float* acts;
+    float* grad_scratch;
+} gpt2_buffers;
+
+/* Validate the config, carve the arenas for batches of at most B*T positions with
+ * T <= max_seq_len, zero grads, m and v on `stream` (a hipStream_t or NULL).  The caller
+ * writes the initial parameters.  *out receives the handle.  Allocates only a small
+ * host struct and a small pinned host block for the loss read-back. */
+int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buffers* bufs,
+               void* stream);
+
+/* Forward pass (huxiu page 核心代码解读 item 3: outputs and loss).  inputs and targets
+ * are device pointers to B*T int32 token ids, row-major (B,T); ids must lie in
+ * [0, vocab_size).  Requires 1 <= T <= max_seq_len and B*T <= the built B*T.
+ * Returns the mean cross-entropy over the B*T positions.  With targets == NULL the
+ * logits and probabilities are computed and -1.0f is returned.  Synchronises the
+ * stream.  Returns NaN on error (GPT2_EINVAL for bad shapes or token ids found on the
+ * device, GPT2_EDEVICE for a HIP failure). */
+float gpt2_forward(gpt2* model, const int32_t* inputs, const int32_t* targets, int B, int T);
+
+/* Zero the parameter gradients (activation gradients are scratch that each backward
+ * rewrites, so there is nothing else to clear).  Enqueue only. */
+int gpt2_zero_grad(gpt2* model);
+
+/* Backward pass of the last forward (which must have had targets, else GPT2_ESTATE).
+ * ADDS into grads: two calls without gpt2_zero_grad give twice the gradients.
+ * Enqueue only. */
+int gpt2_backward(gpt2* model);
+
+/* AdamW over the whole flat buffer (huxiu page 核心代码解读 item 3; lr 1e-4 on the
+ * 新智元 page 快速入门):  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ * p -= lr * (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + weight_decay * p).
+ * t is the 1-based step count (GPT2_ESTATE if t < 1).  Enqueue only. */
+int gpt2_update(gpt2* model, float lr, float beta1, float beta2, float eps, float weight_decay,
+                int t);
+
+/* Last error recorded on the handle (GPT2_OK if none). */
+int gpt2_last_error(const gpt2* model);
+
+/* Static string for a status code. */
+const char* gpt2_strerror(int code);
+
+/* Release the handle (not the caller's buffers).  Synchronises the stream first. */
+void gpt2_free(gpt2* model);
+
+/* Activation tensors inside `acts`, for inspection and tests. */
+enum {
+    GPT2_ACT_ENCODED = 0,  /* (B*T, C) token + position embedding */
+    GPT2_ACT_LN1,          /* per layer (B*T, C) */
+    GPT2_ACT_LN1_MEAN,     /* per layer (B*T) */
+    GPT2_ACT_LN1_RSTD,     /* per layer (B*T) */
+    GPT2_ACT_QKV,          /* per layer (B*T, 3C) */
+    GPT2_ACT_ATTY,         /* per layer (B*T, C) attention output, heads concatenated */
+    GPT2_ACT_ATT_LSE,      /* per layer (B, NH, T) log-sum-exp of each softmax row */
+    GPT2_ACT_RESIDUAL2,    /* per layer (B*T, C) */
+    GPT2_ACT_LN2,          /* per layer (B*T, C) */
+    GPT2_ACT_LN2_MEAN,     /* per layer (B*T) */
+    GPT2_ACT_LN2_RSTD,     /* per layer (B*T) */
+    GPT2_ACT_FCH,          /* per layer (B*T, 4C) pre-GELU */
+    GPT2_ACT_FCH_GELU,     /* per layer (B*T, 4C) */
+    GPT2_ACT_RESIDUAL3,    /* per layer (B*T, C) */
+    GPT2_ACT_LNF,          /* (B*T, C) */
+    GPT2_ACT_LNF_MEAN,     /* (B*T) */
+    GPT2_ACT_LNF_RSTD,     /* (B*T) */
+    GPT2_ACT_PROBS,        /* (B*T, V) with leading dimension ld >= V: softmax after the
+                              forward, d(loss)/d(logits) after the backward */
+    GPT2_ACT_LOSSES,       /* (B*T) per-position cross-entropy */
+    GPT2_NUM_ACTS
+};
+
+/* Where tensor `tensor` of layer `layer` (ignored for whole-model tensors) lives:
+ * offset in floats from `acts`, rows, columns and leading dimension, at the batch shape
+ * of the last forward (the built shape before any forward).  Host-only. */
+int gpt2_activation_view(const gpt2* model, int tensor, int layer, size_t* offset, size_t* rows,
+                         size_t* cols, size_t* ld);
+
+/* Standalone LayerNorm forward, overwrite semantics (the pages' worked layer: dakule
+ * page 手动实现每个层前向 / 反向传播; 新智元 page 教程).  Device pointers: x, y (N,C);
+ * w, b (C); mean, rstd (N).  y = (x - mean) * rstd * w + b with biased variance and
+ * rstd = 1/sqrt(var + eps).  C must be a multiple of 4 and at most 4096. */
+int gpt2_layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,
+                           const float* b, int N, int C, float eps, void* stream);
+
+/* Floats of device workspace gpt2_layernorm_backward needs for (N, C). */
+size_t gpt2_layernorm_backward_workspace(int N, int C);
+
+/* Standalone LayerNorm backward, overwrite semantics: writes dx (N,C), dw and db (C)
+ * from dy, x, w, and the mean and rstd the forward kept.  `workspace` is a device
+ * buffer of at least gpt2_layernorm_backward_workspace(N, C) floats (GPT2_EINVAL if
+ * smaller); its contents on entry do not matter.  Deterministic. */
+int gpt2_layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x,
+                            const float* w, const float* mean, const float* rstd, int N, int C,
+                            float* workspace, size_t workspace_floats, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT2_MI355X_H */

@@ -589,18 +589,31 @@ static void carve(oracle_gpt2* g, int B, int T) {
     size_t o = 0;
     for (int i = 0; i < NACT; i++) {
         g->a[i] = g->acts + o;
-        g->da[i] = g->dacts + o;
+        g->da[i] = g->dacts ? g->dacts + o : NULL;
         o += len[i];
     }
 }
 
-/* Build: borrow the four caller-owned flat buffers (params, grads, m, v; params
- * already initialised), zero grads/m/v, allocate the two activation blocks once. */
+/* The activation-gradient block, allocated on first use. */
+static int ensure_dacts(oracle_gpt2* g) {
+    if (!g->grads) return O_ESTATE;
+    if (!g->dacts) {
+        g->dacts = (real*)calloc(g->num_acts, sizeof(real));
+        if (!g->dacts) return O_ENOMEM;
+        carve(g, g->B ? g->B : g->maxB, g->T ? g->T : g->maxT);
+    }
+    return O_OK;
+}
+
+/* Build: borrow the caller-owned flat buffers (params already initialised; grads, m,
+ * v zeroed here), allocate the activation block once.  grads, m and v may all be NULL
+ * for a forward-only model; the activation-gradient block is allocated on the first
+ * zero_grad or backward. */
 EXPORT int oracle_gpt2_build(oracle_gpt2** out, const oracle_config* cfg, int B, int T,
                              real* params, real* grads, real* m, real* v) {
-    if (!out || !config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !params ||
-        !grads || !m || !v)
+    if (!out || !config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !params)
         return O_EINVAL;
+    if ((grads || m || v) && !(grads && m && v)) return O_EINVAL;
     oracle_gpt2* g = (oracle_gpt2*)calloc(1, sizeof(oracle_gpt2));
     if (!g) return O_ENOMEM;
     g->cfg = *cfg;
@@ -615,17 +628,18 @@ EXPORT int oracle_gpt2_build(oracle_gpt2** out, const oracle_config* cfg, int B,
     oracle_gpt2_param_layout(cfg, off, len);
     for (int i = 0; i < NPARAM; i++) {
         g->p[i] = params + off[i];
-        g->gp[i] = grads + off[i];
+        g->gp[i] = grads ? grads + off[i] : NULL;
     }
-    memset(grads, 0, g->num_params * sizeof(real));
-    memset(m, 0, g->num_params * sizeof(real));
-    memset(v, 0, g->num_params * sizeof(real));
+    if (grads) {
+        memset(grads, 0, g->num_params * sizeof(real));
+        memset(m, 0, g->num_params * sizeof(real));
+        memset(v, 0, g->num_params * sizeof(real));
+    }
     g->num_acts = oracle_gpt2_num_activations(cfg, B, T);
     g->acts = (real*)calloc(g->num_acts, sizeof(real));
-    g->dacts = (real*)calloc(g->num_acts, sizeof(real));
     g->inputs = (int32_t*)calloc((size_t)B * T, sizeof(int32_t));
     g->targets = (int32_t*)calloc((size_t)B * T, sizeof(int32_t));
-    if (!g->acts || !g->dacts || !g->inputs || !g->targets) {
+    if (!g->acts || !g->inputs || !g->targets) {
         free(g->acts);
         free(g->dacts);
         free(g->inputs);
@@ -730,6 +744,8 @@ EXPORT double oracle_gpt2_forward(oracle_gpt2* g, const int32_t* inputs, const i
  * item 3 says zero_grad clears both). */
 EXPORT int oracle_gpt2_zero_grad(oracle_gpt2* g) {
     if (!g) return O_EINVAL;
+    int rc = ensure_dacts(g);
+    if (rc != O_OK) return g->last_error = rc;
     memset(g->grads, 0, g->num_params * sizeof(real));
     memset(g->dacts, 0, g->num_acts * sizeof(real));
     return O_OK;
@@ -746,6 +762,8 @@ EXPORT int oracle_gpt2_backward(oracle_gpt2* g) {
         g->last_error = O_ESTATE;
         return O_ESTATE;
     }
+    int rc = ensure_dacts(g);
+    if (rc != O_OK) return g->last_error = rc;
     const oracle_config* cfg = &g->cfg;
     int B = g->B, T = g->T;
     int V = cfg->vocab_size, C = cfg->channels, L = cfg->num_layers, NH = cfg->num_heads;
@@ -798,7 +816,7 @@ EXPORT int oracle_gpt2_backward(oracle_gpt2* g) {
 
 EXPORT int oracle_gpt2_update(oracle_gpt2* g, real lr, real b1, real b2, real eps, real wd, int t) {
     if (!g) return O_EINVAL;
-    if (t < 1) {
+    if (t < 1 || !g->grads) {
         g->last_error = O_ESTATE;
         return O_ESTATE;
     }
@@ -818,5 +836,6 @@ EXPORT real* oracle_gpt2_activation(oracle_gpt2* g, int id, int layer, int grad,
     if (per_layer && (layer < 0 || layer >= g->cfg.num_layers)) return NULL;
     if (count) *count = n;
     real* base = grad ? g->da[id] : g->a[id];
+    if (!base) return NULL;
     return base + (per_layer ? (size_t)layer * n : 0);
 }

@@ -127,7 +127,8 @@ def set_threads(n: int, precision: str = "f64") -> None:
 class OracleGPT2:
     """The oracle model: owns numpy params/grads/m/v in the oracle's precision."""
 
-    def __init__(self, shape, B: int, T: int, params: np.ndarray, precision: str = "f64"):
+    def __init__(self, shape, B: int, T: int, params: np.ndarray, precision: str = "f64",
+                 forward_only: bool = False):
         self.lib = load(precision)
         self.precision = precision
         self.dtype = dtype_of(precision)
@@ -137,9 +138,12 @@ class OracleGPT2:
         if params.size != n:
             raise ValueError(f"params has {params.size} elements, model needs {n}")
         self.params = np.ascontiguousarray(params, dtype=self.dtype).copy()
-        self.grads = np.zeros(n, self.dtype)
-        self.m = np.zeros(n, self.dtype)
-        self.v = np.zeros(n, self.dtype)
+        if forward_only:
+            self.grads = self.m = self.v = None
+        else:
+            self.grads = np.zeros(n, self.dtype)
+            self.m = np.zeros(n, self.dtype)
+            self.v = np.zeros(n, self.dtype)
         h = ct.c_void_p()
         rc = self.lib.oracle_gpt2_build(ct.byref(h), ct.byref(self.cfg), B, T, _ptr(self.params),
                                         _ptr(self.grads), _ptr(self.m), _ptr(self.v))

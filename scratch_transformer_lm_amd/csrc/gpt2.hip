@@ -1,0 +1,473 @@
+// The C ABI of the GPT-2 fp32 training step: parameter layout, arena carving and the
+// order of kernel launches for forward, zero_grad, backward and update.
+//
+// Structure follows the pages' train_gpt2.c walk-through (huxiu page "llm.c：Andrej
+// Karpathy带你从零复现LLM", 核心代码解读): GPT2Config, ParameterTensors in one flat
+// buffer, ActivationTensors in one flat arena carved once ("OpenAI创始大神手搓千行C代码
+// 训练GPT", 手动实现每个层前向 / 反向传播), and the calls forward / zero_grad /
+// backward / update.  The block is GPT-2's pre-LayerNorm block:
+//   x += attproj(attention(qkv(ln1(x))));  x += fcproj(gelu(fc(ln2(x))))
+// followed by a final LayerNorm and the LM head tied to the token embedding (the only
+// reading that reproduces the 124,439,808 parameters the pages print).
+//
+// Differences from the plain layer-by-layer decomposition, none of which changes what
+// is computed: residual adds and GELU run in the GEMM epilogues; attention keeps a
+// per-row log-sum-exp instead of the two (B,NH,T,T) score tensors and recomputes the
+// probabilities in its backward; activation gradients live in a small per-layer
+// scratch that each backward rewrites (the residual stream's gradient is one buffer
+// that every block adds into), so zero_grad only clears the parameter gradients.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/gpt2.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace gpt2k;
+
+namespace {
+
+constexpr int NP = GPT2_NUM_PARAM_TENSORS;
+constexpr size_t ALIGN = 64;  // floats (256 bytes)
+
+size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
+
+enum { P_WTE, P_WPE, P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_ATTPROJW, P_ATTPROJB, P_LN2W, P_LN2B,
+       P_FCW, P_FCB, P_FCPROJW, P_FCPROJB, P_LNFW, P_LNFB };
+
+bool config_ok(const gpt2_config* c) {
+    if (!c || c->max_seq_len <= 0 || c->vocab_size <= 0 || c->num_layers <= 0 || c->num_heads <= 0 ||
+        c->channels <= 0)
+        return false;
+    if (c->channels % c->num_heads || c->channels % 4 || c->channels > 4096) return false;
+    const int hs = c->channels / c->num_heads;
+    return hs == 16 || hs == 32 || hs == 64;
+}
+
+void param_sizes(const gpt2_config* cfg, size_t len[NP]) {
+    const size_t V = cfg->vocab_size, C = cfg->channels, L = cfg->num_layers, maxT = cfg->max_seq_len;
+    const size_t s[NP] = {V * C, maxT * C, L * C, L * C, L * 3 * C * C, L * 3 * C, L * C * C, L * C,
+                          L * C, L * C, L * 4 * C * C, L * 4 * C, L * C * 4 * C, L * C, C, C};
+    for (int i = 0; i < NP; i++) len[i] = s[i];
+}
+
+// Where each activation lives: base offset, per-layer stride (0 for whole-model
+// tensors), columns and leading dimension; rows are the current B*T (the lse tensor is
+// (B, NH, T), stored as B*T rows of NH... see lse_index).
+struct ActInfo {
+    size_t off, layer_stride, cols, ld;
+};
+
+struct Layout {
+    size_t BT, Vp;
+    ActInfo a[GPT2_NUM_ACTS];
+    size_t tok_in, tok_tgt;  // int32 arrays inside acts (offset in 4-byte words)
+    size_t n_acts;
+    // grad_scratch
+    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, partial, n_partial, n_scratch;
+};
+
+long split_budget(const gpt2_config* c, size_t BT) {
+    const size_t C = c->channels;
+    return (long)std::max<size_t>(8 * 4 * C * C, 2 * BT * C);
+}
+
+Layout make_layout(const gpt2_config* c, int B, int T) {
+    Layout y{};
+    const size_t C = c->channels, L = c->num_layers, NH = c->num_heads, V = c->vocab_size;
+    const size_t BT = (size_t)B * T;
+    y.BT = BT;
+    y.Vp = (V + 63) / 64 * 64;
+    size_t o = 0;
+    auto put = [&](int id, size_t cols, size_t ld, bool per_layer, size_t rows) {
+        const size_t slab = align_up(rows * ld);
+        y.a[id] = ActInfo{o, per_layer ? slab : 0, cols, ld};
+        o += per_layer ? L * slab : slab;
+    };
+    put(GPT2_ACT_ENCODED, C, C, false, BT);
+    put(GPT2_ACT_LN1, C, C, true, BT);
+    put(GPT2_ACT_LN1_MEAN, 1, 1, true, BT);
+    put(GPT2_ACT_LN1_RSTD, 1, 1, true, BT);
+    put(GPT2_ACT_QKV, 3 * C, 3 * C, true, BT);
+    put(GPT2_ACT_ATTY, C, C, true, BT);
+    put(GPT2_ACT_ATT_LSE, NH, NH, true, BT);
+    put(GPT2_ACT_RESIDUAL2, C, C, true, BT);
+    put(GPT2_ACT_LN2, C, C, true, BT);
+    put(GPT2_ACT_LN2_MEAN, 1, 1, true, BT);
+    put(GPT2_ACT_LN2_RSTD, 1, 1, true, BT);
+    put(GPT2_ACT_FCH, 4 * C, 4 * C, true, BT);
+    put(GPT2_ACT_FCH_GELU, 4 * C, 4 * C, true, BT);
+    put(GPT2_ACT_RESIDUAL3, C, C, true, BT);
+    put(GPT2_ACT_LNF, C, C, false, BT);
+    put(GPT2_ACT_LNF_MEAN, 1, 1, false, BT);
+    put(GPT2_ACT_LNF_RSTD, 1, 1, false, BT);
+    put(GPT2_ACT_PROBS, V, y.Vp, false, BT);
+    put(GPT2_ACT_LOSSES, 1, 1, false, BT);
+    y.tok_in = o;
+    o += align_up(BT);
+    y.tok_tgt = o;
+    o += align_up(BT);
+    y.n_acts = o;
+
+    size_t s = HDR_WORDS;
+    auto take = [&](size_t n) {
+        const size_t at = s;
+        s += align_up(n);
+        return at;
+    };
+    y.dres = take(BT * C);
+    y.dln = take(BT * C);
+    y.datty = take(BT * C);
+    y.dqkv = take(BT * 3 * C);
+    y.dfch = take(BT * 4 * C);
+    y.delta = take(BT * NH);
+    y.enc_work = take(1 + BT);
+    size_t np = (size_t)split_budget(c, BT);
+    np = std::max(np, layernorm_partial_floats((int)BT, (int)C));
+    np = std::max(np, colsum_partial_floats((int)BT, (int)(4 * C)));
+    y.n_partial = np;
+    y.partial = take(np);
+    y.n_scratch = s;
+    return y;
+}
+
+// Split-K count for a GEMM with `tiles` output tiles and reduction length K: enough
+// blocks to put two on every CU, at least 256 of K per split, within the partial budget.
+int choose_splits(long tiles, int K, long MN, long budget) {
+    if (tiles >= 512) return 1;
+    long s = (512 + tiles - 1) / tiles;
+    s = std::min<long>(s, std::max(1, K / 256));
+    s = std::min<long>(s, 32);
+    s = std::min<long>(s, std::max<long>(1, budget / std::max<long>(1, MN)));
+    return splitk_effective(K, (int)std::max<long>(1, s));
+}
+
+long tiles_of(long M, long N) { return ((M + 127) / 128) * ((N + 127) / 128); }
+
+}  // namespace
+
+struct gpt2 {
+    gpt2_config cfg;
+    int maxB, maxT;
+    int B, T;
+    Layout lay;
+    hipStream_t st;
+    gpt2_buffers buf;
+    size_t nparams;
+    size_t poff[NP], plen[NP];
+    int* host_ret;  // pinned: [loss bits, flags]
+    int last_error;
+    bool have_forward, have_targets, probs_are_grads;
+};
+
+namespace {
+
+int fail(gpt2* g, int code) {
+    if (g) g->last_error = code;
+    return code;
+}
+
+#define HIPCHK(g, expr)                                    \
+    do {                                                   \
+        hipError_t e_ = (expr);                            \
+        if (e_ != hipSuccess) return fail((g), GPT2_EDEVICE); \
+    } while (0)
+
+float* P(gpt2* g, int i) { return g->buf.params + g->poff[i]; }
+float* G(gpt2* g, int i) { return g->buf.grads + g->poff[i]; }
+float* A(gpt2* g, int id, int l = 0) { return g->buf.acts + g->lay.a[id].off + (size_t)l * g->lay.a[id].layer_stride; }
+float* S(gpt2* g, size_t off) { return g->buf.grad_scratch + off; }
+int32_t* tok_in(gpt2* g) { return reinterpret_cast<int32_t*>(g->buf.acts + g->lay.tok_in); }
+int32_t* tok_tgt(gpt2* g) { return reinterpret_cast<int32_t*>(g->buf.acts + g->lay.tok_tgt); }
+int* flags(gpt2* g) { return reinterpret_cast<int*>(g->buf.grad_scratch + HDR_FLAGS); }
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, int T, float* loss_out) {
+    const gpt2_config& c = g->cfg;
+    const int C = c.channels, L = c.num_layers, NH = c.num_heads, V = c.vocab_size;
+    const int BT = B * T;
+    const long Vp = (long)g->lay.Vp;
+    hipStream_t st = g->st;
+    g->B = B;
+    g->T = T;
+    g->have_forward = false;
+    g->probs_are_grads = false;
+    HIPCHK(g, hipMemcpyAsync(tok_in(g), inputs, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
+    if (targets) HIPCHK(g, hipMemcpyAsync(tok_tgt(g), targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
+    HIPCHK(g, hipMemsetAsync(g->buf.grad_scratch, 0, HDR_WORDS * sizeof(float), st));
+    HIPCHK(g, encoder_forward(A(g, GPT2_ACT_ENCODED), tok_in(g), P(g, P_WTE), P(g, P_WPE), B, T, C, V, flags(g), st));
+    for (int l = 0; l < L; l++) {
+        float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
+        HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LN1, l), A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l),
+                                    residual, P(g, P_LN1W) + l * C, P(g, P_LN1B) + l * C, BT, C, 1e-5f, st));
+        HIPCHK(g, linear_forward(A(g, GPT2_ACT_QKV, l), 3 * C, A(g, GPT2_ACT_LN1, l), P(g, P_QKVW) + (size_t)l * 3 * C * C,
+                                 P(g, P_QKVB) + l * 3 * C, nullptr, nullptr, BT, 3 * C, C, st));
+        HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T, C, NH, st));
+        HIPCHK(g, linear_forward(A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), P(g, P_ATTPROJW) + (size_t)l * C * C,
+                                 P(g, P_ATTPROJB) + l * C, residual, nullptr, BT, C, C, st));
+        HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LN2, l), A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l),
+                                    A(g, GPT2_ACT_RESIDUAL2, l), P(g, P_LN2W) + l * C, P(g, P_LN2B) + l * C, BT, C, 1e-5f, st));
+        HIPCHK(g, linear_forward(A(g, GPT2_ACT_FCH_GELU, l), 4 * C, A(g, GPT2_ACT_LN2, l), P(g, P_FCW) + (size_t)l * 4 * C * C,
+                                 P(g, P_FCB) + l * 4 * C, nullptr, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C, st));
+        HIPCHK(g, linear_forward(A(g, GPT2_ACT_RESIDUAL3, l), C, A(g, GPT2_ACT_FCH_GELU, l), P(g, P_FCPROJW) + (size_t)l * 4 * C * C,
+                                 P(g, P_FCPROJB) + l * C, A(g, GPT2_ACT_RESIDUAL2, l), nullptr, BT, C, 4 * C, st));
+    }
+    HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LNF), A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD),
+                                A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, 1e-5f, st));
+    HIPCHK(g, linear_forward(A(g, GPT2_ACT_PROBS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT, V, C, st));
+    HIPCHK(g, softmax_xent_forward(A(g, GPT2_ACT_PROBS), Vp, A(g, GPT2_ACT_LOSSES), targets ? tok_tgt(g) : nullptr, BT, V,
+                                   flags(g), st));
+    if (targets) HIPCHK(g, loss_mean(g->buf.grad_scratch + HDR_LOSS, A(g, GPT2_ACT_LOSSES), BT, st));
+    HIPCHK(g, hipMemcpyAsync(g->host_ret, g->buf.grad_scratch, 2 * sizeof(int), hipMemcpyDeviceToHost, st));
+    HIPCHK(g, hipStreamSynchronize(st));
+    if (g->host_ret[1] != 0) return fail(g, GPT2_EINVAL);
+    float loss;
+    memcpy(&loss, &g->host_ret[0], sizeof(float));
+    *loss_out = targets ? loss : -1.0f;
+    g->have_forward = true;
+    g->have_targets = targets != nullptr;
+    return GPT2_OK;
+}
+
+int backward_impl(gpt2* g) {
+    const gpt2_config& c = g->cfg;
+    const int C = c.channels, L = c.num_layers, NH = c.num_heads, V = c.vocab_size;
+    const int B = g->B, T = g->T, BT = B * T;
+    const long Vp = (long)g->lay.Vp;
+    const long budget = (long)g->lay.n_partial;
+    hipStream_t st = g->st;
+    float* part = S(g, g->lay.partial);
+    float* dres = S(g, g->lay.dres);
+    float* dln = S(g, g->lay.dln);
+    float* datty = S(g, g->lay.datty);
+    float* dqkv = S(g, g->lay.dqkv);
+    float* dfch = S(g, g->lay.dfch);
+    float* probs = A(g, GPT2_ACT_PROBS);
+
+    // d loss / d logits = (p - onehot) / (B*T), in place over the probabilities.
+    if (!g->probs_are_grads) {
+        HIPCHK(g, xent_backward(probs, Vp, tok_tgt(g), BT, V, 1.0f / (float)BT, st));
+        g->probs_are_grads = true;
+    }
+    // LM head (tied): dlnf = dlogits . wte;  dwte += dlogits^T . lnf.
+    HIPCHK(g, linear_dgrad(dln, probs, Vp, P(g, P_WTE), nullptr, BT, C, V,
+                           choose_splits(tiles_of(BT, C), V, (long)BT * C, budget), part, st));
+    HIPCHK(g, linear_wgrad(G(g, P_WTE), probs, Vp, A(g, GPT2_ACT_LNF), V, C, BT,
+                           choose_splits(tiles_of(V, C), BT, (long)V * C, budget), part, st));
+    HIPCHK(g, layernorm_backward(dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
+                                 A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
+    for (int l = L - 1; l >= 0; l--) {
+        float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
+        // MLP projection: residual3 = residual2 + gelu(fch) . Wp^T + bp.
+        HIPCHK(g, linear_wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, dres, C, A(g, GPT2_ACT_FCH_GELU, l), C, 4 * C, BT,
+                               choose_splits(tiles_of(C, 4 * C), BT, 4L * C * C, budget), part, st));
+        HIPCHK(g, colsum_accumulate(G(g, P_FCPROJB) + l * C, dres, C, BT, C, part, st));
+        HIPCHK(g, linear_dgrad(dfch, dres, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C,
+                               1, part, st));
+        // MLP expansion: fch = ln2 . Wf^T + bf.
+        HIPCHK(g, linear_wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, dfch, 4 * C, A(g, GPT2_ACT_LN2, l), 4 * C, C, BT,
+                               choose_splits(tiles_of(4 * C, C), BT, 4L * C * C, budget), part, st));
+        HIPCHK(g, colsum_accumulate(G(g, P_FCB) + l * 4 * C, dfch, 4 * C, BT, 4 * C, part, st));
+        HIPCHK(g, linear_dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, nullptr, BT, C, 4 * C,
+                               choose_splits(tiles_of(BT, C), 4 * C, (long)BT * C, budget), part, st));
+        HIPCHK(g, layernorm_backward(dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
+                                     P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C,
+                                     true, true, part, st));
+        // Attention projection: residual2 = residual + atty . Wa^T + ba.
+        HIPCHK(g, linear_wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, dres, C, A(g, GPT2_ACT_ATTY, l), C, C, BT,
+                               choose_splits(tiles_of(C, C), BT, (long)C * C, budget), part, st));
+        HIPCHK(g, colsum_accumulate(G(g, P_ATTPROJB) + l * C, dres, C, BT, C, part, st));
+        HIPCHK(g, linear_dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, nullptr, BT, C, C,
+                               choose_splits(tiles_of(BT, C), C, (long)BT * C, budget), part, st));
+        HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
+                                     A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
+        // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
+        HIPCHK(g, linear_wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, dqkv, 3 * C, A(g, GPT2_ACT_LN1, l), 3 * C, C, BT,
+                               choose_splits(tiles_of(3 * C, C), BT, 3L * C * C, budget), part, st));
+        HIPCHK(g, colsum_accumulate(G(g, P_QKVB) + l * 3 * C, dqkv, 3 * C, BT, 3 * C, part, st));
+        HIPCHK(g, linear_dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, nullptr, BT, C, 3 * C,
+                               choose_splits(tiles_of(BT, C), 3 * C, (long)BT * C, budget), part, st));
+        HIPCHK(g, layernorm_backward(dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
+                                     A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
+    }
+    HIPCHK(g, encoder_backward_ws(G(g, P_WTE), G(g, P_WPE), dres, tok_in(g), B, T, C,
+                                  reinterpret_cast<int*>(S(g, g->lay.enc_work)), st));
+    return GPT2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gpt2_num_parameters(const gpt2_config* cfg) {
+    if (!config_ok(cfg)) return 0;
+    size_t len[NP], n = 0;
+    param_sizes(cfg, len);
+    for (int i = 0; i < NP; i++) n += len[i];
+    return n;
+}
+
+int gpt2_param_layout(const gpt2_config* cfg, size_t off[NP], size_t len[NP]) {
+    if (!config_ok(cfg) || !off || !len) return GPT2_EINVAL;
+    param_sizes(cfg, len);
+    size_t o = 0;
+    for (int i = 0; i < NP; i++) {
+        off[i] = o;
+        o += len[i];
+    }
+    return GPT2_OK;
+}
+
+int gpt2_arena_sizes(const gpt2_config* cfg, int B, int T, size_t* n_acts, size_t* n_grad_scratch) {
+    if (!config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !n_acts || !n_grad_scratch)
+        return GPT2_EINVAL;
+    if ((long)B * T > (1L << 30)) return GPT2_EINVAL;
+    const Layout y = make_layout(cfg, B, T);
+    *n_acts = y.n_acts;
+    *n_grad_scratch = y.n_scratch;
+    return GPT2_OK;
+}
+
+int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buffers* bufs, void* stream) {
+    if (!out) return GPT2_EINVAL;
+    *out = nullptr;
+    if (!config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !bufs) return GPT2_EINVAL;
+    if ((long)B * T > (1L << 30)) return GPT2_EINVAL;
+    const gpt2_buffers& b = *bufs;
+    if (!b.params || !b.grads || !b.m || !b.v || !b.acts || !b.grad_scratch) return GPT2_EINVAL;
+    if (!aligned(b.params) || !aligned(b.grads) || !aligned(b.m) || !aligned(b.v) || !aligned(b.acts) ||
+        !aligned(b.grad_scratch))
+        return GPT2_EINVAL;
+    gpt2* g = (gpt2*)calloc(1, sizeof(gpt2));
+    if (!g) return GPT2_ENOMEM;
+    g->cfg = *cfg;
+    g->maxB = B;
+    g->maxT = T;
+    g->B = B;
+    g->T = T;
+    g->lay = make_layout(cfg, B, T);
+    g->st = (hipStream_t)stream;
+    g->buf = b;
+    g->nparams = gpt2_num_parameters(cfg);
+    gpt2_param_layout(cfg, g->poff, g->plen);
+    if (hipHostMalloc((void**)&g->host_ret, 2 * sizeof(int), hipHostMallocDefault) != hipSuccess) {
+        free(g);
+        return GPT2_EDEVICE;
+    }
+    if (fill_zero(b.grads, g->nparams, g->st) != hipSuccess || fill_zero(b.m, g->nparams, g->st) != hipSuccess ||
+        fill_zero(b.v, g->nparams, g->st) != hipSuccess) {
+        hipHostFree(g->host_ret);
+        free(g);
+        return GPT2_EDEVICE;
+    }
+    *out = g;
+    return GPT2_OK;
+}
+
+float gpt2_forward(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, int T) {
+    if (!g) return NAN;
+    g->last_error = GPT2_OK;
+    if (!inputs || B <= 0 || T <= 0 || T > g->cfg.max_seq_len || (long)B * T > (long)g->maxB * g->maxT) {
+        g->last_error = GPT2_EINVAL;
+        return NAN;
+    }
+    float loss = NAN;
+    const int rc = forward_impl(g, inputs, targets, B, T, &loss);
+    if (rc != GPT2_OK) {
+        g->last_error = rc;
+        g->have_forward = false;
+        return NAN;
+    }
+    return loss;
+}
+
+int gpt2_zero_grad(gpt2* g) {
+    if (!g) return GPT2_EINVAL;
+    HIPCHK(g, fill_zero(g->buf.grads, g->nparams, g->st));
+    return GPT2_OK;
+}
+
+int gpt2_backward(gpt2* g) {
+    if (!g) return GPT2_EINVAL;
+    if (!g->have_forward || !g->have_targets) return fail(g, GPT2_ESTATE);
+    return backward_impl(g);
+}
+
+int gpt2_update(gpt2* g, float lr, float beta1, float beta2, float eps, float weight_decay, int t) {
+    if (!g) return GPT2_EINVAL;
+    if (t < 1) return fail(g, GPT2_ESTATE);
+    const float bc1 = (float)(1.0 - pow((double)beta1, (double)t));
+    const float bc2 = (float)(1.0 - pow((double)beta2, (double)t));
+    HIPCHK(g, adamw(g->buf.params, g->buf.grads, g->buf.m, g->buf.v, g->nparams, lr, beta1, beta2, eps, weight_decay,
+                    bc1, bc2, g->st));
+    return GPT2_OK;
+}
+
+int gpt2_last_error(const gpt2* g) { return g ? g->last_error : GPT2_EINVAL; }
+
+const char* gpt2_strerror(int code) {
+    switch (code) {
+        case GPT2_OK: return "ok";
+        case GPT2_EINVAL: return "invalid argument, shape or token id";
+        case GPT2_ESTATE: return "call out of order";
+        case GPT2_EDEVICE: return "HIP call failed";
+        case GPT2_ENOMEM: return "out of host memory";
+        default: return "unknown error";
+    }
+}
+
+void gpt2_free(gpt2* g) {
+    if (!g) return;
+    hipStreamSynchronize(g->st);
+    hipHostFree(g->host_ret);
+    free(g);
+}
+
+int gpt2_activation_view(const gpt2* g, int tensor, int layer, size_t* offset, size_t* rows, size_t* cols,
+                         size_t* ld) {
+    if (!g || tensor < 0 || tensor >= GPT2_NUM_ACTS || !offset || !rows || !cols || !ld) return GPT2_EINVAL;
+    const ActInfo& a = g->lay.a[tensor];
+    if (a.layer_stride && (layer < 0 || layer >= g->cfg.num_layers)) return GPT2_EINVAL;
+    *offset = a.off + (a.layer_stride ? (size_t)layer * a.layer_stride : 0);
+    *rows = (size_t)g->B * g->T;
+    *cols = a.cols;
+    *ld = a.ld;
+    if (tensor == GPT2_ACT_ATT_LSE) {  // stored (B, NH, T)
+        *rows = (size_t)g->B * g->cfg.num_heads;
+        *cols = (size_t)g->T;
+        *ld = (size_t)g->T;
+    }
+    return GPT2_OK;
+}
+
+int gpt2_layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w, const float* b, int N,
+                           int C, float eps, void* stream) {
+    if (N < 0 || C <= 0 || C % 4 || C > 4096) return GPT2_EINVAL;
+    if (N == 0) return GPT2_OK;
+    if (!y || !mean || !rstd || !x || !w || !b) return GPT2_EINVAL;
+    if (!aligned(y) || !aligned(x) || !aligned(w) || !aligned(b)) return GPT2_EINVAL;
+    return layernorm_forward(y, mean, rstd, x, w, b, N, C, eps, (hipStream_t)stream) == hipSuccess ? GPT2_OK
+                                                                                                      : GPT2_EDEVICE;
+}
+
+size_t gpt2_layernorm_backward_workspace(int N, int C) {
+    if (N < 0 || C <= 0) return 0;
+    return layernorm_partial_floats(N, C);
+}
+
+int gpt2_layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x, const float* w,
+                            const float* mean, const float* rstd, int N, int C, float* workspace,
+                            size_t workspace_floats, void* stream) {
+    if (!dw || !db || N < 0 || C <= 0 || C % 4 || C > 4096) return GPT2_EINVAL;
+    if (N > 0 && (!dx || !dy || !x || !w || !mean || !rstd)) return GPT2_EINVAL;
+    if (N > 0 && (!aligned(dx) || !aligned(dy) || !aligned(x) || !aligned(w))) return GPT2_EINVAL;
+    if (N > 0 && (!workspace || workspace_floats < layernorm_partial_floats(N, C))) return GPT2_EINVAL;
+    return layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, N, C, false, false, workspace,
+                              (hipStream_t)stream) == hipSuccess
+               ? GPT2_OK
+               : GPT2_EDEVICE;
+}
+
+}  // extern "C"

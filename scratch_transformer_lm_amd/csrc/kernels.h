@@ -1,0 +1,80 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// All launchers enqueue on `st` and return the launch status; none synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace gpt2k {
+
+// ---- linear layers (gemm.hip) -------------------------------------------------------
+// out[M,N] (ld ldo) = inp[M,K] . w[N,K]^T, then by the non-null extras:
+//   bias: + bias[n];  resid: out = resid + (...) (resid has ld ldo);
+//   pre:  pre = (...) and out = gelu(pre) (pre has ld ldo).
+hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
+                          const float* bias, const float* resid, float* pre, int M, int N, int K,
+                          hipStream_t st);
+// din[M,N] = dout[M,K] (ld ld_dout) . w[K,N]; with gelu_pre: din *= gelu'(gelu_pre[M,N]).
+// splits > 1 (and no gelu_pre) splits K and adds the parts in order through `partial`
+// (splits*M*N floats).
+hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float* w,
+                        const float* gelu_pre, int M, int N, int K, int splits, float* partial,
+                        hipStream_t st);
+// dw[M,N] += dout[K,M]^T (dout ld ld_dout) . inp[K,N]; split-K as above.
+hipError_t linear_wgrad(float* dw, const float* dout, long ld_dout, const float* inp, int M, int N,
+                        int K, int splits, float* partial, hipStream_t st);
+// Number of splits linear_* actually uses for a requested count.
+int splitk_effective(int K, int splits);
+
+// ---- column sums (bias gradients) (norm.hip) ------------------------------------------
+// db[n] += sum_m x[m, n] over M rows (row stride ld); deterministic two-phase reduction
+// through `partial` (colsum_partial_floats(M, N) floats).
+size_t colsum_partial_floats(int M, int N);
+hipError_t colsum_accumulate(float* db, const float* x, long ld, int M, int N, float* partial,
+                             hipStream_t st);
+
+// ---- LayerNorm (norm.hip) -----------------------------------------------------------
+hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,
+                             const float* b, int N, int C, float eps, hipStream_t st);
+// dx (+)= ..., dw/db (+)= ...; accumulate flags choose += or =.  partial needs
+// layernorm_partial_floats(N, C) floats.
+size_t layernorm_partial_floats(int N, int C);
+hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x,
+                              const float* w, const float* mean, const float* rstd, int N, int C,
+                              bool accumulate_dx, bool accumulate_dwdb, float* partial,
+                              hipStream_t st);
+
+// ---- embedding (encoder.hip) --------------------------------------------------------
+hipError_t encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe,
+                           int B, int T, int C, int V, int* flags, hipStream_t st);
+// dwte/dwpe += ...; `work` is an int scratch of 1 + B*T entries.  Deterministic.
+hipError_t encoder_backward_ws(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
+                               int B, int T, int C, int* work, hipStream_t st);
+
+// ---- attention (attention.hip) ------------------------------------------------------
+// qkv (B,T,3C) -> out (B,T,C), lse (B,NH,T).
+hipError_t attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
+                             hipStream_t st);
+// dout (B,T,C) -> dqkv (B,T,3C) (overwritten); delta needs B*NH*T floats.
+hipError_t attention_backward(float* dqkv, float* delta, const float* dout, const float* qkv,
+                              const float* out, const float* lse, int B, int T, int C, int NH,
+                              hipStream_t st);
+
+// ---- softmax + cross-entropy (softmax_xent.hip) -------------------------------------
+// In place over logits rows (ld): probs; per-row loss when targets != NULL.
+hipError_t softmax_xent_forward(float* logits, long ld, float* losses, const int32_t* targets,
+                                int N, int V, int* flags, hipStream_t st);
+// Mean of losses[0..N) in double, written as float to *out.
+hipError_t loss_mean(float* out, const float* losses, int N, hipStream_t st);
+// In place: probs -> (probs - onehot(target)) * scale.
+hipError_t xent_backward(float* probs, long ld, const int32_t* targets, int N, int V, float scale,
+                         hipStream_t st);
+
+// ---- optimizer and fills (adamw.hip) ------------------------------------------------
+hipError_t adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float b1,
+                 float b2, float eps, float wd, float bc1, float bc2, hipStream_t st);
+hipError_t fill_zero(float* x, size_t n, hipStream_t st);
+
+}  // namespace gpt2k

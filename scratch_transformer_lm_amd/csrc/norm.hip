@@ -1,0 +1,274 @@
+// LayerNorm forward/backward and column sums (bias gradients) for gfx950.
+//
+// LayerNorm is the pages' worked example of a hand-written layer ("OpenAI创始大神手搓
+// 千行C代码训练GPT", 手动实现每个层前向 / 反向传播; 新智元 article, 教程).  Both
+// directions are HBM-bound: one wave64 owns a row, holds it in registers as float4s,
+// and reduces with cross-lane shuffles; nothing is re-read from memory.  The
+// cross-row sums (dgamma, dbeta, bias gradients) go through per-block partial rows that a
+// second kernel adds in a fixed order, so results are deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+
+namespace {
+
+constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
+constexpr int LN_MAX_BLOCKS = 512;
+constexpr int COLSUM_ROWS = 32;
+constexpr int COLSUM_MAX_CHUNKS = 256;
+
+template <int VPL>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, float* __restrict__ mean,
+                                                     float* __restrict__ rstd, const float* __restrict__ x,
+                                                     const float* __restrict__ w, const float* __restrict__ b,
+                                                     int N, int C, float eps) {
+    const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= N) return;
+    const int C4 = C >> 2;
+    const float4* xr = reinterpret_cast<const float4*>(x + (long)row * C);
+    float4 v[VPL];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; j++) {
+        const int i = lane + 64 * j;
+        v[j] = i < C4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    }
+    const float m = wave_sum(s) / (float)C;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; j++) {
+        const int i = lane + 64 * j;
+        if (i < C4) {
+            const float a = v[j].x - m, bb = v[j].y - m, c = v[j].z - m, d = v[j].w - m;
+            ss += (a * a + bb * bb) + (c * c + d * d);
+        }
+    }
+    const float var = wave_sum(ss) / (float)C;
+    const float r = 1.0f / sqrtf(var + eps);
+    float4* yr = reinterpret_cast<float4*>(y + (long)row * C);
+    const float4* w4 = reinterpret_cast<const float4*>(w);
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+#pragma unroll
+    for (int j = 0; j < VPL; j++) {
+        const int i = lane + 64 * j;
+        if (i < C4) {
+            const float4 ww = w4[i], bv = b4[i];
+            float4 o;
+            o.x = (v[j].x - m) * r * ww.x + bv.x;
+            o.y = (v[j].y - m) * r * ww.y + bv.y;
+            o.z = (v[j].z - m) * r * ww.z + bv.z;
+            o.w = (v[j].w - m) * r * ww.w + bv.w;
+            yr[i] = o;
+        }
+    }
+    if (lane == 0) {
+        mean[row] = m;
+        rstd[row] = r;
+    }
+}
+
+// dx = rstd * (g - mean(g) - xh * mean(g*xh)), g = w*dy, xh = (x-mean)*rstd.
+// Each block also leaves one partial row [dw | db] (2C floats) in `partial`.
+template <int VPL>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, float* __restrict__ partial,
+                                                     const float* __restrict__ dy, const float* __restrict__ x,
+                                                     const float* __restrict__ w, const float* __restrict__ mean,
+                                                     const float* __restrict__ rstd, int N, int C, int accumulate) {
+    extern __shared__ float red[];  // [4][C]
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int C4 = C >> 2;
+    const float4* w4 = reinterpret_cast<const float4*>(w);
+    float4 wv[VPL], pdw[VPL], pdb[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; j++) {
+        const int i = lane + 64 * j;
+        wv[j] = i < C4 ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        pdw[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        pdb[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int row = blockIdx.x * ROWS_PER_BLOCK + wave; row < N; row += gridDim.x * ROWS_PER_BLOCK) {
+        const float4* xr = reinterpret_cast<const float4*>(x + (long)row * C);
+        const float4* dr = reinterpret_cast<const float4*>(dy + (long)row * C);
+        const float m = mean[row], r = rstd[row];
+        float4 xh[VPL], g[VPL];
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            const int i = lane + 64 * j;
+            float4 xv = make_float4(0.f, 0.f, 0.f, 0.f), dv = xv;
+            if (i < C4) {
+                xv = xr[i];
+                dv = dr[i];
+            }
+            xh[j] = make_float4((xv.x - m) * r, (xv.y - m) * r, (xv.z - m) * r, (xv.w - m) * r);
+            if (i >= C4) xh[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            g[j] = make_float4(wv[j].x * dv.x, wv[j].y * dv.y, wv[j].z * dv.z, wv[j].w * dv.w);
+            sg += (g[j].x + g[j].y) + (g[j].z + g[j].w);
+            sgx += (g[j].x * xh[j].x + g[j].y * xh[j].y) + (g[j].z * xh[j].z + g[j].w * xh[j].w);
+            pdw[j].x += dv.x * xh[j].x;
+            pdw[j].y += dv.y * xh[j].y;
+            pdw[j].z += dv.z * xh[j].z;
+            pdw[j].w += dv.w * xh[j].w;
+            pdb[j].x += dv.x;
+            pdb[j].y += dv.y;
+            pdb[j].z += dv.z;
+            pdb[j].w += dv.w;
+        }
+        const float mg = wave_sum(sg) / (float)C;
+        const float mgx = wave_sum(sgx) / (float)C;
+        float4* o = reinterpret_cast<float4*>(dx + (long)row * C);
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            const int i = lane + 64 * j;
+            if (i < C4) {
+                float4 d;
+                d.x = r * (g[j].x - mg - xh[j].x * mgx);
+                d.y = r * (g[j].y - mg - xh[j].y * mgx);
+                d.z = r * (g[j].z - mg - xh[j].z * mgx);
+                d.w = r * (g[j].w - mg - xh[j].w * mgx);
+                if (accumulate) {
+                    const float4 old = o[i];
+                    d.x += old.x;
+                    d.y += old.y;
+                    d.z += old.z;
+                    d.w += old.w;
+                }
+                o[i] = d;
+            }
+        }
+    }
+    // Combine the 4 waves' partials in wave order, then write the block's partial row.
+    for (int part = 0; part < 2; part++) {
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            const int i = lane + 64 * j;
+            if (i < C4) reinterpret_cast<float4*>(red + wave * C)[i] = part == 0 ? pdw[j] : pdb[j];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < C; c += blockDim.x) {
+            const float s = ((red[c] + red[C + c]) + red[2 * C + c]) + red[3 * C + c];
+            partial[(long)blockIdx.x * 2 * C + part * C + c] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// out[w] (+)= sum_r part[r*W + w] over R rows, added in row order within 4 interleaved
+// groups that are then added in group order.  Columns w < W1 go to out_lo[w], the rest
+// to out_hi[w - W1].  Block: 64 columns x 4 groups.
+__global__ __launch_bounds__(256) void reduce_rows_kernel(float* out_lo, float* out_hi, int W1,
+                                                          const float* __restrict__ part, int R, int W,
+                                                          int accumulate) {
+    __shared__ float s[4][64];
+    const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
+    const int wcol = blockIdx.x * 64 + cl;
+    float acc = 0.f;
+    if (wcol < W)
+        for (int r = grp; r < R; r += 4) acc += part[(long)r * W + wcol];
+    s[grp][cl] = acc;
+    __syncthreads();
+    if (grp == 0 && wcol < W) {
+        const float tot = ((s[0][cl] + s[1][cl]) + s[2][cl]) + s[3][cl];
+        float* dst = wcol < W1 ? out_lo + wcol : out_hi + (wcol - W1);
+        *dst = accumulate ? *dst + tot : tot;
+    }
+}
+
+// part[chunk][n] = sum over the chunk's rows of x[m][n]; 4 columns per thread.
+__global__ __launch_bounds__(256) void colsum_partial_kernel(float* __restrict__ part, const float* __restrict__ x,
+                                                             long ld, int M, int N) {
+    const int c4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c4 * 4 >= N) return;
+    const int r0 = blockIdx.y * COLSUM_ROWS;
+    const int r1 = min(M, r0 + COLSUM_ROWS);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = r0; r < r1; r++) {
+        const float4 v = *reinterpret_cast<const float4*>(x + (long)r * ld + c4 * 4);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(part + (long)blockIdx.y * N + c4 * 4) = acc;
+}
+
+int ln_blocks(int N) { return std::min((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, LN_MAX_BLOCKS); }
+
+int colsum_chunks(int M) { return (M + COLSUM_ROWS - 1) / COLSUM_ROWS; }
+
+}  // namespace
+
+hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,
+                             const float* b, int N, int C, float eps, hipStream_t st) {
+    if (C % 4 || C > 4096 || N < 0) return hipErrorInvalidValue;
+    if (N == 0) return hipSuccess;
+    const int vpl = (C / 4 + 63) / 64;
+    dim3 grid((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), block(256);
+#define LN_FWD(V) hipLaunchKernelGGL(ln_fwd_kernel<V>, grid, block, 0, st, y, mean, rstd, x, w, b, N, C, eps)
+    switch (vpl) {
+        case 1: LN_FWD(1); break;
+        case 2: LN_FWD(2); break;
+        case 3: LN_FWD(3); break;
+        case 4: LN_FWD(4); break;
+        case 5: case 6: case 7: case 8: LN_FWD(8); break;
+        default: LN_FWD(16); break;
+    }
+#undef LN_FWD
+    return hipGetLastError();
+}
+
+size_t layernorm_partial_floats(int N, int C) { return (size_t)ln_blocks(N) * 2 * C; }
+
+hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x,
+                              const float* w, const float* mean, const float* rstd, int N, int C,
+                              bool accumulate_dx, bool accumulate_dwdb, float* partial,
+                              hipStream_t st) {
+    if (C % 4 || C > 4096 || N < 0) return hipErrorInvalidValue;
+    if (N == 0) {
+        if (!accumulate_dwdb) {
+            hipError_t e = fill_zero(dw, C, st);
+            if (e != hipSuccess) return e;
+            return fill_zero(db, C, st);
+        }
+        return hipSuccess;
+    }
+    const int vpl = (C / 4 + 63) / 64;
+    const int G = ln_blocks(N);
+    const size_t lds = (size_t)4 * C * sizeof(float);
+#define LN_BWD(V) hipLaunchKernelGGL(ln_bwd_kernel<V>, dim3(G), dim3(256), lds, st, dx, partial, dy, x, w, mean, rstd, N, C, (int)accumulate_dx)
+    switch (vpl) {
+        case 1: LN_BWD(1); break;
+        case 2: LN_BWD(2); break;
+        case 3: LN_BWD(3); break;
+        case 4: LN_BWD(4); break;
+        case 5: case 6: case 7: case 8: LN_BWD(8); break;
+        default: LN_BWD(16); break;
+    }
+#undef LN_BWD
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_rows_kernel, dim3((2 * C + 63) / 64), dim3(256), 0, st, dw, db, C,
+                       (const float*)partial, G, 2 * C, (int)accumulate_dwdb);
+    return hipGetLastError();
+}
+
+size_t colsum_partial_floats(int M, int N) { return (size_t)colsum_chunks(M) * N; }
+
+hipError_t colsum_accumulate(float* db, const float* x, long ld, int M, int N, float* partial,
+                             hipStream_t st) {
+    if (N % 4 || ld % 4 || M <= 0) return M == 0 ? hipSuccess : hipErrorInvalidValue;
+    const int chunks = colsum_chunks(M);
+    dim3 grid((N / 4 + 255) / 256, chunks);
+    hipLaunchKernelGGL(colsum_partial_kernel, grid, dim3(256), 0, st, partial, x, ld, M, N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_rows_kernel, dim3((N + 63) / 64), dim3(256), 0, st, db, db, N,
+                       (const float*)partial, chunks, N, 1);
+    return hipGetLastError();
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,232 @@
+"""Thin ctypes binding of libgpt2_mi355x.so (include/gpt2.h).
+
+Argument marshalling only: torch provides device memory and the current HIP stream,
+every step of the computation runs in the library's kernels.  There is no fallback: if
+the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import re
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgpt2_mi355x.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gpt2.h")
+
+GPT2_OK, GPT2_EINVAL, GPT2_ESTATE, GPT2_EDEVICE, GPT2_ENOMEM = 0, -1, -2, -3, -4
+PARAM_NAMES = ("wte", "wpe", "ln1w", "ln1b", "qkvw", "qkvb", "attprojw", "attprojb",
+               "ln2w", "ln2b", "fcw", "fcb", "fcprojw", "fcprojb", "lnfw", "lnfb")
+ACT_NAMES = ("encoded", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "att_lse", "residual2",
+             "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "residual3", "lnf", "lnf_mean",
+             "lnf_rstd", "probs", "losses")
+
+
+class Config(ct.Structure):
+    _fields_ = [("max_seq_len", ct.c_int), ("vocab_size", ct.c_int), ("num_layers", ct.c_int),
+                ("num_heads", ct.c_int), ("channels", ct.c_int)]
+
+
+class Buffers(ct.Structure):
+    _fields_ = [(n, ct.c_void_p) for n in ("params", "grads", "m", "v", "acts", "grad_scratch")]
+
+
+class GPT2Error(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+_LIB = None
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/gpt2.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(gpt2_[a-z_0-9]+)\s*\(", text)
+
+
+def load() -> ct.CDLL:
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run scratch_transformer_lm_amd/build.py "
+                           "(there is no CPU fallback)")
+    lib = ct.CDLL(LIB_PATH)
+    P, sz, i, f = ct.c_void_p, ct.c_size_t, ct.c_int, ct.c_float
+    C = ct.POINTER(Config)
+    lib.gpt2_num_parameters.argtypes = [C]
+    lib.gpt2_num_parameters.restype = sz
+    lib.gpt2_param_layout.argtypes = [C, P, P]
+    lib.gpt2_param_layout.restype = i
+    lib.gpt2_arena_sizes.argtypes = [C, i, i, ct.POINTER(sz), ct.POINTER(sz)]
+    lib.gpt2_arena_sizes.restype = i
+    lib.gpt2_build.argtypes = [ct.POINTER(P), C, i, i, ct.POINTER(Buffers), P]
+    lib.gpt2_build.restype = i
+    lib.gpt2_forward.argtypes = [P, P, P, i, i]
+    lib.gpt2_forward.restype = f
+    lib.gpt2_zero_grad.argtypes = [P]
+    lib.gpt2_zero_grad.restype = i
+    lib.gpt2_backward.argtypes = [P]
+    lib.gpt2_backward.restype = i
+    lib.gpt2_update.argtypes = [P, f, f, f, f, f, i]
+    lib.gpt2_update.restype = i
+    lib.gpt2_last_error.argtypes = [P]
+    lib.gpt2_last_error.restype = i
+    lib.gpt2_strerror.argtypes = [i]
+    lib.gpt2_strerror.restype = ct.c_char_p
+    lib.gpt2_free.argtypes = [P]
+    lib.gpt2_free.restype = None
+    lib.gpt2_activation_view.argtypes = [P, i, i] + [ct.POINTER(sz)] * 4
+    lib.gpt2_activation_view.restype = i
+    lib.gpt2_layernorm_forward.argtypes = [P, P, P, P, P, P, i, i, f, P]
+    lib.gpt2_layernorm_forward.restype = i
+    lib.gpt2_layernorm_backward_workspace.argtypes = [i, i]
+    lib.gpt2_layernorm_backward_workspace.restype = sz
+    lib.gpt2_layernorm_backward.argtypes = [P, P, P, P, P, P, P, P, i, i, P, sz, P]
+    lib.gpt2_layernorm_backward.restype = i
+    _LIB = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().gpt2_strerror(code).decode()
+
+
+def config(shape) -> Config:
+    return Config(shape.max_seq_len, shape.vocab_size, shape.num_layers, shape.num_heads,
+                  shape.channels)
+
+
+def num_parameters(shape) -> int:
+    c = config(shape)
+    return load().gpt2_num_parameters(ct.byref(c))
+
+
+def param_layout(shape):
+    c = config(shape)
+    off = np.zeros(16, np.uint64)
+    ln = np.zeros(16, np.uint64)
+    rc = load().gpt2_param_layout(ct.byref(c), off.ctypes.data, ln.ctypes.data)
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, "gpt2_param_layout")
+    return [int(x) for x in off], [int(x) for x in ln]
+
+
+def arena_sizes(shape, B: int, T: int):
+    c = config(shape)
+    a, s = ct.c_size_t(), ct.c_size_t()
+    rc = load().gpt2_arena_sizes(ct.byref(c), B, T, ct.byref(a), ct.byref(s))
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, "gpt2_arena_sizes")
+    return a.value, s.value
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class GPT2:
+    """One model: six torch device buffers and the library handle built over them."""
+
+    def __init__(self, shape, B: int, T: int, device="cuda", stream=None):
+        import torch
+        self.lib = load()
+        self.shape = shape
+        self.B, self.T = B, T
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        n = num_parameters(shape)
+        if n == 0:
+            raise GPT2Error(GPT2_EINVAL, "gpt2_num_parameters")
+        na, ns = arena_sizes(shape, B, T)
+        f32 = torch.float32
+        self.params = torch.empty(n, dtype=f32, device=self.device)
+        self.grads = torch.empty(n, dtype=f32, device=self.device)
+        self.m = torch.empty(n, dtype=f32, device=self.device)
+        self.v = torch.empty(n, dtype=f32, device=self.device)
+        self.acts = torch.empty(na, dtype=f32, device=self.device)
+        self.grad_scratch = torch.empty(ns, dtype=f32, device=self.device)
+        self.offsets, self.lengths = param_layout(shape)
+        bufs = Buffers(*(t.data_ptr() for t in (self.params, self.grads, self.m, self.v, self.acts,
+                                                  self.grad_scratch)))
+        h = ct.c_void_p()
+        cfg = config(shape)
+        rc = self.lib.gpt2_build(ct.byref(h), ct.byref(cfg), B, T, ct.byref(bufs),
+                                 _stream_ptr(self.stream))
+        if rc != GPT2_OK:
+            raise GPT2Error(rc, "gpt2_build")
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.gpt2_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- the five calls -------------------------------------------------------------
+    def forward(self, inputs, targets=None) -> float:
+        """inputs/targets: int32 device tensors (B, T)."""
+        B, T = inputs.shape
+        tp = targets.data_ptr() if targets is not None else None
+        return self.lib.gpt2_forward(self.h, inputs.data_ptr(), tp, B, T)
+
+    def zero_grad(self) -> int:
+        return self.lib.gpt2_zero_grad(self.h)
+
+    def backward(self) -> int:
+        return self.lib.gpt2_backward(self.h)
+
+    def update(self, lr, beta1, beta2, eps, weight_decay, t) -> int:
+        return self.lib.gpt2_update(self.h, lr, beta1, beta2, eps, weight_decay, t)
+
+    def last_error(self) -> int:
+        return self.lib.gpt2_last_error(self.h)
+
+    # -- views ------------------------------------------------------------------------
+    def tensor(self, buf, name: str):
+        i = PARAM_NAMES.index(name)
+        return buf[self.offsets[i]: self.offsets[i] + self.lengths[i]]
+
+    def activation(self, name: str, layer: int = 0):
+        """(rows, cols) view of an activation tensor (padding columns dropped)."""
+        vals = [ct.c_size_t() for _ in range(4)]
+        rc = self.lib.gpt2_activation_view(self.h, ACT_NAMES.index(name), layer,
+                                           *[ct.byref(v) for v in vals])
+        if rc != GPT2_OK:
+            raise GPT2Error(rc, "gpt2_activation_view")
+        off, rows, cols, ld = (v.value for v in vals)
+        return self.acts[off: off + rows * ld].view(rows, ld)[:, :cols]
+
+
+def layernorm_forward(y, mean, rstd, x, w, b, eps=1e-5, stream=None) -> None:
+    N, C = x.shape
+    rc = load().gpt2_layernorm_forward(y.data_ptr(), mean.data_ptr(), rstd.data_ptr(), x.data_ptr(),
+                                       w.data_ptr(), b.data_ptr(), N, C, eps, _stream_ptr(stream))
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, "gpt2_layernorm_forward")
+
+
+def layernorm_backward_workspace(N: int, C: int) -> int:
+    return load().gpt2_layernorm_backward_workspace(N, C)
+
+
+def layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, workspace, stream=None) -> None:
+    N, C = x.shape
+    rc = load().gpt2_layernorm_backward(dx.data_ptr(), dw.data_ptr(), db.data_ptr(), dy.data_ptr(),
+                                        x.data_ptr(), w.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
+                                        N, C, workspace.data_ptr(), workspace.numel(),
+                                        _stream_ptr(stream))
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, "gpt2_layernorm_backward")

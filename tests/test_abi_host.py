@@ -1,0 +1,78 @@
+"""Host-side checks of the HIP library (CPU only: no kernel runs).
+
+The library must load, export every function include/gpt2.h declares, and its host
+logic (parameter count and layout, arena sizes, argument checks) must agree with the
+closed form and with the oracle.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+import pytest
+
+from oracle import oracle as O
+from scratch_transformer_lm_amd import gpt2 as G
+from scratch_transformer_lm_amd import synthetic as S
+
+pytestmark = pytest.mark.skipif(not os.path.exists(G.LIB_PATH), reason="library not built")
+
+
+def test_every_declared_symbol_is_exported():
+    lib = G.load()
+    names = G.header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def closed_form(m):
+    V, C, L, T = m.vocab_size, m.channels, m.num_layers, m.max_seq_len
+    return V * C + T * C + L * (12 * C * C + 13 * C) + 2 * C
+
+
+@pytest.mark.parametrize("w", [S.TINY, S.GPT2_124M, S.GPT2_350M])
+def test_parameter_count_and_layout(w):
+    assert G.num_parameters(w.model) == closed_form(w.model) == O.num_parameters(w.model)
+    assert G.param_layout(w.model) == O.param_layout(w.model)
+
+
+def test_printed_parameter_count():
+    assert G.num_parameters(S.GPT2_124M.model) == 124439808
+
+
+def test_bad_configs_rejected():
+    bad = [S.ModelShape(64, 512, 2, 3, 64),    # C not a multiple of NH
+           S.ModelShape(64, 512, 2, 1, 128),   # head size 128 unsupported
+           S.ModelShape(64, 512, 0, 4, 64),    # no layers
+           S.ModelShape(64, 512, 2, 2, 66)]    # C not a multiple of 4 (and head size 33)
+    for m in bad:
+        assert G.num_parameters(m) == 0
+        with pytest.raises(G.GPT2Error):
+            G.arena_sizes(m, 2, 32)
+
+
+def test_arena_sizes():
+    a, s = G.arena_sizes(S.TINY.model, 2, 32)
+    assert a > 0 and s > 0
+    a2, s2 = G.arena_sizes(S.TINY.model, 4, 32)
+    assert a2 > a and s2 >= s
+    with pytest.raises(G.GPT2Error):
+        G.arena_sizes(S.TINY.model, 1, 65)          # T > max_seq_len
+    a3, _ = G.arena_sizes(S.GPT2_124M.model, 8, 1024)
+    # no (B,NH,T,T) score tensors: far below the plain inventory at full context
+    assert a3 < O.num_activations(S.GPT2_124M.model, 8, 1024) / 2
+
+
+def test_build_argument_checks_need_no_gpu():
+    lib = G.load()
+    cfg = G.config(S.TINY.model)
+    h = ct.c_void_p()
+    bufs = G.Buffers()
+    assert lib.gpt2_build(ct.byref(h), ct.byref(cfg), 2, 32, ct.byref(bufs), None) == G.GPT2_EINVAL
+    assert lib.gpt2_build(None, ct.byref(cfg), 2, 32, ct.byref(bufs), None) == G.GPT2_EINVAL
+    assert lib.gpt2_forward(None, None, None, 1, 1) != lib.gpt2_forward(None, None, None, 1, 1)  # NaN
+    assert lib.gpt2_backward(None) == G.GPT2_EINVAL
+    assert lib.gpt2_layernorm_forward(None, None, None, None, None, None, 4, 8, 1e-5, None) == G.GPT2_EINVAL
+    assert lib.gpt2_layernorm_backward_workspace(8192, 768) >= 2 * 768
+    assert G.strerror(G.GPT2_ESTATE) == "call out of order"

@@ -431,3 +431,20 @@ def test_abi_errors_and_accumulation():
     np.testing.assert_allclose(m.grads, 2 * g1, rtol=0, atol=1e-12 * np.abs(g1).max())
     with pytest.raises(ValueError):
         O.OracleGPT2(S.ModelShape(64, 512, 2, 3, 64), 2, 32, np.zeros(10))
+
+
+def test_key_bias_gradient_vanishes():
+    """Softmax ignores a constant added to one query's scores, and a key bias adds q.b_k
+    to all of them: its gradient is zero in exact arithmetic (a pin of the attention
+    backward, and the reason AdamW parity on that slice is limited by rounding noise)."""
+    w = S.TINY
+    p = S.init_params(w.model)
+    x, y = S.tokens(w)
+    m = O.OracleGPT2(w.model, w.B, w.T, p)
+    m.forward(x, y)
+    m.zero_grad()
+    m.backward()
+    C, L = w.model.channels, w.model.num_layers
+    g = m.tensor(m.grads, "qkvb").reshape(L, 3, C)
+    assert np.abs(g[:, 1]).max() <= 1e-15 * np.abs(g).max()
+    assert np.abs(g[:, 0]).max() > 1e-6 and np.abs(g[:, 2]).max() > 1e-6
