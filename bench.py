@@ -39,6 +39,41 @@ def step_flops(m: S.ModelShape, B: int, T: int) -> float:
     return 3.0 * (linear + attn)
 
 
+def roofline(kernels):
+    """Roofline position of the kernel with the largest total time: its algorithmic work
+    per launch over its average launch duration, against the MI355X peak of its bound
+    (fp32 matrix cores for kernels that count flops, HBM otherwise)."""
+    k = max(kernels, key=lambda e: e["ms"])
+    avg_s = k["ms"] / k["launches"] / 1e3
+    if k["flops"] > 0:
+        achieved = k["flops"] / k["launches"] / avg_s / 1e12
+        r = dict(bound="mfma", achieved=achieved, peak=PEAK_FP32_MFMA / 1e12, unit="TFLOP/s")
+    else:
+        achieved = k["bytes"] / k["launches"] / avg_s / 1e9
+        r = dict(bound="hbm", achieved=achieved, peak=PEAK_HBM / 1e9, unit="GB/s")
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = None
+    r["kernel"] = k["name"]
+    r["launches"] = k["launches"]
+    r["avg_launch_us"] = avg_s * 1e6
+    return r
+
+
+def breakdown(kernels, steps):
+    out = []
+    for k in sorted(kernels, key=lambda e: -e["ms"]):
+        avg_s = k["ms"] / k["launches"] / 1e3
+        e = dict(name=k["name"], ms_per_step=k["ms"] / steps, launches_per_step=k["launches"] / steps)
+        if k["flops"] > 0:
+            e["tflops"] = k["flops"] / k["launches"] / avg_s / 1e12
+            e["frac_mfma"] = e["tflops"] * 1e12 / PEAK_FP32_MFMA
+        else:
+            e["gbps"] = k["bytes"] / k["launches"] / avg_s / 1e9
+            e["frac_hbm"] = e["gbps"] * 1e9 / PEAK_HBM
+        out.append(e)
+    return out
+
+
 def cpu_baseline(w: S.Workload, rows: int = 1):
     """The oracle (float64, as it stands) on a bounded sample: `rows` sequences of the
     workload, one full step (forward, zero_grad, backward, AdamW)."""
@@ -95,15 +130,33 @@ def main():
         model.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
         return loss
 
-    for _ in range(args.warmup):
+    # Warm-up; all but the first warm-up step carry events around every kernel, which
+    # gives the per-kernel breakdown and names the kernel that takes the most time.
+    step()
+    model.profile_enable(True)
+    for _ in range(max(1, args.warmup - 1)):
         step()
     torch.cuda.synchronize()
-    prof = model.profile_enable(True) if hasattr(model, "profile_enable") else False
+    all_kernels = model.profile_entries()
+    dominant = max(all_kernels, key=lambda e: e["ms"])["name"]
+    # The timed region: K steps, with HIP events on the library's stream around each
+    # launch of the dominant kernel only.
+    model.profile_enable(True)
+    model.profile_filter(dominant)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     losses = [step() for _ in range(args.steps)]
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    kernels = model.profile_entries()
+    model.profile_enable(False)
+    # The same K steps without any events, to show what the events cost.
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt_plain = time.perf_counter() - t1
     if model.last_error() != 0 or not all(np.isfinite(losses)):
         print(f"bench: step failed: {G.strerror(model.last_error())}, losses {losses}", file=sys.stderr)
         sys.exit(1)
@@ -132,8 +185,9 @@ def main():
         "step_roofline_frac": flops / PEAK_FP32_MFMA / (dt / args.steps),
         "loss_first_last": [losses[0], losses[-1]],
     }
-    if prof:
-        out["roofline"], out["kernels"] = model.profile_report(args.steps)
+    out["ms_per_step_without_events"] = dt_plain * 1e3 / args.steps
+    out["roofline"] = roofline(kernels)
+    out["kernels"] = breakdown(all_kernels, max(1, args.warmup - 1))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -156,6 +156,22 @@ enum {
 int gpt2_activation_view(const gpt2* model, int tensor, int layer, size_t* offset, size_t* rows,
                          size_t* cols, size_t* ld);
 
+/* Per-kernel timing (profiling aid; the pages only print whole-step times).
+ * gpt2_profile_enable(model, 1) synchronises the stream and creates a pool of HIP
+ * events (outside any step); from then on every kernel launch of the model records an
+ * event pair around itself on the model's stream, with that launch's algorithmic work.
+ * Enabling again clears the records; enable = 0 releases the pool.  gpt2_profile_collect
+ * waits for the recorded events and returns the number of distinct kernels seen (< 0 on
+ * error); gpt2_profile_entry(i) then gives kernel i's name (valid until the next
+ * enable or free), launch count, summed duration in ms, and summed algorithmic flops
+ * and bytes.  gpt2_profile_filter(model, name) limits recording to the kernel of that
+ * name (NULL: all kernels), so that a timed run carries events around one kernel only. */
+int gpt2_profile_enable(gpt2* model, int enable);
+int gpt2_profile_filter(gpt2* model, const char* kernel_name);
+int gpt2_profile_collect(gpt2* model);
+int gpt2_profile_entry(gpt2* model, int i, const char** name, long* launches, double* total_ms,
+                       double* flops, double* bytes);
+
 /* Standalone LayerNorm forward, overwrite semantics (the pages' worked layer: dakule
  * page 手动实现每个层前向 / 反向传播; 新智元 page 教程).  Device pointers: x, y (N,C);
  * w, b (C); mean, rstd (N).  y = (x - mean) * rstd * w + b with biased variance and

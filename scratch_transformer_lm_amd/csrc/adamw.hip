@@ -5,6 +5,7 @@
 // (28 bytes per parameter), float4-wide with a grid-stride loop sized to the chip.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace gpt2k {
 
@@ -61,12 +62,14 @@ unsigned grid_for(size_t n4) {
 hipError_t adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float b1,
                  float b2, float eps, float wd, float bc1, float bc2, hipStream_t st) {
     if (n == 0) return hipSuccess;
+    ProfScope ps(st, "adamw_kernel", 0.0, 28.0 * (double)n);
     hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n / 4 + 1)), dim3(256), 0, st, p, g, m, v, n, lr, b1, b2, eps, wd, bc1, bc2);
     return hipGetLastError();
 }
 
 hipError_t fill_zero(float* x, size_t n, hipStream_t st) {
     if (n == 0) return hipSuccess;
+    ProfScope ps(st, "zero_kernel", 0.0, 4.0 * (double)n);
     hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n / 4 + 1)), dim3(256), 0, st, x, n);
     return hipGetLastError();
 }

@@ -10,6 +10,7 @@
 // therefore bitwise reproducible.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace gpt2k {
 
@@ -144,6 +145,7 @@ hipError_t encoder_forward(float* out, const int32_t* tok, const float* wte, con
     const int BT = B * T;
     if (C % 4) return hipErrorInvalidValue;
     if (BT == 0) return hipSuccess;
+    ProfScope ps(st, "encoder_fwd_kernel", 0.0, 4.0 * ((double)BT * C * 3 + BT));
     hipLaunchKernelGGL(encoder_fwd_kernel, dim3((BT + 3) / 4), dim3(256), 0, st, out, tok, wte, wpe, BT, T, C, V, flags);
     return hipGetLastError();
 }
@@ -155,9 +157,17 @@ hipError_t encoder_backward_ws(float* dwte, float* dwpe, const float* dout, cons
     if (C % 4 || C > 4096) return hipErrorInvalidValue;
     if (BT == 0) return hipSuccess;
     const long n = (long)T * (C / 4);
-    hipLaunchKernelGGL(wpe_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dwpe, dout, B, T, C);
+    {
+        ProfScope ps(st, "wpe_bwd_kernel", 0.0, 4.0 * ((double)BT * C + 2.0 * T * C));
+        hipLaunchKernelGGL(wpe_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dwpe, dout, B, T, C);
+    }
     hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, st, work);
-    hipLaunchKernelGGL(first_occurrence_kernel, dim3((BT + 255) / 256), dim3(256), 0, st, work, tok, BT);
+    {
+        ProfScope ps(st, "first_occurrence_kernel", 0.0, 4.0 * BT);
+        hipLaunchKernelGGL(first_occurrence_kernel, dim3((BT + 255) / 256), dim3(256), 0, st, work, tok, BT);
+    }
+    // rows of dout read once; each touched wte row read and written once (at most BT rows)
+    ProfScope ps(st, "wte_bwd_kernel", 0.0, 4.0 * ((double)BT * C + BT));
     hipLaunchKernelGGL(wte_bwd_kernel, dim3(BT), dim3(256), 0, st, dwte, dout, tok, (const int*)work, BT, C);
     return hipGetLastError();
 }

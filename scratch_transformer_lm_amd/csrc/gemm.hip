@@ -16,12 +16,23 @@
 // conflicts.  Inside a group of 8 k values each lane takes 4 consecutive k for its
 // half-wave (k = 8g + 4h + s for MFMA step s), so a k-contiguous fragment is one
 // 16-byte LDS read; the sum over k is the same sum in another order.
-// Blocks are renumbered so that each XCD (blocks are dealt round-robin to the 8 XCDs)
-// gets a contiguous range of tiles, grouped 8 tile-rows at a time for L2 reuse.
-// Split-K writes per-split partial tiles that a second kernel adds in split order, so
-// results never depend on timing.
+//
+// Work distribution is stream-K: with two 74 KB blocks resident per CU the chip holds
+// 512 blocks, and the many shapes here with a few hundred 128x128 tiles would leave
+// most of a second round idle.  So a persistent grid of up to 512 blocks splits the
+// (tile, k-tile) iteration space into equal contiguous ranges.  A block finishes whole
+// tiles with the fused epilogue; a tile shared by several blocks is left as partial
+// accumulators (in fragment order, fully coalesced) that a fix-up kernel adds in k order
+// before running the same epilogue, so the result never depends on timing.  Logical
+// block ids are laid out so that each XCD (blocks are dealt round-robin to the 8 XCDs)
+// owns a contiguous iteration range, and tiles are ordered 8 tile-rows at a time, which
+// keeps neighbouring blocks on the same operand panels in one L2.  Shapes with many
+// tiles use the same kernel with one tile per block.
+#include <string>
+
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace gpt2k {
 
@@ -31,10 +42,12 @@ constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
 constexpr int LDK = BK + 4;   // row stride of a k-contiguous LDS tile [row][k]
 constexpr int LDR = BM + 8;   // row stride of a row-contiguous LDS tile [k][row]
 constexpr int GROUP_M = 8;
+constexpr int RESIDENT = 512;              // blocks the chip holds at once (2 per CU)
+constexpr int TILE_FLOATS = BM * BN;       // one partial tile
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-enum Epi { EPI_STORE = 0, EPI_BIAS, EPI_BIAS_RESID, EPI_BIAS_GELU, EPI_ACCUM, EPI_GELU_BWD, EPI_PARTIAL };
+enum Epi { EPI_STORE = 0, EPI_BIAS, EPI_BIAS_RESID, EPI_BIAS_GELU, EPI_ACCUM, EPI_GELU_BWD };
 
 struct Params {
     int M, N, K;
@@ -49,10 +62,31 @@ struct Params {
     long ldaux;
     float* pre;         // pre-GELU output (EPI_BIAS_GELU)
     long ldpre;
-    float* partial;     // split-K partial tiles, [split][M][N]
-    int k_split;        // k extent of one split (multiple of BK)
-    int tiles_m, tiles_n, splits;
+    float* partial;     // 2 partial tiles per block
+    int tiles_m, tiles_n, nk;
+    long total;         // tiles * nk iterations
+    int G;              // persistent blocks
 };
+
+GPT2_DEV long range_start(long total, int G, int lb) { return (long)lb * total / G; }
+
+// Block (logical id) whose iteration range contains iteration x.
+GPT2_DEV int owner(long total, int G, long x) {
+    int lb = (int)(x * G / total);
+    while (lb + 1 < G && range_start(total, G, lb + 1) <= x) lb++;
+    while (lb > 0 && range_start(total, G, lb) > x) lb--;
+    return lb;
+}
+
+GPT2_DEV void tile_coords(const Params& p, int tile, int& m0, int& n0) {
+    const int group_size = GROUP_M * p.tiles_n;
+    const int group = tile / group_size;
+    const int first_m = group * GROUP_M;
+    const int gm = min(p.tiles_m - first_m, GROUP_M);
+    const int in_group = tile - group * group_size;
+    m0 = (first_m + in_group % gm) * BM;
+    n0 = (in_group / gm) * BN;
+}
 
 // Loads the 128 x 32 slab of an operand whose rows (m or n index) have k contiguous:
 // element (r, k) at X[r*ld + k].  Thread t covers rows t/8 + 32j, k = 4*(t%8)..+3.
@@ -135,6 +169,60 @@ GPT2_DEV void read_frag(float (&f)[4], const float* S, int rb, int g) {
     }
 }
 
+// Fused epilogue on one finished 32x32 block (a, b) of this thread's wave.  32x32
+// accumulator layout: lane holds column lane%32 and, in register v, row
+// 8*(v/4) + 4*(lane/32) + v%4.
+template <int EPI>
+GPT2_DEV void epilogue_block(const Params& p, const f32x16& acc, int m0, int n0, int a, int b) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int col = n0 + wn + 32 * b + (lane & 31), half = lane >> 5;
+    if (col >= p.N) return;
+    float bias_v = 0.f;
+    if (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) bias_v = p.bias ? p.bias[col] : 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+        const int row = m0 + wm + 32 * a + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (row >= p.M) continue;
+        const float x = acc[v];
+        float* c = p.C + (long)row * p.ldc + col;
+        if (EPI == EPI_STORE) {
+            *c = x;
+        } else if (EPI == EPI_BIAS) {
+            *c = x + bias_v;
+        } else if (EPI == EPI_BIAS_RESID) {
+            *c = p.aux[(long)row * p.ldaux + col] + (x + bias_v);
+        } else if (EPI == EPI_BIAS_GELU) {
+            const float u = x + bias_v;
+            p.pre[(long)row * p.ldpre + col] = u;
+            *c = gelu_f(u);
+        } else if (EPI == EPI_ACCUM) {
+            *c += x;
+        } else {  // EPI_GELU_BWD
+            *c = x * gelu_grad_f(p.aux[(long)row * p.ldaux + col]);
+        }
+    }
+}
+
+template <int EPI>
+GPT2_DEV void epilogue(const Params& p, const f32x16 (&acc)[2][2], int m0, int n0) {
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++) epilogue_block<EPI>(p, acc[a][b], m0, n0, a, b);
+}
+
+// Partial tile in fragment order: thread t's 64 accumulators at slot[(j*256 + t)].
+GPT2_DEV void store_partial(float* slot, const f32x16 (&acc)[2][2]) {
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) slot[((a * 2 + b) * 16 + v) * NT + threadIdx.x] = acc[a][b][v];
+}
+
+
 template <bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     constexpr int A_STAGE = A_K ? BM * LDK : BK * LDR;
@@ -143,163 +231,162 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     float* As = smem;
     float* Bs = smem + 2 * A_STAGE;
 
-    // XCD-aware renumbering, then grouped tile order.
+    // XCD-aware logical block id: XCD x (= blockIdx % 8) gets a contiguous id range.
     const int nb = gridDim.x;
     const int bid = blockIdx.x;
     const int xcd = bid & 7, local = bid >> 3;
-    const int q = nb >> 3, r = nb & 7;
-    const int lin = xcd * q + min(xcd, r) + local;
-    const int per_split = p.tiles_m * p.tiles_n;
-    const int split = lin / per_split;
-    const int tile = lin - split * per_split;
-    const int group_size = GROUP_M * p.tiles_n;
-    const int group = tile / group_size;
-    const int first_m = group * GROUP_M;
-    const int gm = min(p.tiles_m - first_m, GROUP_M);
-    const int in_group = tile - group * group_size;
-    const int tm = first_m + in_group % gm;
-    const int tn = in_group / gm;
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const int k_begin = split * p.k_split;
-    const int k_end = min(p.K, k_begin + p.k_split);
-    const int nk = (k_end - k_begin + BK - 1) / BK;
+    const int lb = xcd * (nb >> 3) + min(xcd, nb & 7) + local;
+    const long it_begin = range_start(p.total, p.G, lb);
+    const long it_end = range_start(p.total, p.G, lb + 1);
 
     const int wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) acc[a][b][e] = 0.f;
-
     float4 ra[4], rb[4];
-    auto load = [&](int k0) {
-        if (A_K) load_kcontig(ra, p.A, p.lda, m0, p.M, k0, k_end);
-        else load_rcontig(ra, p.A, p.lda, m0, p.M, k0, k_end);
-        if (B_K) load_kcontig(rb, p.B, p.ldb, n0, p.N, k0, k_end);
-        else load_rcontig(rb, p.B, p.ldb, n0, p.N, k0, k_end);
-    };
-    auto store = [&](int stage) {
-        if (A_K) store_kcontig(As + stage * A_STAGE, ra);
-        else store_rcontig(As + stage * A_STAGE, ra);
-        if (B_K) store_kcontig(Bs + stage * B_STAGE, rb);
-        else store_rcontig(Bs + stage * B_STAGE, rb);
-    };
 
-    if (nk > 0) {
-        load(k_begin);
+    for (long it = it_begin; it < it_end;) {
+        const int tile = (int)(it / p.nk);
+        const int ks = (int)(it - (long)tile * p.nk);
+        const int ke = (int)min((long)p.nk, ks + (it_end - it));
+        int m0, n0;
+        tile_coords(p, tile, m0, n0);
+        const int k_end = min(p.K, ke * BK);
+
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int b = 0; b < 2; b++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) acc[a][b][e] = 0.f;
+
+        auto load = [&](int k0) {
+            if (A_K) load_kcontig(ra, p.A, p.lda, m0, p.M, k0, k_end);
+            else load_rcontig(ra, p.A, p.lda, m0, p.M, k0, k_end);
+            if (B_K) load_kcontig(rb, p.B, p.ldb, n0, p.N, k0, k_end);
+            else load_rcontig(rb, p.B, p.ldb, n0, p.N, k0, k_end);
+        };
+        auto store = [&](int stage) {
+            if (A_K) store_kcontig(As + stage * A_STAGE, ra);
+            else store_rcontig(As + stage * A_STAGE, ra);
+            if (B_K) store_kcontig(Bs + stage * B_STAGE, rb);
+            else store_rcontig(Bs + stage * B_STAGE, rb);
+        };
+
+        load(ks * BK);
         store(0);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load(k_begin + (kt + 1) * BK);
-        const float* Acur = As + cur * A_STAGE;
-        const float* Bcur = Bs + cur * B_STAGE;
-#pragma unroll
-        for (int g = 0; g < BK / 8; g++) {
-            float fa[2][4], fb[2][4];
-            read_frag<A_K>(fa[0], Acur, wm, g);
-            read_frag<A_K>(fa[1], Acur, wm + 32, g);
-            read_frag<B_K>(fb[0], Bcur, wn, g);
-            read_frag<B_K>(fb[1], Bcur, wn + 32, g);
-#pragma unroll
-            for (int s = 0; s < 4; s++)
-#pragma unroll
-                for (int a = 0; a < 2; a++)
-#pragma unroll
-                    for (int b = 0; b < 2; b++)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
-        }
-        if (kt + 1 < nk) store(cur ^ 1);
         __syncthreads();
-    }
-
-    // Epilogue.  32x32 accumulator layout: lane holds column lane%32 and, in register
-    // v, row 8*(v/4) + 4*(lane/32) + v%4.
-    const int lane = threadIdx.x & 63;
-    const int col_in = lane & 31, half = lane >> 5;
+        const int n = ke - ks;
+        for (int kt = 0; kt < n; kt++) {
+            const int cur = kt & 1;
+            if (kt + 1 < n) load((ks + kt + 1) * BK);
+            const float* Acur = As + cur * A_STAGE;
+            const float* Bcur = Bs + cur * B_STAGE;
 #pragma unroll
-    for (int a = 0; a < 2; a++)
+            for (int g = 0; g < BK / 8; g++) {
+                float fa[2][4], fb[2][4];
+                read_frag<A_K>(fa[0], Acur, wm, g);
+                read_frag<A_K>(fa[1], Acur, wm + 32, g);
+                read_frag<B_K>(fb[0], Bcur, wn, g);
+                read_frag<B_K>(fb[1], Bcur, wn + 32, g);
 #pragma unroll
-        for (int b = 0; b < 2; b++) {
-            const int col = n0 + wn + 32 * b + col_in;
-            if (col >= p.N) continue;
-            float bias_v = 0.f;
-            if (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU)
-                bias_v = p.bias ? p.bias[col] : 0.f;
+                for (int s = 0; s < 4; s++)
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int row = m0 + wm + 32 * a + 8 * (v >> 2) + 4 * half + (v & 3);
-                if (row >= p.M) continue;
-                const float x = acc[a][b][v];
-                if (EPI == EPI_STORE) {
-                    p.C[(long)row * p.ldc + col] = x;
-                } else if (EPI == EPI_BIAS) {
-                    p.C[(long)row * p.ldc + col] = x + bias_v;
-                } else if (EPI == EPI_BIAS_RESID) {
-                    p.C[(long)row * p.ldc + col] = p.aux[(long)row * p.ldaux + col] + (x + bias_v);
-                } else if (EPI == EPI_BIAS_GELU) {
-                    const float u = x + bias_v;
-                    p.pre[(long)row * p.ldpre + col] = u;
-                    p.C[(long)row * p.ldc + col] = gelu_f(u);
-                } else if (EPI == EPI_ACCUM) {
-                    p.C[(long)row * p.ldc + col] += x;
-                } else if (EPI == EPI_GELU_BWD) {
-                    p.C[(long)row * p.ldc + col] = x * gelu_grad_f(p.aux[(long)row * p.ldaux + col]);
-                } else {  // EPI_PARTIAL
-                    p.partial[((long)split * p.M + row) * p.N + col] = x;
-                }
+                    for (int a = 0; a < 2; a++)
+#pragma unroll
+                        for (int b = 0; b < 2; b++)
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
             }
+            if (kt + 1 < n) store(cur ^ 1);
+            __syncthreads();
         }
+
+        if (ks == 0 && ke == p.nk) {
+            epilogue<EPI>(p, acc, m0, n0);
+        } else {
+            // first segment of the range -> slot 0, the range's last (shared) tile -> slot 1
+            const int which = it == it_begin ? 0 : 1;
+            store_partial(p.partial + ((long)lb * 2 + which) * TILE_FLOATS, acc);
+        }
+        it += ke - ks;
+    }
 }
 
-// C (+)= sum over splits of partial[s], splits added in order.  N % 4 == 0.
-__global__ void splitk_reduce_kernel(float* C, long ldc, const float* partial, int M, int N,
-                                     int splits, int accumulate) {
-    const long n4 = (long)M * N / 4;
-    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
-        const long e = i * 4;
-        const int row = (int)(e / N), col = (int)(e - (long)row * N);
-        float4 s = *reinterpret_cast<const float4*>(partial + e);
-        for (int k = 1; k < splits; k++) {
-            const float4 t = *reinterpret_cast<const float4*>(partial + (long)k * M * N + e);
-            s.x += t.x;
-            s.y += t.y;
-            s.z += t.z;
-            s.w += t.w;
-        }
-        float4* c = reinterpret_cast<float4*>(C + (long)row * ldc + col);
-        if (accumulate) {
-            const float4 o = *c;
-            s.x += o.x;
-            s.y += o.y;
-            s.z += o.z;
-            s.w += o.w;
-        }
-        *c = s;
+// Four blocks per range boundary that falls strictly inside a tile, one per 32x32
+// block (a, b) of the waves' sub-tiles; for the lowest such boundary of a tile they add
+// that tile's partials in k order and run the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
+    const int quarter = blockIdx.x & 3;
+    const int lbb = (blockIdx.x >> 2) + 1;  // boundary between blocks lbb-1 and lbb
+    const long x = range_start(p.total, p.G, lbb);
+    if (x % p.nk == 0) return;
+    const int tile = (int)(x / p.nk);
+    if (lbb >= 2) {
+        const long xp = range_start(p.total, p.G, lbb - 1);
+        if (xp / p.nk == tile && xp % p.nk != 0) return;
     }
+    const long t0 = (long)tile * p.nk;
+    const int first = owner(p.total, p.G, t0);
+    const int last = owner(p.total, p.G, t0 + p.nk - 1);
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; e++) acc[e] = 0.f;
+    for (int l = first; l <= last; l++) {
+        const int which = range_start(p.total, p.G, l) / p.nk == tile ? 0 : 1;
+        const float* slot = p.partial + ((long)l * 2 + which) * TILE_FLOATS + quarter * 16 * NT + threadIdx.x;
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; e++) v[e] = slot[e * NT];
+#pragma unroll
+        for (int e = 0; e < 16; e++) acc[e] += v[e];
+    }
+    int m0, n0;
+    tile_coords(p, tile, m0, n0);
+    epilogue_block<EPI>(p, acc, m0, n0, quarter >> 1, quarter & 1);
+}
+
+// Kernel name as profilers print the instantiation.
+template <bool A_K, bool B_K, int EPI>
+const char* gemm_name() {
+    static const std::string s = std::string("gemm_kernel<") + (A_K ? "true" : "false") + ", " +
+                                 (B_K ? "true" : "false") + ", " + std::to_string(EPI) + ">";
+    return s.c_str();
+}
+
+template <int EPI>
+const char* fixup_name() {
+    static const std::string s = "gemm_fixup_kernel<" + std::to_string(EPI) + ">";
+    return s.c_str();
 }
 
 template <bool A_K, bool B_K, int EPI>
 hipError_t launch(Params& p, hipStream_t st) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
-    if (p.splits < 1) p.splits = 1;
-    if (p.splits == 1) {
-        p.k_split = p.K;
-    } else {
-        int ks = (p.K + p.splits - 1) / p.splits;
-        p.k_split = (ks + BK - 1) / BK * BK;
-        p.splits = (p.K + p.k_split - 1) / p.k_split;
+    p.nk = (p.K + BK - 1) / BK;
+    const long tiles = (long)p.tiles_m * p.tiles_n;
+    if (tiles == 0) return hipSuccess;
+    if (p.nk == 0) {
+        // empty reduction: every output is the epilogue of 0
+        p.nk = 1;
     }
-    const long blocks = (long)p.tiles_m * p.tiles_n * p.splits;
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI>), dim3((unsigned)blocks), dim3(NT), 0, st, p);
+    p.total = tiles * p.nk;
+    // Many tiles: one tile per block.  Otherwise stream-K over the resident blocks.
+    const bool sk = tiles < 8L * RESIDENT && p.partial != nullptr;
+    p.G = sk ? (int)std::min<long>(RESIDENT, p.total) : (int)tiles;
+    const double mn = (double)p.M * p.N;
+    const double extra = (EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_BIAS_GELU) ? mn : 0.0;
+    {
+        // algorithmic work: 2MNK flops; operands read once, C written (and read for += / aux)
+        ProfScope ps(st, gemm_name<A_K, B_K, EPI>(), 2.0 * mn * p.K,
+                     4.0 * ((double)p.M * p.K + (double)p.N * p.K + mn + extra));
+        hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI>), dim3(p.G), dim3(NT), 0, st, p);
+    }
+    const bool aligned_ranges = p.total % p.G == 0 && (p.total / p.G) % p.nk == 0;
+    if (sk && !aligned_ranges && p.G > 1) {
+        ProfScope ps(st, fixup_name<EPI>(), 0.0, 4.0 * (2.0 * p.G * TILE_FLOATS + extra));
+        hipLaunchKernelGGL((gemm_fixup_kernel<EPI>), dim3(4 * (p.G - 1)), dim3(NT), 0, st, p);
+    }
     return hipGetLastError();
 }
 
@@ -307,9 +394,11 @@ bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
 
 }  // namespace
 
+size_t gemm_partial_floats() { return (size_t)RESIDENT * 2 * TILE_FLOATS; }
+
 hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
-                          hipStream_t st) {
+                          float* partial, hipStream_t st) {
     if (K % 4 || !aligned16(inp) || !aligned16(w)) return hipErrorInvalidValue;
     Params p{};
     p.M = M;
@@ -322,7 +411,7 @@ hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w
     p.C = out;
     p.ldc = ldo;
     p.bias = bias;
-    p.splits = 1;
+    p.partial = partial;
     if (pre) {
         p.pre = pre;
         p.ldpre = ldo;
@@ -338,8 +427,7 @@ hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w
 }
 
 hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float* w,
-                        const float* gelu_pre, int M, int N, int K, int splits, float* partial,
-                        hipStream_t st) {
+                        const float* gelu_pre, int M, int N, int K, float* partial, hipStream_t st) {
     if (ld_dout % 4 || N % 4 || !aligned16(dout) || !aligned16(w)) return hipErrorInvalidValue;
     Params p{};
     p.M = M;
@@ -351,28 +439,17 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
     p.ldb = N;
     p.C = din;
     p.ldc = N;
+    p.partial = partial;
     if (gelu_pre) {
         p.aux = gelu_pre;
         p.ldaux = N;
-        p.splits = 1;
         return launch<true, false, EPI_GELU_BWD>(p, st);
     }
-    if (splits > 1 && partial) {
-        p.partial = partial;
-        p.splits = splits;
-        hipError_t e = launch<true, false, EPI_PARTIAL>(p, st);
-        if (e != hipSuccess) return e;
-        const long n4 = (long)M * N / 4;
-        const int grid = (int)std::min<long>((n4 + 255) / 256, 4096);
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, st, din, (long)N, partial, M, N, p.splits, 0);
-        return hipGetLastError();
-    }
-    p.splits = 1;
     return launch<true, false, EPI_STORE>(p, st);
 }
 
 hipError_t linear_wgrad(float* dw, const float* dout, long ld_dout, const float* inp, int M, int N,
-                        int K, int splits, float* partial, hipStream_t st) {
+                        int K, float* partial, hipStream_t st) {
     if (ld_dout % 4 || N % 4 || !aligned16(dout) || !aligned16(inp)) return hipErrorInvalidValue;
     Params p{};
     p.M = M;
@@ -384,25 +461,8 @@ hipError_t linear_wgrad(float* dw, const float* dout, long ld_dout, const float*
     p.ldb = N;
     p.C = dw;
     p.ldc = N;
-    if (splits > 1 && partial) {
-        p.partial = partial;
-        p.splits = splits;
-        hipError_t e = launch<false, false, EPI_PARTIAL>(p, st);
-        if (e != hipSuccess) return e;
-        const long n4 = (long)M * N / 4;
-        const int grid = (int)std::min<long>((n4 + 255) / 256, 4096);
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, st, dw, (long)N, partial, M, N, p.splits, 1);
-        return hipGetLastError();
-    }
-    p.splits = 1;
+    p.partial = partial;
     return launch<false, false, EPI_ACCUM>(p, st);
-}
-
-int splitk_effective(int K, int splits) {
-    if (splits <= 1) return 1;
-    int ks = (K + splits - 1) / splits;
-    ks = (ks + BK - 1) / BK * BK;
-    return (K + ks - 1) / ks;
 }
 
 }  // namespace gpt2k

@@ -23,6 +23,7 @@
 #include "../../include/gpt2.h"
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 using namespace gpt2k;
 
@@ -67,11 +68,6 @@ struct Layout {
     // grad_scratch
     size_t dres, dln, datty, dqkv, dfch, delta, enc_work, partial, n_partial, n_scratch;
 };
-
-long split_budget(const gpt2_config* c, size_t BT) {
-    const size_t C = c->channels;
-    return (long)std::max<size_t>(8 * 4 * C * C, 2 * BT * C);
-}
 
 Layout make_layout(const gpt2_config* c, int B, int T) {
     Layout y{};
@@ -123,7 +119,7 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     y.dfch = take(BT * 4 * C);
     y.delta = take(BT * NH);
     y.enc_work = take(1 + BT);
-    size_t np = (size_t)split_budget(c, BT);
+    size_t np = gemm_partial_floats();
     np = std::max(np, layernorm_partial_floats((int)BT, (int)C));
     np = std::max(np, colsum_partial_floats((int)BT, (int)(4 * C)));
     y.n_partial = np;
@@ -131,19 +127,6 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     y.n_scratch = s;
     return y;
 }
-
-// Split-K count for a GEMM with `tiles` output tiles and reduction length K: enough
-// blocks to put two on every CU, at least 256 of K per split, within the partial budget.
-int choose_splits(long tiles, int K, long MN, long budget) {
-    if (tiles >= 512) return 1;
-    long s = (512 + tiles - 1) / tiles;
-    s = std::min<long>(s, std::max(1, K / 256));
-    s = std::min<long>(s, 32);
-    s = std::min<long>(s, std::max<long>(1, budget / std::max<long>(1, MN)));
-    return splitk_effective(K, (int)std::max<long>(1, s));
-}
-
-long tiles_of(long M, long N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
 }  // namespace
 
@@ -159,9 +142,16 @@ struct gpt2 {
     int* host_ret;  // pinned: [loss bits, flags]
     int last_error;
     bool have_forward, have_targets, probs_are_grads;
+    Profiler* prof;  // non-null while per-kernel timing is enabled
 };
 
 namespace {
+
+// Makes the handle's profiler (if any) visible to the launchers for one ABI call.
+struct ProfBind {
+    explicit ProfBind(gpt2* g) { g_prof = g ? g->prof : nullptr; }
+    ~ProfBind() { g_prof = nullptr; }
+};
 
 int fail(gpt2* g, int code) {
     if (g) g->last_error = code;
@@ -186,6 +176,7 @@ bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, int T, float* loss_out) {
     const gpt2_config& c = g->cfg;
+    float* part = S(g, g->lay.partial);
     const int C = c.channels, L = c.num_layers, NH = c.num_heads, V = c.vocab_size;
     const int BT = B * T;
     const long Vp = (long)g->lay.Vp;
@@ -203,20 +194,20 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
         HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LN1, l), A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l),
                                     residual, P(g, P_LN1W) + l * C, P(g, P_LN1B) + l * C, BT, C, 1e-5f, st));
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_QKV, l), 3 * C, A(g, GPT2_ACT_LN1, l), P(g, P_QKVW) + (size_t)l * 3 * C * C,
-                                 P(g, P_QKVB) + l * 3 * C, nullptr, nullptr, BT, 3 * C, C, st));
+                                 P(g, P_QKVB) + l * 3 * C, nullptr, nullptr, BT, 3 * C, C, part, st));
         HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T, C, NH, st));
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), P(g, P_ATTPROJW) + (size_t)l * C * C,
-                                 P(g, P_ATTPROJB) + l * C, residual, nullptr, BT, C, C, st));
+                                 P(g, P_ATTPROJB) + l * C, residual, nullptr, BT, C, C, part, st));
         HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LN2, l), A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l),
                                     A(g, GPT2_ACT_RESIDUAL2, l), P(g, P_LN2W) + l * C, P(g, P_LN2B) + l * C, BT, C, 1e-5f, st));
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_FCH_GELU, l), 4 * C, A(g, GPT2_ACT_LN2, l), P(g, P_FCW) + (size_t)l * 4 * C * C,
-                                 P(g, P_FCB) + l * 4 * C, nullptr, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C, st));
+                                 P(g, P_FCB) + l * 4 * C, nullptr, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C, part, st));
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_RESIDUAL3, l), C, A(g, GPT2_ACT_FCH_GELU, l), P(g, P_FCPROJW) + (size_t)l * 4 * C * C,
-                                 P(g, P_FCPROJB) + l * C, A(g, GPT2_ACT_RESIDUAL2, l), nullptr, BT, C, 4 * C, st));
+                                 P(g, P_FCPROJB) + l * C, A(g, GPT2_ACT_RESIDUAL2, l), nullptr, BT, C, 4 * C, part, st));
     }
     HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LNF), A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD),
                                 A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, 1e-5f, st));
-    HIPCHK(g, linear_forward(A(g, GPT2_ACT_PROBS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT, V, C, st));
+    HIPCHK(g, linear_forward(A(g, GPT2_ACT_PROBS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT, V, C, part, st));
     HIPCHK(g, softmax_xent_forward(A(g, GPT2_ACT_PROBS), Vp, A(g, GPT2_ACT_LOSSES), targets ? tok_tgt(g) : nullptr, BT, V,
                                    flags(g), st));
     if (targets) HIPCHK(g, loss_mean(g->buf.grad_scratch + HDR_LOSS, A(g, GPT2_ACT_LOSSES), BT, st));
@@ -236,7 +227,6 @@ int backward_impl(gpt2* g) {
     const int C = c.channels, L = c.num_layers, NH = c.num_heads, V = c.vocab_size;
     const int B = g->B, T = g->T, BT = B * T;
     const long Vp = (long)g->lay.Vp;
-    const long budget = (long)g->lay.n_partial;
     hipStream_t st = g->st;
     float* part = S(g, g->lay.partial);
     float* dres = S(g, g->lay.dres);
@@ -252,43 +242,37 @@ int backward_impl(gpt2* g) {
         g->probs_are_grads = true;
     }
     // LM head (tied): dlnf = dlogits . wte;  dwte += dlogits^T . lnf.
-    HIPCHK(g, linear_dgrad(dln, probs, Vp, P(g, P_WTE), nullptr, BT, C, V,
-                           choose_splits(tiles_of(BT, C), V, (long)BT * C, budget), part, st));
-    HIPCHK(g, linear_wgrad(G(g, P_WTE), probs, Vp, A(g, GPT2_ACT_LNF), V, C, BT,
-                           choose_splits(tiles_of(V, C), BT, (long)V * C, budget), part, st));
+    HIPCHK(g, linear_dgrad(dln, probs, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st));
+    HIPCHK(g, linear_wgrad(G(g, P_WTE), probs, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part, st));
     HIPCHK(g, layernorm_backward(dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
                                  A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
     for (int l = L - 1; l >= 0; l--) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         // MLP projection: residual3 = residual2 + gelu(fch) . Wp^T + bp.
         HIPCHK(g, linear_wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, dres, C, A(g, GPT2_ACT_FCH_GELU, l), C, 4 * C, BT,
-                               choose_splits(tiles_of(C, 4 * C), BT, 4L * C * C, budget), part, st));
+                               part, st));
         HIPCHK(g, colsum_accumulate(G(g, P_FCPROJB) + l * C, dres, C, BT, C, part, st));
         HIPCHK(g, linear_dgrad(dfch, dres, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C,
-                               1, part, st));
+                               part, st));
         // MLP expansion: fch = ln2 . Wf^T + bf.
         HIPCHK(g, linear_wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, dfch, 4 * C, A(g, GPT2_ACT_LN2, l), 4 * C, C, BT,
-                               choose_splits(tiles_of(4 * C, C), BT, 4L * C * C, budget), part, st));
+                               part, st));
         HIPCHK(g, colsum_accumulate(G(g, P_FCB) + l * 4 * C, dfch, 4 * C, BT, 4 * C, part, st));
-        HIPCHK(g, linear_dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, nullptr, BT, C, 4 * C,
-                               choose_splits(tiles_of(BT, C), 4 * C, (long)BT * C, budget), part, st));
+        HIPCHK(g, linear_dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, nullptr, BT, C, 4 * C, part, st));
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
                                      P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C,
                                      true, true, part, st));
         // Attention projection: residual2 = residual + atty . Wa^T + ba.
-        HIPCHK(g, linear_wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, dres, C, A(g, GPT2_ACT_ATTY, l), C, C, BT,
-                               choose_splits(tiles_of(C, C), BT, (long)C * C, budget), part, st));
+        HIPCHK(g, linear_wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, dres, C, A(g, GPT2_ACT_ATTY, l), C, C, BT, part, st));
         HIPCHK(g, colsum_accumulate(G(g, P_ATTPROJB) + l * C, dres, C, BT, C, part, st));
-        HIPCHK(g, linear_dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, nullptr, BT, C, C,
-                               choose_splits(tiles_of(BT, C), C, (long)BT * C, budget), part, st));
+        HIPCHK(g, linear_dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, nullptr, BT, C, C, part, st));
         HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
                                      A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
         HIPCHK(g, linear_wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, dqkv, 3 * C, A(g, GPT2_ACT_LN1, l), 3 * C, C, BT,
-                               choose_splits(tiles_of(3 * C, C), BT, 3L * C * C, budget), part, st));
+                               part, st));
         HIPCHK(g, colsum_accumulate(G(g, P_QKVB) + l * 3 * C, dqkv, 3 * C, BT, 3 * C, part, st));
-        HIPCHK(g, linear_dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, nullptr, BT, C, 3 * C,
-                               choose_splits(tiles_of(BT, C), 3 * C, (long)BT * C, budget), part, st));
+        HIPCHK(g, linear_dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, nullptr, BT, C, 3 * C, part, st));
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                                      A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
     }
@@ -358,7 +342,7 @@ int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buff
     }
     if (fill_zero(b.grads, g->nparams, g->st) != hipSuccess || fill_zero(b.m, g->nparams, g->st) != hipSuccess ||
         fill_zero(b.v, g->nparams, g->st) != hipSuccess) {
-        hipHostFree(g->host_ret);
+        (void)hipHostFree(g->host_ret);
         free(g);
         return GPT2_EDEVICE;
     }
@@ -374,6 +358,7 @@ float gpt2_forward(gpt2* g, const int32_t* inputs, const int32_t* targets, int B
         return NAN;
     }
     float loss = NAN;
+    ProfBind bind(g);
     const int rc = forward_impl(g, inputs, targets, B, T, &loss);
     if (rc != GPT2_OK) {
         g->last_error = rc;
@@ -385,6 +370,7 @@ float gpt2_forward(gpt2* g, const int32_t* inputs, const int32_t* targets, int B
 
 int gpt2_zero_grad(gpt2* g) {
     if (!g) return GPT2_EINVAL;
+    ProfBind bind(g);
     HIPCHK(g, fill_zero(g->buf.grads, g->nparams, g->st));
     return GPT2_OK;
 }
@@ -392,6 +378,7 @@ int gpt2_zero_grad(gpt2* g) {
 int gpt2_backward(gpt2* g) {
     if (!g) return GPT2_EINVAL;
     if (!g->have_forward || !g->have_targets) return fail(g, GPT2_ESTATE);
+    ProfBind bind(g);
     return backward_impl(g);
 }
 
@@ -400,6 +387,7 @@ int gpt2_update(gpt2* g, float lr, float beta1, float beta2, float eps, float we
     if (t < 1) return fail(g, GPT2_ESTATE);
     const float bc1 = (float)(1.0 - pow((double)beta1, (double)t));
     const float bc2 = (float)(1.0 - pow((double)beta2, (double)t));
+    ProfBind bind(g);
     HIPCHK(g, adamw(g->buf.params, g->buf.grads, g->buf.m, g->buf.v, g->nparams, lr, beta1, beta2, eps, weight_decay,
                     bc1, bc2, g->st));
     return GPT2_OK;
@@ -420,9 +408,43 @@ const char* gpt2_strerror(int code) {
 
 void gpt2_free(gpt2* g) {
     if (!g) return;
-    hipStreamSynchronize(g->st);
-    hipHostFree(g->host_ret);
+    (void)hipStreamSynchronize(g->st);
+    if (g->prof) prof_destroy(g->prof);
+    (void)hipHostFree(g->host_ret);
     free(g);
+}
+
+int gpt2_profile_enable(gpt2* g, int enable) {
+    if (!g) return GPT2_EINVAL;
+    if (hipStreamSynchronize(g->st) != hipSuccess) return fail(g, GPT2_EDEVICE);
+    if (enable && !g->prof) {
+        g->prof = prof_create();
+        if (!g->prof) return fail(g, GPT2_EDEVICE);
+    } else if (enable) {
+        prof_reset(g->prof);
+    } else if (g->prof) {
+        prof_destroy(g->prof);
+        g->prof = nullptr;
+    }
+    return GPT2_OK;
+}
+
+int gpt2_profile_filter(gpt2* g, const char* kernel_name) {
+    if (!g || !g->prof) return GPT2_ESTATE;
+    prof_filter(g->prof, kernel_name);
+    return GPT2_OK;
+}
+
+int gpt2_profile_collect(gpt2* g) {
+    if (!g || !g->prof) return GPT2_ESTATE;
+    const int n = prof_collect(g->prof);
+    return n < 0 ? fail(g, GPT2_EDEVICE) : n;
+}
+
+int gpt2_profile_entry(gpt2* g, int i, const char** name, long* launches, double* total_ms, double* flops,
+                       double* bytes) {
+    if (!g || !g->prof || !name || !launches || !total_ms || !flops || !bytes) return GPT2_EINVAL;
+    return prof_entry(g->prof, i, name, launches, total_ms, flops, bytes) == 0 ? GPT2_OK : GPT2_EINVAL;
 }
 
 int gpt2_activation_view(const gpt2* g, int tensor, int layer, size_t* offset, size_t* rows, size_t* cols,

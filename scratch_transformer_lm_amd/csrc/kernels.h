@@ -10,23 +10,21 @@
 namespace gpt2k {
 
 // ---- linear layers (gemm.hip) -------------------------------------------------------
+// `partial` is a scratch of gemm_partial_floats() floats for stream-K partial tiles
+// (nullptr: one tile per block, no sharing of tiles).
+size_t gemm_partial_floats();
 // out[M,N] (ld ldo) = inp[M,K] . w[N,K]^T, then by the non-null extras:
 //   bias: + bias[n];  resid: out = resid + (...) (resid has ld ldo);
 //   pre:  pre = (...) and out = gelu(pre) (pre has ld ldo).
 hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
-                          hipStream_t st);
+                          float* partial, hipStream_t st);
 // din[M,N] = dout[M,K] (ld ld_dout) . w[K,N]; with gelu_pre: din *= gelu'(gelu_pre[M,N]).
-// splits > 1 (and no gelu_pre) splits K and adds the parts in order through `partial`
-// (splits*M*N floats).
 hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float* w,
-                        const float* gelu_pre, int M, int N, int K, int splits, float* partial,
-                        hipStream_t st);
-// dw[M,N] += dout[K,M]^T (dout ld ld_dout) . inp[K,N]; split-K as above.
+                        const float* gelu_pre, int M, int N, int K, float* partial, hipStream_t st);
+// dw[M,N] += dout[K,M]^T (dout ld ld_dout) . inp[K,N].
 hipError_t linear_wgrad(float* dw, const float* dout, long ld_dout, const float* inp, int M, int N,
-                        int K, int splits, float* partial, hipStream_t st);
-// Number of splits linear_* actually uses for a requested count.
-int splitk_effective(int K, int splits);
+                        int K, float* partial, hipStream_t st);
 
 // ---- column sums (bias gradients) (norm.hip) ------------------------------------------
 // db[n] += sum_m x[m, n] over M rows (row stride ld); deterministic two-phase reduction

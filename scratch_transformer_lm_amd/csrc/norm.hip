@@ -8,6 +8,7 @@
 // second kernel adds in a fixed order, so results are deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace gpt2k {
 
@@ -16,7 +17,6 @@ namespace {
 constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
 constexpr int LN_MAX_BLOCKS = 512;
 constexpr int COLSUM_ROWS = 32;
-constexpr int COLSUM_MAX_CHUNKS = 256;
 
 template <int VPL>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, float* __restrict__ mean,
@@ -157,24 +157,44 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
     }
 }
 
-// out[w] (+)= sum_r part[r*W + w] over R rows, added in row order within 4 interleaved
-// groups that are then added in group order.  Columns w < W1 go to out_lo[w], the rest
-// to out_hi[w - W1].  Block: 64 columns x 4 groups.
+// out[w] (+)= sum_r part[r*W + w] over R rows (W % 4 == 0).  A block covers 64 columns as
+// 16 float4 columns x 16 row groups; group j adds rows j, j+16, ... in order, then the 16
+// group sums are added in group order.  Columns w < W1 go to out_lo[w], the rest to
+// out_hi[w - W1].
 __global__ __launch_bounds__(256) void reduce_rows_kernel(float* out_lo, float* out_hi, int W1,
                                                           const float* __restrict__ part, int R, int W,
                                                           int accumulate) {
-    __shared__ float s[4][64];
-    const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
-    const int wcol = blockIdx.x * 64 + cl;
-    float acc = 0.f;
-    if (wcol < W)
-        for (int r = grp; r < R; r += 4) acc += part[(long)r * W + wcol];
-    s[grp][cl] = acc;
+    __shared__ float4 s[16][16];
+    const int c4 = threadIdx.x & 15, grp = threadIdx.x >> 4;
+    const int w = blockIdx.x * 64 + c4 * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (w < W) {
+#pragma unroll 8
+        for (int r = grp; r < R; r += 16) {
+            const float4 v = *reinterpret_cast<const float4*>(part + (long)r * W + w);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+    }
+    s[grp][c4] = acc;
     __syncthreads();
-    if (grp == 0 && wcol < W) {
-        const float tot = ((s[0][cl] + s[1][cl]) + s[2][cl]) + s[3][cl];
-        float* dst = wcol < W1 ? out_lo + wcol : out_hi + (wcol - W1);
-        *dst = accumulate ? *dst + tot : tot;
+    if (grp == 0 && w < W) {
+        float4 tot = s[0][c4];
+        for (int j = 1; j < 16; j++) {
+            const float4 v = s[j][c4];
+            tot.x += v.x;
+            tot.y += v.y;
+            tot.z += v.z;
+            tot.w += v.w;
+        }
+        const float t4[4] = {tot.x, tot.y, tot.z, tot.w};
+        for (int e = 0; e < 4; e++) {
+            const int we = w + e;
+            float* dst = we < W1 ? out_lo + we : out_hi + (we - W1);
+            *dst = accumulate ? *dst + t4[e] : t4[e];
+        }
     }
 }
 
@@ -208,6 +228,7 @@ hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x,
     if (N == 0) return hipSuccess;
     const int vpl = (C / 4 + 63) / 64;
     dim3 grid((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), block(256);
+    ProfScope ps(st, "ln_fwd_kernel", 0.0, 4.0 * ((double)N * C * 2 + 2.0 * N + 2.0 * C));
 #define LN_FWD(V) hipLaunchKernelGGL(ln_fwd_kernel<V>, grid, block, 0, st, y, mean, rstd, x, w, b, N, C, eps)
     switch (vpl) {
         case 1: LN_FWD(1); break;
@@ -239,18 +260,23 @@ hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, 
     const int vpl = (C / 4 + 63) / 64;
     const int G = ln_blocks(N);
     const size_t lds = (size_t)4 * C * sizeof(float);
+    {
+        ProfScope ps(st, "ln_bwd_kernel", 0.0,
+                     4.0 * ((double)N * C * (accumulate_dx ? 4 : 3) + 2.0 * N + C + 2.0 * G * C));
 #define LN_BWD(V) hipLaunchKernelGGL(ln_bwd_kernel<V>, dim3(G), dim3(256), lds, st, dx, partial, dy, x, w, mean, rstd, N, C, (int)accumulate_dx)
-    switch (vpl) {
-        case 1: LN_BWD(1); break;
-        case 2: LN_BWD(2); break;
-        case 3: LN_BWD(3); break;
-        case 4: LN_BWD(4); break;
-        case 5: case 6: case 7: case 8: LN_BWD(8); break;
-        default: LN_BWD(16); break;
-    }
+        switch (vpl) {
+            case 1: LN_BWD(1); break;
+            case 2: LN_BWD(2); break;
+            case 3: LN_BWD(3); break;
+            case 4: LN_BWD(4); break;
+            case 5: case 6: case 7: case 8: LN_BWD(8); break;
+            default: LN_BWD(16); break;
+        }
 #undef LN_BWD
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    ProfScope ps2(st, "reduce_rows_kernel", 0.0, 4.0 * ((double)G * 2 * C + 2.0 * C * (accumulate_dwdb ? 2 : 1)));
     hipLaunchKernelGGL(reduce_rows_kernel, dim3((2 * C + 63) / 64), dim3(256), 0, st, dw, db, C,
                        (const float*)partial, G, 2 * C, (int)accumulate_dwdb);
     return hipGetLastError();
@@ -263,9 +289,13 @@ hipError_t colsum_accumulate(float* db, const float* x, long ld, int M, int N, f
     if (N % 4 || ld % 4 || M <= 0) return M == 0 ? hipSuccess : hipErrorInvalidValue;
     const int chunks = colsum_chunks(M);
     dim3 grid((N / 4 + 255) / 256, chunks);
-    hipLaunchKernelGGL(colsum_partial_kernel, grid, dim3(256), 0, st, partial, x, ld, M, N);
+    {
+        ProfScope ps(st, "colsum_partial_kernel", 0.0, 4.0 * ((double)M * N + (double)chunks * N));
+        hipLaunchKernelGGL(colsum_partial_kernel, grid, dim3(256), 0, st, partial, x, ld, M, N);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    ProfScope ps(st, "reduce_rows_kernel", 0.0, 4.0 * ((double)chunks * N + 2.0 * N));
     hipLaunchKernelGGL(reduce_rows_kernel, dim3((N + 63) / 64), dim3(256), 0, st, db, db, N,
                        (const float*)partial, chunks, N, 1);
     return hipGetLastError();

@@ -9,6 +9,7 @@
 // Rows are padded to a multiple of 64 floats so every row starts 256-byte aligned.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace gpt2k {
 
@@ -126,6 +127,7 @@ hipError_t softmax_xent_forward(float* logits, long ld, float* losses, const int
                                 int N, int V, int* flags, hipStream_t st) {
     if (ld % 4 || ld < V) return hipErrorInvalidValue;
     if (N == 0) return hipSuccess;
+    ProfScope ps(st, "softmax_xent_kernel", 0.0, 8.0 * (double)N * V);
     hipLaunchKernelGGL(softmax_xent_kernel, dim3(N), dim3(SX_THREADS), 0, st, logits, ld, losses, targets, V, flags);
     return hipGetLastError();
 }
@@ -139,6 +141,7 @@ hipError_t xent_backward(float* probs, long ld, const int32_t* targets, int N, i
                          hipStream_t st) {
     if (ld % 4 || ld < V) return hipErrorInvalidValue;
     if (N == 0) return hipSuccess;
+    ProfScope ps(st, "xent_bwd_kernel", 0.0, 8.0 * (double)N * V);
     hipLaunchKernelGGL(xent_bwd_kernel, dim3(N), dim3(SX_THREADS), 0, st, probs, ld, targets, V, scale);
     return hipGetLastError();
 }

@@ -83,6 +83,16 @@ def load() -> ct.CDLL:
     lib.gpt2_free.restype = None
     lib.gpt2_activation_view.argtypes = [P, i, i] + [ct.POINTER(sz)] * 4
     lib.gpt2_activation_view.restype = i
+    lib.gpt2_profile_enable.argtypes = [P, i]
+    lib.gpt2_profile_enable.restype = i
+    lib.gpt2_profile_filter.argtypes = [P, ct.c_char_p]
+    lib.gpt2_profile_filter.restype = i
+    lib.gpt2_profile_collect.argtypes = [P]
+    lib.gpt2_profile_collect.restype = i
+    lib.gpt2_profile_entry.argtypes = [P, i, ct.POINTER(ct.c_char_p), ct.POINTER(ct.c_long),
+                                       ct.POINTER(ct.c_double), ct.POINTER(ct.c_double),
+                                       ct.POINTER(ct.c_double)]
+    lib.gpt2_profile_entry.restype = i
     lib.gpt2_layernorm_forward.argtypes = [P, P, P, P, P, P, i, i, f, P]
     lib.gpt2_layernorm_forward.restype = i
     lib.gpt2_layernorm_backward_workspace.argtypes = [i, i]
@@ -193,6 +203,34 @@ class GPT2:
 
     def last_error(self) -> int:
         return self.lib.gpt2_last_error(self.h)
+
+    # -- per-kernel timing ------------------------------------------------------------
+    def profile_enable(self, on: bool = True) -> bool:
+        rc = self.lib.gpt2_profile_enable(self.h, int(on))
+        if rc != GPT2_OK:
+            raise GPT2Error(rc, "gpt2_profile_enable")
+        return True
+
+    def profile_filter(self, kernel_name: str | None) -> None:
+        rc = self.lib.gpt2_profile_filter(self.h, kernel_name.encode() if kernel_name else None)
+        if rc != GPT2_OK:
+            raise GPT2Error(rc, "gpt2_profile_filter")
+
+    def profile_entries(self) -> list[dict]:
+        n = self.lib.gpt2_profile_collect(self.h)
+        if n < 0:
+            raise GPT2Error(n, "gpt2_profile_collect")
+        out = []
+        for i in range(n):
+            name, cnt = ct.c_char_p(), ct.c_long()
+            ms, fl, by = ct.c_double(), ct.c_double(), ct.c_double()
+            rc = self.lib.gpt2_profile_entry(self.h, i, ct.byref(name), ct.byref(cnt), ct.byref(ms),
+                                             ct.byref(fl), ct.byref(by))
+            if rc != GPT2_OK:
+                raise GPT2Error(rc, "gpt2_profile_entry")
+            out.append(dict(name=name.value.decode(), launches=cnt.value, ms=ms.value,
+                            flops=fl.value, bytes=by.value))
+        return out
 
     # -- views ------------------------------------------------------------------------
     def tensor(self, buf, name: str):
