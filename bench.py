@@ -74,6 +74,31 @@ def breakdown(kernels, steps):
     return out
 
 
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "scratch_transformer_lm_amd", "csrc"))):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(ROOT, "scratch_transformer_lm_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
+    there is none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("kernel") != kernel or rec.get("sources") != kernel_source_digest():
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w: S.Workload, rows: int = 1):
     """The oracle (float64, as it stands) on a bounded sample: `rows` sequences of the
     workload, one full step (forward, zero_grad, backward, AdamW)."""
@@ -102,6 +127,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=S.GPT2_124M.name)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run a plain device copy of MIB MiB three times "
+                         "(a kernel of known traffic for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU data "
@@ -188,6 +216,17 @@ def main():
     out["ms_per_step_without_events"] = dt_plain * 1e3 / args.steps
     out["roofline"] = roofline(kernels)
     out["kernels"] = breakdown(all_kernels, max(1, args.warmup - 1))
+    traffic = recorded_traffic(out["roofline"]["kernel"])
+    if traffic is not None:
+        out["roofline"]["traffic"] = traffic
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 2 * 4 * n
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
