@@ -95,7 +95,8 @@ int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buff
  * are device pointers to B*T int32 token ids, row-major (B,T); ids must lie in
  * [0, vocab_size).  Requires 1 <= T <= max_seq_len and B*T <= the built B*T.
  * Returns the mean cross-entropy over the B*T positions.  With targets == NULL the
- * logits and probabilities are computed and -1.0f is returned.  Synchronises the
+ * logits and each row's log-sum-exp (which gives the softmax) are computed and -1.0f is
+ * returned.  Synchronises the
  * stream.  Returns NaN on error (GPT2_EINVAL for bad shapes or token ids found on the
  * device, GPT2_EDEVICE for a HIP failure). */
 float gpt2_forward(gpt2* model, const int32_t* inputs, const int32_t* targets, int B, int T);
@@ -144,8 +145,8 @@ enum {
     GPT2_ACT_LNF,          /* (B*T, C) */
     GPT2_ACT_LNF_MEAN,     /* (B*T) */
     GPT2_ACT_LNF_RSTD,     /* (B*T) */
-    GPT2_ACT_PROBS,        /* (B*T, V) with leading dimension ld >= V: softmax after the
-                              forward, d(loss)/d(logits) after the backward */
+    GPT2_ACT_LOGITS,       /* (B*T, V) with leading dimension ld >= V (rows 256-byte aligned) */
+    GPT2_ACT_LOGITS_LSE,   /* (B*T) log-sum-exp of each logits row: softmax = exp(logit - lse) */
     GPT2_ACT_LOSSES,       /* (B*T) per-position cross-entropy */
     GPT2_NUM_ACTS
 };

@@ -32,14 +32,18 @@ GPT2_DEV double wave_sum_d(double v) {
 constexpr float GELU_K0 = 0.7978845608028654f;  // sqrt(2/pi)
 constexpr float GELU_K1 = 0.044715f;
 
+// tanh z = 1 - 2 / (e^{2z} + 1), with e^x and 1/x on the hardware transcendental unit
+// (a few ulp; e^{2z} overflowing to +inf still gives exactly 1).
+GPT2_DEV float tanh_fast(float z) { return 1.0f - 2.0f * __frcp_rn(__expf(2.0f * z) + 1.0f); }
+
 GPT2_DEV float gelu_f(float u) {
     float z = GELU_K0 * (u + GELU_K1 * u * u * u);
-    return 0.5f * u * (1.0f + tanhf(z));
+    return 0.5f * u * (1.0f + tanh_fast(z));
 }
 
 GPT2_DEV float gelu_grad_f(float u) {
     float z = GELU_K0 * (u + GELU_K1 * u * u * u);
-    float th = tanhf(z);
+    float th = tanh_fast(z);
     float dz = GELU_K0 * (1.0f + 3.0f * GELU_K1 * u * u);
     return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
 }

@@ -45,7 +45,7 @@ constexpr int LDK = BK + 4;   // row stride of a k-contiguous LDS tile [row][k]
 constexpr int LDR = BM + 4;   // row stride of a row-contiguous LDS tile [k][row]
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;              // blocks the chip holds at once (2 per CU)
-constexpr int TILE_FLOATS = BM * BN;       // one partial tile
+constexpr int SLOT_FLOATS = BM * BN + BM;  // one partial tile + its bias-gradient row sums
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -64,7 +64,11 @@ struct Params {
     long ldaux;
     float* pre;         // pre-GELU output (EPI_BIAS_GELU)
     long ldpre;
-    float* partial;     // 2 partial tiles per block
+    float* partial;     // 2 partial slots per block
+    float* dbias;       // wgrad: db[m] += sum over k of A(m, k), by the tiles with n0 == 0
+    const float* lse;   // dlogits operand: per-row log-sum-exp of the logits
+    const int32_t* tgt; // dlogits operand: per-row target id
+    float xscale;       // dlogits operand: d loss / d loss_row (1 / rows)
     int tiles_m, tiles_n, nk;
     long total;         // tiles * nk iterations
     int G;              // persistent blocks
@@ -101,13 +105,13 @@ GPT2_DEV void load_kcontig(float4 (&reg)[4], const float* X, long ld, int r0, in
         const int r = r0 + (t >> 3) + 32 * j;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (r < nrows) {
-            const float* p = X + (long)r * ld + kk;
+            const float* q = X + (long)r * ld + kk;
             if (kk + 3 < K) {
-                v = *reinterpret_cast<const float4*>(p);
+                v = *reinterpret_cast<const float4*>(q);
             } else {
-                if (kk + 0 < K) v.x = p[0];
-                if (kk + 1 < K) v.y = p[1];
-                if (kk + 2 < K) v.z = p[2];
+                if (kk + 0 < K) v.x = q[0];
+                if (kk + 1 < K) v.y = q[1];
+                if (kk + 2 < K) v.z = q[2];
             }
         }
         reg[j] = v;
@@ -133,16 +137,58 @@ GPT2_DEV void load_rcontig(float4 (&reg)[4], const float* X, long ld, int r0, in
         const int kk = k0 + (t >> 5) + 8 * j;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (kk < K) {
-            const float* p = X + (long)kk * ld + r;
+            const float* q = X + (long)kk * ld + r;
             if (r + 3 < nrows) {
-                v = *reinterpret_cast<const float4*>(p);
+                v = *reinterpret_cast<const float4*>(q);
             } else {
-                if (r + 0 < nrows) v.x = p[0];
-                if (r + 1 < nrows) v.y = p[1];
-                if (r + 2 < nrows) v.z = p[2];
+                if (r + 0 < nrows) v.x = q[0];
+                if (r + 1 < nrows) v.y = q[1];
+                if (r + 2 < nrows) v.z = q[2];
             }
         }
         reg[j] = v;
+    }
+}
+
+// The logits operand of the LM-head backward: each logit z of row `row` in vocabulary
+// column c becomes d loss / d z = (exp(z - lse[row]) - [c == target[row]]) * scale.
+// Applied to the prefetched registers just before they go to LDS (so the global loads
+// keep their full k-tile of latency hiding); out-of-range elements stay zero.
+GPT2_DEV float dlogit(float z, float lse, int tgt, int c, float scale) {
+    return (__expf(z - lse) - (c == tgt ? 1.0f : 0.0f)) * scale;
+}
+
+// k-contiguous slab (LM-head dgrad): row r = r0 + t/8 + 32j is a logits row; its lse and
+// target are `rl[j]`, `rt[j]`; columns kk.. are vocabulary ids.
+GPT2_DEV void dlogit_kcontig(float4 (&reg)[4], const float (&rl)[4], const int (&rt)[4], int r0, int nrows,
+                             int k0, int K, float scale) {
+    const int t = threadIdx.x;
+    const int kk = k0 + (t & 7) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        if (r0 + (t >> 3) + 32 * j >= nrows) continue;
+        float4& v = reg[j];
+        if (kk + 0 < K) v.x = dlogit(v.x, rl[j], rt[j], kk + 0, scale);
+        if (kk + 1 < K) v.y = dlogit(v.y, rl[j], rt[j], kk + 1, scale);
+        if (kk + 2 < K) v.z = dlogit(v.z, rl[j], rt[j], kk + 2, scale);
+        if (kk + 3 < K) v.w = dlogit(v.w, rl[j], rt[j], kk + 3, scale);
+    }
+}
+
+// row-contiguous slab (LM-head wgrad): k = k0 + t/32 + 8j is a logits row (lse rl[j],
+// target rt[j]); the row index r.. is the vocabulary id.
+GPT2_DEV void dlogit_rcontig(float4 (&reg)[4], const float (&rl)[4], const int (&rt)[4], int r0, int nrows,
+                             int k0, int K, float scale) {
+    const int t = threadIdx.x;
+    const int r = r0 + (t & 31) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        if (k0 + (t >> 5) + 8 * j >= K) continue;
+        float4& v = reg[j];
+        if (r + 0 < nrows) v.x = dlogit(v.x, rl[j], rt[j], r + 0, scale);
+        if (r + 1 < nrows) v.y = dlogit(v.y, rl[j], rt[j], r + 1, scale);
+        if (r + 2 < nrows) v.z = dlogit(v.z, rl[j], rt[j], r + 2, scale);
+        if (r + 3 < nrows) v.w = dlogit(v.w, rl[j], rt[j], r + 3, scale);
     }
 }
 
@@ -225,7 +271,7 @@ GPT2_DEV void store_partial(float* slot, const f32x4 (&acc)[4][4]) {
 }
 
 
-template <bool A_K, bool B_K, int EPI>
+template <bool A_K, bool B_K, int EPI, bool XF>
 __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     constexpr int A_STAGE = A_K ? BM * LDK : BK * LDR;
     constexpr int B_STAGE = B_K ? BN * LDK : BK * LDR;
@@ -259,13 +305,52 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
 #pragma unroll
             for (int b = 0; b < 4; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+        // wgrad with bias: row sums of A over this segment's k, 4 rows per thread
+        const bool bias_rows = !A_K && p.dbias != nullptr && n0 == 0;
+        float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+
+        // dlogits operand: lse / target of the logits rows this thread's A slab covers
+        float xl[4];
+        int xt[4];
+        int ra_k0 = 0;
+        if (XF && A_K) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int r = m0 + (threadIdx.x >> 3) + 32 * j;
+                xl[j] = r < p.M ? p.lse[r] : 0.f;
+                xt[j] = r < p.M ? p.tgt[r] : -1;
+            }
+        }
+
         auto load = [&](int k0) {
             if (A_K) load_kcontig(ra, p.A, p.lda, m0, p.M, k0, k_end);
             else load_rcontig(ra, p.A, p.lda, m0, p.M, k0, k_end);
             if (B_K) load_kcontig(rb, p.B, p.ldb, n0, p.N, k0, k_end);
             else load_rcontig(rb, p.B, p.ldb, n0, p.N, k0, k_end);
+            if (XF && !A_K) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int kk = k0 + (threadIdx.x >> 5) + 8 * j;
+                    xl[j] = kk < k_end ? p.lse[kk] : 0.f;
+                    xt[j] = kk < k_end ? p.tgt[kk] : -1;
+                }
+            }
+            ra_k0 = k0;
         };
         auto store = [&](int stage) {
+            if (XF) {
+                if (A_K) dlogit_kcontig(ra, xl, xt, m0, p.M, ra_k0, k_end, p.xscale);
+                else dlogit_rcontig(ra, xl, xt, m0, p.M, ra_k0, k_end, p.xscale);
+            }
+            if (!A_K && bias_rows) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    bsum[0] += ra[j].x;
+                    bsum[1] += ra[j].y;
+                    bsum[2] += ra[j].z;
+                    bsum[3] += ra[j].w;
+                }
+            }
             if (A_K) store_kcontig(As + stage * A_STAGE, ra);
             else store_rcontig(As + stage * A_STAGE, ra);
             if (B_K) store_kcontig(Bs + stage * B_STAGE, rb);
@@ -300,12 +385,35 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
             __syncthreads();
         }
 
-        if (ks == 0 && ke == p.nk) {
+        const bool full = ks == 0 && ke == p.nk;
+        // first segment of the range -> slot 0, the range's last (shared) tile -> slot 1
+        float* slot = p.partial + ((long)lb * 2 + (it == it_begin ? 0 : 1)) * SLOT_FLOATS;
+        if (bias_rows) {
+            // combine the 8 threads that share rows (t%32), in k-group order; the LDS
+            // operand buffers are free after the loop's final barrier
+            float* red = As;
+#pragma unroll
+            for (int e = 0; e < 4; e++) red[threadIdx.x * 4 + e] = bsum[e];
+            __syncthreads();
+            if (threadIdx.x < 32) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    float s = 0.f;
+                    for (int g8 = 0; g8 < 8; g8++) s += red[(g8 * 32 + threadIdx.x) * 4 + e];
+                    const int m = m0 + 4 * threadIdx.x + e;
+                    if (full) {
+                        if (m < p.M) p.dbias[m] += s;
+                    } else {
+                        slot[BM * BN + 4 * threadIdx.x + e] = s;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        if (full) {
             epilogue<EPI>(p, acc, m0, n0);
         } else {
-            // first segment of the range -> slot 0, the range's last (shared) tile -> slot 1
-            const int which = it == it_begin ? 0 : 1;
-            store_partial(p.partial + ((long)lb * 2 + which) * TILE_FLOATS, acc);
+            store_partial(slot, acc);
         }
         it += ke - ks;
     }
@@ -333,7 +441,7 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
     for (int b = 0; b < 4; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int l = first; l <= last; l++) {
         const int which = range_start(p.total, p.G, l) / p.nk == tile ? 0 : 1;
-        const float* slot = p.partial + ((long)l * 2 + which) * TILE_FLOATS + quarter * 16 * NT + threadIdx.x;
+        const float* slot = p.partial + ((long)l * 2 + which) * SLOT_FLOATS + quarter * 16 * NT + threadIdx.x;
         float v[16];
 #pragma unroll
         for (int e = 0; e < 16; e++) v[e] = slot[e * NT];
@@ -344,13 +452,22 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
     tile_coords(p, tile, m0, n0);
 #pragma unroll
     for (int b = 0; b < 4; b++) epilogue_block<EPI>(p, acc[b], m0, n0, quarter, b);
+    if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
+        float s = 0.f;
+        for (int l = first; l <= last; l++) {
+            const int which = range_start(p.total, p.G, l) / p.nk == tile ? 0 : 1;
+            s += p.partial[((long)l * 2 + which) * SLOT_FLOATS + BM * BN + threadIdx.x];
+        }
+        p.dbias[m0 + threadIdx.x] += s;
+    }
 }
 
 // Kernel name as profilers print the instantiation.
-template <bool A_K, bool B_K, int EPI>
+template <bool A_K, bool B_K, int EPI, bool XF>
 const char* gemm_name() {
     static const std::string s = std::string("gemm_kernel<") + (A_K ? "true" : "false") + ", " +
-                                 (B_K ? "true" : "false") + ", " + std::to_string(EPI) + ">";
+                                 (B_K ? "true" : "false") + ", " + std::to_string(EPI) + ", " +
+                                 (XF ? "true" : "false") + ">";
     return s.c_str();
 }
 
@@ -360,7 +477,7 @@ const char* fixup_name() {
     return s.c_str();
 }
 
-template <bool A_K, bool B_K, int EPI>
+template <bool A_K, bool B_K, int EPI, bool XF = false>
 hipError_t launch(Params& p, hipStream_t st) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
@@ -379,13 +496,13 @@ hipError_t launch(Params& p, hipStream_t st) {
     const double extra = (EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_BIAS_GELU) ? mn : 0.0;
     {
         // algorithmic work: 2MNK flops; operands read once, C written (and read for += / aux)
-        ProfScope ps(st, gemm_name<A_K, B_K, EPI>(), 2.0 * mn * p.K,
+        ProfScope ps(st, gemm_name<A_K, B_K, EPI, XF>(), 2.0 * mn * p.K,
                      4.0 * ((double)p.M * p.K + (double)p.N * p.K + mn + extra));
-        hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI>), dim3(p.G), dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF>), dim3(p.G), dim3(NT), 0, st, p);
     }
     const bool aligned_ranges = p.total % p.G == 0 && (p.total / p.G) % p.nk == 0;
     if (sk && !aligned_ranges && p.G > 1) {
-        ProfScope ps(st, fixup_name<EPI>(), 0.0, 4.0 * (2.0 * p.G * TILE_FLOATS + extra));
+        ProfScope ps(st, fixup_name<EPI>(), 0.0, 4.0 * (2.0 * p.G * SLOT_FLOATS + extra));
         hipLaunchKernelGGL((gemm_fixup_kernel<EPI>), dim3(4 * (p.G - 1)), dim3(NT), 0, st, p);
     }
     return hipGetLastError();
@@ -395,7 +512,7 @@ bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
 
 }  // namespace
 
-size_t gemm_partial_floats() { return (size_t)RESIDENT * 2 * TILE_FLOATS; }
+size_t gemm_partial_floats() { return (size_t)RESIDENT * 2 * SLOT_FLOATS; }
 
 hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
@@ -428,7 +545,8 @@ hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w
 }
 
 hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float* w,
-                        const float* gelu_pre, int M, int N, int K, float* partial, hipStream_t st) {
+                        const float* gelu_pre, int M, int N, int K, float* partial, hipStream_t st,
+                        const XentOperand* xent) {
     if (ld_dout % 4 || N % 4 || !aligned16(dout) || !aligned16(w)) return hipErrorInvalidValue;
     Params p{};
     p.M = M;
@@ -446,11 +564,17 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
         p.ldaux = N;
         return launch<true, false, EPI_GELU_BWD>(p, st);
     }
+    if (xent) {
+        p.lse = xent->lse;
+        p.tgt = xent->targets;
+        p.xscale = xent->scale;
+        return launch<true, false, EPI_STORE, true>(p, st);
+    }
     return launch<true, false, EPI_STORE>(p, st);
 }
 
-hipError_t linear_wgrad(float* dw, const float* dout, long ld_dout, const float* inp, int M, int N,
-                        int K, float* partial, hipStream_t st) {
+hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout, const float* inp, int M,
+                        int N, int K, float* partial, hipStream_t st, const XentOperand* xent) {
     if (ld_dout % 4 || N % 4 || !aligned16(dout) || !aligned16(inp)) return hipErrorInvalidValue;
     Params p{};
     p.M = M;
@@ -463,6 +587,13 @@ hipError_t linear_wgrad(float* dw, const float* dout, long ld_dout, const float*
     p.C = dw;
     p.ldc = N;
     p.partial = partial;
+    p.dbias = dbias;
+    if (xent) {
+        p.lse = xent->lse;
+        p.tgt = xent->targets;
+        p.xscale = xent->scale;
+        return launch<false, false, EPI_ACCUM, true>(p, st);
+    }
     return launch<false, false, EPI_ACCUM>(p, st);
 }
 

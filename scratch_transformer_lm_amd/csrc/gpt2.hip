@@ -98,7 +98,8 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     put(GPT2_ACT_LNF, C, C, false, BT);
     put(GPT2_ACT_LNF_MEAN, 1, 1, false, BT);
     put(GPT2_ACT_LNF_RSTD, 1, 1, false, BT);
-    put(GPT2_ACT_PROBS, V, y.Vp, false, BT);
+    put(GPT2_ACT_LOGITS, V, y.Vp, false, BT);
+    put(GPT2_ACT_LOGITS_LSE, 1, 1, false, BT);
     put(GPT2_ACT_LOSSES, 1, 1, false, BT);
     y.tok_in = o;
     o += align_up(BT);
@@ -141,7 +142,7 @@ struct gpt2 {
     size_t poff[NP], plen[NP];
     int* host_ret;  // pinned: [loss bits, flags]
     int last_error;
-    bool have_forward, have_targets, probs_are_grads;
+    bool have_forward, have_targets;
     Profiler* prof;  // non-null while per-kernel timing is enabled
 };
 
@@ -184,7 +185,6 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     g->B = B;
     g->T = T;
     g->have_forward = false;
-    g->probs_are_grads = false;
     HIPCHK(g, hipMemcpyAsync(tok_in(g), inputs, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
     if (targets) HIPCHK(g, hipMemcpyAsync(tok_tgt(g), targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(g, hipMemsetAsync(g->buf.grad_scratch, 0, HDR_WORDS * sizeof(float), st));
@@ -207,9 +207,10 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     }
     HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LNF), A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD),
                                 A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, 1e-5f, st));
-    HIPCHK(g, linear_forward(A(g, GPT2_ACT_PROBS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT, V, C, part, st));
-    HIPCHK(g, softmax_xent_forward(A(g, GPT2_ACT_PROBS), Vp, A(g, GPT2_ACT_LOSSES), targets ? tok_tgt(g) : nullptr, BT, V,
-                                   flags(g), st));
+    HIPCHK(g, linear_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT, V,
+                             C, part, st));
+    HIPCHK(g, lse_xent_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LOGITS_LSE), A(g, GPT2_ACT_LOSSES),
+                               targets ? tok_tgt(g) : nullptr, BT, V, flags(g), st));
     if (targets) HIPCHK(g, loss_mean(g->buf.grad_scratch + HDR_LOSS, A(g, GPT2_ACT_LOSSES), BT, st));
     HIPCHK(g, hipMemcpyAsync(g->host_ret, g->buf.grad_scratch, 2 * sizeof(int), hipMemcpyDeviceToHost, st));
     HIPCHK(g, hipStreamSynchronize(st));
@@ -234,44 +235,38 @@ int backward_impl(gpt2* g) {
     float* datty = S(g, g->lay.datty);
     float* dqkv = S(g, g->lay.dqkv);
     float* dfch = S(g, g->lay.dfch);
-    float* probs = A(g, GPT2_ACT_PROBS);
+    float* logits = A(g, GPT2_ACT_LOGITS);
 
-    // d loss / d logits = (p - onehot) / (B*T), in place over the probabilities.
-    if (!g->probs_are_grads) {
-        HIPCHK(g, xent_backward(probs, Vp, tok_tgt(g), BT, V, 1.0f / (float)BT, st));
-        g->probs_are_grads = true;
-    }
-    // LM head (tied): dlnf = dlogits . wte;  dwte += dlogits^T . lnf.
-    HIPCHK(g, linear_dgrad(dln, probs, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st));
-    HIPCHK(g, linear_wgrad(G(g, P_WTE), probs, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part, st));
+    // LM head (tied): dlnf = dlogits . wte;  dwte += dlogits^T . lnf, where
+    // dlogits = (softmax(logits) - onehot(target)) / (B*T) is formed as the GEMMs load the
+    // logits (softmax = exp(logit - lse)).
+    const XentOperand xo{A(g, GPT2_ACT_LOGITS_LSE), tok_tgt(g), 1.0f / (float)BT};
+    HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
+    HIPCHK(g, linear_wgrad(G(g, P_WTE), nullptr, logits, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part, st, &xo));
     HIPCHK(g, layernorm_backward(dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
                                  A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
     for (int l = L - 1; l >= 0; l--) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         // MLP projection: residual3 = residual2 + gelu(fch) . Wp^T + bp.
-        HIPCHK(g, linear_wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, dres, C, A(g, GPT2_ACT_FCH_GELU, l), C, 4 * C, BT,
+        HIPCHK(g, linear_wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, G(g, P_FCPROJB) + l * C, dres, C, A(g, GPT2_ACT_FCH_GELU, l), C, 4 * C, BT,
                                part, st));
-        HIPCHK(g, colsum_accumulate(G(g, P_FCPROJB) + l * C, dres, C, BT, C, part, st));
         HIPCHK(g, linear_dgrad(dfch, dres, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C,
                                part, st));
         // MLP expansion: fch = ln2 . Wf^T + bf.
-        HIPCHK(g, linear_wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, dfch, 4 * C, A(g, GPT2_ACT_LN2, l), 4 * C, C, BT,
+        HIPCHK(g, linear_wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, G(g, P_FCB) + l * 4 * C, dfch, 4 * C, A(g, GPT2_ACT_LN2, l), 4 * C, C, BT,
                                part, st));
-        HIPCHK(g, colsum_accumulate(G(g, P_FCB) + l * 4 * C, dfch, 4 * C, BT, 4 * C, part, st));
         HIPCHK(g, linear_dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, nullptr, BT, C, 4 * C, part, st));
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
                                      P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C,
                                      true, true, part, st));
         // Attention projection: residual2 = residual + atty . Wa^T + ba.
-        HIPCHK(g, linear_wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, dres, C, A(g, GPT2_ACT_ATTY, l), C, C, BT, part, st));
-        HIPCHK(g, colsum_accumulate(G(g, P_ATTPROJB) + l * C, dres, C, BT, C, part, st));
+        HIPCHK(g, linear_wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, G(g, P_ATTPROJB) + l * C, dres, C, A(g, GPT2_ACT_ATTY, l), C, C, BT, part, st));
         HIPCHK(g, linear_dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, nullptr, BT, C, C, part, st));
         HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
                                      A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
-        HIPCHK(g, linear_wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, dqkv, 3 * C, A(g, GPT2_ACT_LN1, l), 3 * C, C, BT,
+        HIPCHK(g, linear_wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, 3 * C, A(g, GPT2_ACT_LN1, l), 3 * C, C, BT,
                                part, st));
-        HIPCHK(g, colsum_accumulate(G(g, P_QKVB) + l * 3 * C, dqkv, 3 * C, BT, 3 * C, part, st));
         HIPCHK(g, linear_dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, nullptr, BT, C, 3 * C, part, st));
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                                      A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));

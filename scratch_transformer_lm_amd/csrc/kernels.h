@@ -19,12 +19,21 @@ size_t gemm_partial_floats();
 hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
                           float* partial, hipStream_t st);
+// Marks a `dout` operand as logits whose gradient is formed while loading:
+// dlogit = (exp(z - lse[row]) - [col == targets[row]]) * scale.
+struct XentOperand {
+    const float* lse;
+    const int32_t* targets;
+    float scale;
+};
 // din[M,N] = dout[M,K] (ld ld_dout) . w[K,N]; with gelu_pre: din *= gelu'(gelu_pre[M,N]).
 hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float* w,
-                        const float* gelu_pre, int M, int N, int K, float* partial, hipStream_t st);
-// dw[M,N] += dout[K,M]^T (dout ld ld_dout) . inp[K,N].
-hipError_t linear_wgrad(float* dw, const float* dout, long ld_dout, const float* inp, int M, int N,
-                        int K, float* partial, hipStream_t st);
+                        const float* gelu_pre, int M, int N, int K, float* partial, hipStream_t st,
+                        const XentOperand* xent = nullptr);
+// dw[M,N] += dout[K,M]^T (dout ld ld_dout) . inp[K,N]; dbias (optional) += column sums of
+// dout over its K rows.
+hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout, const float* inp, int M,
+                        int N, int K, float* partial, hipStream_t st, const XentOperand* xent = nullptr);
 
 // ---- column sums (bias gradients) (norm.hip) ------------------------------------------
 // db[n] += sum_m x[m, n] over M rows (row stride ld); deterministic two-phase reduction
@@ -61,14 +70,11 @@ hipError_t attention_backward(float* dqkv, float* delta, const float* dout, cons
                               hipStream_t st);
 
 // ---- softmax + cross-entropy (softmax_xent.hip) -------------------------------------
-// In place over logits rows (ld): probs; per-row loss when targets != NULL.
-hipError_t softmax_xent_forward(float* logits, long ld, float* losses, const int32_t* targets,
-                                int N, int V, int* flags, hipStream_t st);
+// Per logits row (ld): lse = log sum exp; loss = lse - z[target] when targets != NULL.
+hipError_t lse_xent_forward(const float* logits, long ld, float* lse, float* losses, const int32_t* targets,
+                            int N, int V, int* flags, hipStream_t st);
 // Mean of losses[0..N) in double, written as float to *out.
 hipError_t loss_mean(float* out, const float* losses, int N, hipStream_t st);
-// In place: probs -> (probs - onehot(target)) * scale.
-hipError_t xent_backward(float* probs, long ld, const int32_t* targets, int N, int V, float scale,
-                         hipStream_t st);
 
 // ---- optimizer and fills (adamw.hip) ------------------------------------------------
 hipError_t adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float b1,

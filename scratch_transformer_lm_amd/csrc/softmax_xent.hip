@@ -1,12 +1,15 @@
-// Softmax + cross-entropy over the vocabulary, forward and backward, for gfx950.
+// Softmax + cross-entropy over the vocabulary, for gfx950.
 //
 // The pages list softmax_forward, crossentropy_forward and the fused
 // crossentropy_softmax_backward (huxiu page "llm.c：Andrej Karpathy带你从零复现LLM",
 // 核心代码解读 item 1).  Rows are V = 50257 floats, far too long for one wave, so a
-// 256-thread block owns a row: pass 1 keeps a running (max, sum of exp) per thread
-// (rescaling the sum when the max grows), the block merges the pairs, pass 2 writes the
-// probabilities in place.  The loss is log(sum) + max - z[target], i.e. -log p[target].
-// Rows are padded to a multiple of 64 floats so every row starts 256-byte aligned.
+// 256-thread block owns a row and keeps a running (max, sum of exp) per thread
+// (rescaling the sum when the max grows); the block merges the pairs into
+// lse = max + log(sum).  The loss is lse - z[target] = -log softmax(z)[target].
+// Nothing else is written: the probabilities exp(z - lse) and the logits' gradient
+// (p - onehot)/rows are formed by the LM-head backward GEMMs as they load the logits,
+// which saves writing and re-reading two 1.6 GB tensors.  Rows are padded to a multiple
+// of 64 floats so every row starts 256-byte aligned.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -33,14 +36,13 @@ GPT2_DEV void online_merge(float& m, float& s, float m2, float s2) {
     m = M;
 }
 
-__global__ __launch_bounds__(SX_THREADS) void softmax_xent_kernel(float* __restrict__ logits, long ld,
-                                                                  float* __restrict__ losses,
-                                                                  const int32_t* __restrict__ targets, int V,
-                                                                  int* flags) {
+__global__ __launch_bounds__(SX_THREADS) void lse_xent_kernel(const float* __restrict__ logits, long ld,
+                                                              float* __restrict__ lse, float* __restrict__ losses,
+                                                              const int32_t* __restrict__ targets, int V,
+                                                              int* flags) {
     __shared__ float sm_m[SX_THREADS / 64], sm_s[SX_THREADS / 64];
-    __shared__ float zt;
     const long row = blockIdx.x;
-    float* z = logits + row * ld;
+    const float* z = logits + row * ld;
     const int V4 = V >> 2;
     float m = -INFINITY, s = 0.f;
     for (int i = threadIdx.x; i < V4; i += SX_THREADS) {
@@ -61,30 +63,22 @@ __global__ __launch_bounds__(SX_THREADS) void softmax_xent_kernel(float* __restr
         sm_m[wave] = m;
         sm_s[wave] = s;
     }
-    int tgt = -1;
-    if (threadIdx.x == 0 && targets) {
-        tgt = targets[row];
-        if (tgt < 0 || tgt >= V) {
-            atomicOr(flags, ERR_BAD_TARGET_TOKEN);
-            zt = NAN;
-        } else {
-            zt = z[tgt];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float M = sm_m[0], S = sm_s[0];
+        for (int w = 1; w < SX_THREADS / 64; w++) online_merge(M, S, sm_m[w], sm_s[w]);
+        const float L = logf(S) + M;
+        lse[row] = L;
+        if (targets) {
+            const int tgt = targets[row];
+            if (tgt < 0 || tgt >= V) {
+                atomicOr(flags, ERR_BAD_TARGET_TOKEN);
+                losses[row] = NAN;
+            } else {
+                losses[row] = L - z[tgt];
+            }
         }
     }
-    __syncthreads();
-    float M = sm_m[0], S = sm_s[0];
-    for (int w = 1; w < SX_THREADS / 64; w++) online_merge(M, S, sm_m[w], sm_s[w]);
-    const float inv = 1.0f / S;
-    for (int i = threadIdx.x; i < V4; i += SX_THREADS) {
-        float4 v = reinterpret_cast<float4*>(z)[i];
-        v.x = expf(v.x - M) * inv;
-        v.y = expf(v.y - M) * inv;
-        v.z = expf(v.z - M) * inv;
-        v.w = expf(v.w - M) * inv;
-        reinterpret_cast<float4*>(z)[i] = v;
-    }
-    for (int i = 4 * V4 + threadIdx.x; i < V; i += SX_THREADS) z[i] = expf(z[i] - M) * inv;
-    if (threadIdx.x == 0 && targets) losses[row] = (logf(S) + M) - zt;
 }
 
 // Mean in double, fixed order: strided per-thread sums, then a tree in LDS.
@@ -101,48 +95,19 @@ __global__ __launch_bounds__(256) void loss_mean_kernel(float* out, const float*
     if (threadIdx.x == 0) *out = (float)(sm[0] / (double)N);
 }
 
-__global__ __launch_bounds__(SX_THREADS) void xent_bwd_kernel(float* __restrict__ probs, long ld,
-                                                              const int32_t* __restrict__ targets, int V,
-                                                              float scale) {
-    const long row = blockIdx.x;
-    float* z = probs + row * ld;
-    int tgt = targets[row];
-    if (tgt < 0 || tgt >= V) tgt = -1;  // flagged by the forward
-    const int V4 = V >> 2;
-    for (int i = threadIdx.x; i < V4; i += SX_THREADS) {
-        float4 v = reinterpret_cast<float4*>(z)[i];
-        const int c = 4 * i;
-        v.x = (v.x - (c + 0 == tgt ? 1.f : 0.f)) * scale;
-        v.y = (v.y - (c + 1 == tgt ? 1.f : 0.f)) * scale;
-        v.z = (v.z - (c + 2 == tgt ? 1.f : 0.f)) * scale;
-        v.w = (v.w - (c + 3 == tgt ? 1.f : 0.f)) * scale;
-        reinterpret_cast<float4*>(z)[i] = v;
-    }
-    for (int i = 4 * V4 + threadIdx.x; i < V; i += SX_THREADS) z[i] = (z[i] - (i == tgt ? 1.f : 0.f)) * scale;
-}
-
 }  // namespace
 
-hipError_t softmax_xent_forward(float* logits, long ld, float* losses, const int32_t* targets,
-                                int N, int V, int* flags, hipStream_t st) {
+hipError_t lse_xent_forward(const float* logits, long ld, float* lse, float* losses, const int32_t* targets,
+                            int N, int V, int* flags, hipStream_t st) {
     if (ld % 4 || ld < V) return hipErrorInvalidValue;
     if (N == 0) return hipSuccess;
-    ProfScope ps(st, "softmax_xent_kernel", 0.0, 8.0 * (double)N * V);
-    hipLaunchKernelGGL(softmax_xent_kernel, dim3(N), dim3(SX_THREADS), 0, st, logits, ld, losses, targets, V, flags);
+    ProfScope ps(st, "lse_xent_kernel", 0.0, 4.0 * ((double)N * V + 2.0 * N));
+    hipLaunchKernelGGL(lse_xent_kernel, dim3(N), dim3(SX_THREADS), 0, st, logits, ld, lse, losses, targets, V, flags);
     return hipGetLastError();
 }
 
 hipError_t loss_mean(float* out, const float* losses, int N, hipStream_t st) {
     hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(256), 0, st, out, losses, N);
-    return hipGetLastError();
-}
-
-hipError_t xent_backward(float* probs, long ld, const int32_t* targets, int N, int V, float scale,
-                         hipStream_t st) {
-    if (ld % 4 || ld < V) return hipErrorInvalidValue;
-    if (N == 0) return hipSuccess;
-    ProfScope ps(st, "xent_bwd_kernel", 0.0, 8.0 * (double)N * V);
-    hipLaunchKernelGGL(xent_bwd_kernel, dim3(N), dim3(SX_THREADS), 0, st, probs, ld, targets, V, scale);
     return hipGetLastError();
 }
 

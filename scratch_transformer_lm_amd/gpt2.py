@@ -21,7 +21,7 @@ PARAM_NAMES = ("wte", "wpe", "ln1w", "ln1b", "qkvw", "qkvb", "attprojw", "attpro
                "ln2w", "ln2b", "fcw", "fcb", "fcprojw", "fcprojb", "lnfw", "lnfb")
 ACT_NAMES = ("encoded", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "att_lse", "residual2",
              "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "residual3", "lnf", "lnf_mean",
-             "lnf_rstd", "probs", "losses")
+             "lnf_rstd", "logits", "logits_lse", "losses")
 
 
 class Config(ct.Structure):

@@ -10,6 +10,7 @@ import sys
 
 import numpy as np
 import pytest
+from scipy.special import logsumexp
 
 from scratch_transformer_lm_amd import synthetic as S
 from tests.parity import (GRAD_TOL, LN_BWD_TOL, LN_FWD_TOL, LOSS_RTOL, param_bound, per_tensor,
@@ -140,7 +141,9 @@ def test_tiny_forward_activations(G):
     errs = {}
     for name in ("encoded", "lnf", "lnf_mean", "lnf_rstd", "losses"):
         errs[name] = rel_max(host(m.activation(name)).reshape(-1), o.activation(name))
-    errs["probs"] = rel_max(host(m.activation("probs")).reshape(-1), o.activation("probs"))
+    logits = o.activation("logits").reshape(w.B * w.T, -1)
+    errs["logits"] = rel_max(host(m.activation("logits")), logits)
+    errs["logits_lse"] = rel_max(host(m.activation("logits_lse")).reshape(-1), logsumexp(logits, axis=1))
     for l in range(w.model.num_layers):
         for name in ("ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "residual2", "ln2", "fch",
                      "fch_gelu", "residual3"):
