@@ -12,9 +12,10 @@
 // The 16x16x4 form is used because it sustains the full fp32 matrix rate on gfx950,
 // where the 32x32x2 form measures about 12% lower.  Global tiles are prefetched into
 // registers one k-tile ahead and written to one of two LDS buffers, so each k-tile
-// costs one barrier.  LDS keeps the operand's own contiguity (k-contiguous rows padded
-// to 36 floats, m/n-contiguous rows padded to 132), which keeps both the float4 stores
-// and the fragment reads free of bank conflicts.  Inside a group of 16 k values each
+// costs one barrier.  LDS keeps the operand's own contiguity: k-contiguous rows are 32
+// floats with their 16-byte chunks XOR-swizzled by row, m/n-contiguous rows are padded
+// to 132 floats, which keeps both the float4 stores and the fragment reads free of bank
+// conflicts.  Inside a group of 16 k values each
 // lane takes 4 consecutive k for its lane group (k = 16g + 4(lane/16) + s for MFMA step
 // s), so a k-contiguous fragment is one 16-byte LDS read; the sum over k is the same
 // sum in another order.
@@ -41,7 +42,7 @@ namespace gpt2k {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
-constexpr int LDK = BK + 4;   // row stride of a k-contiguous LDS tile [row][k]
+constexpr int LDK = BK;       // row stride of a k-contiguous LDS tile [row][k] (16-byte chunks XOR-swizzled)
 constexpr int LDR = BM + 4;   // row stride of a row-contiguous LDS tile [k][row]
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;              // blocks the chip holds at once (2 per CU)
@@ -122,7 +123,10 @@ GPT2_DEV void store_kcontig(float* S, const float4 (&reg)[4]) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < 4; j++)
-        *reinterpret_cast<float4*>(S + ((t >> 3) + 32 * j) * LDK + (t & 7) * 4) = reg[j];
+    {
+        const int row = (t >> 3) + 32 * j;
+        *reinterpret_cast<float4*>(S + row * LDK + (((t & 7) ^ ((row >> 1) & 7)) * 4)) = reg[j];
+    }
 }
 
 // Loads the 32 x 128 slab of an operand whose rows are k and whose row index (m or n)
@@ -206,7 +210,8 @@ GPT2_DEV void read_frag(float (&f)[4], const float* S, int rb, int g) {
     const int lane = threadIdx.x & 63;
     const int i = lane & 15, grp = lane >> 4;
     if (KCONTIG) {
-        float4 v = *reinterpret_cast<const float4*>(S + (rb + i) * LDK + 16 * g + 4 * grp);
+        const int row = rb + i;
+        float4 v = *reinterpret_cast<const float4*>(S + row * LDK + (((4 * g + grp) ^ ((row >> 1) & 7)) * 4));
         f[0] = v.x;
         f[1] = v.y;
         f[2] = v.z;
@@ -366,21 +371,24 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
             if (kt + 1 < n) load((ks + kt + 1) * BK);
             const float* Acur = As + cur * A_STAGE;
             const float* Bcur = Bs + cur * B_STAGE;
+            // both 16-k groups' fragments are read before the first MFMA
+            float fa[BK / 16][4][4], fb[BK / 16][4][4];
 #pragma unroll
             for (int g = 0; g < BK / 16; g++) {
-                float fa[4][4], fb[4][4];
 #pragma unroll
-                for (int a = 0; a < 4; a++) read_frag<A_K>(fa[a], Acur, wm + 16 * a, g);
+                for (int a = 0; a < 4; a++) read_frag<A_K>(fa[g][a], Acur, wm + 16 * a, g);
 #pragma unroll
-                for (int b = 0; b < 4; b++) read_frag<B_K>(fb[b], Bcur, wn + 16 * b, g);
+                for (int b = 0; b < 4; b++) read_frag<B_K>(fb[g][b], Bcur, wn + 16 * b, g);
+            }
+#pragma unroll
+            for (int g = 0; g < BK / 16; g++)
 #pragma unroll
                 for (int s = 0; s < 4; s++)
 #pragma unroll
                     for (int a = 0; a < 4; a++)
 #pragma unroll
                         for (int b = 0; b < 4; b++)
-                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
-            }
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[g][a][s], fb[g][b][s], acc[a][b], 0, 0, 0);
             if (kt + 1 < n) store(cur ^ 1);
             __syncthreads();
         }
