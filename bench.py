@@ -74,12 +74,16 @@ def breakdown(kernels, steps):
     return out
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(kernel: str) -> str:
+    """Digest of the source file that defines `kernel` and of the shared kernel headers."""
     import hashlib
+    csrc = os.path.join(ROOT, "scratch_transformer_lm_amd", "csrc")
+    base = kernel.split("<")[0]
+    files = sorted(f for f in os.listdir(csrc) if f.endswith(".hip")
+                   and (base + "(") in open(os.path.join(csrc, f)).read())
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "scratch_transformer_lm_amd", "csrc"))):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(ROOT, "scratch_transformer_lm_amd", "csrc", f), "rb").read())
+    for f in files + ["common.h", "kernels.h"]:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -94,7 +98,7 @@ def recorded_traffic(kernel: str):
         if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("kernel") != kernel or rec.get("sources") != kernel_source_digest():
+    if rec.get("kernel") != kernel or rec.get("sources") != kernel_source_digest(kernel):
         return None
     return float(rec["traffic_bytes_per_launch"])
 

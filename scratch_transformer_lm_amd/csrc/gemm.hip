@@ -7,30 +7,31 @@
 //   dgrad    dX = dY W:               A = dY (k contiguous),  B = W  (n contiguous)
 //   wgrad    dW += dY^T X:            A = dY (m contiguous),  B = X  (n contiguous)
 //
-// Design for CDNA4: 256 threads = 4 wave64s, block tile 128x128, k-tile 32, each wave a
+// Design for CDNA4: 256 threads = 4 wave64s, block tile 128x128, k-tile 16, each wave a
 // 64x64 sub-tile made of 4x4 v_mfma_f32_16x16x4f32 blocks (64 accumulators per lane).
 // The 16x16x4 form is used because it sustains the full fp32 matrix rate on gfx950,
-// where the 32x32x2 form measures about 12% lower.  Global tiles are prefetched into
-// registers one k-tile ahead and written to one of two LDS buffers, so each k-tile
-// costs one barrier.  LDS keeps the operand's own contiguity: k-contiguous rows are 32
-// floats with their 16-byte chunks XOR-swizzled by row, m/n-contiguous rows are padded
-// to 132 floats, which keeps both the float4 stores and the fragment reads free of bank
-// conflicts.  Inside a group of 16 k values each
-// lane takes 4 consecutive k for its lane group (k = 16g + 4(lane/16) + s for MFMA step
-// s), so a k-contiguous fragment is one 16-byte LDS read; the sum over k is the same
-// sum in another order.
+// where the 32x32x2 form measures about 12% lower.  Operand k-tiles go from global
+// memory straight into LDS (global_load_lds_dwordx4, no register staging) through a ring
+// of 4 buffers, so 3 k-tiles are in flight while one is consumed, and each k-tile costs
+// one barrier.  LDS tiles are unpadded (a wave's transfer is 1 KB of consecutive LDS) and
+// bank conflicts are avoided by XOR-swizzling 16-byte chunks: k-contiguous tiles
+// [row][16] by (row/2)%4, row-contiguous tiles [k][128] by 4*((k/4)%4).  Each lane takes 4
+// consecutive k for its lane group (k = 4(lane/16) + s for MFMA step s), so a
+// k-contiguous fragment is one 16-byte LDS read; the sum over k is the same sum in
+// another order.
 //
-// Work distribution is stream-K: with two 74 KB blocks resident per CU the chip holds
-// 512 blocks, and the many shapes here with a few hundred 128x128 tiles would leave
-// most of a second round idle.  So a persistent grid of up to 512 blocks splits the
-// (tile, k-tile) iteration space into equal contiguous ranges.  A block finishes whole
-// tiles with the fused epilogue; a tile shared by several blocks is left as partial
-// accumulators (in fragment order, fully coalesced) that a fix-up kernel adds in k order
-// before running the same epilogue, so the result never depends on timing.  Logical
-// block ids are laid out so that each XCD (blocks are dealt round-robin to the 8 XCDs)
-// owns a contiguous iteration range, and tiles are ordered 8 tile-rows at a time, which
-// keeps neighbouring blocks on the same operand panels in one L2.  Shapes with many
-// tiles use the same kernel with one tile per block.
+// Work distribution: a persistent grid of up to 512 blocks (two 64 KB blocks per CU).
+// Shapes with at least 512 tiles are first run in whole-tile rounds, block lb taking tile
+// r*512 + lb in round r, so that the 64 blocks of an XCD work on 64 neighbouring tiles at
+// the same k and share operand panels in that XCD's L2.  The remaining tiles (all tiles of
+// the many shapes here with only a few hundred) are split stream-K style: their
+// (tile, k-tile) iteration space is cut into equal contiguous ranges, one per block.  A
+// block finishes whole tiles with the fused epilogue; a tile shared by several blocks is
+// left as partial accumulators (in fragment order, fully coalesced) that a fix-up kernel
+// adds in k order before running the same epilogue, so the result never depends on
+// timing.  Logical block ids are laid out so that each XCD (blocks are dealt round-robin
+// to the 8 XCDs) owns a contiguous id range, and tiles are ordered 8 tile-rows at a time.
+#include <algorithm>
 #include <string>
 
 #include "common.h"
@@ -41,11 +42,12 @@ namespace gpt2k {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
-constexpr int LDK = BK;       // row stride of a k-contiguous LDS tile [row][k] (16-byte chunks XOR-swizzled)
-constexpr int LDR = BM + 4;   // row stride of a row-contiguous LDS tile [k][row]
+constexpr int BM = 128, BN = 128, BK = 16, NT = 256;
+constexpr int STAGES = 4;                        // LDS ring depth (k-tiles in flight + 1)
+constexpr int OP_FLOATS = BM * BK;               // one operand's k-tile in LDS (8 KB)
+constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse/target slots
 constexpr int GROUP_M = 8;
-constexpr int RESIDENT = 512;              // blocks the chip holds at once (2 per CU)
+constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
 constexpr int SLOT_FLOATS = BM * BN + BM;  // one partial tile + its bias-gradient row sums
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -71,8 +73,12 @@ struct Params {
     const int32_t* tgt; // dlogits operand: per-row target id
     float xscale;       // dlogits operand: d loss / d loss_row (1 / rows)
     int tiles_m, tiles_n, nk;
-    long total;         // tiles * nk iterations
     int G;              // persistent blocks
+    int R;              // whole-tile rounds: block lb takes tiles r*G + lb, r < R
+    int tile0;          // first tile of the split region (R * G)
+    int skt;            // tiles in the split region
+    long total;         // skt * nk iterations of the split region
+    int nr;             // ranges the split region is cut into (<= G), range lb for block lb
 };
 
 GPT2_DEV long range_start(long total, int G, int lb) { return (long)lb * total / G; }
@@ -93,133 +99,6 @@ GPT2_DEV void tile_coords(const Params& p, int tile, int& m0, int& n0) {
     const int in_group = tile - group * group_size;
     m0 = (first_m + in_group % gm) * BM;
     n0 = (in_group / gm) * BN;
-}
-
-// Loads the 128 x 32 slab of an operand whose rows (m or n index) have k contiguous:
-// element (r, k) at X[r*ld + k].  Thread t covers rows t/8 + 32j, k = 4*(t%8)..+3.
-GPT2_DEV void load_kcontig(float4 (&reg)[4], const float* X, long ld, int r0, int nrows, int k0,
-                           int K) {
-    const int t = threadIdx.x;
-    const int kk = k0 + (t & 7) * 4;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int r = r0 + (t >> 3) + 32 * j;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < nrows) {
-            const float* q = X + (long)r * ld + kk;
-            if (kk + 3 < K) {
-                v = *reinterpret_cast<const float4*>(q);
-            } else {
-                if (kk + 0 < K) v.x = q[0];
-                if (kk + 1 < K) v.y = q[1];
-                if (kk + 2 < K) v.z = q[2];
-            }
-        }
-        reg[j] = v;
-    }
-}
-
-GPT2_DEV void store_kcontig(float* S, const float4 (&reg)[4]) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-    {
-        const int row = (t >> 3) + 32 * j;
-        *reinterpret_cast<float4*>(S + row * LDK + (((t & 7) ^ ((row >> 1) & 7)) * 4)) = reg[j];
-    }
-}
-
-// Loads the 32 x 128 slab of an operand whose rows are k and whose row index (m or n)
-// is contiguous: element (r, k) at X[k*ld + r].  Thread t covers k = t/32 + 8j and
-// r = 4*(t%32)..+3.
-GPT2_DEV void load_rcontig(float4 (&reg)[4], const float* X, long ld, int r0, int nrows, int k0,
-                           int K) {
-    const int t = threadIdx.x;
-    const int r = r0 + (t & 31) * 4;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int kk = k0 + (t >> 5) + 8 * j;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (kk < K) {
-            const float* q = X + (long)kk * ld + r;
-            if (r + 3 < nrows) {
-                v = *reinterpret_cast<const float4*>(q);
-            } else {
-                if (r + 0 < nrows) v.x = q[0];
-                if (r + 1 < nrows) v.y = q[1];
-                if (r + 2 < nrows) v.z = q[2];
-            }
-        }
-        reg[j] = v;
-    }
-}
-
-// The logits operand of the LM-head backward: each logit z of row `row` in vocabulary
-// column c becomes d loss / d z = (exp(z - lse[row]) - [c == target[row]]) * scale.
-// Applied to the prefetched registers just before they go to LDS (so the global loads
-// keep their full k-tile of latency hiding); out-of-range elements stay zero.
-GPT2_DEV float dlogit(float z, float lse, int tgt, int c, float scale) {
-    return (__expf(z - lse) - (c == tgt ? 1.0f : 0.0f)) * scale;
-}
-
-// k-contiguous slab (LM-head dgrad): row r = r0 + t/8 + 32j is a logits row; its lse and
-// target are `rl[j]`, `rt[j]`; columns kk.. are vocabulary ids.
-GPT2_DEV void dlogit_kcontig(float4 (&reg)[4], const float (&rl)[4], const int (&rt)[4], int r0, int nrows,
-                             int k0, int K, float scale) {
-    const int t = threadIdx.x;
-    const int kk = k0 + (t & 7) * 4;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        if (r0 + (t >> 3) + 32 * j >= nrows) continue;
-        float4& v = reg[j];
-        if (kk + 0 < K) v.x = dlogit(v.x, rl[j], rt[j], kk + 0, scale);
-        if (kk + 1 < K) v.y = dlogit(v.y, rl[j], rt[j], kk + 1, scale);
-        if (kk + 2 < K) v.z = dlogit(v.z, rl[j], rt[j], kk + 2, scale);
-        if (kk + 3 < K) v.w = dlogit(v.w, rl[j], rt[j], kk + 3, scale);
-    }
-}
-
-// row-contiguous slab (LM-head wgrad): k = k0 + t/32 + 8j is a logits row (lse rl[j],
-// target rt[j]); the row index r.. is the vocabulary id.
-GPT2_DEV void dlogit_rcontig(float4 (&reg)[4], const float (&rl)[4], const int (&rt)[4], int r0, int nrows,
-                             int k0, int K, float scale) {
-    const int t = threadIdx.x;
-    const int r = r0 + (t & 31) * 4;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        if (k0 + (t >> 5) + 8 * j >= K) continue;
-        float4& v = reg[j];
-        if (r + 0 < nrows) v.x = dlogit(v.x, rl[j], rt[j], r + 0, scale);
-        if (r + 1 < nrows) v.y = dlogit(v.y, rl[j], rt[j], r + 1, scale);
-        if (r + 2 < nrows) v.z = dlogit(v.z, rl[j], rt[j], r + 2, scale);
-        if (r + 3 < nrows) v.w = dlogit(v.w, rl[j], rt[j], r + 3, scale);
-    }
-}
-
-GPT2_DEV void store_rcontig(float* S, const float4 (&reg)[4]) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-        *reinterpret_cast<float4*>(S + ((t >> 5) + 8 * j) * LDR + (t & 31) * 4) = reg[j];
-}
-
-// Fragment for k group g: the 4 values lane (i = lane%16, grp = lane/16) feeds to the
-// four MFMA steps, rows rb + i, k = 16g + 4grp + s.
-template <bool KCONTIG>
-GPT2_DEV void read_frag(float (&f)[4], const float* S, int rb, int g) {
-    const int lane = threadIdx.x & 63;
-    const int i = lane & 15, grp = lane >> 4;
-    if (KCONTIG) {
-        const int row = rb + i;
-        float4 v = *reinterpret_cast<const float4*>(S + row * LDK + (((4 * g + grp) ^ ((row >> 1) & 7)) * 4));
-        f[0] = v.x;
-        f[1] = v.y;
-        f[2] = v.z;
-        f[3] = v.w;
-    } else {
-#pragma unroll
-        for (int s = 0; s < 4; s++) f[s] = S[(16 * g + 4 * grp + s) * LDR + rb + i];
-    }
 }
 
 // Fused epilogue on one finished 16x16 block (a, b) of this thread's wave.  16x16
@@ -276,33 +155,169 @@ GPT2_DEV void store_partial(float* slot, const f32x4 (&acc)[4][4]) {
 }
 
 
+
+typedef __attribute__((address_space(3))) float lds_float;
+
+// LDS offset of a pointer into shared memory.
+GPT2_DEV unsigned lds_offset(const float* p) { return (unsigned)(uintptr_t)(const lds_float*)p; }
+
+// Global -> LDS transfers (16 or 4 bytes per lane): lane l's bytes land at lds + l*size,
+// lds being uniform over the wave.  Written as inline asm so that the compiler, which
+// cannot tell these LDS writes apart from the k-tiles being read, does not wait for all
+// of them before every LDS read; the kernel waits for them itself (wait_vm).  M0 holds the
+// LDS base; nothing else in these kernels uses M0.
+GPT2_DEV void dma16(const float* g, float* lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds_offset(lds))), "v"(g) : "memory", "m0");
+}
+GPT2_DEV void dma4(const void* g, float* lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds_offset(lds))), "v"(g) : "memory", "m0");
+}
+
+// LDS layouts of one k-tile (16 k values, 128 rows), both without padding so that a
+// wave's 1 KB transfer is contiguous:
+//  k-contiguous [row][16]: 16-byte chunk c of row r sits at chunk position c ^ ((r>>1)&3)
+//  row-contiguous [k][128]: chunk c (rows 4c..4c+3) of k row kr sits at c ^ rswz(kr)
+GPT2_DEV int kswz(int r) { return (r >> 1) & 3; }
+GPT2_DEV int rswz(int kr) { return ((kr >> 2) & 3) << 2; }
+
+// k-contiguous operand X[r*ld + k]: rows r0.. (clamped to rmax: such rows only feed
+// outputs that are never stored), k = k0..k0+15 (all < K).
+GPT2_DEV void issue_kcontig(float* S, const float* X, long ld, int r0, int rmax, int k0) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int q = j * 4 + w;
+        const int R = q * 16 + (l >> 2);
+        const int c = (l & 3) ^ kswz(R);
+        const int r = min(r0 + R, rmax);
+        dma16(X + (long)r * ld + k0 + 4 * c, S + q * 256);
+    }
+}
+
+// row-contiguous operand X[k*ld + r]: k = k0..k0+15 (clamped to kmax), rows r0..r0+127 in
+// float4 groups clamped to rmax4 (a multiple of 4 inside the row).
+GPT2_DEV void issue_rcontig(float* S, const float* X, long ld, int r0, int rmax4, int k0, int kmax) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int q = j * 4 + w;
+        const int kr = 2 * q + (l >> 5);
+        const int c = (l & 31) ^ rswz(kr);
+        const int r = min(r0 + 4 * c, rmax4);
+        const int k = min(k0 + kr, kmax);
+        dma16(X + (long)k * ld + r, S + q * 256);
+    }
+}
+
+// Bounds-checked k-tile through registers (the last k-tile when K is not a multiple of
+// 16): zero outside the operand, written in the same swizzled layouts.
+GPT2_DEV void fill_kcontig(float* S, const float* X, long ld, int r0, int nrows, int k0, int K) {
+    const int t = threadIdx.x;
+    const int c = t & 3, kk = k0 + 4 * c;
+    float4 v[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int R = (t >> 2) + 64 * j, r = r0 + R;
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < nrows) {
+            const float* q = X + (long)r * ld + kk;
+            if (kk + 0 < K) v[j].x = q[0];
+            if (kk + 1 < K) v[j].y = q[1];
+            if (kk + 2 < K) v[j].z = q[2];
+            if (kk + 3 < K) v[j].w = q[3];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int R = (t >> 2) + 64 * j;
+        *reinterpret_cast<float4*>(S + R * BK + ((c ^ kswz(R)) << 2)) = v[j];
+    }
+}
+
+GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows, int k0, int K) {
+    const int t = threadIdx.x;
+    const int c = t & 31, r = r0 + 4 * c;
+    float4 v[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int kr = (t >> 5) + 8 * j, k = k0 + kr;
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (k < K) {
+            const float* q = X + (long)k * ld + r;
+            if (r + 0 < nrows) v[j].x = q[0];
+            if (r + 1 < nrows) v[j].y = q[1];
+            if (r + 2 < nrows) v[j].z = q[2];
+            if (r + 3 < nrows) v[j].w = q[3];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int kr = (t >> 5) + 8 * j;
+        *reinterpret_cast<float4*>(S + kr * BM + ((c ^ rswz(kr)) << 2)) = v[j];
+    }
+}
+
+// The logits operand of the LM-head backward: each logit z of row `row` in vocabulary
+// column c becomes d loss / d z = (exp(z - lse[row]) - [c == target[row]]) * scale.
+GPT2_DEV float dlogit(float z, float lse, int tgt, int c, float scale) {
+    return (__expf(z - lse) - (c == tgt ? 1.0f : 0.0f)) * scale;
+}
+
+template <int N>
+GPT2_DEV void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
 template <bool A_K, bool B_K, int EPI, bool XF>
 __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
-    constexpr int A_STAGE = A_K ? BM * LDK : BK * LDR;
-    constexpr int B_STAGE = B_K ? BN * LDK : BK * LDR;
-    __shared__ __attribute__((aligned(16))) float smem[2 * (A_STAGE + B_STAGE)];
-    float* As = smem;
-    float* Bs = smem + 2 * A_STAGE;
+    constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
+    constexpr int STAGE_FLOATS = 2 * OP_FLOATS + (XR ? XF_FLOATS : 0);
+    constexpr int LPS = 4 + (XR ? 1 : 0);  // transfers per thread per k-tile
+    __shared__ __attribute__((aligned(1024))) float smem[STAGES * STAGE_FLOATS];
 
     // XCD-aware logical block id: XCD x (= blockIdx % 8) gets a contiguous id range.
     const int nb = gridDim.x;
     const int bid = blockIdx.x;
     const int xcd = bid & 7, local = bid >> 3;
     const int lb = xcd * (nb >> 3) + min(xcd, nb & 7) + local;
-    const long it_begin = range_start(p.total, p.G, lb);
-    const long it_end = range_start(p.total, p.G, lb + 1);
-
-    const int wave = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-    float4 ra[4], rb[4];
+    const int li = lane & 15, grp = lane >> 4;
+    const int kfull = p.K / BK;  // k-tiles that need no bounds check
+    // row clamps: k-contiguous rows to the last row; row-contiguous float4 groups to the
+    // last whole group inside the row (for the logits operand, inside the padded row)
+    const int rmaxA = A_K ? p.M - 1 : (XF ? (int)p.lda - 4 : p.M - 4);
+    const int rmaxB = B_K ? p.N - 1 : p.N - 4;
 
-    for (long it = it_begin; it < it_end;) {
-        const int tile = (int)(it / p.nk);
-        const int ks = (int)(it - (long)tile * p.nk);
-        const int ke = (int)min((long)p.nk, ks + (it_end - it));
+    // Work items: R whole tiles, then this block's range of the split region.
+    long it = 0, it_begin = 0, it_end = 0;
+    if (lb < p.nr) {
+        it_begin = range_start(p.total, p.nr, lb);
+        it_end = range_start(p.total, p.nr, lb + 1);
+    }
+    it = it_begin;
+    for (int r = 0;; r++) {
+        int tile, ks, ke;
+        float* slot = nullptr;
+        if (r < p.R) {
+            tile = r * p.G + lb;
+            ks = 0;
+            ke = p.nk;
+        } else if (it < it_end) {
+            const int t = (int)(it / p.nk);
+            ks = (int)(it - (long)t * p.nk);
+            ke = (int)min((long)p.nk, ks + (it_end - it));
+            // first segment of the range -> slot 0, the range's last (shared) tile -> slot 1
+            slot = p.partial + ((long)lb * 2 + (it == it_begin ? 0 : 1)) * SLOT_FLOATS;
+            tile = p.tile0 + t;
+            it += ke - ks;
+        } else {
+            break;
+        }
         int m0, n0;
         tile_coords(p, tile, m0, n0);
-        const int k_end = min(p.K, ke * BK);
 
         f32x4 acc[4][4];
 #pragma unroll
@@ -310,120 +325,160 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
 #pragma unroll
             for (int b = 0; b < 4; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // wgrad with bias: row sums of A over this segment's k, 4 rows per thread
-        const bool bias_rows = !A_K && p.dbias != nullptr && n0 == 0;
+        // wgrad with bias: the waves of sub-tile column 0 sum their A fragments
+        const bool bias_rows = !A_K && p.dbias != nullptr && n0 == 0 && wn == 0;
         float bsum[4] = {0.f, 0.f, 0.f, 0.f};
 
-        // dlogits operand: lse / target of the logits rows this thread's A slab covers
+        // dlogits as the k-contiguous operand (LM-head dgrad): lse / target of this
+        // lane's four fragment rows
         float xl[4];
         int xt[4];
-        int ra_k0 = 0;
         if (XF && A_K) {
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int r = m0 + (threadIdx.x >> 3) + 32 * j;
-                xl[j] = r < p.M ? p.lse[r] : 0.f;
-                xt[j] = r < p.M ? p.tgt[r] : -1;
+            for (int a = 0; a < 4; a++) {
+                const int r = m0 + wm + 16 * a + li;
+                xl[a] = r < p.M ? p.lse[r] : 0.f;
+                xt[a] = r < p.M ? p.tgt[r] : -1;
             }
         }
 
-        auto load = [&](int k0) {
-            if (A_K) load_kcontig(ra, p.A, p.lda, m0, p.M, k0, k_end);
-            else load_rcontig(ra, p.A, p.lda, m0, p.M, k0, k_end);
-            if (B_K) load_kcontig(rb, p.B, p.ldb, n0, p.N, k0, k_end);
-            else load_rcontig(rb, p.B, p.ldb, n0, p.N, k0, k_end);
-            if (XF && !A_K) {
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int kk = k0 + (threadIdx.x >> 5) + 8 * j;
-                    xl[j] = kk < k_end ? p.lse[kk] : 0.f;
-                    xt[j] = kk < k_end ? p.tgt[kk] : -1;
-                }
+        auto issue = [&](int buf, int kstep) {
+            float* Sa = smem + buf * STAGE_FLOATS;
+            float* Sb = Sa + OP_FLOATS;
+            const int k0 = kstep * BK;
+            if (kstep < kfull) {
+                if (A_K) issue_kcontig(Sa, p.A, p.lda, m0, rmaxA, k0);
+                else issue_rcontig(Sa, p.A, p.lda, m0, rmaxA, k0, p.K - 1);
+                if (B_K) issue_kcontig(Sb, p.B, p.ldb, n0, rmaxB, k0);
+                else issue_rcontig(Sb, p.B, p.ldb, n0, rmaxB, k0, p.K - 1);
+            } else {
+                if (A_K) fill_kcontig(Sa, p.A, p.lda, m0, p.M, k0, p.K);
+                else fill_rcontig(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
+                if (B_K) fill_kcontig(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+                else fill_rcontig(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
             }
-            ra_k0 = k0;
-        };
-        auto store = [&](int stage) {
-            if (XF) {
-                if (A_K) dlogit_kcontig(ra, xl, xt, m0, p.M, ra_k0, k_end, p.xscale);
-                else dlogit_rcontig(ra, xl, xt, m0, p.M, ra_k0, k_end, p.xscale);
+            if (XR) {
+                // lanes 0-15: lse of k rows k0.., lanes 16-31: their targets (copied as bits)
+                const int kk = min(k0 + (lane & 15), p.K - 1);
+                const void* src = (lane & 16) ? (const void*)(p.tgt + kk) : (const void*)(p.lse + kk);
+                dma4(src, Sb + OP_FLOATS + wave * 64);
             }
-            if (!A_K && bias_rows) {
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    bsum[0] += ra[j].x;
-                    bsum[1] += ra[j].y;
-                    bsum[2] += ra[j].z;
-                    bsum[3] += ra[j].w;
-                }
-            }
-            if (A_K) store_kcontig(As + stage * A_STAGE, ra);
-            else store_rcontig(As + stage * A_STAGE, ra);
-            if (B_K) store_kcontig(Bs + stage * B_STAGE, rb);
-            else store_rcontig(Bs + stage * B_STAGE, rb);
         };
 
-        load(ks * BK);
-        store(0);
-        __syncthreads();
-        const int n = ke - ks;
-        for (int kt = 0; kt < n; kt++) {
-            const int cur = kt & 1;
-            if (kt + 1 < n) load((ks + kt + 1) * BK);
-            const float* Acur = As + cur * A_STAGE;
-            const float* Bcur = Bs + cur * B_STAGE;
-            // both 16-k groups' fragments are read before the first MFMA
-            float fa[BK / 16][4][4], fb[BK / 16][4][4];
+        auto compute = [&](int buf, int kstep) {
+            const float* Sa = smem + buf * STAGE_FLOATS;
+            const float* Sb = Sa + OP_FLOATS;
+            const int k0 = kstep * BK;
+            float fa[4][4], fb[4][4];
 #pragma unroll
-            for (int g = 0; g < BK / 16; g++) {
+            for (int a = 0; a < 4; a++) {
+                const int row = wm + 16 * a + li;
+                if (A_K) {
+                    const float4 v = *reinterpret_cast<const float4*>(Sa + row * BK + ((grp ^ kswz(row)) << 2));
+                    fa[a][0] = v.x;
+                    fa[a][1] = v.y;
+                    fa[a][2] = v.z;
+                    fa[a][3] = v.w;
+                } else {
 #pragma unroll
-                for (int a = 0; a < 4; a++) read_frag<A_K>(fa[g][a], Acur, wm + 16 * a, g);
-#pragma unroll
-                for (int b = 0; b < 4; b++) read_frag<B_K>(fb[g][b], Bcur, wn + 16 * b, g);
-            }
-#pragma unroll
-            for (int g = 0; g < BK / 16; g++)
-#pragma unroll
-                for (int s = 0; s < 4; s++)
-#pragma unroll
-                    for (int a = 0; a < 4; a++)
-#pragma unroll
-                        for (int b = 0; b < 4; b++)
-                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[g][a][s], fb[g][b][s], acc[a][b], 0, 0, 0);
-            if (kt + 1 < n) store(cur ^ 1);
-            __syncthreads();
-        }
-
-        const bool full = ks == 0 && ke == p.nk;
-        // first segment of the range -> slot 0, the range's last (shared) tile -> slot 1
-        float* slot = p.partial + ((long)lb * 2 + (it == it_begin ? 0 : 1)) * SLOT_FLOATS;
-        if (bias_rows) {
-            // combine the 8 threads that share rows (t%32), in k-group order; the LDS
-            // operand buffers are free after the loop's final barrier
-            float* red = As;
-#pragma unroll
-            for (int e = 0; e < 4; e++) red[threadIdx.x * 4 + e] = bsum[e];
-            __syncthreads();
-            if (threadIdx.x < 32) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    float s = 0.f;
-                    for (int g8 = 0; g8 < 8; g8++) s += red[(g8 * 32 + threadIdx.x) * 4 + e];
-                    const int m = m0 + 4 * threadIdx.x + e;
-                    if (full) {
-                        if (m < p.M) p.dbias[m] += s;
-                    } else {
-                        slot[BM * BN + 4 * threadIdx.x + e] = s;
+                    for (int s = 0; s < 4; s++) {
+                        const int kr = 4 * grp + s;
+                        fa[a][s] = Sa[kr * BM + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
                     }
                 }
             }
-            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const int row = wn + 16 * b + li;
+                if (B_K) {
+                    const float4 v = *reinterpret_cast<const float4*>(Sb + row * BK + ((grp ^ kswz(row)) << 2));
+                    fb[b][0] = v.x;
+                    fb[b][1] = v.y;
+                    fb[b][2] = v.z;
+                    fb[b][3] = v.w;
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 4; s++) {
+                        const int kr = 4 * grp + s;
+                        fb[b][s] = Sb[kr * BN + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                    }
+                }
+            }
+            // dlogits: no bounds checks needed, since B is zero for k >= K (the bounds-checked
+            // k-tile) and rows m >= M only feed outputs that are never stored
+            if (XF && A_K) {
+#pragma unroll
+                for (int a = 0; a < 4; a++)
+#pragma unroll
+                    for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], xl[a], xt[a], k0 + 4 * grp + s, p.xscale);
+            }
+            if (XR) {
+                const float* xs = Sb + OP_FLOATS + wave * 64;
+                const float4 l4 = *reinterpret_cast<const float4*>(xs + 4 * grp);
+                const float4 t4 = *reinterpret_cast<const float4*>(xs + 16 + 4 * grp);
+                const float ls[4] = {l4.x, l4.y, l4.z, l4.w};
+                const int ts[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
+#pragma unroll
+                for (int a = 0; a < 4; a++) {
+                    const int m = m0 + wm + 16 * a + li;
+#pragma unroll
+                    for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], ls[s], ts[s], m, p.xscale);
+                }
+            }
+            if (!A_K && bias_rows) {
+#pragma unroll
+                for (int a = 0; a < 4; a++) bsum[a] += (fa[a][0] + fa[a][1]) + (fa[a][2] + fa[a][3]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+#pragma unroll
+                for (int a = 0; a < 4; a++)
+#pragma unroll
+                    for (int b = 0; b < 4; b++)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
+        };
+
+        // LDS ring: k-tile kt lives in buffer kt % STAGES; STAGES-1 tiles are in flight
+        // while one is consumed.  Each thread waits for its own transfers of tile kt, and
+        // the barrier then makes every thread's transfers visible (and retires all reads
+        // of the buffer the next transfer overwrites).
+        const int n = ke - ks;
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; s++)
+            if (s < n) issue(s, ks + s);
+        for (int kt = 0; kt < n; kt++) {
+            if (kt + STAGES - 2 < n) wait_vm<(STAGES - 2) * LPS>();
+            else wait_vm<0>();
+            __builtin_amdgcn_s_barrier();
+            if (kt + STAGES - 1 < n) issue((kt + STAGES - 1) % STAGES, ks + kt + STAGES - 1);
+            compute(kt % STAGES, ks + kt);
+        }
+        wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+
+        const bool full = ks == 0 && ke == p.nk;
+        if (bias_rows) {
+            // add the four lane groups (k offsets) of each row
+#pragma unroll
+            for (int a = 0; a < 4; a++) {
+                float s = bsum[a];
+                s += __shfl_xor(s, 16, 64);
+                s += __shfl_xor(s, 32, 64);
+                const int r = wm + 16 * a + li;
+                if (grp == 0) {
+                    if (full) {
+                        if (m0 + r < p.M) p.dbias[m0 + r] += s;
+                    } else {
+                        slot[BM * BN + r] = s;
+                    }
+                }
+            }
         }
         if (full) {
             epilogue<EPI>(p, acc, m0, n0);
         } else {
             store_partial(slot, acc);
         }
-        it += ke - ks;
     }
 }
 
@@ -434,21 +489,21 @@ template <int EPI>
 __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
     const int quarter = blockIdx.x & 3;
     const int lbb = (blockIdx.x >> 2) + 1;  // boundary between blocks lbb-1 and lbb
-    const long x = range_start(p.total, p.G, lbb);
+    const long x = range_start(p.total, p.nr, lbb);
     if (x % p.nk == 0) return;
     const int tile = (int)(x / p.nk);
     if (lbb >= 2) {
-        const long xp = range_start(p.total, p.G, lbb - 1);
+        const long xp = range_start(p.total, p.nr, lbb - 1);
         if (xp / p.nk == tile && xp % p.nk != 0) return;
     }
     const long t0 = (long)tile * p.nk;
-    const int first = owner(p.total, p.G, t0);
-    const int last = owner(p.total, p.G, t0 + p.nk - 1);
+    const int first = owner(p.total, p.nr, t0);
+    const int last = owner(p.total, p.nr, t0 + p.nk - 1);
     f32x4 acc[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int l = first; l <= last; l++) {
-        const int which = range_start(p.total, p.G, l) / p.nk == tile ? 0 : 1;
+        const int which = range_start(p.total, p.nr, l) / p.nk == tile ? 0 : 1;
         const float* slot = p.partial + ((long)l * 2 + which) * SLOT_FLOATS + quarter * 16 * NT + threadIdx.x;
         float v[16];
 #pragma unroll
@@ -457,13 +512,13 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
         for (int e = 0; e < 16; e++) acc[e >> 2][e & 3] += v[e];
     }
     int m0, n0;
-    tile_coords(p, tile, m0, n0);
+    tile_coords(p, p.tile0 + tile, m0, n0);
 #pragma unroll
     for (int b = 0; b < 4; b++) epilogue_block<EPI>(p, acc[b], m0, n0, quarter, b);
     if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
         float s = 0.f;
         for (int l = first; l <= last; l++) {
-            const int which = range_start(p.total, p.G, l) / p.nk == tile ? 0 : 1;
+            const int which = range_start(p.total, p.nr, l) / p.nk == tile ? 0 : 1;
             s += p.partial[((long)l * 2 + which) * SLOT_FLOATS + BM * BN + threadIdx.x];
         }
         p.dbias[m0 + threadIdx.x] += s;
@@ -485,6 +540,31 @@ const char* fixup_name() {
     return s.c_str();
 }
 
+// Work distribution over a persistent grid of up to RESIDENT blocks: whole-tile rounds
+// while at least RESIDENT tiles remain, then equal ranges of the rest.
+void schedule(Params& p, long tiles) {
+    p.R = 0;
+    p.tile0 = 0;
+    if (p.partial == nullptr) {  // nowhere to put partial tiles: one tile per block
+        p.G = (int)tiles;
+        p.R = 1;
+        p.tile0 = (int)tiles;
+        p.skt = 0;
+        p.total = 0;
+        p.nr = 0;
+        return;
+    }
+    if (tiles >= RESIDENT) {
+        p.G = RESIDENT;
+        p.R = (int)(tiles / RESIDENT);
+        p.tile0 = p.R * RESIDENT;
+    }
+    p.skt = (int)(tiles - p.tile0);
+    p.total = (long)p.skt * p.nk;
+    p.nr = (int)std::min<long>(RESIDENT, p.total);
+    if (p.R == 0) p.G = p.nr;
+}
+
 template <bool A_K, bool B_K, int EPI, bool XF = false>
 hipError_t launch(Params& p, hipStream_t st) {
     p.tiles_m = (p.M + BM - 1) / BM;
@@ -496,10 +576,7 @@ hipError_t launch(Params& p, hipStream_t st) {
         // empty reduction: every output is the epilogue of 0
         p.nk = 1;
     }
-    p.total = tiles * p.nk;
-    // Many tiles: one tile per block.  Otherwise stream-K over the resident blocks.
-    const bool sk = tiles < 8L * RESIDENT && p.partial != nullptr;
-    p.G = sk ? (int)std::min<long>(RESIDENT, p.total) : (int)tiles;
+    schedule(p, tiles);
     const double mn = (double)p.M * p.N;
     const double extra = (EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_BIAS_GELU) ? mn : 0.0;
     {
@@ -508,10 +585,9 @@ hipError_t launch(Params& p, hipStream_t st) {
                      4.0 * ((double)p.M * p.K + (double)p.N * p.K + mn + extra));
         hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF>), dim3(p.G), dim3(NT), 0, st, p);
     }
-    const bool aligned_ranges = p.total % p.G == 0 && (p.total / p.G) % p.nk == 0;
-    if (sk && !aligned_ranges && p.G > 1) {
-        ProfScope ps(st, fixup_name<EPI>(), 0.0, 4.0 * (2.0 * p.G * SLOT_FLOATS + extra));
-        hipLaunchKernelGGL((gemm_fixup_kernel<EPI>), dim3(4 * (p.G - 1)), dim3(NT), 0, st, p);
+    if (p.nr > 1 && !(p.total % p.nr == 0 && (p.total / p.nr) % p.nk == 0)) {
+        ProfScope ps(st, fixup_name<EPI>(), 0.0, 4.0 * (2.0 * p.nr * SLOT_FLOATS + extra));
+        hipLaunchKernelGGL((gemm_fixup_kernel<EPI>), dim3(4 * (p.nr - 1)), dim3(NT), 0, st, p);
     }
     return hipGetLastError();
 }
@@ -583,7 +659,10 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
 
 hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout, const float* inp, int M,
                         int N, int K, float* partial, hipStream_t st, const XentOperand* xent) {
-    if (ld_dout % 4 || N % 4 || !aligned16(dout) || !aligned16(inp)) return hipErrorInvalidValue;
+    // row-contiguous operands move in 16-byte groups: dout's row groups must stay inside
+    // its M columns (or, for the logits operand, inside its padded row)
+    if (ld_dout % 4 || N % 4 || ld_dout < M || (!xent && M % 4) || !aligned16(dout) || !aligned16(inp))
+        return hipErrorInvalidValue;
     Params p{};
     p.M = M;
     p.N = N;

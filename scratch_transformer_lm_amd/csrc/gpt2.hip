@@ -122,7 +122,6 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     y.enc_work = take(1 + BT);
     size_t np = gemm_partial_floats();
     np = std::max(np, layernorm_partial_floats((int)BT, (int)C));
-    np = std::max(np, colsum_partial_floats((int)BT, (int)(4 * C)));
     y.n_partial = np;
     y.partial = take(np);
     y.n_scratch = s;

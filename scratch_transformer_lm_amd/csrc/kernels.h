@@ -10,8 +10,9 @@
 namespace gpt2k {
 
 // ---- linear layers (gemm.hip) -------------------------------------------------------
-// `partial` is a scratch of gemm_partial_floats() floats for stream-K partial tiles
-// (nullptr: one tile per block, no sharing of tiles).
+// `partial` is a scratch of gemm_partial_floats() floats for split partial tiles
+// (nullptr: one tile per block, no sharing of tiles).  Operands must be 16-byte aligned
+// with leading dimensions that are multiples of 4 floats.
 size_t gemm_partial_floats();
 // out[M,N] (ld ldo) = inp[M,K] . w[N,K]^T, then by the non-null extras:
 //   bias: + bias[n];  resid: out = resid + (...) (resid has ld ldo);
@@ -20,7 +21,8 @@ hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
                           float* partial, hipStream_t st);
 // Marks a `dout` operand as logits whose gradient is formed while loading:
-// dlogit = (exp(z - lse[row]) - [col == targets[row]]) * scale.
+// dlogit = (exp(z - lse[row]) - [col == targets[row]]) * scale.  The logits' padding
+// columns (up to the leading dimension) must be readable; their values are not used.
 struct XentOperand {
     const float* lse;
     const int32_t* targets;
@@ -31,16 +33,9 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
                         const float* gelu_pre, int M, int N, int K, float* partial, hipStream_t st,
                         const XentOperand* xent = nullptr);
 // dw[M,N] += dout[K,M]^T (dout ld ld_dout) . inp[K,N]; dbias (optional) += column sums of
-// dout over its K rows.
+// dout over its K rows.  M must be a multiple of 4 unless dout is a logits operand.
 hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout, const float* inp, int M,
                         int N, int K, float* partial, hipStream_t st, const XentOperand* xent = nullptr);
-
-// ---- column sums (bias gradients) (norm.hip) ------------------------------------------
-// db[n] += sum_m x[m, n] over M rows (row stride ld); deterministic two-phase reduction
-// through `partial` (colsum_partial_floats(M, N) floats).
-size_t colsum_partial_floats(int M, int N);
-hipError_t colsum_accumulate(float* db, const float* x, long ld, int M, int N, float* partial,
-                             hipStream_t st);
 
 // ---- LayerNorm (norm.hip) -----------------------------------------------------------
 hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,

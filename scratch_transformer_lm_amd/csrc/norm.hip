@@ -1,10 +1,10 @@
-// LayerNorm forward/backward and column sums (bias gradients) for gfx950.
+// LayerNorm forward/backward for gfx950.
 //
 // LayerNorm is the pages' worked example of a hand-written layer ("OpenAI创始大神手搓
 // 千行C代码训练GPT", 手动实现每个层前向 / 反向传播; 新智元 article, 教程).  Both
 // directions are HBM-bound: one wave64 owns a row, holds it in registers as float4s,
 // and reduces with cross-lane shuffles; nothing is re-read from memory.  The
-// cross-row sums (dgamma, dbeta, bias gradients) go through per-block partial rows that a
+// cross-row sums (dgamma, dbeta) go through per-block partial rows that a
 // second kernel adds in a fixed order, so results are deterministic.
 #include "common.h"
 #include "kernels.h"
@@ -16,7 +16,6 @@ namespace {
 
 constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
 constexpr int LN_MAX_BLOCKS = 512;
-constexpr int COLSUM_ROWS = 32;
 
 template <int VPL>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, float* __restrict__ mean,
@@ -198,27 +197,7 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(float* out_lo, float* 
     }
 }
 
-// part[chunk][n] = sum over the chunk's rows of x[m][n]; 4 columns per thread.
-__global__ __launch_bounds__(256) void colsum_partial_kernel(float* __restrict__ part, const float* __restrict__ x,
-                                                             long ld, int M, int N) {
-    const int c4 = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c4 * 4 >= N) return;
-    const int r0 = blockIdx.y * COLSUM_ROWS;
-    const int r1 = min(M, r0 + COLSUM_ROWS);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int r = r0; r < r1; r++) {
-        const float4 v = *reinterpret_cast<const float4*>(x + (long)r * ld + c4 * 4);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
-    }
-    *reinterpret_cast<float4*>(part + (long)blockIdx.y * N + c4 * 4) = acc;
-}
-
 int ln_blocks(int N) { return std::min((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, LN_MAX_BLOCKS); }
-
-int colsum_chunks(int M) { return (M + COLSUM_ROWS - 1) / COLSUM_ROWS; }
 
 }  // namespace
 
@@ -279,25 +258,6 @@ hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, 
     ProfScope ps2(st, "reduce_rows_kernel", 0.0, 4.0 * ((double)G * 2 * C + 2.0 * C * (accumulate_dwdb ? 2 : 1)));
     hipLaunchKernelGGL(reduce_rows_kernel, dim3((2 * C + 63) / 64), dim3(256), 0, st, dw, db, C,
                        (const float*)partial, G, 2 * C, (int)accumulate_dwdb);
-    return hipGetLastError();
-}
-
-size_t colsum_partial_floats(int M, int N) { return (size_t)colsum_chunks(M) * N; }
-
-hipError_t colsum_accumulate(float* db, const float* x, long ld, int M, int N, float* partial,
-                             hipStream_t st) {
-    if (N % 4 || ld % 4 || M <= 0) return M == 0 ? hipSuccess : hipErrorInvalidValue;
-    const int chunks = colsum_chunks(M);
-    dim3 grid((N / 4 + 255) / 256, chunks);
-    {
-        ProfScope ps(st, "colsum_partial_kernel", 0.0, 4.0 * ((double)M * N + (double)chunks * N));
-        hipLaunchKernelGGL(colsum_partial_kernel, grid, dim3(256), 0, st, partial, x, ld, M, N);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    ProfScope ps(st, "reduce_rows_kernel", 0.0, 4.0 * ((double)chunks * N + 2.0 * N));
-    hipLaunchKernelGGL(reduce_rows_kernel, dim3((N + 63) / 64), dim3(256), 0, st, db, db, N,
-                       (const float*)partial, chunks, N, 1);
     return hipGetLastError();
 }
 
