@@ -33,8 +33,8 @@ constexpr float GELU_K0 = 0.7978845608028654f;  // sqrt(2/pi)
 constexpr float GELU_K1 = 0.044715f;
 
 // tanh z = 1 - 2 / (e^{2z} + 1), with e^x and 1/x on the hardware transcendental unit
-// (a few ulp; e^{2z} overflowing to +inf still gives exactly 1).
-GPT2_DEV float tanh_fast(float z) { return 1.0f - 2.0f * __frcp_rn(__expf(2.0f * z) + 1.0f); }
+// (v_exp_f32, v_rcp_f32: a few ulp; e^{2z} overflowing to +inf still gives exactly 1).
+GPT2_DEV float tanh_fast(float z) { return 1.0f - 2.0f * __builtin_amdgcn_rcpf(__expf(2.0f * z) + 1.0f); }
 
 GPT2_DEV float gelu_f(float u) {
     float z = GELU_K0 * (u + GELU_K1 * u * u * u);

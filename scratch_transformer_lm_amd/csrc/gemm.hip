@@ -101,46 +101,84 @@ GPT2_DEV void tile_coords(const Params& p, int tile, int& m0, int& n0) {
     n0 = (in_group / gm) * BN;
 }
 
-// Fused epilogue on one finished 16x16 block (a, b) of this thread's wave.  16x16
-// accumulator layout: lane holds column lane%16 and, in register v, row 4*(lane/16) + v.
-template <int EPI>
-GPT2_DEV void epilogue_block(const Params& p, const f32x4& acc, int m0, int n0, int a, int b) {
+// Fused epilogue on NA rows of finished 16x16 blocks (a = a0 .. a0+NA-1, b = 0..3) of
+// this thread's wave.  16x16 accumulator layout: lane holds column lane%16 and, in
+// register v, row 4*(lane/16) + v.  One row of blocks at a time: the values the epilogue
+// reads for the next row (residual, pre-activation, old C) are requested before this
+// row's outputs are stored, and a row's 16 (or 32) stores go out back to back, so the
+// memory operations overlap instead of each waiting for the one before.  CHECK: the tile
+// crosses the edge of C, so rows and columns are bounds-checked.
+template <int EPI, int NA, bool CHECK>
+GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, int a0) {
+    constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
+    constexpr bool READS = EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-    const int col = n0 + wn + 16 * b + (lane & 15), grp = lane >> 4;
-    if (col >= p.N) return;
-    float bias_v = 0.f;
-    if (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) bias_v = p.bias ? p.bias[col] : 0.f;
+    const int grp = lane >> 4;
+    const float* src = EPI == EPI_ACCUM ? p.C : p.aux;
+    const long lds = EPI == EPI_ACCUM ? p.ldc : p.ldaux;
+    // this lane's element (i, b, v) is at row r0 + 16 i + v, column c0 + 16 b
+    const int r0 = m0 + wm + 16 * a0 + 4 * grp, c0 = n0 + wn + (lane & 15);
+    auto inside = [&](int i, int b, int v) { return !CHECK || (r0 + 16 * i + v < p.M && c0 + 16 * b < p.N); };
+    float bias_v[4];
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-        const int row = m0 + wm + 16 * a + 4 * grp + v;
-        if (row >= p.M) continue;
-        const float x = acc[v];
-        float* c = p.C + (long)row * p.ldc + col;
-        if (EPI == EPI_STORE) {
-            *c = x;
-        } else if (EPI == EPI_BIAS) {
-            *c = x + bias_v;
-        } else if (EPI == EPI_BIAS_RESID) {
-            *c = p.aux[(long)row * p.ldaux + col] + (x + bias_v);
-        } else if (EPI == EPI_BIAS_GELU) {
-            const float u = x + bias_v;
-            p.pre[(long)row * p.ldpre + col] = u;
-            *c = gelu_f(u);
-        } else if (EPI == EPI_ACCUM) {
-            *c += x;
-        } else {  // EPI_GELU_BWD
-            *c = x * gelu_grad_f(p.aux[(long)row * p.ldaux + col]);
+    for (int b = 0; b < 4; b++) {
+        bias_v[b] = 0.f;
+        if (HAS_BIAS && p.bias && (!CHECK || c0 + 16 * b < p.N)) bias_v[b] = p.bias[c0 + 16 * b];
+    }
+    auto load_row = [&](float (&in)[4][4], int i) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const float* q = src + (long)(r0 + 16 * i + v) * lds + c0;
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                in[b][v] = 0.f;
+                if (READS && inside(i, b, v)) in[b][v] = q[16 * b];
+            }
         }
+    };
+    auto store_row = [&](const float (&o)[4][4], float* dst, long ld, int i) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            float* q = dst + (long)(r0 + 16 * i + v) * ld + c0;
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+                if (inside(i, b, v)) q[16 * b] = o[b][v];
+        }
+    };
+    float in[2][4][4];
+    if (READS) load_row(in[0], 0);
+#pragma unroll
+    for (int i = 0; i < NA; i++) {
+        float (&cur)[4][4] = in[i & 1];
+        if (READS && i + 1 < NA) load_row(in[(i + 1) & 1], i + 1);
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const float x = acc[i * 4 + b][v];
+                float& o = cur[b][v];
+                if (EPI == EPI_STORE) o = x;
+                else if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) o = x + bias_v[b];
+                else if (EPI == EPI_BIAS_RESID) o = o + (x + bias_v[b]);
+                else if (EPI == EPI_ACCUM) o = o + x;
+                else o = x * gelu_grad_f(o);  // EPI_GELU_BWD
+            }
+        if (EPI == EPI_BIAS_GELU) {
+            store_row(cur, p.pre, p.ldpre, i);  // the pre-activation, then its GELU
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) cur[b][v] = gelu_f(cur[b][v]);
+        }
+        store_row(cur, p.C, p.ldc, i);
     }
 }
 
-template <int EPI>
-GPT2_DEV void epilogue(const Params& p, const f32x4 (&acc)[4][4], int m0, int n0) {
-#pragma unroll
-    for (int a = 0; a < 4; a++)
-#pragma unroll
-        for (int b = 0; b < 4; b++) epilogue_block<EPI>(p, acc[a][b], m0, n0, a, b);
+template <int EPI, int NA>
+GPT2_DEV void epilogue_rows(const Params& p, const f32x4* acc, int m0, int n0, int a0) {
+    if (m0 + BM <= p.M && n0 + BN <= p.N) epilogue_rows_<EPI, NA, false>(p, acc, m0, n0, a0);
+    else epilogue_rows_<EPI, NA, true>(p, acc, m0, n0, a0);
 }
 
 // Partial tile in fragment order: thread t's 64 accumulators at slot[(j*256 + t)],
@@ -298,27 +336,67 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
         it_end = range_start(p.total, p.nr, lb + 1);
     }
     it = it_begin;
-    for (int r = 0;; r++) {
-        int tile, ks, ke;
-        float* slot = nullptr;
+    int r = 0;
+    struct Item {
+        int tile, ks, ke, m0, n0;
+        float* slot;  // partial-tile slot (split tiles only)
+    };
+    auto next_item = [&](Item& w) -> bool {
+        w.slot = nullptr;
         if (r < p.R) {
-            tile = r * p.G + lb;
-            ks = 0;
-            ke = p.nk;
+            w.tile = r * p.G + lb;
+            w.ks = 0;
+            w.ke = p.nk;
+            r++;
         } else if (it < it_end) {
             const int t = (int)(it / p.nk);
-            ks = (int)(it - (long)t * p.nk);
-            ke = (int)min((long)p.nk, ks + (it_end - it));
+            w.ks = (int)(it - (long)t * p.nk);
+            w.ke = (int)min((long)p.nk, w.ks + (it_end - it));
             // first segment of the range -> slot 0, the range's last (shared) tile -> slot 1
-            slot = p.partial + ((long)lb * 2 + (it == it_begin ? 0 : 1)) * SLOT_FLOATS;
-            tile = p.tile0 + t;
-            it += ke - ks;
+            w.slot = p.partial + ((long)lb * 2 + (it == it_begin ? 0 : 1)) * SLOT_FLOATS;
+            w.tile = p.tile0 + t;
+            it += w.ke - w.ks;
         } else {
-            break;
+            return false;
         }
-        int m0, n0;
-        tile_coords(p, tile, m0, n0);
+        tile_coords(p, w.tile, w.m0, w.n0);
+        return true;
+    };
 
+    auto issue = [&](int buf, int kstep, int m0, int n0) {
+        float* Sa = smem + buf * STAGE_FLOATS;
+        float* Sb = Sa + OP_FLOATS;
+        const int k0 = kstep * BK;
+        if (kstep < kfull) {
+            if (A_K) issue_kcontig(Sa, p.A, p.lda, m0, rmaxA, k0);
+            else issue_rcontig(Sa, p.A, p.lda, m0, rmaxA, k0, p.K - 1);
+            if (B_K) issue_kcontig(Sb, p.B, p.ldb, n0, rmaxB, k0);
+            else issue_rcontig(Sb, p.B, p.ldb, n0, rmaxB, k0, p.K - 1);
+        } else {
+            if (A_K) fill_kcontig(Sa, p.A, p.lda, m0, p.M, k0, p.K);
+            else fill_rcontig(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
+            if (B_K) fill_kcontig(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+            else fill_rcontig(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+        }
+        if (XR) {
+            // lanes 0-15: lse of k rows k0.., lanes 16-31: their targets (copied as bits)
+            const int kk = min(k0 + (lane & 15), p.K - 1);
+            const void* src = (lane & 16) ? (const void*)(p.tgt + kk) : (const void*)(p.lse + kk);
+            dma4(src, Sb + OP_FLOATS + wave * 64);
+        }
+    };
+    // the first STAGES-1 k-tiles of an item
+    auto prologue = [&](const Item& w) {
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; s++)
+            if (s < w.ke - w.ks) issue(s, w.ks + s, w.m0, w.n0);
+    };
+
+    Item cur;
+    bool have = next_item(cur);
+    if (have) prologue(cur);
+    while (have) {
+        const int m0 = cur.m0, n0 = cur.n0, ks = cur.ks, ke = cur.ke;
         f32x4 acc[4][4];
 #pragma unroll
         for (int a = 0; a < 4; a++)
@@ -336,125 +414,107 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
         if (XF && A_K) {
 #pragma unroll
             for (int a = 0; a < 4; a++) {
-                const int r = m0 + wm + 16 * a + li;
-                xl[a] = r < p.M ? p.lse[r] : 0.f;
-                xt[a] = r < p.M ? p.tgt[r] : -1;
+                const int row = m0 + wm + 16 * a + li;
+                xl[a] = row < p.M ? p.lse[row] : 0.f;
+                xt[a] = row < p.M ? p.tgt[row] : -1;
             }
         }
 
-        auto issue = [&](int buf, int kstep) {
-            float* Sa = smem + buf * STAGE_FLOATS;
-            float* Sb = Sa + OP_FLOATS;
-            const int k0 = kstep * BK;
-            if (kstep < kfull) {
-                if (A_K) issue_kcontig(Sa, p.A, p.lda, m0, rmaxA, k0);
-                else issue_rcontig(Sa, p.A, p.lda, m0, rmaxA, k0, p.K - 1);
-                if (B_K) issue_kcontig(Sb, p.B, p.ldb, n0, rmaxB, k0);
-                else issue_rcontig(Sb, p.B, p.ldb, n0, rmaxB, k0, p.K - 1);
+    auto compute = [&](int buf, int kstep) {
+        const float* Sa = smem + buf * STAGE_FLOATS;
+        const float* Sb = Sa + OP_FLOATS;
+        const int k0 = kstep * BK;
+        float fa[4][4], fb[4][4];
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+            const int row = wm + 16 * a + li;
+            if (A_K) {
+                const float4 v = *reinterpret_cast<const float4*>(Sa + row * BK + ((grp ^ kswz(row)) << 2));
+                fa[a][0] = v.x;
+                fa[a][1] = v.y;
+                fa[a][2] = v.z;
+                fa[a][3] = v.w;
             } else {
-                if (A_K) fill_kcontig(Sa, p.A, p.lda, m0, p.M, k0, p.K);
-                else fill_rcontig(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
-                if (B_K) fill_kcontig(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
-                else fill_rcontig(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    const int kr = 4 * grp + s;
+                    fa[a][s] = Sa[kr * BM + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                }
             }
-            if (XR) {
-                // lanes 0-15: lse of k rows k0.., lanes 16-31: their targets (copied as bits)
-                const int kk = min(k0 + (lane & 15), p.K - 1);
-                const void* src = (lane & 16) ? (const void*)(p.tgt + kk) : (const void*)(p.lse + kk);
-                dma4(src, Sb + OP_FLOATS + wave * 64);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int row = wn + 16 * b + li;
+            if (B_K) {
+                const float4 v = *reinterpret_cast<const float4*>(Sb + row * BK + ((grp ^ kswz(row)) << 2));
+                fb[b][0] = v.x;
+                fb[b][1] = v.y;
+                fb[b][2] = v.z;
+                fb[b][3] = v.w;
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    const int kr = 4 * grp + s;
+                    fb[b][s] = Sb[kr * BN + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                }
             }
-        };
-
-        auto compute = [&](int buf, int kstep) {
-            const float* Sa = smem + buf * STAGE_FLOATS;
-            const float* Sb = Sa + OP_FLOATS;
-            const int k0 = kstep * BK;
-            float fa[4][4], fb[4][4];
+        }
+        // dlogits: no bounds checks needed, since B is zero for k >= K (the bounds-checked
+        // k-tile) and rows m >= M only feed outputs that are never stored
+        if (XF && A_K) {
+#pragma unroll
+            for (int a = 0; a < 4; a++)
+#pragma unroll
+                for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], xl[a], xt[a], k0 + 4 * grp + s, p.xscale);
+        }
+        if (XR) {
+            const float* xs = Sb + OP_FLOATS + wave * 64;
+            const float4 l4 = *reinterpret_cast<const float4*>(xs + 4 * grp);
+            const float4 t4 = *reinterpret_cast<const float4*>(xs + 16 + 4 * grp);
+            const float ls[4] = {l4.x, l4.y, l4.z, l4.w};
+            const int ts[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
 #pragma unroll
             for (int a = 0; a < 4; a++) {
-                const int row = wm + 16 * a + li;
-                if (A_K) {
-                    const float4 v = *reinterpret_cast<const float4*>(Sa + row * BK + ((grp ^ kswz(row)) << 2));
-                    fa[a][0] = v.x;
-                    fa[a][1] = v.y;
-                    fa[a][2] = v.z;
-                    fa[a][3] = v.w;
-                } else {
+                const int m = m0 + wm + 16 * a + li;
 #pragma unroll
-                    for (int s = 0; s < 4; s++) {
-                        const int kr = 4 * grp + s;
-                        fa[a][s] = Sa[kr * BM + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
-                    }
-                }
+                for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], ls[s], ts[s], m, p.xscale);
             }
+        }
+        if (!A_K && bias_rows) {
 #pragma unroll
-            for (int b = 0; b < 4; b++) {
-                const int row = wn + 16 * b + li;
-                if (B_K) {
-                    const float4 v = *reinterpret_cast<const float4*>(Sb + row * BK + ((grp ^ kswz(row)) << 2));
-                    fb[b][0] = v.x;
-                    fb[b][1] = v.y;
-                    fb[b][2] = v.z;
-                    fb[b][3] = v.w;
-                } else {
+            for (int a = 0; a < 4; a++) bsum[a] += (fa[a][0] + fa[a][1]) + (fa[a][2] + fa[a][3]);
+        }
 #pragma unroll
-                    for (int s = 0; s < 4; s++) {
-                        const int kr = 4 * grp + s;
-                        fb[b][s] = Sb[kr * BN + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
-                    }
-                }
-            }
-            // dlogits: no bounds checks needed, since B is zero for k >= K (the bounds-checked
-            // k-tile) and rows m >= M only feed outputs that are never stored
-            if (XF && A_K) {
+        for (int s = 0; s < 4; s++)
 #pragma unroll
-                for (int a = 0; a < 4; a++)
+            for (int a = 0; a < 4; a++)
 #pragma unroll
-                    for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], xl[a], xt[a], k0 + 4 * grp + s, p.xscale);
-            }
-            if (XR) {
-                const float* xs = Sb + OP_FLOATS + wave * 64;
-                const float4 l4 = *reinterpret_cast<const float4*>(xs + 4 * grp);
-                const float4 t4 = *reinterpret_cast<const float4*>(xs + 16 + 4 * grp);
-                const float ls[4] = {l4.x, l4.y, l4.z, l4.w};
-                const int ts[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
-#pragma unroll
-                for (int a = 0; a < 4; a++) {
-                    const int m = m0 + wm + 16 * a + li;
-#pragma unroll
-                    for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], ls[s], ts[s], m, p.xscale);
-                }
-            }
-            if (!A_K && bias_rows) {
-#pragma unroll
-                for (int a = 0; a < 4; a++) bsum[a] += (fa[a][0] + fa[a][1]) + (fa[a][2] + fa[a][3]);
-            }
-#pragma unroll
-            for (int s = 0; s < 4; s++)
-#pragma unroll
-                for (int a = 0; a < 4; a++)
-#pragma unroll
-                    for (int b = 0; b < 4; b++)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
-        };
+                for (int b = 0; b < 4; b++)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
+    };
 
         // LDS ring: k-tile kt lives in buffer kt % STAGES; STAGES-1 tiles are in flight
-        // while one is consumed.  Each thread waits for its own transfers of tile kt, and
-        // the barrier then makes every thread's transfers visible (and retires all reads
-        // of the buffer the next transfer overwrites).
+        // while one is consumed.  Each thread waits for its own transfers of the next
+        // k-tile, and the barrier then makes every thread's transfers visible (and retires
+        // all reads of the buffer the next transfer overwrites).  Before k-tile 0 the
+        // previous item's epilogue loads and stores may still be outstanding, and stores
+        // can complete out of order with loads, so that wait is for everything.
         const int n = ke - ks;
-#pragma unroll
-        for (int s = 0; s < STAGES - 1; s++)
-            if (s < n) issue(s, ks + s);
-        for (int kt = 0; kt < n; kt++) {
-            if (kt + STAGES - 2 < n) wait_vm<(STAGES - 2) * LPS>();
-            else wait_vm<0>();
-            __builtin_amdgcn_s_barrier();
-            if (kt + STAGES - 1 < n) issue((kt + STAGES - 1) % STAGES, ks + kt + STAGES - 1);
-            compute(kt % STAGES, ks + kt);
-        }
         wait_vm<0>();
         __builtin_amdgcn_s_barrier();
+        for (int kt = 0; kt < n; kt++) {
+            if (kt + STAGES - 1 < n) issue((kt + STAGES - 1) % STAGES, ks + kt + STAGES - 1, m0, n0);
+            compute(kt % STAGES, ks + kt);
+            // k-tile kt+1 must have landed: STAGES-2 later ones may still be in flight
+            if (kt + STAGES - 1 < n) wait_vm<(STAGES - 2) * LPS>();
+            else wait_vm<0>();
+            __builtin_amdgcn_s_barrier();
+        }
+
+        // start the next item's transfers, then finish this one while they fly
+        float* slot = cur.slot;
+        have = next_item(cur);
+        if (have) prologue(cur);
 
         const bool full = ks == 0 && ke == p.nk;
         if (bias_rows) {
@@ -464,18 +524,18 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
                 float s = bsum[a];
                 s += __shfl_xor(s, 16, 64);
                 s += __shfl_xor(s, 32, 64);
-                const int r = wm + 16 * a + li;
+                const int row = wm + 16 * a + li;
                 if (grp == 0) {
                     if (full) {
-                        if (m0 + r < p.M) p.dbias[m0 + r] += s;
+                        if (m0 + row < p.M) p.dbias[m0 + row] += s;
                     } else {
-                        slot[BM * BN + r] = s;
+                        slot[BM * BN + row] = s;
                     }
                 }
             }
         }
         if (full) {
-            epilogue<EPI>(p, acc, m0, n0);
+            epilogue_rows<EPI, 4>(p, &acc[0][0], m0, n0, 0);
         } else {
             store_partial(slot, acc);
         }
@@ -513,8 +573,7 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
     }
     int m0, n0;
     tile_coords(p, p.tile0 + tile, m0, n0);
-#pragma unroll
-    for (int b = 0; b < 4; b++) epilogue_block<EPI>(p, acc[b], m0, n0, quarter, b);
+    epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter);
     if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
         float s = 0.f;
         for (int l = first; l <= last; l++) {
