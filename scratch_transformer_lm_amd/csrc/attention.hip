@@ -37,6 +37,13 @@ GPT2_DEV f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 GPT2_DEV float comp(const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
+// Softmax arithmetic runs in base 2 on the hardware transcendental unit (v_exp_f32,
+// v_log_f32): exp(x) = 2^(x log2 e), with log2 e folded into the score scale and the
+// stored log-sum-exp converted back to natural log.
+constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+GPT2_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+GPT2_DEV float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
 // Loads a 64-row x HS tile of rows [r0, r0+64) (row stride ld floats, rows >= T are
 // zero) into registers: thread t covers row t/(HS/4) + (256/(HS/4))*j, float4 column t%(HS/4).
 template <int HS>
@@ -87,7 +94,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
     f32x4 o[DG];
 #pragma unroll
     for (int d = 0; d < DG; d++) o[d] = zero4();
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f;  // running max (base 2) and sum of this lane's query row
+    const float scale2 = scale * LOG2E;
 
     float4 kreg[DG], vreg[DG];
     const int nkt = qt + 1;
@@ -116,26 +124,27 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
                 for (int st = 0; st < 4; st++) s[kb] = mfma4(comp(kf, st), comp(qreg[g], st), s[kb]);
             }
         }
-        // lane holds scores of query tq against keys kt*64 + kb*16 + 4*g4 + v
+        // lane holds scores of query tq against keys kt*64 + kb*16 + 4*g4 + v, in base-2
+        // units; only the diagonal tile (kt == qt) has keys after the query
         float mx = m;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int key = kt * TILE + kb * 16 + 4 * g4 + v;
-                const float x = key <= tq ? s[kb][v] * scale : -INFINITY;
+                const float x = (kt < qt || key <= tq) ? s[kb][v] * scale2 : -INFINITY;
                 s[kb][v] = x;
                 mx = fmaxf(mx, x);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float alpha = expf(m - mx);
+        const float alpha = exp2_hw(m - mx);
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                const float p = expf(s[kb][v] - mx);
+                const float p = exp2_hw(s[kb][v] - mx);
                 s[kb][v] = p;
                 rs += p;
             }
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
             for (int d = 0; d < DG; d++) orow[16 * d] = o[d][v] * a;
         }
     }
-    if (g4 == 0 && tq < T) lse[((long)b * NH + h) * T + tq] = m + logf(l);
+    if (g4 == 0 && tq < T) lse[((long)b * NH + h) * T + tq] = (m + log2_hw(l)) * LN2;
 }
 
 // ---------------------------------------------------------------------------- dq (+ D)
@@ -218,6 +227,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
     dd += __shfl_xor(dd, 32, 64);
     const float D = dd;
     const float L = valid ? lse[((long)b * NH + h) * T + tq] : INFINITY;
+    const float L2 = L * LOG2E, scale2 = scale * LOG2E;
     if (g4 == 0 && valid) delta[((long)b * NH + h) * T + tq] = D;
 
     f32x4 dq[DG];
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int key = kt * TILE + kb * 16 + 4 * g4 + v;
-                const float p = key <= tq ? expf(s[v] * scale - L) : 0.f;
+                const float p = (kt < qt || key <= tq) ? exp2_hw(s[v] * scale2 - L2) : 0.f;
                 ds[v] = p * (dp[v] - D);
             }
 #pragma unroll
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
     constexpr int DG = HS / 16, LD = HS + 4;
     __shared__ __attribute__((aligned(16))) float Qs[2][TILE * LD];
     __shared__ __attribute__((aligned(16))) float Os[2][TILE * LD];
-    __shared__ float Ls[2][TILE], Ds[2][TILE];
+    __shared__ float Ls[2][TILE], Ds[2][TILE];  // base-2 log-sum-exp and D of the query tile
     const int nqt = (T + TILE - 1) / TILE;
     const int bh = blockIdx.x % (B * NH);
     const int kt = (int)(blockIdx.x / (B * NH));  // key tile 0 sees the most queries: first
@@ -321,13 +331,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
     f32x4 dk[DG], dv[DG];
 #pragma unroll
     for (int d = 0; d < DG; d++) dk[d] = dv[d] = zero4();
+    const float scale2 = scale * LOG2E;
 
     float4 qreg[DG], oreg[DG];
     float lv = 0.f, dv1 = 0.f;
     auto load_side = [&](int qt) {
         const int r = qt * TILE + (threadIdx.x & 63);
         if (threadIdx.x < 64) {
-            lv = r < T ? lrow[r] : INFINITY;
+            lv = r < T ? lrow[r] * LOG2E : INFINITY;
             dv1 = r < T ? drow_[r] : 0.f;
         }
     };
@@ -372,7 +383,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
             for (int v = 0; v < 4; v++) {
                 const int qi = qb * 16 + 4 * g4 + v;
                 const int q = qt * TILE + qi;
-                const float pv = tu <= q ? expf(s[v] * scale - Ls[cur][qi]) : 0.f;
+                const float pv = (qt > kt || tu <= q) ? exp2_hw(s[v] * scale2 - Ls[cur][qi]) : 0.f;
                 p[v] = pv;
                 ds[v] = pv * (dp[v] - Ds[cur][qi]);
             }

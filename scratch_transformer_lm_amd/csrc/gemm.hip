@@ -42,9 +42,17 @@ namespace gpt2k {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16, NT = 256;
-constexpr int STAGES = 4;                        // LDS ring depth (k-tiles in flight + 1)
-constexpr int OP_FLOATS = BM * BK;               // one operand's k-tile in LDS (8 KB)
+#ifndef GEMM_BK
+#define GEMM_BK 16
+#endif
+#ifndef GEMM_STAGES
+#define GEMM_STAGES 4
+#endif
+constexpr int BM = 128, BN = 128, BK = GEMM_BK, NT = 256;
+constexpr int KC = BK / 4;  // 16-byte chunks per k-contiguous row
+constexpr int WN = BN / 2, NB = WN / 16;  // per-wave n extent and its 16-wide blocks
+constexpr int STAGES = GEMM_STAGES;                        // LDS ring depth (k-tiles in flight + 1)
+constexpr int A_FLOATS = BM * BK, B_FLOATS = BN * BK;  // the operands' k-tiles in LDS
 constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse/target slots
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
@@ -113,50 +121,50 @@ GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, 
     constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
     constexpr bool READS = EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * WN;
     const int grp = lane >> 4;
     const float* src = EPI == EPI_ACCUM ? p.C : p.aux;
     const long lds = EPI == EPI_ACCUM ? p.ldc : p.ldaux;
     // this lane's element (i, b, v) is at row r0 + 16 i + v, column c0 + 16 b
     const int r0 = m0 + wm + 16 * a0 + 4 * grp, c0 = n0 + wn + (lane & 15);
     auto inside = [&](int i, int b, int v) { return !CHECK || (r0 + 16 * i + v < p.M && c0 + 16 * b < p.N); };
-    float bias_v[4];
+    float bias_v[NB];
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
+    for (int b = 0; b < NB; b++) {
         bias_v[b] = 0.f;
         if (HAS_BIAS && p.bias && (!CHECK || c0 + 16 * b < p.N)) bias_v[b] = p.bias[c0 + 16 * b];
     }
-    auto load_row = [&](float (&in)[4][4], int i) {
+    auto load_row = [&](float (&in)[NB][4], int i) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const float* q = src + (long)(r0 + 16 * i + v) * lds + c0;
 #pragma unroll
-            for (int b = 0; b < 4; b++) {
+            for (int b = 0; b < NB; b++) {
                 in[b][v] = 0.f;
                 if (READS && inside(i, b, v)) in[b][v] = q[16 * b];
             }
         }
     };
-    auto store_row = [&](const float (&o)[4][4], float* dst, long ld, int i) {
+    auto store_row = [&](const float (&o)[NB][4], float* dst, long ld, int i) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             float* q = dst + (long)(r0 + 16 * i + v) * ld + c0;
 #pragma unroll
-            for (int b = 0; b < 4; b++)
+            for (int b = 0; b < NB; b++)
                 if (inside(i, b, v)) q[16 * b] = o[b][v];
         }
     };
-    float in[2][4][4];
+    float in[2][NB][4];
     if (READS) load_row(in[0], 0);
 #pragma unroll
     for (int i = 0; i < NA; i++) {
-        float (&cur)[4][4] = in[i & 1];
+        float (&cur)[NB][4] = in[i & 1];
         if (READS && i + 1 < NA) load_row(in[(i + 1) & 1], i + 1);
 #pragma unroll
-        for (int b = 0; b < 4; b++)
+        for (int b = 0; b < NB; b++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                const float x = acc[i * 4 + b][v];
+                const float x = acc[i * NB + b][v];
                 float& o = cur[b][v];
                 if (EPI == EPI_STORE) o = x;
                 else if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) o = x + bias_v[b];
@@ -167,7 +175,7 @@ GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, 
         if (EPI == EPI_BIAS_GELU) {
             store_row(cur, p.pre, p.ldpre, i);  // the pre-activation, then its GELU
 #pragma unroll
-            for (int b = 0; b < 4; b++)
+            for (int b = 0; b < NB; b++)
 #pragma unroll
                 for (int v = 0; v < 4; v++) cur[b][v] = gelu_f(cur[b][v]);
         }
@@ -181,15 +189,15 @@ GPT2_DEV void epilogue_rows(const Params& p, const f32x4* acc, int m0, int n0, i
     else epilogue_rows_<EPI, NA, true>(p, acc, m0, n0, a0);
 }
 
-// Partial tile in fragment order: thread t's 64 accumulators at slot[(j*256 + t)],
-// j = (a*4 + b)*4 + v.
-GPT2_DEV void store_partial(float* slot, const f32x4 (&acc)[4][4]) {
+// Partial tile in fragment order: thread t's 16*NB accumulators at slot[(j*256 + t)],
+// j = (a*NB + b)*4 + v.
+GPT2_DEV void store_partial(float* slot, const f32x4 (&acc)[4][NB]) {
 #pragma unroll
     for (int a = 0; a < 4; a++)
 #pragma unroll
-        for (int b = 0; b < 4; b++)
+        for (int b = 0; b < NB; b++)
 #pragma unroll
-            for (int v = 0; v < 4; v++) slot[((a * 4 + b) * 4 + v) * NT + threadIdx.x] = acc[a][b][v];
+            for (int v = 0; v < 4; v++) slot[((a * NB + b) * 4 + v) * NT + threadIdx.x] = acc[a][b][v];
 }
 
 
@@ -217,32 +225,37 @@ GPT2_DEV void dma4(const void* g, float* lds) {
 // wave's 1 KB transfer is contiguous:
 //  k-contiguous [row][16]: 16-byte chunk c of row r sits at chunk position c ^ ((r>>1)&3)
 //  row-contiguous [k][128]: chunk c (rows 4c..4c+3) of k row kr sits at c ^ rswz(kr)
-GPT2_DEV int kswz(int r) { return (r >> 1) & 3; }
+GPT2_DEV int kswz(int r) { return (r >> 1) & (KC - 1); }
 GPT2_DEV int rswz(int kr) { return ((kr >> 2) & 3) << 2; }
 
-// k-contiguous operand X[r*ld + k]: rows r0.. (clamped to rmax: such rows only feed
-// outputs that are never stored), k = k0..k0+15 (all < K).
+// k-contiguous operand X[r*ld + k]: ROWS rows r0.. (clamped to rmax: such rows only
+// feed outputs that are never stored), k = k0..k0+15 (all < K).  Each wave transfer
+// covers 16 rows.
+template <int ROWS>
 GPT2_DEV void issue_kcontig(float* S, const float* X, long ld, int r0, int rmax, int k0) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < ROWS * BK / 1024; j++) {
         const int q = j * 4 + w;
-        const int R = q * 16 + (l >> 2);
-        const int c = (l & 3) ^ kswz(R);
+        const int R = q * (64 / KC) + l / KC;
+        const int c = (l % KC) ^ kswz(R);
         const int r = min(r0 + R, rmax);
         dma16(X + (long)r * ld + k0 + 4 * c, S + q * 256);
     }
 }
 
-// row-contiguous operand X[k*ld + r]: k = k0..k0+15 (clamped to kmax), rows r0..r0+127 in
-// float4 groups clamped to rmax4 (a multiple of 4 inside the row).
+// row-contiguous operand X[k*ld + r]: k = k0..k0+15 (clamped to kmax), ROWS rows r0.. in
+// float4 groups clamped to rmax4 (a multiple of 4 inside the row).  Each wave transfer
+// covers 256/ROWS k rows.
+template <int ROWS>
 GPT2_DEV void issue_rcontig(float* S, const float* X, long ld, int r0, int rmax4, int k0, int kmax) {
+    constexpr int CH = ROWS / 4;  // 16-byte chunks per k row
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < ROWS * BK / 1024; j++) {
         const int q = j * 4 + w;
-        const int kr = 2 * q + (l >> 5);
-        const int c = (l & 31) ^ rswz(kr);
+        const int kr = q * (64 / CH) + l / CH;
+        const int c = (l % CH) ^ rswz(kr);
         const int r = min(r0 + 4 * c, rmax4);
         const int k = min(k0 + kr, kmax);
         dma16(X + (long)k * ld + r, S + q * 256);
@@ -251,13 +264,15 @@ GPT2_DEV void issue_rcontig(float* S, const float* X, long ld, int r0, int rmax4
 
 // Bounds-checked k-tile through registers (the last k-tile when K is not a multiple of
 // 16): zero outside the operand, written in the same swizzled layouts.
+template <int ROWS>
 GPT2_DEV void fill_kcontig(float* S, const float* X, long ld, int r0, int nrows, int k0, int K) {
+    constexpr int RPP = NT / KC;  // rows per pass
     const int t = threadIdx.x;
-    const int c = t & 3, kk = k0 + 4 * c;
-    float4 v[2];
+    const int c = t % KC, kk = k0 + 4 * c;
+    float4 v[ROWS / RPP];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int R = (t >> 2) + 64 * j, r = r0 + R;
+    for (int j = 0; j < ROWS / RPP; j++) {
+        const int R = t / KC + RPP * j, r = r0 + R;
         v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (r < nrows) {
             const float* q = X + (long)r * ld + kk;
@@ -268,19 +283,21 @@ GPT2_DEV void fill_kcontig(float* S, const float* X, long ld, int r0, int nrows,
         }
     }
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int R = (t >> 2) + 64 * j;
+    for (int j = 0; j < ROWS / RPP; j++) {
+        const int R = t / KC + RPP * j;
         *reinterpret_cast<float4*>(S + R * BK + ((c ^ kswz(R)) << 2)) = v[j];
     }
 }
 
+template <int ROWS>
 GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows, int k0, int K) {
+    constexpr int CH = ROWS / 4, KPP = NT / CH;  // chunks per k row, k rows per pass
     const int t = threadIdx.x;
-    const int c = t & 31, r = r0 + 4 * c;
-    float4 v[2];
+    const int c = t % CH, r = r0 + 4 * c;
+    float4 v[BK / KPP];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int kr = (t >> 5) + 8 * j, k = k0 + kr;
+    for (int j = 0; j < BK / KPP; j++) {
+        const int kr = t / CH + KPP * j, k = k0 + kr;
         v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (k < K) {
             const float* q = X + (long)k * ld + r;
@@ -291,9 +308,9 @@ GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows,
         }
     }
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int kr = (t >> 5) + 8 * j;
-        *reinterpret_cast<float4*>(S + kr * BM + ((c ^ rswz(kr)) << 2)) = v[j];
+    for (int j = 0; j < BK / KPP; j++) {
+        const int kr = t / CH + KPP * j;
+        *reinterpret_cast<float4*>(S + kr * ROWS + ((c ^ rswz(kr)) << 2)) = v[j];
     }
 }
 
@@ -311,8 +328,8 @@ GPT2_DEV void wait_vm() {
 template <bool A_K, bool B_K, int EPI, bool XF>
 __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
-    constexpr int STAGE_FLOATS = 2 * OP_FLOATS + (XR ? XF_FLOATS : 0);
-    constexpr int LPS = 4 + (XR ? 1 : 0);  // transfers per thread per k-tile
+    constexpr int STAGE_FLOATS = A_FLOATS + B_FLOATS + (XR ? XF_FLOATS : 0);
+    constexpr int LPS = (BM + BN) * BK / 1024 + (XR ? 1 : 0);  // transfers per thread per k-tile
     __shared__ __attribute__((aligned(1024))) float smem[STAGES * STAGE_FLOATS];
 
     // XCD-aware logical block id: XCD x (= blockIdx % 8) gets a contiguous id range.
@@ -321,7 +338,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     const int xcd = bid & 7, local = bid >> 3;
     const int lb = xcd * (nb >> 3) + min(xcd, nb & 7) + local;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * WN;
     const int li = lane & 15, grp = lane >> 4;
     const int kfull = p.K / BK;  // k-tiles that need no bounds check
     // row clamps: k-contiguous rows to the last row; row-contiguous float4 groups to the
@@ -365,24 +382,25 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
 
     auto issue = [&](int buf, int kstep, int m0, int n0) {
         float* Sa = smem + buf * STAGE_FLOATS;
-        float* Sb = Sa + OP_FLOATS;
+        float* Sb = Sa + A_FLOATS;
         const int k0 = kstep * BK;
         if (kstep < kfull) {
-            if (A_K) issue_kcontig(Sa, p.A, p.lda, m0, rmaxA, k0);
-            else issue_rcontig(Sa, p.A, p.lda, m0, rmaxA, k0, p.K - 1);
-            if (B_K) issue_kcontig(Sb, p.B, p.ldb, n0, rmaxB, k0);
-            else issue_rcontig(Sb, p.B, p.ldb, n0, rmaxB, k0, p.K - 1);
+            if (A_K) issue_kcontig<BM>(Sa, p.A, p.lda, m0, rmaxA, k0);
+            else issue_rcontig<BM>(Sa, p.A, p.lda, m0, rmaxA, k0, p.K - 1);
+            if (B_K) issue_kcontig<BN>(Sb, p.B, p.ldb, n0, rmaxB, k0);
+            else issue_rcontig<BN>(Sb, p.B, p.ldb, n0, rmaxB, k0, p.K - 1);
         } else {
-            if (A_K) fill_kcontig(Sa, p.A, p.lda, m0, p.M, k0, p.K);
-            else fill_rcontig(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
-            if (B_K) fill_kcontig(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
-            else fill_rcontig(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+            if (A_K) fill_kcontig<BM>(Sa, p.A, p.lda, m0, p.M, k0, p.K);
+            else fill_rcontig<BM>(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
+            if (B_K) fill_kcontig<BN>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+            else fill_rcontig<BN>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
         }
         if (XR) {
-            // lanes 0-15: lse of k rows k0.., lanes 16-31: their targets (copied as bits)
-            const int kk = min(k0 + (lane & 15), p.K - 1);
-            const void* src = (lane & 16) ? (const void*)(p.tgt + kk) : (const void*)(p.lse + kk);
-            dma4(src, Sb + OP_FLOATS + wave * 64);
+            // lanes 0..BK-1: lse of k rows k0.., lanes BK..2BK-1: their targets (copied as
+            // bits); any further lanes repeat the targets
+            const int kk = min(k0 + lane % BK, p.K - 1);
+            const void* src = lane >= BK ? (const void*)(p.tgt + kk) : (const void*)(p.lse + kk);
+            dma4(src, Sb + B_FLOATS + wave * 64);
         }
     };
     // the first STAGES-1 k-tiles of an item
@@ -397,11 +415,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     if (have) prologue(cur);
     while (have) {
         const int m0 = cur.m0, n0 = cur.n0, ks = cur.ks, ke = cur.ke;
-        f32x4 acc[4][4];
+        f32x4 acc[4][NB];
 #pragma unroll
         for (int a = 0; a < 4; a++)
 #pragma unroll
-            for (int b = 0; b < 4; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < NB; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // wgrad with bias: the waves of sub-tile column 0 sum their A fragments
         const bool bias_rows = !A_K && p.dbias != nullptr && n0 == 0 && wn == 0;
@@ -420,78 +438,83 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
             }
         }
 
-    auto compute = [&](int buf, int kstep) {
-        const float* Sa = smem + buf * STAGE_FLOATS;
-        const float* Sb = Sa + OP_FLOATS;
-        const int k0 = kstep * BK;
-        float fa[4][4], fb[4][4];
+        // one k-tile: BK/16 groups of 16 k, each 4 MFMA steps over this wave's blocks
+        auto compute = [&](int buf, int kstep) {
+            const float* Sa = smem + buf * STAGE_FLOATS;
+            const float* Sb = Sa + A_FLOATS;
+            const int k0 = kstep * BK;
 #pragma unroll
-        for (int a = 0; a < 4; a++) {
-            const int row = wm + 16 * a + li;
-            if (A_K) {
-                const float4 v = *reinterpret_cast<const float4*>(Sa + row * BK + ((grp ^ kswz(row)) << 2));
-                fa[a][0] = v.x;
-                fa[a][1] = v.y;
-                fa[a][2] = v.z;
-                fa[a][3] = v.w;
-            } else {
+            for (int g = 0; g < BK / 16; g++) {
+                float fa[4][4], fb[NB][4];
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    const int kr = 4 * grp + s;
-                    fa[a][s] = Sa[kr * BM + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                for (int a = 0; a < 4; a++) {
+                    const int row = wm + 16 * a + li;
+                    if (A_K) {
+                        const float4 v = *reinterpret_cast<const float4*>(Sa + row * BK + (((4 * g + grp) ^ kswz(row)) << 2));
+                        fa[a][0] = v.x;
+                        fa[a][1] = v.y;
+                        fa[a][2] = v.z;
+                        fa[a][3] = v.w;
+                    } else {
+#pragma unroll
+                        for (int s = 0; s < 4; s++) {
+                            const int kr = 16 * g + 4 * grp + s;
+                            fa[a][s] = Sa[kr * BM + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                        }
+                    }
                 }
-            }
-        }
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int row = wn + 16 * b + li;
-            if (B_K) {
-                const float4 v = *reinterpret_cast<const float4*>(Sb + row * BK + ((grp ^ kswz(row)) << 2));
-                fb[b][0] = v.x;
-                fb[b][1] = v.y;
-                fb[b][2] = v.z;
-                fb[b][3] = v.w;
-            } else {
+                for (int b = 0; b < NB; b++) {
+                    const int row = wn + 16 * b + li;
+                    if (B_K) {
+                        const float4 v = *reinterpret_cast<const float4*>(Sb + row * BK + (((4 * g + grp) ^ kswz(row)) << 2));
+                        fb[b][0] = v.x;
+                        fb[b][1] = v.y;
+                        fb[b][2] = v.z;
+                        fb[b][3] = v.w;
+                    } else {
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    const int kr = 4 * grp + s;
-                    fb[b][s] = Sb[kr * BN + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                        for (int s = 0; s < 4; s++) {
+                            const int kr = 16 * g + 4 * grp + s;
+                            fb[b][s] = Sb[kr * BN + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                        }
+                    }
                 }
+                // dlogits: no bounds checks needed, since B is zero for k >= K (the
+                // bounds-checked k-tile) and rows m >= M only feed outputs never stored
+                if (XF && A_K) {
+#pragma unroll
+                    for (int a = 0; a < 4; a++)
+#pragma unroll
+                        for (int s = 0; s < 4; s++)
+                            fa[a][s] = dlogit(fa[a][s], xl[a], xt[a], k0 + 16 * g + 4 * grp + s, p.xscale);
+                }
+                if (XR) {
+                    const float* xs = Sb + B_FLOATS + wave * 64 + 16 * g + 4 * grp;
+                    const float4 l4 = *reinterpret_cast<const float4*>(xs);
+                    const float4 t4 = *reinterpret_cast<const float4*>(xs + BK);
+                    const float ls[4] = {l4.x, l4.y, l4.z, l4.w};
+                    const int ts[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
+#pragma unroll
+                    for (int a = 0; a < 4; a++) {
+                        const int m = m0 + wm + 16 * a + li;
+#pragma unroll
+                        for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], ls[s], ts[s], m, p.xscale);
+                    }
+                }
+                if (!A_K && bias_rows) {
+#pragma unroll
+                    for (int a = 0; a < 4; a++) bsum[a] += (fa[a][0] + fa[a][1]) + (fa[a][2] + fa[a][3]);
+                }
+#pragma unroll
+                for (int s = 0; s < 4; s++)
+#pragma unroll
+                    for (int a = 0; a < 4; a++)
+#pragma unroll
+                        for (int b = 0; b < NB; b++)
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
             }
-        }
-        // dlogits: no bounds checks needed, since B is zero for k >= K (the bounds-checked
-        // k-tile) and rows m >= M only feed outputs that are never stored
-        if (XF && A_K) {
-#pragma unroll
-            for (int a = 0; a < 4; a++)
-#pragma unroll
-                for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], xl[a], xt[a], k0 + 4 * grp + s, p.xscale);
-        }
-        if (XR) {
-            const float* xs = Sb + OP_FLOATS + wave * 64;
-            const float4 l4 = *reinterpret_cast<const float4*>(xs + 4 * grp);
-            const float4 t4 = *reinterpret_cast<const float4*>(xs + 16 + 4 * grp);
-            const float ls[4] = {l4.x, l4.y, l4.z, l4.w};
-            const int ts[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
-#pragma unroll
-            for (int a = 0; a < 4; a++) {
-                const int m = m0 + wm + 16 * a + li;
-#pragma unroll
-                for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], ls[s], ts[s], m, p.xscale);
-            }
-        }
-        if (!A_K && bias_rows) {
-#pragma unroll
-            for (int a = 0; a < 4; a++) bsum[a] += (fa[a][0] + fa[a][1]) + (fa[a][2] + fa[a][3]);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; s++)
-#pragma unroll
-            for (int a = 0; a < 4; a++)
-#pragma unroll
-                for (int b = 0; b < 4; b++)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
-    };
+        };
 
         // LDS ring: k-tile kt lives in buffer kt % STAGES; STAGES-1 tiles are in flight
         // while one is consumed.  Each thread waits for its own transfers of the next
@@ -559,17 +582,17 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
     const long t0 = (long)tile * p.nk;
     const int first = owner(p.total, p.nr, t0);
     const int last = owner(p.total, p.nr, t0 + p.nk - 1);
-    f32x4 acc[4];
+    f32x4 acc[NB];
 #pragma unroll
-    for (int b = 0; b < 4; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int l = first; l <= last; l++) {
         const int which = range_start(p.total, p.nr, l) / p.nk == tile ? 0 : 1;
-        const float* slot = p.partial + ((long)l * 2 + which) * SLOT_FLOATS + quarter * 16 * NT + threadIdx.x;
-        float v[16];
+        const float* slot = p.partial + ((long)l * 2 + which) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
+        float v[4 * NB];
 #pragma unroll
-        for (int e = 0; e < 16; e++) v[e] = slot[e * NT];
+        for (int e = 0; e < 4 * NB; e++) v[e] = slot[e * NT];
 #pragma unroll
-        for (int e = 0; e < 16; e++) acc[e >> 2][e & 3] += v[e];
+        for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[e];
     }
     int m0, n0;
     tile_coords(p, p.tile0 + tile, m0, n0);
