@@ -7,16 +7,17 @@
 //   dgrad    dX = dY W:               A = dY (k contiguous),  B = W  (n contiguous)
 //   wgrad    dW += dY^T X:            A = dY (m contiguous),  B = X  (n contiguous)
 //
-// Design for CDNA4: 256 threads = 4 wave64s, block tile 128x128, k-tile 16, each wave a
-// 64x64 sub-tile made of 4x4 v_mfma_f32_16x16x4f32 blocks (64 accumulators per lane).
-// The 16x16x4 form is used because it sustains the full fp32 matrix rate on gfx950,
-// where the 32x32x2 form measures about 12% lower.  Operand k-tiles go from global
-// memory straight into LDS (global_load_lds_dwordx4, no register staging) through a ring
-// of 4 buffers, so 3 k-tiles are in flight while one is consumed, and each k-tile costs
-// one barrier.  LDS tiles are unpadded (a wave's transfer is 1 KB of consecutive LDS) and
-// bank conflicts are avoided by XOR-swizzling 16-byte chunks: k-contiguous tiles
-// [row][16] by (row/2)%4, row-contiguous tiles [k][128] by 4*((k/4)%4).  Each lane takes 4
-// consecutive k for its lane group (k = 4(lane/16) + s for MFMA step s), so a
+// Design for CDNA4: 256 threads = 4 wave64s, block tile 128x128, each wave a 64x64
+// sub-tile made of 4x4 v_mfma_f32_16x16x4f32 blocks (64 accumulators per lane).  The
+// 16x16x4 form is used because it sustains the full fp32 matrix rate on gfx950, where
+// the 32x32x2 form measures about 12% lower.  Operand k-tiles go from global memory
+// straight into LDS (global_load_lds_dwordx4, no register staging) through a ring of LDS
+// buffers: 32-wide k-tiles in 2 buffers when A is k-contiguous, 16-wide k-tiles in 4
+// buffers (3 in flight while one is consumed) for the wgrad; each k-tile costs one
+// barrier.  LDS tiles are unpadded (a wave's transfer is 1 KB of consecutive LDS) and bank
+// conflicts are avoided by XOR-swizzling 16-byte chunks: k-contiguous tiles [row][BK] by
+// (row/2) % (BK/4), row-contiguous tiles [k][128] by 4*((k/4)%4).  Each lane takes 4
+// consecutive k for its lane group (k = 16g + 4(lane/16) + s for MFMA step s), so a
 // k-contiguous fragment is one 16-byte LDS read; the sum over k is the same sum in
 // another order.
 //
@@ -42,17 +43,17 @@ namespace gpt2k {
 
 namespace {
 
-#ifndef GEMM_BK
-#define GEMM_BK 16
-#endif
-#ifndef GEMM_STAGES
-#define GEMM_STAGES 4
-#endif
-constexpr int BM = 128, BN = 128, BK = GEMM_BK, NT = 256;
-constexpr int KC = BK / 4;  // 16-byte chunks per k-contiguous row
+constexpr int BM = 128, BN = 128, NT = 256;
 constexpr int WN = BN / 2, NB = WN / 16;  // per-wave n extent and its 16-wide blocks
-constexpr int STAGES = GEMM_STAGES;                        // LDS ring depth (k-tiles in flight + 1)
-constexpr int A_FLOATS = BM * BK, B_FLOATS = BN * BK;  // the operands' k-tiles in LDS
+// k-tile width and LDS ring depth (k-tiles in flight + 1) per operand layout: 32 and 2
+// when A is k-contiguous (forward, dgrad), 16 and 4 for the wgrad, whose row-contiguous
+// fragments and fused bias sums need more registers than a second wave per SIMD leaves
+// with 32-wide k-tiles.  Both rings take 64 KB.
+template <bool A_K>
+struct KTile {
+    static constexpr int BK = A_K ? 32 : 16;
+    static constexpr int STAGES = A_K ? 2 : 4;
+};
 constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse/target slots
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
@@ -223,22 +224,24 @@ GPT2_DEV void dma4(const void* g, float* lds) {
 
 // LDS layouts of one k-tile (16 k values, 128 rows), both without padding so that a
 // wave's 1 KB transfer is contiguous:
-//  k-contiguous [row][16]: 16-byte chunk c of row r sits at chunk position c ^ ((r>>1)&3)
+//  k-contiguous [row][BK]: 16-byte chunk c of row r sits at chunk position c ^ ((r>>1) % (BK/4))
 //  row-contiguous [k][128]: chunk c (rows 4c..4c+3) of k row kr sits at c ^ rswz(kr)
-GPT2_DEV int kswz(int r) { return (r >> 1) & (KC - 1); }
+template <int BK>
+GPT2_DEV int kswz(int r) { return (r >> 1) & (BK / 4 - 1); }
 GPT2_DEV int rswz(int kr) { return ((kr >> 2) & 3) << 2; }
 
 // k-contiguous operand X[r*ld + k]: ROWS rows r0.. (clamped to rmax: such rows only
 // feed outputs that are never stored), k = k0..k0+15 (all < K).  Each wave transfer
 // covers 16 rows.
-template <int ROWS>
+template <int ROWS, int BK>
 GPT2_DEV void issue_kcontig(float* S, const float* X, long ld, int r0, int rmax, int k0) {
+    constexpr int KC = BK / 4;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
     for (int j = 0; j < ROWS * BK / 1024; j++) {
         const int q = j * 4 + w;
         const int R = q * (64 / KC) + l / KC;
-        const int c = (l % KC) ^ kswz(R);
+        const int c = (l % KC) ^ kswz<BK>(R);
         const int r = min(r0 + R, rmax);
         dma16(X + (long)r * ld + k0 + 4 * c, S + q * 256);
     }
@@ -247,7 +250,7 @@ GPT2_DEV void issue_kcontig(float* S, const float* X, long ld, int r0, int rmax,
 // row-contiguous operand X[k*ld + r]: k = k0..k0+15 (clamped to kmax), ROWS rows r0.. in
 // float4 groups clamped to rmax4 (a multiple of 4 inside the row).  Each wave transfer
 // covers 256/ROWS k rows.
-template <int ROWS>
+template <int ROWS, int BK>
 GPT2_DEV void issue_rcontig(float* S, const float* X, long ld, int r0, int rmax4, int k0, int kmax) {
     constexpr int CH = ROWS / 4;  // 16-byte chunks per k row
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -264,9 +267,9 @@ GPT2_DEV void issue_rcontig(float* S, const float* X, long ld, int r0, int rmax4
 
 // Bounds-checked k-tile through registers (the last k-tile when K is not a multiple of
 // 16): zero outside the operand, written in the same swizzled layouts.
-template <int ROWS>
+template <int ROWS, int BK>
 GPT2_DEV void fill_kcontig(float* S, const float* X, long ld, int r0, int nrows, int k0, int K) {
-    constexpr int RPP = NT / KC;  // rows per pass
+    constexpr int KC = BK / 4, RPP = NT / KC;  // chunks per row, rows per pass
     const int t = threadIdx.x;
     const int c = t % KC, kk = k0 + 4 * c;
     float4 v[ROWS / RPP];
@@ -285,11 +288,11 @@ GPT2_DEV void fill_kcontig(float* S, const float* X, long ld, int r0, int nrows,
 #pragma unroll
     for (int j = 0; j < ROWS / RPP; j++) {
         const int R = t / KC + RPP * j;
-        *reinterpret_cast<float4*>(S + R * BK + ((c ^ kswz(R)) << 2)) = v[j];
+        *reinterpret_cast<float4*>(S + R * BK + ((c ^ kswz<BK>(R)) << 2)) = v[j];
     }
 }
 
-template <int ROWS>
+template <int ROWS, int BK>
 GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows, int k0, int K) {
     constexpr int CH = ROWS / 4, KPP = NT / CH;  // chunks per k row, k rows per pass
     const int t = threadIdx.x;
@@ -328,6 +331,8 @@ GPT2_DEV void wait_vm() {
 template <bool A_K, bool B_K, int EPI, bool XF>
 __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
+    constexpr int BK = KTile<A_K>::BK, STAGES = KTile<A_K>::STAGES;
+    constexpr int A_FLOATS = BM * BK, B_FLOATS = BN * BK;  // the operands' k-tiles in LDS
     constexpr int STAGE_FLOATS = A_FLOATS + B_FLOATS + (XR ? XF_FLOATS : 0);
     constexpr int LPS = (BM + BN) * BK / 1024 + (XR ? 1 : 0);  // transfers per thread per k-tile
     __shared__ __attribute__((aligned(1024))) float smem[STAGES * STAGE_FLOATS];
@@ -385,15 +390,15 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
         float* Sb = Sa + A_FLOATS;
         const int k0 = kstep * BK;
         if (kstep < kfull) {
-            if (A_K) issue_kcontig<BM>(Sa, p.A, p.lda, m0, rmaxA, k0);
-            else issue_rcontig<BM>(Sa, p.A, p.lda, m0, rmaxA, k0, p.K - 1);
-            if (B_K) issue_kcontig<BN>(Sb, p.B, p.ldb, n0, rmaxB, k0);
-            else issue_rcontig<BN>(Sb, p.B, p.ldb, n0, rmaxB, k0, p.K - 1);
+            if (A_K) issue_kcontig<BM, BK>(Sa, p.A, p.lda, m0, rmaxA, k0);
+            else issue_rcontig<BM, BK>(Sa, p.A, p.lda, m0, rmaxA, k0, p.K - 1);
+            if (B_K) issue_kcontig<BN, BK>(Sb, p.B, p.ldb, n0, rmaxB, k0);
+            else issue_rcontig<BN, BK>(Sb, p.B, p.ldb, n0, rmaxB, k0, p.K - 1);
         } else {
-            if (A_K) fill_kcontig<BM>(Sa, p.A, p.lda, m0, p.M, k0, p.K);
-            else fill_rcontig<BM>(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
-            if (B_K) fill_kcontig<BN>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
-            else fill_rcontig<BN>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+            if (A_K) fill_kcontig<BM, BK>(Sa, p.A, p.lda, m0, p.M, k0, p.K);
+            else fill_rcontig<BM, BK>(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
+            if (B_K) fill_kcontig<BN, BK>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+            else fill_rcontig<BN, BK>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
         }
         if (XR) {
             // lanes 0..BK-1: lse of k rows k0.., lanes BK..2BK-1: their targets (copied as
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
                 for (int a = 0; a < 4; a++) {
                     const int row = wm + 16 * a + li;
                     if (A_K) {
-                        const float4 v = *reinterpret_cast<const float4*>(Sa + row * BK + (((4 * g + grp) ^ kswz(row)) << 2));
+                        const float4 v = *reinterpret_cast<const float4*>(Sa + row * BK + (((4 * g + grp) ^ kswz<BK>(row)) << 2));
                         fa[a][0] = v.x;
                         fa[a][1] = v.y;
                         fa[a][2] = v.z;
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
                 for (int b = 0; b < NB; b++) {
                     const int row = wn + 16 * b + li;
                     if (B_K) {
-                        const float4 v = *reinterpret_cast<const float4*>(Sb + row * BK + (((4 * g + grp) ^ kswz(row)) << 2));
+                        const float4 v = *reinterpret_cast<const float4*>(Sb + row * BK + (((4 * g + grp) ^ kswz<BK>(row)) << 2));
                         fb[b][0] = v.x;
                         fb[b][1] = v.y;
                         fb[b][2] = v.z;
@@ -651,7 +656,7 @@ template <bool A_K, bool B_K, int EPI, bool XF = false>
 hipError_t launch(Params& p, hipStream_t st) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
-    p.nk = (p.K + BK - 1) / BK;
+    p.nk = (p.K + KTile<A_K>::BK - 1) / KTile<A_K>::BK;
     const long tiles = (long)p.tiles_m * p.tiles_n;
     if (tiles == 0) return hipSuccess;
     if (p.nk == 0) {
