@@ -33,6 +33,7 @@
 // timing.  Logical block ids are laid out so that each XCD (blocks are dealt round-robin
 // to the 8 XCDs) owns a contiguous id range, and tiles are ordered 8 tile-rows at a time.
 #include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "common.h"
@@ -61,7 +62,9 @@ constexpr int SLOT_FLOATS = BM * BN + BM;  // one partial tile + its bias-gradie
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum Epi { EPI_STORE = 0, EPI_BIAS, EPI_BIAS_RESID, EPI_BIAS_GELU, EPI_ACCUM, EPI_GELU_BWD };
+// EPI_DLOGITS: LM-head dgrad whose A held s * softmax only; the one-hot part of dlogits,
+// s * onehot(target) . W = s * W[target], is subtracted here.
+enum Epi { EPI_STORE = 0, EPI_BIAS, EPI_BIAS_RESID, EPI_BIAS_GELU, EPI_ACCUM, EPI_GELU_BWD, EPI_DLOGITS };
 
 struct Params {
     int M, N, K;
@@ -81,6 +84,7 @@ struct Params {
     const float* lse;   // dlogits operand: per-row log-sum-exp of the logits
     const int32_t* tgt; // dlogits operand: per-row target id
     float xscale;       // dlogits operand: d loss / d loss_row (1 / rows)
+    float xlog2s;       // log2(xscale)
     int tiles_m, tiles_n, nk;
     int G;              // persistent blocks
     int R;              // whole-tile rounds: block lb takes tiles r*G + lb, r < R
@@ -120,7 +124,7 @@ GPT2_DEV void tile_coords(const Params& p, int tile, int& m0, int& n0) {
 template <int EPI, int NA, bool CHECK>
 GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, int a0) {
     constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
-    constexpr bool READS = EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD;
+    constexpr bool READS = EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_DLOGITS;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * WN;
     const int grp = lane >> 4;
@@ -138,7 +142,10 @@ GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, 
     auto load_row = [&](float (&in)[NB][4], int i) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const float* q = src + (long)(r0 + 16 * i + v) * lds + c0;
+            const int row = r0 + 16 * i + v;
+            const float* q = src + (long)row * lds + c0;
+            // EPI_DLOGITS reads row target[row] of W (B, k = vocabulary id) instead
+            if (EPI == EPI_DLOGITS) q = p.B + (long)(!CHECK || row < p.M ? p.tgt[row] : 0) * p.ldb + c0;
 #pragma unroll
             for (int b = 0; b < NB; b++) {
                 in[b][v] = 0.f;
@@ -171,6 +178,7 @@ GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, 
                 else if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) o = x + bias_v[b];
                 else if (EPI == EPI_BIAS_RESID) o = o + (x + bias_v[b]);
                 else if (EPI == EPI_ACCUM) o = o + x;
+                else if (EPI == EPI_DLOGITS) o = x - p.xscale * o;
                 else o = x * gelu_grad_f(o);  // EPI_GELU_BWD
             }
         if (EPI == EPI_BIAS_GELU) {
@@ -317,11 +325,12 @@ GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows,
     }
 }
 
-// The logits operand of the LM-head backward: each logit z of row `row` in vocabulary
-// column c becomes d loss / d z = (exp(z - lse[row]) - [c == target[row]]) * scale.
-GPT2_DEV float dlogit(float z, float lse, int tgt, int c, float scale) {
-    return (__expf(z - lse) - (c == tgt ? 1.0f : 0.0f)) * scale;
-}
+// The logits operand of the LM-head backward: each logit z of row r in vocabulary column
+// c becomes d loss / d z = s * (exp(z - lse_r) - [c == target_r]), s = 1/rows.  The
+// first term is formed as 2^(z log2 e - (lse_r log2 e - log2 s)) on v_exp_f32 with the
+// row constant precomputed; the dgrad leaves the one-hot term to its epilogue.
+constexpr float LOG2E = 1.4426950408889634f;
+GPT2_DEV float softmax_s(float z, float c2) { return __builtin_amdgcn_exp2f(fmaf(z, LOG2E, -c2)); }
 
 template <int N>
 GPT2_DEV void wait_vm() {
@@ -430,16 +439,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
         const bool bias_rows = !A_K && p.dbias != nullptr && n0 == 0 && wn == 0;
         float bsum[4] = {0.f, 0.f, 0.f, 0.f};
 
-        // dlogits as the k-contiguous operand (LM-head dgrad): lse / target of this
-        // lane's four fragment rows
+        // dlogits as the k-contiguous operand (LM-head dgrad): the exponent offset
+        // lse log2 e - log2 s of this lane's four fragment rows
         float xl[4];
-        int xt[4];
         if (XF && A_K) {
 #pragma unroll
             for (int a = 0; a < 4; a++) {
                 const int row = m0 + wm + 16 * a + li;
-                xl[a] = row < p.M ? p.lse[row] : 0.f;
-                xt[a] = row < p.M ? p.tgt[row] : -1;
+                xl[a] = row < p.M ? fmaf(p.lse[row], LOG2E, -p.xlog2s) : 0.f;
             }
         }
 
@@ -491,20 +498,23 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
 #pragma unroll
                     for (int a = 0; a < 4; a++)
 #pragma unroll
-                        for (int s = 0; s < 4; s++)
-                            fa[a][s] = dlogit(fa[a][s], xl[a], xt[a], k0 + 16 * g + 4 * grp + s, p.xscale);
+                        for (int s = 0; s < 4; s++) fa[a][s] = softmax_s(fa[a][s], xl[a]);
                 }
                 if (XR) {
                     const float* xs = Sb + B_FLOATS + wave * 64 + 16 * g + 4 * grp;
                     const float4 l4 = *reinterpret_cast<const float4*>(xs);
                     const float4 t4 = *reinterpret_cast<const float4*>(xs + BK);
-                    const float ls[4] = {l4.x, l4.y, l4.z, l4.w};
+                    const float ls[4] = {fmaf(l4.x, LOG2E, -p.xlog2s), fmaf(l4.y, LOG2E, -p.xlog2s),
+                                         fmaf(l4.z, LOG2E, -p.xlog2s), fmaf(l4.w, LOG2E, -p.xlog2s)};
                     const int ts[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
 #pragma unroll
                     for (int a = 0; a < 4; a++) {
                         const int m = m0 + wm + 16 * a + li;
 #pragma unroll
-                        for (int s = 0; s < 4; s++) fa[a][s] = dlogit(fa[a][s], ls[s], ts[s], m, p.xscale);
+                        for (int s = 0; s < 4; s++) {
+                            const float e = softmax_s(fa[a][s], ls[s]);
+                            fa[a][s] = m == ts[s] ? e - p.xscale : e;
+                        }
                     }
                 }
                 if (!A_K && bias_rows) {
@@ -665,7 +675,8 @@ hipError_t launch(Params& p, hipStream_t st) {
     }
     schedule(p, tiles);
     const double mn = (double)p.M * p.N;
-    const double extra = (EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_BIAS_GELU) ? mn : 0.0;
+    const double extra = (EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_BIAS_GELU ||
+                          EPI == EPI_DLOGITS) ? mn : 0.0;
     {
         // algorithmic work: 2MNK flops; operands read once, C written (and read for += / aux)
         ProfScope ps(st, gemm_name<A_K, B_K, EPI, XF>(), 2.0 * mn * p.K,
@@ -738,8 +749,10 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
     if (xent) {
         p.lse = xent->lse;
         p.tgt = xent->targets;
+        if (!(xent->scale > 0.f)) return hipErrorInvalidValue;
         p.xscale = xent->scale;
-        return launch<true, false, EPI_STORE, true>(p, st);
+        p.xlog2s = (float)std::log2((double)xent->scale);
+        return launch<true, false, EPI_DLOGITS, true>(p, st);
     }
     return launch<true, false, EPI_STORE>(p, st);
 }
@@ -765,7 +778,9 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
     if (xent) {
         p.lse = xent->lse;
         p.tgt = xent->targets;
+        if (!(xent->scale > 0.f)) return hipErrorInvalidValue;
         p.xscale = xent->scale;
+        p.xlog2s = (float)std::log2((double)xent->scale);
         return launch<false, false, EPI_ACCUM, true>(p, st);
     }
     return launch<false, false, EPI_ACCUM>(p, st);
