@@ -5,9 +5,14 @@
 // The backward is a scatter-add into the wte rows that were read.  Token frequencies
 // are skewed (a few ids fill a large share of the positions), so instead of float
 // atomics, which would serialise on the hot rows and make the sums order-dependent,
-// the backward finds the first position of every distinct id and lets one block own
-// that id: it walks the later positions in order and adds their rows.  Results are
-// therefore bitwise reproducible.
+// one block sorts the (token, position) pairs in LDS (bitonic sort of 32-bit keys
+// token << 16 | position, so equal tokens keep position order) and cuts the sorted list
+// into one segment per distinct token; then one block per segment adds that token's
+// rows in position order.  Results are therefore bitwise reproducible.  Batches too large
+// for the one-block sort fall back to a first-occurrence scan: one block per distinct
+// token walks all later positions.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -16,7 +21,15 @@ namespace gpt2k {
 
 namespace {
 
-constexpr int STAGE = 4096;  // tokens staged in LDS per pass
+constexpr int STAGE = 4096;       // tokens staged in LDS per pass (fallback path)
+constexpr int SORT_MAX = 32768;   // (token, position) keys one block sorts in LDS (128 KB)
+constexpr int SORT_NT = 1024;
+
+int pow2_at_least(int n) {
+    int p = 2;
+    while (p < n) p <<= 1;
+    return p;
+}
 
 __global__ __launch_bounds__(256) void encoder_fwd_kernel(float* __restrict__ out, const int32_t* __restrict__ tok,
                                                           const float* __restrict__ wte, const float* __restrict__ wpe,
@@ -58,9 +71,10 @@ __global__ __launch_bounds__(256) void wpe_bwd_kernel(float* __restrict__ dwpe, 
 }
 
 // For each position p, is it the first position holding its token id?  Such positions
-// are appended to list (slot order does not matter: each one is processed alone).
-// work[0] is the list length and must be 0 on entry.
-__global__ __launch_bounds__(256) void first_occurrence_kernel(int* work, const int32_t* __restrict__ tok, int BT) {
+// are appended to list (slot order does not matter: each one is processed alone); ids
+// outside [0, V) are never listed.  work[0] is the list length and must be 0 on entry.
+__global__ __launch_bounds__(256) void first_occurrence_kernel(int* work, const int32_t* __restrict__ tok, int BT,
+                                                               int V) {
     __shared__ int s[STAGE];
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     const int v = p < BT ? tok[p] : -1;
@@ -74,17 +88,17 @@ __global__ __launch_bounds__(256) void first_occurrence_kernel(int* work, const 
         const int lim = min(n, p - base);
         for (int i = 0; i < lim; i++) found |= (s[i] == v);
     }
-    if (p < BT && !found) {
+    if (p < BT && !found && v >= 0 && v < V) {
         const int slot = atomicAdd(work, 1);
         work[1 + slot] = p;
     }
 }
 
-// Block k owns the k-th listed first position p: dwte[tok[p]] += sum of dout[q] over
-// q >= p with the same id, q increasing.
-__global__ __launch_bounds__(256) void wte_bwd_kernel(float* __restrict__ dwte, const float* __restrict__ dout,
-                                                      const int32_t* __restrict__ tok, const int* __restrict__ work,
-                                                      int BT, int C) {
+// Block k owns the k-th listed first position p: dwte[tok[p]] += scale * (sum of src[q]
+// over q >= p with the same id, q increasing).
+__global__ __launch_bounds__(256) void wte_bwd_kernel(float* __restrict__ dwte, const float* __restrict__ src, long ld,
+                                                      float scale, const int32_t* __restrict__ tok,
+                                                      const int* __restrict__ work, int BT, int C) {
     __shared__ unsigned long long masks[4];
     if ((int)blockIdx.x >= work[0]) return;
     const int p = work[1 + blockIdx.x];
@@ -105,7 +119,7 @@ __global__ __launch_bounds__(256) void wte_bwd_kernel(float* __restrict__ dwte, 
             while (mm) {
                 const int bit = __ffsll((long long)mm) - 1;
                 mm &= mm - 1;
-                const float4* row = reinterpret_cast<const float4*>(dout + (long)(base + w * 64 + bit) * C);
+                const float4* row = reinterpret_cast<const float4*>(src + (long)(base + w * 64 + bit) * ld);
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     const int c = threadIdx.x + 256 * j;
@@ -127,16 +141,127 @@ __global__ __launch_bounds__(256) void wte_bwd_kernel(float* __restrict__ dwte, 
         const int c = threadIdx.x + 256 * j;
         if (c < C4) {
             float4 o = dst[c];
-            o.x += acc[j].x;
-            o.y += acc[j].y;
-            o.z += acc[j].z;
-            o.w += acc[j].w;
+            o.x += scale * acc[j].x;
+            o.y += scale * acc[j].y;
+            o.z += scale * acc[j].z;
+            o.w += scale * acc[j].w;
             dst[c] = o;
         }
     }
 }
 
 __global__ void zero_int_kernel(int* x) { *x = 0; }
+
+// One block: sorts keys token << 16 | position for the n positions (ids outside [0, V)
+// sort last and are dropped), then lists the start of every run of equal tokens.
+// work: [0] run count, [1, 1+np) sorted keys, [1+np, ...) run starts, then the end of the
+// last run.
+__global__ __launch_bounds__(SORT_NT) void sort_tokens_kernel(int* __restrict__ work, const int32_t* __restrict__ tok,
+                                                              int n, int np, int V) {
+    __shared__ unsigned keys[SORT_MAX];
+    __shared__ int wsum[SORT_NT / 64];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < np; i += SORT_NT) {
+        unsigned k = 0xFFFFFFFFu;
+        if (i < n) {
+            const int v = tok[i];
+            if (v >= 0 && v < V) k = ((unsigned)v << 16) | (unsigned)i;
+        }
+        keys[i] = k;
+    }
+    __syncthreads();
+    // bitonic sort, ascending: pass (size, stride) compares i and i + stride for every i
+    // whose stride bit is clear, in the direction of bit `size` of i
+    for (int size = 2; size <= np; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < np / 2; i += SORT_NT) {
+                const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+                const unsigned a = keys[lo], b = keys[hi];
+                if ((a > b) == ((lo & size) == 0)) {
+                    keys[lo] = b;
+                    keys[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    // run starts, compacted in order: thread t owns keys [t*per, (t+1)*per)
+    const int per = np / SORT_NT > 0 ? np / SORT_NT : 1;
+    const int j0 = tid * per, j1 = min(np, j0 + per);
+    int cnt = 0;
+    for (int j = j0; j < j1; j++)
+        cnt += keys[j] != 0xFFFFFFFFu && (j == 0 || (keys[j] >> 16) != (keys[j - 1] >> 16));
+    // exclusive scan of cnt over the block
+    const int lane = tid & 63, wv = tid >> 6;
+    int incl = cnt;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int off = 0;
+    for (int w = 0; w < wv; w++) off += wsum[w];
+    int at = off + incl - cnt;
+    int* runs = work + 1 + np;
+    for (int j = j0; j < j1; j++)
+        if (keys[j] != 0xFFFFFFFFu && (j == 0 || (keys[j] >> 16) != (keys[j - 1] >> 16))) runs[at++] = j;
+    unsigned* out = reinterpret_cast<unsigned*>(work + 1);
+    for (int i = tid; i < np; i += SORT_NT) out[i] = keys[i];
+    if (tid == SORT_NT - 1) {
+        int total = 0;
+        for (int w = 0; w < SORT_NT / 64; w++) total += wsum[w];
+        work[0] = total;
+        // end of the last run: the number of valid keys
+        int valid = np;
+        while (valid > 0 && keys[valid - 1] == 0xFFFFFFFFu) valid--;
+        runs[total] = valid;
+    }
+}
+
+// Block r < run count owns run r of the sorted keys: dst[token] += scale * (sum of the
+// run's source rows, in position order).
+__global__ __launch_bounds__(256) void scatter_rows_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                           long ld, int C, float scale, const int* __restrict__ work,
+                                                           int np) {
+    const int nrun = work[0];
+    const unsigned* keys = reinterpret_cast<const unsigned*>(work + 1);
+    const int* runs = work + 1 + np;
+    for (int r = blockIdx.x; r < nrun; r += gridDim.x) {
+        const int j0 = runs[r], j1 = runs[r + 1];
+        const int v = (int)(keys[j0] >> 16);
+        for (int c4 = threadIdx.x; c4 < C / 4; c4 += blockDim.x) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            int j = j0;
+            for (; j + 4 <= j1; j += 4) {
+                float4 d[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    d[u] = reinterpret_cast<const float4*>(src + (long)(keys[j + u] & 0xFFFFu) * ld)[c4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    acc.x += d[u].x;
+                    acc.y += d[u].y;
+                    acc.z += d[u].z;
+                    acc.w += d[u].w;
+                }
+            }
+            for (; j < j1; j++) {
+                const float4 d = reinterpret_cast<const float4*>(src + (long)(keys[j] & 0xFFFFu) * ld)[c4];
+                acc.x += d.x;
+                acc.y += d.y;
+                acc.z += d.z;
+                acc.w += d.w;
+            }
+            float4* o = reinterpret_cast<float4*>(dst + (long)v * C) + c4;
+            float4 w = *o;
+            w.x += scale * acc.x;
+            w.y += scale * acc.y;
+            w.z += scale * acc.z;
+            w.w += scale * acc.w;
+            *o = w;
+        }
+    }
+}
 
 }  // namespace
 
@@ -150,9 +275,43 @@ hipError_t encoder_forward(float* out, const int32_t* tok, const float* wte, con
     return hipGetLastError();
 }
 
-// `work` is an int scratch of 1 + B*T entries.
+size_t encoder_backward_work_ints(long BT) {
+    if (BT <= SORT_MAX) return 2 + 2 * (size_t)pow2_at_least((int)std::max<long>(BT, 2));
+    return 1 + (size_t)BT;
+}
+
+hipError_t embedding_scatter(float* dwte, int V, int C, const int32_t* tok, int n, const float* src, long ld,
+                             float scale, int* work, hipStream_t st) {
+    if (C % 4 || ld % 4 || C > 4096) return hipErrorInvalidValue;
+    if (n <= 0) return hipSuccess;
+    if (n <= SORT_MAX && V <= 65536) {
+        const int np = pow2_at_least(n);
+        {
+            ProfScope ps(st, "sort_tokens_kernel", 0.0, 4.0 * (n + 2.0 * np));
+            hipLaunchKernelGGL(sort_tokens_kernel, dim3(1), dim3(SORT_NT), 0, st, work, tok, n, np, V);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // rows read once; each touched wte row read and written once
+        ProfScope ps(st, "scatter_rows_kernel", 0.0, 4.0 * ((double)n * C + 2.0 * (double)std::min(n, V) * C));
+        hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)std::min(n, 4096)), dim3(256), 0, st, dwte, src, ld, C,
+                           scale, (const int*)work, np);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, st, work);
+    {
+        ProfScope ps(st, "first_occurrence_kernel", 0.0, 4.0 * n);
+        hipLaunchKernelGGL(first_occurrence_kernel, dim3((n + 255) / 256), dim3(256), 0, st, work, tok, n, V);
+    }
+    // rows of src read once; each touched wte row read and written once (at most n rows)
+    ProfScope ps(st, "wte_bwd_kernel", 0.0, 4.0 * ((double)n * C + n));
+    hipLaunchKernelGGL(wte_bwd_kernel, dim3(n), dim3(256), 0, st, dwte, src, ld, scale, tok, (const int*)work, n, C);
+    return hipGetLastError();
+}
+
+// `work` is an int scratch of encoder_backward_work_ints(B*T) entries.
 hipError_t encoder_backward_ws(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
-                               int B, int T, int C, int* work, hipStream_t st) {
+                               int B, int T, int C, int V, int* work, hipStream_t st) {
     const int BT = B * T;
     if (C % 4 || C > 4096) return hipErrorInvalidValue;
     if (BT == 0) return hipSuccess;
@@ -161,15 +320,9 @@ hipError_t encoder_backward_ws(float* dwte, float* dwpe, const float* dout, cons
         ProfScope ps(st, "wpe_bwd_kernel", 0.0, 4.0 * ((double)BT * C + 2.0 * T * C));
         hipLaunchKernelGGL(wpe_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dwpe, dout, B, T, C);
     }
-    hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, st, work);
-    {
-        ProfScope ps(st, "first_occurrence_kernel", 0.0, 4.0 * BT);
-        hipLaunchKernelGGL(first_occurrence_kernel, dim3((BT + 255) / 256), dim3(256), 0, st, work, tok, BT);
-    }
-    // rows of dout read once; each touched wte row read and written once (at most BT rows)
-    ProfScope ps(st, "wte_bwd_kernel", 0.0, 4.0 * ((double)BT * C + BT));
-    hipLaunchKernelGGL(wte_bwd_kernel, dim3(BT), dim3(256), 0, st, dwte, dout, tok, (const int*)work, BT, C);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return embedding_scatter(dwte, V, C, tok, BT, dout, C, 1.0f, work, st);
 }
 
 }  // namespace gpt2k

@@ -55,7 +55,7 @@ struct KTile {
     static constexpr int BK = A_K ? 32 : 16;
     static constexpr int STAGES = A_K ? 2 : 4;
 };
-constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse/target slots
+constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse slots
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
 constexpr int SLOT_FLOATS = BM * BN + BM;  // one partial tile + its bias-gradient row sums
@@ -328,7 +328,8 @@ GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows,
 // The logits operand of the LM-head backward: each logit z of row r in vocabulary column
 // c becomes d loss / d z = s * (exp(z - lse_r) - [c == target_r]), s = 1/rows.  The
 // first term is formed as 2^(z log2 e - (lse_r log2 e - log2 s)) on v_exp_f32 with the
-// row constant precomputed; the dgrad leaves the one-hot term to its epilogue.
+// row constant precomputed; the dgrad leaves the one-hot term to its epilogue and the
+// wgrad to its caller.
 constexpr float LOG2E = 1.4426950408889634f;
 GPT2_DEV float softmax_s(float z, float c2) { return __builtin_amdgcn_exp2f(fmaf(z, LOG2E, -c2)); }
 
@@ -410,11 +411,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
             else fill_rcontig<BN, BK>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
         }
         if (XR) {
-            // lanes 0..BK-1: lse of k rows k0.., lanes BK..2BK-1: their targets (copied as
-            // bits); any further lanes repeat the targets
-            const int kk = min(k0 + lane % BK, p.K - 1);
-            const void* src = lane >= BK ? (const void*)(p.tgt + kk) : (const void*)(p.lse + kk);
-            dma4(src, Sb + B_FLOATS + wave * 64);
+            // lanes 0..BK-1: lse of k rows k0.. (further lanes repeat them)
+            dma4(p.lse + min(k0 + lane % BK, p.K - 1), Sb + B_FLOATS + wave * 64);
         }
     };
     // the first STAGES-1 k-tiles of an item
@@ -503,19 +501,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
                 if (XR) {
                     const float* xs = Sb + B_FLOATS + wave * 64 + 16 * g + 4 * grp;
                     const float4 l4 = *reinterpret_cast<const float4*>(xs);
-                    const float4 t4 = *reinterpret_cast<const float4*>(xs + BK);
+                    // softmax term only: the caller subtracts the one-hot term
                     const float ls[4] = {fmaf(l4.x, LOG2E, -p.xlog2s), fmaf(l4.y, LOG2E, -p.xlog2s),
                                          fmaf(l4.z, LOG2E, -p.xlog2s), fmaf(l4.w, LOG2E, -p.xlog2s)};
-                    const int ts[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
 #pragma unroll
-                    for (int a = 0; a < 4; a++) {
-                        const int m = m0 + wm + 16 * a + li;
+                    for (int a = 0; a < 4; a++)
 #pragma unroll
-                        for (int s = 0; s < 4; s++) {
-                            const float e = softmax_s(fa[a][s], ls[s]);
-                            fa[a][s] = m == ts[s] ? e - p.xscale : e;
-                        }
-                    }
+                        for (int s = 0; s < 4; s++) fa[a][s] = softmax_s(fa[a][s], ls[s]);
                 }
                 if (!A_K && bias_rows) {
 #pragma unroll

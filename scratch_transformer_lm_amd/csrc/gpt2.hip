@@ -119,7 +119,7 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     y.dqkv = take(BT * 3 * C);
     y.dfch = take(BT * 4 * C);
     y.delta = take(BT * NH);
-    y.enc_work = take(1 + BT);
+    y.enc_work = take(encoder_backward_work_ints((long)BT));
     size_t np = gemm_partial_floats();
     np = std::max(np, layernorm_partial_floats((int)BT, (int)C));
     y.n_partial = np;
@@ -242,6 +242,9 @@ int backward_impl(gpt2* g) {
     const XentOperand xo{A(g, GPT2_ACT_LOGITS_LSE), tok_tgt(g), 1.0f / (float)BT};
     HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
     HIPCHK(g, linear_wgrad(G(g, P_WTE), nullptr, logits, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part, st, &xo));
+    // the one-hot part of dlogits: dwte[target] -= lnf / BT
+    HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale,
+                                reinterpret_cast<int*>(S(g, g->lay.enc_work)), st));
     HIPCHK(g, layernorm_backward(dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
                                  A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
     for (int l = L - 1; l >= 0; l--) {
@@ -270,7 +273,7 @@ int backward_impl(gpt2* g) {
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                                      A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
     }
-    HIPCHK(g, encoder_backward_ws(G(g, P_WTE), G(g, P_WPE), dres, tok_in(g), B, T, C,
+    HIPCHK(g, encoder_backward_ws(G(g, P_WTE), G(g, P_WPE), dres, tok_in(g), B, T, C, V,
                                   reinterpret_cast<int*>(S(g, g->lay.enc_work)), st));
     return GPT2_OK;
 }

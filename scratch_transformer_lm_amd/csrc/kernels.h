@@ -23,6 +23,8 @@ hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w
 // Marks a `dout` operand as logits whose gradient is formed while loading:
 // dlogit = (exp(z - lse[row]) - [col == targets[row]]) * scale.  The logits' padding
 // columns (up to the leading dimension) must be readable; their values are not used.
+// linear_dgrad applies both terms; linear_wgrad only the softmax term, leaving
+// dw[targets[row]] -= scale * inp[row] to the caller (embedding_scatter).
 struct XentOperand {
     const float* lse;
     const int32_t* targets;
@@ -51,9 +53,15 @@ hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, 
 // ---- embedding (encoder.hip) --------------------------------------------------------
 hipError_t encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe,
                            int B, int T, int C, int V, int* flags, hipStream_t st);
-// dwte/dwpe += ...; `work` is an int scratch of 1 + B*T entries.  Deterministic.
+// dwte/dwpe += ...; `work` is an int scratch of encoder_backward_work_ints(B*T) entries.
+// Deterministic.
+size_t encoder_backward_work_ints(long BT);
 hipError_t encoder_backward_ws(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
-                               int B, int T, int C, int* work, hipStream_t st);
+                               int B, int T, int C, int V, int* work, hipStream_t st);
+// dwte[tok[i]] += scale * src[i] (row stride ld) for i < n, each token's rows added in
+// position order; `work` as above for BT = n.
+hipError_t embedding_scatter(float* dwte, int V, int C, const int32_t* tok, int n, const float* src, long ld,
+                             float scale, int* work, hipStream_t st);
 
 // ---- attention (attention.hip) ------------------------------------------------------
 // qkv (B,T,3C) -> out (B,T,C), lse (B,NH,T).

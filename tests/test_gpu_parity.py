@@ -176,6 +176,24 @@ def test_smaller_batch_than_built(G):
     assert max(e.values()) <= GRAD_TOL, e
 
 
+@pytest.mark.parametrize("B,T", [(520, 64), (512, 64)])
+def test_embedding_backward_paths(G, B, T):
+    """B*T = 33280 takes the embedding backward's first-occurrence fallback (more positions
+    than its one-block sort holds), B*T = 32768 the largest sorted batch; one step against
+    the oracle, every gradient tensor."""
+    w = S.TINY
+    say(f"[embedding backward] B={B} T={T}")
+    params = S.init_params(w.model)
+    x, y = S.tokens(w, B=B, T=T, seed=11)
+    gr = gpu_run(G, w, params, x, y, 1, capture=(1,))
+    orc = run_oracle(w, params, x, y, 1, capture_steps=(1,))
+    assert np.all(np.abs(gr["losses"] - orc["losses"]) / orc["losses"] <= LOSS_RTOL)
+    m = gr["model"]
+    e = per_tensor(G.PARAM_NAMES, m.offsets, m.lengths, gr["grads"][1], orc["grads"][1])
+    say({k: f"{v:.1e}" for k, v in e.items()})
+    assert max(e.values()) <= GRAD_TOL, e
+
+
 # ------------------------------------------------------------------ full context (sampled)
 
 def full_context_check(G, w, rows):
