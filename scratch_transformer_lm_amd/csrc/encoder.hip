@@ -156,9 +156,13 @@ __global__ void zero_int_kernel(int* x) { *x = 0; }
 // sort last and are dropped), then lists the start of every run of equal tokens.
 // work: [0] run count, [1, 1+np) sorted keys, [1+np, ...) run starts, then the end of the
 // last run.
-__global__ __launch_bounds__(SORT_NT) void sort_tokens_kernel(int* __restrict__ work, const int32_t* __restrict__ tok,
+// Block b sorts list b (work_b, tok_b).
+__global__ __launch_bounds__(SORT_NT) void sort_tokens_kernel(int* __restrict__ work0, const int32_t* __restrict__ tok0,
+                                                              int* __restrict__ work1, const int32_t* __restrict__ tok1,
                                                               int n, int np, int V) {
     __shared__ unsigned keys[SORT_MAX];
+    int* work = blockIdx.x == 0 ? work0 : work1;
+    const int32_t* tok = blockIdx.x == 0 ? tok0 : tok1;
     __shared__ int wsum[SORT_NT / 64];
     const int tid = threadIdx.x;
     for (int i = tid; i < np; i += SORT_NT) {
@@ -219,47 +223,66 @@ __global__ __launch_bounds__(SORT_NT) void sort_tokens_kernel(int* __restrict__ 
 }
 
 // Block r < run count owns run r of the sorted keys: dst[token] += scale * (sum of the
-// run's source rows, in position order).
-__global__ __launch_bounds__(256) void scatter_rows_kernel(float* __restrict__ dst, const float* __restrict__ src,
-                                                           long ld, int C, float scale, const int* __restrict__ work,
-                                                           int np) {
+// run's source rows).  The block's G = blockDim / (C/4) thread groups each add every G-th
+// row of the run (8 rows in flight per thread), and the G partial sums are then added in
+// group order, so the result is the same on every run.
+constexpr int SCATTER_NT = 1024;
+__global__ __launch_bounds__(SCATTER_NT) void scatter_rows_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                                  long ld, int C, float scale,
+                                                                  const int* __restrict__ work, int np) {
+    __shared__ float4 part[SCATTER_NT];
     const int nrun = work[0];
     const unsigned* keys = reinterpret_cast<const unsigned*>(work + 1);
     const int* runs = work + 1 + np;
+    const int C4 = C / 4, G = SCATTER_NT / C4;
+    const int g = threadIdx.x / C4, c4 = threadIdx.x - g * C4;
     for (int r = blockIdx.x; r < nrun; r += gridDim.x) {
         const int j0 = runs[r], j1 = runs[r + 1];
         const int v = (int)(keys[j0] >> 16);
-        for (int c4 = threadIdx.x; c4 < C / 4; c4 += blockDim.x) {
+        if (g < G) {
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            int j = j0;
-            for (; j + 4 <= j1; j += 4) {
-                float4 d[4];
+            int j = j0 + g;
+            for (; j + 7 * G < j1; j += 8 * G) {
+                float4 d[8];
 #pragma unroll
-                for (int u = 0; u < 4; u++)
-                    d[u] = reinterpret_cast<const float4*>(src + (long)(keys[j + u] & 0xFFFFu) * ld)[c4];
+                for (int u = 0; u < 8; u++)
+                    d[u] = reinterpret_cast<const float4*>(src + (long)(keys[j + u * G] & 0xFFFFu) * ld)[c4];
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
+                for (int u = 0; u < 8; u++) {
                     acc.x += d[u].x;
                     acc.y += d[u].y;
                     acc.z += d[u].z;
                     acc.w += d[u].w;
                 }
             }
-            for (; j < j1; j++) {
+            for (; j < j1; j += G) {
                 const float4 d = reinterpret_cast<const float4*>(src + (long)(keys[j] & 0xFFFFu) * ld)[c4];
                 acc.x += d.x;
                 acc.y += d.y;
                 acc.z += d.z;
                 acc.w += d.w;
             }
+            part[threadIdx.x] = acc;
+        }
+        __syncthreads();
+        if (g == 0) {
+            float4 t = part[c4];
+            for (int h = 1; h < G; h++) {
+                const float4 q = part[h * C4 + c4];
+                t.x += q.x;
+                t.y += q.y;
+                t.z += q.z;
+                t.w += q.w;
+            }
             float4* o = reinterpret_cast<float4*>(dst + (long)v * C) + c4;
             float4 w = *o;
-            w.x += scale * acc.x;
-            w.y += scale * acc.y;
-            w.z += scale * acc.z;
-            w.w += scale * acc.w;
+            w.x += scale * t.x;
+            w.y += scale * t.y;
+            w.z += scale * t.z;
+            w.w += scale * t.w;
             *o = w;
         }
+        __syncthreads();
     }
 }
 
@@ -280,23 +303,38 @@ size_t encoder_backward_work_ints(long BT) {
     return 1 + (size_t)BT;
 }
 
+bool embedding_sortable(int n, int V) { return n <= SORT_MAX && V <= 65536; }
+
+hipError_t sort_token_lists(int* work0, const int32_t* tok0, int* work1, const int32_t* tok1, int n, int V,
+                            hipStream_t st) {
+    if (!embedding_sortable(n, V)) return hipErrorInvalidValue;
+    if (n <= 0) return hipSuccess;
+    const int np = pow2_at_least(n);
+    const int lists = tok1 ? 2 : 1;
+    ProfScope ps(st, "sort_tokens_kernel", 0.0, 4.0 * lists * (n + 2.0 * np));
+    hipLaunchKernelGGL(sort_tokens_kernel, dim3(lists), dim3(SORT_NT), 0, st, work0, tok0, work1, tok1, n, np, V);
+    return hipGetLastError();
+}
+
+hipError_t scatter_sorted(float* dwte, int C, const float* src, long ld, float scale, const int* work, int n,
+                          hipStream_t st) {
+    if (C % 4 || ld % 4 || C > 4 * SCATTER_NT) return hipErrorInvalidValue;
+    if (n <= 0) return hipSuccess;
+    // rows read once; each touched wte row read and written once
+    ProfScope ps(st, "scatter_rows_kernel", 0.0, 4.0 * ((double)n * C + 2.0 * (double)n * C));
+    hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)std::min(n, 2048)), dim3(SCATTER_NT), 0, st, dwte, src, ld,
+                       C, scale, work, pow2_at_least(n));
+    return hipGetLastError();
+}
+
 hipError_t embedding_scatter(float* dwte, int V, int C, const int32_t* tok, int n, const float* src, long ld,
                              float scale, int* work, hipStream_t st) {
     if (C % 4 || ld % 4 || C > 4096) return hipErrorInvalidValue;
     if (n <= 0) return hipSuccess;
-    if (n <= SORT_MAX && V <= 65536) {
-        const int np = pow2_at_least(n);
-        {
-            ProfScope ps(st, "sort_tokens_kernel", 0.0, 4.0 * (n + 2.0 * np));
-            hipLaunchKernelGGL(sort_tokens_kernel, dim3(1), dim3(SORT_NT), 0, st, work, tok, n, np, V);
-        }
-        hipError_t e = hipGetLastError();
+    if (embedding_sortable(n, V)) {
+        hipError_t e = sort_token_lists(work, tok, nullptr, nullptr, n, V, st);
         if (e != hipSuccess) return e;
-        // rows read once; each touched wte row read and written once
-        ProfScope ps(st, "scatter_rows_kernel", 0.0, 4.0 * ((double)n * C + 2.0 * (double)std::min(n, V) * C));
-        hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)std::min(n, 4096)), dim3(256), 0, st, dwte, src, ld, C,
-                           scale, (const int*)work, np);
-        return hipGetLastError();
+        return scatter_sorted(dwte, C, src, ld, scale, work, n, st);
     }
     hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, st, work);
     {
@@ -309,20 +347,13 @@ hipError_t embedding_scatter(float* dwte, int V, int C, const int32_t* tok, int 
     return hipGetLastError();
 }
 
-// `work` is an int scratch of encoder_backward_work_ints(B*T) entries.
-hipError_t encoder_backward_ws(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
-                               int B, int T, int C, int V, int* work, hipStream_t st) {
-    const int BT = B * T;
-    if (C % 4 || C > 4096) return hipErrorInvalidValue;
-    if (BT == 0) return hipSuccess;
+hipError_t wpe_backward(float* dwpe, const float* dout, int B, int T, int C, hipStream_t st) {
+    if (C % 4) return hipErrorInvalidValue;
     const long n = (long)T * (C / 4);
-    {
-        ProfScope ps(st, "wpe_bwd_kernel", 0.0, 4.0 * ((double)BT * C + 2.0 * T * C));
-        hipLaunchKernelGGL(wpe_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dwpe, dout, B, T, C);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return embedding_scatter(dwte, V, C, tok, BT, dout, C, 1.0f, work, st);
+    if ((long)B * T == 0) return hipSuccess;
+    ProfScope ps(st, "wpe_bwd_kernel", 0.0, 4.0 * ((double)B * T * C + 2.0 * T * C));
+    hipLaunchKernelGGL(wpe_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dwpe, dout, B, T, C);
+    return hipGetLastError();
 }
 
 }  // namespace gpt2k

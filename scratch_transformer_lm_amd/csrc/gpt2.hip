@@ -66,7 +66,7 @@ struct Layout {
     size_t tok_in, tok_tgt;  // int32 arrays inside acts (offset in 4-byte words)
     size_t n_acts;
     // grad_scratch
-    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, partial, n_partial, n_scratch;
+    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, n_scratch;
 };
 
 Layout make_layout(const gpt2_config* c, int B, int T) {
@@ -119,7 +119,8 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     y.dqkv = take(BT * 3 * C);
     y.dfch = take(BT * 4 * C);
     y.delta = take(BT * NH);
-    y.enc_work = take(encoder_backward_work_ints((long)BT));
+    y.enc_work = take(encoder_backward_work_ints((long)BT));      // input tokens
+    y.enc_work_tgt = take(encoder_backward_work_ints((long)BT));  // target tokens
     size_t np = gemm_partial_floats();
     np = std::max(np, layernorm_partial_floats((int)BT, (int)C));
     y.n_partial = np;
@@ -236,6 +237,13 @@ int backward_impl(gpt2* g) {
     float* dfch = S(g, g->lay.dfch);
     float* logits = A(g, GPT2_ACT_LOGITS);
 
+    // wte receives rows by token twice (targets' lnf rows below, inputs' residual-gradient
+    // rows at the end): both token lists are sorted once, up front
+    int* wk_in = reinterpret_cast<int*>(S(g, g->lay.enc_work));
+    int* wk_tgt = reinterpret_cast<int*>(S(g, g->lay.enc_work_tgt));
+    const bool sorted = embedding_sortable(BT, V);
+    if (sorted) HIPCHK(g, sort_token_lists(wk_in, tok_in(g), wk_tgt, tok_tgt(g), BT, V, st));
+
     // LM head (tied): dlnf = dlogits . wte;  dwte += dlogits^T . lnf, where
     // dlogits = (softmax(logits) - onehot(target)) / (B*T) is formed as the GEMMs load the
     // logits (softmax = exp(logit - lse)).
@@ -243,8 +251,8 @@ int backward_impl(gpt2* g) {
     HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
     HIPCHK(g, linear_wgrad(G(g, P_WTE), nullptr, logits, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part, st, &xo));
     // the one-hot part of dlogits: dwte[target] -= lnf / BT
-    HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale,
-                                reinterpret_cast<int*>(S(g, g->lay.enc_work)), st));
+    if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, BT, st));
+    else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, st));
     HIPCHK(g, layernorm_backward(dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
                                  A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
     for (int l = L - 1; l >= 0; l--) {
@@ -273,8 +281,9 @@ int backward_impl(gpt2* g) {
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                                      A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
     }
-    HIPCHK(g, encoder_backward_ws(G(g, P_WTE), G(g, P_WPE), dres, tok_in(g), B, T, C, V,
-                                  reinterpret_cast<int*>(S(g, g->lay.enc_work)), st));
+    HIPCHK(g, wpe_backward(G(g, P_WPE), dres, B, T, C, st));
+    if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, dres, C, 1.0f, wk_in, BT, st));
+    else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_in(g), BT, dres, C, 1.0f, wk_in, st));
     return GPT2_OK;
 }
 

@@ -53,15 +53,23 @@ hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, 
 // ---- embedding (encoder.hip) --------------------------------------------------------
 hipError_t encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe,
                            int B, int T, int C, int V, int* flags, hipStream_t st);
-// dwte/dwpe += ...; `work` is an int scratch of encoder_backward_work_ints(B*T) entries.
-// Deterministic.
+// Backward scatter-adds into wte, deterministic (each token's rows added in position
+// order).  `work` is an int scratch of encoder_backward_work_ints(n) entries per list.
 size_t encoder_backward_work_ints(long BT);
-hipError_t encoder_backward_ws(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
-                               int B, int T, int C, int V, int* work, hipStream_t st);
-// dwte[tok[i]] += scale * src[i] (row stride ld) for i < n, each token's rows added in
-// position order; `work` as above for BT = n.
+// Lists of up to 32768 positions with V <= 65536 go through a one-block sort.
+bool embedding_sortable(int n, int V);
+// Sorts the (token, position) pairs of tok0 (and of tok1 unless null) into work0 (work1),
+// one launch; ids outside [0, V) are dropped.
+hipError_t sort_token_lists(int* work0, const int32_t* tok0, int* work1, const int32_t* tok1, int n, int V,
+                            hipStream_t st);
+// dwte[token] += scale * src[position] (row stride ld) over a list sorted as above.
+hipError_t scatter_sorted(float* dwte, int C, const float* src, long ld, float scale, const int* work, int n,
+                          hipStream_t st);
+// The same for a list of any size (sorts first, or falls back to a first-occurrence scan).
 hipError_t embedding_scatter(float* dwte, int V, int C, const int32_t* tok, int n, const float* src, long ld,
                              float scale, int* work, hipStream_t st);
+// dwpe[t] += sum over b of dout[b, t].
+hipError_t wpe_backward(float* dwpe, const float* dout, int B, int T, int C, hipStream_t st);
 
 // ---- attention (attention.hip) ------------------------------------------------------
 // qkv (B,T,3C) -> out (B,T,C), lse (B,NH,T).
