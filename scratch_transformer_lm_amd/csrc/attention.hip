@@ -19,6 +19,8 @@
 // read.  K/V (or Q/dO) tiles are double-buffered in LDS with register prefetch.
 // dq and dk/dv come from two kernels (query-tile and key-tile ownership) so every
 // output element has one writer: no atomics, bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -104,7 +106,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
     tile_store<HS>(Ks[0], kreg);
     tile_store<HS>(Vs[0], vreg);
     __syncthreads();
-    for (int kt = 0; kt < nkt; kt++) {
+    // one key tile; only the diagonal tile (kt == qt) has keys after the query
+    auto step = [&](int kt, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
         const int cur = kt & 1;
         if (kt + 1 < nkt) {
             tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
@@ -125,14 +129,14 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
             }
         }
         // lane holds scores of query tq against keys kt*64 + kb*16 + 4*g4 + v, in base-2
-        // units; only the diagonal tile (kt == qt) has keys after the query
+        // units
         float mx = m;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int key = kt * TILE + kb * 16 + 4 * g4 + v;
-                const float x = (kt < qt || key <= tq) ? s[kb][v] * scale2 : -INFINITY;
+                const float x = (!DIAG || key <= tq) ? s[kb][v] * scale2 : -INFINITY;
                 s[kb][v] = x;
                 mx = fmaxf(mx, x);
             }
@@ -173,7 +177,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
             tile_store<HS>(Vs[cur ^ 1], vreg);
         }
         __syncthreads();
-    }
+    };
+    for (int kt = 0; kt < qt; kt++) step(kt, std::false_type{});
+    step(qt, std::true_type{});
     const float linv = 1.0f / l;
 #pragma unroll
     for (int v = 0; v < 4; v++) {
@@ -240,7 +246,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
     tile_store<HS>(Ks[0], kreg);
     tile_store<HS>(Vs[0], vreg);
     __syncthreads();
-    for (int kt = 0; kt < nkt; kt++) {
+    // one key tile; only the diagonal tile (kt == qt) has keys after the query
+    auto step = [&](int kt, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
         const int cur = kt & 1;
         if (kt + 1 < nkt) {
             tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int key = kt * TILE + kb * 16 + 4 * g4 + v;
-                const float p = (kt < qt || key <= tq) ? exp2_hw(s[v] * scale2 - L2) : 0.f;
+                const float p = (!DIAG || key <= tq) ? exp2_hw(s[v] * scale2 - L2) : 0.f;
                 ds[v] = p * (dp[v] - D);
             }
 #pragma unroll
@@ -281,7 +289,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
             tile_store<HS>(Vs[cur ^ 1], vreg);
         }
         __syncthreads();
-    }
+    };
+    for (int kt = 0; kt < qt; kt++) step(kt, std::false_type{});
+    step(qt, std::true_type{});
 #pragma unroll
     for (int v = 0; v < 4; v++) {
         const int q = q0 + 4 * g4 + v;
@@ -355,7 +365,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
     tile_store<HS>(Os[0], oreg);
     store_side(0);
     __syncthreads();
-    for (int qt = kt; qt < nqt; qt++) {
+    // one query tile; only the diagonal tile (qt == kt) has queries before the key
+    auto step = [&](int qt, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
         const int cur = (qt - kt) & 1;
         if (qt + 1 < nqt) {
             tile_load<HS>(qreg, base + h * HS, ld, (qt + 1) * TILE, T);
@@ -383,7 +395,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
             for (int v = 0; v < 4; v++) {
                 const int qi = qb * 16 + 4 * g4 + v;
                 const int q = qt * TILE + qi;
-                const float pv = (qt > kt || tu <= q) ? exp2_hw(s[v] * scale2 - Ls[cur][qi]) : 0.f;
+                const float pv = (!DIAG || tu <= q) ? exp2_hw(s[v] * scale2 - Ls[cur][qi]) : 0.f;
                 p[v] = pv;
                 ds[v] = pv * (dp[v] - Ds[cur][qi]);
             }
@@ -405,7 +417,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
             store_side(cur ^ 1);
         }
         __syncthreads();
-    }
+    };
+    step(kt, std::true_type{});
+    for (int qt = kt + 1; qt < nqt; qt++) step(qt, std::false_type{});
 #pragma unroll
     for (int v = 0; v < 4; v++) {
         const int u = u0 + 4 * g4 + v;
