@@ -128,41 +128,46 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
                 for (int st = 0; st < 4; st++) s[kb] = mfma4(comp(kf, st), comp(qreg[g], st), s[kb]);
             }
         }
-        // lane holds scores of query tq against keys kt*64 + kb*16 + 4*g4 + v, in base-2
-        // units
-        float mx = m;
+        // lane holds raw scores of query tq against keys kt*64 + kb*16 + 4*g4 + v
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                const int key = kt * TILE + kb * 16 + 4 * g4 + v;
-                const float x = (!DIAG || key <= tq) ? s[kb][v] * scale2 : -INFINITY;
-                s[kb][v] = x;
-                mx = fmaxf(mx, x);
+                if (DIAG && kt * TILE + kb * 16 + 4 * g4 + v > tq) s[kb][v] = -INFINITY;
+                mx = fmaxf(mx, s[kb][v]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float alpha = exp2_hw(m - mx);
+        // The reference max m (base 2) of each row moves only when the row's new max
+        // exceeds it by more than 8, i.e. probabilities relative to m stay below 2^8; the
+        // result is the same softmax, and O is rescaled only on the (rare, wave-wide)
+        // occasions when some row's reference moves.
+        const float mnew = fmaxf(m, mx * scale2);
+        if (__any(mnew > m + 8.0f)) {
+            const float alpha = exp2_hw(m - mnew);
+            l *= alpha;
+            m = mnew;
+            // O rows are queries 4*g4 + v of the wave: rescale with their alpha.
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const float a = __shfl(alpha, 4 * g4 + v, 64);
+#pragma unroll
+                for (int d = 0; d < DG; d++) o[d][v] *= a;
+            }
+        }
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                const float p = exp2_hw(s[kb][v] - mx);
+                const float p = exp2_hw(fmaf(s[kb][v], scale2, -m));
                 s[kb][v] = p;
                 rs += p;
             }
         rs += __shfl_xor(rs, 16, 64);
         rs += __shfl_xor(rs, 32, 64);
-        l = l * alpha + rs;
-        m = mx;
-        // O rows are queries 4*g4 + v of the wave: rescale with their alpha.
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const float a = __shfl(alpha, 4 * g4 + v, 64);
-#pragma unroll
-            for (int d = 0; d < DG; d++) o[d][v] *= a;
-        }
+        l += rs;
         // O += P V
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int key = kt * TILE + kb * 16 + 4 * g4 + v;
-                const float p = (!DIAG || key <= tq) ? exp2_hw(s[v] * scale2 - L2) : 0.f;
+                const float p = (!DIAG || key <= tq) ? exp2_hw(fmaf(s[v], scale2, -L2)) : 0.f;
                 ds[v] = p * (dp[v] - D);
             }
 #pragma unroll
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
             for (int v = 0; v < 4; v++) {
                 const int qi = qb * 16 + 4 * g4 + v;
                 const int q = qt * TILE + qi;
-                const float pv = (!DIAG || tu <= q) ? exp2_hw(s[v] * scale2 - Ls[cur][qi]) : 0.f;
+                const float pv = (!DIAG || tu <= q) ? exp2_hw(fmaf(s[v], scale2, -Ls[cur][qi])) : 0.f;
                 p[v] = pv;
                 ds[v] = pv * (dp[v] - Ds[cur][qi]);
             }
