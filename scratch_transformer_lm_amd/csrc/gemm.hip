@@ -58,6 +58,7 @@ struct KTile {
 constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse slots
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
+constexpr int MAX_UNITS = 1536;                  // split-K units the partial region holds
 constexpr int SLOT_FLOATS = BM * BN + BM;  // one partial tile + its bias-gradient row sums
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -79,7 +80,7 @@ struct Params {
     long ldaux;
     float* pre;         // pre-GELU output (EPI_BIAS_GELU)
     long ldpre;
-    float* partial;     // 2 partial slots per block
+    float* partial;     // partial-tile slots
     float* dbias;       // wgrad: db[m] += sum over k of A(m, k), by the tiles with n0 == 0
     const float* lse;   // dlogits operand: per-row log-sum-exp of the logits
     const int32_t* tgt; // dlogits operand: per-row target id
@@ -92,6 +93,8 @@ struct Params {
     int skt;            // tiles in the split region
     long total;         // skt * nk iterations of the split region
     int nr;             // ranges the split region is cut into (<= G), range lb for block lb
+    int S;              // > 1: split-K rounds instead (units = tiles * S, see schedule)
+    int units;
 };
 
 GPT2_DEV long range_start(long total, int G, int lb) { return (long)lb * total / G; }
@@ -225,6 +228,11 @@ GPT2_DEV void dma16(const float* g, float* lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                  ::"s"(__builtin_amdgcn_readfirstlane(lds_offset(lds))), "v"(g) : "memory", "m0");
 }
+// Same with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset, so
+// that moving to the next k-tile is a scalar add.
+GPT2_DEV void dma16s(const char* base, unsigned off, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
 GPT2_DEV void dma4(const void* g, float* lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  ::"s"(__builtin_amdgcn_readfirstlane(lds_offset(lds))), "v"(g) : "memory", "m0");
@@ -238,11 +246,14 @@ template <int BK>
 GPT2_DEV int kswz(int r) { return (r >> 1) & (BK / 4 - 1); }
 GPT2_DEV int rswz(int kr) { return ((kr >> 2) & 3) << 2; }
 
-// k-contiguous operand X[r*ld + k]: ROWS rows r0.. (clamped to rmax: such rows only
-// feed outputs that are never stored), k = k0..k0+15 (all < K).  Each wave transfer
-// covers 16 rows.
+// Per-lane byte offsets of a tile's transfers from the tile's base, the operand element
+// (row r0, k 0) for a k-contiguous operand X[r*ld + k] or (k 0, row r0) for a
+// row-contiguous one X[k*ld + r].  A k-tile is then base + kstep * (its k stride), and
+// wave transfer j of wave w fills LDS chunk q = 4j + w (1 KB).
+//  k-contiguous: transfer q covers 16 rows (BK = 16: 64/KC rows); rows past rmax are
+//  clamped to it (they only feed outputs that are never stored).
 template <int ROWS, int BK>
-GPT2_DEV void issue_kcontig(float* S, const float* X, long ld, int r0, int rmax, int k0) {
+GPT2_DEV void kcontig_offsets(unsigned (&off)[ROWS * BK / 1024], long ld, int r0, int rmax) {
     constexpr int KC = BK / 4;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
@@ -251,15 +262,14 @@ GPT2_DEV void issue_kcontig(float* S, const float* X, long ld, int r0, int rmax,
         const int R = q * (64 / KC) + l / KC;
         const int c = (l % KC) ^ kswz<BK>(R);
         const int r = min(r0 + R, rmax);
-        dma16(X + (long)r * ld + k0 + 4 * c, S + q * 256);
+        off[j] = (unsigned)(((long)(r - r0) * ld + 4 * c) * 4);
     }
 }
 
-// row-contiguous operand X[k*ld + r]: k = k0..k0+15 (clamped to kmax), ROWS rows r0.. in
-// float4 groups clamped to rmax4 (a multiple of 4 inside the row).  Each wave transfer
-// covers 256/ROWS k rows.
+//  row-contiguous: transfer q covers 256/ROWS k rows; float4 row groups are clamped to
+//  rmax4 (a multiple of 4 inside the row).
 template <int ROWS, int BK>
-GPT2_DEV void issue_rcontig(float* S, const float* X, long ld, int r0, int rmax4, int k0, int kmax) {
+GPT2_DEV void rcontig_offsets(unsigned (&off)[ROWS * BK / 1024], long ld, int r0, int rmax4) {
     constexpr int CH = ROWS / 4;  // 16-byte chunks per k row
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
@@ -268,8 +278,7 @@ GPT2_DEV void issue_rcontig(float* S, const float* X, long ld, int r0, int rmax4
         const int kr = q * (64 / CH) + l / CH;
         const int c = (l % CH) ^ rswz(kr);
         const int r = min(r0 + 4 * c, rmax4);
-        const int k = min(k0 + kr, kmax);
-        dma16(X + (long)k * ld + r, S + q * 256);
+        off[j] = (unsigned)(((long)kr * ld + (r - r0)) * 4);
     }
 }
 
@@ -339,7 +348,7 @@ GPT2_DEV void wait_vm() {
 }
 
 template <bool A_K, bool B_K, int EPI, bool XF>
-__global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
+__global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
     constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
     constexpr int BK = KTile<A_K>::BK, STAGES = KTile<A_K>::STAGES;
     constexpr int A_FLOATS = BM * BK, B_FLOATS = BN * BK;  // the operands' k-tiles in LDS
@@ -375,7 +384,18 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     };
     auto next_item = [&](Item& w) -> bool {
         w.slot = nullptr;
-        if (r < p.R) {
+        if (p.S > 1) {
+            // split-K rounds: unit u = r*G + lb is k-segment u / tiles of tile u % tiles
+            const int u = r * p.G + lb;
+            if (u >= p.units) return false;
+            const int tiles = p.tiles_m * p.tiles_n;
+            const int sg = u / tiles;
+            w.tile = u - sg * tiles;
+            w.ks = (int)((long)sg * p.nk / p.S);
+            w.ke = (int)((long)(sg + 1) * p.nk / p.S);
+            w.slot = p.partial + (long)u * SLOT_FLOATS;
+            r++;
+        } else if (r < p.R) {
             w.tile = r * p.G + lb;
             w.ks = 0;
             w.ke = p.nk;
@@ -395,15 +415,25 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
         return true;
     };
 
+    // per-lane transfer offsets of the current item's tile (set by prologue)
+    unsigned offA[BM * BK / 1024], offB[BN * BK / 1024];
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](int buf, int kstep, int m0, int n0) {
         float* Sa = smem + buf * STAGE_FLOATS;
         float* Sb = Sa + A_FLOATS;
         const int k0 = kstep * BK;
         if (kstep < kfull) {
-            if (A_K) issue_kcontig<BM, BK>(Sa, p.A, p.lda, m0, rmaxA, k0);
-            else issue_rcontig<BM, BK>(Sa, p.A, p.lda, m0, rmaxA, k0, p.K - 1);
-            if (B_K) issue_kcontig<BN, BK>(Sb, p.B, p.ldb, n0, rmaxB, k0);
-            else issue_rcontig<BN, BK>(Sb, p.B, p.ldb, n0, rmaxB, k0, p.K - 1);
+            const char* ba = reinterpret_cast<const char*>(p.A) +
+                             (A_K ? (long)m0 * p.lda + k0 : (long)k0 * p.lda + m0) * 4;
+            const char* bb = reinterpret_cast<const char*>(p.B) +
+                             (B_K ? (long)n0 * p.ldb + k0 : (long)k0 * p.ldb + n0) * 4;
+            const unsigned la = lds0 + (unsigned)(buf * STAGE_FLOATS) * 4 + (unsigned)wave_u * 1024;
+            const unsigned lb_ = la + A_FLOATS * 4;
+#pragma unroll
+            for (int j = 0; j < BM * BK / 1024; j++) dma16s(ba, offA[j], la + j * 4096);
+#pragma unroll
+            for (int j = 0; j < BN * BK / 1024; j++) dma16s(bb, offB[j], lb_ + j * 4096);
         } else {
             if (A_K) fill_kcontig<BM, BK>(Sa, p.A, p.lda, m0, p.M, k0, p.K);
             else fill_rcontig<BM, BK>(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
@@ -417,6 +447,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
     };
     // the first STAGES-1 k-tiles of an item
     auto prologue = [&](const Item& w) {
+        if (A_K) kcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
+        else rcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
+        if (B_K) kcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
+        else rcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
 #pragma unroll
         for (int s = 0; s < STAGES - 1; s++)
             if (s < w.ke - w.ks) issue(s, w.ks + s, w.m0, w.n0);
@@ -614,6 +648,33 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
     }
 }
 
+// Split-K rounds: four blocks per tile, one per row of 16x16 blocks (a) of the waves'
+// sub-tiles, add the tile's S partials in k order and run the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(NT) void gemm_splitk_fixup_kernel(Params p) {
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int tile = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sg = 0; sg < p.S; sg++) {
+        const float* slot = p.partial + ((long)sg * tiles + tile) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
+        float v[4 * NB];
+#pragma unroll
+        for (int e = 0; e < 4 * NB; e++) v[e] = slot[e * NT];
+#pragma unroll
+        for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[e];
+    }
+    int m0, n0;
+    tile_coords(p, tile, m0, n0);
+    epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter);
+    if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
+        float sum = 0.f;
+        for (int sg = 0; sg < p.S; sg++) sum += p.partial[((long)sg * tiles + tile) * SLOT_FLOATS + BM * BN + threadIdx.x];
+        p.dbias[m0 + threadIdx.x] += sum;
+    }
+}
+
 // Kernel name as profilers print the instantiation.
 template <bool A_K, bool B_K, int EPI, bool XF>
 const char* gemm_name() {
@@ -629,11 +690,28 @@ const char* fixup_name() {
     return s.c_str();
 }
 
+template <int EPI>
+const char* splitk_fixup_name() {
+    static const std::string s = "gemm_splitk_fixup_kernel<" + std::to_string(EPI) + ">";
+    return s.c_str();
+}
+
 // Work distribution over a persistent grid of up to RESIDENT blocks: whole-tile rounds
 // while at least RESIDENT tiles remain, then equal ranges of the rest.
-void schedule(Params& p, long tiles) {
+void schedule(Params& p, long tiles, int split) {
     p.R = 0;
     p.tile0 = 0;
+    p.S = 0;
+    p.units = 0;
+    if (split > 1 && p.partial != nullptr && tiles * split <= MAX_UNITS && split <= p.nk) {
+        p.S = split;
+        p.units = (int)tiles * split;
+        p.G = std::min(RESIDENT, p.units);
+        p.nr = 0;
+        p.skt = 0;
+        p.total = 0;
+        return;
+    }
     if (p.partial == nullptr) {  // nowhere to put partial tiles: one tile per block
         p.G = (int)tiles;
         p.R = 1;
@@ -655,7 +733,7 @@ void schedule(Params& p, long tiles) {
 }
 
 template <bool A_K, bool B_K, int EPI, bool XF = false>
-hipError_t launch(Params& p, hipStream_t st) {
+hipError_t launch(Params& p, hipStream_t st, int split = 0) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
     p.nk = (p.K + KTile<A_K>::BK - 1) / KTile<A_K>::BK;
@@ -665,7 +743,7 @@ hipError_t launch(Params& p, hipStream_t st) {
         // empty reduction: every output is the epilogue of 0
         p.nk = 1;
     }
-    schedule(p, tiles);
+    schedule(p, tiles, split);
     const double mn = (double)p.M * p.N;
     const double extra = (EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_BIAS_GELU ||
                           EPI == EPI_DLOGITS) ? mn : 0.0;
@@ -675,7 +753,10 @@ hipError_t launch(Params& p, hipStream_t st) {
                      4.0 * ((double)p.M * p.K + (double)p.N * p.K + mn + extra));
         hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF>), dim3(p.G), dim3(NT), 0, st, p);
     }
-    if (p.nr > 1 && !(p.total % p.nr == 0 && (p.total / p.nr) % p.nk == 0)) {
+    if (p.S > 1) {
+        ProfScope ps(st, splitk_fixup_name<EPI>(), 0.0, 4.0 * ((double)p.units * SLOT_FLOATS + extra));
+        hipLaunchKernelGGL((gemm_splitk_fixup_kernel<EPI>), dim3(4 * (p.units / p.S)), dim3(NT), 0, st, p);
+    } else if (p.nr > 1 && !(p.total % p.nr == 0 && (p.total / p.nr) % p.nk == 0)) {
         ProfScope ps(st, fixup_name<EPI>(), 0.0, 4.0 * (2.0 * p.nr * SLOT_FLOATS + extra));
         hipLaunchKernelGGL((gemm_fixup_kernel<EPI>), dim3(4 * (p.nr - 1)), dim3(NT), 0, st, p);
     }
@@ -684,9 +765,22 @@ hipError_t launch(Params& p, hipStream_t st) {
 
 bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
 
+// k-split factor that turns a shape with fewer tiles than resident blocks and a long k
+// extent into whole rounds of split-K units (e.g. 384 tiles -> 4 segments, 3 rounds); 0
+// when there is none (stream-K then).
+template <bool A_K>
+int pick_split(int M, int N, int K) {
+    const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int nk = (K + KTile<A_K>::BK - 1) / KTile<A_K>::BK;
+    if (tiles == 0 || tiles >= RESIDENT) return 0;
+    for (int s = 2; s <= 8; s++)
+        if ((tiles * s) % RESIDENT == 0 && tiles * s <= MAX_UNITS && nk >= 16 * s) return s;
+    return 0;
+}
+
 }  // namespace
 
-size_t gemm_partial_floats() { return (size_t)RESIDENT * 2 * SLOT_FLOATS; }
+size_t gemm_partial_floats() { return (size_t)std::max(RESIDENT * 2, MAX_UNITS) * SLOT_FLOATS; }
 
 hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
@@ -744,7 +838,9 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
         if (!(xent->scale > 0.f)) return hipErrorInvalidValue;
         p.xscale = xent->scale;
         p.xlog2s = (float)std::log2((double)xent->scale);
-        return launch<true, false, EPI_DLOGITS, true>(p, st);
+        // a long k extent over few tiles: split-K rounds keep the blocks of an XCD on the
+        // same k-segment of neighbouring tiles, so they share the logits and wte panels
+        return launch<true, false, EPI_DLOGITS, true>(p, st, pick_split<true>(M, N, K));
     }
     return launch<true, false, EPI_STORE>(p, st);
 }
