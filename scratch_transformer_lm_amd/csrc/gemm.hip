@@ -124,8 +124,8 @@ GPT2_DEV void tile_coords(const Params& p, int tile, int& m0, int& n0) {
 // row's outputs are stored, and a row's 16 (or 32) stores go out back to back, so the
 // memory operations overlap instead of each waiting for the one before.  CHECK: the tile
 // crosses the edge of C, so rows and columns are bounds-checked.
-template <int EPI, int NA, bool CHECK>
-GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, int a0) {
+template <int EPI, int NA, bool CHECK, class Pre>
+GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, int a0, Pre&& pre) {
     constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
     constexpr bool READS = EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_DLOGITS;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -167,6 +167,7 @@ GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, 
     };
     float in[2][NB][4];
     if (READS) load_row(in[0], 0);
+    pre();  // the caller's last step before the outputs are formed (the fix-up's partial sums)
 #pragma unroll
     for (int i = 0; i < NA; i++) {
         float (&cur)[NB][4] = in[i & 1];
@@ -195,10 +196,10 @@ GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, 
     }
 }
 
-template <int EPI, int NA>
-GPT2_DEV void epilogue_rows(const Params& p, const f32x4* acc, int m0, int n0, int a0) {
-    if (m0 + BM <= p.M && n0 + BN <= p.N) epilogue_rows_<EPI, NA, false>(p, acc, m0, n0, a0);
-    else epilogue_rows_<EPI, NA, true>(p, acc, m0, n0, a0);
+template <int EPI, int NA, class Pre>
+GPT2_DEV void epilogue_rows(const Params& p, const f32x4* acc, int m0, int n0, int a0, Pre&& pre) {
+    if (m0 + BM <= p.M && n0 + BN <= p.N) epilogue_rows_<EPI, NA, false>(p, acc, m0, n0, a0, pre);
+    else epilogue_rows_<EPI, NA, true>(p, acc, m0, n0, a0, pre);
 }
 
 // Partial tile in fragment order: thread t's 16*NB accumulators at slot[(j*256 + t)],
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
             }
         }
         if (full) {
-            epilogue_rows<EPI, 4>(p, &acc[0][0], m0, n0, 0);
+            epilogue_rows<EPI, 4>(p, &acc[0][0], m0, n0, 0, [] {});
         } else {
             store_partial(slot, acc);
         }
@@ -626,18 +627,33 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
     f32x4 acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int l = first; l <= last; l++) {
-        const int which = range_start(p.total, p.nr, l) / p.nk == tile ? 0 : 1;
-        const float* slot = p.partial + ((long)l * 2 + which) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
-        float v[4 * NB];
-#pragma unroll
-        for (int e = 0; e < 4 * NB; e++) v[e] = slot[e * NT];
-#pragma unroll
-        for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[e];
-    }
     int m0, n0;
     tile_coords(p, p.tile0 + tile, m0, n0);
-    epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter);
+    // the partials are summed after the epilogue has requested its own inputs
+    auto slot_of = [&](int l) {
+        const int which = range_start(p.total, p.nr, l) / p.nk == tile ? 0 : 1;
+        return p.partial + ((long)l * 2 + which) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
+    };
+    epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter, [&] {
+        // two partials at a time in flight, added in k order
+        for (int l = first; l <= last; l += 2) {
+            float v[2][4 * NB];
+            const float* s0 = slot_of(l);
+#pragma unroll
+            for (int e = 0; e < 4 * NB; e++) v[0][e] = s0[e * NT];
+            if (l + 1 <= last) {
+                const float* s1 = slot_of(l + 1);
+#pragma unroll
+                for (int e = 0; e < 4 * NB; e++) v[1][e] = s1[e * NT];
+            }
+#pragma unroll
+            for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[0][e];
+            if (l + 1 <= last) {
+#pragma unroll
+                for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[1][e];
+            }
+        }
+    });
     if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
         float s = 0.f;
         for (int l = first; l <= last; l++) {
@@ -657,17 +673,18 @@ __global__ __launch_bounds__(NT) void gemm_splitk_fixup_kernel(Params p) {
     f32x4 acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sg = 0; sg < p.S; sg++) {
-        const float* slot = p.partial + ((long)sg * tiles + tile) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
-        float v[4 * NB];
-#pragma unroll
-        for (int e = 0; e < 4 * NB; e++) v[e] = slot[e * NT];
-#pragma unroll
-        for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[e];
-    }
     int m0, n0;
     tile_coords(p, tile, m0, n0);
-    epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter);
+    epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter, [&] {
+        for (int sg = 0; sg < p.S; sg++) {
+            const float* slot = p.partial + ((long)sg * tiles + tile) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
+            float v[4 * NB];
+#pragma unroll
+            for (int e = 0; e < 4 * NB; e++) v[e] = slot[e * NT];
+#pragma unroll
+            for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[e];
+        }
+    });
     if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
         float sum = 0.f;
         for (int sg = 0; sg < p.S; sg++) sum += p.partial[((long)sg * tiles + tile) * SLOT_FLOATS + BM * BN + threadIdx.x];
