@@ -117,87 +117,99 @@ GPT2_DEV void tile_coords(const Params& p, int tile, int& m0, int& n0) {
     n0 = (in_group / gm) * BN;
 }
 
-// Fused epilogue on NA rows of finished 16x16 blocks (a = a0 .. a0+NA-1, b = 0..3) of
-// this thread's wave.  16x16 accumulator layout: lane holds column lane%16 and, in
-// register v, row 4*(lane/16) + v.  One row of blocks at a time: the values the epilogue
-// reads for the next row (residual, pre-activation, old C) are requested before this
-// row's outputs are stored, and a row's 16 (or 32) stores go out back to back, so the
-// memory operations overlap instead of each waiting for the one before.  CHECK: the tile
-// crosses the edge of C, so rows and columns are bounds-checked.
-template <int EPI, int NA, bool CHECK, class Pre>
-GPT2_DEV void epilogue_rows_(const Params& p, const f32x4* acc, int m0, int n0, int a0, Pre&& pre) {
-    constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
-    constexpr bool READS = EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_DLOGITS;
+// Fused epilogue, one row of this wave's 16x16 blocks (a, b = 0..NB-1) at a time.
+// 16x16 accumulator layout: lane holds column lane%16 and, in register v, row
+// 4*(lane/16) + v.  epi_load requests the values the row's epilogue reads (residual,
+// pre-activation, old C, target rows of W); epi_store forms the outputs and stores them
+// back to back.  CHECK: the tile crosses the edge of C, so rows and columns are
+// bounds-checked.
+template <int EPI>
+constexpr bool epi_reads() {
+    return EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_DLOGITS;
+}
+
+template <int EPI, bool CHECK>
+GPT2_DEV void epi_load(const Params& p, int m0, int n0, int a, float (&in)[NB][4]) {
+    if (!epi_reads<EPI>()) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * WN;
-    const int grp = lane >> 4;
+    const int r0 = m0 + (wave >> 1) * 64 + 16 * a + 4 * (lane >> 4), c0 = n0 + (wave & 1) * WN + (lane & 15);
     const float* src = EPI == EPI_ACCUM ? p.C : p.aux;
     const long lds = EPI == EPI_ACCUM ? p.ldc : p.ldaux;
-    // this lane's element (i, b, v) is at row r0 + 16 i + v, column c0 + 16 b
-    const int r0 = m0 + wm + 16 * a0 + 4 * grp, c0 = n0 + wn + (lane & 15);
-    auto inside = [&](int i, int b, int v) { return !CHECK || (r0 + 16 * i + v < p.M && c0 + 16 * b < p.N); };
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const int row = r0 + v;
+        const float* q = src + (long)row * lds + c0;
+        // EPI_DLOGITS reads row target[row] of W (B, k = vocabulary id) instead
+        if (EPI == EPI_DLOGITS) q = p.B + (long)(!CHECK || row < p.M ? p.tgt[row] : 0) * p.ldb + c0;
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            in[b][v] = 0.f;
+            if (!CHECK || (row < p.M && c0 + 16 * b < p.N)) in[b][v] = q[16 * b];
+        }
+    }
+}
+
+template <int EPI, bool CHECK>
+GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0, int a, float (&in)[NB][4]) {
+    constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r0 = m0 + (wave >> 1) * 64 + 16 * a + 4 * (lane >> 4), c0 = n0 + (wave & 1) * WN + (lane & 15);
+    auto inside = [&](int b, int v) { return !CHECK || (r0 + v < p.M && c0 + 16 * b < p.N); };
     float bias_v[NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) {
         bias_v[b] = 0.f;
         if (HAS_BIAS && p.bias && (!CHECK || c0 + 16 * b < p.N)) bias_v[b] = p.bias[c0 + 16 * b];
     }
-    auto load_row = [&](float (&in)[NB][4], int i) {
+#pragma unroll
+    for (int b = 0; b < NB; b++)
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const int row = r0 + 16 * i + v;
-            const float* q = src + (long)row * lds + c0;
-            // EPI_DLOGITS reads row target[row] of W (B, k = vocabulary id) instead
-            if (EPI == EPI_DLOGITS) q = p.B + (long)(!CHECK || row < p.M ? p.tgt[row] : 0) * p.ldb + c0;
-#pragma unroll
-            for (int b = 0; b < NB; b++) {
-                in[b][v] = 0.f;
-                if (READS && inside(i, b, v)) in[b][v] = q[16 * b];
-            }
+            const float x = acc[b][v];
+            float& o = in[b][v];
+            if (EPI == EPI_STORE) o = x;
+            else if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) o = x + bias_v[b];
+            else if (EPI == EPI_BIAS_RESID) o = o + (x + bias_v[b]);
+            else if (EPI == EPI_ACCUM) o = o + x;
+            else if (EPI == EPI_DLOGITS) o = x - p.xscale * o;
+            else o = x * gelu_grad_f(o);  // EPI_GELU_BWD
         }
-    };
-    auto store_row = [&](const float (&o)[NB][4], float* dst, long ld, int i) {
+    auto store_row = [&](float* dst, long ld) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            float* q = dst + (long)(r0 + 16 * i + v) * ld + c0;
+            float* q = dst + (long)(r0 + v) * ld + c0;
 #pragma unroll
             for (int b = 0; b < NB; b++)
-                if (inside(i, b, v)) q[16 * b] = o[b][v];
+                if (inside(b, v)) q[16 * b] = in[b][v];
         }
     };
-    float in[2][NB][4];
-    if (READS) load_row(in[0], 0);
-    pre();  // the caller's last step before the outputs are formed (the fix-up's partial sums)
-#pragma unroll
-    for (int i = 0; i < NA; i++) {
-        float (&cur)[NB][4] = in[i & 1];
-        if (READS && i + 1 < NA) load_row(in[(i + 1) & 1], i + 1);
+    if (EPI == EPI_BIAS_GELU) {
+        store_row(p.pre, p.ldpre);  // the pre-activation, then its GELU
 #pragma unroll
         for (int b = 0; b < NB; b++)
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const float x = acc[i * NB + b][v];
-                float& o = cur[b][v];
-                if (EPI == EPI_STORE) o = x;
-                else if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) o = x + bias_v[b];
-                else if (EPI == EPI_BIAS_RESID) o = o + (x + bias_v[b]);
-                else if (EPI == EPI_ACCUM) o = o + x;
-                else if (EPI == EPI_DLOGITS) o = x - p.xscale * o;
-                else o = x * gelu_grad_f(o);  // EPI_GELU_BWD
-            }
-        if (EPI == EPI_BIAS_GELU) {
-            store_row(cur, p.pre, p.ldpre, i);  // the pre-activation, then its GELU
+            for (int v = 0; v < 4; v++) in[b][v] = gelu_f(in[b][v]);
+    }
+    store_row(p.C, p.ldc);
+}
+
+// NA rows (a0 ..) of blocks: the next row's inputs are requested before this row's
+// outputs are stored, so the memory operations overlap.  `pre` runs once the first row's
+// inputs are requested (the fix-up sums its partials there).
+template <int EPI, int NA, bool CHECK, class Pre>
+GPT2_DEV void epilogue_rows_(const Params& p, const f32x4 (&acc)[NA][NB], int m0, int n0, int a0, Pre&& pre) {
+    float in0[NB][4], in1[NB][4];
+    epi_load<EPI, CHECK>(p, m0, n0, a0, in0);
+    pre();
 #pragma unroll
-            for (int b = 0; b < NB; b++)
-#pragma unroll
-                for (int v = 0; v < 4; v++) cur[b][v] = gelu_f(cur[b][v]);
-        }
-        store_row(cur, p.C, p.ldc, i);
+    for (int i = 0; i < NA; i++) {
+        if (i + 1 < NA) epi_load<EPI, CHECK>(p, m0, n0, a0 + i + 1, (i & 1) ? in0 : in1);
+        epi_store<EPI, CHECK>(p, acc[i], m0, n0, a0 + i, (i & 1) ? in1 : in0);
     }
 }
 
 template <int EPI, int NA, class Pre>
-GPT2_DEV void epilogue_rows(const Params& p, const f32x4* acc, int m0, int n0, int a0, Pre&& pre) {
+GPT2_DEV void epilogue_rows(const Params& p, const f32x4 (&acc)[NA][NB], int m0, int n0, int a0, Pre&& pre) {
     if (m0 + BM <= p.M && n0 + BN <= p.N) epilogue_rows_<EPI, NA, false>(p, acc, m0, n0, a0, pre);
     else epilogue_rows_<EPI, NA, true>(p, acc, m0, n0, a0, pre);
 }
@@ -600,7 +612,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
             }
         }
         if (full) {
-            epilogue_rows<EPI, 4>(p, &acc[0][0], m0, n0, 0, [] {});
+            epilogue_rows<EPI, 4>(p, acc, m0, n0, 0, [] {});
         } else {
             store_partial(slot, acc);
         }
@@ -624,9 +636,9 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
     const long t0 = (long)tile * p.nk;
     const int first = owner(p.total, p.nr, t0);
     const int last = owner(p.total, p.nr, t0 + p.nk - 1);
-    f32x4 acc[NB];
+    f32x4 acc[1][NB];
 #pragma unroll
-    for (int b = 0; b < NB; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; b++) acc[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     int m0, n0;
     tile_coords(p, p.tile0 + tile, m0, n0);
     // the partials are summed after the epilogue has requested its own inputs
@@ -647,10 +659,10 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
                 for (int e = 0; e < 4 * NB; e++) v[1][e] = s1[e * NT];
             }
 #pragma unroll
-            for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[0][e];
+            for (int e = 0; e < 4 * NB; e++) acc[0][e >> 2][e & 3] += v[0][e];
             if (l + 1 <= last) {
 #pragma unroll
-                for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[1][e];
+                for (int e = 0; e < 4 * NB; e++) acc[0][e >> 2][e & 3] += v[1][e];
             }
         }
     });
@@ -670,9 +682,9 @@ template <int EPI>
 __global__ __launch_bounds__(NT) void gemm_splitk_fixup_kernel(Params p) {
     const int tiles = p.tiles_m * p.tiles_n;
     const int tile = blockIdx.x >> 2, quarter = blockIdx.x & 3;
-    f32x4 acc[NB];
+    f32x4 acc[1][NB];
 #pragma unroll
-    for (int b = 0; b < NB; b++) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; b++) acc[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     int m0, n0;
     tile_coords(p, tile, m0, n0);
     epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter, [&] {
@@ -682,7 +694,7 @@ __global__ __launch_bounds__(NT) void gemm_splitk_fixup_kernel(Params p) {
 #pragma unroll
             for (int e = 0; e < 4 * NB; e++) v[e] = slot[e * NT];
 #pragma unroll
-            for (int e = 0; e < 4 * NB; e++) acc[e >> 2][e & 3] += v[e];
+            for (int e = 0; e < 4 * NB; e++) acc[0][e >> 2][e & 3] += v[e];
         }
     });
     if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
