@@ -173,6 +173,19 @@ int gpt2_profile_collect(gpt2* model);
 int gpt2_profile_entry(gpt2* model, int i, const char** name, long* launches, double* total_ms,
                        double* flops, double* bytes);
 
+/* Tile width of the forward and dgrad matmuls (process-wide; call it between steps, not
+ * while another host thread launches work).  GPT2_GEMM_TILES_AUTO (the default) uses
+ * 128 x 96 output tiles where their count is a whole number of rounds of the chip's 512
+ * resident blocks and the 128 x 128 count is not (for 8192 rows: N = 768 and N = 2304),
+ * and 128 x 128 tiles elsewhere; _128 and _96 force one width for every forward and
+ * dgrad matmul.  Results agree between widths to rounding: each output sums its k terms
+ * in the same order within a block, and split tiles add their k segments in k order.
+ * Returns GPT2_OK, or GPT2_EINVAL for an unknown value (the setting is then unchanged). */
+#define GPT2_GEMM_TILES_AUTO 0
+#define GPT2_GEMM_TILES_128 1
+#define GPT2_GEMM_TILES_96 2
+int gpt2_set_gemm_tiles(int policy);
+
 /* Standalone LayerNorm forward, overwrite semantics (the pages' worked layer: dakule
  * page 手动实现每个层前向 / 反向传播; 新智元 page 教程).  Device pointers: x, y (N,C);
  * w, b (C); mean, rstd (N).  y = (x - mean) * rstd * w + b with biased variance and

@@ -7,16 +7,16 @@
 //   dgrad    dX = dY W:               A = dY (k contiguous),  B = W  (n contiguous)
 //   wgrad    dW += dY^T X:            A = dY (m contiguous),  B = X  (n contiguous)
 //
-// Design for CDNA4: 256 threads = 4 wave64s, block tile 128x128, each wave a 64x64
-// sub-tile made of 4x4 v_mfma_f32_16x16x4f32 blocks (64 accumulators per lane).  The
+// Design for CDNA4: 256 threads = 4 wave64s, block tile 128x128 (or 128x96 where that
+// count of tiles fills whole rounds of the grid and 128x128 does not), each wave a
+// 64x64 (64x48) sub-tile made of 4x4 (4x3) v_mfma_f32_16x16x4f32 blocks.  The
 // 16x16x4 form is used because it sustains the full fp32 matrix rate on gfx950, where
 // the 32x32x2 form measures about 12% lower.  Operand k-tiles go from global memory
 // straight into LDS (global_load_lds_dwordx4, no register staging) through a ring of LDS
 // buffers: 32-wide k-tiles in 2 buffers when A is k-contiguous, 16-wide k-tiles in 4
 // buffers (3 in flight while one is consumed) for the wgrad; each k-tile costs one
 // barrier.  LDS tiles are unpadded (a wave's transfer is 1 KB of consecutive LDS) and bank
-// conflicts are avoided by XOR-swizzling 16-byte chunks: k-contiguous tiles [row][BK] by
-// (row/2) % (BK/4), row-contiguous tiles [k][128] by 4*((k/4)%4).  Each lane takes 4
+// conflicts are avoided by swizzling 16-byte chunks (layouts at rpos below).  Each lane takes 4
 // consecutive k for its lane group (k = 16g + 4(lane/16) + s for MFMA step s), so a
 // k-contiguous fragment is one 16-byte LDS read; the sum over k is the same sum in
 // another order.
@@ -44,8 +44,10 @@ namespace gpt2k {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, NT = 256;
-constexpr int WN = BN / 2, NB = WN / 16;  // per-wave n extent and its 16-wide blocks
+// Block tile BM x BN, BN = 128 or (A k-contiguous only) 96, a template parameter; wave w
+// holds the 64 x BN/2 sub-tile at (64 (w/2), BN/2 (w%2)) as 4 x NB blocks of 16x16,
+// NB = BN/32.
+constexpr int BM = 128, NT = 256;
 // k-tile width and LDS ring depth (k-tiles in flight + 1) per operand layout: 32 and 2
 // when A is k-contiguous (forward, dgrad), 16 and 4 for the wgrad, whose row-contiguous
 // fragments and fused bias sums need more registers than a second wave per SIMD leaves
@@ -59,7 +61,8 @@ constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse 
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
 constexpr int MAX_UNITS = 1536;                  // split-K units the partial region holds
-constexpr int SLOT_FLOATS = BM * BN + BM;  // one partial tile + its bias-gradient row sums
+constexpr int SLOT_BIAS = BM * 128;            // partial slot: tile, then its bias-gradient row sums
+constexpr int SLOT_FLOATS = SLOT_BIAS + BM;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -107,6 +110,7 @@ GPT2_DEV int owner(long total, int G, long x) {
     return lb;
 }
 
+template <int BN>
 GPT2_DEV void tile_coords(const Params& p, int tile, int& m0, int& n0) {
     const int group_size = GROUP_M * p.tiles_n;
     const int group = tile / group_size;
@@ -128,9 +132,10 @@ constexpr bool epi_reads() {
     return EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_DLOGITS;
 }
 
-template <int EPI, bool CHECK>
+template <int EPI, bool CHECK, int NB>
 GPT2_DEV void epi_load(const Params& p, int m0, int n0, int a, float (&in)[NB][4]) {
     if (!epi_reads<EPI>()) return;
+    constexpr int WN = 16 * NB;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r0 = m0 + (wave >> 1) * 64 + 16 * a + 4 * (lane >> 4), c0 = n0 + (wave & 1) * WN + (lane & 15);
     const float* src = EPI == EPI_ACCUM ? p.C : p.aux;
@@ -149,8 +154,9 @@ GPT2_DEV void epi_load(const Params& p, int m0, int n0, int a, float (&in)[NB][4
     }
 }
 
-template <int EPI, bool CHECK>
+template <int EPI, bool CHECK, int NB>
 GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0, int a, float (&in)[NB][4]) {
+    constexpr int WN = 16 * NB;
     constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r0 = m0 + (wave >> 1) * 64 + 16 * a + 4 * (lane >> 4), c0 = n0 + (wave & 1) * WN + (lane & 15);
@@ -196,7 +202,7 @@ GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0,
 // NA rows (a0 ..) of blocks: the next row's inputs are requested before this row's
 // outputs are stored, so the memory operations overlap.  `pre` runs once the first row's
 // inputs are requested (the fix-up sums its partials there).
-template <int EPI, int NA, bool CHECK, class Pre>
+template <int EPI, int NA, bool CHECK, int NB, class Pre>
 GPT2_DEV void epilogue_rows_(const Params& p, const f32x4 (&acc)[NA][NB], int m0, int n0, int a0, Pre&& pre) {
     float in0[NB][4], in1[NB][4];
     epi_load<EPI, CHECK>(p, m0, n0, a0, in0);
@@ -208,14 +214,15 @@ GPT2_DEV void epilogue_rows_(const Params& p, const f32x4 (&acc)[NA][NB], int m0
     }
 }
 
-template <int EPI, int NA, class Pre>
+template <int EPI, int NA, int NB, class Pre>
 GPT2_DEV void epilogue_rows(const Params& p, const f32x4 (&acc)[NA][NB], int m0, int n0, int a0, Pre&& pre) {
-    if (m0 + BM <= p.M && n0 + BN <= p.N) epilogue_rows_<EPI, NA, false>(p, acc, m0, n0, a0, pre);
+    if (m0 + BM <= p.M && n0 + 32 * NB <= p.N) epilogue_rows_<EPI, NA, false>(p, acc, m0, n0, a0, pre);
     else epilogue_rows_<EPI, NA, true>(p, acc, m0, n0, a0, pre);
 }
 
 // Partial tile in fragment order: thread t's 16*NB accumulators at slot[(j*256 + t)],
 // j = (a*NB + b)*4 + v.
+template <int NB>
 GPT2_DEV void store_partial(float* slot, const f32x4 (&acc)[4][NB]) {
 #pragma unroll
     for (int a = 0; a < 4; a++)
@@ -251,13 +258,28 @@ GPT2_DEV void dma4(const void* g, float* lds) {
                  ::"s"(__builtin_amdgcn_readfirstlane(lds_offset(lds))), "v"(g) : "memory", "m0");
 }
 
-// LDS layouts of one k-tile (16 k values, 128 rows), both without padding so that a
-// wave's 1 KB transfer is contiguous:
+// LDS layouts of one k-tile (BK k values of ROWS rows), without padding so that a wave's
+// 1 KB transfer is contiguous:
 //  k-contiguous [row][BK]: 16-byte chunk c of row r sits at chunk position c ^ ((r>>1) % (BK/4))
-//  row-contiguous [k][128]: chunk c (rows 4c..4c+3) of k row kr sits at c ^ rswz(kr)
+//  row-contiguous, 128 rows, [k][128]: chunk c (rows 4c..4c+3) of k row kr sits at
+//  c ^ rswz(kr)
+//  row-contiguous, 96 rows, [row/16][kperm(kr)][16]: a 96-float k row cannot be swizzled
+//  within itself (its six 16-float blocks cannot take four distinct bank groups for four k
+//  rows), so each 16-row block is stored as a column of BK k rows with k row kr at
+//  kperm(kr) = kr ^ ((kr>>2) & 3).
+// A fragment read takes, for MFMA step s, k rows 16g + 4q + s (q = lane group) and 16
+// consecutive rows: the swizzles put the four lane groups in four different 16-bank groups.
 template <int BK>
 GPT2_DEV int kswz(int r) { return (r >> 1) & (BK / 4 - 1); }
 GPT2_DEV int rswz(int kr) { return ((kr >> 2) & 3) << 2; }
+GPT2_DEV int kperm(int kr) { return kr ^ ((kr >> 2) & 3); }  // an involution
+// float position of (k row kr, row r) in a row-contiguous tile of ROWS rows
+template <int ROWS, int BK>
+GPT2_DEV int rpos(int kr, int r) {
+    static_assert(ROWS == 128 || ROWS == 96, "row-contiguous tiles are 128 or 96 rows");
+    if (ROWS == 128) return kr * 128 + ((((r >> 2) ^ rswz(kr)) << 2) | (r & 3));
+    return (((r >> 4) * BK + kperm(kr)) << 4) | (r & 15);
+}
 
 // Per-lane byte offsets of a tile's transfers from the tile's base, the operand element
 // (row r0, k 0) for a k-contiguous operand X[r*ld + k] or (k 0, row r0) for a
@@ -279,18 +301,24 @@ GPT2_DEV void kcontig_offsets(unsigned (&off)[ROWS * BK / 1024], long ld, int r0
     }
 }
 
-//  row-contiguous: transfer q covers 256/ROWS k rows; float4 row groups are clamped to
-//  rmax4 (a multiple of 4 inside the row).
+//  row-contiguous: LDS chunk 64q + l holds 4 rows of one k row (the inverse of rpos);
+//  float4 row groups are clamped to rmax4 (a multiple of 4 inside the row).
 template <int ROWS, int BK>
 GPT2_DEV void rcontig_offsets(unsigned (&off)[ROWS * BK / 1024], long ld, int r0, int rmax4) {
-    constexpr int CH = ROWS / 4;  // 16-byte chunks per k row
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
     for (int j = 0; j < ROWS * BK / 1024; j++) {
-        const int q = j * 4 + w;
-        const int kr = q * (64 / CH) + l / CH;
-        const int c = (l % CH) ^ rswz(kr);
-        const int r = min(r0 + 4 * c, rmax4);
+        const int ch = (j * 4 + w) * 64 + l;
+        int kr, rr;
+        if (ROWS == 128) {
+            kr = ch >> 5;
+            rr = ((ch & 31) ^ rswz(kr)) << 2;
+        } else {
+            const int blk = ch >> 2;  // 16-float block: 16-row group blk / BK, k row kperm(blk % BK)
+            kr = kperm(blk % BK);
+            rr = (blk / BK) * 16 + 4 * (ch & 3);
+        }
+        const int r = min(r0 + rr, rmax4);
         off[j] = (unsigned)(((long)kr * ld + (r - r0)) * 4);
     }
 }
@@ -324,13 +352,13 @@ GPT2_DEV void fill_kcontig(float* S, const float* X, long ld, int r0, int nrows,
 
 template <int ROWS, int BK>
 GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows, int k0, int K) {
-    constexpr int CH = ROWS / 4, KPP = NT / CH;  // chunks per k row, k rows per pass
+    constexpr int CH = ROWS / 4, PASSES = BK * CH / NT;  // chunks per k row, chunks per thread
+    static_assert(BK * CH % NT == 0, "whole passes");
     const int t = threadIdx.x;
-    const int c = t % CH, r = r0 + 4 * c;
-    float4 v[BK / KPP];
+    float4 v[PASSES];
 #pragma unroll
-    for (int j = 0; j < BK / KPP; j++) {
-        const int kr = t / CH + KPP * j, k = k0 + kr;
+    for (int j = 0; j < PASSES; j++) {
+        const int kr = (t + NT * j) / CH, k = k0 + kr, r = r0 + 4 * ((t + NT * j) % CH);
         v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (k < K) {
             const float* q = X + (long)k * ld + r;
@@ -341,9 +369,9 @@ GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows,
         }
     }
 #pragma unroll
-    for (int j = 0; j < BK / KPP; j++) {
-        const int kr = t / CH + KPP * j;
-        *reinterpret_cast<float4*>(S + kr * ROWS + ((c ^ rswz(kr)) << 2)) = v[j];
+    for (int j = 0; j < PASSES; j++) {
+        const int kr = (t + NT * j) / CH, c = (t + NT * j) % CH;
+        *reinterpret_cast<float4*>(S + rpos<ROWS, BK>(kr, 4 * c)) = v[j];
     }
 }
 
@@ -360,8 +388,10 @@ GPT2_DEV void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
 }
 
-template <bool A_K, bool B_K, int EPI, bool XF>
+template <bool A_K, bool B_K, int EPI, bool XF, int BN>
 __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
+    static_assert(BN == 128 || (BN == 96 && A_K), "96-wide tiles take 32-wide k-tiles");
+    constexpr int WN = BN / 2, NB = BN / 32;
     constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
     constexpr int BK = KTile<A_K>::BK, STAGES = KTile<A_K>::STAGES;
     constexpr int A_FLOATS = BM * BK, B_FLOATS = BN * BK;  // the operands' k-tiles in LDS
@@ -424,7 +454,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
         } else {
             return false;
         }
-        tile_coords(p, w.tile, w.m0, w.n0);
+        tile_coords<BN>(p, w.tile, w.m0, w.n0);
         return true;
     };
 
@@ -516,7 +546,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
 #pragma unroll
                         for (int s = 0; s < 4; s++) {
                             const int kr = 16 * g + 4 * grp + s;
-                            fa[a][s] = Sa[kr * BM + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                            fa[a][s] = Sa[rpos<BM, BK>(kr, row)];
                         }
                     }
                 }
@@ -533,7 +563,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
 #pragma unroll
                         for (int s = 0; s < 4; s++) {
                             const int kr = 16 * g + 4 * grp + s;
-                            fb[b][s] = Sb[kr * BN + ((((row >> 2) ^ rswz(kr)) << 2) | (row & 3))];
+                            fb[b][s] = Sb[rpos<BN, BK>(kr, row)];
                         }
                     }
                 }
@@ -606,7 +636,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
                     if (full) {
                         if (m0 + row < p.M) p.dbias[m0 + row] += s;
                     } else {
-                        slot[BM * BN + row] = s;
+                        slot[SLOT_BIAS + row] = s;
                     }
                 }
             }
@@ -622,8 +652,9 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
 // Four blocks per range boundary that falls strictly inside a tile, one per row of
 // 16x16 blocks (a) of the waves' sub-tiles; for the lowest such boundary of a tile they
 // add that tile's partials in k order and run the epilogue.
-template <int EPI>
+template <int EPI, int BN>
 __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
+    constexpr int NB = BN / 32;
     const int quarter = blockIdx.x & 3;
     const int lbb = (blockIdx.x >> 2) + 1;  // boundary between blocks lbb-1 and lbb
     const long x = range_start(p.total, p.nr, lbb);
@@ -640,7 +671,7 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
 #pragma unroll
     for (int b = 0; b < NB; b++) acc[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     int m0, n0;
-    tile_coords(p, p.tile0 + tile, m0, n0);
+    tile_coords<BN>(p, p.tile0 + tile, m0, n0);
     // the partials are summed after the epilogue has requested its own inputs
     auto slot_of = [&](int l) {
         const int which = range_start(p.total, p.nr, l) / p.nk == tile ? 0 : 1;
@@ -670,7 +701,7 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
         float s = 0.f;
         for (int l = first; l <= last; l++) {
             const int which = range_start(p.total, p.nr, l) / p.nk == tile ? 0 : 1;
-            s += p.partial[((long)l * 2 + which) * SLOT_FLOATS + BM * BN + threadIdx.x];
+            s += p.partial[((long)l * 2 + which) * SLOT_FLOATS + SLOT_BIAS + threadIdx.x];
         }
         p.dbias[m0 + threadIdx.x] += s;
     }
@@ -678,15 +709,16 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
 
 // Split-K rounds: four blocks per tile, one per row of 16x16 blocks (a) of the waves'
 // sub-tiles, add the tile's S partials in k order and run the epilogue.
-template <int EPI>
+template <int EPI, int BN>
 __global__ __launch_bounds__(NT) void gemm_splitk_fixup_kernel(Params p) {
+    constexpr int NB = BN / 32;
     const int tiles = p.tiles_m * p.tiles_n;
     const int tile = blockIdx.x >> 2, quarter = blockIdx.x & 3;
     f32x4 acc[1][NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) acc[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     int m0, n0;
-    tile_coords(p, tile, m0, n0);
+    tile_coords<BN>(p, tile, m0, n0);
     epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter, [&] {
         for (int sg = 0; sg < p.S; sg++) {
             const float* slot = p.partial + ((long)sg * tiles + tile) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
@@ -699,29 +731,29 @@ __global__ __launch_bounds__(NT) void gemm_splitk_fixup_kernel(Params p) {
     });
     if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
         float sum = 0.f;
-        for (int sg = 0; sg < p.S; sg++) sum += p.partial[((long)sg * tiles + tile) * SLOT_FLOATS + BM * BN + threadIdx.x];
+        for (int sg = 0; sg < p.S; sg++) sum += p.partial[((long)sg * tiles + tile) * SLOT_FLOATS + SLOT_BIAS + threadIdx.x];
         p.dbias[m0 + threadIdx.x] += sum;
     }
 }
 
 // Kernel name as profilers print the instantiation.
-template <bool A_K, bool B_K, int EPI, bool XF>
+template <bool A_K, bool B_K, int EPI, bool XF, int BN>
 const char* gemm_name() {
     static const std::string s = std::string("gemm_kernel<") + (A_K ? "true" : "false") + ", " +
                                  (B_K ? "true" : "false") + ", " + std::to_string(EPI) + ", " +
-                                 (XF ? "true" : "false") + ">";
+                                 (XF ? "true" : "false") + ", " + std::to_string(BN) + ">";
     return s.c_str();
 }
 
-template <int EPI>
+template <int EPI, int BN>
 const char* fixup_name() {
-    static const std::string s = "gemm_fixup_kernel<" + std::to_string(EPI) + ">";
+    static const std::string s = "gemm_fixup_kernel<" + std::to_string(EPI) + ", " + std::to_string(BN) + ">";
     return s.c_str();
 }
 
-template <int EPI>
+template <int EPI, int BN>
 const char* splitk_fixup_name() {
-    static const std::string s = "gemm_splitk_fixup_kernel<" + std::to_string(EPI) + ">";
+    static const std::string s = "gemm_splitk_fixup_kernel<" + std::to_string(EPI) + ", " + std::to_string(BN) + ">";
     return s.c_str();
 }
 
@@ -761,8 +793,8 @@ void schedule(Params& p, long tiles, int split) {
     if (p.R == 0) p.G = p.nr;
 }
 
-template <bool A_K, bool B_K, int EPI, bool XF = false>
-hipError_t launch(Params& p, hipStream_t st, int split = 0) {
+template <bool A_K, bool B_K, int EPI, bool XF, int BN>
+hipError_t launch(Params& p, hipStream_t st, int split) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
     p.nk = (p.K + KTile<A_K>::BK - 1) / KTile<A_K>::BK;
@@ -778,16 +810,17 @@ hipError_t launch(Params& p, hipStream_t st, int split = 0) {
                           EPI == EPI_DLOGITS) ? mn : 0.0;
     {
         // algorithmic work: 2MNK flops; operands read once, C written (and read for += / aux)
-        ProfScope ps(st, gemm_name<A_K, B_K, EPI, XF>(), 2.0 * mn * p.K,
+        ProfScope ps(st, gemm_name<A_K, B_K, EPI, XF, BN>(), 2.0 * mn * p.K,
                      4.0 * ((double)p.M * p.K + (double)p.N * p.K + mn + extra));
-        hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF>), dim3(p.G), dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF, BN>), dim3(p.G), dim3(NT), 0, st, p);
     }
+    const double slot = (double)BM * BN + BM;
     if (p.S > 1) {
-        ProfScope ps(st, splitk_fixup_name<EPI>(), 0.0, 4.0 * ((double)p.units * SLOT_FLOATS + extra));
-        hipLaunchKernelGGL((gemm_splitk_fixup_kernel<EPI>), dim3(4 * (p.units / p.S)), dim3(NT), 0, st, p);
+        ProfScope ps(st, splitk_fixup_name<EPI, BN>(), 0.0, 4.0 * ((double)p.units * slot + extra));
+        hipLaunchKernelGGL((gemm_splitk_fixup_kernel<EPI, BN>), dim3(4 * (p.units / p.S)), dim3(NT), 0, st, p);
     } else if (p.nr > 1 && !(p.total % p.nr == 0 && (p.total / p.nr) % p.nk == 0)) {
-        ProfScope ps(st, fixup_name<EPI>(), 0.0, 4.0 * (2.0 * p.nr * SLOT_FLOATS + extra));
-        hipLaunchKernelGGL((gemm_fixup_kernel<EPI>), dim3(4 * (p.nr - 1)), dim3(NT), 0, st, p);
+        ProfScope ps(st, fixup_name<EPI, BN>(), 0.0, 4.0 * (2.0 * p.nr * slot + extra));
+        hipLaunchKernelGGL((gemm_fixup_kernel<EPI, BN>), dim3(4 * (p.nr - 1)), dim3(NT), 0, st, p);
     }
     return hipGetLastError();
 }
@@ -797,7 +830,7 @@ bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
 // k-split factor that turns a shape with fewer tiles than resident blocks and a long k
 // extent into whole rounds of split-K units (e.g. 384 tiles -> 4 segments, 3 rounds); 0
 // when there is none (stream-K then).
-template <bool A_K>
+template <bool A_K, int BN>
 int pick_split(int M, int N, int K) {
     const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int nk = (K + KTile<A_K>::BK - 1) / KTile<A_K>::BK;
@@ -807,9 +840,40 @@ int pick_split(int M, int N, int K) {
     return 0;
 }
 
+// Tile width of the kernels whose A is k-contiguous (forward, dgrad): 96 when that gives
+// whole rounds of resident blocks and 128 does not, else 128.  For 8192 rows, N = 768 is
+// 512 tiles of 128x96 (one round, no split tiles) against 384 of 128x128, and N = 2304 is
+// 1536 (three rounds) against 1152.  gemm_set_tile_policy can force either width.
+int g_tile_policy = GEMM_TILES_AUTO;
+
+int tile_n(int M, int N) {
+    if (g_tile_policy == GEMM_TILES_128) return 128;
+    if (g_tile_policy == GEMM_TILES_96) return 96;
+    const long tm = (M + BM - 1) / BM;
+    const long t128 = tm * ((N + 127) / 128), t96 = tm * ((N + 95) / 96);
+    return (t96 > 0 && t96 % RESIDENT == 0 && t128 % RESIDENT != 0) ? 96 : 128;
+}
+
+template <bool B_K, int EPI, bool XF = false>
+hipError_t launch_ak(Params& p, hipStream_t st) {
+    // The dlogits dgrad keeps 128-wide tiles unless forced: its exponentials are spread
+    // over 16 instead of 12 MFMAs per fragment row, and its long k extent over few tiles
+    // runs as split-K rounds (measured: 128 x 128 with 4 k-segments beats one round of
+    // 128 x 96 tiles over the whole vocabulary).
+    const int bn = (XF && g_tile_policy == GEMM_TILES_AUTO) ? 128 : tile_n(p.M, p.N);
+    if (bn == 96) return launch<true, B_K, EPI, XF, 96>(p, st, XF ? pick_split<true, 96>(p.M, p.N, p.K) : 0);
+    return launch<true, B_K, EPI, XF, 128>(p, st, XF ? pick_split<true, 128>(p.M, p.N, p.K) : 0);
+}
+
 }  // namespace
 
 size_t gemm_partial_floats() { return (size_t)std::max(RESIDENT * 2, MAX_UNITS) * SLOT_FLOATS; }
+
+bool gemm_set_tile_policy(int policy) {
+    if (policy != GEMM_TILES_AUTO && policy != GEMM_TILES_128 && policy != GEMM_TILES_96) return false;
+    g_tile_policy = policy;
+    return true;
+}
 
 hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
@@ -830,15 +894,15 @@ hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w
     if (pre) {
         p.pre = pre;
         p.ldpre = ldo;
-        return launch<true, true, EPI_BIAS_GELU>(p, st);
+        return launch_ak<true, EPI_BIAS_GELU>(p, st);
     }
     if (resid) {
         p.aux = resid;
         p.ldaux = ldo;
-        return launch<true, true, EPI_BIAS_RESID>(p, st);
+        return launch_ak<true, EPI_BIAS_RESID>(p, st);
     }
-    if (bias) return launch<true, true, EPI_BIAS>(p, st);
-    return launch<true, true, EPI_STORE>(p, st);
+    if (bias) return launch_ak<true, EPI_BIAS>(p, st);
+    return launch_ak<true, EPI_STORE>(p, st);
 }
 
 hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float* w,
@@ -859,7 +923,7 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
     if (gelu_pre) {
         p.aux = gelu_pre;
         p.ldaux = N;
-        return launch<true, false, EPI_GELU_BWD>(p, st);
+        return launch_ak<false, EPI_GELU_BWD>(p, st);
     }
     if (xent) {
         p.lse = xent->lse;
@@ -867,11 +931,9 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
         if (!(xent->scale > 0.f)) return hipErrorInvalidValue;
         p.xscale = xent->scale;
         p.xlog2s = (float)std::log2((double)xent->scale);
-        // a long k extent over few tiles: split-K rounds keep the blocks of an XCD on the
-        // same k-segment of neighbouring tiles, so they share the logits and wte panels
-        return launch<true, false, EPI_DLOGITS, true>(p, st, pick_split<true>(M, N, K));
+        return launch_ak<false, EPI_DLOGITS, true>(p, st);
     }
-    return launch<true, false, EPI_STORE>(p, st);
+    return launch_ak<false, EPI_STORE>(p, st);
 }
 
 hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout, const float* inp, int M,
@@ -898,9 +960,9 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
         if (!(xent->scale > 0.f)) return hipErrorInvalidValue;
         p.xscale = xent->scale;
         p.xlog2s = (float)std::log2((double)xent->scale);
-        return launch<false, false, EPI_ACCUM, true>(p, st);
+        return launch<false, false, EPI_ACCUM, true, 128>(p, st, 0);
     }
-    return launch<false, false, EPI_ACCUM>(p, st);
+    return launch<false, false, EPI_ACCUM, false, 128>(p, st, 0);
 }
 
 }  // namespace gpt2k

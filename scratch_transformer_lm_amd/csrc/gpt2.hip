@@ -480,6 +480,13 @@ int gpt2_layernorm_forward(float* y, float* mean, float* rstd, const float* x, c
                                                                                                       : GPT2_EDEVICE;
 }
 
+int gpt2_set_gemm_tiles(int policy) {
+    static_assert(GPT2_GEMM_TILES_AUTO == GEMM_TILES_AUTO && GPT2_GEMM_TILES_128 == GEMM_TILES_128 &&
+                      GPT2_GEMM_TILES_96 == GEMM_TILES_96,
+                  "tile policy values");
+    return gemm_set_tile_policy(policy) ? GPT2_OK : GPT2_EINVAL;
+}
+
 size_t gpt2_layernorm_backward_workspace(int N, int C) {
     if (N < 0 || C <= 0) return 0;
     return layernorm_partial_floats(N, C);

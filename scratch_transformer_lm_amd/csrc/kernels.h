@@ -14,6 +14,11 @@ namespace gpt2k {
 // (nullptr: one tile per block, no sharing of tiles).  Operands must be 16-byte aligned
 // with leading dimensions that are multiples of 4 floats.
 size_t gemm_partial_floats();
+// Tile width of the forward and dgrad GEMMs (process-wide; set it between launches, not
+// while other host threads launch): automatic (96 where that gives whole rounds of
+// resident blocks), or forced to 128 or 96 columns.  False for an unknown value.
+enum { GEMM_TILES_AUTO = 0, GEMM_TILES_128 = 1, GEMM_TILES_96 = 2 };
+bool gemm_set_tile_policy(int policy);
 // out[M,N] (ld ldo) = inp[M,K] . w[N,K]^T, then by the non-null extras:
 //   bias: + bias[n];  resid: out = resid + (...) (resid has ld ldo);
 //   pre:  pre = (...) and out = gelu(pre) (pre has ld ldo).

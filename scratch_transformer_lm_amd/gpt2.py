@@ -93,6 +93,8 @@ def load() -> ct.CDLL:
                                        ct.POINTER(ct.c_double), ct.POINTER(ct.c_double),
                                        ct.POINTER(ct.c_double)]
     lib.gpt2_profile_entry.restype = i
+    lib.gpt2_set_gemm_tiles.argtypes = [i]
+    lib.gpt2_set_gemm_tiles.restype = i
     lib.gpt2_layernorm_forward.argtypes = [P, P, P, P, P, P, i, i, f, P]
     lib.gpt2_layernorm_forward.restype = i
     lib.gpt2_layernorm_backward_workspace.argtypes = [i, i]
@@ -246,6 +248,16 @@ class GPT2:
             raise GPT2Error(rc, "gpt2_activation_view")
         off, rows, cols, ld = (v.value for v in vals)
         return self.acts[off: off + rows * ld].view(rows, ld)[:, :cols]
+
+
+GEMM_TILES_AUTO, GEMM_TILES_128, GEMM_TILES_96 = 0, 1, 2
+
+
+def set_gemm_tiles(policy: int) -> None:
+    """gpt2_set_gemm_tiles: tile width of the forward and dgrad matmuls (process-wide)."""
+    rc = load().gpt2_set_gemm_tiles(policy)
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, "gpt2_set_gemm_tiles")
 
 
 def layernorm_forward(y, mean, rstd, x, w, b, eps=1e-5, stream=None) -> None:

@@ -76,3 +76,13 @@ def test_build_argument_checks_need_no_gpu():
     assert lib.gpt2_layernorm_forward(None, None, None, None, None, None, 4, 8, 1e-5, None) == G.GPT2_EINVAL
     assert lib.gpt2_layernorm_backward_workspace(8192, 768) >= 2 * 768
     assert G.strerror(G.GPT2_ESTATE) == "call out of order"
+
+
+def test_gemm_tile_policy_values():
+    lib = G.load()
+    for bad in (-1, 3, 96):
+        assert lib.gpt2_set_gemm_tiles(bad) == G.GPT2_EINVAL
+    for ok in (G.GEMM_TILES_128, G.GEMM_TILES_96, G.GEMM_TILES_AUTO):
+        assert lib.gpt2_set_gemm_tiles(ok) == G.GPT2_OK
+    with pytest.raises(G.GPT2Error):
+        G.set_gemm_tiles(5)

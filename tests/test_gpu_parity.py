@@ -163,6 +163,21 @@ def test_gpt2_124m_short_ten_steps(G):
     check_training(G, S.GPT2_124M_SHORT, 10)
 
 
+@pytest.mark.parametrize("tiles", ["128", "96"])
+@pytest.mark.parametrize("wl", ["tiny", "124m_short"])
+def test_gemm_tile_widths(G, tiles, wl):
+    """Every forward and dgrad matmul forced to one tile width (the automatic choice only
+    takes 96-wide tiles at whole rounds of the grid): ragged column edges, split tiles and
+    their fix-ups, and the dlogits dgrad at both widths, three steps against the oracle."""
+    w = S.TINY if wl == "tiny" else S.GPT2_124M_SHORT
+    G.set_gemm_tiles(G.GEMM_TILES_128 if tiles == "128" else G.GEMM_TILES_96)
+    try:
+        say(f"[gemm tiles {tiles}]")
+        check_training(G, w, 3)
+    finally:
+        G.set_gemm_tiles(G.GEMM_TILES_AUTO)
+
+
 def test_smaller_batch_than_built(G):
     w = S.TINY
     say("[smaller batch]")
