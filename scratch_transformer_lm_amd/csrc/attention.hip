@@ -13,10 +13,23 @@
 // every product is a v_mfma_f32_16x16x4f32 chain (A[i][k] from lane i + 16k, B[k][j]
 // from lane j + 16k, C[i][j] in lane j + 16(i/4), register i%4).  The score tile is
 // computed transposed where that puts the probabilities directly into the A-operand
-// layout of the next product, so P never goes through LDS.  Inside each group of 16
-// head dimensions a lane feeds 4 consecutive dimensions to 4 consecutive MFMAs (a
-// reordering of the dot product), which makes every operand read one 16-byte LDS
-// read.  K/V (or Q/dO) tiles are double-buffered in LDS with register prefetch.
+// layout of the next product, so P never goes through LDS.  The next K/V (or Q/dO) tile
+// is prefetched into registers while the current one is used.  Forward and dQ keep one
+// LDS copy of each tile (two barriers per tile) so that three blocks fit a CU: with the
+// query tiles' very unequal lengths (1 to T/64 key tiles), 768 block slots schedule the
+// 1536 blocks of the 124M shape almost evenly where 512 slots leave a 9% tail.  dK/dV
+// double-buffers its tiles at two blocks per CU (measured faster there).
+//
+// LDS rows are stored head-dimension interleaved: dimension d = 16j + i (i < 16,
+// j < HS/16) sits at position (HS/16) i + j.  A tile is read two ways, and both become
+// one LDS read of HS/16 consecutive floats per lane (16 bytes at HS = 64):
+//  - as the operand of a dot product over d (S = Q K^T, dP = dO V^T): MFMA (a, j) takes
+//    from lane group g the dimension 16j + 4a + g, so a lane's HS/16 values for fixed a
+//    are the run at i = 4a + g (the dot product is summed in another order);
+//  - as the B operand of a product into d (O += P V, dQ += dS K, dK, dV): output block j
+//    holds dimensions 16j + i for lane i, i.e. the run at i.
+// Rows are padded to HS + 4 floats so that 16 lanes reading 16 rows, or 16 runs of one
+// row, hit 16 different bank groups.
 // dq and dk/dv come from two kernels (query-tile and key-tile ownership) so every
 // output element has one writer: no atomics, bitwise reproducible.
 #include <type_traits>
@@ -37,7 +50,6 @@ GPT2_DEV f32x4 mfma4(float a, float b, f32x4 c) { return __builtin_amdgcn_mfma_f
 
 GPT2_DEV f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-GPT2_DEV float comp(const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 // Softmax arithmetic runs in base 2 on the hardware transcendental unit (v_exp_f32,
 // v_log_f32): exp(x) = 2^(x log2 e), with log2 e folded into the score scale and the
@@ -46,37 +58,90 @@ constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
 GPT2_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 GPT2_DEV float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
-// Loads a 64-row x HS tile of rows [r0, r0+64) (row stride ld floats, rows >= T are
-// zero) into registers: thread t covers row t/(HS/4) + (256/(HS/4))*j, float4 column t%(HS/4).
+// DG = HS/16 consecutive floats of an interleaved LDS row (aligned to 4*DG bytes).
+template <int DG>
+GPT2_DEV void lds_get(float (&v)[DG], const float* src) {
+    if constexpr (DG == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(src);
+        v[0] = t.x;
+        v[1] = t.y;
+        v[2] = t.z;
+        v[3] = t.w;
+    } else if constexpr (DG == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(src);
+        v[0] = t.x;
+        v[1] = t.y;
+    } else {
+        v[0] = src[0];
+    }
+}
+
+template <int DG>
+GPT2_DEV void lds_put(float* dst, const float (&v)[DG]) {
+    if constexpr (DG == 4) *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    else if constexpr (DG == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+    else dst[0] = v[0];
+}
+
+// A 64-row x HS tile of rows [r0, r0+64) (row stride ld floats, rows >= T are zero) in
+// registers as 16-byte loads: thread t holds float4 column t % (HS/4) of rows
+// t / (HS/4) + (256 / (HS/4)) p.
 template <int HS>
 GPT2_DEV void tile_load(float4 (&reg)[HS / 16], const float* src, long ld, int r0, int T) {
     constexpr int C4 = HS / 4, RPP = 256 / C4;
     const int t = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < HS / 16; j++) {
-        const int r = r0 + t / C4 + RPP * j;
-        reg[j] = r < T ? *reinterpret_cast<const float4*>(src + (long)r * ld + (t % C4) * 4)
+    for (int p = 0; p < HS / 16; p++) {
+        const int r = r0 + t / C4 + RPP * p;
+        reg[p] = r < T ? *reinterpret_cast<const float4*>(src + (long)r * ld + (t % C4) * 4)
                        : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
 
+// Writes the tile into the interleaved layout: element e of float4 column c is dimension
+// d = 4c + e at position (HS/16)(d % 16) + d / 16.  At HS = 64 a wave's four single-float
+// writes per float4 each cover 64 distinct banks.
 template <int HS>
 GPT2_DEV void tile_store(float* S, const float4 (&reg)[HS / 16]) {
-    constexpr int C4 = HS / 4, RPP = 256 / C4, LD = HS + 4;
-    const int t = threadIdx.x;
+    constexpr int C4 = HS / 4, RPP = 256 / C4, LD = HS + 4, DG = HS / 16;
+    const int t = threadIdx.x, c = t % C4;
 #pragma unroll
-    for (int j = 0; j < HS / 16; j++)
-        *reinterpret_cast<float4*>(S + (t / C4 + RPP * j) * LD + (t % C4) * 4) = reg[j];
+    for (int p = 0; p < HS / 16; p++) {
+        float* row = S + (t / C4 + RPP * p) * LD;
+        if (DG == 1) {
+            *reinterpret_cast<float4*>(row + 4 * c) = reg[p];
+        } else {
+            const float e4[4] = {reg[p].x, reg[p].y, reg[p].z, reg[p].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int d = 4 * c + e;
+                row[DG * (d % 16) + d / 16] = e4[e];
+            }
+        }
+    }
+}
+
+// Keeps the compiler from moving instructions across this point: LDS reads issued before
+// it stay ahead of the MFMAs after it, so their latency is covered.
+GPT2_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// This lane's dimensions of one row for the dot-product operand: v[a][j] = row[16j + 4a + g].
+template <int HS>
+GPT2_DEV void dot_operand(float (&v)[4][HS / 16], const float* row, bool valid, int g) {
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int j = 0; j < HS / 16; j++) v[a][j] = valid ? row[16 * j + 4 * a + g] : 0.f;
 }
 
 // ---------------------------------------------------------------------------- forward
 template <int HS>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, float* __restrict__ lse,
+__global__ __launch_bounds__(256, 3) void attn_fwd_kernel(float* __restrict__ out, float* __restrict__ lse,
                                                        const float* __restrict__ qkv, int B, int T, int C, int NH,
                                                        float scale) {
     constexpr int DG = HS / 16, LD = HS + 4;
-    __shared__ __attribute__((aligned(16))) float Ks[2][TILE * LD];
-    __shared__ __attribute__((aligned(16))) float Vs[2][TILE * LD];
+    __shared__ __attribute__((aligned(16))) float Ks[TILE * LD];
+    __shared__ __attribute__((aligned(16))) float Vs[TILE * LD];
     const int nqt = (T + TILE - 1) / TILE;
     const int bh = blockIdx.x % (B * NH);
     const int qt = nqt - 1 - (int)(blockIdx.x / (B * NH));  // longest rows first
@@ -88,11 +153,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
     const int q0 = qt * TILE + wave * 16;
     const int tq = q0 + i16;
 
-    float4 qreg[DG];
-#pragma unroll
-    for (int g = 0; g < DG; g++)
-        qreg[g] = tq < T ? *reinterpret_cast<const float4*>(base + (long)tq * ld + h * HS + 16 * g + 4 * g4)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    float qreg[4][DG];
+    dot_operand<HS>(qreg, base + (long)min(tq, T - 1) * ld + h * HS, tq < T, g4);
     f32x4 o[DG];
 #pragma unroll
     for (int d = 0; d < DG; d++) o[d] = zero4();
@@ -103,31 +165,47 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
     const int nkt = qt + 1;
     tile_load<HS>(kreg, base + C + h * HS, ld, 0, T);
     tile_load<HS>(vreg, base + 2 * C + h * HS, ld, 0, T);
-    tile_store<HS>(Ks[0], kreg);
-    tile_store<HS>(Vs[0], vreg);
+    tile_store<HS>(Ks, kreg);
+    tile_store<HS>(Vs, vreg);
     __syncthreads();
     // one key tile; only the diagonal tile (kt == qt) has keys after the query
     auto step = [&](int kt, auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
-        const int cur = kt & 1;
         if (kt + 1 < nkt) {
             tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
             tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
         }
-        const float* K = Ks[cur];
-        const float* V = Vs[cur];
-        // S^T[key][query] = K Q^T for 4 blocks of 16 keys.
+        const float* K = Ks;
+        const float* V = Vs;
+        // S^T[key][query] = K Q^T for 4 blocks of 16 keys, the four chains interleaved;
+        // the K runs of step a+1 are read while step a multiplies
         f32x4 s[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
-            s[kb] = zero4();
+        for (int kb = 0; kb < 4; kb++) s[kb] = zero4();
+        float kf[2][4][DG];
+        auto read_k = [&](int a, float (&dst)[4][DG]) {
 #pragma unroll
-            for (int g = 0; g < DG; g++) {
-                const float4 kf = *reinterpret_cast<const float4*>(K + (kb * 16 + i16) * LD + 16 * g + 4 * g4);
+            for (int kb = 0; kb < 4; kb++) lds_get<DG>(dst[kb], K + (kb * 16 + i16) * LD + DG * (4 * a + g4));
+        };
+        read_k(0, kf[0]);
 #pragma unroll
-                for (int st = 0; st < 4; st++) s[kb] = mfma4(comp(kf, st), comp(qreg[g], st), s[kb]);
-            }
+        for (int a = 0; a < 4; a++) {
+            if (a + 1 < 4) read_k(a + 1, kf[(a + 1) & 1]);
+            sched_fence();
+#pragma unroll
+            for (int j = 0; j < DG; j++)
+#pragma unroll
+                for (int kb = 0; kb < 4; kb++) s[kb] = mfma4(kf[a & 1][kb][j], qreg[a][j], s[kb]);
+            sched_fence();
         }
+        // the V runs of the first key block, read while the softmax runs
+        float vf[2][4][DG];
+        auto read_v = [&](int kb, float (&dst)[4][DG]) {
+#pragma unroll
+            for (int v = 0; v < 4; v++) lds_get<DG>(dst[v], V + (kb * 16 + 4 * g4 + v) * LD + DG * i16);
+        };
+        read_v(0, vf[0]);
+        sched_fence();
         // lane holds raw scores of query tq against keys kt*64 + kb*16 + 4*g4 + v
         float mx = -INFINITY;
 #pragma unroll
@@ -168,20 +246,25 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
         rs += __shfl_xor(rs, 16, 64);
         rs += __shfl_xor(rs, 32, 64);
         l += rs;
-        // O += P V
+        // O += P V: for key kb*16 + 4*g4 + v this lane needs V[key][16d + i16], d < DG,
+        // which is one interleaved run; block kb+1's runs are read while block kb multiplies
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++)
+        for (int kb = 0; kb < 4; kb++) {
+            if (kb + 1 < 4) read_v(kb + 1, vf[(kb + 1) & 1]);
+            sched_fence();
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const float* vrow = V + (kb * 16 + 4 * g4 + v) * LD + i16;
+            for (int v = 0; v < 4; v++)
 #pragma unroll
-                for (int d = 0; d < DG; d++) o[d] = mfma4(s[kb][v], vrow[16 * d], o[d]);
-            }
-        if (kt + 1 < nkt) {
-            tile_store<HS>(Ks[cur ^ 1], kreg);
-            tile_store<HS>(Vs[cur ^ 1], vreg);
+                for (int d = 0; d < DG; d++) o[d] = mfma4(s[kb][v], vf[kb & 1][v][d], o[d]);
+            sched_fence();
         }
-        __syncthreads();
+        if (kt + 1 < nkt) {
+            // every wave is done with this tile before the next one overwrites it
+            __syncthreads();
+            tile_store<HS>(Ks, kreg);
+            tile_store<HS>(Vs, vreg);
+            __syncthreads();
+        }
     };
     for (int kt = 0; kt < qt; kt++) step(kt, std::false_type{});
     step(qt, std::true_type{});
@@ -201,13 +284,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(float* __restrict__ out, 
 
 // ---------------------------------------------------------------------------- dq (+ D)
 template <int HS>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dqkv, float* __restrict__ delta,
+__global__ __launch_bounds__(256, 3) void attn_bwd_dq_kernel(float* __restrict__ dqkv, float* __restrict__ delta,
                                                           const float* __restrict__ dout, const float* __restrict__ qkv,
                                                           const float* __restrict__ out, const float* __restrict__ lse,
                                                           int B, int T, int C, int NH, float scale) {
     constexpr int DG = HS / 16, LD = HS + 4;
-    __shared__ __attribute__((aligned(16))) float Ks[2][TILE * LD];
-    __shared__ __attribute__((aligned(16))) float Vs[2][TILE * LD];
+    __shared__ __attribute__((aligned(16))) float Ks[TILE * LD];
+    __shared__ __attribute__((aligned(16))) float Vs[TILE * LD];
     const int nqt = (T + TILE - 1) / TILE;
     const int bh = blockIdx.x % (B * NH);
     const int qt = nqt - 1 - (int)(blockIdx.x / (B * NH));
@@ -219,21 +302,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
     const int q0 = qt * TILE + wave * 16;
     const int tq = q0 + i16;
     const bool valid = tq < T;
+    const long trow = (long)b * T + min(tq, T - 1);
 
-    float4 qreg[DG], doreg[DG];
+    float qreg[4][DG], doreg[4][DG], oreg[4][DG];
+    dot_operand<HS>(qreg, qkv + trow * ld + h * HS, valid, g4);
+    dot_operand<HS>(doreg, dout + trow * C + h * HS, valid, g4);
+    dot_operand<HS>(oreg, out + trow * C + h * HS, valid, g4);
     float dd = 0.f;
 #pragma unroll
-    for (int g = 0; g < DG; g++) {
-        const int col = h * HS + 16 * g + 4 * g4;
-        if (valid) {
-            qreg[g] = *reinterpret_cast<const float4*>(base + (long)tq * ld + col);
-            doreg[g] = *reinterpret_cast<const float4*>(dout + ((long)b * T + tq) * C + col);
-            const float4 ov = *reinterpret_cast<const float4*>(out + ((long)b * T + tq) * C + col);
-            dd += doreg[g].x * ov.x + doreg[g].y * ov.y + doreg[g].z * ov.z + doreg[g].w * ov.w;
-        } else {
-            qreg[g] = doreg[g] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int j = 0; j < DG; j++) dd = fmaf(doreg[a][j], oreg[a][j], dd);
     dd += __shfl_xor(dd, 16, 64);
     dd += __shfl_xor(dd, 32, 64);
     const float D = dd;
@@ -248,31 +327,41 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
     const int nkt = qt + 1;
     tile_load<HS>(kreg, base + C + h * HS, ld, 0, T);
     tile_load<HS>(vreg, base + 2 * C + h * HS, ld, 0, T);
-    tile_store<HS>(Ks[0], kreg);
-    tile_store<HS>(Vs[0], vreg);
+    tile_store<HS>(Ks, kreg);
+    tile_store<HS>(Vs, vreg);
     __syncthreads();
     // one key tile; only the diagonal tile (kt == qt) has keys after the query
     auto step = [&](int kt, auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
-        const int cur = kt & 1;
         if (kt + 1 < nkt) {
             tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
             tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
         }
-        const float* K = Ks[cur];
-        const float* V = Vs[cur];
+        const float* K = Ks;
+        const float* V = Vs;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
             f32x4 s = zero4(), dp = zero4();
+            // the K runs for dQ first (used last), then K and V fragments one step ahead
+            float kr[4][DG];
 #pragma unroll
-            for (int g = 0; g < DG; g++) {
-                const float4 kf = *reinterpret_cast<const float4*>(K + (kb * 16 + i16) * LD + 16 * g + 4 * g4);
-                const float4 vf = *reinterpret_cast<const float4*>(V + (kb * 16 + i16) * LD + 16 * g + 4 * g4);
+            for (int v = 0; v < 4; v++) lds_get<DG>(kr[v], K + (kb * 16 + 4 * g4 + v) * LD + DG * i16);
+            float kf[2][DG], vf[2][DG];
+            auto read_kv = [&](int a, float (&k)[DG], float (&v)[DG]) {
+                lds_get<DG>(k, K + (kb * 16 + i16) * LD + DG * (4 * a + g4));
+                lds_get<DG>(v, V + (kb * 16 + i16) * LD + DG * (4 * a + g4));
+            };
+            read_kv(0, kf[0], vf[0]);
 #pragma unroll
-                for (int st = 0; st < 4; st++) {
-                    s = mfma4(comp(kf, st), comp(qreg[g], st), s);
-                    dp = mfma4(comp(vf, st), comp(doreg[g], st), dp);
+            for (int a = 0; a < 4; a++) {
+                if (a + 1 < 4) read_kv(a + 1, kf[(a + 1) & 1], vf[(a + 1) & 1]);
+                sched_fence();
+#pragma unroll
+                for (int j = 0; j < DG; j++) {
+                    s = mfma4(kf[a & 1][j], qreg[a][j], s);
+                    dp = mfma4(vf[a & 1][j], doreg[a][j], dp);
                 }
+                sched_fence();
             }
             // lane: key kt*64 + kb*16 + 4*g4 + v, query tq
             float ds[4];
@@ -283,17 +372,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(float* __restrict__ dq
                 ds[v] = p * (dp[v] - D);
             }
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const float* krow = K + (kb * 16 + 4 * g4 + v) * LD + i16;
+            for (int v = 0; v < 4; v++)
 #pragma unroll
-                for (int d = 0; d < DG; d++) dq[d] = mfma4(ds[v], krow[16 * d], dq[d]);
-            }
+                for (int d = 0; d < DG; d++) dq[d] = mfma4(ds[v], kr[v][d], dq[d]);
         }
         if (kt + 1 < nkt) {
-            tile_store<HS>(Ks[cur ^ 1], kreg);
-            tile_store<HS>(Vs[cur ^ 1], vreg);
+            // every wave is done with this tile before the next one overwrites it
+            __syncthreads();
+            tile_store<HS>(Ks, kreg);
+            tile_store<HS>(Vs, vreg);
+            __syncthreads();
         }
-        __syncthreads();
     };
     for (int kt = 0; kt < qt; kt++) step(kt, std::false_type{});
     step(qt, std::true_type{});
@@ -332,17 +421,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
     const int u0 = kt * TILE + wave * 16;
     const int tu = u0 + i16;
 
-    float4 kreg[DG], vreg[DG];
-#pragma unroll
-    for (int g = 0; g < DG; g++) {
-        const int col = h * HS + 16 * g + 4 * g4;
-        if (tu < T) {
-            kreg[g] = *reinterpret_cast<const float4*>(base + (long)tu * ld + C + col);
-            vreg[g] = *reinterpret_cast<const float4*>(base + (long)tu * ld + 2 * C + col);
-        } else {
-            kreg[g] = vreg[g] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
+    float kreg[4][DG], vreg[4][DG];
+    dot_operand<HS>(kreg, base + (long)min(tu, T - 1) * ld + C + h * HS, tu < T, g4);
+    dot_operand<HS>(vreg, base + (long)min(tu, T - 1) * ld + 2 * C + h * HS, tu < T, g4);
     f32x4 dk[DG], dv[DG];
 #pragma unroll
     for (int d = 0; d < DG; d++) dk[d] = dv[d] = zero4();
@@ -384,15 +465,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
 #pragma unroll
         for (int qb = 0; qb < 4; qb++) {
             f32x4 s = zero4(), dp = zero4();
+            // dV += P^T dO, dK += dS^T Q: this lane needs dO and Q of query qb*16 + 4*g4 + v
+            // at dimensions 16d + i16, one interleaved run each (read first, used last)
+            float orun[4][DG], qrun[4][DG];
 #pragma unroll
-            for (int g = 0; g < DG; g++) {
-                const float4 qf = *reinterpret_cast<const float4*>(Q + (qb * 16 + i16) * LD + 16 * g + 4 * g4);
-                const float4 of = *reinterpret_cast<const float4*>(O + (qb * 16 + i16) * LD + 16 * g + 4 * g4);
+            for (int v = 0; v < 4; v++) {
+                const int qi = qb * 16 + 4 * g4 + v;
+                lds_get<DG>(orun[v], O + qi * LD + DG * i16);
+                lds_get<DG>(qrun[v], Q + qi * LD + DG * i16);
+            }
+            float qf[2][DG], of[2][DG];
+            auto read_qo = [&](int a, float (&q)[DG], float (&o)[DG]) {
+                lds_get<DG>(q, Q + (qb * 16 + i16) * LD + DG * (4 * a + g4));
+                lds_get<DG>(o, O + (qb * 16 + i16) * LD + DG * (4 * a + g4));
+            };
+            read_qo(0, qf[0], of[0]);
 #pragma unroll
-                for (int st = 0; st < 4; st++) {
-                    s = mfma4(comp(qf, st), comp(kreg[g], st), s);
-                    dp = mfma4(comp(of, st), comp(vreg[g], st), dp);
+            for (int a = 0; a < 4; a++) {
+                if (a + 1 < 4) read_qo(a + 1, qf[(a + 1) & 1], of[(a + 1) & 1]);
+                sched_fence();
+#pragma unroll
+                for (int j = 0; j < DG; j++) {
+                    s = mfma4(qf[a & 1][j], kreg[a][j], s);
+                    dp = mfma4(of[a & 1][j], vreg[a][j], dp);
                 }
+                sched_fence();
             }
             // lane: query qt*64 + qb*16 + 4*g4 + v, key tu
             float p[4], ds[4];
@@ -405,16 +502,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
                 ds[v] = pv * (dp[v] - Ds[cur][qi]);
             }
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int qi = qb * 16 + 4 * g4 + v;
-                const float* orow = O + qi * LD + i16;
-                const float* qrow = Q + qi * LD + i16;
+            for (int v = 0; v < 4; v++)
 #pragma unroll
                 for (int d = 0; d < DG; d++) {
-                    dv[d] = mfma4(p[v], orow[16 * d], dv[d]);
-                    dk[d] = mfma4(ds[v], qrow[16 * d], dk[d]);
+                    dv[d] = mfma4(p[v], orun[v][d], dv[d]);
+                    dk[d] = mfma4(ds[v], qrun[v][d], dk[d]);
                 }
-            }
         }
         if (qt + 1 < nqt) {
             tile_store<HS>(Qs[cur ^ 1], qreg);
