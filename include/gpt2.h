@@ -173,6 +173,16 @@ int gpt2_profile_collect(gpt2* model);
 int gpt2_profile_entry(gpt2* model, int i, const char** name, long* launches, double* total_ms,
                        double* flops, double* bytes);
 
+/* Stream schedule of gpt2_backward.  streams = 2 (the default): each layer's weight
+ * gradients (dW += dY^T X and the bias sums, which need only that layer's output
+ * gradient) run on a second stream the handle owns, overlapping the main chain of
+ * dgrads, attention and LayerNorm; events order the two streams and gpt2_backward's work
+ * is complete, in order, on the model's stream when everything enqueued after it runs.
+ * streams = 1 runs everything on the model's stream.  Both schedules compute bitwise
+ * the same results (every kernel's arithmetic is the same).  Returns GPT2_OK, or
+ * GPT2_EINVAL for a null model or another value. */
+int gpt2_set_backward_streams(gpt2* model, int streams);
+
 /* Tile width of the forward and dgrad matmuls (process-wide; call it between steps, not
  * while another host thread launches work).  GPT2_GEMM_TILES_AUTO (the default) uses
  * 128 x 96 output tiles where their count is a whole number of rounds of the chip's 512

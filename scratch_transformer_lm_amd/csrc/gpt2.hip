@@ -66,7 +66,7 @@ struct Layout {
     size_t tok_in, tok_tgt;  // int32 arrays inside acts (offset in 4-byte words)
     size_t n_acts;
     // grad_scratch
-    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, n_scratch;
+    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, n_scratch;
 };
 
 Layout make_layout(const gpt2_config* c, int B, int T) {
@@ -125,6 +125,7 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     np = std::max(np, layernorm_partial_floats((int)BT, (int)C));
     y.n_partial = np;
     y.partial = take(np);
+    y.partial_w = take(gemm_partial_floats());  // split tiles of the weight-gradient stream
     y.n_scratch = s;
     return y;
 }
@@ -137,6 +138,11 @@ struct gpt2 {
     int B, T;
     Layout lay;
     hipStream_t st;
+    // Backward runs the weight-gradient GEMMs on a second stream of the handle's own,
+    // ordered against the main chain by events (see backward_impl).
+    hipStream_t st_w;
+    hipEvent_t ev[8];
+    int backward_streams;  // 2: weight gradients on st_w; 1: everything on st
     gpt2_buffers buf;
     size_t nparams;
     size_t poff[NP], plen[NP];
@@ -255,32 +261,64 @@ int backward_impl(gpt2* g) {
     else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, st));
     HIPCHK(g, layernorm_backward(dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
                                  A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
+    // Per layer, the weight gradients (dW += dY^T X, db) need only that layer's output
+    // gradient, so they run on the handle's second stream and overlap the main chain
+    // (dgrads, attention, LayerNorm).  Events order the two: the second stream waits for
+    // each dY it reads; the main stream waits before it rewrites a buffer the second
+    // stream still reads (dres by the LayerNorm backwards, dfch by the next layer's fcproj
+    // dgrad, dqkv by the next layer's attention backward), and before returning.  The
+    // arithmetic of every kernel is unchanged, so results are bitwise those of one stream.
+    hipStream_t sw = g->backward_streams == 2 ? g->st_w : st;
+    float* part_w = S(g, g->lay.partial_w);
+    enum { EV_DRES_A, EV_DFCH, EV_DRES_B, EV_DQKV, EV_W_FCPROJ, EV_W_FC, EV_W_ATTPROJ, EV_W_QKV };
+    auto mark = [&](int e, hipStream_t s) { return hipEventRecord(g->ev[e], s); };
+    auto after = [&](hipStream_t s, int e) { return hipStreamWaitEvent(s, g->ev[e], 0); };
     for (int l = L - 1; l >= 0; l--) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
+        const bool later = l < L - 1;  // the previous iteration's weight gradients exist
         // MLP projection: residual3 = residual2 + gelu(fch) . Wp^T + bp.
+        HIPCHK(g, mark(EV_DRES_A, st));
+        HIPCHK(g, after(sw, EV_DRES_A));
         HIPCHK(g, linear_wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, G(g, P_FCPROJB) + l * C, dres, C, A(g, GPT2_ACT_FCH_GELU, l), C, 4 * C, BT,
-                               part, st));
+                               part_w, sw));
+        HIPCHK(g, mark(EV_W_FCPROJ, sw));
+        if (later) HIPCHK(g, after(st, EV_W_FC));  // the fc wgrad above still reads dfch
         HIPCHK(g, linear_dgrad(dfch, dres, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C,
                                part, st));
         // MLP expansion: fch = ln2 . Wf^T + bf.
+        HIPCHK(g, mark(EV_DFCH, st));
+        HIPCHK(g, after(sw, EV_DFCH));
         HIPCHK(g, linear_wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, G(g, P_FCB) + l * 4 * C, dfch, 4 * C, A(g, GPT2_ACT_LN2, l), 4 * C, C, BT,
-                               part, st));
+                               part_w, sw));
+        HIPCHK(g, mark(EV_W_FC, sw));
         HIPCHK(g, linear_dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, nullptr, BT, C, 4 * C, part, st));
+        HIPCHK(g, after(st, EV_W_FCPROJ));  // dres is about to change
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
                                      P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C,
                                      true, true, part, st));
         // Attention projection: residual2 = residual + atty . Wa^T + ba.
-        HIPCHK(g, linear_wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, G(g, P_ATTPROJB) + l * C, dres, C, A(g, GPT2_ACT_ATTY, l), C, C, BT, part, st));
+        HIPCHK(g, mark(EV_DRES_B, st));
+        HIPCHK(g, after(sw, EV_DRES_B));
+        HIPCHK(g, linear_wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, G(g, P_ATTPROJB) + l * C, dres, C, A(g, GPT2_ACT_ATTY, l), C, C, BT,
+                               part_w, sw));
+        HIPCHK(g, mark(EV_W_ATTPROJ, sw));
         HIPCHK(g, linear_dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, nullptr, BT, C, C, part, st));
+        if (later) HIPCHK(g, after(st, EV_W_QKV));  // the qkv wgrad above still reads dqkv
         HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
                                      A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
+        HIPCHK(g, mark(EV_DQKV, st));
+        HIPCHK(g, after(sw, EV_DQKV));
         HIPCHK(g, linear_wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, 3 * C, A(g, GPT2_ACT_LN1, l), 3 * C, C, BT,
-                               part, st));
+                               part_w, sw));
+        HIPCHK(g, mark(EV_W_QKV, sw));
         HIPCHK(g, linear_dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, nullptr, BT, C, 3 * C, part, st));
+        HIPCHK(g, after(st, EV_W_ATTPROJ));  // dres is about to change
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                                      A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
     }
+    // the second stream's last kernel (layer 0's qkv wgrad) ends all of its work
+    if (L > 0) HIPCHK(g, after(st, EV_W_QKV));
     HIPCHK(g, wpe_backward(G(g, P_WPE), dres, B, T, C, st));
     if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, dres, C, 1.0f, wk_in, BT, st));
     else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_in(g), BT, dres, C, 1.0f, wk_in, st));
@@ -339,6 +377,7 @@ int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buff
     g->T = T;
     g->lay = make_layout(cfg, B, T);
     g->st = (hipStream_t)stream;
+    g->backward_streams = 2;
     g->buf = b;
     g->nparams = gpt2_num_parameters(cfg);
     gpt2_param_layout(cfg, g->poff, g->plen);
@@ -346,8 +385,18 @@ int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buff
         free(g);
         return GPT2_EDEVICE;
     }
-    if (fill_zero(b.grads, g->nparams, g->st) != hipSuccess || fill_zero(b.m, g->nparams, g->st) != hipSuccess ||
-        fill_zero(b.v, g->nparams, g->st) != hipSuccess) {
+    // the weight-gradient stream (default priority, no implicit sync with the null stream)
+    // and the events that order it against the main stream
+    bool ok = hipStreamCreateWithFlags(&g->st_w, hipStreamNonBlocking) == hipSuccess;
+    int nev = 0;
+    for (; ok && nev < 8; nev++) ok = hipEventCreateWithFlags(&g->ev[nev], hipEventDisableTiming) == hipSuccess;
+    if (ok) {
+        ok = fill_zero(b.grads, g->nparams, g->st) == hipSuccess && fill_zero(b.m, g->nparams, g->st) == hipSuccess &&
+             fill_zero(b.v, g->nparams, g->st) == hipSuccess;
+    }
+    if (!ok) {
+        for (int i = 0; i < nev; i++) (void)hipEventDestroy(g->ev[i]);
+        if (g->st_w) (void)hipStreamDestroy(g->st_w);
         (void)hipHostFree(g->host_ret);
         free(g);
         return GPT2_EDEVICE;
@@ -415,6 +464,9 @@ const char* gpt2_strerror(int code) {
 void gpt2_free(gpt2* g) {
     if (!g) return;
     (void)hipStreamSynchronize(g->st);
+    (void)hipStreamSynchronize(g->st_w);
+    for (hipEvent_t e : g->ev) (void)hipEventDestroy(e);
+    (void)hipStreamDestroy(g->st_w);
     if (g->prof) prof_destroy(g->prof);
     (void)hipHostFree(g->host_ret);
     free(g);
@@ -422,7 +474,8 @@ void gpt2_free(gpt2* g) {
 
 int gpt2_profile_enable(gpt2* g, int enable) {
     if (!g) return GPT2_EINVAL;
-    if (hipStreamSynchronize(g->st) != hipSuccess) return fail(g, GPT2_EDEVICE);
+    if (hipStreamSynchronize(g->st) != hipSuccess || hipStreamSynchronize(g->st_w) != hipSuccess)
+        return fail(g, GPT2_EDEVICE);
     if (enable && !g->prof) {
         g->prof = prof_create();
         if (!g->prof) return fail(g, GPT2_EDEVICE);
@@ -478,6 +531,12 @@ int gpt2_layernorm_forward(float* y, float* mean, float* rstd, const float* x, c
     if (!aligned(y) || !aligned(x) || !aligned(w) || !aligned(b)) return GPT2_EINVAL;
     return layernorm_forward(y, mean, rstd, x, w, b, N, C, eps, (hipStream_t)stream) == hipSuccess ? GPT2_OK
                                                                                                       : GPT2_EDEVICE;
+}
+
+int gpt2_set_backward_streams(gpt2* g, int streams) {
+    if (!g || (streams != 1 && streams != 2)) return GPT2_EINVAL;
+    g->backward_streams = streams;
+    return GPT2_OK;
 }
 
 int gpt2_set_gemm_tiles(int policy) {

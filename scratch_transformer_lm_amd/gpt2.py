@@ -93,6 +93,8 @@ def load() -> ct.CDLL:
                                        ct.POINTER(ct.c_double), ct.POINTER(ct.c_double),
                                        ct.POINTER(ct.c_double)]
     lib.gpt2_profile_entry.restype = i
+    lib.gpt2_set_backward_streams.argtypes = [P, i]
+    lib.gpt2_set_backward_streams.restype = i
     lib.gpt2_set_gemm_tiles.argtypes = [i]
     lib.gpt2_set_gemm_tiles.restype = i
     lib.gpt2_layernorm_forward.argtypes = [P, P, P, P, P, P, i, i, f, P]
@@ -205,6 +207,12 @@ class GPT2:
 
     def last_error(self) -> int:
         return self.lib.gpt2_last_error(self.h)
+
+    def set_backward_streams(self, streams: int) -> None:
+        """gpt2_set_backward_streams: 2 overlaps the weight gradients with the main chain."""
+        rc = self.lib.gpt2_set_backward_streams(self.h, streams)
+        if rc != GPT2_OK:
+            raise GPT2Error(rc, "gpt2_set_backward_streams")
 
     # -- per-kernel timing ------------------------------------------------------------
     def profile_enable(self, on: bool = True) -> bool:

@@ -86,3 +86,9 @@ def test_gemm_tile_policy_values():
         assert lib.gpt2_set_gemm_tiles(ok) == G.GPT2_OK
     with pytest.raises(G.GPT2Error):
         G.set_gemm_tiles(5)
+
+
+def test_backward_streams_argument_checks():
+    lib = G.load()
+    assert lib.gpt2_set_backward_streams(None, 2) == G.GPT2_EINVAL
+    assert lib.gpt2_set_backward_streams(None, 1) == G.GPT2_EINVAL

@@ -178,6 +178,35 @@ def test_gemm_tile_widths(G, tiles, wl):
         G.set_gemm_tiles(G.GEMM_TILES_AUTO)
 
 
+def test_backward_stream_schedules_agree_bitwise(G):
+    """The default backward overlaps the weight gradients on a second stream; the
+    single-stream schedule runs the same kernels in one order.  Two steps each: losses,
+    gradients and updated parameters must be bitwise equal."""
+    w = S.GPT2_124M_SHORT
+    say("[backward streams]")
+    params = S.init_params(w.model)
+    x, y = S.tokens(w)
+    runs = []
+    for streams in (2, 1):
+        m = G.GPT2(w.model, w.B, w.T)
+        m.set_backward_streams(streams)
+        m.params.copy_(dev(params))
+        tx, ty = dev(x, torch.int32), dev(y, torch.int32)
+        losses, grads = [], []
+        for t in (1, 2):
+            losses.append(m.forward(tx, ty))
+            assert m.zero_grad() == 0 and m.backward() == 0, G.strerror(m.last_error())
+            grads.append(host(m.grads).copy())
+            assert m.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t) == 0
+        runs.append((losses, grads, host(m.params).copy()))
+        m.close()
+    (l2, g2, p2), (l1, g1, p1) = runs
+    assert l2 == l1
+    for a, b in zip(g2, g1):
+        assert np.array_equal(a, b)
+    assert np.array_equal(p2, p1)
+
+
 def test_smaller_batch_than_built(G):
     w = S.TINY
     say("[smaller batch]")
