@@ -141,7 +141,7 @@ struct gpt2 {
     // Backward runs the weight-gradient GEMMs on a second stream of the handle's own,
     // ordered against the main chain by events (see backward_impl).
     hipStream_t st_w;
-    hipEvent_t ev[8];
+    hipEvent_t ev[10];
     int backward_streams;  // 2: weight gradients on st_w; 1: everything on st
     gpt2_buffers buf;
     size_t nparams;
@@ -254,11 +254,22 @@ int backward_impl(gpt2* g) {
     // dlogits = (softmax(logits) - onehot(target)) / (B*T) is formed as the GEMMs load the
     // logits (softmax = exp(logit - lse)).
     const XentOperand xo{A(g, GPT2_ACT_LOGITS_LSE), tok_tgt(g), 1.0f / (float)BT};
-    HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
-    HIPCHK(g, linear_wgrad(G(g, P_WTE), nullptr, logits, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part, st, &xo));
+    // Weight gradients run on the handle's second stream (see below); the LM head's
+    // (dwte += dlogits^T lnf, then the one-hot rows) go first, both on that stream since
+    // both accumulate into dwte.
+    hipStream_t sw = g->backward_streams == 2 ? g->st_w : st;
+    float* part_w = S(g, g->lay.partial_w);
+    enum { EV_DRES_A, EV_DFCH, EV_DRES_B, EV_DQKV, EV_W_FCPROJ, EV_W_FC, EV_W_ATTPROJ, EV_W_QKV, EV_LM, EV_W_LM };
+    auto mark = [&](int e, hipStream_t s) { return hipEventRecord(g->ev[e], s); };
+    auto after = [&](hipStream_t s, int e) { return hipStreamWaitEvent(s, g->ev[e], 0); };
+    HIPCHK(g, mark(EV_LM, st));
+    HIPCHK(g, after(sw, EV_LM));
+    HIPCHK(g, linear_wgrad(G(g, P_WTE), nullptr, logits, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part_w, sw, &xo));
     // the one-hot part of dlogits: dwte[target] -= lnf / BT
-    if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, BT, st));
-    else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, st));
+    if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, BT, sw));
+    else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, sw));
+    HIPCHK(g, mark(EV_W_LM, sw));
+    HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
     HIPCHK(g, layernorm_backward(dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
                                  A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
     // Per layer, the weight gradients (dW += dY^T X, db) need only that layer's output
@@ -268,11 +279,6 @@ int backward_impl(gpt2* g) {
     // stream still reads (dres by the LayerNorm backwards, dfch by the next layer's fcproj
     // dgrad, dqkv by the next layer's attention backward), and before returning.  The
     // arithmetic of every kernel is unchanged, so results are bitwise those of one stream.
-    hipStream_t sw = g->backward_streams == 2 ? g->st_w : st;
-    float* part_w = S(g, g->lay.partial_w);
-    enum { EV_DRES_A, EV_DFCH, EV_DRES_B, EV_DQKV, EV_W_FCPROJ, EV_W_FC, EV_W_ATTPROJ, EV_W_QKV };
-    auto mark = [&](int e, hipStream_t s) { return hipEventRecord(g->ev[e], s); };
-    auto after = [&](hipStream_t s, int e) { return hipStreamWaitEvent(s, g->ev[e], 0); };
     for (int l = L - 1; l >= 0; l--) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         const bool later = l < L - 1;  // the previous iteration's weight gradients exist
@@ -317,8 +323,8 @@ int backward_impl(gpt2* g) {
         HIPCHK(g, layernorm_backward(dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                                      A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
     }
-    // the second stream's last kernel (layer 0's qkv wgrad) ends all of its work
-    if (L > 0) HIPCHK(g, after(st, EV_W_QKV));
+    // the second stream's last kernel ends all of its work (dwte is written below)
+    HIPCHK(g, after(st, L > 0 ? EV_W_QKV : EV_W_LM));
     HIPCHK(g, wpe_backward(G(g, P_WPE), dres, B, T, C, st));
     if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, dres, C, 1.0f, wk_in, BT, st));
     else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_in(g), BT, dres, C, 1.0f, wk_in, st));
@@ -389,7 +395,7 @@ int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buff
     // and the events that order it against the main stream
     bool ok = hipStreamCreateWithFlags(&g->st_w, hipStreamNonBlocking) == hipSuccess;
     int nev = 0;
-    for (; ok && nev < 8; nev++) ok = hipEventCreateWithFlags(&g->ev[nev], hipEventDisableTiming) == hipSuccess;
+    for (; ok && nev < 10; nev++) ok = hipEventCreateWithFlags(&g->ev[nev], hipEventDisableTiming) == hipSuccess;
     if (ok) {
         ok = fill_zero(b.grads, g->nparams, g->st) == hipSuccess && fill_zero(b.m, g->nparams, g->st) == hipSuccess &&
              fill_zero(b.v, g->nparams, g->st) == hipSuccess;
