@@ -199,6 +199,21 @@ def main():
     isolated = model.profile_entries()
     model.profile_enable(False)
     model.set_backward_streams(2)
+    # Forward-only generation with the trained-for-K-steps weights (the pages' sample
+    # loop): 64 new tokens from the end-of-text token, one fixed coin per token, each
+    # step recomputing the whole prefix; the sampling kernel timed with events.
+    gen_new = 64
+    coins = np.random.default_rng(7).random(gen_new).astype(np.float32)
+    eot = w.model.vocab_size - 1
+    model.profile_enable(True)
+    model.profile_filter("sample_kernel")
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    gen = model.generate([eot], gen_new + 1, coins)
+    torch.cuda.synchronize()
+    dt_gen = time.perf_counter() - t2
+    sk = [e for e in model.profile_entries() if e["name"] == "sample_kernel"]
+    model.profile_enable(False)
     if model.last_error() != 0 or not all(np.isfinite(losses)):
         print(f"bench: step failed: {G.strerror(model.last_error())}, losses {losses}", file=sys.stderr)
         sys.exit(1)
@@ -238,6 +253,14 @@ def main():
     out["roofline"]["schedule"] = ("timed steps overlap each layer's weight-gradient GEMMs (second stream) "
                                    "with the dgrad/attention/LayerNorm chain; 'isolated' is one "
                                    "single-stream step")
+    out["generation"] = {
+        "new_tokens": gen_new, "prompt": [eot], "tokens_per_s": gen_new / dt_gen,
+        "ms_per_token": dt_gen * 1e3 / gen_new, "batch": 1,
+        "method": "forward over the whole prefix per token (no key/value cache), then sample_mult on the "
+                  "last position; coins from numpy default_rng(7)",
+        "sample_kernel_us": sk[0]["ms"] * 1e3 / sk[0]["launches"] if sk else None,
+        "first_tokens": [int(v) for v in gen[:9]],
+    }
     out["kernels"] = breakdown(all_kernels, max(1, args.warmup - 1))
     out["kernels_isolated"] = breakdown(isolated, 1)
     traffic = recorded_traffic(out["roofline"]["kernel"])

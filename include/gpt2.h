@@ -173,6 +173,33 @@ int gpt2_profile_collect(gpt2* model);
 int gpt2_profile_entry(gpt2* model, int i, const char** name, long* launches, double* total_ms,
                        double* flops, double* bytes);
 
+/* Next-token sampling, the pages' sample_mult (huxiu page "llm.c：Andrej Karpathy带你从零
+ * 复现LLM", 核心代码解读 item 5: draw an index from a probability distribution; the main
+ * loop samples with it to generate text).  For each request i, row rows[i] (= b*T + t of
+ * the last gpt2_forward, which may have had targets == NULL) gives the distribution
+ * p = softmax(logits[row, 0..V)), and tokens[i] is the smallest index j with
+ * coins[i] < p_0 + ... + p_j, or V-1 if rounding leaves the total at or below the coin.
+ * The coins are the random numbers the caller draws, uniform in [0, 1): the library
+ * holds no random state, so a run is reproducible from its coins.
+ * Host arrays of n entries (the caller owns them); the call synchronises the model's
+ * stream.  The probabilities are fp32 exp(z - lse) with fp64 running sums, so a coin
+ * within ~1e-6 of a cumulative boundary may land on either neighbour.
+ * Returns GPT2_OK; GPT2_EINVAL for a null model or array, n < 0, n > B*T of the last
+ * forward, a row outside it or a coin outside [0, 1); GPT2_ESTATE without a forward. */
+int gpt2_sample(gpt2* model, const int32_t* rows, const float* coins, int n, int32_t* tokens);
+
+/* The pages' generation loop (新智元 article, 快速入门: the program ends by generating a
+ * sample; the printed samples start from token 50256).  tokens is a host array of
+ * total_len entries whose first prompt_len are given; for t = prompt_len .. total_len-1
+ * it runs gpt2_forward over tokens[0..t) as one row (B = 1, no targets) and sets
+ * tokens[t] = gpt2_sample of row t-1 with coins[t - prompt_len].  Each step recomputes
+ * the whole prefix (no key/value cache), as the pages' loop does.  Needs
+ * 1 <= prompt_len < total_len <= max_seq_len and total_len - 1 <= the build's B*T.
+ * Afterwards the model holds the last step's forward (B = 1, no targets).
+ * Returns GPT2_OK, GPT2_EINVAL (arguments, or a token outside [0, V)), or an error of
+ * the underlying forward or sample. */
+int gpt2_generate(gpt2* model, int32_t* tokens, int prompt_len, int total_len, const float* coins);
+
 /* Stream schedule of gpt2_backward.  streams = 2 (the default): each layer's weight
  * gradients (dW += dY^T X and the bias sums, which need only that layer's output
  * gradient) run on a second stream the handle owns, overlapping the main chain of

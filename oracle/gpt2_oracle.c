@@ -419,6 +419,19 @@ EXPORT void oracle_softmax_forward(real* probs, const real* logits, int N, int V
     }
 }
 
+/* sample_mult (huxiu page, 核心代码解读 item 5: draw an index from a probability
+ * distribution): walk the distribution in index order, accumulating its mass, and
+ * return the first index whose running total exceeds the coin; if rounding leaves the
+ * total at or below the coin, the last index. */
+EXPORT int oracle_sample_mult(const real* probs, int n, real coin) {
+    real cdf = 0;
+    for (int i = 0; i < n; i++) {
+        cdf += probs[i];
+        if (coin < cdf) return i;
+    }
+    return n - 1;
+}
+
 /* loss[i] = -log probs[i, target[i]]; every position counts (no ignored index). */
 EXPORT void oracle_crossentropy_forward(real* losses, const real* probs, const int32_t* targets,
                                         int N, int V) {

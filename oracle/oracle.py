@@ -76,6 +76,8 @@ def load(precision: str = "f64") -> ct.CDLL:
     lib.oracle_residual_forward.argtypes = [P, P, P, sz]
     lib.oracle_residual_backward.argtypes = [P, P, P, sz]
     lib.oracle_softmax_forward.argtypes = [P, P, i, i]
+    lib.oracle_sample_mult.argtypes = [P, i, real]
+    lib.oracle_sample_mult.restype = i
     lib.oracle_crossentropy_forward.argtypes = [P, P, P, i, i]
     lib.oracle_crossentropy_softmax_backward.argtypes = [P, P, P, P, i, i]
     lib.oracle_adamw.argtypes = [P, P, P, P, sz, real, real, real, real, real, i]
@@ -298,6 +300,13 @@ def softmax_forward(logits, precision="f64"):
     p = np.empty_like(z)
     lib.oracle_softmax_forward(_ptr(p), _ptr(z), N, V)
     return p
+
+
+def sample_mult(probs, coin, precision="f64"):
+    """Index drawn from the distribution `probs` (1-D) by the coin in [0, 1)."""
+    lib = load(precision)
+    p = _real(probs, precision).reshape(-1)
+    return int(lib.oracle_sample_mult(_ptr(p), len(p), float(coin)))
 
 
 def crossentropy_forward(probs, targets, precision="f64"):

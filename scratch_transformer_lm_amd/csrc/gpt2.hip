@@ -66,7 +66,7 @@ struct Layout {
     size_t tok_in, tok_tgt;  // int32 arrays inside acts (offset in 4-byte words)
     size_t n_acts;
     // grad_scratch
-    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, n_scratch;
+    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, sample, n_scratch;
 };
 
 Layout make_layout(const gpt2_config* c, int B, int T) {
@@ -126,6 +126,7 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     y.n_partial = np;
     y.partial = take(np);
     y.partial_w = take(gemm_partial_floats());  // split tiles of the weight-gradient stream
+    y.sample = take(3 * BT);                      // sampling requests: rows, coins, tokens
     y.n_scratch = s;
     return y;
 }
@@ -191,7 +192,7 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     g->B = B;
     g->T = T;
     g->have_forward = false;
-    HIPCHK(g, hipMemcpyAsync(tok_in(g), inputs, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
+    if (inputs != tok_in(g)) HIPCHK(g, hipMemcpyAsync(tok_in(g), inputs, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
     if (targets) HIPCHK(g, hipMemcpyAsync(tok_tgt(g), targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(g, hipMemsetAsync(g->buf.grad_scratch, 0, HDR_WORDS * sizeof(float), st));
     HIPCHK(g, encoder_forward(A(g, GPT2_ACT_ENCODED), tok_in(g), P(g, P_WTE), P(g, P_WPE), B, T, C, V, flags(g), st));
@@ -226,6 +227,46 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     *loss_out = targets ? loss : -1.0f;
     g->have_forward = true;
     g->have_targets = targets != nullptr;
+    return GPT2_OK;
+}
+
+// Samples n next tokens from the last forward's logits (host arrays in and out).
+int sample_impl(gpt2* g, const int32_t* rows, const float* coins, int n, int32_t* tokens) {
+    if (n == 0) return GPT2_OK;
+    if (n < 0 || !rows || !coins || !tokens) return GPT2_EINVAL;
+    if (!g->have_forward) return GPT2_ESTATE;
+    const long BT = (long)g->B * g->T;
+    if (n > BT) return GPT2_EINVAL;
+    for (int i = 0; i < n; i++)
+        if (rows[i] < 0 || rows[i] >= BT || !(coins[i] >= 0.0f && coins[i] < 1.0f)) return GPT2_EINVAL;
+    hipStream_t st = g->st;
+    int32_t* drows = reinterpret_cast<int32_t*>(S(g, g->lay.sample));
+    float* dcoins = S(g, g->lay.sample) + BT;
+    int32_t* dtok = reinterpret_cast<int32_t*>(S(g, g->lay.sample) + 2 * BT);
+    HIPCHK(g, hipMemcpyAsync(drows, rows, (size_t)n * 4, hipMemcpyHostToDevice, st));
+    HIPCHK(g, hipMemcpyAsync(dcoins, coins, (size_t)n * 4, hipMemcpyHostToDevice, st));
+    HIPCHK(g, sample_tokens(A(g, GPT2_ACT_LOGITS), (long)g->lay.Vp, A(g, GPT2_ACT_LOGITS_LSE), drows, dcoins, n,
+                            g->cfg.vocab_size, dtok, st));
+    HIPCHK(g, hipMemcpyAsync(tokens, dtok, (size_t)n * 4, hipMemcpyDeviceToHost, st));
+    HIPCHK(g, hipStreamSynchronize(st));
+    return GPT2_OK;
+}
+
+// The pages' generation loop: for t = prompt_len .. total_len-1, run the forward over
+// tokens[0..t) as one row and sample tokens[t] from the logits at position t-1.
+int generate_impl(gpt2* g, int32_t* tokens, int prompt_len, int total_len, const float* coins) {
+    if (!tokens || !coins || prompt_len < 1 || total_len <= prompt_len || total_len > g->cfg.max_seq_len ||
+        (long)(total_len - 1) > (long)g->maxB * g->maxT)
+        return GPT2_EINVAL;
+    for (int t = prompt_len; t < total_len; t++) {
+        HIPCHK(g, hipMemcpyAsync(tok_in(g), tokens, (size_t)t * 4, hipMemcpyHostToDevice, g->st));
+        float loss;
+        const int rc = forward_impl(g, tok_in(g), nullptr, 1, t, &loss);
+        if (rc != GPT2_OK) return rc;
+        const int32_t row = t - 1;
+        const int rs = sample_impl(g, &row, coins + (t - prompt_len), 1, tokens + t);
+        if (rs != GPT2_OK) return rs;
+    }
     return GPT2_OK;
 }
 
@@ -537,6 +578,22 @@ int gpt2_layernorm_forward(float* y, float* mean, float* rstd, const float* x, c
     if (!aligned(y) || !aligned(x) || !aligned(w) || !aligned(b)) return GPT2_EINVAL;
     return layernorm_forward(y, mean, rstd, x, w, b, N, C, eps, (hipStream_t)stream) == hipSuccess ? GPT2_OK
                                                                                                       : GPT2_EDEVICE;
+}
+
+int gpt2_sample(gpt2* g, const int32_t* rows, const float* coins, int n, int32_t* tokens) {
+    if (!g) return GPT2_EINVAL;
+    g->last_error = GPT2_OK;
+    ProfBind bind(g);
+    const int rc = sample_impl(g, rows, coins, n, tokens);
+    return rc == GPT2_OK ? GPT2_OK : fail(g, rc);
+}
+
+int gpt2_generate(gpt2* g, int32_t* tokens, int prompt_len, int total_len, const float* coins) {
+    if (!g) return GPT2_EINVAL;
+    g->last_error = GPT2_OK;
+    ProfBind bind(g);
+    const int rc = generate_impl(g, tokens, prompt_len, total_len, coins);
+    return rc == GPT2_OK ? GPT2_OK : fail(g, rc);
 }
 
 int gpt2_set_backward_streams(gpt2* g, int streams) {

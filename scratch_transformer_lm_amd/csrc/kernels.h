@@ -91,6 +91,11 @@ hipError_t lse_xent_forward(const float* logits, long ld, float* lse, float* los
                             int N, int V, int* flags, hipStream_t st);
 // Mean of losses[0..N) in double, written as float to *out.
 hipError_t loss_mean(float* out, const float* losses, int N, hipStream_t st);
+// tokens[i] = the sampled next token at logits row rows[i] for coins[i] in [0,1):
+// the smallest j with coin < sum_{k<=j} exp(z_k - lse[row]) (V-1 if none).  Device
+// arrays; rows must be valid rows of the last forward.
+hipError_t sample_tokens(const float* logits, long ld, const float* lse, const int32_t* rows, const float* coins,
+                         int n, int V, int32_t* tokens, hipStream_t st);
 
 // ---- optimizer and fills (adamw.hip) ------------------------------------------------
 hipError_t adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float b1,

@@ -95,6 +95,62 @@ __global__ __launch_bounds__(256) void loss_mean_kernel(float* out, const float*
     if (threadIdx.x == 0) *out = (float)(sm[0] / (double)N);
 }
 
+// Next-token sampling (the pages' sample_mult: huxiu page "llm.c：Andrej Karpathy带你从零复现
+// LLM", 核心代码解读 item 5): the token is the smallest index j whose cumulative
+// probability sum_{k<=j} p_k exceeds the coin (the last index when rounding leaves the
+// total below it).  One 1024-thread block per request: p_k = exp(z_k - lse) in fp32
+// from the stored log-sum-exp; each thread sums a contiguous chunk in fp64, a block scan
+// gives every chunk its starting cumulative sum, and the thread whose range holds the
+// coin walks its chunk.  The decision is taken on fp64 sums of the fp32 probabilities,
+// so it does not depend on the chunking beyond ~1e-16.
+constexpr int SAMPLE_THREADS = 1024;
+
+__global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __restrict__ logits, long ld,
+                                                                const float* __restrict__ lse,
+                                                                const int32_t* __restrict__ rows,
+                                                                const float* __restrict__ coins, int V,
+                                                                int32_t* __restrict__ tokens) {
+    __shared__ double part[SAMPLE_THREADS];
+    const int t = threadIdx.x;
+    const long row = rows[blockIdx.x];
+    const double coin = coins[blockIdx.x];
+    const float* z = logits + row * ld;
+    const float L = lse[row];
+    const int chunk = (V + SAMPLE_THREADS - 1) / SAMPLE_THREADS;
+    const int j0 = min(V, t * chunk), j1 = min(V, j0 + chunk);
+    double s = 0.0;
+    for (int j = j0; j < j1; j++) s += (double)expf(z[j] - L);
+    // inclusive scan of the chunk sums (fixed order: Hillis-Steele over the block)
+    part[t] = s;
+    __syncthreads();
+    for (int off = 1; off < SAMPLE_THREADS; off <<= 1) {
+        const double add = t >= off ? part[t - off] : 0.0;
+        __syncthreads();
+        part[t] += add;
+        __syncthreads();
+    }
+    // chunk t covers [part[t-1], part[t]): consecutive ranges share their bounds exactly
+    const double hi = part[t], lo = t > 0 ? part[t - 1] : 0.0;
+    const double total = part[SAMPLE_THREADS - 1];
+    if (coin >= total) {
+        if (t == 0) tokens[blockIdx.x] = V - 1;
+        return;
+    }
+    if (lo <= coin && coin < hi) {
+        // exactly one thread's [lo, hi) holds the coin
+        double c = lo;
+        int pick = j1 - 1;
+        for (int j = j0; j < j1; j++) {
+            c += (double)expf(z[j] - L);
+            if (coin < c) {
+                pick = j;
+                break;
+            }
+        }
+        tokens[blockIdx.x] = pick;
+    }
+}
+
 }  // namespace
 
 hipError_t lse_xent_forward(const float* logits, long ld, float* lse, float* losses, const int32_t* targets,
@@ -103,6 +159,14 @@ hipError_t lse_xent_forward(const float* logits, long ld, float* lse, float* los
     if (N == 0) return hipSuccess;
     ProfScope ps(st, "lse_xent_kernel", 0.0, 4.0 * ((double)N * V + 2.0 * N));
     hipLaunchKernelGGL(lse_xent_kernel, dim3(N), dim3(SX_THREADS), 0, st, logits, ld, lse, losses, targets, V, flags);
+    return hipGetLastError();
+}
+
+hipError_t sample_tokens(const float* logits, long ld, const float* lse, const int32_t* rows, const float* coins,
+                         int n, int V, int32_t* tokens, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    ProfScope ps(st, "sample_kernel", 0.0, 4.0 * n * ((double)V + 3));
+    hipLaunchKernelGGL(sample_kernel, dim3(n), dim3(SAMPLE_THREADS), 0, st, logits, ld, lse, rows, coins, V, tokens);
     return hipGetLastError();
 }
 

@@ -93,6 +93,10 @@ def load() -> ct.CDLL:
                                        ct.POINTER(ct.c_double), ct.POINTER(ct.c_double),
                                        ct.POINTER(ct.c_double)]
     lib.gpt2_profile_entry.restype = i
+    lib.gpt2_sample.argtypes = [P, P, P, i, P]
+    lib.gpt2_sample.restype = i
+    lib.gpt2_generate.argtypes = [P, P, i, i, P]
+    lib.gpt2_generate.restype = i
     lib.gpt2_set_backward_streams.argtypes = [P, i]
     lib.gpt2_set_backward_streams.restype = i
     lib.gpt2_set_gemm_tiles.argtypes = [i]
@@ -207,6 +211,29 @@ class GPT2:
 
     def last_error(self) -> int:
         return self.lib.gpt2_last_error(self.h)
+
+    def sample(self, rows, coins) -> np.ndarray:
+        """gpt2_sample: next tokens at logits rows `rows` of the last forward for `coins` in [0,1)."""
+        r = np.ascontiguousarray(rows, dtype=np.int32)
+        c = np.ascontiguousarray(coins, dtype=np.float32)
+        assert r.shape == c.shape and r.ndim == 1
+        out = np.zeros(r.shape, dtype=np.int32)
+        rc = self.lib.gpt2_sample(self.h, r.ctypes.data, c.ctypes.data, len(r), out.ctypes.data)
+        if rc != GPT2_OK:
+            raise GPT2Error(rc, "gpt2_sample")
+        return out
+
+    def generate(self, prompt, total_len: int, coins) -> np.ndarray:
+        """gpt2_generate: extends `prompt` to `total_len` tokens, one coin per new token."""
+        p = np.ascontiguousarray(prompt, dtype=np.int32).reshape(-1)
+        c = np.ascontiguousarray(coins, dtype=np.float32).reshape(-1)
+        assert len(c) >= total_len - len(p)
+        toks = np.zeros(total_len, dtype=np.int32)
+        toks[:len(p)] = p
+        rc = self.lib.gpt2_generate(self.h, toks.ctypes.data, len(p), total_len, c.ctypes.data)
+        if rc != GPT2_OK:
+            raise GPT2Error(rc, "gpt2_generate")
+        return toks
 
     def set_backward_streams(self, streams: int) -> None:
         """gpt2_set_backward_streams: 2 overlaps the weight gradients with the main chain."""

@@ -92,3 +92,9 @@ def test_backward_streams_argument_checks():
     lib = G.load()
     assert lib.gpt2_set_backward_streams(None, 2) == G.GPT2_EINVAL
     assert lib.gpt2_set_backward_streams(None, 1) == G.GPT2_EINVAL
+
+
+def test_sampling_argument_checks_need_no_gpu():
+    lib = G.load()
+    assert lib.gpt2_sample(None, None, None, 1, None) == G.GPT2_EINVAL
+    assert lib.gpt2_generate(None, None, 1, 2, None) == G.GPT2_EINVAL

@@ -207,6 +207,91 @@ def test_backward_stream_schedules_agree_bitwise(G):
     assert np.array_equal(p2, p1)
 
 
+# ------------------------------------------------------------------ sampling (sample_mult)
+
+SAMPLE_SLACK = 2e-6  # coin distance from a cumulative boundary within which either side may differ
+
+
+def sample_valid(probs, coin, token):
+    """`token` is the oracle's sample_mult pick, or a neighbour the coin is within
+    SAMPLE_SLACK of (the GPU forms fp32 probabilities; the oracle's are float64)."""
+    from oracle import oracle as O
+    if token == O.sample_mult(probs, coin):
+        return True
+    cdf = np.cumsum(np.asarray(probs, dtype=np.float64))
+    lo = cdf[token - 1] if token > 0 else 0.0
+    return 0 <= token < len(probs) and lo - SAMPLE_SLACK <= coin < cdf[token] + SAMPLE_SLACK
+
+
+def test_sample_matches_oracle(G):
+    """gpt2_sample over a no-target forward at the 124M shape (V = 50257, B=4, T=64):
+    rows spread over the batch, seeded coins plus the edges 0 and just below 1."""
+    from oracle import oracle as O
+    w = S.GPT2_124M_SHORT
+    say("[sample]")
+    params = S.init_params(w.model)
+    x, _ = S.tokens(w)
+    m = G.GPT2(w.model, w.B, w.T)
+    m.params.copy_(dev(params))
+    assert m.forward(dev(x, torch.int32), None) == -1.0
+    rng = np.random.default_rng(21)
+    rows = np.concatenate([[0, w.B * w.T - 1, 63, 64], rng.integers(0, w.B * w.T, 28)]).astype(np.int32)
+    coins = np.concatenate([[0.0, 0.9999999, 0.5, 0.25], rng.random(28)]).astype(np.float32)
+    toks = m.sample(rows, coins)
+    o = O.OracleGPT2(w.model, w.B, w.T, params)
+    assert o.forward(x, None) < 0
+    probs = o.activation("probs").reshape(w.B * w.T, -1)
+    exact = 0
+    for r, c, t in zip(rows, coins, toks):
+        assert sample_valid(probs[r], float(c), int(t)), (r, c, t, O.sample_mult(probs[r], float(c)))
+        exact += int(t) == O.sample_mult(probs[r], float(c))
+    say(f"sampled {len(rows)} rows, {exact} identical to the oracle's picks")
+    assert exact >= len(rows) - 1
+    # error paths: coin 1.0, row outside the forward, more requests than rows
+    with pytest.raises(G.GPT2Error):
+        m.sample([0], [1.0])
+    with pytest.raises(G.GPT2Error):
+        m.sample([w.B * w.T], [0.5])
+    with pytest.raises(G.GPT2Error):
+        m.sample(np.zeros(w.B * w.T + 1, np.int32), np.zeros(w.B * w.T + 1, np.float32))
+
+
+def test_sample_needs_a_forward(G):
+    w = S.TINY
+    m = G.GPT2(w.model, w.B, w.T)
+    with pytest.raises(G.GPT2Error) as e:
+        m.sample([0], [0.5])
+    assert e.value.code == G.GPT2_ESTATE
+
+
+def test_generate_matches_oracle(G):
+    """gpt2_generate on the tiny model from the end-of-text token (V-1): every generated
+    token is checked against the oracle run on the GPU's own prefix, so one boundary
+    coin cannot derail the rest of the comparison."""
+    from oracle import oracle as O
+    w = S.TINY
+    say("[generate]")
+    params = S.init_params(w.model)
+    V = w.model.vocab_size
+    total = 40
+    coins = np.random.default_rng(33).random(total).astype(np.float32)
+    m = G.GPT2(w.model, w.B, w.T)
+    m.params.copy_(dev(params))
+    toks = m.generate([V - 1], total, coins)
+    assert toks[0] == V - 1 and np.all((toks >= 0) & (toks < V))
+    o = O.OracleGPT2(w.model, 1, total - 1, params)
+    exact = 0
+    for t in range(1, total):
+        o.forward(toks[None, :t], None)
+        p = o.activation("probs").reshape(1 * t, -1)[t - 1]
+        assert sample_valid(p, float(coins[t - 1]), int(toks[t])), t
+        exact += int(toks[t]) == O.sample_mult(p, float(coins[t - 1]))
+    say(f"generated {total - 1} tokens, {exact} identical to the oracle's picks")
+    assert exact >= total - 2
+    with pytest.raises(G.GPT2Error):
+        m.generate([V - 1], w.model.max_seq_len + 1, np.zeros(w.model.max_seq_len + 1))
+
+
 def test_smaller_batch_than_built(G):
     w = S.TINY
     say("[smaller batch]")

@@ -448,3 +448,33 @@ def test_key_bias_gradient_vanishes():
     g = m.tensor(m.grads, "qkvb").reshape(L, 3, C)
     assert np.abs(g[:, 1]).max() <= 1e-15 * np.abs(g).max()
     assert np.abs(g[:, 0]).max() > 1e-6 and np.abs(g[:, 2]).max() > 1e-6
+
+
+# ------------------------------------------------------------------ sample_mult
+
+def test_sample_mult_closed_forms():
+    """sample_mult (huxiu page, 核心代码解读 item 5) pinned by distributions whose answer is
+    known without accumulating: a uniform distribution over n picks floor(coin * n); a
+    one-hot distribution always picks its index; zero-probability entries are never
+    picked; the comparison is strict; a total below the coin falls to the last index."""
+    n = 7
+    for k in range(n):
+        assert O.sample_mult(np.full(n, 1.0 / n), (k + 0.5) / n) == k
+    assert O.sample_mult(np.full(n, 1.0 / n), 0.0) == 0
+    for c in (0.0, 0.3, 0.999999):
+        assert O.sample_mult(np.eye(9)[4], c) == 4
+    p = np.array([0.0, 0.25, 0.0, 0.5, 0.25])
+    assert [O.sample_mult(p, c) for c in (0.0, 0.1, 0.25, 0.3, 0.74, 0.75, 0.99)] == [1, 1, 3, 3, 3, 4, 4]
+    assert O.sample_mult(np.array([0.5, 0.4999]), 0.99995) == 1
+    assert O.sample_mult(np.array([0.5, 0.4999, 0.0]), 0.99995) == 2
+
+
+def test_sample_mult_frequencies():
+    """Drawing many coins reproduces the distribution: every index's frequency lies
+    within 5 standard deviations of its probability."""
+    rng = np.random.default_rng(5)
+    p = rng.dirichlet(np.ones(10))
+    coins = rng.random(20000)
+    counts = np.bincount([O.sample_mult(p, c) for c in coins], minlength=10)
+    sd = np.sqrt(len(coins) * p * (1 - p))
+    assert np.all(np.abs(counts - len(coins) * p) <= 5 * sd + 1), (counts, len(coins) * p)
