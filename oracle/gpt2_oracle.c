@@ -42,12 +42,18 @@ typedef float real;
 #define R_SQRT sqrtf
 #define R_TANH tanhf
 #define R_POW powf
+#define R_COS cosf
+#define R_SIN sinf
+#define R_POW powf
 #else
 typedef double real;
 #define R_EXP exp
 #define R_LOG log
 #define R_SQRT sqrt
 #define R_TANH tanh
+#define R_POW pow
+#define R_COS cos
+#define R_SIN sin
 #define R_POW pow
 #endif
 
@@ -91,8 +97,11 @@ EXPORT void oracle_encoder_forward(real* out, const int32_t* tok, const real* wt
         for (int t = 0; t < T; t++) {
             real* o = out + ((size_t)b * T + t) * C;
             const real* we = wte + (size_t)tok[b * T + t] * C;
-            const real* pe = wpe + (size_t)t * C;
-            for (int c = 0; c < C; c++) o[c] = we[c] + pe[c];
+            for (int c = 0; c < C; c++) o[c] = we[c];
+            if (wpe) {  /* NULL: no position rows (the rotary variant) */
+                const real* pe = wpe + (size_t)t * C;
+                for (int c = 0; c < C; c++) o[c] += pe[c];
+            }
         }
 }
 
@@ -106,7 +115,7 @@ EXPORT void oracle_encoder_backward(real* dwte, real* dwpe, const real* dout,
             for (int t = 0; t < T; t++) {
                 real d = dout[((size_t)b * T + t) * C + c];
                 dwte[(size_t)tok[b * T + t] * C + c] += d;
-                dwpe[(size_t)t * C + c] += d;
+                if (dwpe) dwpe[(size_t)t * C + c] += d;
             }
 }
 
@@ -177,6 +186,97 @@ EXPORT void oracle_layernorm_backward(real* dinp, real* dw, real* db, const real
         dw[c] += sw;
         db[c] += sb;
     }
+}
+
+/* RMSNorm, the normalisation of the Llama-style layers the pages name as other model
+ * families (新智元 article, 纯CUDA也可训; lianzai README, 项目简介): no mean subtraction
+ * and no bias; r = 1/sqrt(mean(x^2) + eps), y = x * r * w.  The pages give no formula:
+ * this is the published RMSNorm (Zhang & Sennrich, 2019), with eps = 1e-5 like the
+ * LayerNorm here.  r is kept for the backward. */
+EXPORT void oracle_rmsnorm_forward(real* out, real* rstd, const real* inp, const real* w,
+                                   int N, int C, real eps) {
+#pragma omp parallel for
+    for (int i = 0; i < N; i++) {
+        const real* x = inp + (size_t)i * C;
+        real ms = 0;
+        for (int c = 0; c < C; c++) ms += x[c] * x[c];
+        ms = ms / C;
+        real s = (real)1 / R_SQRT(ms + eps);
+        real* y = out + (size_t)i * C;
+        for (int c = 0; c < C; c++) y[c] = x[c] * s * w[c];
+        rstd[i] = s;
+    }
+}
+
+/* RMSNorm backward, by hand from the forward: with xh = x*r and g = w*dy,
+ * dr/dx_j = -r^3 x_j / C gives dx += r * (g - xh * mean(g*xh)); dw += sum_rows dy*xh. */
+EXPORT void oracle_rmsnorm_backward(real* dinp, real* dw, const real* dout, const real* inp,
+                                    const real* w, const real* rstd, int N, int C) {
+#pragma omp parallel for
+    for (int i = 0; i < N; i++) {
+        const real* x = inp + (size_t)i * C;
+        const real* dy = dout + (size_t)i * C;
+        real s = rstd[i];
+        real gxmean = 0;
+        for (int c = 0; c < C; c++) gxmean += w[c] * dy[c] * x[c] * s;
+        gxmean = gxmean / C;
+        real* dx = dinp + (size_t)i * C;
+        for (int c = 0; c < C; c++) dx[c] += s * (w[c] * dy[c] - x[c] * s * gxmean);
+    }
+#pragma omp parallel for
+    for (int c = 0; c < C; c++) {
+        real sw = 0;
+        for (int i = 0; i < N; i++) sw += dout[(size_t)i * C + c] * inp[(size_t)i * C + c] * rstd[i];
+        dw[c] += sw;
+    }
+}
+
+/* Rotary position embedding, the positional encoding of the same Llama-style layers (the
+ * pages name it as a variant, not its formula): the published RoPE (Su et al., 2021).
+ * In every head of q and k, dimension pair (2i, 2i+1) at position t (restarting at 0 in
+ * every row) is rotated by the angle t * 10000^(-2i/hs):
+ *   q'[2i] = q[2i] cos - q[2i+1] sin,  q'[2i+1] = q[2i] sin + q[2i+1] cos;  v is copied.
+ * inp and out are (B, T, 3C) with q, k, v the column blocks. */
+EXPORT void oracle_rope_forward(real* out, const real* inp, int B, int T, int C, int NH) {
+    int hs = C / NH;
+#pragma omp parallel for collapse(2)
+    for (int b = 0; b < B; b++)
+        for (int t = 0; t < T; t++) {
+            const real* x = inp + ((size_t)b * T + t) * 3 * C;
+            real* y = out + ((size_t)b * T + t) * 3 * C;
+            for (int c = 0; c < 3 * C; c++) y[c] = x[c];
+            for (int part = 0; part < 2; part++)
+                for (int h = 0; h < NH; h++)
+                    for (int i = 0; i < hs / 2; i++) {
+                        real ang = (real)t * R_POW((real)10000, -(real)(2 * i) / (real)hs);
+                        real cs = R_COS(ang), sn = R_SIN(ang);
+                        size_t o = (size_t)part * C + (size_t)h * hs + 2 * i;
+                        y[o] = x[o] * cs - x[o + 1] * sn;
+                        y[o + 1] = x[o] * sn + x[o + 1] * cs;
+                    }
+        }
+}
+
+/* Backward: a rotation's transpose is the rotation by the opposite angle, so
+ * dinp += R(-angle) dout on q and k, and dinp += dout on v. */
+EXPORT void oracle_rope_backward(real* dinp, const real* dout, int B, int T, int C, int NH) {
+    int hs = C / NH;
+#pragma omp parallel for collapse(2)
+    for (int b = 0; b < B; b++)
+        for (int t = 0; t < T; t++) {
+            const real* d = dout + ((size_t)b * T + t) * 3 * C;
+            real* dx = dinp + ((size_t)b * T + t) * 3 * C;
+            for (int c = 2 * C; c < 3 * C; c++) dx[c] += d[c];
+            for (int part = 0; part < 2; part++)
+                for (int h = 0; h < NH; h++)
+                    for (int i = 0; i < hs / 2; i++) {
+                        real ang = (real)t * R_POW((real)10000, -(real)(2 * i) / (real)hs);
+                        real cs = R_COS(ang), sn = R_SIN(ang);
+                        size_t o = (size_t)part * C + (size_t)h * hs + 2 * i;
+                        dx[o] += d[o] * cs + d[o + 1] * sn;
+                        dx[o + 1] += -d[o] * sn + d[o + 1] * cs;
+                    }
+        }
 }
 
 /* Linear layer: out[r,o] = bias[o] + sum_{i=0..IC-1} inp[r,i] * w[o,i], with w stored
@@ -594,7 +694,16 @@ typedef struct oracle_gpt2 {
     int have_forward;
     real mean_loss;
     int last_error;
+    int variant;         /* ORACLE_VARIANT_* bits */
+    real* qkvr;          /* rotary variant: q and k rotated, per layer (L, B, T, 3C) */
+    real* dqkvr;
 } oracle_gpt2;
+
+/* Llama-style layer variants: RMSNorm in place of every LayerNorm (the
+ * LayerNorm biases then take no part and keep zero gradients), and rotary position
+ * embedding on q and k in place of the position rows (wpe then takes no part). */
+#define ORACLE_VARIANT_RMSNORM 1
+#define ORACLE_VARIANT_ROPE 2
 
 static void carve(oracle_gpt2* g, int B, int T) {
     size_t len[NACT];
@@ -622,14 +731,17 @@ static int ensure_dacts(oracle_gpt2* g) {
  * v zeroed here), allocate the activation block once.  grads, m and v may all be NULL
  * for a forward-only model; the activation-gradient block is allocated on the first
  * zero_grad or backward. */
-EXPORT int oracle_gpt2_build(oracle_gpt2** out, const oracle_config* cfg, int B, int T,
-                             real* params, real* grads, real* m, real* v) {
+EXPORT int oracle_gpt2_build_variant(oracle_gpt2** out, const oracle_config* cfg, int B, int T,
+                                     real* params, real* grads, real* m, real* v, int variant) {
     if (!out || !config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !params)
         return O_EINVAL;
+    if (variant & ~(ORACLE_VARIANT_RMSNORM | ORACLE_VARIANT_ROPE)) return O_EINVAL;
+    if ((variant & ORACLE_VARIANT_ROPE) && (cfg->channels / cfg->num_heads) % 2) return O_EINVAL;
     if ((grads || m || v) && !(grads && m && v)) return O_EINVAL;
     oracle_gpt2* g = (oracle_gpt2*)calloc(1, sizeof(oracle_gpt2));
     if (!g) return O_ENOMEM;
     g->cfg = *cfg;
+    g->variant = variant;
     g->maxB = B;
     g->maxT = T;
     g->params = params;
@@ -652,11 +764,18 @@ EXPORT int oracle_gpt2_build(oracle_gpt2** out, const oracle_config* cfg, int B,
     g->acts = (real*)calloc(g->num_acts, sizeof(real));
     g->inputs = (int32_t*)calloc((size_t)B * T, sizeof(int32_t));
     g->targets = (int32_t*)calloc((size_t)B * T, sizeof(int32_t));
-    if (!g->acts || !g->inputs || !g->targets) {
+    if (variant & ORACLE_VARIANT_ROPE) {
+        size_t n = (size_t)cfg->num_layers * B * T * 3 * cfg->channels;
+        g->qkvr = (real*)calloc(n, sizeof(real));
+        g->dqkvr = (real*)calloc(n, sizeof(real));
+    }
+    if (!g->acts || !g->inputs || !g->targets || ((variant & ORACLE_VARIANT_ROPE) && (!g->qkvr || !g->dqkvr))) {
         free(g->acts);
         free(g->dacts);
         free(g->inputs);
         free(g->targets);
+        free(g->qkvr);
+        free(g->dqkvr);
         free(g);
         return O_ENOMEM;
     }
@@ -665,8 +784,15 @@ EXPORT int oracle_gpt2_build(oracle_gpt2** out, const oracle_config* cfg, int B,
     return O_OK;
 }
 
+EXPORT int oracle_gpt2_build(oracle_gpt2** out, const oracle_config* cfg, int B, int T,
+                             real* params, real* grads, real* m, real* v) {
+    return oracle_gpt2_build_variant(out, cfg, B, T, params, grads, m, v, 0);
+}
+
 EXPORT void oracle_gpt2_free(oracle_gpt2* g) {
     if (!g) return;
+    free(g->qkvr);
+    free(g->dqkvr);
     free(g->acts);
     free(g->dacts);
     free(g->inputs);
@@ -675,6 +801,24 @@ EXPORT void oracle_gpt2_free(oracle_gpt2* g) {
 }
 
 EXPORT int oracle_gpt2_last_error(const oracle_gpt2* g) { return g ? g->last_error : O_EINVAL; }
+
+/* The block's normalisation: LayerNorm, or RMSNorm in the RMSNorm variant (whose mean
+ * slot then holds 0 and whose bias takes no part). */
+static void norm_forward(int rms, real* out, real* mean, real* rstd, const real* x, const real* w,
+                         const real* b, int N, int C) {
+    if (rms) {
+        oracle_rmsnorm_forward(out, rstd, x, w, N, C, (real)1e-5);
+        for (int i = 0; i < N; i++) mean[i] = 0;
+    } else {
+        oracle_layernorm_forward(out, mean, rstd, x, w, b, N, C, (real)1e-5);
+    }
+}
+
+static void norm_backward(int rms, real* dx, real* dw, real* db, const real* dy, const real* x, const real* w,
+                          const real* mean, const real* rstd, int N, int C) {
+    if (rms) oracle_rmsnorm_backward(dx, dw, dy, x, w, rstd, N, C);
+    else oracle_layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, N, C);
+}
 
 /* Forward: GPT-2 pre-LN blocks,
  *   x = x + attproj(attention(qkv(ln1(x))));  x = x + fcproj(gelu(fc(ln2(x)))),
@@ -707,7 +851,8 @@ EXPORT double oracle_gpt2_forward(oracle_gpt2* g, const int32_t* inputs, const i
     real** A = g->a;
     size_t BT = (size_t)B * T;
     size_t att_l = (size_t)B * NH * T * T;
-    oracle_encoder_forward(A[A_ENCODED], inputs, P[0], P[1], B, T, C);
+    const int rms = g->variant & ORACLE_VARIANT_RMSNORM, rope = g->variant & ORACLE_VARIANT_ROPE;
+    oracle_encoder_forward(A[A_ENCODED], inputs, P[0], rope ? NULL : P[1], B, T, C);
     for (int l = 0; l < L; l++) {
         real* residual = l == 0 ? A[A_ENCODED] : A[A_RESIDUAL3] + (size_t)(l - 1) * BT * C;
         real* ln1 = A[A_LN1] + l * BT * C;
@@ -726,19 +871,24 @@ EXPORT double oracle_gpt2_forward(oracle_gpt2* g, const int32_t* inputs, const i
         real* fchg = A[A_FCH_GELU] + l * BT * 4 * C;
         real* fcproj = A[A_FCPROJ] + l * BT * C;
         real* res3 = A[A_RESIDUAL3] + l * BT * C;
-        oracle_layernorm_forward(ln1, ln1m, ln1r, residual, P[2] + l * C, P[3] + l * C, (int)BT, C, (real)1e-5);
+        norm_forward(rms, ln1, ln1m, ln1r, residual, P[2] + l * C, P[3] + l * C, (int)BT, C);
         oracle_matmul_forward(qkv, ln1, P[4] + (size_t)l * 3 * C * C, P[5] + l * 3 * C, (int)BT, C, 3 * C);
-        oracle_attention_forward(atty, preatt, att, qkv, B, T, C, NH);
+        real* qkv_in = qkv;
+        if (rope) {
+            qkv_in = g->qkvr + (size_t)l * BT * 3 * C;
+            oracle_rope_forward(qkv_in, qkv, B, T, C, NH);
+        }
+        oracle_attention_forward(atty, preatt, att, qkv_in, B, T, C, NH);
         oracle_matmul_forward(attproj, atty, P[6] + (size_t)l * C * C, P[7] + l * C, (int)BT, C, C);
         oracle_residual_forward(res2, residual, attproj, BT * C);
-        oracle_layernorm_forward(ln2, ln2m, ln2r, res2, P[8] + l * C, P[9] + l * C, (int)BT, C, (real)1e-5);
+        norm_forward(rms, ln2, ln2m, ln2r, res2, P[8] + l * C, P[9] + l * C, (int)BT, C);
         oracle_matmul_forward(fch, ln2, P[10] + (size_t)l * 4 * C * C, P[11] + l * 4 * C, (int)BT, C, 4 * C);
         oracle_gelu_forward(fchg, fch, BT * 4 * C);
         oracle_matmul_forward(fcproj, fchg, P[12] + (size_t)l * 4 * C * C, P[13] + l * C, (int)BT, 4 * C, C);
         oracle_residual_forward(res3, res2, fcproj, BT * C);
     }
     real* last = A[A_RESIDUAL3] + (size_t)(L - 1) * BT * C;
-    oracle_layernorm_forward(A[A_LNF], A[A_LNF_MEAN], A[A_LNF_RSTD], last, P[14], P[15], (int)BT, C, (real)1e-5);
+    norm_forward(rms, A[A_LNF], A[A_LNF_MEAN], A[A_LNF_RSTD], last, P[14], P[15], (int)BT, C);
     oracle_matmul_forward(A[A_LOGITS], A[A_LNF], P[0], NULL, (int)BT, C, V);
     oracle_softmax_forward(A[A_PROBS], A[A_LOGITS], (int)BT, V);
     g->have_forward = 1;
@@ -787,13 +937,15 @@ EXPORT int oracle_gpt2_backward(oracle_gpt2* g) {
     real** A = g->a;
     real** D = g->da;
     memset(g->dacts, 0, g->num_acts * sizeof(real));
+    const int rms = g->variant & ORACLE_VARIANT_RMSNORM, rope = g->variant & ORACLE_VARIANT_ROPE;
+    if (rope) memset(g->dqkvr, 0, (size_t)L * BT * 3 * C * sizeof(real));
     real dl = (real)1 / (real)BT;
     for (size_t i = 0; i < BT; i++) D[A_LOSSES][i] = dl;
     oracle_crossentropy_softmax_backward(D[A_LOGITS], D[A_LOSSES], A[A_PROBS], g->targets, (int)BT, V);
     oracle_matmul_backward(D[A_LNF], G[0], NULL, D[A_LOGITS], A[A_LNF], P[0], (int)BT, C, V);
     real* last = A[A_RESIDUAL3] + (size_t)(L - 1) * BT * C;
     real* dlast = D[A_RESIDUAL3] + (size_t)(L - 1) * BT * C;
-    oracle_layernorm_backward(dlast, G[14], G[15], D[A_LNF], last, P[14], A[A_LNF_MEAN], A[A_LNF_RSTD], (int)BT, C);
+    norm_backward(rms, dlast, G[14], G[15], D[A_LNF], last, P[14], A[A_LNF_MEAN], A[A_LNF_RSTD], (int)BT, C);
     for (int l = L - 1; l >= 0; l--) {
         real* residual = l == 0 ? A[A_ENCODED] : A[A_RESIDUAL3] + (size_t)(l - 1) * BT * C;
         real* dresidual = l == 0 ? D[A_ENCODED] : D[A_RESIDUAL3] + (size_t)(l - 1) * BT * C;
@@ -807,23 +959,28 @@ EXPORT int oracle_gpt2_backward(oracle_gpt2* g) {
         oracle_matmul_backward(D[A_LN2] + o1, G[10] + (size_t)l * 4 * C * C, G[11] + l * 4 * C,
                                D[A_FCH] + o4, A[A_LN2] + o1, P[10] + (size_t)l * 4 * C * C,
                                (int)BT, C, 4 * C);
-        oracle_layernorm_backward(D[A_RESIDUAL2] + o1, G[8] + l * C, G[9] + l * C, D[A_LN2] + o1,
-                                  A[A_RESIDUAL2] + o1, P[8] + l * C, A[A_LN2_MEAN] + os,
-                                  A[A_LN2_RSTD] + os, (int)BT, C);
+        norm_backward(rms, D[A_RESIDUAL2] + o1, G[8] + l * C, G[9] + l * C, D[A_LN2] + o1,
+                      A[A_RESIDUAL2] + o1, P[8] + l * C, A[A_LN2_MEAN] + os, A[A_LN2_RSTD] + os, (int)BT, C);
         /* Attention half, backwards. */
         oracle_residual_backward(dresidual, D[A_ATTPROJ] + o1, D[A_RESIDUAL2] + o1, BT * C);
         oracle_matmul_backward(D[A_ATTY] + o1, G[6] + (size_t)l * C * C, G[7] + l * C,
                                D[A_ATTPROJ] + o1, A[A_ATTY] + o1, P[6] + (size_t)l * C * C,
                                (int)BT, C, C);
-        oracle_attention_backward(D[A_QKV] + o3, D[A_PREATT] + oa, D[A_ATT] + oa, D[A_ATTY] + o1,
-                                  A[A_QKV] + o3, A[A_ATT] + oa, B, T, C, NH);
+        if (rope) {
+            oracle_attention_backward(g->dqkvr + o3, D[A_PREATT] + oa, D[A_ATT] + oa, D[A_ATTY] + o1,
+                                      g->qkvr + o3, A[A_ATT] + oa, B, T, C, NH);
+            oracle_rope_backward(D[A_QKV] + o3, g->dqkvr + o3, B, T, C, NH);
+        } else {
+            oracle_attention_backward(D[A_QKV] + o3, D[A_PREATT] + oa, D[A_ATT] + oa, D[A_ATTY] + o1,
+                                      A[A_QKV] + o3, A[A_ATT] + oa, B, T, C, NH);
+        }
         oracle_matmul_backward(D[A_LN1] + o1, G[4] + (size_t)l * 3 * C * C, G[5] + l * 3 * C,
                                D[A_QKV] + o3, A[A_LN1] + o1, P[4] + (size_t)l * 3 * C * C,
                                (int)BT, C, 3 * C);
-        oracle_layernorm_backward(dresidual, G[2] + l * C, G[3] + l * C, D[A_LN1] + o1, residual,
-                                  P[2] + l * C, A[A_LN1_MEAN] + os, A[A_LN1_RSTD] + os, (int)BT, C);
+        norm_backward(rms, dresidual, G[2] + l * C, G[3] + l * C, D[A_LN1] + o1, residual,
+                      P[2] + l * C, A[A_LN1_MEAN] + os, A[A_LN1_RSTD] + os, (int)BT, C);
     }
-    oracle_encoder_backward(G[0], G[1], D[A_ENCODED], g->inputs, B, T, C);
+    oracle_encoder_backward(G[0], rope ? NULL : G[1], D[A_ENCODED], g->inputs, B, T, C);
     return O_OK;
 }
 
@@ -841,6 +998,12 @@ EXPORT int oracle_gpt2_update(oracle_gpt2* g, real lr, real b1, real b2, real ep
  * of the last forward; *count gets its element count.  grad != 0 selects the
  * activation-gradient block instead. */
 EXPORT real* oracle_gpt2_activation(oracle_gpt2* g, int id, int layer, int grad, size_t* count) {
+    if (g && id == NACT && g->qkvr) {  /* the rotary variant's rotated qkv, per layer */
+        if (layer < 0 || layer >= g->cfg.num_layers) return NULL;
+        size_t n = (size_t)(g->B ? g->B : g->maxB) * (g->T ? g->T : g->maxT) * 3 * g->cfg.channels;
+        if (count) *count = n;
+        return (grad ? g->dqkvr : g->qkvr) + (size_t)layer * n;
+    }
     if (!g || id < 0 || id >= NACT) return NULL;
     size_t len[NACT];
     act_sizes(&g->cfg, g->B ? g->B : g->maxB, g->T ? g->T : g->maxT, len);

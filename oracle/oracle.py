@@ -18,6 +18,8 @@ ACT_NAMES = ("encoded", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "preatt", 
              "residual2", "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "fcproj", "residual3",
              "lnf", "lnf_mean", "lnf_rstd", "logits", "probs", "losses")
 PER_LAYER = set(ACT_NAMES[1:17])
+# Llama-style layer variants (bit mask): RMSNorm for every LayerNorm, rotary q/k positions.
+VARIANT_RMSNORM, VARIANT_ROPE = 1, 2
 
 
 class Config(ct.Structure):
@@ -49,6 +51,7 @@ def load(precision: str = "f64") -> ct.CDLL:
     lib.oracle_gpt2_num_activations.argtypes = [ct.POINTER(Config), i, i]
     lib.oracle_gpt2_num_activations.restype = sz
     lib.oracle_gpt2_build.argtypes = [ct.POINTER(P), ct.POINTER(Config), i, i, P, P, P, P]
+    lib.oracle_gpt2_build_variant.argtypes = [ct.POINTER(P), ct.POINTER(Config), i, i, P, P, P, P, i]
     lib.oracle_gpt2_build.restype = i
     lib.oracle_gpt2_free.argtypes = [P]
     lib.oracle_gpt2_last_error.argtypes = [P]
@@ -77,6 +80,10 @@ def load(precision: str = "f64") -> ct.CDLL:
     lib.oracle_residual_backward.argtypes = [P, P, P, sz]
     lib.oracle_softmax_forward.argtypes = [P, P, i, i]
     lib.oracle_sample_mult.argtypes = [P, i, real]
+    lib.oracle_rmsnorm_forward.argtypes = [P, P, P, P, i, i, real]
+    lib.oracle_rmsnorm_backward.argtypes = [P, P, P, P, P, P, i, i]
+    lib.oracle_rope_forward.argtypes = [P, P, i, i, i, i]
+    lib.oracle_rope_backward.argtypes = [P, P, i, i, i, i]
     lib.oracle_sample_mult.restype = i
     lib.oracle_crossentropy_forward.argtypes = [P, P, P, i, i]
     lib.oracle_crossentropy_softmax_backward.argtypes = [P, P, P, P, i, i]
@@ -130,7 +137,7 @@ class OracleGPT2:
     """The oracle model: owns numpy params/grads/m/v in the oracle's precision."""
 
     def __init__(self, shape, B: int, T: int, params: np.ndarray, precision: str = "f64",
-                 forward_only: bool = False):
+                 forward_only: bool = False, variant: int = 0):
         self.lib = load(precision)
         self.precision = precision
         self.dtype = dtype_of(precision)
@@ -147,8 +154,8 @@ class OracleGPT2:
             self.m = np.zeros(n, self.dtype)
             self.v = np.zeros(n, self.dtype)
         h = ct.c_void_p()
-        rc = self.lib.oracle_gpt2_build(ct.byref(h), ct.byref(self.cfg), B, T, _ptr(self.params),
-                                        _ptr(self.grads), _ptr(self.m), _ptr(self.v))
+        rc = self.lib.oracle_gpt2_build_variant(ct.byref(h), ct.byref(self.cfg), B, T, _ptr(self.params),
+                                                _ptr(self.grads), _ptr(self.m), _ptr(self.v), variant)
         if rc != 0:
             raise ValueError(f"oracle_gpt2_build failed: {rc}")
         self.h = h
@@ -191,8 +198,8 @@ class OracleGPT2:
 
     def activation(self, name: str, layer: int = 0, grad: bool = False) -> np.ndarray:
         cnt = ct.c_size_t()
-        p = self.lib.oracle_gpt2_activation(self.h, ACT_NAMES.index(name), layer, int(grad),
-                                            ct.byref(cnt))
+        aid = len(ACT_NAMES) if name == "qkv_rot" else ACT_NAMES.index(name)  # rotary variant only
+        p = self.lib.oracle_gpt2_activation(self.h, aid, layer, int(grad), ct.byref(cnt))
         if not p:
             raise ValueError(f"no activation {name}[{layer}]")
         buf = (ct.c_double if self.precision == "f64" else ct.c_float) * cnt.value
@@ -300,6 +307,46 @@ def softmax_forward(logits, precision="f64"):
     p = np.empty_like(z)
     lib.oracle_softmax_forward(_ptr(p), _ptr(z), N, V)
     return p
+
+
+def rmsnorm_forward(x, w, eps=1e-5, precision="f64"):
+    lib = load(precision)
+    x = _real(x, precision)
+    N, C = x.shape
+    y = np.empty_like(x)
+    r = np.empty(N, dtype=x.dtype)
+    lib.oracle_rmsnorm_forward(_ptr(y), _ptr(r), _ptr(x), _ptr(_real(w, precision)), N, C, eps)
+    return y, r
+
+
+def rmsnorm_backward(dy, x, w, rstd, precision="f64"):
+    lib = load(precision)
+    x = _real(x, precision)
+    N, C = x.shape
+    dx = np.zeros_like(x)
+    dw = np.zeros(C, dtype=x.dtype)
+    lib.oracle_rmsnorm_backward(_ptr(dx), _ptr(dw), _ptr(_real(dy, precision)), _ptr(x), _ptr(_real(w, precision)),
+                                _ptr(_real(rstd, precision)), N, C)
+    return dx, dw
+
+
+def rope_forward(qkv, NH, precision="f64"):
+    """qkv (B, T, 3C) -> the same with q and k rotated (v copied)."""
+    lib = load(precision)
+    x = _real(qkv, precision)
+    B, T, C3 = x.shape
+    y = np.empty_like(x)
+    lib.oracle_rope_forward(_ptr(y), _ptr(x), B, T, C3 // 3, NH)
+    return y
+
+
+def rope_backward(dout, NH, precision="f64"):
+    lib = load(precision)
+    d = _real(dout, precision)
+    B, T, C3 = d.shape
+    dx = np.zeros_like(d)
+    lib.oracle_rope_backward(_ptr(dx), _ptr(d), B, T, C3 // 3, NH)
+    return dx
 
 
 def sample_mult(probs, coin, precision="f64"):

@@ -478,3 +478,110 @@ def test_sample_mult_frequencies():
     counts = np.bincount([O.sample_mult(p, c) for c in coins], minlength=10)
     sd = np.sqrt(len(coins) * p * (1 - p))
     assert np.all(np.abs(counts - len(coins) * p) <= 5 * sd + 1), (counts, len(coins) * p)
+
+
+# ------------------------------------------------------------------ Llama-style variants
+
+def test_rmsnorm_vs_torch_and_invariants():
+    """RMSNorm against torch's own rms_norm and autograd; at eps = 0 every row of x*r has
+    mean square 1 exactly and the output does not change when x is scaled."""
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((37, 64)) * 3
+    w = 1 + 0.1 * rng.standard_normal(64)
+    dy = rng.standard_normal((37, 64))
+    y, r = O.rmsnorm_forward(x, w)
+    tx = torch.tensor(x, requires_grad=True)
+    tw = torch.tensor(w, requires_grad=True)
+    ty = torch.nn.functional.rms_norm(tx, (64,), tw, eps=1e-5)
+    ty.backward(torch.tensor(dy))
+    np.testing.assert_allclose(y, ty.detach().numpy(), rtol=1e-13, atol=1e-13)
+    dx, dw = O.rmsnorm_backward(dy, x, w, r)
+    np.testing.assert_allclose(dx, tx.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dw, tw.grad.numpy(), rtol=1e-12, atol=1e-12)
+    y0, r0 = O.rmsnorm_forward(x, np.ones(64), eps=0.0)
+    np.testing.assert_allclose(np.mean(y0 ** 2, axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(O.rmsnorm_forward(7.5 * x, w, eps=0.0)[0], O.rmsnorm_forward(x, w, eps=0.0)[0],
+                               rtol=1e-13)
+    c = np.full((1, 64), 0.25)
+    np.testing.assert_allclose(O.rmsnorm_forward(c, np.ones(64))[0], 0.25 / np.sqrt(0.0625 + 1e-5), rtol=1e-15)
+
+
+def test_rope_properties():
+    """Rotary positions: identity at position 0, every rotated pair keeps its length, a
+    query/key score depends only on the positions' difference, the backward is the
+    forward's transpose, and torch's complex-number formulation agrees."""
+    from tests.torch_gpt2 import rope as torch_rope
+    rng = np.random.default_rng(41)
+    B, T, C, NH = 2, 9, 32, 2
+    hs = C // NH
+    x = rng.standard_normal((B, T, 3 * C))
+    y = O.rope_forward(x, NH)
+    np.testing.assert_array_equal(y[:, 0], x[:, 0])
+    np.testing.assert_array_equal(y[..., 2 * C:], x[..., 2 * C:])
+    pn = lambda a: np.hypot(a[..., 0:2 * C:2], a[..., 1:2 * C:2])
+    np.testing.assert_allclose(pn(y), pn(x), rtol=1e-13)
+    # the same q and k vectors at every position: q_t . k_u must depend on t - u only
+    qk = np.tile(x[:1, :1], (1, T, 1))
+    r = O.rope_forward(qk, NH)[0]
+    q, k = r[:, :hs], r[:, C:C + hs]
+    s = q @ k.T
+    for d in range(-T + 1, T):
+        diag = np.diagonal(s, offset=d)
+        np.testing.assert_allclose(diag, diag[0], rtol=1e-12, atol=1e-12)
+    g = rng.standard_normal((B, T, 3 * C))
+    assert abs(np.sum(y * g) - np.sum(x * O.rope_backward(g, NH))) <= 1e-11 * np.sum(np.abs(x * g))
+    tq = torch.tensor(x[..., :C].reshape(B, T, NH, hs).transpose(0, 2, 1, 3))
+    ref = torch_rope(tq).numpy().transpose(0, 2, 1, 3).reshape(B, T, C)
+    np.testing.assert_allclose(y[..., :C], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_variant_finite_differences_micro_every_coordinate(variant):
+    x, y = micro_inputs()
+    p = micro_params()
+    m = O.OracleGPT2(MICRO.model, 2, 4, p, variant=variant)
+    m.forward(x, y)
+    m.zero_grad()
+    m.backward()
+    g = m.grads.copy()
+    h = 1e-5
+    fd = np.empty_like(g)
+    for i in range(p.size):
+        old = m.params[i]
+        m.params[i] = old + h
+        lp = m.forward(x, y)
+        m.params[i] = old - h
+        lm = m.forward(x, y)
+        m.params[i] = old
+        fd[i] = (lp - lm) / (2 * h)
+    for name, off, n in zip(O.PARAM_NAMES, m.offsets, m.lengths):
+        gt, ft = g[off:off + n], fd[off:off + n]
+        assert np.max(np.abs(gt - ft)) <= 1e-7 * max(np.max(np.abs(gt)), 1e-12), name
+    if variant & O.VARIANT_RMSNORM:  # unused LayerNorm biases
+        for name in ("ln1b", "ln2b", "lnfb"):
+            assert not np.any(m.tensor(g, name)), name
+    if variant & O.VARIANT_ROPE:  # unused position rows
+        assert not np.any(m.tensor(g, "wpe"))
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_variant_ten_steps_vs_pytorch_tiny(variant):
+    w = S.TINY
+    p = S.init_params(w.model)
+    x, y = S.tokens(w)
+    losses_t, g_t, p_t = torch_gpt2.train(w.model, p, x, y, 10, weight_decay=0.1, variant=variant)
+    m = O.OracleGPT2(w.model, w.B, w.T, p, variant=variant)
+    losses, g1 = [], None
+    for t in range(1, 11):
+        losses.append(m.forward(x, y))
+        m.zero_grad()
+        m.backward()
+        if g1 is None:
+            g1 = m.grads.copy()
+        m.update(1e-4, 0.9, 0.999, 1e-8, 0.1, t)
+    np.testing.assert_allclose(losses, losses_t, rtol=1e-13)
+    for name, off, n in zip(O.PARAM_NAMES, m.offsets, m.lengths):
+        sl = slice(off, off + n)
+        scale = max(np.max(np.abs(g_t[sl])), 1e-300)
+        assert np.max(np.abs(g1[sl] - g_t[sl])) <= 1e-11 * scale, name
+        assert np.max(np.abs(m.params[sl] - p_t[sl])) <= 1e-10 * max(np.max(np.abs(p_t[sl])), 1e-300), name

@@ -26,26 +26,48 @@ def to_tensors(shape, flat: np.ndarray):
     return out
 
 
-def loss_fn(shape, P, inputs, targets):
+RMSNORM, ROPE = 1, 2  # Llama-style layer variants (bit mask)
+
+
+def rope(x):
+    """Rotary positions as complex multiplication: consecutive dimension pairs of every
+    head are complex numbers, multiplied by exp(i t 10000^(-2j/hs)) at position t."""
+    T, hs = x.shape[-2], x.shape[-1]
+    inv = 10000.0 ** (-torch.arange(0, hs, 2, dtype=torch.float64) / hs)
+    ang = torch.arange(T, dtype=torch.float64)[:, None] * inv[None, :]
+    rot = torch.polar(torch.ones_like(ang), ang)
+    xc = torch.view_as_complex(x.reshape(*x.shape[:-1], hs // 2, 2).contiguous())
+    return torch.view_as_real(xc * rot).reshape(x.shape)
+
+
+def loss_fn(shape, P, inputs, targets, variant=0):
     C, NH, L = shape.channels, shape.num_heads, shape.num_layers
     tok = torch.as_tensor(np.asarray(inputs, dtype=np.int64))
     tgt = torch.as_tensor(np.asarray(targets, dtype=np.int64))
     B, T = tok.shape
-    x = P["wte"][tok] + P["wpe"][:T][None]
+
+    def norm(x, w, b):
+        if variant & RMSNORM:
+            return F.rms_norm(x, (C,), w, eps=1e-5)
+        return F.layer_norm(x, (C,), w, b, eps=1e-5)
+
+    x = P["wte"][tok] if variant & ROPE else P["wte"][tok] + P["wpe"][:T][None]
     for l in range(L):
-        h = F.layer_norm(x, (C,), P["ln1w"][l], P["ln1b"][l], eps=1e-5)
+        h = norm(x, P["ln1w"][l], P["ln1b"][l])
         qkv = F.linear(h, P["qkvw"][l], P["qkvb"][l])
         q, k, v = qkv.split(C, dim=-1)
         q = q.view(B, T, NH, C // NH).transpose(1, 2)
         k = k.view(B, T, NH, C // NH).transpose(1, 2)
         v = v.view(B, T, NH, C // NH).transpose(1, 2)
+        if variant & ROPE:
+            q, k = rope(q), rope(k)
         y = F.scaled_dot_product_attention(q, k, v, is_causal=True)
         y = y.transpose(1, 2).reshape(B, T, C)
         x = x + F.linear(y, P["attprojw"][l], P["attprojb"][l])
-        h = F.layer_norm(x, (C,), P["ln2w"][l], P["ln2b"][l], eps=1e-5)
+        h = norm(x, P["ln2w"][l], P["ln2b"][l])
         h = F.gelu(F.linear(h, P["fcw"][l], P["fcb"][l]), approximate="tanh")
         x = x + F.linear(h, P["fcprojw"][l], P["fcprojb"][l])
-    x = F.layer_norm(x, (C,), P["lnfw"], P["lnfb"], eps=1e-5)
+    x = norm(x, P["lnfw"], P["lnfb"])
     logits = x @ P["wte"].t()
     return F.cross_entropy(logits.view(B * T, -1), tgt.view(-1)), logits
 
@@ -59,7 +81,7 @@ def flat(P, attr: str | None = None) -> np.ndarray:
 
 
 def train(shape, flat_params, inputs, targets, steps, lr=1e-4, betas=(0.9, 0.999), eps=1e-8,
-          weight_decay=0.0):
+          weight_decay=0.0, variant=0):
     """Runs `steps` (forward, zero_grad, backward, AdamW) on one batch.
 
     Returns (losses, grads of the first step, params after the last step)."""
@@ -69,8 +91,11 @@ def train(shape, flat_params, inputs, targets, steps, lr=1e-4, betas=(0.9, 0.999
     losses, first_grads = [], None
     for _ in range(steps):
         opt.zero_grad()
-        loss, _ = loss_fn(shape, P, inputs, targets)
+        loss, _ = loss_fn(shape, P, inputs, targets, variant)
         loss.backward()
+        for t in P.values():  # tensors a variant leaves unused have a zero gradient
+            if t.grad is None:
+                t.grad = torch.zeros_like(t)
         losses.append(float(loss))
         if first_grads is None:
             first_grads = flat(P, "grad")
