@@ -214,6 +214,36 @@ def main():
     dt_gen = time.perf_counter() - t2
     sk = [e for e in model.profile_entries() if e["name"] == "sample_kernel"]
     model.profile_enable(False)
+    # The Llama-style variant (RMSNorm + rotary positions) at the same shape: a second
+    # model, 2 warm-up steps (the second with events on every kernel), 5 timed steps.
+    vm = G.GPT2(w.model, w.B, w.T, stream=stream, variant=G.VARIANT_RMSNORM | G.VARIANT_ROPE)
+    vm.params.copy_(model.params)
+    tv = 0
+
+    def vstep():
+        nonlocal tv
+        tv += 1
+        loss = vm.forward(tx, ty)
+        vm.zero_grad()
+        vm.backward()
+        vm.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, tv)
+        return loss
+
+    vstep()
+    vm.profile_enable(True)
+    vstep()
+    torch.cuda.synchronize()
+    vkernels = vm.profile_entries()
+    vm.profile_enable(False)
+    t3 = time.perf_counter()
+    vlosses = [vstep() for _ in range(5)]
+    torch.cuda.synchronize()
+    dt_var = (time.perf_counter() - t3) / 5
+    verr = vm.last_error()
+    vm.close()
+    if verr != 0 or not all(np.isfinite(vlosses)):
+        print(f"bench: variant step failed: {G.strerror(verr)}, losses {vlosses}", file=sys.stderr)
+        sys.exit(1)
     if model.last_error() != 0 or not all(np.isfinite(losses)):
         print(f"bench: step failed: {G.strerror(model.last_error())}, losses {losses}", file=sys.stderr)
         sys.exit(1)
@@ -260,6 +290,13 @@ def main():
                   "last position; coins from numpy default_rng(7)",
         "sample_kernel_us": sk[0]["ms"] * 1e3 / sk[0]["launches"] if sk else None,
         "first_tokens": [int(v) for v in gen[:9]],
+    }
+    vb = {k["name"]: k for k in breakdown(vkernels, 1)}
+    out["variant_rmsnorm_rope"] = {
+        "tokens_per_s": tokens / dt_var, "ms_per_step": dt_var * 1e3, "steps": 5,
+        "what": "every LayerNorm replaced by RMSNorm, rotary q/k positions instead of wpe; same shape and step",
+        "kernels": {n: vb[n] for n in ("rope_kernel<1>", "rope_kernel<-1>", "rms_fwd_kernel", "rms_bwd_kernel")
+                    if n in vb},
     }
     out["kernels"] = breakdown(all_kernels, max(1, args.warmup - 1))
     out["kernels_isolated"] = breakdown(isolated, 1)

@@ -91,6 +91,24 @@ typedef struct gpt2_buffers {
 int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buffers* bufs,
                void* stream);
 
+/* Llama-style layer variants (the pages name Llama 2, Gemma and Mistral
+ * as further llm.c targets, 新智元 article 纯CUDA也可训, but give no formulas, so the
+ * published definitions are used).  A bit mask:
+ *   GPT2_VARIANT_RMSNORM: every LayerNorm becomes RMSNorm, y = x r w with
+ *     r = 1/sqrt(mean(x^2) + 1e-5); no mean subtraction, no bias (ln1b, ln2b, lnfb take no
+ *     part and keep zero gradients; their mean activations read 0);
+ *   GPT2_VARIANT_ROPE: no position rows (wpe takes no part); after the qkv projection, in
+ *     every head of q and k the pair (2i, 2i+1) at position t is rotated by
+ *     t * 10000^(-2i/hs); the qkv activation then holds the rotated q and k.  Needs an
+ *     even head size.
+ * The parameter layout, buffers and every other call are those of gpt2_build (variant 0).
+ * Returns as gpt2_build, and GPT2_EINVAL for an unknown bit or an odd head size with
+ * GPT2_VARIANT_ROPE. */
+#define GPT2_VARIANT_RMSNORM 1
+#define GPT2_VARIANT_ROPE 2
+int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buffers* bufs, void* stream,
+                       int variant);
+
 /* Forward pass (huxiu page 核心代码解读 item 3: outputs and loss).  inputs and targets
  * are device pointers to B*T int32 token ids, row-major (B,T); ids must lie in
  * [0, vocab_size).  Requires 1 <= T <= max_seq_len and B*T <= the built B*T.

@@ -44,8 +44,12 @@ __global__ __launch_bounds__(256) void encoder_fwd_kernel(float* __restrict__ ou
     }
     const int t = row % T;
     const float4* we = reinterpret_cast<const float4*>(wte + (long)id * C);
-    const float4* pe = reinterpret_cast<const float4*>(wpe + (long)t * C);
     float4* o = reinterpret_cast<float4*>(out + (long)row * C);
+    if (!wpe) {  // no position rows (the rotary variant puts positions into q and k)
+        for (int i = lane; i < C / 4; i += 64) o[i] = we[i];
+        return;
+    }
+    const float4* pe = reinterpret_cast<const float4*>(wpe + (long)t * C);
     for (int i = lane; i < C / 4; i += 64) {
         const float4 a = we[i], b = pe[i];
         o[i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);

@@ -66,7 +66,7 @@ struct Layout {
     size_t tok_in, tok_tgt;  // int32 arrays inside acts (offset in 4-byte words)
     size_t n_acts;
     // grad_scratch
-    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, sample, n_scratch;
+    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, sample, rope, n_scratch;
 };
 
 Layout make_layout(const gpt2_config* c, int B, int T) {
@@ -127,6 +127,7 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     y.partial = take(np);
     y.partial_w = take(gemm_partial_floats());  // split tiles of the weight-gradient stream
     y.sample = take(3 * BT);                      // sampling requests: rows, coins, tokens
+    y.rope = take(rope_table_floats(c->max_seq_len, (int)(C / NH)));  // rotary variant's (cos, sin) table
     y.n_scratch = s;
     return y;
 }
@@ -144,6 +145,7 @@ struct gpt2 {
     hipStream_t st_w;
     hipEvent_t ev[10];
     int backward_streams;  // 2: weight gradients on st_w; 1: everything on st
+    int variant;           // GPT2_VARIANT_* bits (Llama-style layers)
     gpt2_buffers buf;
     size_t nparams;
     size_t poff[NP], plen[NP];
@@ -182,6 +184,24 @@ int* flags(gpt2* g) { return reinterpret_cast<int*>(g->buf.grad_scratch + HDR_FL
 
 bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// The block's normalisation: LayerNorm, or RMSNorm in the RMSNorm variant (its mean slot
+// then holds 0 and the LayerNorm bias takes no part, keeping a zero gradient).
+hipError_t norm_fwd(gpt2* g, float* y, float* mean, float* rstd, const float* x, const float* w, const float* b,
+                    int N, int C, hipStream_t st) {
+    if (g->variant & GPT2_VARIANT_RMSNORM) return rmsnorm_forward(y, mean, rstd, x, w, N, C, 1e-5f, st);
+    return layernorm_forward(y, mean, rstd, x, w, b, N, C, 1e-5f, st);
+}
+
+hipError_t norm_bwd(gpt2* g, float* dx, float* dw, float* db, const float* dy, const float* x, const float* w,
+                    const float* mean, const float* rstd, int N, int C, bool acc_dx, bool acc_dw, float* part,
+                    hipStream_t st) {
+    if (g->variant & GPT2_VARIANT_RMSNORM)
+        return rmsnorm_backward(dx, dw, dy, x, w, mean, rstd, N, C, acc_dx, acc_dw, part, st);
+    return layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, N, C, acc_dx, acc_dw, part, st);
+}
+
+bool rope_on(const gpt2* g) { return (g->variant & GPT2_VARIANT_ROPE) != 0; }
+
 int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, int T, float* loss_out) {
     const gpt2_config& c = g->cfg;
     float* part = S(g, g->lay.partial);
@@ -195,25 +215,28 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     if (inputs != tok_in(g)) HIPCHK(g, hipMemcpyAsync(tok_in(g), inputs, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
     if (targets) HIPCHK(g, hipMemcpyAsync(tok_tgt(g), targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(g, hipMemsetAsync(g->buf.grad_scratch, 0, HDR_WORDS * sizeof(float), st));
-    HIPCHK(g, encoder_forward(A(g, GPT2_ACT_ENCODED), tok_in(g), P(g, P_WTE), P(g, P_WPE), B, T, C, V, flags(g), st));
+    HIPCHK(g, encoder_forward(A(g, GPT2_ACT_ENCODED), tok_in(g), P(g, P_WTE), rope_on(g) ? nullptr : P(g, P_WPE), B, T,
+                              C, V, flags(g), st));
     for (int l = 0; l < L; l++) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
-        HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LN1, l), A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l),
-                                    residual, P(g, P_LN1W) + l * C, P(g, P_LN1B) + l * C, BT, C, 1e-5f, st));
+        HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN1, l), A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), residual,
+                           P(g, P_LN1W) + l * C, P(g, P_LN1B) + l * C, BT, C, st));
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_QKV, l), 3 * C, A(g, GPT2_ACT_LN1, l), P(g, P_QKVW) + (size_t)l * 3 * C * C,
                                  P(g, P_QKVB) + l * 3 * C, nullptr, nullptr, BT, 3 * C, C, part, st));
+        // rotary variant: q and k rotated in place (the stored qkv is the rotated one)
+        if (rope_on(g)) HIPCHK(g, rope_forward(A(g, GPT2_ACT_QKV, l), S(g, g->lay.rope), B, T, C, NH, st));
         HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T, C, NH, st));
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), P(g, P_ATTPROJW) + (size_t)l * C * C,
                                  P(g, P_ATTPROJB) + l * C, residual, nullptr, BT, C, C, part, st));
-        HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LN2, l), A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l),
-                                    A(g, GPT2_ACT_RESIDUAL2, l), P(g, P_LN2W) + l * C, P(g, P_LN2B) + l * C, BT, C, 1e-5f, st));
+        HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN2, l), A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l),
+                           A(g, GPT2_ACT_RESIDUAL2, l), P(g, P_LN2W) + l * C, P(g, P_LN2B) + l * C, BT, C, st));
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_FCH_GELU, l), 4 * C, A(g, GPT2_ACT_LN2, l), P(g, P_FCW) + (size_t)l * 4 * C * C,
                                  P(g, P_FCB) + l * 4 * C, nullptr, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C, part, st));
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_RESIDUAL3, l), C, A(g, GPT2_ACT_FCH_GELU, l), P(g, P_FCPROJW) + (size_t)l * 4 * C * C,
                                  P(g, P_FCPROJB) + l * C, A(g, GPT2_ACT_RESIDUAL2, l), nullptr, BT, C, 4 * C, part, st));
     }
-    HIPCHK(g, layernorm_forward(A(g, GPT2_ACT_LNF), A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD),
-                                A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, 1e-5f, st));
+    HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LNF), A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD),
+                       A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, st));
     HIPCHK(g, linear_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT, V,
                              C, part, st));
     HIPCHK(g, lse_xent_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LOGITS_LSE), A(g, GPT2_ACT_LOSSES),
@@ -311,8 +334,8 @@ int backward_impl(gpt2* g) {
     else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, sw));
     HIPCHK(g, mark(EV_W_LM, sw));
     HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
-    HIPCHK(g, layernorm_backward(dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
-                                 A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
+    HIPCHK(g, norm_bwd(g, dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
+                       A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
     // Per layer, the weight gradients (dW += dY^T X, db) need only that layer's output
     // gradient, so they run on the handle's second stream and overlap the main chain
     // (dgrads, attention, LayerNorm).  Events order the two: the second stream waits for
@@ -340,9 +363,9 @@ int backward_impl(gpt2* g) {
         HIPCHK(g, mark(EV_W_FC, sw));
         HIPCHK(g, linear_dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, nullptr, BT, C, 4 * C, part, st));
         HIPCHK(g, after(st, EV_W_FCPROJ));  // dres is about to change
-        HIPCHK(g, layernorm_backward(dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
-                                     P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C,
-                                     true, true, part, st));
+        HIPCHK(g, norm_bwd(g, dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
+                           P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C, true,
+                           true, part, st));
         // Attention projection: residual2 = residual + atty . Wa^T + ba.
         HIPCHK(g, mark(EV_DRES_B, st));
         HIPCHK(g, after(sw, EV_DRES_B));
@@ -354,6 +377,8 @@ int backward_impl(gpt2* g) {
         HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
                                      A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
+        // rotary variant: attention gave the gradient of the rotated q and k; rotate it back
+        if (rope_on(g)) HIPCHK(g, rope_backward(dqkv, S(g, g->lay.rope), B, T, C, NH, st));
         HIPCHK(g, mark(EV_DQKV, st));
         HIPCHK(g, after(sw, EV_DQKV));
         HIPCHK(g, linear_wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, 3 * C, A(g, GPT2_ACT_LN1, l), 3 * C, C, BT,
@@ -361,12 +386,12 @@ int backward_impl(gpt2* g) {
         HIPCHK(g, mark(EV_W_QKV, sw));
         HIPCHK(g, linear_dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, nullptr, BT, C, 3 * C, part, st));
         HIPCHK(g, after(st, EV_W_ATTPROJ));  // dres is about to change
-        HIPCHK(g, layernorm_backward(dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
-                                     A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
+        HIPCHK(g, norm_bwd(g, dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
+                           A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
     }
     // the second stream's last kernel ends all of its work (dwte is written below)
     HIPCHK(g, after(st, L > 0 ? EV_W_QKV : EV_W_LM));
-    HIPCHK(g, wpe_backward(G(g, P_WPE), dres, B, T, C, st));
+    if (!rope_on(g)) HIPCHK(g, wpe_backward(G(g, P_WPE), dres, B, T, C, st));
     if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, dres, C, 1.0f, wk_in, BT, st));
     else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_in(g), BT, dres, C, 1.0f, wk_in, st));
     return GPT2_OK;
@@ -406,9 +431,16 @@ int gpt2_arena_sizes(const gpt2_config* cfg, int B, int T, size_t* n_acts, size_
 }
 
 int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buffers* bufs, void* stream) {
+    return gpt2_build_variant(out, cfg, B, T, bufs, stream, 0);
+}
+
+int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buffers* bufs, void* stream,
+                       int variant) {
     if (!out) return GPT2_EINVAL;
     *out = nullptr;
     if (!config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !bufs) return GPT2_EINVAL;
+    if (variant & ~(GPT2_VARIANT_RMSNORM | GPT2_VARIANT_ROPE)) return GPT2_EINVAL;
+    if ((variant & GPT2_VARIANT_ROPE) && (cfg->channels / cfg->num_heads) % 2) return GPT2_EINVAL;
     if ((long)B * T > (1L << 30)) return GPT2_EINVAL;
     const gpt2_buffers& b = *bufs;
     if (!b.params || !b.grads || !b.m || !b.v || !b.acts || !b.grad_scratch) return GPT2_EINVAL;
@@ -425,6 +457,7 @@ int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buff
     g->lay = make_layout(cfg, B, T);
     g->st = (hipStream_t)stream;
     g->backward_streams = 2;
+    g->variant = variant;
     g->buf = b;
     g->nparams = gpt2_num_parameters(cfg);
     gpt2_param_layout(cfg, g->poff, g->plen);
@@ -441,6 +474,8 @@ int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buff
         ok = fill_zero(b.grads, g->nparams, g->st) == hipSuccess && fill_zero(b.m, g->nparams, g->st) == hipSuccess &&
              fill_zero(b.v, g->nparams, g->st) == hipSuccess;
     }
+    if (ok && (variant & GPT2_VARIANT_ROPE))
+        ok = rope_table(S(g, g->lay.rope), cfg->max_seq_len, cfg->channels / cfg->num_heads, g->st) == hipSuccess;
     if (!ok) {
         for (int i = 0; i < nev; i++) (void)hipEventDestroy(g->ev[i]);
         if (g->st_w) (void)hipStreamDestroy(g->st_w);

@@ -54,8 +54,17 @@ hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, 
                               const float* w, const float* mean, const float* rstd, int N, int C,
                               bool accumulate_dx, bool accumulate_dwdb, float* partial,
                               hipStream_t st);
+// RMSNorm (no mean subtraction, no bias): y = x r w, r = 1/sqrt(mean(x^2) + eps); mean[]
+// is written as 0 so the LayerNorm activation layout still holds.  The backward adds
+// only dw (same partial scratch as layernorm_backward, at most that size).
+hipError_t rmsnorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w, int N, int C,
+                           float eps, hipStream_t st);
+hipError_t rmsnorm_backward(float* dx, float* dw, const float* dy, const float* x, const float* w,
+                            const float* mean, const float* rstd, int N, int C, bool accumulate_dx,
+                            bool accumulate_dw, float* partial, hipStream_t st);
 
 // ---- embedding (encoder.hip) --------------------------------------------------------
+// out[b,t] = wte[tok[b,t]] + wpe[t]; wpe may be null (no position rows).
 hipError_t encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe,
                            int B, int T, int C, int V, int* flags, hipStream_t st);
 // Backward scatter-adds into wte, deterministic (each token's rows added in position
@@ -84,6 +93,15 @@ hipError_t attention_forward(float* out, float* lse, const float* qkv, int B, in
 hipError_t attention_backward(float* dqkv, float* delta, const float* dout, const float* qkv,
                               const float* out, const float* lse, int B, int T, int C, int NH,
                               hipStream_t st);
+
+// ---- rotary positions (rope.hip) ------------------------------------------------------
+// table: rope_table_floats(maxT, hs) floats of (cos, sin) pairs, filled by rope_table.
+// rope_forward rotates q and k of qkv (B, T, 3C) in place; rope_backward applies the
+// transpose to dq and dk of dqkv in place.  hs = C/NH must be even.
+size_t rope_table_floats(int maxT, int hs);
+hipError_t rope_table(float* table, int maxT, int hs, hipStream_t st);
+hipError_t rope_forward(float* qkv, const float* table, int B, int T, int C, int NH, hipStream_t st);
+hipError_t rope_backward(float* dqkv, const float* table, int B, int T, int C, int NH, hipStream_t st);
 
 // ---- softmax + cross-entropy (softmax_xent.hip) -------------------------------------
 // Per logits row (ld): lse = log sum exp; loss = lse - z[target] when targets != NULL.

@@ -6,6 +6,11 @@
 // and reduces with cross-lane shuffles; nothing is re-read from memory.  The
 // cross-row sums (dgamma, dbeta) go through per-block partial rows that a
 // second kernel adds in a fixed order, so results are deterministic.
+//
+// RMS = true gives RMSNorm, the Llama-style variant (published definition; the pages only
+// name those model families): no mean subtraction and no bias, r = 1/sqrt(mean(x^2) +
+// eps), y = x r w; the mean slot is written as 0, so the backward's x_hat = (x - mean) r
+// is the same expression, and dx = r (g - x_hat mean(g x_hat)) with no dbeta.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -17,7 +22,7 @@ namespace {
 constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
 constexpr int LN_MAX_BLOCKS = 512;
 
-template <int VPL>
+template <int VPL, bool RMS>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, float* __restrict__ mean,
                                                      float* __restrict__ rstd, const float* __restrict__ x,
                                                      const float* __restrict__ w, const float* __restrict__ b,
@@ -35,7 +40,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, floa
         v[j] = i < C4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
     }
-    const float m = wave_sum(s) / (float)C;
+    const float m = RMS ? 0.f : wave_sum(s) / (float)C;
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < VPL; j++) {
@@ -54,7 +59,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, floa
     for (int j = 0; j < VPL; j++) {
         const int i = lane + 64 * j;
         if (i < C4) {
-            const float4 ww = w4[i], bv = b4[i];
+            const float4 ww = w4[i], bv = RMS ? make_float4(0.f, 0.f, 0.f, 0.f) : b4[i];
             float4 o;
             o.x = (v[j].x - m) * r * ww.x + bv.x;
             o.y = (v[j].y - m) * r * ww.y + bv.y;
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, floa
 
 // dx = rstd * (g - mean(g) - xh * mean(g*xh)), g = w*dy, xh = (x-mean)*rstd.
 // Each block also leaves one partial row [dw | db] (2C floats) in `partial`.
-template <int VPL>
+template <int VPL, bool RMS>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, float* __restrict__ partial,
                                                      const float* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ w, const float* __restrict__ mean,
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
             pdb[j].z += dv.z;
             pdb[j].w += dv.w;
         }
-        const float mg = wave_sum(sg) / (float)C;
+        const float mg = RMS ? 0.f : wave_sum(sg) / (float)C;
         const float mgx = wave_sum(sgx) / (float)C;
         float4* o = reinterpret_cast<float4*>(dx + (long)row * C);
 #pragma unroll
@@ -140,8 +145,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
             }
         }
     }
-    // Combine the 4 waves' partials in wave order, then write the block's partial row.
-    for (int part = 0; part < 2; part++) {
+    // Combine the 4 waves' partials in wave order, then write the block's partial row
+    // ([dw | db], or [dw] for RMSNorm).
+    constexpr int PARTS = RMS ? 1 : 2;
+    for (int part = 0; part < PARTS; part++) {
 #pragma unroll
         for (int j = 0; j < VPL; j++) {
             const int i = lane + 64 * j;
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
         __syncthreads();
         for (int c = threadIdx.x; c < C; c += blockDim.x) {
             const float s = ((red[c] + red[C + c]) + red[2 * C + c]) + red[3 * C + c];
-            partial[(long)blockIdx.x * 2 * C + part * C + c] = s;
+            partial[(long)blockIdx.x * PARTS * C + part * C + c] = s;
         }
         __syncthreads();
     }
@@ -201,14 +208,18 @@ int ln_blocks(int N) { return std::min((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK
 
 }  // namespace
 
-hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,
-                             const float* b, int N, int C, float eps, hipStream_t st) {
+namespace {
+
+template <bool RMS>
+hipError_t norm_forward(float* y, float* mean, float* rstd, const float* x, const float* w, const float* b, int N,
+                        int C, float eps, hipStream_t st) {
     if (C % 4 || C > 4096 || N < 0) return hipErrorInvalidValue;
     if (N == 0) return hipSuccess;
     const int vpl = (C / 4 + 63) / 64;
     dim3 grid((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), block(256);
-    ProfScope ps(st, "ln_fwd_kernel", 0.0, 4.0 * ((double)N * C * 2 + 2.0 * N + 2.0 * C));
-#define LN_FWD(V) hipLaunchKernelGGL(ln_fwd_kernel<V>, grid, block, 0, st, y, mean, rstd, x, w, b, N, C, eps)
+    ProfScope ps(st, RMS ? "rms_fwd_kernel" : "ln_fwd_kernel", 0.0,
+                 4.0 * ((double)N * C * 2 + 2.0 * N + (RMS ? 1.0 : 2.0) * C));
+#define LN_FWD(V) hipLaunchKernelGGL((ln_fwd_kernel<V, RMS>), grid, block, 0, st, y, mean, rstd, x, w, b, N, C, eps)
     switch (vpl) {
         case 1: LN_FWD(1); break;
         case 2: LN_FWD(2); break;
@@ -221,28 +232,27 @@ hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x,
     return hipGetLastError();
 }
 
-size_t layernorm_partial_floats(int N, int C) { return (size_t)ln_blocks(N) * 2 * C; }
-
-hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x,
-                              const float* w, const float* mean, const float* rstd, int N, int C,
-                              bool accumulate_dx, bool accumulate_dwdb, float* partial,
-                              hipStream_t st) {
+template <bool RMS>
+hipError_t norm_backward(float* dx, float* dw, float* db, const float* dy, const float* x, const float* w,
+                         const float* mean, const float* rstd, int N, int C, bool accumulate_dx,
+                         bool accumulate_dwdb, float* partial, hipStream_t st) {
     if (C % 4 || C > 4096 || N < 0) return hipErrorInvalidValue;
     if (N == 0) {
         if (!accumulate_dwdb) {
             hipError_t e = fill_zero(dw, C, st);
-            if (e != hipSuccess) return e;
+            if (e != hipSuccess || RMS) return e;
             return fill_zero(db, C, st);
         }
         return hipSuccess;
     }
+    constexpr int PARTS = RMS ? 1 : 2;
     const int vpl = (C / 4 + 63) / 64;
     const int G = ln_blocks(N);
     const size_t lds = (size_t)4 * C * sizeof(float);
     {
-        ProfScope ps(st, "ln_bwd_kernel", 0.0,
-                     4.0 * ((double)N * C * (accumulate_dx ? 4 : 3) + 2.0 * N + C + 2.0 * G * C));
-#define LN_BWD(V) hipLaunchKernelGGL(ln_bwd_kernel<V>, dim3(G), dim3(256), lds, st, dx, partial, dy, x, w, mean, rstd, N, C, (int)accumulate_dx)
+        ProfScope ps(st, RMS ? "rms_bwd_kernel" : "ln_bwd_kernel", 0.0,
+                     4.0 * ((double)N * C * (accumulate_dx ? 4 : 3) + 2.0 * N + C + (double)PARTS * G * C));
+#define LN_BWD(V) hipLaunchKernelGGL((ln_bwd_kernel<V, RMS>), dim3(G), dim3(256), lds, st, dx, partial, dy, x, w, mean, rstd, N, C, (int)accumulate_dx)
         switch (vpl) {
             case 1: LN_BWD(1); break;
             case 2: LN_BWD(2); break;
@@ -255,10 +265,40 @@ hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    ProfScope ps2(st, "reduce_rows_kernel", 0.0, 4.0 * ((double)G * 2 * C + 2.0 * C * (accumulate_dwdb ? 2 : 1)));
-    hipLaunchKernelGGL(reduce_rows_kernel, dim3((2 * C + 63) / 64), dim3(256), 0, st, dw, db, C,
-                       (const float*)partial, G, 2 * C, (int)accumulate_dwdb);
+    ProfScope ps2(st, "reduce_rows_kernel", 0.0,
+                  4.0 * ((double)G * PARTS * C + (double)PARTS * C * (accumulate_dwdb ? 2 : 1)));
+    hipLaunchKernelGGL(reduce_rows_kernel, dim3((PARTS * C + 63) / 64), dim3(256), 0, st, dw, db, C,
+                       (const float*)partial, G, PARTS * C, (int)accumulate_dwdb);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,
+                             const float* b, int N, int C, float eps, hipStream_t st) {
+    return norm_forward<false>(y, mean, rstd, x, w, b, N, C, eps, st);
+}
+
+hipError_t rmsnorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w, int N, int C,
+                           float eps, hipStream_t st) {
+    return norm_forward<true>(y, mean, rstd, x, w, nullptr, N, C, eps, st);
+}
+
+size_t layernorm_partial_floats(int N, int C) { return (size_t)ln_blocks(N) * 2 * C; }
+
+hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x,
+                              const float* w, const float* mean, const float* rstd, int N, int C,
+                              bool accumulate_dx, bool accumulate_dwdb, float* partial,
+                              hipStream_t st) {
+    return norm_backward<false>(dx, dw, db, dy, x, w, mean, rstd, N, C, accumulate_dx, accumulate_dwdb, partial,
+                                st);
+}
+
+hipError_t rmsnorm_backward(float* dx, float* dw, const float* dy, const float* x, const float* w,
+                            const float* mean, const float* rstd, int N, int C, bool accumulate_dx,
+                            bool accumulate_dw, float* partial, hipStream_t st) {
+    return norm_backward<true>(dx, dw, nullptr, dy, x, w, mean, rstd, N, C, accumulate_dx, accumulate_dw, partial,
+                               st);
 }
 
 }  // namespace gpt2k

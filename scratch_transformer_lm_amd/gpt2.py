@@ -67,6 +67,8 @@ def load() -> ct.CDLL:
     lib.gpt2_arena_sizes.restype = i
     lib.gpt2_build.argtypes = [ct.POINTER(P), C, i, i, ct.POINTER(Buffers), P]
     lib.gpt2_build.restype = i
+    lib.gpt2_build_variant.argtypes = [ct.POINTER(P), C, i, i, ct.POINTER(Buffers), P, i]
+    lib.gpt2_build_variant.restype = i
     lib.gpt2_forward.argtypes = [P, P, P, i, i]
     lib.gpt2_forward.restype = f
     lib.gpt2_zero_grad.argtypes = [P]
@@ -153,7 +155,7 @@ def _stream_ptr(stream) -> int:
 class GPT2:
     """One model: six torch device buffers and the library handle built over them."""
 
-    def __init__(self, shape, B: int, T: int, device="cuda", stream=None):
+    def __init__(self, shape, B: int, T: int, device="cuda", stream=None, variant: int = 0):
         import torch
         self.lib = load()
         self.shape = shape
@@ -176,10 +178,11 @@ class GPT2:
                                                   self.grad_scratch)))
         h = ct.c_void_p()
         cfg = config(shape)
-        rc = self.lib.gpt2_build(ct.byref(h), ct.byref(cfg), B, T, ct.byref(bufs),
-                                 _stream_ptr(self.stream))
+        rc = self.lib.gpt2_build_variant(ct.byref(h), ct.byref(cfg), B, T, ct.byref(bufs),
+                                         _stream_ptr(self.stream), variant)
         if rc != GPT2_OK:
-            raise GPT2Error(rc, "gpt2_build")
+            raise GPT2Error(rc, "gpt2_build_variant")
+        self.variant = variant
         self.h = h
 
     def close(self):
@@ -286,6 +289,7 @@ class GPT2:
 
 
 GEMM_TILES_AUTO, GEMM_TILES_128, GEMM_TILES_96 = 0, 1, 2
+VARIANT_RMSNORM, VARIANT_ROPE = 1, 2  # gpt2_build_variant bits (Llama-style layers)
 
 
 def set_gemm_tiles(policy: int) -> None:

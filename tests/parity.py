@@ -49,9 +49,9 @@ def per_tensor(names, offsets, lengths, a, ref):
     return {n: rel_max(a[o:o + l], ref[o:o + l]) for n, o, l in zip(names, offsets, lengths)}
 
 
-def run_oracle(w, params, inputs, targets, steps, capture_steps=(1,), precision="f64"):
+def run_oracle(w, params, inputs, targets, steps, capture_steps=(1,), precision="f64", variant=0):
     from oracle import oracle as O
-    m = O.OracleGPT2(w.model, inputs.shape[0], inputs.shape[1], params, precision)
+    m = O.OracleGPT2(w.model, inputs.shape[0], inputs.shape[1], params, precision, variant=variant)
     losses, grads = [], {}
     for t in range(1, steps + 1):
         losses.append(m.forward(inputs, targets))

@@ -98,3 +98,12 @@ def test_sampling_argument_checks_need_no_gpu():
     lib = G.load()
     assert lib.gpt2_sample(None, None, None, 1, None) == G.GPT2_EINVAL
     assert lib.gpt2_generate(None, None, 1, 2, None) == G.GPT2_EINVAL
+
+
+def test_build_variant_argument_checks_need_no_gpu():
+    lib = G.load()
+    cfg = G.config(S.TINY.model)
+    h = ct.c_void_p()
+    bufs = G.Buffers()
+    assert lib.gpt2_build_variant(ct.byref(h), ct.byref(cfg), 2, 32, ct.byref(bufs), None, 4) == G.GPT2_EINVAL
+    assert lib.gpt2_build_variant(None, ct.byref(cfg), 2, 32, ct.byref(bufs), None, 3) == G.GPT2_EINVAL

@@ -82,10 +82,10 @@ def test_layernorm_standalone(G, N, C):
 
 # ------------------------------------------------------------------ full training step
 
-def gpu_run(G, w, params, x, y, steps, capture=(1,), B=None, T=None):
+def gpu_run(G, w, params, x, y, steps, capture=(1,), B=None, T=None, variant=0):
     B = B or x.shape[0]
     T = T or x.shape[1]
-    m = G.GPT2(w.model, B, T)
+    m = G.GPT2(w.model, B, T, variant=variant)
     m.params.copy_(dev(params))
     tx, ty = dev(x, torch.int32), dev(y, torch.int32)
     losses, grads = [], {}
@@ -100,14 +100,14 @@ def gpu_run(G, w, params, x, y, steps, capture=(1,), B=None, T=None):
     return dict(losses=np.array(losses), grads=grads, params=host(m.params).copy(), model=m)
 
 
-def check_training(G, w, steps):
+def check_training(G, w, steps, variant=0):
     params = S.init_params(w.model)
     x, y = S.tokens(w)
-    say(f"[train] {w.name} steps={steps}")
-    gr = gpu_run(G, w, params, x, y, steps, capture=(1, steps))
+    say(f"[train] {w.name} steps={steps} variant={variant}")
+    gr = gpu_run(G, w, params, x, y, steps, capture=(1, steps), variant=variant)
     say("[train] gpu done; running oracle (float64, then float32)")
-    orc = run_oracle(w, params, x, y, steps, capture_steps=(1, steps))
-    o32 = run_oracle(w, params, x, y, steps, capture_steps=(), precision="f32")
+    orc = run_oracle(w, params, x, y, steps, capture_steps=(1, steps), variant=variant)
+    o32 = run_oracle(w, params, x, y, steps, capture_steps=(), precision="f32", variant=variant)
     m = gr["model"]
     loss_err = np.abs(gr["losses"] - orc["losses"]) / np.abs(orc["losses"])
     say("loss gpu", gr["losses"].tolist())
@@ -290,6 +290,45 @@ def test_generate_matches_oracle(G):
     assert exact >= total - 2
     with pytest.raises(G.GPT2Error):
         m.generate([V - 1], w.model.max_seq_len + 1, np.zeros(w.model.max_seq_len + 1))
+
+
+# ------------------------------------------------------------------ Llama-style variants
+
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_variant_tiny_ten_steps(G, variant):
+    """RMSNorm (1), rotary positions (2) and both (3): ten steps of the tiny model with
+    weight decay against the oracle's variant, every gradient tensor at steps 1 and 10."""
+    import dataclasses
+    check_training(G, dataclasses.replace(S.TINY, weight_decay=0.1), 10, variant=variant)
+
+
+def test_variant_124m_short_three_steps(G):
+    check_training(G, S.GPT2_124M_SHORT, 3, variant=3)
+
+
+def test_variant_tiny_forward_activations(G):
+    """Both variants: RMSNorm outputs, their zero mean slots, the rotated qkv and every
+    later activation against the oracle."""
+    from oracle import oracle as O
+    w = S.TINY
+    params = S.init_params(w.model)
+    x, y = S.tokens(w)
+    m = G.GPT2(w.model, w.B, w.T, variant=3)
+    m.params.copy_(dev(params))
+    loss = m.forward(dev(x, torch.int32), dev(y, torch.int32))
+    o = O.OracleGPT2(w.model, w.B, w.T, params, variant=3)
+    lo = o.forward(x, y)
+    errs = {}
+    for name in ("encoded", "lnf", "lnf_rstd", "losses"):
+        errs[name] = rel_max(host(m.activation(name)).reshape(-1), o.activation(name))
+    for l in range(w.model.num_layers):
+        errs[f"qkv[{l}]"] = rel_max(host(m.activation("qkv", l)).reshape(-1), o.activation("qkv_rot", l))
+        for name in ("ln1", "ln1_rstd", "atty", "residual2", "ln2", "fch_gelu", "residual3"):
+            errs[f"{name}[{l}]"] = rel_max(host(m.activation(name, l)).reshape(-1), o.activation(name, l))
+        assert not np.any(host(m.activation("ln1_mean", l)))
+    say({k: f"{v:.1e}" for k, v in errs.items()})
+    assert abs(loss - lo) / lo <= LOSS_RTOL
+    assert max(errs.values()) <= 1e-5, errs
 
 
 def test_smaller_batch_than_built(G):
