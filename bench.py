@@ -3,9 +3,11 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload gpt2-124M B8 T1024]
                     [--no-cpu-baseline]
 
-One step = gpt2_forward + gpt2_zero_grad + gpt2_backward + gpt2_update (AdamW) over one
-synthetic batch already resident in HBM (the pages' forward / zero_grad / backward /
-update loop on a single batch).  Prints ONE JSON line.  Besides throughput it reports
+One step = gpt2_forward + gpt2_zero_grad + gpt2_backward_update over one synthetic batch
+already resident in HBM: the pages' forward / zero_grad / backward / update loop on a
+single batch, with backward and the AdamW update in the library's fused call (bitwise
+gpt2_backward followed by gpt2_update; it starts each layer's update as soon as that
+layer's gradients are final).  Prints ONE JSON line.  Besides throughput it reports
 the roofline position of the kernel that takes the most time (measured with HIP events
 around each of its launches, on the stream that launch runs on, over the timed region;
 plus the same kernel in a single-stream step) and the CPU oracle timed on a bounded
@@ -159,8 +161,7 @@ def main():
         t += 1
         loss = model.forward(tx, ty)
         model.zero_grad()
-        model.backward()
-        model.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
+        model.backward_update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
         return loss
 
     # Warm-up; all but the first warm-up step carry events around every kernel, which
@@ -225,8 +226,7 @@ def main():
         tv += 1
         loss = vm.forward(tx, ty)
         vm.zero_grad()
-        vm.backward()
-        vm.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, tv)
+        vm.backward_update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, tv)
         return loss
 
     vstep()

@@ -135,6 +135,16 @@ int gpt2_backward(gpt2* model);
 int gpt2_update(gpt2* model, float lr, float beta1, float beta2, float eps, float weight_decay,
                 int t);
 
+/* gpt2_backward followed by gpt2_update(lr, beta1, beta2, eps, weight_decay, t) in one
+ * call, bitwise the same result: every parameter gets the same elementwise AdamW.  Each
+ * layer's parameters are updated as soon as its gradients are final (after its
+ * LayerNorm backward and weight-gradient GEMMs), on the second backward stream, while the
+ * gradients of the layers below are still being formed; wte, wpe and the final norm are
+ * updated last.  Gradients are left in `grads` as gpt2_backward leaves them.
+ * Returns GPT2_OK, GPT2_EINVAL for a null model, GPT2_ESTATE without a forward with
+ * targets or with t < 1, GPT2_EDEVICE on a HIP error. */
+int gpt2_backward_update(gpt2* model, float lr, float beta1, float beta2, float eps, float weight_decay, int t);
+
 /* Last error recorded on the handle (GPT2_OK if none). */
 int gpt2_last_error(const gpt2* model);
 

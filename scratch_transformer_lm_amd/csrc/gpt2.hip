@@ -143,7 +143,8 @@ struct gpt2 {
     // Backward runs the weight-gradient GEMMs on a second stream of the handle's own,
     // ordered against the main chain by events (see backward_impl).
     hipStream_t st_w;
-    hipEvent_t ev[10];
+    hipStream_t st_u;  // per-layer AdamW of gpt2_backward_update
+    hipEvent_t ev[13];
     int backward_streams;  // 2: weight gradients on st_w; 1: everything on st
     int variant;           // GPT2_VARIANT_* bits (Llama-style layers)
     gpt2_buffers buf;
@@ -293,7 +294,30 @@ int generate_impl(gpt2* g, int32_t* tokens, int prompt_len, int total_len, const
     return GPT2_OK;
 }
 
-int backward_impl(gpt2* g) {
+// AdamW arguments of a fused backward + update (bias corrections precomputed).
+struct UpdateArgs {
+    float lr, b1, b2, eps, wd, bc1, bc2;
+};
+
+// AdamW over parameter tensors `ids` (16-tensor order) of layer l, or whole when l < 0.
+hipError_t adam_tensors(gpt2* g, const int* ids, int n, int l, const UpdateArgs& u, hipStream_t s) {
+    size_t off[ADAM_MAX_SEGS], len[ADAM_MAX_SEGS];
+    const size_t L = (size_t)g->cfg.num_layers;
+    for (int i = 0; i < n; i++) {
+        const size_t per = l < 0 ? g->plen[ids[i]] : g->plen[ids[i]] / L;
+        off[i] = g->poff[ids[i]] + (l < 0 ? 0 : (size_t)l * per);
+        len[i] = per;
+    }
+    return adamw_segments(g->buf.params, g->buf.grads, g->buf.m, g->buf.v, off, len, n, u.lr, u.b1, u.b2, u.eps,
+                          u.wd, u.bc1, u.bc2, s);
+}
+
+// With `up`, each layer's parameters are updated (AdamW) as soon as its gradients are
+// final, on the weight-gradient stream, while the main chain continues with the layers
+// below; wte, wpe and the final norm's parameters are updated at the end.  Every
+// parameter goes through the same elementwise update as gpt2_update, so the result is
+// bitwise that of gpt2_backward followed by gpt2_update.
+int backward_impl(gpt2* g, const UpdateArgs* up) {
     const gpt2_config& c = g->cfg;
     const int C = c.channels, L = c.num_layers, NH = c.num_heads, V = c.vocab_size;
     const int B = g->B, T = g->T, BT = B * T;
@@ -323,7 +347,9 @@ int backward_impl(gpt2* g) {
     // both accumulate into dwte.
     hipStream_t sw = g->backward_streams == 2 ? g->st_w : st;
     float* part_w = S(g, g->lay.partial_w);
-    enum { EV_DRES_A, EV_DFCH, EV_DRES_B, EV_DQKV, EV_W_FCPROJ, EV_W_FC, EV_W_ATTPROJ, EV_W_QKV, EV_LM, EV_W_LM };
+    enum { EV_DRES_A, EV_DFCH, EV_DRES_B, EV_DQKV, EV_W_FCPROJ, EV_W_FC, EV_W_ATTPROJ, EV_W_QKV, EV_LM, EV_W_LM, EV_LN1,
+           EV_W_END, EV_U_END };
+    hipStream_t su = g->backward_streams == 2 ? g->st_u : st;
     auto mark = [&](int e, hipStream_t s) { return hipEventRecord(g->ev[e], s); };
     auto after = [&](hipStream_t s, int e) { return hipStreamWaitEvent(s, g->ev[e], 0); };
     HIPCHK(g, mark(EV_LM, st));
@@ -388,12 +414,30 @@ int backward_impl(gpt2* g) {
         HIPCHK(g, after(st, EV_W_ATTPROJ));  // dres is about to change
         HIPCHK(g, norm_bwd(g, dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                            A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
+        if (up) {
+            // layer l's gradients are final once its LayerNorm backwards (main stream, just
+            // queued) and its weight gradients (last: the qkv wgrad on the second stream)
+            // are done; a third stream updates its parameters without holding either up
+            static const int layer_ids[12] = {P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_ATTPROJW, P_ATTPROJB,
+                                              P_LN2W, P_LN2B, P_FCW, P_FCB, P_FCPROJW, P_FCPROJB};
+            HIPCHK(g, mark(EV_LN1, st));
+            HIPCHK(g, after(su, EV_LN1));
+            HIPCHK(g, after(su, EV_W_QKV));
+            HIPCHK(g, adam_tensors(g, layer_ids, 12, l, *up, su));
+        }
     }
-    // the second stream's last kernel ends all of its work (dwte is written below)
-    HIPCHK(g, after(st, L > 0 ? EV_W_QKV : EV_W_LM));
+    // the second stream's last operation ends all of its work (dwte is written below)
+    HIPCHK(g, mark(EV_W_END, sw));
+    HIPCHK(g, after(st, EV_W_END));
     if (!rope_on(g)) HIPCHK(g, wpe_backward(G(g, P_WPE), dres, B, T, C, st));
     if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, dres, C, 1.0f, wk_in, BT, st));
     else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_in(g), BT, dres, C, 1.0f, wk_in, st));
+    if (up) {
+        static const int global_ids[4] = {P_WTE, P_WPE, P_LNFW, P_LNFB};
+        HIPCHK(g, adam_tensors(g, global_ids, 4, -1, *up, st));
+        HIPCHK(g, mark(EV_U_END, su));
+        HIPCHK(g, after(st, EV_U_END));
+    }
     return GPT2_OK;
 }
 
@@ -467,9 +511,10 @@ int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const g
     }
     // the weight-gradient stream (default priority, no implicit sync with the null stream)
     // and the events that order it against the main stream
-    bool ok = hipStreamCreateWithFlags(&g->st_w, hipStreamNonBlocking) == hipSuccess;
+    bool ok = hipStreamCreateWithFlags(&g->st_w, hipStreamNonBlocking) == hipSuccess &&
+              hipStreamCreateWithFlags(&g->st_u, hipStreamNonBlocking) == hipSuccess;
     int nev = 0;
-    for (; ok && nev < 10; nev++) ok = hipEventCreateWithFlags(&g->ev[nev], hipEventDisableTiming) == hipSuccess;
+    for (; ok && nev < 13; nev++) ok = hipEventCreateWithFlags(&g->ev[nev], hipEventDisableTiming) == hipSuccess;
     if (ok) {
         ok = fill_zero(b.grads, g->nparams, g->st) == hipSuccess && fill_zero(b.m, g->nparams, g->st) == hipSuccess &&
              fill_zero(b.v, g->nparams, g->st) == hipSuccess;
@@ -479,6 +524,7 @@ int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const g
     if (!ok) {
         for (int i = 0; i < nev; i++) (void)hipEventDestroy(g->ev[i]);
         if (g->st_w) (void)hipStreamDestroy(g->st_w);
+        if (g->st_u) (void)hipStreamDestroy(g->st_u);
         (void)hipHostFree(g->host_ret);
         free(g);
         return GPT2_EDEVICE;
@@ -516,7 +562,16 @@ int gpt2_backward(gpt2* g) {
     if (!g) return GPT2_EINVAL;
     if (!g->have_forward || !g->have_targets) return fail(g, GPT2_ESTATE);
     ProfBind bind(g);
-    return backward_impl(g);
+    return backward_impl(g, nullptr);
+}
+
+int gpt2_backward_update(gpt2* g, float lr, float beta1, float beta2, float eps, float weight_decay, int t) {
+    if (!g) return GPT2_EINVAL;
+    if (t < 1 || !g->have_forward || !g->have_targets) return fail(g, GPT2_ESTATE);
+    const UpdateArgs up{lr, beta1, beta2, eps, weight_decay, (float)(1.0 - pow((double)beta1, (double)t)),
+                        (float)(1.0 - pow((double)beta2, (double)t))};
+    ProfBind bind(g);
+    return backward_impl(g, &up);
 }
 
 int gpt2_update(gpt2* g, float lr, float beta1, float beta2, float eps, float weight_decay, int t) {
@@ -547,8 +602,10 @@ void gpt2_free(gpt2* g) {
     if (!g) return;
     (void)hipStreamSynchronize(g->st);
     (void)hipStreamSynchronize(g->st_w);
+    (void)hipStreamSynchronize(g->st_u);
     for (hipEvent_t e : g->ev) (void)hipEventDestroy(e);
     (void)hipStreamDestroy(g->st_w);
+    (void)hipStreamDestroy(g->st_u);
     if (g->prof) prof_destroy(g->prof);
     (void)hipHostFree(g->host_ret);
     free(g);
@@ -556,7 +613,8 @@ void gpt2_free(gpt2* g) {
 
 int gpt2_profile_enable(gpt2* g, int enable) {
     if (!g) return GPT2_EINVAL;
-    if (hipStreamSynchronize(g->st) != hipSuccess || hipStreamSynchronize(g->st_w) != hipSuccess)
+    if (hipStreamSynchronize(g->st) != hipSuccess || hipStreamSynchronize(g->st_w) != hipSuccess ||
+        hipStreamSynchronize(g->st_u) != hipSuccess)
         return fail(g, GPT2_EDEVICE);
     if (enable && !g->prof) {
         g->prof = prof_create();

@@ -118,6 +118,17 @@ hipError_t sample_tokens(const float* logits, long ld, const float* lse, const i
 // ---- optimizer and fills (adamw.hip) ------------------------------------------------
 hipError_t adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float b1,
                  float b2, float eps, float wd, float bc1, float bc2, hipStream_t st);
+// AdamW over n <= ADAM_MAX_SEGS disjoint slices [off[i], off[i] + len[i]) of the flat
+// buffers (offsets and lengths multiples of 4 floats): bitwise the update adamw gives
+// those elements.
+constexpr int ADAM_MAX_SEGS = 16;
+struct AdamSegments {
+    int n;
+    size_t off4[ADAM_MAX_SEGS];
+    size_t start4[ADAM_MAX_SEGS + 1];
+};
+hipError_t adamw_segments(float* p, const float* g, float* m, float* v, const size_t* off, const size_t* len, int n,
+                          float lr, float b1, float b2, float eps, float wd, float bc1, float bc2, hipStream_t st);
 hipError_t fill_zero(float* x, size_t n, hipStream_t st);
 
 }  // namespace gpt2k

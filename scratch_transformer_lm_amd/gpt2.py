@@ -95,6 +95,8 @@ def load() -> ct.CDLL:
                                        ct.POINTER(ct.c_double), ct.POINTER(ct.c_double),
                                        ct.POINTER(ct.c_double)]
     lib.gpt2_profile_entry.restype = i
+    lib.gpt2_backward_update.argtypes = [P, f, f, f, f, f, i]
+    lib.gpt2_backward_update.restype = i
     lib.gpt2_sample.argtypes = [P, P, P, i, P]
     lib.gpt2_sample.restype = i
     lib.gpt2_generate.argtypes = [P, P, i, i, P]
@@ -211,6 +213,9 @@ class GPT2:
 
     def update(self, lr, beta1, beta2, eps, weight_decay, t) -> int:
         return self.lib.gpt2_update(self.h, lr, beta1, beta2, eps, weight_decay, t)
+
+    def backward_update(self, lr, beta1, beta2, eps, weight_decay, t) -> int:
+        return self.lib.gpt2_backward_update(self.h, lr, beta1, beta2, eps, weight_decay, t)
 
     def last_error(self) -> int:
         return self.lib.gpt2_last_error(self.h)

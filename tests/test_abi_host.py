@@ -107,3 +107,8 @@ def test_build_variant_argument_checks_need_no_gpu():
     bufs = G.Buffers()
     assert lib.gpt2_build_variant(ct.byref(h), ct.byref(cfg), 2, 32, ct.byref(bufs), None, 4) == G.GPT2_EINVAL
     assert lib.gpt2_build_variant(None, ct.byref(cfg), 2, 32, ct.byref(bufs), None, 3) == G.GPT2_EINVAL
+
+
+def test_backward_update_argument_checks_need_no_gpu():
+    lib = G.load()
+    assert lib.gpt2_backward_update(None, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1) == G.GPT2_EINVAL

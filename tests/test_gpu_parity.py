@@ -331,6 +331,38 @@ def test_variant_tiny_forward_activations(G):
     assert max(errs.values()) <= 1e-5, errs
 
 
+def test_backward_update_is_backward_then_update_bitwise(G):
+    """gpt2_backward_update (each layer's AdamW as soon as its gradients are final) against
+    gpt2_backward + gpt2_update, with both backward schedules: losses, gradients, params
+    and both moments bitwise equal after three steps with weight decay."""
+    w = S.GPT2_124M_SHORT
+    say("[backward_update]")
+    params = S.init_params(w.model)
+    x, y = S.tokens(w)
+    runs = []
+    for fused, streams in ((False, 2), (True, 2), (True, 1)):
+        m = G.GPT2(w.model, w.B, w.T)
+        m.set_backward_streams(streams)
+        m.params.copy_(dev(params))
+        tx, ty = dev(x, torch.int32), dev(y, torch.int32)
+        losses = []
+        for t in (1, 2, 3):
+            losses.append(m.forward(tx, ty))
+            assert m.zero_grad() == 0
+            if fused:
+                assert m.backward_update(w.lr, w.beta1, w.beta2, w.eps, 0.1, t) == 0
+            else:
+                assert m.backward() == 0
+                assert m.update(w.lr, w.beta1, w.beta2, w.eps, 0.1, t) == 0
+        runs.append((losses, host(m.grads).copy(), host(m.params).copy(), host(m.m).copy(), host(m.v).copy()))
+        m.close()
+    ref = runs[0]
+    for r in runs[1:]:
+        assert r[0] == ref[0]
+        for a, b in zip(r[1:], ref[1:]):
+            assert np.array_equal(a, b)
+
+
 def test_smaller_batch_than_built(G):
     w = S.TINY
     say("[smaller batch]")
