@@ -369,6 +369,26 @@ EXPORT void oracle_matmul_backward(real* dinp, real* dw, real* dbias, const real
     }
 }
 
+/* bfloat16 rounding, for the mixed-precision variant (the pages name mixed precision
+ * as llm.c's next step: 新智元 article "千行C代码训完GPT-2", 纯CUDA也可训 and its
+ * outlook; OpenAI创始大神手搓千行C代码训练GPT, opening).  bfloat16 keeps the float
+ * exponent range and 8 significant bits (7 stored); a value is rounded to the nearest
+ * such number, ties to the one with an even last bit.  Written from that definition:
+ * x = m 2^e with 0.5 <= |m| < 1, and m 2^8 is rounded to an integer (nearbyint rounds
+ * ties to even in the default rounding mode).  Values below the normal bfloat16 range,
+ * infinities and NaN are outside what the model produces and are passed through. */
+EXPORT real oracle_bf16_round(real x) {
+    if (x == 0 || !isfinite(x)) return x;
+    int e;
+    double m = frexp((double)x, &e);
+    return (real)ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
+EXPORT void oracle_bf16_round_array(real* dst, const real* src, size_t n) {
+#pragma omp parallel for
+    for (size_t i = 0; i < n; i++) dst[i] = oracle_bf16_round(src[i]);
+}
+
 /* Causal multi-head self-attention (huxiu 傻瓜式复现GPT-2 names multi-head attention;
  * mask, scale and head split are the plain GPT-2 reading).  inp is (B,T,3C) holding
  * q | k | v; head h uses channels [h*hs, (h+1)*hs) of each, hs = C/NH.
@@ -704,6 +724,13 @@ typedef struct oracle_gpt2 {
  * embedding on q and k in place of the position rows (wpe then takes no part). */
 #define ORACLE_VARIANT_RMSNORM 1
 #define ORACLE_VARIANT_ROPE 2
+/* Mixed precision: every linear layer and the LM head multiply the
+ * bfloat16 roundings of their two operands (input and weight forward; output gradient
+ * and weight, or output gradient and input, backward), the products summed exactly;
+ * the bias gradient sums the unrounded output gradient.  Everything else -- the fp32
+ * master weights, LayerNorm, GELU, residuals, attention, softmax and cross-entropy,
+ * AdamW -- is unchanged. */
+#define ORACLE_VARIANT_BF16 4
 
 static void carve(oracle_gpt2* g, int B, int T) {
     size_t len[NACT];
@@ -735,7 +762,7 @@ EXPORT int oracle_gpt2_build_variant(oracle_gpt2** out, const oracle_config* cfg
                                      real* params, real* grads, real* m, real* v, int variant) {
     if (!out || !config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !params)
         return O_EINVAL;
-    if (variant & ~(ORACLE_VARIANT_RMSNORM | ORACLE_VARIANT_ROPE)) return O_EINVAL;
+    if (variant & ~(ORACLE_VARIANT_RMSNORM | ORACLE_VARIANT_ROPE | ORACLE_VARIANT_BF16)) return O_EINVAL;
     if ((variant & ORACLE_VARIANT_ROPE) && (cfg->channels / cfg->num_heads) % 2) return O_EINVAL;
     if ((grads || m || v) && !(grads && m && v)) return O_EINVAL;
     oracle_gpt2* g = (oracle_gpt2*)calloc(1, sizeof(oracle_gpt2));
@@ -802,6 +829,56 @@ EXPORT void oracle_gpt2_free(oracle_gpt2* g) {
 
 EXPORT int oracle_gpt2_last_error(const oracle_gpt2* g) { return g ? g->last_error : O_EINVAL; }
 
+/* The model's linear layers: plain, or on bfloat16-rounded operands (mixed-precision
+ * variant).  The rounded copies are temporary; the stored activations stay unrounded. */
+static real* bf16_copy(const real* x, size_t n) {
+    real* r = (real*)malloc(n * sizeof(real));
+    if (r) oracle_bf16_round_array(r, x, n);
+    return r;
+}
+
+static int linear_forward(const oracle_gpt2* g, real* out, const real* inp, const real* w, const real* bias,
+                          int N, int IC, int OC) {
+    if (!(g->variant & ORACLE_VARIANT_BF16)) {
+        oracle_matmul_forward(out, inp, w, bias, N, IC, OC);
+        return O_OK;
+    }
+    real* ri = bf16_copy(inp, (size_t)N * IC);
+    real* rw = bf16_copy(w, (size_t)OC * IC);
+    int rc = ri && rw ? O_OK : O_ENOMEM;
+    if (rc == O_OK) oracle_matmul_forward(out, ri, rw, bias, N, IC, OC);
+    free(ri);
+    free(rw);
+    return rc;
+}
+
+static int linear_backward(const oracle_gpt2* g, real* dinp, real* dw, real* dbias, const real* dout,
+                           const real* inp, const real* w, int N, int IC, int OC) {
+    if (!(g->variant & ORACLE_VARIANT_BF16)) {
+        oracle_matmul_backward(dinp, dw, dbias, dout, inp, w, N, IC, OC);
+        return O_OK;
+    }
+    real* rd = bf16_copy(dout, (size_t)N * OC);
+    real* ri = bf16_copy(inp, (size_t)N * IC);
+    real* rw = bf16_copy(w, (size_t)OC * IC);
+    int rc = rd && ri && rw ? O_OK : O_ENOMEM;
+    if (rc == O_OK) {
+        oracle_matmul_backward(dinp, dw, NULL, rd, ri, rw, N, IC, OC);
+        if (dbias) {
+#pragma omp parallel for
+            for (int o = 0; o < OC; o++) {
+                real s = 0;
+                for (int r = 0; r < N; r++) s += dout[(size_t)r * OC + o];
+                dbias[o] += s;
+            }
+        }
+    }
+    free(rd);
+    free(ri);
+    free(rw);
+    return rc;
+}
+
 /* The block's normalisation: LayerNorm, or RMSNorm in the RMSNorm variant (whose mean
  * slot then holds 0 and whose bias takes no part). */
 static void norm_forward(int rms, real* out, real* mean, real* rstd, const real* x, const real* w,
@@ -852,6 +929,7 @@ EXPORT double oracle_gpt2_forward(oracle_gpt2* g, const int32_t* inputs, const i
     size_t BT = (size_t)B * T;
     size_t att_l = (size_t)B * NH * T * T;
     const int rms = g->variant & ORACLE_VARIANT_RMSNORM, rope = g->variant & ORACLE_VARIANT_ROPE;
+    int bad = 0;  /* a linear layer could not allocate its rounded operands */
     oracle_encoder_forward(A[A_ENCODED], inputs, P[0], rope ? NULL : P[1], B, T, C);
     for (int l = 0; l < L; l++) {
         real* residual = l == 0 ? A[A_ENCODED] : A[A_RESIDUAL3] + (size_t)(l - 1) * BT * C;
@@ -872,24 +950,28 @@ EXPORT double oracle_gpt2_forward(oracle_gpt2* g, const int32_t* inputs, const i
         real* fcproj = A[A_FCPROJ] + l * BT * C;
         real* res3 = A[A_RESIDUAL3] + l * BT * C;
         norm_forward(rms, ln1, ln1m, ln1r, residual, P[2] + l * C, P[3] + l * C, (int)BT, C);
-        oracle_matmul_forward(qkv, ln1, P[4] + (size_t)l * 3 * C * C, P[5] + l * 3 * C, (int)BT, C, 3 * C);
+        bad |= linear_forward(g, qkv, ln1, P[4] + (size_t)l * 3 * C * C, P[5] + l * 3 * C, (int)BT, C, 3 * C);
         real* qkv_in = qkv;
         if (rope) {
             qkv_in = g->qkvr + (size_t)l * BT * 3 * C;
             oracle_rope_forward(qkv_in, qkv, B, T, C, NH);
         }
         oracle_attention_forward(atty, preatt, att, qkv_in, B, T, C, NH);
-        oracle_matmul_forward(attproj, atty, P[6] + (size_t)l * C * C, P[7] + l * C, (int)BT, C, C);
+        bad |= linear_forward(g, attproj, atty, P[6] + (size_t)l * C * C, P[7] + l * C, (int)BT, C, C);
         oracle_residual_forward(res2, residual, attproj, BT * C);
         norm_forward(rms, ln2, ln2m, ln2r, res2, P[8] + l * C, P[9] + l * C, (int)BT, C);
-        oracle_matmul_forward(fch, ln2, P[10] + (size_t)l * 4 * C * C, P[11] + l * 4 * C, (int)BT, C, 4 * C);
+        bad |= linear_forward(g, fch, ln2, P[10] + (size_t)l * 4 * C * C, P[11] + l * 4 * C, (int)BT, C, 4 * C);
         oracle_gelu_forward(fchg, fch, BT * 4 * C);
-        oracle_matmul_forward(fcproj, fchg, P[12] + (size_t)l * 4 * C * C, P[13] + l * C, (int)BT, 4 * C, C);
+        bad |= linear_forward(g, fcproj, fchg, P[12] + (size_t)l * 4 * C * C, P[13] + l * C, (int)BT, 4 * C, C);
         oracle_residual_forward(res3, res2, fcproj, BT * C);
     }
     real* last = A[A_RESIDUAL3] + (size_t)(L - 1) * BT * C;
     norm_forward(rms, A[A_LNF], A[A_LNF_MEAN], A[A_LNF_RSTD], last, P[14], P[15], (int)BT, C);
-    oracle_matmul_forward(A[A_LOGITS], A[A_LNF], P[0], NULL, (int)BT, C, V);
+    bad |= linear_forward(g, A[A_LOGITS], A[A_LNF], P[0], NULL, (int)BT, C, V);
+    if (bad) {
+        g->last_error = O_ENOMEM;
+        return NAN;
+    }
     oracle_softmax_forward(A[A_PROBS], A[A_LOGITS], (int)BT, V);
     g->have_forward = 1;
     if (!targets) {
@@ -939,10 +1021,11 @@ EXPORT int oracle_gpt2_backward(oracle_gpt2* g) {
     memset(g->dacts, 0, g->num_acts * sizeof(real));
     const int rms = g->variant & ORACLE_VARIANT_RMSNORM, rope = g->variant & ORACLE_VARIANT_ROPE;
     if (rope) memset(g->dqkvr, 0, (size_t)L * BT * 3 * C * sizeof(real));
+    int bad = 0;  /* a linear layer could not allocate its rounded operands */
     real dl = (real)1 / (real)BT;
     for (size_t i = 0; i < BT; i++) D[A_LOSSES][i] = dl;
     oracle_crossentropy_softmax_backward(D[A_LOGITS], D[A_LOSSES], A[A_PROBS], g->targets, (int)BT, V);
-    oracle_matmul_backward(D[A_LNF], G[0], NULL, D[A_LOGITS], A[A_LNF], P[0], (int)BT, C, V);
+    bad |= linear_backward(g, D[A_LNF], G[0], NULL, D[A_LOGITS], A[A_LNF], P[0], (int)BT, C, V);
     real* last = A[A_RESIDUAL3] + (size_t)(L - 1) * BT * C;
     real* dlast = D[A_RESIDUAL3] + (size_t)(L - 1) * BT * C;
     norm_backward(rms, dlast, G[14], G[15], D[A_LNF], last, P[14], A[A_LNF_MEAN], A[A_LNF_RSTD], (int)BT, C);
@@ -952,18 +1035,18 @@ EXPORT int oracle_gpt2_backward(oracle_gpt2* g) {
         size_t o1 = l * BT * C, o3 = l * BT * 3 * C, o4 = l * BT * 4 * C, oa = l * att_l, os = l * BT;
         /* MLP half, backwards. */
         oracle_residual_backward(D[A_RESIDUAL2] + o1, D[A_FCPROJ] + o1, D[A_RESIDUAL3] + o1, BT * C);
-        oracle_matmul_backward(D[A_FCH_GELU] + o4, G[12] + (size_t)l * 4 * C * C, G[13] + l * C,
+        bad |= linear_backward(g, D[A_FCH_GELU] + o4, G[12] + (size_t)l * 4 * C * C, G[13] + l * C,
                                D[A_FCPROJ] + o1, A[A_FCH_GELU] + o4, P[12] + (size_t)l * 4 * C * C,
                                (int)BT, 4 * C, C);
         oracle_gelu_backward(D[A_FCH] + o4, A[A_FCH] + o4, D[A_FCH_GELU] + o4, BT * 4 * C);
-        oracle_matmul_backward(D[A_LN2] + o1, G[10] + (size_t)l * 4 * C * C, G[11] + l * 4 * C,
+        bad |= linear_backward(g, D[A_LN2] + o1, G[10] + (size_t)l * 4 * C * C, G[11] + l * 4 * C,
                                D[A_FCH] + o4, A[A_LN2] + o1, P[10] + (size_t)l * 4 * C * C,
                                (int)BT, C, 4 * C);
         norm_backward(rms, D[A_RESIDUAL2] + o1, G[8] + l * C, G[9] + l * C, D[A_LN2] + o1,
                       A[A_RESIDUAL2] + o1, P[8] + l * C, A[A_LN2_MEAN] + os, A[A_LN2_RSTD] + os, (int)BT, C);
         /* Attention half, backwards. */
         oracle_residual_backward(dresidual, D[A_ATTPROJ] + o1, D[A_RESIDUAL2] + o1, BT * C);
-        oracle_matmul_backward(D[A_ATTY] + o1, G[6] + (size_t)l * C * C, G[7] + l * C,
+        bad |= linear_backward(g, D[A_ATTY] + o1, G[6] + (size_t)l * C * C, G[7] + l * C,
                                D[A_ATTPROJ] + o1, A[A_ATTY] + o1, P[6] + (size_t)l * C * C,
                                (int)BT, C, C);
         if (rope) {
@@ -974,13 +1057,14 @@ EXPORT int oracle_gpt2_backward(oracle_gpt2* g) {
             oracle_attention_backward(D[A_QKV] + o3, D[A_PREATT] + oa, D[A_ATT] + oa, D[A_ATTY] + o1,
                                       A[A_QKV] + o3, A[A_ATT] + oa, B, T, C, NH);
         }
-        oracle_matmul_backward(D[A_LN1] + o1, G[4] + (size_t)l * 3 * C * C, G[5] + l * 3 * C,
+        bad |= linear_backward(g, D[A_LN1] + o1, G[4] + (size_t)l * 3 * C * C, G[5] + l * 3 * C,
                                D[A_QKV] + o3, A[A_LN1] + o1, P[4] + (size_t)l * 3 * C * C,
                                (int)BT, C, 3 * C);
         norm_backward(rms, dresidual, G[2] + l * C, G[3] + l * C, D[A_LN1] + o1, residual,
                       P[2] + l * C, A[A_LN1_MEAN] + os, A[A_LN1_RSTD] + os, (int)BT, C);
     }
     oracle_encoder_backward(G[0], rope ? NULL : G[1], D[A_ENCODED], g->inputs, B, T, C);
+    if (bad) return g->last_error = O_ENOMEM;
     return O_OK;
 }
 

@@ -18,8 +18,9 @@ ACT_NAMES = ("encoded", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "preatt", 
              "residual2", "ln2", "ln2_mean", "ln2_rstd", "fch", "fch_gelu", "fcproj", "residual3",
              "lnf", "lnf_mean", "lnf_rstd", "logits", "probs", "losses")
 PER_LAYER = set(ACT_NAMES[1:17])
-# Llama-style layer variants (bit mask): RMSNorm for every LayerNorm, rotary q/k positions.
-VARIANT_RMSNORM, VARIANT_ROPE = 1, 2
+# Model variants (bit mask): RMSNorm for every LayerNorm, rotary q/k positions (the
+# Llama-style layers), and mixed precision (bfloat16-rounded matmul operands).
+VARIANT_RMSNORM, VARIANT_ROPE, VARIANT_BF16 = 1, 2, 4
 
 
 class Config(ct.Structure):
@@ -88,6 +89,9 @@ def load(precision: str = "f64") -> ct.CDLL:
     lib.oracle_crossentropy_forward.argtypes = [P, P, P, i, i]
     lib.oracle_crossentropy_softmax_backward.argtypes = [P, P, P, P, i, i]
     lib.oracle_adamw.argtypes = [P, P, P, P, sz, real, real, real, real, real, i]
+    lib.oracle_bf16_round.argtypes = [real]
+    lib.oracle_bf16_round.restype = real
+    lib.oracle_bf16_round_array.argtypes = [P, P, sz]
     _LIBS[precision] = lib
     return lib
 
@@ -298,6 +302,15 @@ def matmul_backward(dout, x, w, with_bias=True, precision="f64"):
     db = np.zeros(OC, x.dtype) if with_bias else None
     lib.oracle_matmul_backward(_ptr(dx), _ptr(dw), _ptr(db), _ptr(dout), _ptr(x), _ptr(w), N, IC, OC)
     return dx, dw, db
+
+
+def bf16_round(x, precision="f64"):
+    """Each element rounded to the nearest bfloat16 value (ties to even)."""
+    lib = load(precision)
+    x = _real(np.asarray(x), precision)
+    out = np.empty_like(x)
+    lib.oracle_bf16_round_array(_ptr(out), _ptr(x), x.size)
+    return out
 
 
 def softmax_forward(logits, precision="f64"):

@@ -564,7 +564,7 @@ def test_variant_finite_differences_micro_every_coordinate(variant):
         assert not np.any(m.tensor(g, "wpe"))
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 7])
 def test_variant_ten_steps_vs_pytorch_tiny(variant):
     w = S.TINY
     p = S.init_params(w.model)
@@ -585,3 +585,42 @@ def test_variant_ten_steps_vs_pytorch_tiny(variant):
         scale = max(np.max(np.abs(g_t[sl])), 1e-300)
         assert np.max(np.abs(g1[sl] - g_t[sl])) <= 1e-11 * scale, name
         assert np.max(np.abs(m.params[sl] - p_t[sl])) <= 1e-10 * max(np.max(np.abs(p_t[sl])), 1e-300), name
+
+
+# ------------------------------------------------------------------ mixed precision
+
+@pytest.mark.parametrize("precision", ["f64", "f32"])
+def test_bf16_round_vs_torch(precision):
+    """The oracle's bfloat16 rounding against torch's float32 -> bfloat16 conversion (a
+    library routine, round to nearest even) on values over 34 binary decades, exact
+    ties (both directions), signs and zero; and the defining properties: the result has
+    at most 8 significant bits and lies within half a bfloat16 unit of the input."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(200_000) * np.exp2(rng.uniform(-17, 17, 200_000))).astype(np.float32)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 2 + 2.0 ** -7, 0.0, -0.0,
+                     3 * 2.0 ** -20 + 2.0 ** -28], np.float32)
+    x = np.concatenate([x, ties, np.float32([np.pi])])
+    r = O.bf16_round(x, precision).astype(np.float64)
+    t = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(r, t)
+    np.testing.assert_array_equal(O.bf16_round(ties[:4].astype(np.float64)),
+                                  [1.0, 1 + 2.0 ** -6, -1.0, 2.0])
+    bits = r.astype(np.float32).view(np.uint32)
+    assert not np.any(bits & 0xFFFF)
+    x64 = x.astype(np.float64)
+    nz = x64 != 0
+    e = np.floor(np.log2(np.abs(x64[nz])))
+    assert np.all(np.abs(r[nz] - x64[nz]) <= np.exp2(e - 8) * (1 + 1e-12))
+
+
+def test_bf16_variant_loss_near_full_precision_tiny():
+    """Rounding every matmul operand to bfloat16 moves the loss by about the operands'
+    relative rounding (2^-9) times the logits' spread, far below the loss itself and far
+    above float64 noise: a variant that rounded nothing, or rounded the wrong values to
+    zero, fails one side."""
+    w = S.TINY
+    p = S.init_params(w.model)
+    x, y = S.tokens(w)
+    l64 = O.OracleGPT2(w.model, w.B, w.T, p).forward(x, y)
+    lbf = O.OracleGPT2(w.model, w.B, w.T, p, variant=O.VARIANT_BF16).forward(x, y)
+    assert 1e-7 < abs(lbf - l64) / l64 < 2e-3

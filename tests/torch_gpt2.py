@@ -26,7 +26,37 @@ def to_tensors(shape, flat: np.ndarray):
     return out
 
 
-RMSNORM, ROPE = 1, 2  # Llama-style layer variants (bit mask)
+RMSNORM, ROPE, BF16 = 1, 2, 4  # model variants (bit mask)
+
+
+def bf16(t):
+    """Nearest bfloat16 value (8 significant bits, ties to even) of each float64 element,
+    rounded once from float64 (a cast through float32 would round twice)."""
+    m, e = torch.frexp(t)
+    return torch.ldexp(torch.round(torch.ldexp(m, torch.tensor(8))), e - 8)
+
+
+class _RoundOperand(torch.autograd.Function):
+    """bfloat16 operand of a product; the gradient passes through unchanged."""
+    @staticmethod
+    def forward(ctx, x):
+        return bf16(x)
+
+    @staticmethod
+    def backward(ctx, g):
+        return g
+
+
+class _RoundGradient(torch.autograd.Function):
+    """Identity on the way forward; the incoming gradient is rounded to bfloat16 on the
+    way back, so both products of a linear layer's backward take the rounded gradient."""
+    @staticmethod
+    def forward(ctx, x):
+        return x.clone()
+
+    @staticmethod
+    def backward(ctx, g):
+        return bf16(g)
 
 
 def rope(x):
@@ -46,6 +76,12 @@ def loss_fn(shape, P, inputs, targets, variant=0):
     tgt = torch.as_tensor(np.asarray(targets, dtype=np.int64))
     B, T = tok.shape
 
+    def linear(x, w, b=None):
+        if variant & BF16:
+            y = _RoundGradient.apply(_RoundOperand.apply(x) @ _RoundOperand.apply(w).t())
+            return y if b is None else y + b
+        return F.linear(x, w, b)
+
     def norm(x, w, b):
         if variant & RMSNORM:
             return F.rms_norm(x, (C,), w, eps=1e-5)
@@ -54,7 +90,7 @@ def loss_fn(shape, P, inputs, targets, variant=0):
     x = P["wte"][tok] if variant & ROPE else P["wte"][tok] + P["wpe"][:T][None]
     for l in range(L):
         h = norm(x, P["ln1w"][l], P["ln1b"][l])
-        qkv = F.linear(h, P["qkvw"][l], P["qkvb"][l])
+        qkv = linear(h, P["qkvw"][l], P["qkvb"][l])
         q, k, v = qkv.split(C, dim=-1)
         q = q.view(B, T, NH, C // NH).transpose(1, 2)
         k = k.view(B, T, NH, C // NH).transpose(1, 2)
@@ -63,12 +99,12 @@ def loss_fn(shape, P, inputs, targets, variant=0):
             q, k = rope(q), rope(k)
         y = F.scaled_dot_product_attention(q, k, v, is_causal=True)
         y = y.transpose(1, 2).reshape(B, T, C)
-        x = x + F.linear(y, P["attprojw"][l], P["attprojb"][l])
+        x = x + linear(y, P["attprojw"][l], P["attprojb"][l])
         h = norm(x, P["ln2w"][l], P["ln2b"][l])
-        h = F.gelu(F.linear(h, P["fcw"][l], P["fcb"][l]), approximate="tanh")
-        x = x + F.linear(h, P["fcprojw"][l], P["fcprojb"][l])
+        h = F.gelu(linear(h, P["fcw"][l], P["fcb"][l]), approximate="tanh")
+        x = x + linear(h, P["fcprojw"][l], P["fcprojb"][l])
     x = norm(x, P["lnfw"], P["lnfb"])
-    logits = x @ P["wte"].t()
+    logits = linear(x, P["wte"])
     return F.cross_entropy(logits.view(B * T, -1), tgt.view(-1)), logits
 
 
