@@ -29,7 +29,13 @@ sys.path.insert(0, ROOT)
 from scratch_transformer_lm_amd import synthetic as S  # noqa: E402
 
 PEAK_FP32_MFMA = 157.3e12
+PEAK_BF16_MFMA = 2.5e15  # dense
 PEAK_HBM = 8.0e12
+
+
+def mfma_peak(name: str) -> float:
+    """Matrix-core peak of a kernel's arithmetic: bf16 for the mixed-precision GEMM."""
+    return PEAK_BF16_MFMA if name.startswith("gemm_bf16_kernel") else PEAK_FP32_MFMA
 
 
 def step_flops(m: S.ModelShape, B: int, T: int) -> float:
@@ -45,12 +51,12 @@ def step_flops(m: S.ModelShape, B: int, T: int) -> float:
 def roofline(kernels):
     """Roofline position of the kernel with the largest total time: its algorithmic work
     per launch over its average launch duration, against the MI355X peak of its bound
-    (fp32 matrix cores for kernels that count flops, HBM otherwise)."""
+    (the matrix cores of its data type for kernels that count flops, HBM otherwise)."""
     k = max(kernels, key=lambda e: e["ms"])
     avg_s = k["ms"] / k["launches"] / 1e3
     if k["flops"] > 0:
         achieved = k["flops"] / k["launches"] / avg_s / 1e12
-        r = dict(bound="mfma", achieved=achieved, peak=PEAK_FP32_MFMA / 1e12, unit="TFLOP/s")
+        r = dict(bound="mfma", achieved=achieved, peak=mfma_peak(k["name"]) / 1e12, unit="TFLOP/s")
     else:
         achieved = k["bytes"] / k["launches"] / avg_s / 1e9
         r = dict(bound="hbm", achieved=achieved, peak=PEAK_HBM / 1e9, unit="GB/s")
@@ -69,7 +75,7 @@ def breakdown(kernels, steps):
         e = dict(name=k["name"], ms_per_step=k["ms"] / steps, launches_per_step=k["launches"] / steps)
         if k["flops"] > 0:
             e["tflops"] = k["flops"] / k["launches"] / avg_s / 1e12
-            e["frac_mfma"] = e["tflops"] * 1e12 / PEAK_FP32_MFMA
+            e["frac_mfma"] = e["tflops"] * 1e12 / mfma_peak(k["name"])
         else:
             e["gbps"] = k["bytes"] / k["launches"] / avg_s / 1e9
             e["frac_hbm"] = e["gbps"] * 1e9 / PEAK_HBM
@@ -244,6 +250,36 @@ def main():
     if verr != 0 or not all(np.isfinite(vlosses)):
         print(f"bench: variant step failed: {G.strerror(verr)}, losses {vlosses}", file=sys.stderr)
         sys.exit(1)
+    # Mixed precision (bf16 matmul operands; fp32 master weights, AdamW and every other
+    # operation) at the same shape: 2 warm-up steps (the second with events on every
+    # kernel), 5 timed steps.
+    bm = G.GPT2(w.model, w.B, w.T, stream=stream, variant=G.VARIANT_BF16)
+    bm.params.copy_(model.params)
+    tb = 0
+
+    def bstep():
+        nonlocal tb
+        tb += 1
+        loss = bm.forward(tx, ty)
+        bm.zero_grad()
+        bm.backward_update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, tb)
+        return loss
+
+    bstep()
+    bm.profile_enable(True)
+    bstep()
+    torch.cuda.synchronize()
+    bkernels = bm.profile_entries()
+    bm.profile_enable(False)
+    t4 = time.perf_counter()
+    blosses = [bstep() for _ in range(5)]
+    torch.cuda.synchronize()
+    dt_bf = (time.perf_counter() - t4) / 5
+    berr = bm.last_error()
+    bm.close()
+    if berr != 0 or not all(np.isfinite(blosses)):
+        print(f"bench: mixed-precision step failed: {G.strerror(berr)}, losses {blosses}", file=sys.stderr)
+        sys.exit(1)
     if model.last_error() != 0 or not all(np.isfinite(losses)):
         print(f"bench: step failed: {G.strerror(model.last_error())}, losses {losses}", file=sys.stderr)
         sys.exit(1)
@@ -297,6 +333,15 @@ def main():
         "what": "every LayerNorm replaced by RMSNorm, rotary q/k positions instead of wpe; same shape and step",
         "kernels": {n: vb[n] for n in ("rope_kernel<1>", "rope_kernel<-1>", "rms_fwd_kernel", "rms_bwd_kernel")
                     if n in vb},
+    }
+    bf_gemms = [k for k in bkernels if k["name"].startswith("gemm_bf16_kernel")]
+    out["mixed_precision_bf16"] = {
+        "tokens_per_s": tokens / dt_bf, "ms_per_step": dt_bf * 1e3, "steps": 5,
+        "loss_first_last": [blosses[0], blosses[-1]],
+        "what": "every linear layer and the LM head multiply bf16 roundings of their operands on the bf16 "
+                "matrix cores (fp32 sums); fp32 master weights, AdamW, LayerNorm, attention, softmax/CE",
+        "roofline_bf16_gemm": roofline(bf_gemms) if bf_gemms else None,
+        "kernels": breakdown(bkernels, 1)[:16],
     }
     out["kernels"] = breakdown(all_kernels, max(1, args.warmup - 1))
     out["kernels_isolated"] = breakdown(isolated, 1)

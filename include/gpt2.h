@@ -71,6 +71,12 @@ int gpt2_param_layout(const gpt2_config* cfg, size_t off[GPT2_NUM_PARAM_TENSORS]
 /* Sizes (in floats) of the two arenas a model of batch shape (B, T) needs: the
  * activation arena and the gradient scratch arena.  Host-only. */
 int gpt2_arena_sizes(const gpt2_config* cfg, int B, int T, size_t* n_acts, size_t* n_grad_scratch);
+/* The same for a model built with gpt2_build_variant(..., variant): GPT2_VARIANT_BF16
+ * adds the bfloat16 operand copies (weights, their transposes, the linear layers' inputs
+ * and their transposes in the activation arena; the output-gradient copies in the
+ * scratch).  GPT2_EINVAL for an unknown bit. */
+int gpt2_arena_sizes_variant(const gpt2_config* cfg, int B, int T, int variant, size_t* n_acts,
+                             size_t* n_grad_scratch);
 
 /* The six caller-owned device buffers.  params, grads, m, v hold
  * gpt2_num_parameters floats each; acts and grad_scratch the sizes gpt2_arena_sizes
@@ -91,9 +97,9 @@ typedef struct gpt2_buffers {
 int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buffers* bufs,
                void* stream);
 
-/* Llama-style layer variants (the pages name Llama 2, Gemma and Mistral
- * as further llm.c targets, 新智元 article 纯CUDA也可训, but give no formulas, so the
- * published definitions are used).  A bit mask:
+/* Model variants, a bit mask.  The Llama-style layers: the pages name Llama 2, Gemma and
+ * Mistral as further llm.c targets (新智元 article 纯CUDA也可训) but give no formulas, so
+ * the published definitions are used:
  *   GPT2_VARIANT_RMSNORM: every LayerNorm becomes RMSNorm, y = x r w with
  *     r = 1/sqrt(mean(x^2) + 1e-5); no mean subtraction, no bias (ln1b, ln2b, lnfb take no
  *     part and keep zero gradients; their mean activations read 0);
@@ -101,11 +107,21 @@ int gpt2_build(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buff
  *     every head of q and k the pair (2i, 2i+1) at position t is rotated by
  *     t * 10000^(-2i/hs); the qkv activation then holds the rotated q and k.  Needs an
  *     even head size.
+ * Mixed precision, the pages' stated next step for llm.c (新智元 article 纯CUDA也可训;
+ * "OpenAI创始大神手搓千行C代码训练GPT", opening):
+ *   GPT2_VARIANT_BF16: every linear layer and the LM head multiply the bfloat16 roundings
+ *     (nearest, ties to even) of their two operands on the bf16 matrix cores, summing the
+ *     products in fp32: forward input and weight; backward output gradient and weight
+ *     (dgrad), output gradient and input (wgrad).  Bias gradients sum the unrounded fp32
+ *     output gradient.  Parameters, gradients, AdamW moments, every activation and every
+ *     other operation (LayerNorm, attention, GELU, softmax, cross-entropy, AdamW) stay
+ *     fp32.  Needs C a multiple of 8, and the larger arenas gpt2_arena_sizes_variant gives.
  * The parameter layout, buffers and every other call are those of gpt2_build (variant 0).
- * Returns as gpt2_build, and GPT2_EINVAL for an unknown bit or an odd head size with
- * GPT2_VARIANT_ROPE. */
+ * Returns as gpt2_build, and GPT2_EINVAL for an unknown bit, an odd head size with
+ * GPT2_VARIANT_ROPE or C not a multiple of 8 with GPT2_VARIANT_BF16. */
 #define GPT2_VARIANT_RMSNORM 1
 #define GPT2_VARIANT_ROPE 2
+#define GPT2_VARIANT_BF16 4
 int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const gpt2_buffers* bufs, void* stream,
                        int variant);
 

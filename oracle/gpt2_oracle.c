@@ -719,12 +719,12 @@ typedef struct oracle_gpt2 {
     real* dqkvr;
 } oracle_gpt2;
 
-/* Llama-style layer variants (SURVEY row f4): RMSNorm in place of every LayerNorm (the
+/* Llama-style layer variants: RMSNorm in place of every LayerNorm (the
  * LayerNorm biases then take no part and keep zero gradients), and rotary position
  * embedding on q and k in place of the position rows (wpe then takes no part). */
 #define ORACLE_VARIANT_RMSNORM 1
 #define ORACLE_VARIANT_ROPE 2
-/* Mixed precision: every linear layer and the LM head multiply the
+/* Mixed precision (bfloat16 rounding defined at oracle_bf16_round): every linear layer and the LM head multiply the
  * bfloat16 roundings of their two operands (input and weight forward; output gradient
  * and weight, or output gradient and input, backward), the products summed exactly;
  * the bias gradient sums the unrounded output gradient.  Everything else -- the fp32

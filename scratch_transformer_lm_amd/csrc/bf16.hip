@@ -1,0 +1,179 @@
+// bfloat16 operand copies for the mixed-precision variant.
+//
+// The pages name mixed precision as llm.c's next step (新智元 article "千行C代码训完
+// GPT-2", 纯CUDA也可训; "OpenAI创始大神手搓千行C代码训练GPT", opening).  Here every
+// linear layer and the LM head multiply bfloat16 roundings of their operands on the
+// matrix cores; master weights, activations and everything else stay fp32.  The bf16
+// GEMM wants both operands k-contiguous, so each operand is written once as a bf16 copy
+// in the layout its products read:
+//   forward:   X (rows, in) and W (out, in) as they are;
+//   dgrad:     dY (rows, out) as it is, W transposed (in, out);
+//   wgrad:     dY and X transposed (out, rows) and (in, rows), rows padded to 64 with
+//              zeros, since k runs over the rows.
+// One 64x64-tile kernel reads an fp32 tensor once and writes the straight copy, the
+// transposed copy (through LDS) and, for an output gradient, the bias gradient's column
+// sums per 64-row block (the bias gradient is summed from the unrounded fp32 values).
+// The LM head's output gradient, softmax minus one-hot over the rows' log-sum-exp, is
+// formed by the same kernel from the logits.  All of these kernels are bound by HBM.
+#include "common.h"
+#include "kernels.h"
+#include "prof.h"
+
+namespace gpt2k {
+
+namespace {
+
+constexpr int TILE = 64, CT_THREADS = 256, LDT = TILE + 1;
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs)
+GPT2_DEV uint32_t bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+GPT2_DEV uint32_t pack2(float lo, float hi) { return bf16_bits(lo) | (bf16_bits(hi) << 16); }
+
+struct XentArgs {
+    const float* lse;
+    const int32_t* targets;
+    float scale;
+    int V;
+};
+
+// Grid (column tiles, row tiles over rows rounded up to 64, batch).  XENT: the input is
+// the logits and each element becomes its loss gradient first.
+template <bool XENT>
+__global__ __launch_bounds__(CT_THREADS) void cast_tile_kernel(CastArgs a, XentArgs xa) {
+    __shared__ float tile[TILE][LDT];
+    const int t = threadIdx.x;
+    const int c0 = blockIdx.x * TILE, r0 = blockIdx.y * TILE, z = blockIdx.z;
+    const float* x = a.x + (long)z * a.sx;
+    // load: 16 threads per row (4 columns each), 16 rows per pass
+    const int c4 = t & 15, rr = t >> 4;
+    const int col = c0 + 4 * c4;
+#pragma unroll
+    for (int j = 0; j < TILE / 16; j++) {
+        const int row = rr + 16 * j, r = r0 + row;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < a.rows && col < a.cols) {
+            v = *reinterpret_cast<const float4*>(x + (long)r * a.ldx + col);
+            if (XENT) {
+                const float l = xa.lse[r];
+                const int tg = xa.targets[r];
+                float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int c = col + i;
+                    e[i] = c < xa.V ? (__expf(e[i] - l) - (c == tg ? 1.f : 0.f)) * xa.scale : 0.f;
+                }
+                v = make_float4(e[0], e[1], e[2], e[3]);
+            }
+            if (a.xb) {
+                uint2 o;
+                o.x = pack2(v.x, v.y);
+                o.y = pack2(v.z, v.w);
+                *reinterpret_cast<uint2*>(a.xb + (long)z * a.sb + (long)r * a.ldb + col) = o;
+            }
+        }
+        tile[row][4 * c4 + 0] = v.x;
+        tile[row][4 * c4 + 1] = v.y;
+        tile[row][4 * c4 + 2] = v.z;
+        tile[row][4 * c4 + 3] = v.w;
+    }
+    __syncthreads();
+    if (a.xt) {
+        // transposed: thread (cc, s) writes rows 16s..16s+15 of column cc as 16 bf16
+        const int cc = t >> 2, s = t & 3;
+        if (c0 + cc < a.cols) {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) w[i] = pack2(tile[16 * s + 2 * i][cc], tile[16 * s + 2 * i + 1][cc]);
+            uint4* q = reinterpret_cast<uint4*>(a.xt + (long)z * a.st + (long)(c0 + cc) * a.ldt + r0 + 16 * s);
+            q[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            q[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+    }
+    if (a.bpart && t < TILE && c0 + t < a.cols) {
+        float s = 0.f;
+        for (int i = 0; i < TILE; i++) s += tile[i][t];
+        a.bpart[(long)blockIdx.y * a.cols + c0 + t] = s;
+    }
+}
+
+__global__ void bias_reduce_kernel(float* db, const float* bpart, int nrb, int cols) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= cols) return;
+    float s = 0.f;
+    for (int rb = 0; rb < nrb; rb++) s += bpart[(long)rb * cols + c];
+    db[c] += s;
+}
+
+__global__ void cast_flat_kernel(uint2* xb, const float4* x, size_t n4) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+        const float4 v = x[i];
+        xb[i] = make_uint2(pack2(v.x, v.y), pack2(v.z, v.w));
+    }
+}
+
+bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+long pad64(long n) { return (n + TILE - 1) / TILE * TILE; }
+
+template <bool XENT>
+hipError_t launch_cast(const CastArgs& a, const XentArgs& xa, hipStream_t st, const char* name) {
+    if (a.rows < 0 || a.cols < 0 || a.cols % 4 || a.ldx % 4 || a.ldx < a.cols || a.batch < 1 || !a.x || !a16(a.x))
+        return hipErrorInvalidValue;
+    if (a.xb && (a.ldb % 8 || a.ldb < a.cols || !a16(a.xb))) return hipErrorInvalidValue;
+    if (a.xt && (a.ldt % 8 || a.ldt < pad64(a.rows) || !a16(a.xt))) return hipErrorInvalidValue;
+    if (a.rows == 0 || a.cols == 0) return hipSuccess;
+    const dim3 grid((unsigned)((a.cols + TILE - 1) / TILE), (unsigned)(pad64(a.rows) / TILE), (unsigned)a.batch);
+    const double n = (double)a.rows * a.cols * a.batch;
+    ProfScope ps(st, name, 0.0, n * (4.0 + (a.xb ? 2.0 : 0.0) + (a.xt ? 2.0 : 0.0)));
+    hipLaunchKernelGGL((cast_tile_kernel<XENT>), grid, dim3(CT_THREADS), 0, st, a, xa);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bias_partial_floats(int rows, int cols) { return (size_t)((rows + TILE - 1) / TILE) * (size_t)cols; }
+
+hipError_t cast_bf16(const CastArgs& a, hipStream_t st) {
+    return launch_cast<false>(a, XentArgs{nullptr, nullptr, 0.f, 0}, st, "cast_tile_kernel<false>");
+}
+
+hipError_t bias_reduce(float* db, const float* bpart, int rows, int cols, hipStream_t st) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    const int nrb = (rows + TILE - 1) / TILE;
+    ProfScope ps(st, "bias_reduce_kernel", 0.0, 4.0 * ((double)nrb * cols + 2.0 * cols));
+    hipLaunchKernelGGL(bias_reduce_kernel, dim3((cols + 255) / 256), dim3(256), 0, st, db, bpart, nrb, cols);
+    return hipGetLastError();
+}
+
+hipError_t cast_bf16_flat(uint16_t* xb, const float* x, size_t n, hipStream_t st) {
+    if (n % 4 || !a16(x) || ((uintptr_t)xb & 7)) return hipErrorInvalidValue;
+    if (n == 0) return hipSuccess;
+    const size_t n4 = n / 4;
+    const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 4096);
+    ProfScope ps(st, "cast_flat_kernel", 0.0, 6.0 * (double)n);
+    hipLaunchKernelGGL(cast_flat_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<uint2*>(xb),
+                       reinterpret_cast<const float4*>(x), n4);
+    return hipGetLastError();
+}
+
+hipError_t xent_grad_bf16(uint16_t* db, uint16_t* dt, long ldt, const float* logits, long Vp, const float* lse,
+                          const int32_t* targets, float scale, int N, int V, hipStream_t st) {
+    if (Vp < V || Vp % 64 || !lse || !targets) return hipErrorInvalidValue;
+    CastArgs a{};
+    a.x = logits;
+    a.ldx = Vp;
+    a.xb = db;
+    a.ldb = Vp;
+    a.xt = dt;
+    a.ldt = ldt;
+    a.rows = N;
+    a.cols = (int)Vp;
+    a.batch = 1;
+    return launch_cast<true>(a, XentArgs{lse, targets, scale, V}, st, "cast_tile_kernel<true>");
+}
+
+}  // namespace gpt2k

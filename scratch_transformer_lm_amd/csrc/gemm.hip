@@ -35,6 +35,7 @@
 #include <algorithm>
 #include <cmath>
 #include <string>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -65,6 +66,7 @@ constexpr int SLOT_BIAS = BM * 128;            // partial slot: tile, then its b
 constexpr int SLOT_FLOATS = SLOT_BIAS + BM;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // EPI_DLOGITS: LM-head dgrad whose A held s * softmax only; the one-hot part of dlogits,
 // s * onehot(target) . W = s * W[target], is subtracted here.
@@ -388,9 +390,15 @@ GPT2_DEV void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
 }
 
-template <bool A_K, bool B_K, int EPI, bool XF, int BN>
-__global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
+// BF: both operands are bfloat16 (mixed-precision variant), addressed as float pairs: a
+// row of K bf16 values is a row of K/2 floats, so the k-tiles, their LDS layout and the
+// transfers are exactly those of the fp32 k-contiguous case, and each 16-float fragment
+// group (16 bytes per lane = 8 bf16) feeds one v_mfma_f32_16x16x32_bf16 per block
+// instead of four fp32 steps.
+template <bool A_K, bool B_K, int EPI, bool XF, int BN, bool BF>
+GPT2_DEV void gemm_body(const Params& p) {
     static_assert(BN == 128 || (BN == 96 && A_K), "96-wide tiles take 32-wide k-tiles");
+    static_assert(!BF || (A_K && B_K && !XF), "bf16 operands are both k-contiguous");
     constexpr int WN = BN / 2, NB = BN / 32;
     constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
     constexpr int BK = KTile<A_K>::BK, STAGES = KTile<A_K>::STAGES;
@@ -525,8 +533,39 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
             }
         }
 
+        // bf16 k-tile: BK/16 groups of 32 bf16, one MFMA per block and group
+        auto compute_bf16 = [&](int buf) {
+            const float* Sa = smem + buf * STAGE_FLOATS;
+            const float* Sb = Sa + A_FLOATS;
+#pragma unroll
+            for (int g = 0; g < BK / 16; g++) {
+                bf16x8 fa[4], fb[NB];
+#pragma unroll
+                for (int a = 0; a < 4; a++) {
+                    const int row = wm + 16 * a + li;
+                    fa[a] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const float4*>(
+                                                           Sa + row * BK + (((4 * g + grp) ^ kswz<BK>(row)) << 2)));
+                }
+#pragma unroll
+                for (int b = 0; b < NB; b++) {
+                    const int row = wn + 16 * b + li;
+                    fb[b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const float4*>(
+                                                           Sb + row * BK + (((4 * g + grp) ^ kswz<BK>(row)) << 2)));
+                }
+#pragma unroll
+                for (int a = 0; a < 4; a++)
+#pragma unroll
+                    for (int b = 0; b < NB; b++)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+            }
+        };
+
         // one k-tile: BK/16 groups of 16 k, each 4 MFMA steps over this wave's blocks
         auto compute = [&](int buf, int kstep) {
+            if constexpr (BF) {
+                compute_bf16(buf);
+                return;
+            }
             const float* Sa = smem + buf * STAGE_FLOATS;
             const float* Sb = Sa + A_FLOATS;
             const int k0 = kstep * BK;
@@ -649,6 +688,16 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
     }
 }
 
+template <bool A_K, bool B_K, int EPI, bool XF, int BN>
+__global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
+    gemm_body<A_K, B_K, EPI, XF, BN, false>(p);
+}
+
+template <int EPI, int BN>
+__global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(Params p) {
+    gemm_body<true, true, EPI, false, BN, true>(p);
+}
+
 // Four blocks per range boundary that falls strictly inside a tile, one per row of
 // 16x16 blocks (a) of the waves' sub-tiles; for the lowest such boundary of a tile they
 // add that tile's partials in k order and run the epilogue.
@@ -746,6 +795,12 @@ const char* gemm_name() {
 }
 
 template <int EPI, int BN>
+const char* bf16_name() {
+    static const std::string s = "gemm_bf16_kernel<" + std::to_string(EPI) + ", " + std::to_string(BN) + ">";
+    return s.c_str();
+}
+
+template <int EPI, int BN>
 const char* fixup_name() {
     static const std::string s = "gemm_fixup_kernel<" + std::to_string(EPI) + ", " + std::to_string(BN) + ">";
     return s.c_str();
@@ -793,7 +848,7 @@ void schedule(Params& p, long tiles, int split) {
     if (p.R == 0) p.G = p.nr;
 }
 
-template <bool A_K, bool B_K, int EPI, bool XF, int BN>
+template <bool A_K, bool B_K, int EPI, bool XF, int BN, bool BF = false>
 hipError_t launch(Params& p, hipStream_t st, int split) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
@@ -810,9 +865,11 @@ hipError_t launch(Params& p, hipStream_t st, int split) {
                           EPI == EPI_DLOGITS) ? mn : 0.0;
     {
         // algorithmic work: 2MNK flops; operands read once, C written (and read for += / aux)
-        ProfScope ps(st, gemm_name<A_K, B_K, EPI, XF, BN>(), 2.0 * mn * p.K,
+        // (bf16: p.K counts float pairs, so the flops double and the operand bytes match)
+        ProfScope ps(st, BF ? bf16_name<EPI, BN>() : gemm_name<A_K, B_K, EPI, XF, BN>(), (BF ? 4.0 : 2.0) * mn * p.K,
                      4.0 * ((double)p.M * p.K + (double)p.N * p.K + mn + extra));
-        hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF, BN>), dim3(p.G), dim3(NT), 0, st, p);
+        if constexpr (BF) hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BN>), dim3(p.G), dim3(NT), 0, st, p);
+        else hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF, BN>), dim3(p.G), dim3(NT), 0, st, p);
     }
     const double slot = (double)BM * BN + BM;
     if (p.S > 1) {
@@ -963,6 +1020,43 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
         return launch<false, false, EPI_ACCUM, true, 128>(p, st, 0);
     }
     return launch<false, false, EPI_ACCUM, false, 128>(p, st, 0);
+}
+
+hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
+                     int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
+                     hipStream_t st) {
+    if (K % 2 || lda % 8 || ldb % 8 || lda < K || ldb < K || !aligned16(a) || !aligned16(b)) return hipErrorInvalidValue;
+    Params p{};
+    p.M = M;
+    p.N = N;
+    p.K = K / 2;  // float pairs
+    p.A = reinterpret_cast<const float*>(a);
+    p.lda = lda / 2;
+    p.B = reinterpret_cast<const float*>(b);
+    p.ldb = ldb / 2;
+    p.C = c;
+    p.ldc = ldc;
+    p.bias = bias;
+    p.aux = aux;
+    p.ldaux = ldaux;
+    p.pre = pre;
+    p.ldpre = ldc;
+    p.partial = partial;
+    const int bn = tile_n(M, N);
+    auto go = [&](auto epi_c) -> hipError_t {
+        constexpr int E = decltype(epi_c)::value;
+        if (bn == 96) return launch<true, true, E, false, 96, true>(p, st, pick_split<true, 96>(p.M, p.N, p.K));
+        return launch<true, true, E, false, 128, true>(p, st, pick_split<true, 128>(p.M, p.N, p.K));
+    };
+    switch (epi) {
+        case BF16_STORE: return go(std::integral_constant<int, EPI_STORE>{});
+        case BF16_BIAS: return go(std::integral_constant<int, EPI_BIAS>{});
+        case BF16_BIAS_RESID: return aux ? go(std::integral_constant<int, EPI_BIAS_RESID>{}) : hipErrorInvalidValue;
+        case BF16_BIAS_GELU: return pre ? go(std::integral_constant<int, EPI_BIAS_GELU>{}) : hipErrorInvalidValue;
+        case BF16_ACCUM: return go(std::integral_constant<int, EPI_ACCUM>{});
+        case BF16_GELU_BWD: return aux ? go(std::integral_constant<int, EPI_GELU_BWD>{}) : hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace gpt2k

@@ -60,6 +60,16 @@ struct ActInfo {
     size_t off, layer_stride, cols, ld;
 };
 
+// bfloat16 copies of the mixed-precision variant: in the activation arena the weights as
+// stored (W*), transposed (WT*) and the linear layers' inputs, straight and transposed
+// (per layer); in the scratch the output gradients (one straight buffer, a transposed one
+// per kind) and the LM head's.  Transposes are (cols, rows rounded up to 64).
+enum { BW_Q, BW_A, BW_F, BW_P, BW_WTE, BWT_Q, BWT_A, BWT_F, BWT_P, BWT_WTE, BA_LN1, BA_LN1T, BA_ATTY, BA_ATTYT,
+       BA_LN2, BA_LN2T, BA_FCHG, BA_FCHGT, BA_LNF, BA_LNFT, NBA };
+enum { BS_DY, BS_DREST, BS_DFCHT, BS_DQKVT, BS_DLOG, BS_DLOGT, NBS };
+
+size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
+
 struct Layout {
     size_t BT, Vp;
     ActInfo a[GPT2_NUM_ACTS];
@@ -67,9 +77,11 @@ struct Layout {
     size_t n_acts;
     // grad_scratch
     size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, sample, rope, n_scratch;
+    // mixed precision: offsets (floats) of the bf16 arrays, per-layer strides (bf16 elements)
+    size_t ba[NBA], ba_l[NBA], bs[NBS], bpart;
 };
 
-Layout make_layout(const gpt2_config* c, int B, int T) {
+Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     Layout y{};
     const size_t C = c->channels, L = c->num_layers, NH = c->num_heads, V = c->vocab_size;
     const size_t BT = (size_t)B * T;
@@ -105,6 +117,20 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     o += align_up(BT);
     y.tok_tgt = o;
     o += align_up(BT);
+    if (variant & GPT2_VARIANT_BF16) {
+        const size_t BTp = pad64(BT);
+        // (id, layers, elements per layer)
+        const size_t spec[NBA][2] = {
+            {L, 3 * C * C}, {L, C * C}, {L, 4 * C * C}, {L, 4 * C * C}, {1, V * C},
+            {L, C * pad64(3 * C)}, {L, C * pad64(C)}, {L, C * pad64(4 * C)}, {L, 4 * C * pad64(C)}, {1, C * y.Vp},
+            {L, BT * C}, {L, C * BTp}, {L, BT * C}, {L, C * BTp}, {L, BT * C}, {L, C * BTp},
+            {L, BT * 4 * C}, {L, 4 * C * BTp}, {1, BT * C}, {1, C * BTp}};
+        for (int i = 0; i < NBA; i++) {
+            y.ba[i] = o;
+            y.ba_l[i] = spec[i][1];
+            o += align_up((spec[i][0] * spec[i][1] + 1) / 2);
+        }
+    }
     y.n_acts = o;
 
     size_t s = HDR_WORDS;
@@ -128,6 +154,12 @@ Layout make_layout(const gpt2_config* c, int B, int T) {
     y.partial_w = take(gemm_partial_floats());  // split tiles of the weight-gradient stream
     y.sample = take(3 * BT);                      // sampling requests: rows, coins, tokens
     y.rope = take(rope_table_floats(c->max_seq_len, (int)(C / NH)));  // rotary variant's (cos, sin) table
+    if (variant & GPT2_VARIANT_BF16) {
+        const size_t BTp = pad64(BT);
+        const size_t n[NBS] = {BT * 4 * C, C * BTp, 4 * C * BTp, 3 * C * BTp, BT * y.Vp, y.Vp * BTp};
+        for (int i = 0; i < NBS; i++) y.bs[i] = take((n[i] + 1) / 2);
+        y.bpart = take(bias_partial_floats((int)BT, (int)(4 * C)));
+    }
     y.n_scratch = s;
     return y;
 }
@@ -185,6 +217,47 @@ int* flags(gpt2* g) { return reinterpret_cast<int*>(g->buf.grad_scratch + HDR_FL
 
 bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+bool bf_on(const gpt2* g) { return (g->variant & GPT2_VARIANT_BF16) != 0; }
+uint16_t* BA(gpt2* g, int id, int l = 0) {
+    return reinterpret_cast<uint16_t*>(g->buf.acts + g->lay.ba[id]) + (size_t)l * g->lay.ba_l[id];
+}
+uint16_t* BS(gpt2* g, int id) { return reinterpret_cast<uint16_t*>(g->buf.grad_scratch + g->lay.bs[id]); }
+
+// bf16 copies of an fp32 (rows, cols) tensor: straight (xb) and transposed (xt, rows
+// padded to 64 with zeros), and the bias gradient's per-block column sums (bpart).
+hipError_t cast_rows(const float* x, int rows, int cols, uint16_t* xb, uint16_t* xt, float* bpart, hipStream_t st) {
+    CastArgs a{};
+    a.x = x;
+    a.ldx = cols;
+    a.xb = xb;
+    a.ldb = cols;
+    a.xt = xt;
+    a.ldt = (long)pad64(rows);
+    a.bpart = bpart;
+    a.rows = rows;
+    a.cols = cols;
+    a.batch = 1;
+    return cast_bf16(a, st);
+}
+
+// The same for `batch` weight matrices (OC, IC) stored back to back.
+hipError_t cast_weights(const float* w, int OC, int IC, int batch, uint16_t* wb, uint16_t* wt, hipStream_t st) {
+    CastArgs a{};
+    a.x = w;
+    a.ldx = IC;
+    a.xb = wb;
+    a.ldb = IC;
+    a.xt = wt;
+    a.ldt = (long)pad64(OC);
+    a.rows = OC;
+    a.cols = IC;
+    a.batch = batch;
+    a.sx = (long)OC * IC;
+    a.sb = (long)OC * IC;
+    a.st = (long)IC * (long)pad64(OC);
+    return cast_bf16(a, st);
+}
+
 // The block's normalisation: LayerNorm, or RMSNorm in the RMSNorm variant (its mean slot
 // then holds 0 and the LayerNorm bias takes no part, keeping a zero gradient).
 hipError_t norm_fwd(gpt2* g, float* y, float* mean, float* rstd, const float* x, const float* w, const float* b,
@@ -218,28 +291,60 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     HIPCHK(g, hipMemsetAsync(g->buf.grad_scratch, 0, HDR_WORDS * sizeof(float), st));
     HIPCHK(g, encoder_forward(A(g, GPT2_ACT_ENCODED), tok_in(g), P(g, P_WTE), rope_on(g) ? nullptr : P(g, P_WPE), B, T,
                               C, V, flags(g), st));
+    // Mixed precision: the weights' bf16 copies (as stored and transposed) are made from
+    // the current parameters at every forward; each linear layer's input gets its copies
+    // right after it is produced (the transposes serve the backward's weight gradients).
+    const bool bf = bf_on(g);
+    if (bf) {
+        HIPCHK(g, cast_weights(P(g, P_QKVW), 3 * C, C, L, BA(g, BW_Q), BA(g, BWT_Q), st));
+        HIPCHK(g, cast_weights(P(g, P_ATTPROJW), C, C, L, BA(g, BW_A), BA(g, BWT_A), st));
+        HIPCHK(g, cast_weights(P(g, P_FCW), 4 * C, C, L, BA(g, BW_F), BA(g, BWT_F), st));
+        HIPCHK(g, cast_weights(P(g, P_FCPROJW), C, 4 * C, L, BA(g, BW_P), BA(g, BWT_P), st));
+        HIPCHK(g, cast_weights(P(g, P_WTE), V, C, 1, BA(g, BW_WTE), BA(g, BWT_WTE), st));
+    }
+    // y = x . W^T + epilogue, in fp32 or on the bf16 copies xb, wb
+    auto linear = [&](int epi, float* out, long ldo, const float* x, const uint16_t* xb, const float* w,
+                      const uint16_t* wb, const float* bias, const float* resid, float* pre, int N, int K) {
+        if (bf) return gemm_bf16(epi, out, ldo, xb, K, wb, K, BT, N, K, bias, resid, ldo, pre, part, st);
+        return linear_forward(out, ldo, x, w, bias, resid, pre, BT, N, K, part, st);
+    };
     for (int l = 0; l < L; l++) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN1, l), A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), residual,
                            P(g, P_LN1W) + l * C, P(g, P_LN1B) + l * C, BT, C, st));
-        HIPCHK(g, linear_forward(A(g, GPT2_ACT_QKV, l), 3 * C, A(g, GPT2_ACT_LN1, l), P(g, P_QKVW) + (size_t)l * 3 * C * C,
-                                 P(g, P_QKVB) + l * 3 * C, nullptr, nullptr, BT, 3 * C, C, part, st));
+        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_LN1, l), BT, C, BA(g, BA_LN1, l), BA(g, BA_LN1T, l), nullptr, st));
+        HIPCHK(g, linear(BF16_BIAS, A(g, GPT2_ACT_QKV, l), 3 * C, A(g, GPT2_ACT_LN1, l), BA(g, BA_LN1, l),
+                         P(g, P_QKVW) + (size_t)l * 3 * C * C, BA(g, BW_Q, l), P(g, P_QKVB) + l * 3 * C, nullptr,
+                         nullptr, 3 * C, C));
         // rotary variant: q and k rotated in place (the stored qkv is the rotated one)
         if (rope_on(g)) HIPCHK(g, rope_forward(A(g, GPT2_ACT_QKV, l), S(g, g->lay.rope), B, T, C, NH, st));
         HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T, C, NH, st));
-        HIPCHK(g, linear_forward(A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), P(g, P_ATTPROJW) + (size_t)l * C * C,
-                                 P(g, P_ATTPROJB) + l * C, residual, nullptr, BT, C, C, part, st));
+        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_ATTY, l), BT, C, BA(g, BA_ATTY, l), BA(g, BA_ATTYT, l), nullptr, st));
+        HIPCHK(g, linear(BF16_BIAS_RESID, A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTY, l),
+                         P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BW_A, l), P(g, P_ATTPROJB) + l * C, residual,
+                         nullptr, C, C));
         HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN2, l), A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l),
                            A(g, GPT2_ACT_RESIDUAL2, l), P(g, P_LN2W) + l * C, P(g, P_LN2B) + l * C, BT, C, st));
-        HIPCHK(g, linear_forward(A(g, GPT2_ACT_FCH_GELU, l), 4 * C, A(g, GPT2_ACT_LN2, l), P(g, P_FCW) + (size_t)l * 4 * C * C,
-                                 P(g, P_FCB) + l * 4 * C, nullptr, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C, part, st));
-        HIPCHK(g, linear_forward(A(g, GPT2_ACT_RESIDUAL3, l), C, A(g, GPT2_ACT_FCH_GELU, l), P(g, P_FCPROJW) + (size_t)l * 4 * C * C,
-                                 P(g, P_FCPROJB) + l * C, A(g, GPT2_ACT_RESIDUAL2, l), nullptr, BT, C, 4 * C, part, st));
+        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_LN2, l), BT, C, BA(g, BA_LN2, l), BA(g, BA_LN2T, l), nullptr, st));
+        HIPCHK(g, linear(BF16_BIAS_GELU, A(g, GPT2_ACT_FCH_GELU, l), 4 * C, A(g, GPT2_ACT_LN2, l), BA(g, BA_LN2, l),
+                         P(g, P_FCW) + (size_t)l * 4 * C * C, BA(g, BW_F, l), P(g, P_FCB) + l * 4 * C, nullptr,
+                         A(g, GPT2_ACT_FCH, l), 4 * C, C));
+        if (bf)
+            HIPCHK(g, cast_rows(A(g, GPT2_ACT_FCH_GELU, l), BT, 4 * C, BA(g, BA_FCHG, l), BA(g, BA_FCHGT, l), nullptr, st));
+        HIPCHK(g, linear(BF16_BIAS_RESID, A(g, GPT2_ACT_RESIDUAL3, l), C, A(g, GPT2_ACT_FCH_GELU, l), BA(g, BA_FCHG, l),
+                         P(g, P_FCPROJW) + (size_t)l * 4 * C * C, BA(g, BW_P, l), P(g, P_FCPROJB) + l * C,
+                         A(g, GPT2_ACT_RESIDUAL2, l), nullptr, C, 4 * C));
     }
     HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LNF), A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD),
                        A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, st));
-    HIPCHK(g, linear_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT, V,
-                             C, part, st));
+    if (bf) {
+        HIPCHK(g, cast_rows(A(g, GPT2_ACT_LNF), BT, C, BA(g, BA_LNF), BA(g, BA_LNFT), nullptr, st));
+        HIPCHK(g, gemm_bf16(BF16_STORE, A(g, GPT2_ACT_LOGITS), Vp, BA(g, BA_LNF), C, BA(g, BW_WTE), C, BT, V, C, nullptr,
+                            nullptr, 0, nullptr, part, st));
+    } else {
+        HIPCHK(g, linear_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT,
+                                 V, C, part, st));
+    }
     HIPCHK(g, lse_xent_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LOGITS_LSE), A(g, GPT2_ACT_LOSSES),
                                targets ? tok_tgt(g) : nullptr, BT, V, flags(g), st));
     if (targets) HIPCHK(g, loss_mean(g->buf.grad_scratch + HDR_LOSS, A(g, GPT2_ACT_LOSSES), BT, st));
@@ -352,14 +457,53 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     hipStream_t su = g->backward_streams == 2 ? g->st_u : st;
     auto mark = [&](int e, hipStream_t s) { return hipEventRecord(g->ev[e], s); };
     auto after = [&](hipStream_t s, int e) { return hipStreamWaitEvent(s, g->ev[e], 0); };
-    HIPCHK(g, mark(EV_LM, st));
-    HIPCHK(g, after(sw, EV_LM));
-    HIPCHK(g, linear_wgrad(G(g, P_WTE), nullptr, logits, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part_w, sw, &xo));
-    // the one-hot part of dlogits: dwte[target] -= lnf / BT
-    if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, BT, sw));
-    else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, sw));
-    HIPCHK(g, mark(EV_W_LM, sw));
-    HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
+    // Mixed precision: every GEMM below multiplies bf16 copies.  dlogits is written once
+    // in bf16, straight and transposed; each output gradient dY gets its copies (and its
+    // bias gradient, from the fp32 values) on the main stream before its GEMMs, the
+    // transposed ones in buffers per kind that the events below protect exactly as they
+    // protect dY itself.
+    const bool bf = bf_on(g);
+    const long BTp = (long)pad64(BT);
+    float* bpart = bf ? S(g, g->lay.bpart) : nullptr;
+    uint16_t* dyb = bf ? BS(g, BS_DY) : nullptr;
+    auto grad_copies = [&](const float* dy, int n, uint16_t* yt, float* db) -> hipError_t {
+        const hipError_t e = cast_rows(dy, BT, n, dyb, yt, bpart, st);
+        return e != hipSuccess ? e : bias_reduce(db, bpart, BT, n, st);
+    };
+    // dW[M,N] += dY^T X (and, fp32 only, db += column sums of dY): dY (BT, M), X (BT, N)
+    auto wgrad = [&](float* dw, float* db, const float* dy, const uint16_t* yt, int M, const float* x,
+                     const uint16_t* xt, int N) {
+        if (bf) return gemm_bf16(BF16_ACCUM, dw, N, yt, BTp, xt, BTp, M, N, (int)BTp, nullptr, nullptr, 0, nullptr,
+                                 part_w, sw);
+        return linear_wgrad(dw, db, dy, M, x, M, N, BT, part_w, sw);
+    };
+    // dX[BT,N] = dY[BT,K] . W[K,N] (times gelu'(gelu_pre) if given); wt = bf16 W^T (N, K padded)
+    auto dgrad = [&](float* dx, const float* dy, int K, const float* w, const uint16_t* wt, int N,
+                     const float* gelu_pre) {
+        if (bf) return gemm_bf16(gelu_pre ? BF16_GELU_BWD : BF16_STORE, dx, N, dyb, K, wt, (long)pad64(K), BT, N, K,
+                                 nullptr, gelu_pre, N, nullptr, part, st);
+        return linear_dgrad(dx, dy, K, w, gelu_pre, BT, N, K, part, st);
+    };
+    if (bf) {
+        HIPCHK(g, xent_grad_bf16(BS(g, BS_DLOG), BS(g, BS_DLOGT), BTp, logits, Vp, A(g, GPT2_ACT_LOGITS_LSE),
+                                 tok_tgt(g), xo.scale, BT, V, st));
+        HIPCHK(g, mark(EV_LM, st));
+        HIPCHK(g, after(sw, EV_LM));
+        HIPCHK(g, gemm_bf16(BF16_ACCUM, G(g, P_WTE), C, BS(g, BS_DLOGT), BTp, BA(g, BA_LNFT), BTp, V, C, (int)BTp,
+                            nullptr, nullptr, 0, nullptr, part_w, sw));
+        HIPCHK(g, mark(EV_W_LM, sw));
+        HIPCHK(g, gemm_bf16(BF16_STORE, dln, C, BS(g, BS_DLOG), Vp, BA(g, BWT_WTE), Vp, BT, C, (int)Vp, nullptr, nullptr,
+                            0, nullptr, part, st));
+    } else {
+        HIPCHK(g, mark(EV_LM, st));
+        HIPCHK(g, after(sw, EV_LM));
+        HIPCHK(g, linear_wgrad(G(g, P_WTE), nullptr, logits, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part_w, sw, &xo));
+        // the one-hot part of dlogits: dwte[target] -= lnf / BT
+        if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, BT, sw));
+        else HIPCHK(g, embedding_scatter(G(g, P_WTE), V, C, tok_tgt(g), BT, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, sw));
+        HIPCHK(g, mark(EV_W_LM, sw));
+        HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
+    }
     HIPCHK(g, norm_bwd(g, dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
                        A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
     // Per layer, the weight gradients (dW += dY^T X, db) need only that layer's output
@@ -373,44 +517,48 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         const bool later = l < L - 1;  // the previous iteration's weight gradients exist
         // MLP projection: residual3 = residual2 + gelu(fch) . Wp^T + bp.
+        if (bf) HIPCHK(g, grad_copies(dres, C, BS(g, BS_DREST), G(g, P_FCPROJB) + l * C));
         HIPCHK(g, mark(EV_DRES_A, st));
         HIPCHK(g, after(sw, EV_DRES_A));
-        HIPCHK(g, linear_wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, G(g, P_FCPROJB) + l * C, dres, C, A(g, GPT2_ACT_FCH_GELU, l), C, 4 * C, BT,
-                               part_w, sw));
+        HIPCHK(g, wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, G(g, P_FCPROJB) + l * C, dres, BS(g, BS_DREST), C,
+                        A(g, GPT2_ACT_FCH_GELU, l), BA(g, BA_FCHGT, l), 4 * C));
         HIPCHK(g, mark(EV_W_FCPROJ, sw));
         if (later) HIPCHK(g, after(st, EV_W_FC));  // the fc wgrad above still reads dfch
-        HIPCHK(g, linear_dgrad(dfch, dres, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, A(g, GPT2_ACT_FCH, l), BT, 4 * C, C,
-                               part, st));
+        HIPCHK(g, dgrad(dfch, dres, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, BA(g, BWT_P, l), 4 * C,
+                        A(g, GPT2_ACT_FCH, l)));
         // MLP expansion: fch = ln2 . Wf^T + bf.
+        if (bf) HIPCHK(g, grad_copies(dfch, 4 * C, BS(g, BS_DFCHT), G(g, P_FCB) + l * 4 * C));
         HIPCHK(g, mark(EV_DFCH, st));
         HIPCHK(g, after(sw, EV_DFCH));
-        HIPCHK(g, linear_wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, G(g, P_FCB) + l * 4 * C, dfch, 4 * C, A(g, GPT2_ACT_LN2, l), 4 * C, C, BT,
-                               part_w, sw));
+        HIPCHK(g, wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, G(g, P_FCB) + l * 4 * C, dfch, BS(g, BS_DFCHT), 4 * C,
+                        A(g, GPT2_ACT_LN2, l), BA(g, BA_LN2T, l), C));
         HIPCHK(g, mark(EV_W_FC, sw));
-        HIPCHK(g, linear_dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, nullptr, BT, C, 4 * C, part, st));
+        HIPCHK(g, dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, BA(g, BWT_F, l), C, nullptr));
         HIPCHK(g, after(st, EV_W_FCPROJ));  // dres is about to change
         HIPCHK(g, norm_bwd(g, dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
                            P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C, true,
                            true, part, st));
         // Attention projection: residual2 = residual + atty . Wa^T + ba.
+        if (bf) HIPCHK(g, grad_copies(dres, C, BS(g, BS_DREST), G(g, P_ATTPROJB) + l * C));
         HIPCHK(g, mark(EV_DRES_B, st));
         HIPCHK(g, after(sw, EV_DRES_B));
-        HIPCHK(g, linear_wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, G(g, P_ATTPROJB) + l * C, dres, C, A(g, GPT2_ACT_ATTY, l), C, C, BT,
-                               part_w, sw));
+        HIPCHK(g, wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, G(g, P_ATTPROJB) + l * C, dres, BS(g, BS_DREST), C,
+                        A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTYT, l), C));
         HIPCHK(g, mark(EV_W_ATTPROJ, sw));
-        HIPCHK(g, linear_dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, nullptr, BT, C, C, part, st));
+        HIPCHK(g, dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BWT_A, l), C, nullptr));
         if (later) HIPCHK(g, after(st, EV_W_QKV));  // the qkv wgrad above still reads dqkv
         HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
                                      A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
         // rotary variant: attention gave the gradient of the rotated q and k; rotate it back
         if (rope_on(g)) HIPCHK(g, rope_backward(dqkv, S(g, g->lay.rope), B, T, C, NH, st));
+        if (bf) HIPCHK(g, grad_copies(dqkv, 3 * C, BS(g, BS_DQKVT), G(g, P_QKVB) + l * 3 * C));
         HIPCHK(g, mark(EV_DQKV, st));
         HIPCHK(g, after(sw, EV_DQKV));
-        HIPCHK(g, linear_wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, 3 * C, A(g, GPT2_ACT_LN1, l), 3 * C, C, BT,
-                               part_w, sw));
+        HIPCHK(g, wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, BS(g, BS_DQKVT), 3 * C,
+                        A(g, GPT2_ACT_LN1, l), BA(g, BA_LN1T, l), C));
         HIPCHK(g, mark(EV_W_QKV, sw));
-        HIPCHK(g, linear_dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, nullptr, BT, C, 3 * C, part, st));
+        HIPCHK(g, dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, BA(g, BWT_Q, l), C, nullptr));
         HIPCHK(g, after(st, EV_W_ATTPROJ));  // dres is about to change
         HIPCHK(g, norm_bwd(g, dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                            A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
@@ -465,10 +613,16 @@ int gpt2_param_layout(const gpt2_config* cfg, size_t off[NP], size_t len[NP]) {
 }
 
 int gpt2_arena_sizes(const gpt2_config* cfg, int B, int T, size_t* n_acts, size_t* n_grad_scratch) {
+    return gpt2_arena_sizes_variant(cfg, B, T, 0, n_acts, n_grad_scratch);
+}
+
+int gpt2_arena_sizes_variant(const gpt2_config* cfg, int B, int T, int variant, size_t* n_acts,
+                             size_t* n_grad_scratch) {
     if (!config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !n_acts || !n_grad_scratch)
         return GPT2_EINVAL;
+    if (variant & ~(GPT2_VARIANT_RMSNORM | GPT2_VARIANT_ROPE | GPT2_VARIANT_BF16)) return GPT2_EINVAL;
     if ((long)B * T > (1L << 30)) return GPT2_EINVAL;
-    const Layout y = make_layout(cfg, B, T);
+    const Layout y = make_layout(cfg, B, T, variant);
     *n_acts = y.n_acts;
     *n_grad_scratch = y.n_scratch;
     return GPT2_OK;
@@ -483,8 +637,9 @@ int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const g
     if (!out) return GPT2_EINVAL;
     *out = nullptr;
     if (!config_ok(cfg) || B <= 0 || T <= 0 || T > cfg->max_seq_len || !bufs) return GPT2_EINVAL;
-    if (variant & ~(GPT2_VARIANT_RMSNORM | GPT2_VARIANT_ROPE)) return GPT2_EINVAL;
+    if (variant & ~(GPT2_VARIANT_RMSNORM | GPT2_VARIANT_ROPE | GPT2_VARIANT_BF16)) return GPT2_EINVAL;
     if ((variant & GPT2_VARIANT_ROPE) && (cfg->channels / cfg->num_heads) % 2) return GPT2_EINVAL;
+    if ((variant & GPT2_VARIANT_BF16) && cfg->channels % 8) return GPT2_EINVAL;
     if ((long)B * T > (1L << 30)) return GPT2_EINVAL;
     const gpt2_buffers& b = *bufs;
     if (!b.params || !b.grads || !b.m || !b.v || !b.acts || !b.grad_scratch) return GPT2_EINVAL;
@@ -498,7 +653,7 @@ int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const g
     g->maxT = T;
     g->B = B;
     g->T = T;
-    g->lay = make_layout(cfg, B, T);
+    g->lay = make_layout(cfg, B, T, variant);
     g->st = (hipStream_t)stream;
     g->backward_streams = 2;
     g->variant = variant;

@@ -44,6 +44,49 @@ hipError_t linear_dgrad(float* din, const float* dout, long ld_dout, const float
 hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout, const float* inp, int M,
                         int N, int K, float* partial, hipStream_t st, const XentOperand* xent = nullptr);
 
+// Mixed precision: C[M,N] (ld ldc, fp32) = A[M,K] . B[N,K]^T with both operands bfloat16
+// bit patterns, k-contiguous (leading dimensions lda, ldb multiples of 8, K even; pad
+// columns of a padded K must be zero), products summed in fp32, then the epilogue:
+//   BF16_STORE: C = .;  BF16_BIAS: C = . + bias;  BF16_BIAS_RESID: C = aux + (. + bias);
+//   BF16_BIAS_GELU: pre = . + bias, C = gelu(pre);  BF16_ACCUM: C += .;
+//   BF16_GELU_BWD: C = . * gelu'(aux).   aux has leading dimension ldaux, pre ldc.
+enum { BF16_STORE = 0, BF16_BIAS, BF16_BIAS_RESID, BF16_BIAS_GELU, BF16_ACCUM, BF16_GELU_BWD };
+hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
+                     int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
+                     hipStream_t st);
+
+// ---- bfloat16 operand copies (bf16.hip) -----------------------------------------------
+// Rounding is to nearest, ties to even.  x is (rows, cols) fp32 with leading dimension
+// ldx (a multiple of 4); batch copies at strides sx / sb / st (elements) of x / xb / xt.
+//   xb (optional): (rows, cols) bf16, leading dimension ldb (a multiple of 8).
+//   xt (optional): the transpose (cols, rows_pad) bf16, leading dimension ldt >= rows_pad,
+//     rows_pad = rows rounded up to 64, columns rows..rows_pad-1 zero.
+//   bpart (optional): per 64-row block rb, bpart[rb * cols + c] = sum of x[r, c] over its
+//     rows in order; bias_reduce then adds them into db in block order.
+// cols must be a multiple of 4.
+struct CastArgs {
+    const float* x;
+    long ldx;
+    uint16_t* xb;
+    long ldb;
+    uint16_t* xt;
+    long ldt;
+    float* bpart;
+    int rows, cols;
+    int batch;
+    long sx, sb, st;
+};
+hipError_t cast_bf16(const CastArgs& a, hipStream_t st);
+size_t bias_partial_floats(int rows, int cols);
+hipError_t bias_reduce(float* db, const float* bpart, int rows, int cols, hipStream_t st);
+// Flat copy: xb[i] = bf16(x[i]), n a multiple of 4.
+hipError_t cast_bf16_flat(uint16_t* xb, const float* x, size_t n, hipStream_t st);
+// The LM head's output gradient in bf16: d[r, c] = (exp(z[r, c] - lse[r]) - [c == targets[r]]) * scale for
+// c < V, 0 for V <= c < Vp, written row-major (N, Vp) to db and transposed (Vp, N_pad) to dt
+// (N_pad = N rounded up to 64, zero beyond N).  logits has leading dimension Vp.
+hipError_t xent_grad_bf16(uint16_t* db, uint16_t* dt, long ldt, const float* logits, long Vp, const float* lse,
+                          const int32_t* targets, float scale, int N, int V, hipStream_t st);
+
 // ---- LayerNorm (norm.hip) -----------------------------------------------------------
 hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,
                              const float* b, int N, int C, float eps, hipStream_t st);

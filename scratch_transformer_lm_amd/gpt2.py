@@ -65,6 +65,8 @@ def load() -> ct.CDLL:
     lib.gpt2_param_layout.restype = i
     lib.gpt2_arena_sizes.argtypes = [C, i, i, ct.POINTER(sz), ct.POINTER(sz)]
     lib.gpt2_arena_sizes.restype = i
+    lib.gpt2_arena_sizes_variant.argtypes = [C, i, i, i, ct.POINTER(sz), ct.POINTER(sz)]
+    lib.gpt2_arena_sizes_variant.restype = i
     lib.gpt2_build.argtypes = [ct.POINTER(P), C, i, i, ct.POINTER(Buffers), P]
     lib.gpt2_build.restype = i
     lib.gpt2_build_variant.argtypes = [ct.POINTER(P), C, i, i, ct.POINTER(Buffers), P, i]
@@ -139,12 +141,12 @@ def param_layout(shape):
     return [int(x) for x in off], [int(x) for x in ln]
 
 
-def arena_sizes(shape, B: int, T: int):
+def arena_sizes(shape, B: int, T: int, variant: int = 0):
     c = config(shape)
     a, s = ct.c_size_t(), ct.c_size_t()
-    rc = load().gpt2_arena_sizes(ct.byref(c), B, T, ct.byref(a), ct.byref(s))
+    rc = load().gpt2_arena_sizes_variant(ct.byref(c), B, T, variant, ct.byref(a), ct.byref(s))
     if rc != GPT2_OK:
-        raise GPT2Error(rc, "gpt2_arena_sizes")
+        raise GPT2Error(rc, "gpt2_arena_sizes_variant")
     return a.value, s.value
 
 
@@ -167,7 +169,7 @@ class GPT2:
         n = num_parameters(shape)
         if n == 0:
             raise GPT2Error(GPT2_EINVAL, "gpt2_num_parameters")
-        na, ns = arena_sizes(shape, B, T)
+        na, ns = arena_sizes(shape, B, T, variant)
         f32 = torch.float32
         self.params = torch.empty(n, dtype=f32, device=self.device)
         self.grads = torch.empty(n, dtype=f32, device=self.device)
@@ -294,7 +296,8 @@ class GPT2:
 
 
 GEMM_TILES_AUTO, GEMM_TILES_128, GEMM_TILES_96 = 0, 1, 2
-VARIANT_RMSNORM, VARIANT_ROPE = 1, 2  # gpt2_build_variant bits (Llama-style layers)
+# gpt2_build_variant bits: Llama-style layers (RMSNorm, rotary positions), mixed precision
+VARIANT_RMSNORM, VARIANT_ROPE, VARIANT_BF16 = 1, 2, 4
 
 
 def set_gemm_tiles(policy: int) -> None:

@@ -105,8 +105,27 @@ def test_build_variant_argument_checks_need_no_gpu():
     cfg = G.config(S.TINY.model)
     h = ct.c_void_p()
     bufs = G.Buffers()
+    assert lib.gpt2_build_variant(ct.byref(h), ct.byref(cfg), 2, 32, ct.byref(bufs), None, 8) == G.GPT2_EINVAL
     assert lib.gpt2_build_variant(ct.byref(h), ct.byref(cfg), 2, 32, ct.byref(bufs), None, 4) == G.GPT2_EINVAL
     assert lib.gpt2_build_variant(None, ct.byref(cfg), 2, 32, ct.byref(bufs), None, 3) == G.GPT2_EINVAL
+
+
+@pytest.mark.parametrize("w,B,T", [(S.TINY, 2, 32), (S.GPT2_124M, 8, 1024), (S.GPT2_124M, 3, 100)])
+def test_bf16_variant_arena_sizes(w, B, T):
+    """The mixed-precision arenas hold at least the bf16 copies: weights straight and
+    transposed, the four per-layer linear inputs and lnf straight and transposed (rows
+    padded to 64); the scratch the output-gradient and logits-gradient copies."""
+    m = w.model
+    L, C, V = m.num_layers, m.channels, m.vocab_size
+    BT, BTp = B * T, -(-B * T // 64) * 64
+    a0, s0 = G.arena_sizes(m, B, T)
+    a4, s4 = G.arena_sizes(m, B, T, G.VARIANT_BF16)
+    weights = L * 12 * C * C + V * C
+    acts = L * 7 * C * (BT + BTp) + C * (BT + BTp)
+    assert (a4 - a0) * 2 >= 2 * weights + acts
+    assert (s4 - s0) * 2 >= 4 * C * BT + 8 * C * BTp + V * (BT + BTp)
+    with pytest.raises(G.GPT2Error):
+        G.arena_sizes(m, B, T, 8)
 
 
 def test_backward_update_argument_checks_need_no_gpu():
