@@ -100,12 +100,29 @@ __global__ __launch_bounds__(CT_THREADS) void cast_tile_kernel(CastArgs a, XentA
     }
 }
 
-__global__ void bias_reduce_kernel(float* db, const float* bpart, int nrb, int cols) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= cols) return;
+// db[c] += sum over row blocks of bpart[rb][c]: 64 columns per block, four threads per
+// column each summing every fourth row block (eight loads in flight), then the four
+// partial sums added in a fixed order.
+constexpr int BR_GROUPS = 4, BR_UNROLL = 8;
+__global__ __launch_bounds__(TILE * BR_GROUPS) void bias_reduce_kernel(float* db, const float* bpart, int nrb, int cols) {
+    __shared__ float part[BR_GROUPS][TILE];
+    const int cl = threadIdx.x % TILE, q = threadIdx.x / TILE;
+    const int c = blockIdx.x * TILE + cl;
     float s = 0.f;
-    for (int rb = 0; rb < nrb; rb++) s += bpart[(long)rb * cols + c];
-    db[c] += s;
+    if (c < cols) {
+        int rb = q;
+        for (; rb + BR_GROUPS * (BR_UNROLL - 1) < nrb; rb += BR_GROUPS * BR_UNROLL) {
+            float v[BR_UNROLL];
+#pragma unroll
+            for (int u = 0; u < BR_UNROLL; u++) v[u] = bpart[(long)(rb + BR_GROUPS * u) * cols + c];
+#pragma unroll
+            for (int u = 0; u < BR_UNROLL; u++) s += v[u];
+        }
+        for (; rb < nrb; rb += BR_GROUPS) s += bpart[(long)rb * cols + c];
+    }
+    part[q][cl] = s;
+    __syncthreads();
+    if (q == 0 && c < cols) db[c] += ((part[0][cl] + part[1][cl]) + part[2][cl]) + part[3][cl];
 }
 
 __global__ void cast_flat_kernel(uint2* xb, const float4* x, size_t n4) {
@@ -145,7 +162,8 @@ hipError_t bias_reduce(float* db, const float* bpart, int rows, int cols, hipStr
     if (rows <= 0 || cols <= 0) return hipSuccess;
     const int nrb = (rows + TILE - 1) / TILE;
     ProfScope ps(st, "bias_reduce_kernel", 0.0, 4.0 * ((double)nrb * cols + 2.0 * cols));
-    hipLaunchKernelGGL(bias_reduce_kernel, dim3((cols + 255) / 256), dim3(256), 0, st, db, bpart, nrb, cols);
+    hipLaunchKernelGGL(bias_reduce_kernel, dim3((cols + TILE - 1) / TILE), dim3(TILE * BR_GROUPS), 0, st, db, bpart,
+                       nrb, cols);
     return hipGetLastError();
 }
 

@@ -58,6 +58,21 @@ struct KTile {
     static constexpr int BK = A_K ? 32 : 16;
     static constexpr int STAGES = A_K ? 2 : 4;
 };
+// bf16 operands (k-tile width in float pairs): a k-tile takes an eighth of the fp32 MFMA
+// time, so more of them must be in flight to cover the global -> LDS latency.
+#ifndef GEMM_BF_BK
+#define GEMM_BF_BK 32
+#endif
+#ifndef GEMM_BF_STAGES
+#define GEMM_BF_STAGES 2
+#endif
+template <bool A_K, bool BF>
+struct KTileOf : KTile<A_K> {};
+template <>
+struct KTileOf<true, true> {
+    static constexpr int BK = GEMM_BF_BK;
+    static constexpr int STAGES = GEMM_BF_STAGES;
+};
 constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse slots
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
@@ -401,7 +416,7 @@ GPT2_DEV void gemm_body(const Params& p) {
     static_assert(!BF || (A_K && B_K && !XF), "bf16 operands are both k-contiguous");
     constexpr int WN = BN / 2, NB = BN / 32;
     constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
-    constexpr int BK = KTile<A_K>::BK, STAGES = KTile<A_K>::STAGES;
+    constexpr int BK = KTileOf<A_K, BF>::BK, STAGES = KTileOf<A_K, BF>::STAGES;
     constexpr int A_FLOATS = BM * BK, B_FLOATS = BN * BK;  // the operands' k-tiles in LDS
     constexpr int STAGE_FLOATS = A_FLOATS + B_FLOATS + (XR ? XF_FLOATS : 0);
     constexpr int LPS = (BM + BN) * BK / 1024 + (XR ? 1 : 0);  // transfers per thread per k-tile
@@ -486,9 +501,9 @@ GPT2_DEV void gemm_body(const Params& p) {
 #pragma unroll
             for (int j = 0; j < BN * BK / 1024; j++) dma16s(bb, offB[j], lb_ + j * 4096);
         } else {
-            if (A_K) fill_kcontig<BM, BK>(Sa, p.A, p.lda, m0, p.M, k0, p.K);
+            if constexpr (A_K) fill_kcontig<BM, BK>(Sa, p.A, p.lda, m0, p.M, k0, p.K);
             else fill_rcontig<BM, BK>(Sa, p.A, p.lda, m0, XF ? (int)p.lda : p.M, k0, p.K);
-            if (B_K) fill_kcontig<BN, BK>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
+            if constexpr (B_K) fill_kcontig<BN, BK>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
             else fill_rcontig<BN, BK>(Sb, p.B, p.ldb, n0, p.N, k0, p.K);
         }
         if (XR) {
@@ -498,9 +513,9 @@ GPT2_DEV void gemm_body(const Params& p) {
     };
     // the first STAGES-1 k-tiles of an item
     auto prologue = [&](const Item& w) {
-        if (A_K) kcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
+        if constexpr (A_K) kcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
         else rcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
-        if (B_K) kcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
+        if constexpr (B_K) kcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
         else rcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
 #pragma unroll
         for (int s = 0; s < STAGES - 1; s++)
@@ -852,7 +867,7 @@ template <bool A_K, bool B_K, int EPI, bool XF, int BN, bool BF = false>
 hipError_t launch(Params& p, hipStream_t st, int split) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
-    p.nk = (p.K + KTile<A_K>::BK - 1) / KTile<A_K>::BK;
+    p.nk = (p.K + KTileOf<A_K, BF>::BK - 1) / KTileOf<A_K, BF>::BK;
     const long tiles = (long)p.tiles_m * p.tiles_n;
     if (tiles == 0) return hipSuccess;
     if (p.nk == 0) {
@@ -887,10 +902,10 @@ bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
 // k-split factor that turns a shape with fewer tiles than resident blocks and a long k
 // extent into whole rounds of split-K units (e.g. 384 tiles -> 4 segments, 3 rounds); 0
 // when there is none (stream-K then).
-template <bool A_K, int BN>
+template <bool A_K, int BN, bool BF = false>
 int pick_split(int M, int N, int K) {
     const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int nk = (K + KTile<A_K>::BK - 1) / KTile<A_K>::BK;
+    const int nk = (K + KTileOf<A_K, BF>::BK - 1) / KTileOf<A_K, BF>::BK;
     if (tiles == 0 || tiles >= RESIDENT) return 0;
     for (int s = 2; s <= 8; s++)
         if ((tiles * s) % RESIDENT == 0 && tiles * s <= MAX_UNITS && nk >= 16 * s) return s;
@@ -1045,8 +1060,8 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
     const int bn = tile_n(M, N);
     auto go = [&](auto epi_c) -> hipError_t {
         constexpr int E = decltype(epi_c)::value;
-        if (bn == 96) return launch<true, true, E, false, 96, true>(p, st, pick_split<true, 96>(p.M, p.N, p.K));
-        return launch<true, true, E, false, 128, true>(p, st, pick_split<true, 128>(p.M, p.N, p.K));
+        if (bn == 96) return launch<true, true, E, false, 96, true>(p, st, pick_split<true, 96, true>(p.M, p.N, p.K));
+        return launch<true, true, E, false, 128, true>(p, st, pick_split<true, 128, true>(p.M, p.N, p.K));
     };
     switch (epi) {
         case BF16_STORE: return go(std::integral_constant<int, EPI_STORE>{});
