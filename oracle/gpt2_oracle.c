@@ -727,9 +727,11 @@ typedef struct oracle_gpt2 {
 /* Mixed precision (bfloat16 rounding defined at oracle_bf16_round): every linear layer and the LM head multiply the
  * bfloat16 roundings of their two operands (input and weight forward; output gradient
  * and weight, or output gradient and input, backward), the products summed exactly;
- * the bias gradient sums the unrounded output gradient.  Everything else -- the fp32
- * master weights, LayerNorm, GELU, residuals, attention, softmax and cross-entropy,
- * AdamW -- is unchanged. */
+ * the bias gradient sums the unrounded output gradient.  Attention multiplies the
+ * roundings of q, k, v (forward and backward) and of its output gradient (backward);
+ * its probabilities and score gradients are not rounded.  Everything else -- the fp32
+ * master weights, LayerNorm, GELU, residuals, softmax and cross-entropy, AdamW -- is
+ * unchanged. */
 #define ORACLE_VARIANT_BF16 4
 
 static void carve(oracle_gpt2* g, int B, int T) {
@@ -956,7 +958,16 @@ EXPORT double oracle_gpt2_forward(oracle_gpt2* g, const int32_t* inputs, const i
             qkv_in = g->qkvr + (size_t)l * BT * 3 * C;
             oracle_rope_forward(qkv_in, qkv, B, T, C, NH);
         }
-        oracle_attention_forward(atty, preatt, att, qkv_in, B, T, C, NH);
+        if (g->variant & ORACLE_VARIANT_BF16) {
+            /* attention multiplies the bf16 roundings of q, k and v (the probabilities
+             * stay unrounded) */
+            real* rq = bf16_copy(qkv_in, BT * 3 * C);
+            bad |= rq ? O_OK : O_ENOMEM;
+            if (rq) oracle_attention_forward(atty, preatt, att, rq, B, T, C, NH);
+            free(rq);
+        } else {
+            oracle_attention_forward(atty, preatt, att, qkv_in, B, T, C, NH);
+        }
         bad |= linear_forward(g, attproj, atty, P[6] + (size_t)l * C * C, P[7] + l * C, (int)BT, C, C);
         oracle_residual_forward(res2, residual, attproj, BT * C);
         norm_forward(rms, ln2, ln2m, ln2r, res2, P[8] + l * C, P[9] + l * C, (int)BT, C);
@@ -1049,13 +1060,24 @@ EXPORT int oracle_gpt2_backward(oracle_gpt2* g) {
         bad |= linear_backward(g, D[A_ATTY] + o1, G[6] + (size_t)l * C * C, G[7] + l * C,
                                D[A_ATTPROJ] + o1, A[A_ATTY] + o1, P[6] + (size_t)l * C * C,
                                (int)BT, C, C);
-        if (rope) {
-            oracle_attention_backward(g->dqkvr + o3, D[A_PREATT] + oa, D[A_ATT] + oa, D[A_ATTY] + o1,
-                                      g->qkvr + o3, A[A_ATT] + oa, B, T, C, NH);
-            oracle_rope_backward(D[A_QKV] + o3, g->dqkvr + o3, B, T, C, NH);
-        } else {
-            oracle_attention_backward(D[A_QKV] + o3, D[A_PREATT] + oa, D[A_ATT] + oa, D[A_ATTY] + o1,
-                                      A[A_QKV] + o3, A[A_ATT] + oa, B, T, C, NH);
+        {
+            /* bf16 variant: the attention backward's products take the bf16 roundings of
+             * q, k, v and of the output gradient; probabilities and score gradients stay
+             * unrounded (the softmax backward is unchanged) */
+            const int bf = g->variant & ORACLE_VARIANT_BF16;
+            const real* ain = rope ? g->qkvr + o3 : A[A_QKV] + o3;
+            const real* adout = D[A_ATTY] + o1;
+            real* rin = bf ? bf16_copy(ain, BT * 3 * C) : NULL;
+            real* rdout = bf ? bf16_copy(adout, BT * C) : NULL;
+            if (bf && (!rin || !rdout)) {
+                bad |= O_ENOMEM;
+            } else {
+                oracle_attention_backward(rope ? g->dqkvr + o3 : D[A_QKV] + o3, D[A_PREATT] + oa, D[A_ATT] + oa,
+                                          bf ? rdout : adout, bf ? rin : ain, A[A_ATT] + oa, B, T, C, NH);
+            }
+            free(rin);
+            free(rdout);
+            if (rope) oracle_rope_backward(D[A_QKV] + o3, g->dqkvr + o3, B, T, C, NH);
         }
         bad |= linear_backward(g, D[A_LN1] + o1, G[4] + (size_t)l * 3 * C * C, G[5] + l * 3 * C,
                                D[A_QKV] + o3, A[A_LN1] + o1, P[4] + (size_t)l * 3 * C * C,

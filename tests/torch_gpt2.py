@@ -97,7 +97,15 @@ def loss_fn(shape, P, inputs, targets, variant=0):
         v = v.view(B, T, NH, C // NH).transpose(1, 2)
         if variant & ROPE:
             q, k = rope(q), rope(k)
-        y = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+        if variant & BF16:
+            # products of bf16-rounded q, k, v; the probabilities stay unrounded; the
+            # output gradient is rounded before both of its products
+            q, k, v = (_RoundOperand.apply(a) for a in (q, k, v))
+            s = (q @ k.transpose(-1, -2)) / (C // NH) ** 0.5
+            s = s.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), float("-inf"))
+            y = _RoundGradient.apply(torch.softmax(s, dim=-1) @ v)
+        else:
+            y = F.scaled_dot_product_attention(q, k, v, is_causal=True)
         y = y.transpose(1, 2).reshape(B, T, C)
         x = x + linear(y, P["attprojw"][l], P["attprojb"][l])
         h = norm(x, P["ln2w"][l], P["ln2b"][l])
