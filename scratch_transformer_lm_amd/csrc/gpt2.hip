@@ -64,9 +64,11 @@ struct ActInfo {
 // stored (W*), transposed (WT*) and the linear layers' inputs, straight and transposed
 // (per layer); in the scratch the output gradients (one straight buffer, a transposed one
 // per kind) and the LM head's.  Transposes are (cols, rows rounded up to 64).
+// Attention's per-head copies of q, k, v (row-major and transposed, per layer) and of its
+// output gradient (scratch) follow.
 enum { BW_Q, BW_A, BW_F, BW_P, BW_WTE, BWT_Q, BWT_A, BWT_F, BWT_P, BWT_WTE, BA_LN1, BA_LN1T, BA_ATTY, BA_ATTYT,
-       BA_LN2, BA_LN2T, BA_FCHG, BA_FCHGT, BA_LNF, BA_LNFT, NBA };
-enum { BS_DY, BS_DREST, BS_DFCHT, BS_DQKVT, BS_DLOG, BS_DLOGT, NBS };
+       BA_LN2, BA_LN2T, BA_FCHG, BA_FCHGT, BA_LNF, BA_LNFT, BA_HQ, BA_HK, BA_HV, BA_HQT, BA_HKT, BA_HVT, NBA };
+enum { BS_DY, BS_DREST, BS_DFCHT, BS_DQKVT, BS_DLOG, BS_DLOGT, BS_HDO, BS_HDOT, NBS };
 
 size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
 
@@ -119,12 +121,14 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     o += align_up(BT);
     if (variant & GPT2_VARIANT_BF16) {
         const size_t BTp = pad64(BT);
+        const size_t HT = attn_bf16_head_elems(B, T, (int)C);
         // (id, layers, elements per layer)
         const size_t spec[NBA][2] = {
             {L, 3 * C * C}, {L, C * C}, {L, 4 * C * C}, {L, 4 * C * C}, {1, V * C},
             {L, C * pad64(3 * C)}, {L, C * pad64(C)}, {L, C * pad64(4 * C)}, {L, 4 * C * pad64(C)}, {1, C * y.Vp},
             {L, BT * C}, {L, C * BTp}, {L, BT * C}, {L, C * BTp}, {L, BT * C}, {L, C * BTp},
-            {L, BT * 4 * C}, {L, 4 * C * BTp}, {1, BT * C}, {1, C * BTp}};
+            {L, BT * 4 * C}, {L, 4 * C * BTp}, {1, BT * C}, {1, C * BTp},
+            {L, BT * C}, {L, BT * C}, {L, BT * C}, {L, HT}, {L, HT}, {L, HT}};
         for (int i = 0; i < NBA; i++) {
             y.ba[i] = o;
             y.ba_l[i] = spec[i][1];
@@ -156,7 +160,8 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     y.rope = take(rope_table_floats(c->max_seq_len, (int)(C / NH)));  // rotary variant's (cos, sin) table
     if (variant & GPT2_VARIANT_BF16) {
         const size_t BTp = pad64(BT);
-        const size_t n[NBS] = {BT * 4 * C, C * BTp, 4 * C * BTp, 3 * C * BTp, BT * y.Vp, y.Vp * BTp};
+        const size_t n[NBS] = {BT * 4 * C, C * BTp, 4 * C * BTp, 3 * C * BTp, BT * y.Vp, y.Vp * BTp, BT * C,
+                               attn_bf16_head_elems(B, T, (int)C)};
         for (int i = 0; i < NBS; i++) y.bs[i] = take((n[i] + 1) / 2);
         y.bpart = take(bias_partial_floats((int)BT, (int)(4 * C)));
     }
@@ -222,6 +227,11 @@ uint16_t* BA(gpt2* g, int id, int l = 0) {
     return reinterpret_cast<uint16_t*>(g->buf.acts + g->lay.ba[id]) + (size_t)l * g->lay.ba_l[id];
 }
 uint16_t* BS(gpt2* g, int id) { return reinterpret_cast<uint16_t*>(g->buf.grad_scratch + g->lay.bs[id]); }
+
+AttnBf16 attn_copies(gpt2* g, int l) {
+    return AttnBf16{BA(g, BA_HQ, l), BA(g, BA_HK, l), BA(g, BA_HV, l), BA(g, BA_HQT, l), BA(g, BA_HKT, l),
+                    BA(g, BA_HVT, l)};
+}
 
 // bf16 copies of an fp32 (rows, cols) tensor: straight (xb) and transposed (xt, rows
 // padded to 64 with zeros), and the bias gradient's per-block column sums (bpart).
@@ -318,7 +328,17 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
                          nullptr, 3 * C, C));
         // rotary variant: q and k rotated in place (the stored qkv is the rotated one)
         if (rope_on(g)) HIPCHK(g, rope_forward(A(g, GPT2_ACT_QKV, l), S(g, g->lay.rope), B, T, C, NH, st));
-        HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T, C, NH, st));
+        if (bf) {
+            // bf16 per-head copies of q, k, v (kept for the backward), then attention on them
+            uint16_t* rm[3] = {BA(g, BA_HQ, l), BA(g, BA_HK, l), BA(g, BA_HV, l)};
+            uint16_t* tr[3] = {BA(g, BA_HQT, l), BA(g, BA_HKT, l), BA(g, BA_HVT, l)};
+            HIPCHK(g, attn_prep_bf16(A(g, GPT2_ACT_QKV, l), 3 * C, C, 3, rm, tr, B, T, C, NH, st));
+            HIPCHK(g, attention_forward_bf16(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), attn_copies(g, l), B, T,
+                                             C, NH, st));
+        } else {
+            HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T,
+                                        C, NH, st));
+        }
         if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_ATTY, l), BT, C, BA(g, BA_ATTY, l), BA(g, BA_ATTYT, l), nullptr, st));
         HIPCHK(g, linear(BF16_BIAS_RESID, A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTY, l),
                          P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BW_A, l), P(g, P_ATTPROJB) + l * C, residual,
@@ -547,8 +567,17 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         HIPCHK(g, mark(EV_W_ATTPROJ, sw));
         HIPCHK(g, dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BWT_A, l), C, nullptr));
         if (later) HIPCHK(g, after(st, EV_W_QKV));  // the qkv wgrad above still reads dqkv
-        HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
-                                     A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
+        if (bf) {
+            uint16_t* rm[1] = {BS(g, BS_HDO)};
+            uint16_t* tr[1] = {BS(g, BS_HDOT)};
+            HIPCHK(g, attn_prep_bf16(datty, C, 0, 1, rm, tr, B, T, C, NH, st));
+            HIPCHK(g, attention_backward_bf16(dqkv, S(g, g->lay.delta), BS(g, BS_HDO), BS(g, BS_HDOT),
+                                              A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), attn_copies(g, l), B,
+                                              T, C, NH, st));
+        } else {
+            HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
+                                         A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
+        }
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
         // rotary variant: attention gave the gradient of the rotated q and k; rotate it back
         if (rope_on(g)) HIPCHK(g, rope_backward(dqkv, S(g, g->lay.rope), B, T, C, NH, st));

@@ -137,6 +137,28 @@ hipError_t attention_backward(float* dqkv, float* delta, const float* dout, cons
                               const float* out, const float* lse, int B, int T, int C, int NH,
                               hipStream_t st);
 
+// ---- attention of the mixed-precision variant (attention_bf16.hip) ------------------
+// bf16 copies of each head, per (batch, head): row-major (T, HS) and transposed (HS, Tp)
+// with the tokens of every 64-token tile permuted (Tp = T rounded up to 64, zero beyond
+// T); attn_bf16_head_elems(B, T, C) bf16 elements hold one transposed tensor.
+size_t attn_bf16_head_elems(int B, int T, int C);
+// Copies of nsrc fp32 (B, T, ld) tensors src + z*zoff (head h at columns h*HS) into
+// rm[z] and tr[z] (either may be null).  HS = C/NH must be 16, 32 or 64.
+hipError_t attn_prep_bf16(const float* src, long ld, long zoff, int nsrc, uint16_t* const* rm, uint16_t* const* tr,
+                          int B, int T, int C, int NH, hipStream_t st);
+struct AttnBf16 {
+    const uint16_t *q, *k, *v;     // row-major copies
+    const uint16_t *qt, *kt, *vt;  // transposed copies
+};
+// out (B,T,C) fp32 and lse (B,NH,T) from bf16 q, k, vt (the probabilities unrounded).
+hipError_t attention_forward_bf16(float* out, float* lse, const AttnBf16& a, int B, int T, int C, int NH,
+                                  hipStream_t st);
+// dqkv (B,T,3C) fp32 (overwritten) from bf16 dO (row-major dob, transposed dot), the fp32
+// output `out`, lse, and q, k, v, qt, kt; delta needs B*NH*T floats.
+hipError_t attention_backward_bf16(float* dqkv, float* delta, const uint16_t* dob, const uint16_t* dot,
+                                   const float* out, const float* lse, const AttnBf16& a, int B, int T, int C, int NH,
+                                   hipStream_t st);
+
 // ---- rotary positions (rope.hip) ------------------------------------------------------
 // table: rope_table_floats(maxT, hs) floats of (cos, sin) pairs, filled by rope_table.
 // rope_forward rotates q and k of qkv (B, T, 3C) in place; rope_backward applies the

@@ -547,6 +547,45 @@ def test_bf16_training(G, wl, steps, variant):
     check_training(G, S.TINY if wl == "tiny" else S.GPT2_124M_SHORT, steps, variant=variant)
 
 
+@pytest.mark.parametrize("variant", [4, 7])
+def test_bf16_forward_activations(G, variant):
+    """Every forward activation of the tiny bf16 model (attention on bf16 q, k, v with
+    unrounded probabilities, then the bf16 linear layers) against the float64 oracle.
+    A value that fp32 and fp64 compute slightly differently may round to bf16 one unit
+    apart when it lies next to a rounding boundary; such a flip moves a product term by
+    at most 2^-7 of itself.  So, per tensor: the 99th percentile of the element errors
+    (relative to the tensor's largest value) within max(1e-5, F32_FACTOR x the oracle's
+    float32 build's), and every element within 1e-2, far below what a wrong index,
+    operand or scale gives."""
+    from oracle import oracle as O
+    w = S.TINY
+    params = S.init_params(w.model)
+    x, y = S.tokens(w)
+    m = G.GPT2(w.model, w.B, w.T, variant=variant)
+    m.params.copy_(dev(params))
+    loss = m.forward(dev(x, torch.int32), dev(y, torch.int32))
+    o64 = O.OracleGPT2(w.model, w.B, w.T, params, variant=variant)
+    o32 = O.OracleGPT2(w.model, w.B, w.T, params, "f32", variant=variant)
+    l64, l32 = o64.forward(x, y), o32.forward(x, y)
+    assert abs(loss - l64) / l64 <= max(LOSS_RTOL, F32_FACTOR * abs(l32 - l64) / l64)
+    def p99(a, ref):
+        ref = np.asarray(ref, np.float64).reshape(-1)
+        d = np.abs(np.asarray(a, np.float64).reshape(-1) - ref) / max(np.max(np.abs(ref)), 1e-30)
+        return float(np.percentile(d, 99)), float(np.max(d))
+
+    bad = []
+    for l in range(w.model.num_layers):
+        for name in ("ln1", "qkv", "atty", "residual2", "ln2", "fch_gelu", "residual3"):
+            oname = "qkv_rot" if name == "qkv" and variant & G.VARIANT_ROPE else name  # GPU keeps it rotated
+            ref = o64.activation(oname, l)
+            e99, emax = p99(host(m.activation(name, l)), ref)
+            f99, fmax = p99(o32.activation(oname, l), ref)
+            say(f"{name}[{l}] p99 {e99:.1e} max {emax:.1e} (float32 oracle p99 {f99:.1e} max {fmax:.1e})")
+            if not (e99 <= max(1e-5, F32_FACTOR * f99) and emax <= 1e-2):
+                bad.append((name, l, e99, emax, f99))
+    assert not bad, bad
+
+
 def test_bf16_ragged_shape(G):
     """bf16 variant at the 124M widths with 300 rows: the transposed copies' zero padding
     (300 -> 320 rows of k) and ragged GEMM edges."""
