@@ -66,19 +66,30 @@ struct KTile {
 #ifndef GEMM_BF_STAGES
 #define GEMM_BF_STAGES 2
 #endif
-template <bool A_K, bool BF>
+// 256-wide bf16 tiles (64 x 128 per wave) take half-width k-tiles in 3 buffers, so that
+// two blocks still fit a CU.
+#ifndef GEMM_BF256_BK
+#define GEMM_BF256_BK 16
+#endif
+#ifndef GEMM_BF256_STAGES
+#define GEMM_BF256_STAGES 3
+#endif
+template <bool A_K, bool BF, int BN = 128>
 struct KTileOf : KTile<A_K> {};
-template <>
-struct KTileOf<true, true> {
-    static constexpr int BK = GEMM_BF_BK;
-    static constexpr int STAGES = GEMM_BF_STAGES;
+template <int BN>
+struct KTileOf<true, true, BN> {
+    static constexpr int BK = BN == 256 ? GEMM_BF256_BK : GEMM_BF_BK;
+    static constexpr int STAGES = BN == 256 ? GEMM_BF256_STAGES : GEMM_BF_STAGES;
 };
 constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse slots
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
 constexpr int MAX_UNITS = 1536;                  // split-K units the partial region holds
-constexpr int SLOT_BIAS = BM * 128;            // partial slot: tile, then its bias-gradient row sums
-constexpr int SLOT_FLOATS = SLOT_BIAS + BM;
+// partial slot of a BM x BN tile: the tile (at least BM x 128), then its bias-gradient row sums
+template <int BN>
+constexpr int slot_bias() { return BM * (BN > 128 ? BN : 128); }
+template <int BN>
+constexpr int slot_floats() { return slot_bias<BN>() + BM; }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -412,11 +423,12 @@ GPT2_DEV void wait_vm() {
 // instead of four fp32 steps.
 template <bool A_K, bool B_K, int EPI, bool XF, int BN, bool BF>
 GPT2_DEV void gemm_body(const Params& p) {
-    static_assert(BN == 128 || (BN == 96 && A_K), "96-wide tiles take 32-wide k-tiles");
+    static_assert(BN == 128 || (BN == 96 && A_K) || (BN == 256 && BF), "tile widths: 128; 96 (A k-contiguous); 256 (bf16)");
+    constexpr int SLOT_BIAS = slot_bias<BN>(), SLOT_FLOATS = slot_floats<BN>();
     static_assert(!BF || (A_K && B_K && !XF), "bf16 operands are both k-contiguous");
     constexpr int WN = BN / 2, NB = BN / 32;
     constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
-    constexpr int BK = KTileOf<A_K, BF>::BK, STAGES = KTileOf<A_K, BF>::STAGES;
+    constexpr int BK = KTileOf<A_K, BF, BN>::BK, STAGES = KTileOf<A_K, BF, BN>::STAGES;
     constexpr int A_FLOATS = BM * BK, B_FLOATS = BN * BK;  // the operands' k-tiles in LDS
     constexpr int STAGE_FLOATS = A_FLOATS + B_FLOATS + (XR ? XF_FLOATS : 0);
     constexpr int LPS = (BM + BN) * BK / 1024 + (XR ? 1 : 0);  // transfers per thread per k-tile
@@ -576,11 +588,8 @@ GPT2_DEV void gemm_body(const Params& p) {
         };
 
         // one k-tile: BK/16 groups of 16 k, each 4 MFMA steps over this wave's blocks
-        auto compute = [&](int buf, int kstep) {
-            if constexpr (BF) {
-                compute_bf16(buf);
-                return;
-            }
+        // (a generic lambda: instantiated only on the fp32 path)
+        auto compute_f32 = [&](int buf, auto kstep) {
             const float* Sa = smem + buf * STAGE_FLOATS;
             const float* Sb = Sa + A_FLOATS;
             const int k0 = kstep * BK;
@@ -653,6 +662,10 @@ GPT2_DEV void gemm_body(const Params& p) {
                             acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
             }
         };
+        auto compute = [&](int buf, int kstep) {
+            if constexpr (BF) compute_bf16(buf);
+            else compute_f32(buf, kstep);
+        };
 
         // LDS ring: k-tile kt lives in buffer kt % STAGES; STAGES-1 tiles are in flight
         // while one is consumed.  Each thread waits for its own transfers of the next
@@ -708,8 +721,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
     gemm_body<A_K, B_K, EPI, XF, BN, false>(p);
 }
 
+#ifndef GEMM_BF_OCC
+#define GEMM_BF_OCC 2
+#endif
 template <int EPI, int BN>
-__global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(Params p) {
+__global__ __launch_bounds__(NT, GEMM_BF_OCC) void gemm_bf16_kernel(Params p) {
     gemm_body<true, true, EPI, false, BN, true>(p);
 }
 
@@ -718,7 +734,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(Params p) {
 // add that tile's partials in k order and run the epilogue.
 template <int EPI, int BN>
 __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
-    constexpr int NB = BN / 32;
+    constexpr int NB = BN / 32, SLOT_BIAS = slot_bias<BN>(), SLOT_FLOATS = slot_floats<BN>();
     const int quarter = blockIdx.x & 3;
     const int lbb = (blockIdx.x >> 2) + 1;  // boundary between blocks lbb-1 and lbb
     const long x = range_start(p.total, p.nr, lbb);
@@ -742,22 +758,24 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
         return p.partial + ((long)l * 2 + which) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
     };
     epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter, [&] {
-        // two partials at a time in flight, added in k order
-        for (int l = first; l <= last; l += 2) {
-            float v[2][4 * NB];
-            const float* s0 = slot_of(l);
+        // four partials at a time in flight, added in k order
+        constexpr int F = 4;
+        for (int l = first; l <= last; l += F) {
+            float v[F][4 * NB];
 #pragma unroll
-            for (int e = 0; e < 4 * NB; e++) v[0][e] = s0[e * NT];
-            if (l + 1 <= last) {
-                const float* s1 = slot_of(l + 1);
+            for (int f = 0; f < F; f++) {
+                if (l + f <= last) {
+                    const float* sf = slot_of(l + f);
 #pragma unroll
-                for (int e = 0; e < 4 * NB; e++) v[1][e] = s1[e * NT];
+                    for (int e = 0; e < 4 * NB; e++) v[f][e] = sf[e * NT];
+                }
             }
 #pragma unroll
-            for (int e = 0; e < 4 * NB; e++) acc[0][e >> 2][e & 3] += v[0][e];
-            if (l + 1 <= last) {
+            for (int f = 0; f < F; f++) {
+                if (l + f <= last) {
 #pragma unroll
-                for (int e = 0; e < 4 * NB; e++) acc[0][e >> 2][e & 3] += v[1][e];
+                    for (int e = 0; e < 4 * NB; e++) acc[0][e >> 2][e & 3] += v[f][e];
+                }
             }
         }
     });
@@ -775,7 +793,7 @@ __global__ __launch_bounds__(NT) void gemm_fixup_kernel(Params p) {
 // sub-tiles, add the tile's S partials in k order and run the epilogue.
 template <int EPI, int BN>
 __global__ __launch_bounds__(NT) void gemm_splitk_fixup_kernel(Params p) {
-    constexpr int NB = BN / 32;
+    constexpr int NB = BN / 32, SLOT_BIAS = slot_bias<BN>(), SLOT_FLOATS = slot_floats<BN>();
     const int tiles = p.tiles_m * p.tiles_n;
     const int tile = blockIdx.x >> 2, quarter = blockIdx.x & 3;
     f32x4 acc[1][NB];
@@ -867,7 +885,7 @@ template <bool A_K, bool B_K, int EPI, bool XF, int BN, bool BF = false>
 hipError_t launch(Params& p, hipStream_t st, int split) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
-    p.nk = (p.K + KTileOf<A_K, BF>::BK - 1) / KTileOf<A_K, BF>::BK;
+    p.nk = (p.K + KTileOf<A_K, BF, BN>::BK - 1) / KTileOf<A_K, BF, BN>::BK;
     const long tiles = (long)p.tiles_m * p.tiles_n;
     if (tiles == 0) return hipSuccess;
     if (p.nk == 0) {
@@ -905,7 +923,7 @@ bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
 template <bool A_K, int BN, bool BF = false>
 int pick_split(int M, int N, int K) {
     const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int nk = (K + KTileOf<A_K, BF>::BK - 1) / KTileOf<A_K, BF>::BK;
+    const int nk = (K + KTileOf<A_K, BF, BN>::BK - 1) / KTileOf<A_K, BF, BN>::BK;
     if (tiles == 0 || tiles >= RESIDENT) return 0;
     for (int s = 2; s <= 8; s++)
         if ((tiles * s) % RESIDENT == 0 && tiles * s <= MAX_UNITS && nk >= 16 * s) return s;
@@ -926,6 +944,18 @@ int tile_n(int M, int N) {
     return (t96 > 0 && t96 % RESIDENT == 0 && t128 % RESIDENT != 0) ? 96 : 128;
 }
 
+// Tile width of the bf16 GEMMs: 256 (a 64 x 128 sub-tile per wave: a quarter less LDS and
+// L2 traffic per MFMA than 64 x 64) where N allows, else as the fp32 forward GEMMs.
+// Measured slower at the 124M shapes (fewer tiles: more and larger stream-K partials,
+// with no faster main loop), so off unless built with -DGEMM_BF_WIDE=1.
+#ifndef GEMM_BF_WIDE
+#define GEMM_BF_WIDE 0
+#endif
+int bf16_tile_n(int M, int N) {
+    if (GEMM_BF_WIDE && N >= 256) return 256;
+    return tile_n(M, N);
+}
+
 template <bool B_K, int EPI, bool XF = false>
 hipError_t launch_ak(Params& p, hipStream_t st) {
     // The dlogits dgrad keeps 128-wide tiles unless forced: its exponentials are spread
@@ -939,7 +969,7 @@ hipError_t launch_ak(Params& p, hipStream_t st) {
 
 }  // namespace
 
-size_t gemm_partial_floats() { return (size_t)std::max(RESIDENT * 2, MAX_UNITS) * SLOT_FLOATS; }
+size_t gemm_partial_floats() { return (size_t)std::max(RESIDENT * 2, MAX_UNITS) * slot_floats<GEMM_BF_WIDE ? 256 : 128>(); }
 
 bool gemm_set_tile_policy(int policy) {
     if (policy != GEMM_TILES_AUTO && policy != GEMM_TILES_128 && policy != GEMM_TILES_96) return false;
@@ -1057,9 +1087,11 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
     p.pre = pre;
     p.ldpre = ldc;
     p.partial = partial;
-    const int bn = tile_n(M, N);
+    const int bn = bf16_tile_n(M, N);
     auto go = [&](auto epi_c) -> hipError_t {
         constexpr int E = decltype(epi_c)::value;
+        if constexpr (GEMM_BF_WIDE != 0)
+            if (bn == 256) return launch<true, true, E, false, 256, true>(p, st, pick_split<true, 256, true>(p.M, p.N, p.K));
         if (bn == 96) return launch<true, true, E, false, 96, true>(p, st, pick_split<true, 96, true>(p.M, p.N, p.K));
         return launch<true, true, E, false, 128, true>(p, st, pick_split<true, 128, true>(p.M, p.N, p.K));
     };
