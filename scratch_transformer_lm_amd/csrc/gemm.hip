@@ -802,13 +802,26 @@ __global__ __launch_bounds__(NT) void gemm_splitk_fixup_kernel(Params p) {
     int m0, n0;
     tile_coords<BN>(p, tile, m0, n0);
     epilogue_rows<EPI, 1>(p, acc, m0, n0, quarter, [&] {
-        for (int sg = 0; sg < p.S; sg++) {
-            const float* slot = p.partial + ((long)sg * tiles + tile) * SLOT_FLOATS + quarter * (4 * NB) * NT + threadIdx.x;
-            float v[4 * NB];
+        // four partials at a time in flight, added in segment order
+        constexpr int F = 4;
+        for (int sg = 0; sg < p.S; sg += F) {
+            float v[F][4 * NB];
 #pragma unroll
-            for (int e = 0; e < 4 * NB; e++) v[e] = slot[e * NT];
+            for (int f = 0; f < F; f++) {
+                if (sg + f < p.S) {
+                    const float* slot = p.partial + ((long)(sg + f) * tiles + tile) * SLOT_FLOATS +
+                                        quarter * (4 * NB) * NT + threadIdx.x;
 #pragma unroll
-            for (int e = 0; e < 4 * NB; e++) acc[0][e >> 2][e & 3] += v[e];
+                    for (int e = 0; e < 4 * NB; e++) v[f][e] = slot[e * NT];
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < F; f++) {
+                if (sg + f < p.S) {
+#pragma unroll
+                    for (int e = 0; e < 4 * NB; e++) acc[0][e >> 2][e & 3] += v[f][e];
+                }
+            }
         }
     });
     if (p.dbias && n0 == 0 && quarter == 0 && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
@@ -942,6 +955,34 @@ int tile_n(int M, int N) {
     const long tm = (M + BM - 1) / BM;
     const long t128 = tm * ((N + 127) / 128), t96 = tm * ((N + 95) / 96);
     return (t96 > 0 && t96 % RESIDENT == 0 && t128 % RESIDENT != 0) ? 96 : 128;
+}
+
+// bf16 shapes with fewer tiles than resident blocks (the weight gradients: few output
+// tiles, k = B*T long) run as split-K rounds ordered k-segment first, so the 64 blocks of
+// an XCD work on 64 neighbouring tiles at the same k and share their operand panels in
+// that XCD's L2 (stream-K gives each block its own k offset, and every panel comes from
+// HBM again).  S is the split that fills rounds best (at least 90%), each unit at least
+// 8 k-tiles long.
+#ifndef GEMM_BF_SPLITK
+#define GEMM_BF_SPLITK 1
+#endif
+template <int BN>
+int pick_split_bf16(int M, int N, int K) {
+    const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int nk = (K + KTileOf<true, true, BN>::BK - 1) / KTileOf<true, true, BN>::BK;
+    if (!GEMM_BF_SPLITK || tiles == 0 || tiles >= RESIDENT) return 0;
+    int best = 0;
+    double best_util = 0.9;
+    for (int s = 2; s <= 16; s++) {
+        const long units = tiles * s;
+        if (units > MAX_UNITS || nk < 8 * s) break;
+        const double util = (double)units / (double)(((units + RESIDENT - 1) / RESIDENT) * RESIDENT);
+        if (util > best_util + 1e-9) {
+            best_util = util;
+            best = s;
+        }
+    }
+    return best;
 }
 
 // Tile width of the bf16 GEMMs: 256 (a 64 x 128 sub-tile per wave: a quarter less LDS and
@@ -1091,9 +1132,9 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
     auto go = [&](auto epi_c) -> hipError_t {
         constexpr int E = decltype(epi_c)::value;
         if constexpr (GEMM_BF_WIDE != 0)
-            if (bn == 256) return launch<true, true, E, false, 256, true>(p, st, pick_split<true, 256, true>(p.M, p.N, p.K));
-        if (bn == 96) return launch<true, true, E, false, 96, true>(p, st, pick_split<true, 96, true>(p.M, p.N, p.K));
-        return launch<true, true, E, false, 128, true>(p, st, pick_split<true, 128, true>(p.M, p.N, p.K));
+            if (bn == 256) return launch<true, true, E, false, 256, true>(p, st, pick_split_bf16<256>(p.M, p.N, p.K));
+        if (bn == 96) return launch<true, true, E, false, 96, true>(p, st, pick_split_bf16<96>(p.M, p.N, p.K));
+        return launch<true, true, E, false, 128, true>(p, st, pick_split_bf16<128>(p.M, p.N, p.K));
     };
     switch (epi) {
         case BF16_STORE: return go(std::integral_constant<int, EPI_STORE>{});

@@ -586,6 +586,14 @@ def test_bf16_forward_activations(G, variant):
     assert not bad, bad
 
 
+def test_bf16_split_k_weight_gradients(G):
+    """One layer at C=512 with B*T = 4096: the fc and fcproj weight gradients (64 output
+    tiles, k = 4096) run as 8-way split-K rounds, k-segment first, with the segment
+    partials added by the split-K fix-up (the full-size shapes take this path too)."""
+    w = S.Workload("gpt2 L1 C512 H8 V512 B4 T1024", S.ModelShape(1024, 512, 1, 8, 512), 4, 1024)
+    check_training(G, w, 1, variant=G.VARIANT_BF16)
+
+
 def test_bf16_ragged_shape(G):
     """bf16 variant at the 124M widths with 300 rows: the transposed copies' zero padding
     (300 -> 320 rows of k) and ragged GEMM edges."""
