@@ -966,11 +966,11 @@ int tile_n(int M, int N) {
 #ifndef GEMM_BF_SPLITK
 #define GEMM_BF_SPLITK 1
 #endif
-template <int BN>
-int pick_split_bf16(int M, int N, int K) {
+template <bool A_K, bool BF, int BN>
+int pick_split_rounds(int M, int N, int K) {
     const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int nk = (K + KTileOf<true, true, BN>::BK - 1) / KTileOf<true, true, BN>::BK;
-    if (!GEMM_BF_SPLITK || tiles == 0 || tiles >= RESIDENT) return 0;
+    const int nk = (K + KTileOf<A_K, BF, BN>::BK - 1) / KTileOf<A_K, BF, BN>::BK;
+    if (tiles == 0 || tiles >= RESIDENT) return 0;
     int best = 0;
     double best_util = 0.9;
     for (int s = 2; s <= 16; s++) {
@@ -983,6 +983,11 @@ int pick_split_bf16(int M, int N, int K) {
         }
     }
     return best;
+}
+
+template <int BN>
+int split_bf16(int M, int N, int K) {
+    return GEMM_BF_SPLITK ? pick_split_rounds<true, true, BN>(M, N, K) : 0;
 }
 
 // Tile width of the bf16 GEMMs: 256 (a 64 x 128 sub-tile per wave: a quarter less LDS and
@@ -1132,9 +1137,9 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
     auto go = [&](auto epi_c) -> hipError_t {
         constexpr int E = decltype(epi_c)::value;
         if constexpr (GEMM_BF_WIDE != 0)
-            if (bn == 256) return launch<true, true, E, false, 256, true>(p, st, pick_split_bf16<256>(p.M, p.N, p.K));
-        if (bn == 96) return launch<true, true, E, false, 96, true>(p, st, pick_split_bf16<96>(p.M, p.N, p.K));
-        return launch<true, true, E, false, 128, true>(p, st, pick_split_bf16<128>(p.M, p.N, p.K));
+            if (bn == 256) return launch<true, true, E, false, 256, true>(p, st, split_bf16<256>(p.M, p.N, p.K));
+        if (bn == 96) return launch<true, true, E, false, 96, true>(p, st, split_bf16<96>(p.M, p.N, p.K));
+        return launch<true, true, E, false, 128, true>(p, st, split_bf16<128>(p.M, p.N, p.K));
     };
     switch (epi) {
         case BF16_STORE: return go(std::integral_constant<int, EPI_STORE>{});
