@@ -93,10 +93,13 @@ constexpr int slot_floats() { return slot_bias<BN>() + BM; }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr float LOG2E_EPI = 1.4426950408889634f;
 
 // EPI_DLOGITS: LM-head dgrad whose A held s * softmax only; the one-hot part of dlogits,
 // s * onehot(target) . W = s * W[target], is subtracted here.
-enum Epi { EPI_STORE = 0, EPI_BIAS, EPI_BIAS_RESID, EPI_BIAS_GELU, EPI_ACCUM, EPI_GELU_BWD, EPI_DLOGITS };
+// EPI_STORE_LSE: the LM-head forward; stores the logits and, per row, the base-2
+// (max, sum of 2^(x log2 e - max)) of each wave's half of the tile's columns.
+enum Epi { EPI_STORE = 0, EPI_BIAS, EPI_BIAS_RESID, EPI_BIAS_GELU, EPI_ACCUM, EPI_GELU_BWD, EPI_DLOGITS, EPI_STORE_LSE };
 
 struct Params {
     int M, N, K;
@@ -117,6 +120,7 @@ struct Params {
     const int32_t* tgt; // dlogits operand: per-row target id
     float xscale;       // dlogits operand: d loss / d loss_row (1 / rows)
     float xlog2s;       // log2(xscale)
+    float* lsep;        // EPI_STORE_LSE: partial (max, sum) pairs, [2 * tiles_n][M] float2
     int tiles_m, tiles_n, nk;
     int G;              // persistent blocks
     int R;              // whole-tile rounds: block lb takes tiles r*G + lb, r < R
@@ -201,7 +205,7 @@ GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0,
         for (int v = 0; v < 4; v++) {
             const float x = acc[b][v];
             float& o = in[b][v];
-            if (EPI == EPI_STORE) o = x;
+            if (EPI == EPI_STORE || EPI == EPI_STORE_LSE) o = x;
             else if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) o = x + bias_v[b];
             else if (EPI == EPI_BIAS_RESID) o = o + (x + bias_v[b]);
             else if (EPI == EPI_ACCUM) o = o + x;
@@ -217,6 +221,35 @@ GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0,
                 if (inside(b, v)) q[16 * b] = in[b][v];
         }
     };
+    if constexpr (EPI == EPI_STORE_LSE) {
+        // this wave's 16*NB columns of each of its 4 rows: 16 lanes x NB values
+        const int part = (n0 / (32 * NB)) * 2 + (wave & 1);
+        float pm = -INFINITY, ps = 0.f;  // lanes 0..3 of each group keep row r0 + (lane & 15)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < NB; b++)
+                if (inside(b, v)) m = fmaxf(m, in[b][v] * LOG2E_EPI);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            float sum = 0.f;
+            if (m > -INFINITY) {
+#pragma unroll
+                for (int b = 0; b < NB; b++)
+                    if (inside(b, v)) sum += __builtin_amdgcn_exp2f(fmaf(in[b][v], LOG2E_EPI, -m));
+            }
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+            if ((lane & 15) == v) {
+                pm = m;
+                ps = sum;
+            }
+        }
+        // one store of 16 consecutive rows (lanes 0..3 of the four groups)
+        const int row = r0 + (lane & 15);
+        if ((lane & 15) < 4 && row < p.M) reinterpret_cast<float2*>(p.lsep)[(long)part * p.M + row] = make_float2(pm, ps);
+    }
     if (EPI == EPI_BIAS_GELU) {
         store_row(p.pre, p.ldpre);  // the pre-activation, then its GELU
 #pragma unroll
@@ -1015,6 +1048,15 @@ hipError_t launch_ak(Params& p, hipStream_t st) {
 
 }  // namespace
 
+size_t lse_partial_floats(int M, int N) { return (size_t)M * 2 * 2 * (size_t)((N + 95) / 96); }
+
+// (max, sum) pairs per row that an LSE-fused forward of this shape writes: two per tile
+// column, at the tile width its launcher picks
+int lse_partial_count(int M, int N, bool bf16) {
+    const int bn = bf16 ? bf16_tile_n(M, N) : tile_n(M, N);
+    return 2 * ((N + bn - 1) / bn);
+}
+
 size_t gemm_partial_floats() { return (size_t)std::max(RESIDENT * 2, MAX_UNITS) * slot_floats<GEMM_BF_WIDE ? 256 : 128>(); }
 
 bool gemm_set_tile_policy(int policy) {
@@ -1025,8 +1067,9 @@ bool gemm_set_tile_policy(int policy) {
 
 hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
-                          float* partial, hipStream_t st) {
+                          float* partial, hipStream_t st, float* lse_part) {
     if (K % 4 || !aligned16(inp) || !aligned16(w)) return hipErrorInvalidValue;
+    if (lse_part && (bias || resid || pre)) return hipErrorInvalidValue;
     Params p{};
     p.M = M;
     p.N = N;
@@ -1050,6 +1093,10 @@ hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w
         return launch_ak<true, EPI_BIAS_RESID>(p, st);
     }
     if (bias) return launch_ak<true, EPI_BIAS>(p, st);
+    if (lse_part) {
+        p.lsep = lse_part;
+        return launch_ak<true, EPI_STORE_LSE>(p, st);
+    }
     return launch_ak<true, EPI_STORE>(p, st);
 }
 
@@ -1115,7 +1162,7 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
 
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
                      int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
-                     hipStream_t st) {
+                     hipStream_t st, float* lse_part) {
     if (K % 2 || lda % 8 || ldb % 8 || lda < K || ldb < K || !aligned16(a) || !aligned16(b)) return hipErrorInvalidValue;
     Params p{};
     p.M = M;
@@ -1142,7 +1189,12 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
         return launch<true, true, E, false, 128, true>(p, st, split_bf16<128>(p.M, p.N, p.K));
     };
     switch (epi) {
-        case BF16_STORE: return go(std::integral_constant<int, EPI_STORE>{});
+        case BF16_STORE:
+            if (lse_part) {
+                p.lsep = lse_part;
+                return go(std::integral_constant<int, EPI_STORE_LSE>{});
+            }
+            return go(std::integral_constant<int, EPI_STORE>{});
         case BF16_BIAS: return go(std::integral_constant<int, EPI_BIAS>{});
         case BF16_BIAS_RESID: return aux ? go(std::integral_constant<int, EPI_BIAS_RESID>{}) : hipErrorInvalidValue;
         case BF16_BIAS_GELU: return pre ? go(std::integral_constant<int, EPI_BIAS_GELU>{}) : hipErrorInvalidValue;

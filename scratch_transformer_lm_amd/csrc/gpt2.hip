@@ -78,7 +78,8 @@ struct Layout {
     size_t tok_in, tok_tgt;  // int32 arrays inside acts (offset in 4-byte words)
     size_t n_acts;
     // grad_scratch
-    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, sample, rope, n_scratch;
+    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, sample, rope, lsep,
+        n_scratch;
     // mixed precision: offsets (floats) of the bf16 arrays, per-layer strides (bf16 elements)
     size_t ba[NBA], ba_l[NBA], bs[NBS], bpart;
 };
@@ -158,6 +159,7 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     y.partial_w = take(gemm_partial_floats());  // split tiles of the weight-gradient stream
     y.sample = take(3 * BT);                      // sampling requests: rows, coins, tokens
     y.rope = take(rope_table_floats(c->max_seq_len, (int)(C / NH)));  // rotary variant's (cos, sin) table
+    y.lsep = take(lse_partial_floats((int)BT, (int)V));  // the LM head's per-tile log-sum-exp partials
     if (variant & GPT2_VARIANT_BF16) {
         const size_t BTp = pad64(BT);
         const size_t n[NBS] = {BT * 4 * C, C * BTp, 4 * C * BTp, 3 * C * BTp, BT * y.Vp, y.Vp * BTp, BT * C,
@@ -357,16 +359,20 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     }
     HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LNF), A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD),
                        A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, st));
+    // LM head: the GEMM's epilogue also leaves each tile's per-row (max, sum of exp), which
+    // one small pass combines into the log-sum-exp and the loss (no second read of the
+    // logits)
+    float* lsep = S(g, g->lay.lsep);
     if (bf) {
         HIPCHK(g, cast_rows(A(g, GPT2_ACT_LNF), BT, C, BA(g, BA_LNF), BA(g, BA_LNFT), nullptr, st));
         HIPCHK(g, gemm_bf16(BF16_STORE, A(g, GPT2_ACT_LOGITS), Vp, BA(g, BA_LNF), C, BA(g, BW_WTE), C, BT, V, C, nullptr,
-                            nullptr, 0, nullptr, part, st));
+                            nullptr, 0, nullptr, part, st, lsep));
     } else {
         HIPCHK(g, linear_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LNF), P(g, P_WTE), nullptr, nullptr, nullptr, BT,
-                                 V, C, part, st));
+                                 V, C, part, st, lsep));
     }
-    HIPCHK(g, lse_xent_forward(A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LOGITS_LSE), A(g, GPT2_ACT_LOSSES),
-                               targets ? tok_tgt(g) : nullptr, BT, V, flags(g), st));
+    HIPCHK(g, lse_combine(lsep, lse_partial_count(BT, V, bf), A(g, GPT2_ACT_LOGITS), Vp, A(g, GPT2_ACT_LOGITS_LSE),
+                          A(g, GPT2_ACT_LOSSES), targets ? tok_tgt(g) : nullptr, BT, V, flags(g), st));
     if (targets) HIPCHK(g, loss_mean(g->buf.grad_scratch + HDR_LOSS, A(g, GPT2_ACT_LOSSES), BT, st));
     HIPCHK(g, hipMemcpyAsync(g->host_ret, g->buf.grad_scratch, 2 * sizeof(int), hipMemcpyDeviceToHost, st));
     HIPCHK(g, hipStreamSynchronize(st));

@@ -22,9 +22,12 @@ bool gemm_set_tile_policy(int policy);
 // out[M,N] (ld ldo) = inp[M,K] . w[N,K]^T, then by the non-null extras:
 //   bias: + bias[n];  resid: out = resid + (...) (resid has ld ldo);
 //   pre:  pre = (...) and out = gelu(pre) (pre has ld ldo).
+//   lse_part (no bias/resid/pre): also the per-row log-sum-exp partials of out, for
+//   lse_combine; it holds lse_partial_floats(M, N) floats.
 hipError_t linear_forward(float* out, long ldo, const float* inp, const float* w,
                           const float* bias, const float* resid, float* pre, int M, int N, int K,
-                          float* partial, hipStream_t st);
+                          float* partial, hipStream_t st, float* lse_part = nullptr);
+size_t lse_partial_floats(int M, int N);
 // Marks a `dout` operand as logits whose gradient is formed while loading:
 // dlogit = (exp(z - lse[row]) - [col == targets[row]]) * scale.  The logits' padding
 // columns (up to the leading dimension) must be readable; their values are not used.
@@ -51,9 +54,10 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
 //   BF16_BIAS_GELU: pre = . + bias, C = gelu(pre);  BF16_ACCUM: C += .;
 //   BF16_GELU_BWD: C = . * gelu'(aux).   aux has leading dimension ldaux, pre ldc.
 enum { BF16_STORE = 0, BF16_BIAS, BF16_BIAS_RESID, BF16_BIAS_GELU, BF16_ACCUM, BF16_GELU_BWD };
+// lse_part with BF16_STORE: the log-sum-exp partials as linear_forward's.
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
                      int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
-                     hipStream_t st);
+                     hipStream_t st, float* lse_part = nullptr);
 
 // ---- bfloat16 operand copies (bf16.hip) -----------------------------------------------
 // Rounding is to nearest, ties to even.  x is (rows, cols) fp32 with leading dimension
@@ -169,9 +173,13 @@ hipError_t rope_forward(float* qkv, const float* table, int B, int T, int C, int
 hipError_t rope_backward(float* dqkv, const float* table, int B, int T, int C, int NH, hipStream_t st);
 
 // ---- softmax + cross-entropy (softmax_xent.hip) -------------------------------------
-// Per logits row (ld): lse = log sum exp; loss = lse - z[target] when targets != NULL.
-hipError_t lse_xent_forward(const float* logits, long ld, float* lse, float* losses, const int32_t* targets,
-                            int N, int V, int* flags, hipStream_t st);
+// Per logits row (ld): lse = log sum exp and, when targets != NULL, loss = lse - z[target],
+// from the partials an LSE-fused LM-head forward wrote (`parts` pairs per row,
+// lse_partial_count of its shape and arithmetic); a target outside [0, V) sets
+// ERR_BAD_TARGET_TOKEN in flags and a NaN loss.
+int lse_partial_count(int M, int N, bool bf16);
+hipError_t lse_combine(const float* lse_part, int parts, const float* logits, long ld, float* lse, float* losses,
+                       const int32_t* targets, int N, int V, int* flags, hipStream_t st);
 // Mean of losses[0..N) in double, written as float to *out.
 hipError_t loss_mean(float* out, const float* losses, int N, hipStream_t st);
 // tokens[i] = the sampled next token at logits row rows[i] for coins[i] in [0,1):

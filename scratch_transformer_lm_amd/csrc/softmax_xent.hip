@@ -2,14 +2,14 @@
 //
 // The pages list softmax_forward, crossentropy_forward and the fused
 // crossentropy_softmax_backward (huxiu page "llm.c：Andrej Karpathy带你从零复现LLM",
-// 核心代码解读 item 1).  Rows are V = 50257 floats, far too long for one wave, so a
-// 256-thread block owns a row and keeps a running (max, sum of exp) per thread
-// (rescaling the sum when the max grows); the block merges the pairs into
-// lse = max + log(sum).  The loss is lse - z[target] = -log softmax(z)[target].
-// Nothing else is written: the probabilities exp(z - lse) and the logits' gradient
-// (p - onehot)/rows are formed by the LM-head backward GEMMs as they load the logits,
-// which saves writing and re-reading two 1.6 GB tensors.  Rows are padded to a multiple
-// of 64 floats so every row starts 256-byte aligned.
+// 核心代码解读 item 1).  Rows are V = 50257 floats.  The LM-head forward GEMM's
+// epilogue leaves, for each tile and row, the (max, sum of exp) of its columns; here
+// those partials are merged into lse = max + log(sum) per row, and the loss is
+// lse - z[target] = -log softmax(z)[target].  Nothing else is written: the
+// probabilities exp(z - lse) and the logits' gradient (p - onehot)/rows are formed by
+// the LM-head backward GEMMs as they load the logits, which saves writing and
+// re-reading two 1.6 GB tensors.  Rows are padded to a multiple of 64 floats so every
+// row starts 256-byte aligned.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -18,56 +18,45 @@ namespace gpt2k {
 
 namespace {
 
-constexpr int SX_THREADS = 256;
-
-GPT2_DEV void online_add(float& m, float& s, float x) {
-    if (x > m) {
-        s = s * expf(m - x) + 1.0f;
-        m = x;
-    } else {
-        s += expf(x - m);
-    }
-}
-
-GPT2_DEV void online_merge(float& m, float& s, float m2, float s2) {
+// Log-sum-exp from the LM-head forward's partials: (max, sum) pairs in base 2, stored
+// [part][row].  A block takes 64 rows; wave q merges parts q, q+4, ... of each row (a
+// wave's loads cover 64 consecutive rows: 512 contiguous bytes), then the four waves'
+// results are merged in LDS, in order.
+constexpr int LC_ROWS = 64, LC_WAVES = 4;
+GPT2_DEV void merge2(float& m, float& s, float m2, float s2) {
     const float M = fmaxf(m, m2);
     if (M == -INFINITY) return;
-    s = s * expf(m - M) + s2 * expf(m2 - M);
+    s = s * __builtin_amdgcn_exp2f(m - M) + s2 * __builtin_amdgcn_exp2f(m2 - M);
     m = M;
 }
 
-__global__ __launch_bounds__(SX_THREADS) void lse_xent_kernel(const float* __restrict__ logits, long ld,
-                                                              float* __restrict__ lse, float* __restrict__ losses,
-                                                              const int32_t* __restrict__ targets, int V,
-                                                              int* flags) {
-    __shared__ float sm_m[SX_THREADS / 64], sm_s[SX_THREADS / 64];
-    const long row = blockIdx.x;
-    const float* z = logits + row * ld;
-    const int V4 = V >> 2;
+__global__ __launch_bounds__(LC_ROWS * LC_WAVES) void lse_combine_kernel(
+    const float2* __restrict__ part, int parts, const float* __restrict__ logits, long ld, float* __restrict__ lse,
+    float* __restrict__ losses, const int32_t* __restrict__ targets, int N, int V, int* flags) {
+    __shared__ float sm_m[LC_WAVES][LC_ROWS], sm_s[LC_WAVES][LC_ROWS];
+    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int row = blockIdx.x * LC_ROWS + lane;
     float m = -INFINITY, s = 0.f;
-    for (int i = threadIdx.x; i < V4; i += SX_THREADS) {
-        const float4 v = reinterpret_cast<const float4*>(z)[i];
-        online_add(m, s, v.x);
-        online_add(m, s, v.y);
-        online_add(m, s, v.z);
-        online_add(m, s, v.w);
-    }
-    for (int i = 4 * V4 + threadIdx.x; i < V; i += SX_THREADS) online_add(m, s, z[i]);
+    if (row < N) {
+        int pi = q;
+        for (; pi + LC_WAVES * 7 < parts; pi += LC_WAVES * 8) {
+            float2 v[8];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
-        online_merge(m, s, m2, s2);
+            for (int u = 0; u < 8; u++) v[u] = part[(long)(pi + LC_WAVES * u) * N + row];
+#pragma unroll
+            for (int u = 0; u < 8; u++) merge2(m, s, v[u].x, v[u].y);
+        }
+        for (; pi < parts; pi += LC_WAVES) {
+            const float2 v = part[(long)pi * N + row];
+            merge2(m, s, v.x, v.y);
+        }
     }
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) {
-        sm_m[wave] = m;
-        sm_s[wave] = s;
-    }
+    sm_m[q][lane] = m;
+    sm_s[q][lane] = s;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        float M = sm_m[0], S = sm_s[0];
-        for (int w = 1; w < SX_THREADS / 64; w++) online_merge(M, S, sm_m[w], sm_s[w]);
-        const float L = logf(S) + M;
+    if (q == 0 && row < N) {
+        for (int w = 1; w < LC_WAVES; w++) merge2(m, s, sm_m[w][lane], sm_s[w][lane]);
+        const float L = (m + __builtin_amdgcn_logf(s)) * 0.6931471805599453f;
         lse[row] = L;
         if (targets) {
             const int tgt = targets[row];
@@ -75,7 +64,7 @@ __global__ __launch_bounds__(SX_THREADS) void lse_xent_kernel(const float* __res
                 atomicOr(flags, ERR_BAD_TARGET_TOKEN);
                 losses[row] = NAN;
             } else {
-                losses[row] = L - z[tgt];
+                losses[row] = L - logits[(long)row * ld + tgt];
             }
         }
     }
@@ -153,20 +142,14 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
 
 }  // namespace
 
-hipError_t lse_xent_forward(const float* logits, long ld, float* lse, float* losses, const int32_t* targets,
-                            int N, int V, int* flags, hipStream_t st) {
-    if (ld % 4 || ld < V) return hipErrorInvalidValue;
-    if (N == 0) return hipSuccess;
-    ProfScope ps(st, "lse_xent_kernel", 0.0, 4.0 * ((double)N * V + 2.0 * N));
-    hipLaunchKernelGGL(lse_xent_kernel, dim3(N), dim3(SX_THREADS), 0, st, logits, ld, lse, losses, targets, V, flags);
-    return hipGetLastError();
-}
-
-hipError_t sample_tokens(const float* logits, long ld, const float* lse, const int32_t* rows, const float* coins,
-                         int n, int V, int32_t* tokens, hipStream_t st) {
-    if (n <= 0) return hipSuccess;
-    ProfScope ps(st, "sample_kernel", 0.0, 4.0 * n * ((double)V + 3));
-    hipLaunchKernelGGL(sample_kernel, dim3(n), dim3(SAMPLE_THREADS), 0, st, logits, ld, lse, rows, coins, V, tokens);
+hipError_t lse_combine(const float* lse_part, int parts, const float* logits, long ld, float* lse, float* losses,
+                       const int32_t* targets, int N, int V, int* flags, hipStream_t st) {
+    if (N <= 0) return hipSuccess;
+    if (parts <= 0 || ((uintptr_t)lse_part & 7)) return hipErrorInvalidValue;
+    ProfScope ps(st, "lse_combine_kernel", 0.0, 8.0 * (double)N * parts + 12.0 * N);
+    hipLaunchKernelGGL(lse_combine_kernel, dim3((N + LC_ROWS - 1) / LC_ROWS), dim3(LC_ROWS * LC_WAVES), 0, st,
+                       reinterpret_cast<const float2*>(lse_part), parts, logits, ld, lse, losses, targets, N, V,
+                       flags);
     return hipGetLastError();
 }
 
