@@ -12,7 +12,7 @@
 //              zeros, since k runs over the rows.
 // One 64x64-tile kernel reads an fp32 tensor once and writes the straight copy, the
 // transposed copy (through LDS) and, for an output gradient, the bias gradient's column
-// sums per 64-row block (the bias gradient is summed from the unrounded fp32 values).
+// sums per 128-row block (the bias gradient is summed from the unrounded fp32 values).
 // The LM head's output gradient, softmax minus one-hot over the rows' log-sum-exp, is
 // formed by the same kernel from the logits.  All of these kernels are bound by HBM.
 #include "common.h"
@@ -40,63 +40,83 @@ struct XentArgs {
     int V;
 };
 
-// Grid (column tiles, row tiles over rows rounded up to 64, batch).  XENT: the input is
-// the logits and each element becomes its loss gradient first.
+// Grid (column tiles of 64, row blocks of RB = 128 over rows rounded up to 64, batch).
+// XENT: the input is the logits and each element becomes its loss gradient first.
+constexpr int RB = 128;
 template <bool XENT>
 __global__ __launch_bounds__(CT_THREADS) void cast_tile_kernel(CastArgs a, XentArgs xa) {
-    __shared__ float tile[TILE][LDT];
+    __shared__ float tile[RB][LDT];
     const int t = threadIdx.x;
-    const int c0 = blockIdx.x * TILE, r0 = blockIdx.y * TILE, z = blockIdx.z;
+    const int c0 = blockIdx.x * TILE, r0 = blockIdx.y * RB, z = blockIdx.z;
     const float* x = a.x + (long)z * a.sx;
-    // load: 16 threads per row (4 columns each), 16 rows per pass
+    // load: 16 threads per row (4 columns each), 16 rows per pass, 8 passes in flight
     const int c4 = t & 15, rr = t >> 4;
     const int col = c0 + 4 * c4;
+    float4 v[RB / 16];
 #pragma unroll
-    for (int j = 0; j < TILE / 16; j++) {
+    for (int j = 0; j < RB / 16; j++) {
+        const int r = r0 + rr + 16 * j;
+        v[j] = (r < a.rows && col < a.cols) ? *reinterpret_cast<const float4*>(x + (long)r * a.ldx + col)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < RB / 16; j++) {
         const int row = rr + 16 * j, r = r0 + row;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < a.rows && col < a.cols) {
-            v = *reinterpret_cast<const float4*>(x + (long)r * a.ldx + col);
-            if (XENT) {
-                const float l = xa.lse[r];
-                const int tg = xa.targets[r];
-                float e[4] = {v.x, v.y, v.z, v.w};
+        if (XENT && r < a.rows && col < a.cols) {
+            const float l = xa.lse[r];
+            const int tg = xa.targets[r];
+            float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int c = col + i;
-                    e[i] = c < xa.V ? (__expf(e[i] - l) - (c == tg ? 1.f : 0.f)) * xa.scale : 0.f;
-                }
-                v = make_float4(e[0], e[1], e[2], e[3]);
+            for (int i = 0; i < 4; i++) {
+                const int c = col + i;
+                e[i] = c < xa.V ? (__expf(e[i] - l) - (c == tg ? 1.f : 0.f)) * xa.scale : 0.f;
             }
-            if (a.xb) {
-                uint2 o;
-                o.x = pack2(v.x, v.y);
-                o.y = pack2(v.z, v.w);
-                *reinterpret_cast<uint2*>(a.xb + (long)z * a.sb + (long)r * a.ldb + col) = o;
-            }
+            v[j] = make_float4(e[0], e[1], e[2], e[3]);
         }
-        tile[row][4 * c4 + 0] = v.x;
-        tile[row][4 * c4 + 1] = v.y;
-        tile[row][4 * c4 + 2] = v.z;
-        tile[row][4 * c4 + 3] = v.w;
+        if (a.xb && r < a.rows && col < a.cols) {
+            uint2 o;
+            o.x = pack2(v[j].x, v[j].y);
+            o.y = pack2(v[j].z, v[j].w);
+            *reinterpret_cast<uint2*>(a.xb + (long)z * a.sb + (long)r * a.ldb + col) = o;
+        }
+        tile[row][4 * c4 + 0] = v[j].x;
+        tile[row][4 * c4 + 1] = v[j].y;
+        tile[row][4 * c4 + 2] = v[j].z;
+        tile[row][4 * c4 + 3] = v[j].w;
     }
     __syncthreads();
     if (a.xt) {
-        // transposed: thread (cc, s) writes rows 16s..16s+15 of column cc as 16 bf16
+        // transposed: thread (cc, s) writes 16 rows of column cc as 16 bf16 per pass; rows
+        // past the padded count (a multiple of 64) are not stored
         const int cc = t >> 2, s = t & 3;
+        const long rpad = (a.rows + TILE - 1) / TILE * TILE;
         if (c0 + cc < a.cols) {
-            uint32_t w[8];
 #pragma unroll
-            for (int i = 0; i < 8; i++) w[i] = pack2(tile[16 * s + 2 * i][cc], tile[16 * s + 2 * i + 1][cc]);
-            uint4* q = reinterpret_cast<uint4*>(a.xt + (long)z * a.st + (long)(c0 + cc) * a.ldt + r0 + 16 * s);
-            q[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            q[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            for (int h = 0; h < RB / 64; h++) {
+                const int rl = 64 * h + 16 * s;
+                if (r0 + rl < rpad) {
+                    uint32_t w[8];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) w[i] = pack2(tile[rl + 2 * i][cc], tile[rl + 2 * i + 1][cc]);
+                    uint4* q = reinterpret_cast<uint4*>(a.xt + (long)z * a.st + (long)(c0 + cc) * a.ldt + r0 + rl);
+                    q[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                    q[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                }
+            }
         }
     }
-    if (a.bpart && t < TILE && c0 + t < a.cols) {
-        float s = 0.f;
-        for (int i = 0; i < TILE; i++) s += tile[i][t];
-        a.bpart[(long)blockIdx.y * a.cols + c0 + t] = s;
+    if (a.bpart) {
+        // column sums of the block's rows: four threads per column, 32 rows each, added in
+        // a fixed order
+        __shared__ float ps[4][TILE];
+        const int cl = t & 63, q = t >> 6;
+        float sum = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < RB / 4; i++) sum += tile[q * (RB / 4) + i][cl];
+        ps[q][cl] = sum;
+        __syncthreads();
+        if (q == 0 && c0 + cl < a.cols)
+            a.bpart[(long)blockIdx.y * a.cols + c0 + cl] = ((ps[0][cl] + ps[1][cl]) + ps[2][cl]) + ps[3][cl];
     }
 }
 
@@ -143,7 +163,7 @@ hipError_t launch_cast(const CastArgs& a, const XentArgs& xa, hipStream_t st, co
     if (a.xb && (a.ldb % 8 || a.ldb < a.cols || !a16(a.xb))) return hipErrorInvalidValue;
     if (a.xt && (a.ldt % 8 || a.ldt < pad64(a.rows) || !a16(a.xt))) return hipErrorInvalidValue;
     if (a.rows == 0 || a.cols == 0) return hipSuccess;
-    const dim3 grid((unsigned)((a.cols + TILE - 1) / TILE), (unsigned)(pad64(a.rows) / TILE), (unsigned)a.batch);
+    const dim3 grid((unsigned)((a.cols + TILE - 1) / TILE), (unsigned)((pad64(a.rows) + RB - 1) / RB), (unsigned)a.batch);
     const double n = (double)a.rows * a.cols * a.batch;
     ProfScope ps(st, name, 0.0, n * (4.0 + (a.xb ? 2.0 : 0.0) + (a.xt ? 2.0 : 0.0)));
     hipLaunchKernelGGL((cast_tile_kernel<XENT>), grid, dim3(CT_THREADS), 0, st, a, xa);
@@ -152,7 +172,7 @@ hipError_t launch_cast(const CastArgs& a, const XentArgs& xa, hipStream_t st, co
 
 }  // namespace
 
-size_t bias_partial_floats(int rows, int cols) { return (size_t)((rows + TILE - 1) / TILE) * (size_t)cols; }
+size_t bias_partial_floats(int rows, int cols) { return (size_t)((rows + RB - 1) / RB) * (size_t)cols; }
 
 hipError_t cast_bf16(const CastArgs& a, hipStream_t st) {
     return launch_cast<false>(a, XentArgs{nullptr, nullptr, 0.f, 0}, st, "cast_tile_kernel<false>");
@@ -160,7 +180,7 @@ hipError_t cast_bf16(const CastArgs& a, hipStream_t st) {
 
 hipError_t bias_reduce(float* db, const float* bpart, int rows, int cols, hipStream_t st) {
     if (rows <= 0 || cols <= 0) return hipSuccess;
-    const int nrb = (rows + TILE - 1) / TILE;
+    const int nrb = (rows + RB - 1) / RB;
     ProfScope ps(st, "bias_reduce_kernel", 0.0, 4.0 * ((double)nrb * cols + 2.0 * cols));
     hipLaunchKernelGGL(bias_reduce_kernel, dim3((cols + TILE - 1) / TILE), dim3(TILE * BR_GROUPS), 0, st, db, bpart,
                        nrb, cols);

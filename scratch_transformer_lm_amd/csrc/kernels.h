@@ -65,7 +65,7 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
 //   xb (optional): (rows, cols) bf16, leading dimension ldb (a multiple of 8).
 //   xt (optional): the transpose (cols, rows_pad) bf16, leading dimension ldt >= rows_pad,
 //     rows_pad = rows rounded up to 64, columns rows..rows_pad-1 zero.
-//   bpart (optional): per 64-row block rb, bpart[rb * cols + c] = sum of x[r, c] over its
+//   bpart (optional): per 128-row block rb, bpart[rb * cols + c] = sum of x[r, c] over its
 //     rows in order; bias_reduce then adds them into db in block order.
 // cols must be a multiple of 4.
 struct CastArgs {

@@ -142,6 +142,15 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
 
 }  // namespace
 
+hipError_t sample_tokens(const float* logits, long ld, const float* lse, const int32_t* rows, const float* coins,
+                         int n, int V, int32_t* tokens, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    ProfScope ps(st, "sample_kernel", 0.0, 4.0 * n * ((double)V + 3));
+    hipLaunchKernelGGL(sample_kernel, dim3(n), dim3(SAMPLE_THREADS), 0, st, logits, ld, lse, rows, coins, V, tokens);
+    return hipGetLastError();
+}
+
+
 hipError_t lse_combine(const float* lse_part, int parts, const float* logits, long ld, float* lse, float* losses,
                        const int32_t* targets, int N, int V, int* flags, hipStream_t st) {
     if (N <= 0) return hipSuccess;

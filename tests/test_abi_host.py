@@ -26,6 +26,19 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, n), n
 
 
+def test_library_defines_every_internal_symbol():
+    """A shared library links with unresolved symbols and fails only when loaded: every
+    gpt2k:: function the library calls must be defined in it (weak TLS helpers aside)."""
+    import shutil
+    import subprocess
+    if not shutil.which("nm"):
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-C", "-u", G.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    missing = [l.strip() for l in out.splitlines()
+               if ("gpt2k::" in l or "gpt2_" in l) and not l.split()[0] in ("w", "v")]
+    assert not missing, missing
+
+
 def closed_form(m):
     V, C, L, T = m.vocab_size, m.channels, m.num_layers, m.max_seq_len
     return V * C + T * C + L * (12 * C * C + 13 * C) + 2 * C
