@@ -245,15 +245,16 @@ def test_backward_stream_schedules_agree_bitwise(G):
 SAMPLE_SLACK = 2e-6  # coin distance from a cumulative boundary within which either side may differ
 
 
-def sample_valid(probs, coin, token):
+def sample_valid(probs, coin, token, slack=None):
     """`token` is the oracle's sample_mult pick, or a neighbour the coin is within
     SAMPLE_SLACK of (the GPU forms fp32 probabilities; the oracle's are float64)."""
     from oracle import oracle as O
+    slack = SAMPLE_SLACK if slack is None else slack
     if token == O.sample_mult(probs, coin):
         return True
     cdf = np.cumsum(np.asarray(probs, dtype=np.float64))
     lo = cdf[token - 1] if token > 0 else 0.0
-    return 0 <= token < len(probs) and lo - SAMPLE_SLACK <= coin < cdf[token] + SAMPLE_SLACK
+    return 0 <= token < len(probs) and lo - slack <= coin < cdf[token] + slack
 
 
 def test_sample_matches_oracle(G):
@@ -297,27 +298,32 @@ def test_sample_needs_a_forward(G):
     assert e.value.code == G.GPT2_ESTATE
 
 
-def test_generate_matches_oracle(G):
+@pytest.mark.parametrize("variant", [0, 4])
+def test_generate_matches_oracle(G, variant):
     """gpt2_generate on the tiny model from the end-of-text token (V-1): every generated
     token is checked against the oracle run on the GPU's own prefix, so one boundary
-    coin cannot derail the rest of the comparison."""
+    coin cannot derail the rest of the comparison.  The forwards run on 1..39 rows, below
+    every tile size.  In the mixed-precision variant a bf16 rounding flip can move a
+    logit by up to 2^-7 of one product term (the tiny model's logits are O(0.1)), so a
+    coin within 1e-3 of the oracle's cumulative probability counts as a boundary."""
     from oracle import oracle as O
     w = S.TINY
-    say("[generate]")
+    say(f"[generate] variant {variant}")
     params = S.init_params(w.model)
     V = w.model.vocab_size
     total = 40
     coins = np.random.default_rng(33).random(total).astype(np.float32)
-    m = G.GPT2(w.model, w.B, w.T)
+    m = G.GPT2(w.model, w.B, w.T, variant=variant)
     m.params.copy_(dev(params))
     toks = m.generate([V - 1], total, coins)
     assert toks[0] == V - 1 and np.all((toks >= 0) & (toks < V))
-    o = O.OracleGPT2(w.model, 1, total - 1, params)
+    o = O.OracleGPT2(w.model, 1, total - 1, params, variant=variant)
+    slack = SAMPLE_SLACK if variant == 0 else 1e-3
     exact = 0
     for t in range(1, total):
         o.forward(toks[None, :t], None)
         p = o.activation("probs").reshape(1 * t, -1)[t - 1]
-        assert sample_valid(p, float(coins[t - 1]), int(toks[t])), t
+        assert sample_valid(p, float(coins[t - 1]), int(toks[t]), slack), t
         exact += int(toks[t]) == O.sample_mult(p, float(coins[t - 1]))
     say(f"generated {total - 1} tokens, {exact} identical to the oracle's picks")
     assert exact >= total - 2
