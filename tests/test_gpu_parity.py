@@ -211,17 +211,29 @@ def test_gemm_tile_widths(G, tiles, wl):
         G.set_gemm_tiles(G.GEMM_TILES_AUTO)
 
 
-def test_backward_stream_schedules_agree_bitwise(G):
+# (workload, variant) pairs for the schedule tests: the base model, and the mixed-precision
+# variant both at the same shape and where its weight gradients run as split-K rounds
+SPLIT_K_SHAPE = S.Workload("gpt2 L1 C512 H8 V512 B4 T1024", S.ModelShape(1024, 512, 1, 8, 512), 4, 1024)
+SCHEDULE_CASES = [("124m", 0), ("124m", 4), ("split-k", 4)]
+
+
+def schedule_workload(name):
+    return S.GPT2_124M_SHORT if name == "124m" else SPLIT_K_SHAPE
+
+
+@pytest.mark.parametrize("wl,variant", SCHEDULE_CASES)
+def test_backward_stream_schedules_agree_bitwise(G, wl, variant):
     """The default backward overlaps the weight gradients on a second stream; the
     single-stream schedule runs the same kernels in one order.  Two steps each: losses,
-    gradients and updated parameters must be bitwise equal."""
-    w = S.GPT2_124M_SHORT
-    say("[backward streams]")
+    gradients and updated parameters must be bitwise equal (in the mixed-precision
+    variant this also covers the bf16 copies that the stream events order)."""
+    w = schedule_workload(wl)
+    say(f"[backward streams] {w.name} variant {variant}")
     params = S.init_params(w.model)
     x, y = S.tokens(w)
     runs = []
     for streams in (2, 1):
-        m = G.GPT2(w.model, w.B, w.T)
+        m = G.GPT2(w.model, w.B, w.T, variant=variant)
         m.set_backward_streams(streams)
         m.params.copy_(dev(params))
         tx, ty = dev(x, torch.int32), dev(y, torch.int32)
@@ -370,17 +382,18 @@ def test_variant_tiny_forward_activations(G):
     assert max(errs.values()) <= 1e-5, errs
 
 
-def test_backward_update_is_backward_then_update_bitwise(G):
+@pytest.mark.parametrize("wl,variant", SCHEDULE_CASES)
+def test_backward_update_is_backward_then_update_bitwise(G, wl, variant):
     """gpt2_backward_update (each layer's AdamW as soon as its gradients are final) against
     gpt2_backward + gpt2_update, with both backward schedules: losses, gradients, params
     and both moments bitwise equal after three steps with weight decay."""
-    w = S.GPT2_124M_SHORT
-    say("[backward_update]")
+    w = schedule_workload(wl)
+    say(f"[backward_update] {w.name} variant {variant}")
     params = S.init_params(w.model)
     x, y = S.tokens(w)
     runs = []
     for fused, streams in ((False, 2), (True, 2), (True, 1)):
-        m = G.GPT2(w.model, w.B, w.T)
+        m = G.GPT2(w.model, w.B, w.T, variant=variant)
         m.set_backward_streams(streams)
         m.params.copy_(dev(params))
         tx, ty = dev(x, torch.int32), dev(y, torch.int32)
@@ -596,8 +609,7 @@ def test_bf16_split_k_weight_gradients(G):
     """One layer at C=512 with B*T = 4096: the fc and fcproj weight gradients (64 output
     tiles, k = 4096) run as 8-way split-K rounds, k-segment first, with the segment
     partials added by the split-K fix-up (the full-size shapes take this path too)."""
-    w = S.Workload("gpt2 L1 C512 H8 V512 B4 T1024", S.ModelShape(1024, 512, 1, 8, 512), 4, 1024)
-    check_training(G, w, 1, variant=G.VARIANT_BF16)
+    check_training(G, SPLIT_K_SHAPE, 1, variant=G.VARIANT_BF16)
 
 
 def test_bf16_ragged_shape(G):
