@@ -455,16 +455,25 @@ def test_embedding_backward_paths(G, B, T):
 
 # ------------------------------------------------------------------ full context (sampled)
 
-def full_context_check(G, w, rows):
+def full_context_check(G, w, rows, variant=0):
     """One step at the full shape: sampled per-position losses against the oracle run on
     single rows, then properties that hold at any size: the gradient is the derivative of
     the GPU's own loss along the gradient, both embeddings receive the same total
-    gradient, and the first AdamW step has a closed form."""
+    gradient, and the first AdamW step has a closed form.
+
+    Mixed-precision variant: each sampled row's bound is max(LOSS_RTOL, F32_FACTOR x the
+    error of the oracle's own float32 build on that row) (bf16 rounding flips, as in
+    check_training); conservation holds exactly only when every row of the logits'
+    gradient sums to zero, which its bf16 rounding breaks slightly (measured 5e-5, the
+    same 1e-3 bound applies); and the directional derivative may differ by 1e-2 (the
+    straight-through backward differs from the exact derivative by about the 3e-3
+    gradient error the oracle itself shows)."""
     from oracle import oracle as O
-    say(f"[full] {w.name}")
+    bf = bool(variant & G.VARIANT_BF16)
+    say(f"[full] {w.name} variant {variant}")
     params = S.init_params(w.model)
     x, y = S.tokens(w)
-    m = G.GPT2(w.model, w.B, w.T)
+    m = G.GPT2(w.model, w.B, w.T, variant=variant)
     m.params.copy_(dev(params))
     tx, ty = dev(x, torch.int32), dev(y, torch.int32)
     loss = m.forward(tx, ty)
@@ -473,14 +482,21 @@ def full_context_check(G, w, rows):
     assert abs(loss - losses.astype(np.float64).mean()) <= 1e-6 * loss
     for r in rows:
         say(f"[full] oracle row {r}")
-        o = O.OracleGPT2(w.model, 1, w.T, params, forward_only=True)
+        o = O.OracleGPT2(w.model, 1, w.T, params, forward_only=True, variant=variant)
         o.forward(x[r:r + 1], y[r:r + 1])
         ref = o.activation("losses")
         err = rel_max(losses[r], ref)
-        say(f"row {r}: per-position loss rel err {err:.2e}")
-        assert err <= LOSS_RTOL
+        tol = LOSS_RTOL
         o.close()
         del o
+        if bf:
+            o32 = O.OracleGPT2(w.model, 1, w.T, params, "f32", forward_only=True, variant=variant)
+            o32.forward(x[r:r + 1], y[r:r + 1])
+            tol = max(LOSS_RTOL, F32_FACTOR * rel_max(o32.activation("losses"), ref))
+            o32.close()
+            del o32
+        say(f"row {r}: per-position loss rel err {err:.2e} (bound {tol:.2e})")
+        assert err <= tol
     m.zero_grad()
     assert m.backward() == 0
     g = m.grads.clone()
@@ -505,7 +521,7 @@ def full_context_check(G, w, rows):
     m.params.copy_(p0)
     fd = (lp - lm) / (2 * h)
     say(f"fd {fd:.6e} vs |g|^2 {gn * gn:.6e}")
-    assert abs(fd - gn * gn) <= 5e-3 * gn * gn
+    assert abs(fd - gn * gn) <= (1e-2 if bf else 5e-3) * gn * gn
     # first AdamW step: p1 = p0 - lr (g/(|g|+eps) + wd p0)
     assert m.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1) == 0
     gd, pd = g.double(), p0.double()
@@ -521,6 +537,12 @@ def test_gpt2_124m_full_context(G):
 
 def test_gpt2_350m_full_context(G):
     full_context_check(G, S.GPT2_350M, rows=(3,))
+
+
+def test_bf16_124m_full_context(G):
+    """The mixed-precision variant at the shape and launch configuration the benchmark
+    times (124M, B=8, T=1024)."""
+    full_context_check(G, S.GPT2_124M, rows=(0, 7), variant=G.VARIANT_BF16)
 
 
 # ------------------------------------------------------------------ ABI behaviour on GPU
