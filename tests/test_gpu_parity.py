@@ -422,6 +422,16 @@ def test_gpt2_124m_ragged_shape(G):
     check_training(G, S.GPT2_124M_SHORT, 1, B=3, T=100)
 
 
+@pytest.mark.parametrize("heads", [4, 2])
+@pytest.mark.parametrize("variant", [0, 4])
+def test_head_sizes_multi_tile(G, heads, variant):
+    """Head sizes 16 and 32 (C=64 with 4 or 2 heads) at T=80: two query/key tiles, the
+    second ragged, in the fp32 and the mixed-precision attention kernels; three steps
+    against the oracle."""
+    w = S.Workload(f"gpt2 L2 C64 H{heads} V512 B2 T80", S.ModelShape(128, 512, 2, heads, 64), 2, 80)
+    check_training(G, w, 3, variant=variant)
+
+
 def test_smaller_batch_than_built(G):
     w = S.TINY
     say("[smaller batch]")
