@@ -48,15 +48,16 @@ GPT2_DEV f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_
 GPT2_DEV bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u)); }
 GPT2_DEV bf16x8 ld8(const uint16_t* p) { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p)); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs)
-GPT2_DEV uint32_t bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// fp32 pair -> packed bf16, round to nearest, ties to even: one v_cvt_pk_bf16_f32
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+GPT2_DEV uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 GPT2_DEV float bf16_float(uint32_t b) { return __uint_as_float(b << 16); }
 
-// x = hi + mid + lo + r, |r| <= 2^-24 |x|, with hi, mid, lo bf16 (see the header)
+// x = hi + mid + lo + r, |r| <= 2^-24 |x|, with hi, mid, lo bf16 (see the header); each
+// rounding of a pair is one v_cvt_pk_bf16_f32 (round to nearest, ties to even)
 struct Split3 {
     bf16x8 p[3];
 };
@@ -64,13 +65,12 @@ GPT2_DEV Split3 split8(const float (&x)[8]) {
     uint32_t w[3][4];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        float r0 = x[2 * e], r1 = x[2 * e + 1];
+        f32x2 r = {x[2 * e], x[2 * e + 1]};
 #pragma unroll
         for (int k = 0; k < 3; k++) {
-            const uint32_t b0 = bf16_bits(r0), b1 = bf16_bits(r1);
-            w[k][e] = b0 | (b1 << 16);
-            r0 -= bf16_float(b0);
-            r1 -= bf16_float(b1);
+            const bf16x2 h = __builtin_convertvector(r, bf16x2);
+            w[k][e] = __builtin_bit_cast(uint32_t, h);
+            r -= __builtin_convertvector(h, f32x2);
         }
     }
     Split3 s;
@@ -128,8 +128,8 @@ __global__ __launch_bounds__(NTH) void attn_prep_kernel(PrepArgs a) {
             v = *reinterpret_cast<const float4*>(src + (long)tok * a.ld + d4);
             if (rm) {
                 uint2 o;
-                o.x = bf16_bits(v.x) | (bf16_bits(v.y) << 16);
-                o.y = bf16_bits(v.z) | (bf16_bits(v.w) << 16);
+                o.x = pack2(v.x, v.y);
+                o.y = pack2(v.z, v.w);
                 *reinterpret_cast<uint2*>(rm + ((long)bh * a.T + tok) * HS + d4) = o;
             }
         }
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NTH) void attn_prep_kernel(PrepArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; e++)
-            w[e] = bf16_bits(tile[tok_of_pos(pos0 + 2 * e)][d]) | (bf16_bits(tile[tok_of_pos(pos0 + 2 * e + 1)][d]) << 16);
+            w[e] = pack2(tile[tok_of_pos(pos0 + 2 * e)][d], tile[tok_of_pos(pos0 + 2 * e + 1)][d]);
         *reinterpret_cast<uint4*>(tr + ((long)bh * HS + d) * a.Tp + t0 + pos0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }

@@ -25,13 +25,12 @@ namespace {
 
 constexpr int TILE = 64, CT_THREADS = 256, LDT = TILE + 1;
 
-// fp32 -> bf16, round to nearest, ties to even (finite inputs)
-GPT2_DEV uint32_t bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// fp32 pair -> packed bf16, round to nearest, ties to even: one v_cvt_pk_bf16_f32
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+GPT2_DEV uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
-GPT2_DEV uint32_t pack2(float lo, float hi) { return bf16_bits(lo) | (bf16_bits(hi) << 16); }
 
 struct XentArgs {
     const float* lse;
