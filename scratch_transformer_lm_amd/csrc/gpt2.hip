@@ -165,7 +165,7 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
         const size_t n[NBS] = {BT * 4 * C, C * BTp, 4 * C * BTp, 3 * C * BTp, BT * y.Vp, y.Vp * BTp, BT * C,
                                attn_bf16_head_elems(B, T, (int)C)};
         for (int i = 0; i < NBS; i++) y.bs[i] = take((n[i] + 1) / 2);
-        y.bpart = take(bias_partial_floats((int)BT, (int)(4 * C)));
+        y.bpart = take(4 * bias_partial_floats((int)BT, (int)(4 * C)));  // one per output-gradient kind
     }
     y.n_scratch = s;
     return y;
@@ -485,17 +485,21 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     auto after = [&](hipStream_t s, int e) { return hipStreamWaitEvent(s, g->ev[e], 0); };
     // Mixed precision: every GEMM below multiplies bf16 copies.  dlogits is written once
     // in bf16, straight and transposed; each output gradient dY gets its copies (and its
-    // bias gradient, from the fp32 values) on the main stream before its GEMMs, the
-    // transposed ones in buffers per kind that the events below protect exactly as they
-    // protect dY itself.
+    // bias gradient's partial sums, from the fp32 values) on the main stream before its
+    // GEMMs, the transposed ones in buffers per kind that the events below protect exactly
+    // as they protect dY itself.
     const bool bf = bf_on(g);
     const long BTp = (long)pad64(BT);
-    float* bpart = bf ? S(g, g->lay.bpart) : nullptr;
     uint16_t* dyb = bf ? BS(g, BS_DY) : nullptr;
-    auto grad_copies = [&](const float* dy, int n, uint16_t* yt, float* db) -> hipError_t {
-        const hipError_t e = cast_rows(dy, BT, n, dyb, yt, bpart, st);
-        return e != hipSuccess ? e : bias_reduce(db, bpart, BT, n, st);
+    // the bias gradient's column sums per row block, one buffer per kind of dY (0 fcproj,
+    // 1 fc, 2 attproj, 3 qkv): the second stream adds them up (bias_w) ahead of the kind's
+    // wgrad, and the events that let the main stream rewrite that kind's dY (or its
+    // transposed copy) in the next layer come after it
+    auto bpart = [&](int kind) { return S(g, g->lay.bpart) + (size_t)kind * bias_partial_floats(BT, 4 * C); };
+    auto grad_copies = [&](const float* dy, int n, uint16_t* yt, int kind) -> hipError_t {
+        return cast_rows(dy, BT, n, dyb, yt, bpart(kind), st);
     };
+    auto bias_w = [&](float* db, int n, int kind) { return bias_reduce(db, bpart(kind), BT, n, sw); };
     // dW[M,N] += dY^T X (and, fp32 only, db += column sums of dY): dY (BT, M), X (BT, N)
     auto wgrad = [&](float* dw, float* db, const float* dy, const uint16_t* yt, int M, const float* x,
                      const uint16_t* xt, int N) {
@@ -543,9 +547,10 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         const bool later = l < L - 1;  // the previous iteration's weight gradients exist
         // MLP projection: residual3 = residual2 + gelu(fch) . Wp^T + bp.
-        if (bf) HIPCHK(g, grad_copies(dres, C, BS(g, BS_DREST), G(g, P_FCPROJB) + l * C));
+        if (bf) HIPCHK(g, grad_copies(dres, C, BS(g, BS_DREST), 0));
         HIPCHK(g, mark(EV_DRES_A, st));
         HIPCHK(g, after(sw, EV_DRES_A));
+        if (bf) HIPCHK(g, bias_w(G(g, P_FCPROJB) + l * C, C, 0));
         HIPCHK(g, wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, G(g, P_FCPROJB) + l * C, dres, BS(g, BS_DREST), C,
                         A(g, GPT2_ACT_FCH_GELU, l), BA(g, BA_FCHGT, l), 4 * C));
         HIPCHK(g, mark(EV_W_FCPROJ, sw));
@@ -553,9 +558,10 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         HIPCHK(g, dgrad(dfch, dres, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, BA(g, BWT_P, l), 4 * C,
                         A(g, GPT2_ACT_FCH, l)));
         // MLP expansion: fch = ln2 . Wf^T + bf.
-        if (bf) HIPCHK(g, grad_copies(dfch, 4 * C, BS(g, BS_DFCHT), G(g, P_FCB) + l * 4 * C));
+        if (bf) HIPCHK(g, grad_copies(dfch, 4 * C, BS(g, BS_DFCHT), 1));
         HIPCHK(g, mark(EV_DFCH, st));
         HIPCHK(g, after(sw, EV_DFCH));
+        if (bf) HIPCHK(g, bias_w(G(g, P_FCB) + l * 4 * C, 4 * C, 1));
         HIPCHK(g, wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, G(g, P_FCB) + l * 4 * C, dfch, BS(g, BS_DFCHT), 4 * C,
                         A(g, GPT2_ACT_LN2, l), BA(g, BA_LN2T, l), C));
         HIPCHK(g, mark(EV_W_FC, sw));
@@ -565,9 +571,10 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
                            P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C, true,
                            true, part, st));
         // Attention projection: residual2 = residual + atty . Wa^T + ba.
-        if (bf) HIPCHK(g, grad_copies(dres, C, BS(g, BS_DREST), G(g, P_ATTPROJB) + l * C));
+        if (bf) HIPCHK(g, grad_copies(dres, C, BS(g, BS_DREST), 2));
         HIPCHK(g, mark(EV_DRES_B, st));
         HIPCHK(g, after(sw, EV_DRES_B));
+        if (bf) HIPCHK(g, bias_w(G(g, P_ATTPROJB) + l * C, C, 2));
         HIPCHK(g, wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, G(g, P_ATTPROJB) + l * C, dres, BS(g, BS_DREST), C,
                         A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTYT, l), C));
         HIPCHK(g, mark(EV_W_ATTPROJ, sw));
@@ -587,9 +594,10 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
         // rotary variant: attention gave the gradient of the rotated q and k; rotate it back
         if (rope_on(g)) HIPCHK(g, rope_backward(dqkv, S(g, g->lay.rope), B, T, C, NH, st));
-        if (bf) HIPCHK(g, grad_copies(dqkv, 3 * C, BS(g, BS_DQKVT), G(g, P_QKVB) + l * 3 * C));
+        if (bf) HIPCHK(g, grad_copies(dqkv, 3 * C, BS(g, BS_DQKVT), 3));
         HIPCHK(g, mark(EV_DQKV, st));
         HIPCHK(g, after(sw, EV_DQKV));
+        if (bf) HIPCHK(g, bias_w(G(g, P_QKVB) + l * 3 * C, 3 * C, 3));
         HIPCHK(g, wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, BS(g, BS_DQKVT), 3 * C,
                         A(g, GPT2_ACT_LN1, l), BA(g, BA_LN1T, l), C));
         HIPCHK(g, mark(EV_W_QKV, sw));
