@@ -72,9 +72,9 @@ int gpt2_param_layout(const gpt2_config* cfg, size_t off[GPT2_NUM_PARAM_TENSORS]
  * activation arena and the gradient scratch arena.  Host-only. */
 int gpt2_arena_sizes(const gpt2_config* cfg, int B, int T, size_t* n_acts, size_t* n_grad_scratch);
 /* The same for a model built with gpt2_build_variant(..., variant): GPT2_VARIANT_BF16
- * adds the bfloat16 operand copies (weights, their transposes, the linear layers' inputs
- * and their transposes in the activation arena; the output-gradient copies in the
- * scratch).  GPT2_EINVAL for an unknown bit. */
+ * adds the bfloat16 operand copies (weights, their transposes and the linear layers'
+ * inputs in the activation arena; the output-gradient copies in the scratch).
+ * GPT2_EINVAL for an unknown bit. */
 int gpt2_arena_sizes_variant(const gpt2_config* cfg, int B, int T, int variant, size_t* n_acts,
                              size_t* n_grad_scratch);
 

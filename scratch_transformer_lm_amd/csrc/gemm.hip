@@ -81,6 +81,20 @@ struct KTileOf<true, true, BN> {
     static constexpr int BK = BN == 256 ? GEMM_BF256_BK : GEMM_BF_BK;
     static constexpr int STAGES = BN == 256 ? GEMM_BF256_STAGES : GEMM_BF_STAGES;
 };
+// bf16 operands stored row-contiguous, [k][rows] (the weight gradient's dY and X as the
+// forward and backward write them): k-tiles of GEMM_BFT_BK k rows, a 128-row tile row
+// being 256 bytes, so a k-tile takes as much LDS as the k-contiguous bf16 one.
+#ifndef GEMM_BFT_BK
+#define GEMM_BFT_BK 64
+#endif
+#ifndef GEMM_BFT_STAGES
+#define GEMM_BFT_STAGES 2
+#endif
+template <int BN>
+struct KTileOf<false, true, BN> {
+    static constexpr int BK = GEMM_BFT_BK;
+    static constexpr int STAGES = GEMM_BFT_STAGES;
+};
 constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse slots
 constexpr int GROUP_M = 8;
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
@@ -436,6 +450,62 @@ GPT2_DEV void fill_rcontig(float* S, const float* X, long ld, int r0, int nrows,
     }
 }
 
+// bf16 row-contiguous tiles, [k][128] bf16 (256 bytes a k row, sixteen 16-byte chunks):
+// chunk c of k row kr sits at chunk position c ^ trswz(kr).  A fragment is read with
+// ds_read_b64_tr_b16, which hands lane i of a 16-lane group the i-th 16-bit value of each
+// of the four 8-byte pieces that lanes 4e..4e+3 of the group loaded: lanes 4e + h load
+// k row kb + e, rows 4h..4h+3 of the fragment, so lane i gets rows i of k rows kb..kb+3,
+// the A (or B) operand layout of v_mfma_f32_16x16x32_bf16 (a second read gives k rows
+// kb+4..kb+7).  One read instruction covers 16 k rows (kb = 8g for lane group g), 32 bytes
+// of each; the swizzle puts them in the 8 32-byte bank windows of a 256-byte LDS row, two
+// each: window (r/16) ^ ((kr & 3) | (kr & 8) >> 1).
+GPT2_DEV int trswz(int kr) { return ((kr & 3) | ((kr >> 1) & 4)) << 1; }
+
+// Per-lane byte offsets of a bf16 row-contiguous tile's transfers from the element (k 0,
+// row r0) of X[k*ld + r] (ld in bf16 elements, a multiple of 8): LDS chunk 64q + l (q =
+// 4j + wave) holds chunk (ch % 16) ^ trswz(ch / 16) of k row ch / 16.  Chunks past the
+// end of a row are clamped to its last chunk (they only feed outputs never stored).
+template <int BK>
+GPT2_DEV void tr_offsets(unsigned (&off)[BK / 16], long ld, int r0) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < BK / 16; j++) {
+        const int ch = (j * 4 + w) * 64 + l;
+        const int kr = ch >> 4, c = (ch & 15) ^ trswz(ch >> 4);
+        const long r = (long)r0 + 8 * c < ld - 8 ? (long)r0 + 8 * c : ld - 8;
+        off[j] = (unsigned)(((long)kr * ld + (r - r0)) * 2);
+    }
+}
+
+// The same tile through registers, zero for k >= K (the last k-tile when K is not a
+// multiple of BK).
+template <int BK>
+GPT2_DEV void fill_tr(float* S, const float* Xf, long ld, int r0, int k0, int K) {
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(Xf);
+    uint4 v[BK * 16 / NT];
+#pragma unroll
+    for (int j = 0; j < BK * 16 / NT; j++) {
+        const int ch = (int)threadIdx.x + NT * j, kr = ch >> 4, c = (ch & 15) ^ trswz(ch >> 4);
+        const long r = (long)r0 + 8 * c < ld - 8 ? (long)r0 + 8 * c : ld - 8;
+        v[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (k0 + kr < K) v[j] = *reinterpret_cast<const uint4*>(X + (long)(k0 + kr) * ld + r);
+    }
+#pragma unroll
+    for (int j = 0; j < BK * 16 / NT; j++) reinterpret_cast<uint4*>(S)[threadIdx.x + NT * j] = v[j];
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 8 consecutive k of one fragment row: two transposing reads 4 k rows (1 KB) apart
+GPT2_DEV bf16x8 tr_frag(const lds_char* p) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 1024));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(bf16x8, (v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
+}
+
 // The logits operand of the LM-head backward: each logit z of row r in vocabulary column
 // c becomes d loss / d z = s * (exp(z - lse_r) - [c == target_r]), s = 1/rows.  The
 // first term is formed as 2^(z log2 e - (lse_r log2 e - log2 s)) on v_exp_f32 with the
@@ -458,13 +528,18 @@ template <bool A_K, bool B_K, int EPI, bool XF, int BN, bool BF>
 GPT2_DEV void gemm_body(const Params& p) {
     static_assert(BN == 128 || (BN == 96 && A_K) || (BN == 256 && BF), "tile widths: 128; 96 (A k-contiguous); 256 (bf16)");
     constexpr int SLOT_BIAS = slot_bias<BN>(), SLOT_FLOATS = slot_floats<BN>();
-    static_assert(!BF || (A_K && B_K && !XF), "bf16 operands are both k-contiguous");
+    static_assert(!BF || (A_K == B_K && !XF), "bf16 operands are both k-contiguous or both row-contiguous");
+    // TR: bf16 row-contiguous operands, fragments by transposing LDS reads; p.K counts k
+    // rows and p.lda, p.ldb bf16 elements
+    constexpr bool TR = BF && !A_K;
+    static_assert(!TR || BN == 128, "row-contiguous bf16 tiles are 128 x 128");
     constexpr int WN = BN / 2, NB = BN / 32;
     constexpr bool XR = XF && !A_K;  // dlogits as the row-contiguous operand (LM-head wgrad)
     constexpr int BK = KTileOf<A_K, BF, BN>::BK, STAGES = KTileOf<A_K, BF, BN>::STAGES;
-    constexpr int A_FLOATS = BM * BK, B_FLOATS = BN * BK;  // the operands' k-tiles in LDS
+    // the operands' k-tiles in LDS (floats)
+    constexpr int A_FLOATS = TR ? BM * BK / 2 : BM * BK, B_FLOATS = TR ? BN * BK / 2 : BN * BK;
     constexpr int STAGE_FLOATS = A_FLOATS + B_FLOATS + (XR ? XF_FLOATS : 0);
-    constexpr int LPS = (BM + BN) * BK / 1024 + (XR ? 1 : 0);  // transfers per thread per k-tile
+    constexpr int LPS = (A_FLOATS + B_FLOATS) / 1024 + (XR ? 1 : 0);  // transfers per thread per k-tile
     __shared__ __attribute__((aligned(1024))) float smem[STAGES * STAGE_FLOATS];
 
     // XCD-aware logical block id: XCD x (= blockIdx % 8) gets a contiguous id range.
@@ -527,14 +602,28 @@ GPT2_DEV void gemm_body(const Params& p) {
     };
 
     // per-lane transfer offsets of the current item's tile (set by prologue)
-    unsigned offA[BM * BK / 1024], offB[BN * BK / 1024];
+    unsigned offA[A_FLOATS / 1024], offB[B_FLOATS / 1024];
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](int buf, int kstep, int m0, int n0) {
         float* Sa = smem + buf * STAGE_FLOATS;
         float* Sb = Sa + A_FLOATS;
         const int k0 = kstep * BK;
-        if (kstep < kfull) {
+        if constexpr (TR) {
+            if (kstep < kfull) {
+                const char* ba = reinterpret_cast<const char*>(p.A) + ((long)k0 * p.lda + m0) * 2;
+                const char* bb = reinterpret_cast<const char*>(p.B) + ((long)k0 * p.ldb + n0) * 2;
+                const unsigned la = lds0 + (unsigned)(buf * STAGE_FLOATS) * 4 + (unsigned)wave_u * 1024;
+                const unsigned lb_ = la + A_FLOATS * 4;
+#pragma unroll
+                for (int j = 0; j < A_FLOATS / 1024; j++) dma16s(ba, offA[j], la + j * 4096);
+#pragma unroll
+                for (int j = 0; j < B_FLOATS / 1024; j++) dma16s(bb, offB[j], lb_ + j * 4096);
+            } else {
+                fill_tr<BK>(Sa, p.A, p.lda, m0, k0, p.K);
+                fill_tr<BK>(Sb, p.B, p.ldb, n0, k0, p.K);
+            }
+        } else if (kstep < kfull) {
             const char* ba = reinterpret_cast<const char*>(p.A) +
                              (A_K ? (long)m0 * p.lda + k0 : (long)k0 * p.lda + m0) * 4;
             const char* bb = reinterpret_cast<const char*>(p.B) +
@@ -558,10 +647,15 @@ GPT2_DEV void gemm_body(const Params& p) {
     };
     // the first STAGES-1 k-tiles of an item
     auto prologue = [&](const Item& w) {
-        if constexpr (A_K) kcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
-        else rcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
-        if constexpr (B_K) kcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
-        else rcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
+        if constexpr (TR) {
+            tr_offsets<BK>(offA, p.lda, w.m0);
+            tr_offsets<BK>(offB, p.ldb, w.n0);
+        } else {
+            if constexpr (A_K) kcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
+            else rcontig_offsets<BM, BK>(offA, p.lda, w.m0, rmaxA);
+            if constexpr (B_K) kcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
+            else rcontig_offsets<BN, BK>(offB, p.ldb, w.n0, rmaxB);
+        }
 #pragma unroll
         for (int s = 0; s < STAGES - 1; s++)
             if (s < w.ke - w.ks) issue(s, w.ks + s, w.m0, w.n0);
@@ -695,8 +789,30 @@ GPT2_DEV void gemm_body(const Params& p) {
                             acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
             }
         };
+        // bf16 row-contiguous k-tile: BK/32 groups of 32 k rows; lane (i, g) reads k rows
+        // 32 kg + 8g + (i / 4) (+4) at fragment rows 4 (i % 4) .. +3
+        auto compute_tr = [&](int buf) {
+            const lds_char* Sa = (const lds_char*)(smem + buf * STAGE_FLOATS);
+            const lds_char* Sb = Sa + A_FLOATS * 4;
+            const int kr = 8 * grp + (li >> 2), sw = trswz(kr);
+            auto frag_off = [&](int r) { return kr * 256 + ((((r >> 3) ^ sw)) << 4) + ((r & 7) << 1); };
+#pragma unroll
+            for (int kg = 0; kg < BK / 32; kg++) {
+                bf16x8 fa[4], fb[NB];
+#pragma unroll
+                for (int a = 0; a < 4; a++) fa[a] = tr_frag(Sa + kg * 8192 + frag_off(wm + 16 * a + 4 * (li & 3)));
+#pragma unroll
+                for (int b = 0; b < NB; b++) fb[b] = tr_frag(Sb + kg * 8192 + frag_off(wn + 16 * b + 4 * (li & 3)));
+#pragma unroll
+                for (int a = 0; a < 4; a++)
+#pragma unroll
+                    for (int b = 0; b < NB; b++)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+            }
+        };
         auto compute = [&](int buf, int kstep) {
-            if constexpr (BF) compute_bf16(buf);
+            if constexpr (TR) compute_tr(buf);
+            else if constexpr (BF) compute_bf16(buf);
             else compute_f32(buf, kstep);
         };
 
@@ -760,6 +876,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(Params p) {
 template <int EPI, int BN>
 __global__ __launch_bounds__(NT, GEMM_BF_OCC) void gemm_bf16_kernel(Params p) {
     gemm_body<true, true, EPI, false, BN, true>(p);
+}
+
+// bf16 operands row-contiguous (the weight gradients)
+template <int EPI, int BN>
+__global__ __launch_bounds__(NT, GEMM_BF_OCC) void gemm_bf16_tr_kernel(Params p) {
+    gemm_body<false, false, EPI, false, BN, true>(p);
 }
 
 // Four blocks per range boundary that falls strictly inside a tile, one per row of
@@ -874,8 +996,10 @@ const char* gemm_name() {
 }
 
 template <int EPI, int BN>
-const char* bf16_name() {
+const char* bf16_name(bool tr = false) {
     static const std::string s = "gemm_bf16_kernel<" + std::to_string(EPI) + ", " + std::to_string(BN) + ">";
+    static const std::string t = "gemm_bf16_tr_kernel<" + std::to_string(EPI) + ", " + std::to_string(BN) + ">";
+    if (tr) return t.c_str();
     return s.c_str();
 }
 
@@ -944,10 +1068,14 @@ hipError_t launch(Params& p, hipStream_t st, int split) {
                           EPI == EPI_DLOGITS) ? mn : 0.0;
     {
         // algorithmic work: 2MNK flops; operands read once, C written (and read for += / aux)
-        // (bf16: p.K counts float pairs, so the flops double and the operand bytes match)
-        ProfScope ps(st, BF ? bf16_name<EPI, BN>() : gemm_name<A_K, B_K, EPI, XF, BN>(), (BF ? 4.0 : 2.0) * mn * p.K,
-                     4.0 * ((double)p.M * p.K + (double)p.N * p.K + mn + extra));
-        if constexpr (BF) hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BN>), dim3(p.G), dim3(NT), 0, st, p);
+        // (bf16 k-contiguous: p.K counts float pairs, so the flops double and the operand
+        // bytes match; bf16 row-contiguous: p.K counts k rows of 2-byte elements)
+        constexpr bool TR = BF && !A_K;
+        ProfScope ps(st, BF ? bf16_name<EPI, BN>(TR) : gemm_name<A_K, B_K, EPI, XF, BN>(),
+                     (BF && !TR ? 4.0 : 2.0) * mn * p.K,
+                     (TR ? 2.0 : 4.0) * ((double)p.M * p.K + (double)p.N * p.K) + 4.0 * (mn + extra));
+        if constexpr (TR) hipLaunchKernelGGL((gemm_bf16_tr_kernel<EPI, BN>), dim3(p.G), dim3(NT), 0, st, p);
+        else if constexpr (BF) hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BN>), dim3(p.G), dim3(NT), 0, st, p);
         else hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF, BN>), dim3(p.G), dim3(NT), 0, st, p);
     }
     const double slot = (double)BM * BN + BM;
@@ -1202,6 +1330,25 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
         case BF16_GELU_BWD: return aux ? go(std::integral_constant<int, EPI_GELU_BWD>{}) : hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t gemm_bf16_rows(float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M, int N,
+                          int K, float* partial, hipStream_t st) {
+    if (M < 0 || N < 0 || K < 0 || lda % 8 || ldb % 8 || lda < M || ldb < N || !aligned16(a) || !aligned16(b))
+        return hipErrorInvalidValue;
+    if (M == 0 || N == 0) return hipSuccess;
+    Params p{};
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.A = reinterpret_cast<const float*>(a);
+    p.lda = lda;
+    p.B = reinterpret_cast<const float*>(b);
+    p.ldb = ldb;
+    p.C = c;
+    p.ldc = ldc;
+    p.partial = partial;
+    return launch<false, false, EPI_ACCUM, false, 128, true>(p, st, GEMM_BF_SPLITK ? pick_split_rounds<false, true, 128>(M, N, K) : 0);
 }
 
 }  // namespace gpt2k

@@ -61,14 +61,14 @@ struct ActInfo {
 };
 
 // bfloat16 copies of the mixed-precision variant: in the activation arena the weights as
-// stored (W*), transposed (WT*) and the linear layers' inputs, straight and transposed
-// (per layer); in the scratch the output gradients (one straight buffer, a transposed one
-// per kind) and the LM head's.  Transposes are (cols, rows rounded up to 64).
-// Attention's per-head copies of q, k, v (row-major and transposed, per layer) and of its
-// output gradient (scratch) follow.
-enum { BW_Q, BW_A, BW_F, BW_P, BW_WTE, BWT_Q, BWT_A, BWT_F, BWT_P, BWT_WTE, BA_LN1, BA_LN1T, BA_ATTY, BA_ATTYT,
-       BA_LN2, BA_LN2T, BA_FCHG, BA_FCHGT, BA_LNF, BA_LNFT, BA_HQ, BA_HK, BA_HV, BA_HQT, BA_HKT, BA_HVT, NBA };
-enum { BS_DY, BS_DREST, BS_DFCHT, BS_DQKVT, BS_DLOG, BS_DLOGT, BS_HDO, BS_HDOT, NBS };
+// stored (W*) and transposed (WT*, (cols, rows rounded up to 64)) and the linear layers'
+// inputs (per layer); in the scratch the output gradients (one buffer per kind) and the
+// LM head's.  The weight gradients read the inputs and output gradients as they are,
+// row-contiguous.  Attention's per-head copies of q, k, v (row-major and transposed, per
+// layer) and of its output gradient (scratch) follow.
+enum { BW_Q, BW_A, BW_F, BW_P, BW_WTE, BWT_Q, BWT_A, BWT_F, BWT_P, BWT_WTE, BA_LN1, BA_ATTY, BA_LN2, BA_FCHG, BA_LNF,
+       BA_HQ, BA_HK, BA_HV, BA_HQT, BA_HKT, BA_HVT, NBA };
+enum { BS_DRES, BS_DFCH, BS_DQKV, BS_DLOG, BS_HDO, BS_HDOT, NBS };
 
 size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
 
@@ -121,14 +121,12 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     y.tok_tgt = o;
     o += align_up(BT);
     if (variant & GPT2_VARIANT_BF16) {
-        const size_t BTp = pad64(BT);
         const size_t HT = attn_bf16_head_elems(B, T, (int)C);
         // (id, layers, elements per layer)
         const size_t spec[NBA][2] = {
             {L, 3 * C * C}, {L, C * C}, {L, 4 * C * C}, {L, 4 * C * C}, {1, V * C},
             {L, C * pad64(3 * C)}, {L, C * pad64(C)}, {L, C * pad64(4 * C)}, {L, 4 * C * pad64(C)}, {1, C * y.Vp},
-            {L, BT * C}, {L, C * BTp}, {L, BT * C}, {L, C * BTp}, {L, BT * C}, {L, C * BTp},
-            {L, BT * 4 * C}, {L, 4 * C * BTp}, {1, BT * C}, {1, C * BTp},
+            {L, BT * C}, {L, BT * C}, {L, BT * C}, {L, BT * 4 * C}, {1, BT * C},
             {L, BT * C}, {L, BT * C}, {L, BT * C}, {L, HT}, {L, HT}, {L, HT}};
         for (int i = 0; i < NBA; i++) {
             y.ba[i] = o;
@@ -161,9 +159,7 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     y.rope = take(rope_table_floats(c->max_seq_len, (int)(C / NH)));  // rotary variant's (cos, sin) table
     y.lsep = take(lse_partial_floats((int)BT, (int)V));  // the LM head's per-tile log-sum-exp partials
     if (variant & GPT2_VARIANT_BF16) {
-        const size_t BTp = pad64(BT);
-        const size_t n[NBS] = {BT * 4 * C, C * BTp, 4 * C * BTp, 3 * C * BTp, BT * y.Vp, y.Vp * BTp, BT * C,
-                               attn_bf16_head_elems(B, T, (int)C)};
+        const size_t n[NBS] = {BT * C, BT * 4 * C, BT * 3 * C, BT * y.Vp, BT * C, attn_bf16_head_elems(B, T, (int)C)};
         for (int i = 0; i < NBS; i++) y.bs[i] = take((n[i] + 1) / 2);
         y.bpart = take(4 * bias_partial_floats((int)BT, (int)(4 * C)));  // one per output-gradient kind
     }
@@ -236,7 +232,8 @@ AttnBf16 attn_copies(gpt2* g, int l) {
 }
 
 // bf16 copies of an fp32 (rows, cols) tensor: straight (xb) and transposed (xt, rows
-// padded to 64 with zeros), and the bias gradient's per-block column sums (bpart).
+// padded to 64 with zeros; the weights only), and the bias gradient's per-block column
+// sums (bpart).
 hipError_t cast_rows(const float* x, int rows, int cols, uint16_t* xb, uint16_t* xt, float* bpart, hipStream_t st) {
     CastArgs a{};
     a.x = x;
@@ -304,8 +301,8 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     HIPCHK(g, encoder_forward(A(g, GPT2_ACT_ENCODED), tok_in(g), P(g, P_WTE), rope_on(g) ? nullptr : P(g, P_WPE), B, T,
                               C, V, flags(g), st));
     // Mixed precision: the weights' bf16 copies (as stored and transposed) are made from
-    // the current parameters at every forward; each linear layer's input gets its copies
-    // right after it is produced (the transposes serve the backward's weight gradients).
+    // the current parameters at every forward; each linear layer's input gets its copy
+    // right after it is produced (the backward's weight gradients read it too).
     const bool bf = bf_on(g);
     if (bf) {
         HIPCHK(g, cast_weights(P(g, P_QKVW), 3 * C, C, L, BA(g, BW_Q), BA(g, BWT_Q), st));
@@ -324,7 +321,7 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN1, l), A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), residual,
                            P(g, P_LN1W) + l * C, P(g, P_LN1B) + l * C, BT, C, st));
-        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_LN1, l), BT, C, BA(g, BA_LN1, l), BA(g, BA_LN1T, l), nullptr, st));
+        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_LN1, l), BT, C, BA(g, BA_LN1, l), nullptr, nullptr, st));
         HIPCHK(g, linear(BF16_BIAS, A(g, GPT2_ACT_QKV, l), 3 * C, A(g, GPT2_ACT_LN1, l), BA(g, BA_LN1, l),
                          P(g, P_QKVW) + (size_t)l * 3 * C * C, BA(g, BW_Q, l), P(g, P_QKVB) + l * 3 * C, nullptr,
                          nullptr, 3 * C, C));
@@ -341,18 +338,18 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
             HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T,
                                         C, NH, st));
         }
-        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_ATTY, l), BT, C, BA(g, BA_ATTY, l), BA(g, BA_ATTYT, l), nullptr, st));
+        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_ATTY, l), BT, C, BA(g, BA_ATTY, l), nullptr, nullptr, st));
         HIPCHK(g, linear(BF16_BIAS_RESID, A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTY, l),
                          P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BW_A, l), P(g, P_ATTPROJB) + l * C, residual,
                          nullptr, C, C));
         HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN2, l), A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l),
                            A(g, GPT2_ACT_RESIDUAL2, l), P(g, P_LN2W) + l * C, P(g, P_LN2B) + l * C, BT, C, st));
-        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_LN2, l), BT, C, BA(g, BA_LN2, l), BA(g, BA_LN2T, l), nullptr, st));
+        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_LN2, l), BT, C, BA(g, BA_LN2, l), nullptr, nullptr, st));
         HIPCHK(g, linear(BF16_BIAS_GELU, A(g, GPT2_ACT_FCH_GELU, l), 4 * C, A(g, GPT2_ACT_LN2, l), BA(g, BA_LN2, l),
                          P(g, P_FCW) + (size_t)l * 4 * C * C, BA(g, BW_F, l), P(g, P_FCB) + l * 4 * C, nullptr,
                          A(g, GPT2_ACT_FCH, l), 4 * C, C));
         if (bf)
-            HIPCHK(g, cast_rows(A(g, GPT2_ACT_FCH_GELU, l), BT, 4 * C, BA(g, BA_FCHG, l), BA(g, BA_FCHGT, l), nullptr, st));
+            HIPCHK(g, cast_rows(A(g, GPT2_ACT_FCH_GELU, l), BT, 4 * C, BA(g, BA_FCHG, l), nullptr, nullptr, st));
         HIPCHK(g, linear(BF16_BIAS_RESID, A(g, GPT2_ACT_RESIDUAL3, l), C, A(g, GPT2_ACT_FCH_GELU, l), BA(g, BA_FCHG, l),
                          P(g, P_FCPROJW) + (size_t)l * 4 * C * C, BA(g, BW_P, l), P(g, P_FCPROJB) + l * C,
                          A(g, GPT2_ACT_RESIDUAL2, l), nullptr, C, 4 * C));
@@ -364,7 +361,7 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     // logits)
     float* lsep = S(g, g->lay.lsep);
     if (bf) {
-        HIPCHK(g, cast_rows(A(g, GPT2_ACT_LNF), BT, C, BA(g, BA_LNF), BA(g, BA_LNFT), nullptr, st));
+        HIPCHK(g, cast_rows(A(g, GPT2_ACT_LNF), BT, C, BA(g, BA_LNF), nullptr, nullptr, st));
         HIPCHK(g, gemm_bf16(BF16_STORE, A(g, GPT2_ACT_LOGITS), Vp, BA(g, BA_LNF), C, BA(g, BW_WTE), C, BT, V, C, nullptr,
                             nullptr, 0, nullptr, part, st, lsep));
     } else {
@@ -484,43 +481,44 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     auto mark = [&](int e, hipStream_t s) { return hipEventRecord(g->ev[e], s); };
     auto after = [&](hipStream_t s, int e) { return hipStreamWaitEvent(s, g->ev[e], 0); };
     // Mixed precision: every GEMM below multiplies bf16 copies.  dlogits is written once
-    // in bf16, straight and transposed; each output gradient dY gets its copies (and its
-    // bias gradient's partial sums, from the fp32 values) on the main stream before its
-    // GEMMs, the transposed ones in buffers per kind that the events below protect exactly
-    // as they protect dY itself.
+    // in bf16; each output gradient dY gets its copy (and its bias gradient's partial sums,
+    // from the fp32 values) on the main stream before its GEMMs, in a buffer per kind that
+    // the events below protect exactly as they protect dY itself: the dgrad (main stream)
+    // and the wgrad (second stream, reading dY and X row-contiguous) both read it.
     const bool bf = bf_on(g);
-    const long BTp = (long)pad64(BT);
-    uint16_t* dyb = bf ? BS(g, BS_DY) : nullptr;
     // the bias gradient's column sums per row block, one buffer per kind of dY (0 fcproj,
     // 1 fc, 2 attproj, 3 qkv): the second stream adds them up (bias_w) ahead of the kind's
     // wgrad, and the events that let the main stream rewrite that kind's dY (or its
     // transposed copy) in the next layer come after it
     auto bpart = [&](int kind) { return S(g, g->lay.bpart) + (size_t)kind * bias_partial_floats(BT, 4 * C); };
-    auto grad_copies = [&](const float* dy, int n, uint16_t* yt, int kind) -> hipError_t {
-        return cast_rows(dy, BT, n, dyb, yt, bpart(kind), st);
+    auto grad_copies = [&](const float* dy, int n, uint16_t* yb, int kind) -> hipError_t {
+        return cast_rows(dy, BT, n, yb, nullptr, bpart(kind), st);
     };
     auto bias_w = [&](float* db, int n, int kind) { return bias_reduce(db, bpart(kind), BT, n, sw); };
-    // dW[M,N] += dY^T X (and, fp32 only, db += column sums of dY): dY (BT, M), X (BT, N)
-    auto wgrad = [&](float* dw, float* db, const float* dy, const uint16_t* yt, int M, const float* x,
-                     const uint16_t* xt, int N) {
-        if (bf) return gemm_bf16(BF16_ACCUM, dw, N, yt, BTp, xt, BTp, M, N, (int)BTp, nullptr, nullptr, 0, nullptr,
-                                 part_w, sw);
+    // dW[M,N] += dY^T X (and, fp32 only, db += column sums of dY): dY (BT, M), X (BT, N);
+    // yb, xb their bf16 copies
+    auto wgrad = [&](float* dw, float* db, const float* dy, const uint16_t* yb, int M, const float* x,
+                     const uint16_t* xb, int N) {
+        if (bf) return gemm_bf16_rows(dw, N, yb, M, xb, N, M, N, BT, part_w, sw);
         return linear_wgrad(dw, db, dy, M, x, M, N, BT, part_w, sw);
     };
-    // dX[BT,N] = dY[BT,K] . W[K,N] (times gelu'(gelu_pre) if given); wt = bf16 W^T (N, K padded)
-    auto dgrad = [&](float* dx, const float* dy, int K, const float* w, const uint16_t* wt, int N,
+    // dX[BT,N] = dY[BT,K] . W[K,N] (times gelu'(gelu_pre) if given); yb = bf16 dY, wt = bf16
+    // W^T (N, K padded)
+    auto dgrad = [&](float* dx, const float* dy, const uint16_t* yb, int K, const float* w, const uint16_t* wt, int N,
                      const float* gelu_pre) {
-        if (bf) return gemm_bf16(gelu_pre ? BF16_GELU_BWD : BF16_STORE, dx, N, dyb, K, wt, (long)pad64(K), BT, N, K,
+        if (bf) return gemm_bf16(gelu_pre ? BF16_GELU_BWD : BF16_STORE, dx, N, yb, K, wt, (long)pad64(K), BT, N, K,
                                  nullptr, gelu_pre, N, nullptr, part, st);
         return linear_dgrad(dx, dy, K, w, gelu_pre, BT, N, K, part, st);
     };
+    uint16_t* dresb = bf ? BS(g, BS_DRES) : nullptr;
+    uint16_t* dfchb = bf ? BS(g, BS_DFCH) : nullptr;
+    uint16_t* dqkvb = bf ? BS(g, BS_DQKV) : nullptr;
     if (bf) {
-        HIPCHK(g, xent_grad_bf16(BS(g, BS_DLOG), BS(g, BS_DLOGT), BTp, logits, Vp, A(g, GPT2_ACT_LOGITS_LSE),
-                                 tok_tgt(g), xo.scale, BT, V, st));
+        HIPCHK(g, xent_grad_bf16(BS(g, BS_DLOG), nullptr, 0, logits, Vp, A(g, GPT2_ACT_LOGITS_LSE), tok_tgt(g), xo.scale,
+                                 BT, V, st));
         HIPCHK(g, mark(EV_LM, st));
         HIPCHK(g, after(sw, EV_LM));
-        HIPCHK(g, gemm_bf16(BF16_ACCUM, G(g, P_WTE), C, BS(g, BS_DLOGT), BTp, BA(g, BA_LNFT), BTp, V, C, (int)BTp,
-                            nullptr, nullptr, 0, nullptr, part_w, sw));
+        HIPCHK(g, gemm_bf16_rows(G(g, P_WTE), C, BS(g, BS_DLOG), Vp, BA(g, BA_LNF), C, V, C, BT, part_w, sw));
         HIPCHK(g, mark(EV_W_LM, sw));
         HIPCHK(g, gemm_bf16(BF16_STORE, dln, C, BS(g, BS_DLOG), Vp, BA(g, BWT_WTE), Vp, BT, C, (int)Vp, nullptr, nullptr,
                             0, nullptr, part, st));
@@ -547,38 +545,38 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         const bool later = l < L - 1;  // the previous iteration's weight gradients exist
         // MLP projection: residual3 = residual2 + gelu(fch) . Wp^T + bp.
-        if (bf) HIPCHK(g, grad_copies(dres, C, BS(g, BS_DREST), 0));
+        if (bf) HIPCHK(g, grad_copies(dres, C, dresb, 0));
         HIPCHK(g, mark(EV_DRES_A, st));
         HIPCHK(g, after(sw, EV_DRES_A));
         if (bf) HIPCHK(g, bias_w(G(g, P_FCPROJB) + l * C, C, 0));
-        HIPCHK(g, wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, G(g, P_FCPROJB) + l * C, dres, BS(g, BS_DREST), C,
-                        A(g, GPT2_ACT_FCH_GELU, l), BA(g, BA_FCHGT, l), 4 * C));
+        HIPCHK(g, wgrad(G(g, P_FCPROJW) + (size_t)l * 4 * C * C, G(g, P_FCPROJB) + l * C, dres, dresb, C,
+                        A(g, GPT2_ACT_FCH_GELU, l), bf ? BA(g, BA_FCHG, l) : nullptr, 4 * C));
         HIPCHK(g, mark(EV_W_FCPROJ, sw));
         if (later) HIPCHK(g, after(st, EV_W_FC));  // the fc wgrad above still reads dfch
-        HIPCHK(g, dgrad(dfch, dres, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, BA(g, BWT_P, l), 4 * C,
+        HIPCHK(g, dgrad(dfch, dres, dresb, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, BA(g, BWT_P, l), 4 * C,
                         A(g, GPT2_ACT_FCH, l)));
         // MLP expansion: fch = ln2 . Wf^T + bf.
-        if (bf) HIPCHK(g, grad_copies(dfch, 4 * C, BS(g, BS_DFCHT), 1));
+        if (bf) HIPCHK(g, grad_copies(dfch, 4 * C, dfchb, 1));
         HIPCHK(g, mark(EV_DFCH, st));
         HIPCHK(g, after(sw, EV_DFCH));
         if (bf) HIPCHK(g, bias_w(G(g, P_FCB) + l * 4 * C, 4 * C, 1));
-        HIPCHK(g, wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, G(g, P_FCB) + l * 4 * C, dfch, BS(g, BS_DFCHT), 4 * C,
-                        A(g, GPT2_ACT_LN2, l), BA(g, BA_LN2T, l), C));
+        HIPCHK(g, wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, G(g, P_FCB) + l * 4 * C, dfch, dfchb, 4 * C,
+                        A(g, GPT2_ACT_LN2, l), bf ? BA(g, BA_LN2, l) : nullptr, C));
         HIPCHK(g, mark(EV_W_FC, sw));
-        HIPCHK(g, dgrad(dln, dfch, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, BA(g, BWT_F, l), C, nullptr));
+        HIPCHK(g, dgrad(dln, dfch, dfchb, 4 * C, P(g, P_FCW) + (size_t)l * 4 * C * C, BA(g, BWT_F, l), C, nullptr));
         HIPCHK(g, after(st, EV_W_FCPROJ));  // dres is about to change
         HIPCHK(g, norm_bwd(g, dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
                            P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C, true,
                            true, part, st));
         // Attention projection: residual2 = residual + atty . Wa^T + ba.
-        if (bf) HIPCHK(g, grad_copies(dres, C, BS(g, BS_DREST), 2));
+        if (bf) HIPCHK(g, grad_copies(dres, C, dresb, 2));
         HIPCHK(g, mark(EV_DRES_B, st));
         HIPCHK(g, after(sw, EV_DRES_B));
         if (bf) HIPCHK(g, bias_w(G(g, P_ATTPROJB) + l * C, C, 2));
-        HIPCHK(g, wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, G(g, P_ATTPROJB) + l * C, dres, BS(g, BS_DREST), C,
-                        A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTYT, l), C));
+        HIPCHK(g, wgrad(G(g, P_ATTPROJW) + (size_t)l * C * C, G(g, P_ATTPROJB) + l * C, dres, dresb, C,
+                        A(g, GPT2_ACT_ATTY, l), bf ? BA(g, BA_ATTY, l) : nullptr, C));
         HIPCHK(g, mark(EV_W_ATTPROJ, sw));
-        HIPCHK(g, dgrad(datty, dres, C, P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BWT_A, l), C, nullptr));
+        HIPCHK(g, dgrad(datty, dres, dresb, C, P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BWT_A, l), C, nullptr));
         if (later) HIPCHK(g, after(st, EV_W_QKV));  // the qkv wgrad above still reads dqkv
         if (bf) {
             uint16_t* rm[1] = {BS(g, BS_HDO)};
@@ -594,14 +592,14 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
         // rotary variant: attention gave the gradient of the rotated q and k; rotate it back
         if (rope_on(g)) HIPCHK(g, rope_backward(dqkv, S(g, g->lay.rope), B, T, C, NH, st));
-        if (bf) HIPCHK(g, grad_copies(dqkv, 3 * C, BS(g, BS_DQKVT), 3));
+        if (bf) HIPCHK(g, grad_copies(dqkv, 3 * C, dqkvb, 3));
         HIPCHK(g, mark(EV_DQKV, st));
         HIPCHK(g, after(sw, EV_DQKV));
         if (bf) HIPCHK(g, bias_w(G(g, P_QKVB) + l * 3 * C, 3 * C, 3));
-        HIPCHK(g, wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, BS(g, BS_DQKVT), 3 * C,
-                        A(g, GPT2_ACT_LN1, l), BA(g, BA_LN1T, l), C));
+        HIPCHK(g, wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, dqkvb, 3 * C,
+                        A(g, GPT2_ACT_LN1, l), bf ? BA(g, BA_LN1, l) : nullptr, C));
         HIPCHK(g, mark(EV_W_QKV, sw));
-        HIPCHK(g, dgrad(dln, dqkv, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, BA(g, BWT_Q, l), C, nullptr));
+        HIPCHK(g, dgrad(dln, dqkv, dqkvb, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, BA(g, BWT_Q, l), C, nullptr));
         HIPCHK(g, after(st, EV_W_ATTPROJ));  // dres is about to change
         HIPCHK(g, norm_bwd(g, dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
                            A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));

@@ -58,6 +58,12 @@ enum { BF16_STORE = 0, BF16_BIAS, BF16_BIAS_RESID, BF16_BIAS_GELU, BF16_ACCUM, B
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
                      int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
                      hipStream_t st, float* lse_part = nullptr);
+// C[M,N] += sum over k of A[k,m] B[k,n] with bfloat16 A, B stored row-contiguous, as
+// [K][lda] and [K][ldb] (the weight gradients dW += dY^T X on the straight copies of dY and
+// X): lda >= M, ldb >= N, both multiples of 8; 16-byte aligned; the elements of a row past
+// M (N) are read but feed no stored output.
+hipError_t gemm_bf16_rows(float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M, int N,
+                          int K, float* partial, hipStream_t st);
 
 // ---- bfloat16 operand copies (bf16.hip) -----------------------------------------------
 // Rounding is to nearest, ties to even.  x is (rows, cols) fp32 with leading dimension

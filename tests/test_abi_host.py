@@ -126,17 +126,17 @@ def test_build_variant_argument_checks_need_no_gpu():
 @pytest.mark.parametrize("w,B,T", [(S.TINY, 2, 32), (S.GPT2_124M, 8, 1024), (S.GPT2_124M, 3, 100)])
 def test_bf16_variant_arena_sizes(w, B, T):
     """The mixed-precision arenas hold at least the bf16 copies: weights straight and
-    transposed, the four per-layer linear inputs and lnf straight and transposed (rows
-    padded to 64); the scratch the output-gradient and logits-gradient copies."""
+    transposed, the four per-layer linear inputs and lnf; the scratch one copy per kind of
+    output gradient (residual stream, fc, qkv) and the logits gradient's."""
     m = w.model
     L, C, V = m.num_layers, m.channels, m.vocab_size
-    BT, BTp = B * T, -(-B * T // 64) * 64
+    BT = B * T
     a0, s0 = G.arena_sizes(m, B, T)
     a4, s4 = G.arena_sizes(m, B, T, G.VARIANT_BF16)
     weights = L * 12 * C * C + V * C
-    acts = L * 7 * C * (BT + BTp) + C * (BT + BTp)
+    acts = L * 7 * C * BT + C * BT
     assert (a4 - a0) * 2 >= 2 * weights + acts
-    assert (s4 - s0) * 2 >= 4 * C * BT + 8 * C * BTp + V * (BT + BTp)
+    assert (s4 - s0) * 2 >= 8 * C * BT + V * BT
     with pytest.raises(G.GPT2Error):
         G.arena_sizes(m, B, T, 8)
 
