@@ -48,12 +48,8 @@ GPT2_DEV f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_
 GPT2_DEV bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u)); }
 GPT2_DEV bf16x8 ld8(const uint16_t* p) { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p)); }
 
-// fp32 pair -> packed bf16, round to nearest, ties to even: one v_cvt_pk_bf16_f32
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-GPT2_DEV uint32_t pack2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
-}
 GPT2_DEV float bf16_float(uint32_t b) { return __uint_as_float(b << 16); }
 
 // x = hi + mid + lo + r, |r| <= 2^-24 |x|, with hi, mid, lo bf16 (see the header); each
@@ -128,8 +124,8 @@ __global__ __launch_bounds__(NTH) void attn_prep_kernel(PrepArgs a) {
             v = *reinterpret_cast<const float4*>(src + (long)tok * a.ld + d4);
             if (rm) {
                 uint2 o;
-                o.x = pack2(v.x, v.y);
-                o.y = pack2(v.z, v.w);
+                o.x = bf16_pack2(v.x, v.y);
+                o.y = bf16_pack2(v.z, v.w);
                 *reinterpret_cast<uint2*>(rm + ((long)bh * a.T + tok) * HS + d4) = o;
             }
         }
@@ -146,7 +142,7 @@ __global__ __launch_bounds__(NTH) void attn_prep_kernel(PrepArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; e++)
-            w[e] = pack2(tile[tok_of_pos(pos0 + 2 * e)][d], tile[tok_of_pos(pos0 + 2 * e + 1)][d]);
+            w[e] = bf16_pack2(tile[tok_of_pos(pos0 + 2 * e)][d], tile[tok_of_pos(pos0 + 2 * e + 1)][d]);
         *reinterpret_cast<uint4*>(tr + ((long)bh * HS + d) * a.Tp + t0 + pos0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
@@ -213,7 +209,8 @@ GPT2_DEV void head_frags(bf16x8 (&f)[(HS + 31) / 32], const uint16_t* row, bool 
 
 // ---------------------------------------------------------------------------- forward
 template <int HS>
-__global__ __launch_bounds__(NTH, 2) void attn_fwd_bf16_kernel(float* __restrict__ out, float* __restrict__ lse,
+__global__ __launch_bounds__(NTH, 2) void attn_fwd_bf16_kernel(float* __restrict__ out, uint16_t* __restrict__ outb,
+                                                             float* __restrict__ lse,
                                                              const uint16_t* __restrict__ qb,
                                                              const uint16_t* __restrict__ kb,
                                                              const uint16_t* __restrict__ vt, int B, int T, int C,
@@ -319,13 +316,26 @@ __global__ __launch_bounds__(NTH, 2) void attn_fwd_bf16_kernel(float* __restrict
     const float linv = 1.0f / l;
 #pragma unroll
     for (int v = 0; v < 4; v++) {
-        const int q = q0 + 4 * g4 + v;
         const float a = __shfl(linv, 4 * g4 + v, 64);
-        if (q < T) {
-            float* orow = out + ((long)b * T + q) * C + h * HS + i16;
 #pragma unroll
-            for (int d = 0; d < DG; d++) orow[16 * d] = o[d][v] * a;
+        for (int d = 0; d < DG; d++) o[d][v] *= a;
+    }
+    const long orow0 = ((long)b * T + q0 + 4 * g4) * C + h * HS + i16;
+#pragma unroll
+    for (int v = 0; v < 4; v++)
+        if (q0 + 4 * g4 + v < T) {
+#pragma unroll
+            for (int d = 0; d < DG; d++) out[orow0 + v * (long)C + 16 * d] = o[d][v];
         }
+    if (outb) {
+        // the bf16 copy of the output, the next GEMM's operand
+#pragma unroll
+        for (int v = 0; v < 4; v += 2)
+#pragma unroll
+            for (int d = 0; d < DG; d++) {
+                uint16_t* p0 = outb + orow0 + v * (long)C + 16 * d;
+                bf16_store_rows2(p0, p0 + C, o[d][v], o[d][v + 1], q0 + 4 * g4 + v < T, q0 + 4 * g4 + v + 1 < T);
+            }
     }
     if (g4 == 0 && tq < T) lse[((long)b * NH + h) * T + tq] = (m + log2_hw(l)) * LN2;
 }
@@ -579,13 +589,14 @@ __global__ __launch_bounds__(NTH, 2) void attn_bwd_dkdv_bf16_kernel(
 }
 
 template <int HS>
-hipError_t fwd_hs(const AttnBf16& a, float* out, float* lse, int B, int T, int C, int NH, hipStream_t st) {
+hipError_t fwd_hs(const AttnBf16& a, float* out, uint16_t* outb, float* lse, int B, int T, int C, int NH,
+                  hipStream_t st) {
     const int nqt = (T + TILE - 1) / TILE, Tp = nqt * TILE;
     const float scale = 1.0f / sqrtf((float)HS);
     const double flops = 4.0 * B * NH * ((double)T * (T + 1) / 2) * HS;
-    ProfScope ps(st, "attn_fwd_bf16_kernel", flops, (double)B * T * C * (3.0 * 2 + 4.0));
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<HS>), dim3(B * NH * nqt), dim3(NTH), 0, st, out, lse, a.q, a.k, a.vt, B,
-                       T, C, NH, Tp, scale);
+    ProfScope ps(st, "attn_fwd_bf16_kernel", flops, (double)B * T * C * (3.0 * 2 + 4.0 + (outb ? 2.0 : 0.0)));
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<HS>), dim3(B * NH * nqt), dim3(NTH), 0, st, out, outb, lse, a.q, a.k,
+                       a.vt, B, T, C, NH, Tp, scale);
     return hipGetLastError();
 }
 
@@ -638,13 +649,14 @@ hipError_t attn_prep_bf16(const float* src, long ld, long zoff, int nsrc, uint16
     return hipGetLastError();
 }
 
-hipError_t attention_forward_bf16(float* out, float* lse, const AttnBf16& a, int B, int T, int C, int NH,
-                                  hipStream_t st) {
+hipError_t attention_forward_bf16(float* out, uint16_t* outb, float* lse, const AttnBf16& a, int B, int T, int C,
+                                  int NH, hipStream_t st) {
+    if (outb && ((uintptr_t)outb & 3)) return hipErrorInvalidValue;
     if (B <= 0 || T <= 0) return hipSuccess;
     switch (C / NH) {
-        case 16: return fwd_hs<16>(a, out, lse, B, T, C, NH, st);
-        case 32: return fwd_hs<32>(a, out, lse, B, T, C, NH, st);
-        case 64: return fwd_hs<64>(a, out, lse, B, T, C, NH, st);
+        case 16: return fwd_hs<16>(a, out, outb, lse, B, T, C, NH, st);
+        case 32: return fwd_hs<32>(a, out, outb, lse, B, T, C, NH, st);
+        case 64: return fwd_hs<64>(a, out, outb, lse, B, T, C, NH, st);
         default: return hipErrorInvalidValue;
     }
 }

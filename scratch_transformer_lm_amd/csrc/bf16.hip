@@ -25,13 +25,6 @@ namespace {
 
 constexpr int TILE = 64, CT_THREADS = 256, LDT = TILE + 1;
 
-// fp32 pair -> packed bf16, round to nearest, ties to even: one v_cvt_pk_bf16_f32
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-GPT2_DEV uint32_t pack2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
-}
-
 struct XentArgs {
     const float* lse;
     const int32_t* targets;
@@ -74,8 +67,8 @@ __global__ __launch_bounds__(CT_THREADS) void cast_tile_kernel(CastArgs a, XentA
         }
         if (a.xb && r < a.rows && col < a.cols) {
             uint2 o;
-            o.x = pack2(v[j].x, v[j].y);
-            o.y = pack2(v[j].z, v[j].w);
+            o.x = bf16_pack2(v[j].x, v[j].y);
+            o.y = bf16_pack2(v[j].z, v[j].w);
             *reinterpret_cast<uint2*>(a.xb + (long)z * a.sb + (long)r * a.ldb + col) = o;
         }
         tile[row][4 * c4 + 0] = v[j].x;
@@ -96,7 +89,7 @@ __global__ __launch_bounds__(CT_THREADS) void cast_tile_kernel(CastArgs a, XentA
                 if (r0 + rl < rpad) {
                     uint32_t w[8];
 #pragma unroll
-                    for (int i = 0; i < 8; i++) w[i] = pack2(tile[rl + 2 * i][cc], tile[rl + 2 * i + 1][cc]);
+                    for (int i = 0; i < 8; i++) w[i] = bf16_pack2(tile[rl + 2 * i][cc], tile[rl + 2 * i + 1][cc]);
                     uint4* q = reinterpret_cast<uint4*>(a.xt + (long)z * a.st + (long)(c0 + cc) * a.ldt + r0 + rl);
                     q[0] = make_uint4(w[0], w[1], w[2], w[3]);
                     q[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -147,7 +140,7 @@ __global__ __launch_bounds__(TILE * BR_GROUPS) void bias_reduce_kernel(float* db
 __global__ void cast_flat_kernel(uint2* xb, const float4* x, size_t n4) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
         const float4 v = x[i];
-        xb[i] = make_uint2(pack2(v.x, v.y), pack2(v.z, v.w));
+        xb[i] = make_uint2(bf16_pack2(v.x, v.y), bf16_pack2(v.z, v.w));
     }
 }
 

@@ -48,6 +48,32 @@ GPT2_DEV float gelu_grad_f(float u) {
     return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
 }
 
+// fp32 pair -> packed bfloat16 (low half = lo), round to nearest, ties to even: one
+// v_cvt_pk_bf16_f32.
+GPT2_DEV uint32_t bf16_pack2(float lo, float hi) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
+}
+
+// bf16 copy of two rows of a 16x16 matrix-core accumulator (lane: column c = lane % 16,
+// rows 4 (lane / 16) + v), written as 4-byte pairs: each lane swaps one value with its
+// neighbour (DPP quad_perm 1,0,3,2), then even lanes write row v, columns (c, c+1), and
+// odd lanes row v+1, columns (c-1, c).  p0 and p1 point at this lane's element of rows v
+// and v+1; ok0, ok1 say whether those rows exist.  Every lane of the wave must call it;
+// the fragment's first column must be even and rows 4-byte aligned.
+GPT2_DEV void bf16_store_rows2(uint16_t* p0, uint16_t* p1, float x0, float x1, bool ok0, bool ok1) {
+    const bool odd = threadIdx.x & 1;
+    const float send = odd ? x0 : x1;
+    const float recv = __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+    if (!odd) {
+        if (ok0) *reinterpret_cast<uint32_t*>(p0) = bf16_pack2(x0, recv);
+    } else if (ok1) {
+        *reinterpret_cast<uint32_t*>(p1 - 1) = bf16_pack2(recv, x1);
+    }
+}
+
 // Error flag bits written by kernels into the scratch header.
 constexpr int ERR_BAD_INPUT_TOKEN = 1;
 constexpr int ERR_BAD_TARGET_TOKEN = 2;

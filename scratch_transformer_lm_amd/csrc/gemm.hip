@@ -135,6 +135,8 @@ struct Params {
     float xscale;       // dlogits operand: d loss / d loss_row (1 / rows)
     float xlog2s;       // log2(xscale)
     float* lsep;        // EPI_STORE_LSE: partial (max, sum) pairs, [2 * tiles_n][M] float2
+    uint16_t* cb;       // EPI_BIAS_GELU: bf16 rounding of C (nullable)
+    long ldcb;
     int tiles_m, tiles_n, nk;
     int G;              // persistent blocks
     int R;              // whole-tile rounds: block lb takes tiles r*G + lb, r < R
@@ -272,6 +274,18 @@ GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0,
             for (int v = 0; v < 4; v++) in[b][v] = gelu_f(in[b][v]);
     }
     store_row(p.C, p.ldc);
+    if constexpr (EPI == EPI_BIAS_GELU) {
+        // the bf16 copy the next GEMM multiplies (and the weight gradient reads)
+        if (p.cb) {
+#pragma unroll
+            for (int b = 0; b < NB; b++)
+#pragma unroll
+                for (int v = 0; v < 4; v += 2) {
+                    uint16_t* q = p.cb + (long)(r0 + v) * p.ldcb + c0 + 16 * b;
+                    bf16_store_rows2(q, q + p.ldcb, in[b][v], in[b][v + 1], inside(b, v), inside(b, v + 1));
+                }
+        }
+    }
 }
 
 // NA rows (a0 ..) of blocks: the next row's inputs are requested before this row's
@@ -1290,8 +1304,10 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
 
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
                      int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
-                     hipStream_t st, float* lse_part) {
+                     hipStream_t st, float* lse_part, uint16_t* cb, long ldcb) {
     if (K % 2 || lda % 8 || ldb % 8 || lda < K || ldb < K || !aligned16(a) || !aligned16(b)) return hipErrorInvalidValue;
+    if (cb && (epi != BF16_BIAS_GELU || N % 2 || ldcb % 2 || ldcb < N || ((uintptr_t)cb & 3)))
+        return hipErrorInvalidValue;
     Params p{};
     p.M = M;
     p.N = N;
@@ -1308,6 +1324,8 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
     p.pre = pre;
     p.ldpre = ldc;
     p.partial = partial;
+    p.cb = cb;
+    p.ldcb = ldcb;
     const int bn = bf16_tile_n(M, N);
     auto go = [&](auto epi_c) -> hipError_t {
         constexpr int E = decltype(epi_c)::value;

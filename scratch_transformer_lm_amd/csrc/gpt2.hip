@@ -231,17 +231,14 @@ AttnBf16 attn_copies(gpt2* g, int l) {
                     BA(g, BA_HVT, l)};
 }
 
-// bf16 copies of an fp32 (rows, cols) tensor: straight (xb) and transposed (xt, rows
-// padded to 64 with zeros; the weights only), and the bias gradient's per-block column
-// sums (bpart).
-hipError_t cast_rows(const float* x, int rows, int cols, uint16_t* xb, uint16_t* xt, float* bpart, hipStream_t st) {
+// bf16 copy of an fp32 (rows, cols) output gradient (xb) and its bias gradient's per-block
+// column sums (bpart).
+hipError_t cast_rows(const float* x, int rows, int cols, uint16_t* xb, float* bpart, hipStream_t st) {
     CastArgs a{};
     a.x = x;
     a.ldx = cols;
     a.xb = xb;
     a.ldb = cols;
-    a.xt = xt;
-    a.ldt = (long)pad64(rows);
     a.bpart = bpart;
     a.rows = rows;
     a.cols = cols;
@@ -269,10 +266,11 @@ hipError_t cast_weights(const float* w, int OC, int IC, int batch, uint16_t* wb,
 
 // The block's normalisation: LayerNorm, or RMSNorm in the RMSNorm variant (its mean slot
 // then holds 0 and the LayerNorm bias takes no part, keeping a zero gradient).
+// yb (nullable): y's bf16 copy as well
 hipError_t norm_fwd(gpt2* g, float* y, float* mean, float* rstd, const float* x, const float* w, const float* b,
-                    int N, int C, hipStream_t st) {
-    if (g->variant & GPT2_VARIANT_RMSNORM) return rmsnorm_forward(y, mean, rstd, x, w, N, C, 1e-5f, st);
-    return layernorm_forward(y, mean, rstd, x, w, b, N, C, 1e-5f, st);
+                    int N, int C, hipStream_t st, uint16_t* yb = nullptr) {
+    if (g->variant & GPT2_VARIANT_RMSNORM) return rmsnorm_forward(y, mean, rstd, x, w, N, C, 1e-5f, st, yb);
+    return layernorm_forward(y, mean, rstd, x, w, b, N, C, 1e-5f, st, yb);
 }
 
 hipError_t norm_bwd(gpt2* g, float* dx, float* dw, float* db, const float* dy, const float* x, const float* w,
@@ -301,8 +299,9 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     HIPCHK(g, encoder_forward(A(g, GPT2_ACT_ENCODED), tok_in(g), P(g, P_WTE), rope_on(g) ? nullptr : P(g, P_WPE), B, T,
                               C, V, flags(g), st));
     // Mixed precision: the weights' bf16 copies (as stored and transposed) are made from
-    // the current parameters at every forward; each linear layer's input gets its copy
-    // right after it is produced (the backward's weight gradients read it too).
+    // the current parameters at every forward; each linear layer's input is written in
+    // bf16 by its producer (LayerNorm, attention, the fc GEMM's GELU epilogue) next to its
+    // fp32 value (the backward's weight gradients read it too).
     const bool bf = bf_on(g);
     if (bf) {
         HIPCHK(g, cast_weights(P(g, P_QKVW), 3 * C, C, L, BA(g, BW_Q), BA(g, BWT_Q), st));
@@ -311,17 +310,18 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
         HIPCHK(g, cast_weights(P(g, P_FCPROJW), C, 4 * C, L, BA(g, BW_P), BA(g, BWT_P), st));
         HIPCHK(g, cast_weights(P(g, P_WTE), V, C, 1, BA(g, BW_WTE), BA(g, BWT_WTE), st));
     }
-    // y = x . W^T + epilogue, in fp32 or on the bf16 copies xb, wb
+    auto bf_copy = [&](int id, int l) { return bf ? BA(g, id, l) : nullptr; };
+    // y = x . W^T + epilogue, in fp32 or on the bf16 copies xb, wb (yb: y's bf16 copy, GELU only)
     auto linear = [&](int epi, float* out, long ldo, const float* x, const uint16_t* xb, const float* w,
-                      const uint16_t* wb, const float* bias, const float* resid, float* pre, int N, int K) {
-        if (bf) return gemm_bf16(epi, out, ldo, xb, K, wb, K, BT, N, K, bias, resid, ldo, pre, part, st);
+                      const uint16_t* wb, const float* bias, const float* resid, float* pre, int N, int K,
+                      uint16_t* yb = nullptr) {
+        if (bf) return gemm_bf16(epi, out, ldo, xb, K, wb, K, BT, N, K, bias, resid, ldo, pre, part, st, nullptr, yb, N);
         return linear_forward(out, ldo, x, w, bias, resid, pre, BT, N, K, part, st);
     };
     for (int l = 0; l < L; l++) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN1, l), A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), residual,
-                           P(g, P_LN1W) + l * C, P(g, P_LN1B) + l * C, BT, C, st));
-        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_LN1, l), BT, C, BA(g, BA_LN1, l), nullptr, nullptr, st));
+                           P(g, P_LN1W) + l * C, P(g, P_LN1B) + l * C, BT, C, st, bf_copy(BA_LN1, l)));
         HIPCHK(g, linear(BF16_BIAS, A(g, GPT2_ACT_QKV, l), 3 * C, A(g, GPT2_ACT_LN1, l), BA(g, BA_LN1, l),
                          P(g, P_QKVW) + (size_t)l * 3 * C * C, BA(g, BW_Q, l), P(g, P_QKVB) + l * 3 * C, nullptr,
                          nullptr, 3 * C, C));
@@ -332,36 +332,32 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
             uint16_t* rm[3] = {BA(g, BA_HQ, l), BA(g, BA_HK, l), BA(g, BA_HV, l)};
             uint16_t* tr[3] = {BA(g, BA_HQT, l), BA(g, BA_HKT, l), BA(g, BA_HVT, l)};
             HIPCHK(g, attn_prep_bf16(A(g, GPT2_ACT_QKV, l), 3 * C, C, 3, rm, tr, B, T, C, NH, st));
-            HIPCHK(g, attention_forward_bf16(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), attn_copies(g, l), B, T,
-                                             C, NH, st));
+            HIPCHK(g, attention_forward_bf16(A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l),
+                                             attn_copies(g, l), B, T, C, NH, st));
         } else {
             HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T,
                                         C, NH, st));
         }
-        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_ATTY, l), BT, C, BA(g, BA_ATTY, l), nullptr, nullptr, st));
         HIPCHK(g, linear(BF16_BIAS_RESID, A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTY, l),
                          P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BW_A, l), P(g, P_ATTPROJB) + l * C, residual,
                          nullptr, C, C));
         HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN2, l), A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l),
-                           A(g, GPT2_ACT_RESIDUAL2, l), P(g, P_LN2W) + l * C, P(g, P_LN2B) + l * C, BT, C, st));
-        if (bf) HIPCHK(g, cast_rows(A(g, GPT2_ACT_LN2, l), BT, C, BA(g, BA_LN2, l), nullptr, nullptr, st));
+                           A(g, GPT2_ACT_RESIDUAL2, l), P(g, P_LN2W) + l * C, P(g, P_LN2B) + l * C, BT, C, st,
+                           bf_copy(BA_LN2, l)));
         HIPCHK(g, linear(BF16_BIAS_GELU, A(g, GPT2_ACT_FCH_GELU, l), 4 * C, A(g, GPT2_ACT_LN2, l), BA(g, BA_LN2, l),
                          P(g, P_FCW) + (size_t)l * 4 * C * C, BA(g, BW_F, l), P(g, P_FCB) + l * 4 * C, nullptr,
-                         A(g, GPT2_ACT_FCH, l), 4 * C, C));
-        if (bf)
-            HIPCHK(g, cast_rows(A(g, GPT2_ACT_FCH_GELU, l), BT, 4 * C, BA(g, BA_FCHG, l), nullptr, nullptr, st));
+                         A(g, GPT2_ACT_FCH, l), 4 * C, C, bf_copy(BA_FCHG, l)));
         HIPCHK(g, linear(BF16_BIAS_RESID, A(g, GPT2_ACT_RESIDUAL3, l), C, A(g, GPT2_ACT_FCH_GELU, l), BA(g, BA_FCHG, l),
                          P(g, P_FCPROJW) + (size_t)l * 4 * C * C, BA(g, BW_P, l), P(g, P_FCPROJB) + l * C,
                          A(g, GPT2_ACT_RESIDUAL2, l), nullptr, C, 4 * C));
     }
     HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LNF), A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD),
-                       A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, st));
+                       A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW), P(g, P_LNFB), BT, C, st, bf_copy(BA_LNF, 0)));
     // LM head: the GEMM's epilogue also leaves each tile's per-row (max, sum of exp), which
     // one small pass combines into the log-sum-exp and the loss (no second read of the
     // logits)
     float* lsep = S(g, g->lay.lsep);
     if (bf) {
-        HIPCHK(g, cast_rows(A(g, GPT2_ACT_LNF), BT, C, BA(g, BA_LNF), nullptr, nullptr, st));
         HIPCHK(g, gemm_bf16(BF16_STORE, A(g, GPT2_ACT_LOGITS), Vp, BA(g, BA_LNF), C, BA(g, BW_WTE), C, BT, V, C, nullptr,
                             nullptr, 0, nullptr, part, st, lsep));
     } else {
@@ -492,7 +488,7 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     // transposed copy) in the next layer come after it
     auto bpart = [&](int kind) { return S(g, g->lay.bpart) + (size_t)kind * bias_partial_floats(BT, 4 * C); };
     auto grad_copies = [&](const float* dy, int n, uint16_t* yb, int kind) -> hipError_t {
-        return cast_rows(dy, BT, n, yb, nullptr, bpart(kind), st);
+        return cast_rows(dy, BT, n, yb, bpart(kind), st);
     };
     auto bias_w = [&](float* db, int n, int kind) { return bias_reduce(db, bpart(kind), BT, n, sw); };
     // dW[M,N] += dY^T X (and, fp32 only, db += column sums of dY): dY (BT, M), X (BT, N);

@@ -54,10 +54,12 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
 //   BF16_BIAS_GELU: pre = . + bias, C = gelu(pre);  BF16_ACCUM: C += .;
 //   BF16_GELU_BWD: C = . * gelu'(aux).   aux has leading dimension ldaux, pre ldc.
 enum { BF16_STORE = 0, BF16_BIAS, BF16_BIAS_RESID, BF16_BIAS_GELU, BF16_ACCUM, BF16_GELU_BWD };
-// lse_part with BF16_STORE: the log-sum-exp partials as linear_forward's.
+// lse_part with BF16_STORE: the log-sum-exp partials as linear_forward's.  cb with
+// BF16_BIAS_GELU: the bf16 rounding of C as well (leading dimension ldcb; N, ldcb even,
+// cb 4-byte aligned).
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
                      int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
-                     hipStream_t st, float* lse_part = nullptr);
+                     hipStream_t st, float* lse_part = nullptr, uint16_t* cb = nullptr, long ldcb = 0);
 // C[M,N] += sum over k of A[k,m] B[k,n] with bfloat16 A, B stored row-contiguous, as
 // [K][lda] and [K][ldb] (the weight gradients dW += dY^T X on the straight copies of dY and
 // X): lda >= M, ldb >= N, both multiples of 8; 16-byte aligned; the elements of a row past
@@ -98,8 +100,9 @@ hipError_t xent_grad_bf16(uint16_t* db, uint16_t* dt, long ldt, const float* log
                           const int32_t* targets, float scale, int N, int V, hipStream_t st);
 
 // ---- LayerNorm (norm.hip) -----------------------------------------------------------
+// yb (nullable, 8-byte aligned): the bf16 rounding of y, same layout.
 hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,
-                             const float* b, int N, int C, float eps, hipStream_t st);
+                             const float* b, int N, int C, float eps, hipStream_t st, uint16_t* yb = nullptr);
 // dx (+)= ..., dw/db (+)= ...; accumulate flags choose += or =.  partial needs
 // layernorm_partial_floats(N, C) floats.
 size_t layernorm_partial_floats(int N, int C);
@@ -111,7 +114,7 @@ hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, 
 // is written as 0 so the LayerNorm activation layout still holds.  The backward adds
 // only dw (same partial scratch as layernorm_backward, at most that size).
 hipError_t rmsnorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w, int N, int C,
-                           float eps, hipStream_t st);
+                           float eps, hipStream_t st, uint16_t* yb = nullptr);
 hipError_t rmsnorm_backward(float* dx, float* dw, const float* dy, const float* x, const float* w,
                             const float* mean, const float* rstd, int N, int C, bool accumulate_dx,
                             bool accumulate_dw, float* partial, hipStream_t st);
@@ -160,9 +163,10 @@ struct AttnBf16 {
     const uint16_t *q, *k, *v;     // row-major copies
     const uint16_t *qt, *kt, *vt;  // transposed copies
 };
-// out (B,T,C) fp32 and lse (B,NH,T) from bf16 q, k, vt (the probabilities unrounded).
-hipError_t attention_forward_bf16(float* out, float* lse, const AttnBf16& a, int B, int T, int C, int NH,
-                                  hipStream_t st);
+// out (B,T,C) fp32 and lse (B,NH,T) from bf16 q, k, vt (the probabilities unrounded);
+// outb (nullable, 4-byte aligned): the bf16 rounding of out, same layout.
+hipError_t attention_forward_bf16(float* out, uint16_t* outb, float* lse, const AttnBf16& a, int B, int T, int C,
+                                  int NH, hipStream_t st);
 // dqkv (B,T,3C) fp32 (overwritten) from bf16 dO (row-major dob, transposed dot), the fp32
 // output `out`, lse, and q, k, v, qt, kt; delta needs B*NH*T floats.
 hipError_t attention_backward_bf16(float* dqkv, float* delta, const uint16_t* dob, const uint16_t* dot,

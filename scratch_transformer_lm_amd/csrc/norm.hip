@@ -23,7 +23,8 @@ constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
 constexpr int LN_MAX_BLOCKS = 512;
 
 template <int VPL, bool RMS>
-__global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, float* __restrict__ mean,
+__global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, uint16_t* __restrict__ yb,
+                                                     float* __restrict__ mean,
                                                      float* __restrict__ rstd, const float* __restrict__ x,
                                                      const float* __restrict__ w, const float* __restrict__ b,
                                                      int N, int C, float eps) {
@@ -66,6 +67,9 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, floa
             o.z = (v[j].z - m) * r * ww.z + bv.z;
             o.w = (v[j].w - m) * r * ww.w + bv.w;
             yr[i] = o;
+            if (yb)
+                reinterpret_cast<uint2*>(yb + (long)row * C)[i] =
+                    make_uint2(bf16_pack2(o.x, o.y), bf16_pack2(o.z, o.w));
         }
     }
     if (lane == 0) {
@@ -212,14 +216,14 @@ namespace {
 
 template <bool RMS>
 hipError_t norm_forward(float* y, float* mean, float* rstd, const float* x, const float* w, const float* b, int N,
-                        int C, float eps, hipStream_t st) {
-    if (C % 4 || C > 4096 || N < 0) return hipErrorInvalidValue;
+                        int C, float eps, hipStream_t st, uint16_t* yb) {
+    if (C % 4 || C > 4096 || N < 0 || ((uintptr_t)yb & 7)) return hipErrorInvalidValue;
     if (N == 0) return hipSuccess;
     const int vpl = (C / 4 + 63) / 64;
     dim3 grid((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), block(256);
     ProfScope ps(st, RMS ? "rms_fwd_kernel" : "ln_fwd_kernel", 0.0,
-                 4.0 * ((double)N * C * 2 + 2.0 * N + (RMS ? 1.0 : 2.0) * C));
-#define LN_FWD(V) hipLaunchKernelGGL((ln_fwd_kernel<V, RMS>), grid, block, 0, st, y, mean, rstd, x, w, b, N, C, eps)
+                 4.0 * ((double)N * C * (yb ? 2.5 : 2.0) + 2.0 * N + (RMS ? 1.0 : 2.0) * C));
+#define LN_FWD(V) hipLaunchKernelGGL((ln_fwd_kernel<V, RMS>), grid, block, 0, st, y, yb, mean, rstd, x, w, b, N, C, eps)
     switch (vpl) {
         case 1: LN_FWD(1); break;
         case 2: LN_FWD(2); break;
@@ -275,13 +279,13 @@ hipError_t norm_backward(float* dx, float* dw, float* db, const float* dy, const
 }  // namespace
 
 hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w,
-                             const float* b, int N, int C, float eps, hipStream_t st) {
-    return norm_forward<false>(y, mean, rstd, x, w, b, N, C, eps, st);
+                             const float* b, int N, int C, float eps, hipStream_t st, uint16_t* yb) {
+    return norm_forward<false>(y, mean, rstd, x, w, b, N, C, eps, st, yb);
 }
 
 hipError_t rmsnorm_forward(float* y, float* mean, float* rstd, const float* x, const float* w, int N, int C,
-                           float eps, hipStream_t st) {
-    return norm_forward<true>(y, mean, rstd, x, w, nullptr, N, C, eps, st);
+                           float eps, hipStream_t st, uint16_t* yb) {
+    return norm_forward<true>(y, mean, rstd, x, w, nullptr, N, C, eps, st, yb);
 }
 
 size_t layernorm_partial_floats(int N, int C) { return (size_t)ln_blocks(N) * 2 * C; }
