@@ -3,18 +3,20 @@
 // The pages name mixed precision as llm.c's next step (新智元 article "千行C代码训完
 // GPT-2", 纯CUDA也可训; "OpenAI创始大神手搓千行C代码训练GPT", opening).  Here every
 // linear layer and the LM head multiply bfloat16 roundings of their operands on the
-// matrix cores; master weights, activations and everything else stay fp32.  The bf16
-// GEMM wants both operands k-contiguous, so each operand is written once as a bf16 copy
-// in the layout its products read:
+// matrix cores; master weights, activations and everything else stay fp32.  Each
+// operand is written once as a bf16 copy in the layout its products read:
 //   forward:   X (rows, in) and W (out, in) as they are;
-//   dgrad:     dY (rows, out) as it is, W transposed (in, out);
-//   wgrad:     dY and X transposed (out, rows) and (in, rows), rows padded to 64 with
-//              zeros, since k runs over the rows.
-// One 64x64-tile kernel reads an fp32 tensor once and writes the straight copy, the
-// transposed copy (through LDS) and, for an output gradient, the bias gradient's column
-// sums per 128-row block (the bias gradient is summed from the unrounded fp32 values).
-// The LM head's output gradient, softmax minus one-hot over the rows' log-sum-exp, is
-// formed by the same kernel from the logits.  All of these kernels are bound by HBM.
+//   dgrad:     dY (rows, out) as it is, W transposed (in, out), rows padded to 64 with
+//              zeros;
+//   wgrad:     dY and X as they are (the GEMM reads them row-contiguous, with
+//              transposing LDS reads).
+// The layers' inputs get their copies from their producers (LayerNorm, attention, the fc
+// GEMM's GELU epilogue).  Here one 64x64-tile kernel reads an fp32 tensor once and
+// writes the straight copy, optionally the transposed copy (through LDS; the weights)
+// and, for an output gradient, the bias gradient's column sums per 128-row block (the
+// bias gradient is summed from the unrounded fp32 values).  The LM head's output
+// gradient, softmax minus one-hot over the rows' log-sum-exp, is formed by the same
+// kernel from the logits.  All of these kernels are bound by HBM.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -190,16 +192,14 @@ hipError_t cast_bf16_flat(uint16_t* xb, const float* x, size_t n, hipStream_t st
     return hipGetLastError();
 }
 
-hipError_t xent_grad_bf16(uint16_t* db, uint16_t* dt, long ldt, const float* logits, long Vp, const float* lse,
-                          const int32_t* targets, float scale, int N, int V, hipStream_t st) {
+hipError_t xent_grad_bf16(uint16_t* db, const float* logits, long Vp, const float* lse, const int32_t* targets,
+                          float scale, int N, int V, hipStream_t st) {
     if (Vp < V || Vp % 64 || !lse || !targets) return hipErrorInvalidValue;
     CastArgs a{};
     a.x = logits;
     a.ldx = Vp;
     a.xb = db;
     a.ldb = Vp;
-    a.xt = dt;
-    a.ldt = ldt;
     a.rows = N;
     a.cols = (int)Vp;
     a.batch = 1;

@@ -484,8 +484,8 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     const bool bf = bf_on(g);
     // the bias gradient's column sums per row block, one buffer per kind of dY (0 fcproj,
     // 1 fc, 2 attproj, 3 qkv): the second stream adds them up (bias_w) ahead of the kind's
-    // wgrad, and the events that let the main stream rewrite that kind's dY (or its
-    // transposed copy) in the next layer come after it
+    // wgrad, and the events that let the main stream rewrite that kind's dY (and its copy)
+    // in the next layer come after it
     auto bpart = [&](int kind) { return S(g, g->lay.bpart) + (size_t)kind * bias_partial_floats(BT, 4 * C); };
     auto grad_copies = [&](const float* dy, int n, uint16_t* yb, int kind) -> hipError_t {
         return cast_rows(dy, BT, n, yb, bpart(kind), st);
@@ -510,8 +510,8 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     uint16_t* dfchb = bf ? BS(g, BS_DFCH) : nullptr;
     uint16_t* dqkvb = bf ? BS(g, BS_DQKV) : nullptr;
     if (bf) {
-        HIPCHK(g, xent_grad_bf16(BS(g, BS_DLOG), nullptr, 0, logits, Vp, A(g, GPT2_ACT_LOGITS_LSE), tok_tgt(g), xo.scale,
-                                 BT, V, st));
+        HIPCHK(g, xent_grad_bf16(BS(g, BS_DLOG), logits, Vp, A(g, GPT2_ACT_LOGITS_LSE), tok_tgt(g), xo.scale, BT, V,
+                                 st));
         HIPCHK(g, mark(EV_LM, st));
         HIPCHK(g, after(sw, EV_LM));
         HIPCHK(g, gemm_bf16_rows(G(g, P_WTE), C, BS(g, BS_DLOG), Vp, BA(g, BA_LNF), C, V, C, BT, part_w, sw));

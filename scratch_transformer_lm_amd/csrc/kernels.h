@@ -94,10 +94,9 @@ hipError_t bias_reduce(float* db, const float* bpart, int rows, int cols, hipStr
 // Flat copy: xb[i] = bf16(x[i]), n a multiple of 4.
 hipError_t cast_bf16_flat(uint16_t* xb, const float* x, size_t n, hipStream_t st);
 // The LM head's output gradient in bf16: d[r, c] = (exp(z[r, c] - lse[r]) - [c == targets[r]]) * scale for
-// c < V, 0 for V <= c < Vp, written row-major (N, Vp) to db and transposed (Vp, N_pad) to dt
-// (N_pad = N rounded up to 64, zero beyond N).  logits has leading dimension Vp.
-hipError_t xent_grad_bf16(uint16_t* db, uint16_t* dt, long ldt, const float* logits, long Vp, const float* lse,
-                          const int32_t* targets, float scale, int N, int V, hipStream_t st);
+// c < V, 0 for V <= c < Vp, written row-major (N, Vp) to db.  logits has leading dimension Vp.
+hipError_t xent_grad_bf16(uint16_t* db, const float* logits, long Vp, const float* lse, const int32_t* targets,
+                          float scale, int N, int V, hipStream_t st);
 
 // ---- LayerNorm (norm.hip) -----------------------------------------------------------
 // yb (nullable, 8-byte aligned): the bf16 rounding of y, same layout.
