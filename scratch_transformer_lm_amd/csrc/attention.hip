@@ -89,7 +89,16 @@ GPT2_DEV void lds_put(float* dst, const float (&v)[DG]) {
 template <int HS>
 GPT2_DEV void tile_load(float4 (&reg)[HS / 16], const float* src, long ld, int r0, int T) {
     constexpr int C4 = HS / 4, RPP = 256 / C4;
+    static_assert(RPP * (HS / 16) == TILE, "one pass per 256 threads covers RPP rows");
     const int t = threadIdx.x;
+    const float* s0 = src + (long)r0 * ld;  // the tile's first row (uniform)
+    if (r0 + TILE <= T) {
+        // whole tile inside the sequence: no per-row checks
+#pragma unroll
+        for (int p = 0; p < HS / 16; p++)
+            reg[p] = *reinterpret_cast<const float4*>(s0 + (long)(t / C4 + RPP * p) * ld + (t % C4) * 4);
+        return;
+    }
 #pragma unroll
     for (int p = 0; p < HS / 16; p++) {
         const int r = r0 + t / C4 + RPP * p;
