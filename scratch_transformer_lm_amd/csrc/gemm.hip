@@ -6,6 +6,8 @@
 //   forward  Y = X W^T (+ bias ...):  A = X  (k contiguous),  B = W  (k contiguous)
 //   dgrad    dX = dY W:               A = dY (k contiguous),  B = W  (n contiguous)
 //   wgrad    dW += dY^T X:            A = dY (m contiguous),  B = X  (n contiguous)
+// (the bfloat16 variant multiplies bf16 copies: forward and dgrad with both operands
+// k-contiguous, W transposed for the dgrad; wgrad as above, see gemm_body)
 //
 // Design for CDNA4: 256 threads = 4 wave64s, block tile 128x128 (or 128x96 where that
 // count of tiles fills whole rounds of the grid and 128x128 does not), each wave a
@@ -533,11 +535,13 @@ GPT2_DEV void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
 }
 
-// BF: both operands are bfloat16 (mixed-precision variant), addressed as float pairs: a
-// row of K bf16 values is a row of K/2 floats, so the k-tiles, their LDS layout and the
-// transfers are exactly those of the fp32 k-contiguous case, and each 16-float fragment
-// group (16 bytes per lane = 8 bf16) feeds one v_mfma_f32_16x16x32_bf16 per block
-// instead of four fp32 steps.
+// BF: both operands are bfloat16 (mixed-precision variant).  k-contiguous (forward,
+// dgrad), they are addressed as float pairs: a row of K bf16 values is a row of K/2
+// floats, so the k-tiles, their LDS layout and the transfers are exactly those of the
+// fp32 k-contiguous case, and each 16-float fragment group (16 bytes per lane = 8 bf16)
+// feeds one v_mfma_f32_16x16x32_bf16 per block instead of four fp32 steps.
+// Row-contiguous (the weight gradients, TR below), the k-tiles are 64 k rows of 128 bf16
+// in the swizzled layout of trswz, and each fragment is two transposing LDS reads.
 template <bool A_K, bool B_K, int EPI, bool XF, int BN, bool BF>
 GPT2_DEV void gemm_body(const Params& p) {
     static_assert(BN == 128 || (BN == 96 && A_K) || (BN == 256 && BF), "tile widths: 128; 96 (A k-contiguous); 256 (bf16)");
