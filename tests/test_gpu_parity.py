@@ -645,6 +645,6 @@ def test_bf16_split_k_weight_gradients(G):
 
 
 def test_bf16_ragged_shape(G):
-    """bf16 variant at the 124M widths with 300 rows: the transposed copies' zero padding
-    (300 -> 320 rows of k) and ragged GEMM edges."""
+    """bf16 variant at the 124M widths with 300 rows: the weight gradients' last k-tile
+    (300 = 4 x 64 + 44 rows, filled with zeros past row 300) and ragged GEMM edges."""
     check_training(G, S.GPT2_124M_SHORT, 1, variant=G.VARIANT_BF16, B=3, T=100)
