@@ -340,11 +340,53 @@ __global__ __launch_bounds__(NTH, 2) void attn_fwd_bf16_kernel(float* __restrict
     if (g4 == 0 && tq < T) lse[((long)b * NH + h) * T + tq] = (m + log2_hw(l)) * LN2;
 }
 
+// Output of a backward kernel: each wave holds 16 rows (row0 + 4 g4 + v) x 16 DG columns
+// (i16 + 16 d) of the block's 64 x HS tile.  Stores the fp32 values, optionally their bf16
+// rounding (pairs of rows through bf16_store_rows2), and optionally the tile's column sums
+// over the rows inside the sequence (the bias gradient's partial row), added in a fixed
+// order: v, then the four lane groups, then the four waves.  red is LDS scratch of
+// 64 DG floats that no wave reads any more.
+template <int DG>
+GPT2_DEV void write_grad(const f32x4 (&x)[DG], float* out, uint16_t* outb, long ld, int row0, int T, float* csum,
+                         float* red, int wave, int i16, int g4) {
+#pragma unroll
+    for (int v = 0; v < 4; v++)
+        if (row0 + 4 * g4 + v < T) {
+#pragma unroll
+            for (int d = 0; d < DG; d++) out[(long)(4 * g4 + v) * ld + 16 * d] = x[d][v];
+        }
+    if (outb) {
+#pragma unroll
+        for (int v = 0; v < 4; v += 2)
+#pragma unroll
+            for (int d = 0; d < DG; d++) {
+                uint16_t* p0 = outb + (long)(4 * g4 + v) * ld + 16 * d;
+                bf16_store_rows2(p0, p0 + ld, x[d][v], x[d][v + 1], row0 + 4 * g4 + v < T, row0 + 4 * g4 + v + 1 < T);
+            }
+    }
+    if (csum) {
+        __syncthreads();
+#pragma unroll
+        for (int d = 0; d < DG; d++) {
+            float sum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                if (row0 + 4 * g4 + v < T) sum += x[d][v];
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            if (g4 == 0) red[wave * 16 * DG + 16 * d + i16] = sum;
+        }
+        __syncthreads();
+        const int t = threadIdx.x;
+        if (t < 16 * DG) csum[t] = ((red[t] + red[16 * DG + t]) + red[32 * DG + t]) + red[48 * DG + t];
+    }
+}
+
 // ---------------------------------------------------------------------------- dq (+ D)
 template <int HS>
 __global__ __launch_bounds__(NTH, 2) void attn_bwd_dq_bf16_kernel(
-    float* __restrict__ dqkv, float* __restrict__ delta, const uint16_t* __restrict__ dob,
-    const float* __restrict__ out, const uint16_t* __restrict__ qb, const uint16_t* __restrict__ kb,
+    float* __restrict__ dqkv, uint16_t* __restrict__ dqkvb, float* __restrict__ bsum, float* __restrict__ delta,
+    const uint16_t* __restrict__ dob, const float* __restrict__ out, const uint16_t* __restrict__ qb, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const uint16_t* __restrict__ kt_, const float* __restrict__ lse, int B, int T,
     int C, int NH, int Tp, float scale) {
     constexpr int NKS = (HS + 31) / 32, DG = HS / 16, RS = HS + 8, TS = TILE + 8;
@@ -448,21 +490,19 @@ __global__ __launch_bounds__(NTH, 2) void attn_bwd_dq_bf16_kernel(
     step(qt, std::true_type{});
     const long ld = 3L * C;
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-        const int q = q0 + 4 * g4 + v;
-        if (q < T) {
-            float* drow = dqkv + ((long)b * T + q) * ld + h * HS + i16;
-#pragma unroll
-            for (int d = 0; d < DG; d++) drow[16 * d] = dq[d][v] * scale;
-        }
-    }
+    for (int d = 0; d < DG; d++) dq[d] *= scale;
+    const long o = ((long)b * T + q0) * ld + h * HS + i16;
+    write_grad<DG>(dq, dqkv + o, dqkvb ? dqkvb + o : nullptr, ld, q0, T,
+                   bsum ? bsum + ((long)b * nqt + qt) * ld + h * HS : nullptr, reinterpret_cast<float*>(Ks), wave, i16,
+                   g4);
 }
 
 // ---------------------------------------------------------------------------- dk, dv
 // One block per (b, h, 64-key tile), each wave 16 keys; query tiles from the diagonal on.
 template <int HS>
 __global__ __launch_bounds__(NTH, 2) void attn_bwd_dkdv_bf16_kernel(
-    float* __restrict__ dqkv, const uint16_t* __restrict__ dob, const uint16_t* __restrict__ dot_,
+    float* __restrict__ dqkv, uint16_t* __restrict__ dqkvb, float* __restrict__ bsum,
+    const uint16_t* __restrict__ dob, const uint16_t* __restrict__ dot_,
     const uint16_t* __restrict__ qb, const uint16_t* __restrict__ qt_, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const float* __restrict__ lse, const float* __restrict__ delta, int B, int T,
     int C, int NH, int Tp, float scale) {
@@ -575,17 +615,14 @@ __global__ __launch_bounds__(NTH, 2) void attn_bwd_dkdv_bf16_kernel(
     for (int qtile = kt + 1; qtile < nqt; qtile++) step(qtile, std::false_type{});
     const long ld = 3L * C;
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-        const int key = k0 + 4 * g4 + v;
-        if (key < T) {
-            float* row = dqkv + ((long)b * T + key) * ld + h * HS + i16;
-#pragma unroll
-            for (int d = 0; d < DG; d++) {
-                row[C + 16 * d] = dk[d][v] * scale;
-                row[2 * C + 16 * d] = dv[d][v];
-            }
-        }
-    }
+    for (int d = 0; d < DG; d++) dk[d] *= scale;
+    const long o = ((long)b * T + k0) * ld + h * HS + i16;
+    float* cs = bsum ? bsum + ((long)b * nqt + kt) * ld + h * HS : nullptr;
+    float* red = reinterpret_cast<float*>(Qs);
+    write_grad<DG>(dk, dqkv + o + C, dqkvb ? dqkvb + o + C : nullptr, ld, k0, T, cs ? cs + C : nullptr, red, wave, i16,
+                   g4);
+    write_grad<DG>(dv, dqkv + o + 2 * C, dqkvb ? dqkvb + o + 2 * C : nullptr, ld, k0, T, cs ? cs + 2 * C : nullptr, red,
+                   wave, i16, g4);
 }
 
 template <int HS>
@@ -601,20 +638,20 @@ hipError_t fwd_hs(const AttnBf16& a, float* out, uint16_t* outb, float* lse, int
 }
 
 template <int HS>
-hipError_t bwd_hs(const AttnBf16& a, float* dqkv, float* delta, const uint16_t* dob, const uint16_t* dot,
-                  const float* out, const float* lse, int B, int T, int C, int NH, hipStream_t st) {
+hipError_t bwd_hs(const AttnBf16& a, float* dqkv, uint16_t* dqkvb, float* bsum, float* delta, const uint16_t* dob,
+                  const uint16_t* dot, const float* out, const float* lse, int B, int T, int C, int NH, hipStream_t st) {
     const int nqt = (T + TILE - 1) / TILE, Tp = nqt * TILE;
     const float scale = 1.0f / sqrtf((float)HS);
     const double tri = B * NH * ((double)T * (T + 1) / 2) * HS;
     {
         ProfScope ps(st, "attn_bwd_dq_bf16_kernel", 6.0 * tri, (double)B * T * C * (2.0 * 5 + 4.0 * 2));
-        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<HS>), dim3(B * NH * nqt), dim3(NTH), 0, st, dqkv, delta, dob, out,
-                           a.q, a.k, a.v, a.kt, lse, B, T, C, NH, Tp, scale);
+        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<HS>), dim3(B * NH * nqt), dim3(NTH), 0, st, dqkv, dqkvb, bsum,
+                           delta, dob, out, a.q, a.k, a.v, a.kt, lse, B, T, C, NH, Tp, scale);
     }
     {
         ProfScope ps(st, "attn_bwd_dkdv_bf16_kernel", 8.0 * tri, (double)B * T * C * (2.0 * 6 + 4.0 * 2));
-        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<HS>), dim3(B * NH * nqt), dim3(NTH), 0, st, dqkv, dob, dot, a.q,
-                           a.qt, a.k, a.v, lse, delta, B, T, C, NH, Tp, scale);
+        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<HS>), dim3(B * NH * nqt), dim3(NTH), 0, st, dqkv, dqkvb, bsum,
+                           dob, dot, a.q, a.qt, a.k, a.v, lse, delta, B, T, C, NH, Tp, scale);
     }
     return hipGetLastError();
 }
@@ -661,14 +698,18 @@ hipError_t attention_forward_bf16(float* out, uint16_t* outb, float* lse, const 
     }
 }
 
-hipError_t attention_backward_bf16(float* dqkv, float* delta, const uint16_t* dob, const uint16_t* dot,
-                                   const float* out, const float* lse, const AttnBf16& a, int B, int T, int C, int NH,
-                                   hipStream_t st) {
+size_t attn_bias_partial_floats(int B, int T, int C) { return (size_t)B * ((T + TILE - 1) / TILE) * 3 * (size_t)C; }
+int attn_bias_partial_rows(int B, int T) { return B * ((T + TILE - 1) / TILE); }
+
+hipError_t attention_backward_bf16(float* dqkv, uint16_t* dqkvb, float* bsum, float* delta, const uint16_t* dob,
+                                   const uint16_t* dot, const float* out, const float* lse, const AttnBf16& a, int B,
+                                   int T, int C, int NH, hipStream_t st) {
+    if (dqkvb && ((uintptr_t)dqkvb & 3)) return hipErrorInvalidValue;
     if (B <= 0 || T <= 0) return hipSuccess;
     switch (C / NH) {
-        case 16: return bwd_hs<16>(a, dqkv, delta, dob, dot, out, lse, B, T, C, NH, st);
-        case 32: return bwd_hs<32>(a, dqkv, delta, dob, dot, out, lse, B, T, C, NH, st);
-        case 64: return bwd_hs<64>(a, dqkv, delta, dob, dot, out, lse, B, T, C, NH, st);
+        case 16: return bwd_hs<16>(a, dqkv, dqkvb, bsum, delta, dob, dot, out, lse, B, T, C, NH, st);
+        case 32: return bwd_hs<32>(a, dqkv, dqkvb, bsum, delta, dob, dot, out, lse, B, T, C, NH, st);
+        case 64: return bwd_hs<64>(a, dqkv, dqkvb, bsum, delta, dob, dot, out, lse, B, T, C, NH, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -173,8 +173,11 @@ hipError_t cast_bf16(const CastArgs& a, hipStream_t st) {
 }
 
 hipError_t bias_reduce(float* db, const float* bpart, int rows, int cols, hipStream_t st) {
-    if (rows <= 0 || cols <= 0) return hipSuccess;
-    const int nrb = (rows + RB - 1) / RB;
+    return bias_reduce_parts(db, bpart, (rows + RB - 1) / RB, cols, st);
+}
+
+hipError_t bias_reduce_parts(float* db, const float* bpart, int nrb, int cols, hipStream_t st) {
+    if (nrb <= 0 || cols <= 0) return hipSuccess;
     ProfScope ps(st, "bias_reduce_kernel", 0.0, 4.0 * ((double)nrb * cols + 2.0 * cols));
     hipLaunchKernelGGL(bias_reduce_kernel, dim3((cols + TILE - 1) / TILE), dim3(TILE * BR_GROUPS), 0, st, db, bpart,
                        nrb, cols);

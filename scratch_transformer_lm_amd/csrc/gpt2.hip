@@ -84,6 +84,12 @@ struct Layout {
     size_t ba[NBA], ba_l[NBA], bs[NBS], bpart;
 };
 
+// floats of one output-gradient kind's bias partial sums: per 128-row block (the casts)
+// or per 64-row tile of each sequence (attention's dqkv)
+size_t bias_slot_floats(size_t B, size_t T, size_t C) {
+    return std::max(bias_partial_floats((int)(B * T), (int)(4 * C)), attn_bias_partial_floats((int)B, (int)T, (int)C));
+}
+
 Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     Layout y{};
     const size_t C = c->channels, L = c->num_layers, NH = c->num_heads, V = c->vocab_size;
@@ -161,7 +167,7 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     if (variant & GPT2_VARIANT_BF16) {
         const size_t n[NBS] = {BT * C, BT * 4 * C, BT * 3 * C, BT * y.Vp, BT * C, attn_bf16_head_elems(B, T, (int)C)};
         for (int i = 0; i < NBS; i++) y.bs[i] = take((n[i] + 1) / 2);
-        y.bpart = take(4 * bias_partial_floats((int)BT, (int)(4 * C)));  // one per output-gradient kind
+        y.bpart = take(4 * bias_slot_floats(B, T, C));  // one per output-gradient kind
     }
     y.n_scratch = s;
     return y;
@@ -486,7 +492,7 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     // 1 fc, 2 attproj, 3 qkv): the second stream adds them up (bias_w) ahead of the kind's
     // wgrad, and the events that let the main stream rewrite that kind's dY (and its copy)
     // in the next layer come after it
-    auto bpart = [&](int kind) { return S(g, g->lay.bpart) + (size_t)kind * bias_partial_floats(BT, 4 * C); };
+    auto bpart = [&](int kind) { return S(g, g->lay.bpart) + (size_t)kind * bias_slot_floats(B, T, C); };
     auto grad_copies = [&](const float* dy, int n, uint16_t* yb, int kind) -> hipError_t {
         return cast_rows(dy, BT, n, yb, bpart(kind), st);
     };
@@ -578,9 +584,12 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
             uint16_t* rm[1] = {BS(g, BS_HDO)};
             uint16_t* tr[1] = {BS(g, BS_HDOT)};
             HIPCHK(g, attn_prep_bf16(datty, C, 0, 1, rm, tr, B, T, C, NH, st));
-            HIPCHK(g, attention_backward_bf16(dqkv, S(g, g->lay.delta), BS(g, BS_HDO), BS(g, BS_HDOT),
-                                              A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), attn_copies(g, l), B,
-                                              T, C, NH, st));
+            // dqkv's bf16 copy and the qkv bias's partial sums come from the attention
+            // kernels, or, in the rotary variant, from a cast after the rotation below
+            const bool rot = rope_on(g);
+            HIPCHK(g, attention_backward_bf16(dqkv, rot ? nullptr : dqkvb, rot ? nullptr : bpart(3), S(g, g->lay.delta),
+                                              BS(g, BS_HDO), BS(g, BS_HDOT), A(g, GPT2_ACT_ATTY, l),
+                                              A(g, GPT2_ACT_ATT_LSE, l), attn_copies(g, l), B, T, C, NH, st));
         } else {
             HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
                                          A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
@@ -588,10 +597,12 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
         // rotary variant: attention gave the gradient of the rotated q and k; rotate it back
         if (rope_on(g)) HIPCHK(g, rope_backward(dqkv, S(g, g->lay.rope), B, T, C, NH, st));
-        if (bf) HIPCHK(g, grad_copies(dqkv, 3 * C, dqkvb, 3));
+        if (bf && rope_on(g)) HIPCHK(g, grad_copies(dqkv, 3 * C, dqkvb, 3));
         HIPCHK(g, mark(EV_DQKV, st));
         HIPCHK(g, after(sw, EV_DQKV));
-        if (bf) HIPCHK(g, bias_w(G(g, P_QKVB) + l * 3 * C, 3 * C, 3));
+        if (bf && rope_on(g)) HIPCHK(g, bias_w(G(g, P_QKVB) + l * 3 * C, 3 * C, 3));
+        if (bf && !rope_on(g))
+            HIPCHK(g, bias_reduce_parts(G(g, P_QKVB) + l * 3 * C, bpart(3), attn_bias_partial_rows(B, T), 3 * C, sw));
         HIPCHK(g, wgrad(G(g, P_QKVW) + (size_t)l * 3 * C * C, G(g, P_QKVB) + l * 3 * C, dqkv, dqkvb, 3 * C,
                         A(g, GPT2_ACT_LN1, l), bf ? BA(g, BA_LN1, l) : nullptr, C));
         HIPCHK(g, mark(EV_W_QKV, sw));

@@ -91,6 +91,8 @@ struct CastArgs {
 hipError_t cast_bf16(const CastArgs& a, hipStream_t st);
 size_t bias_partial_floats(int rows, int cols);
 hipError_t bias_reduce(float* db, const float* bpart, int rows, int cols, hipStream_t st);
+// db[c] += sum over p < nparts of bpart[p * cols + c], in a fixed order
+hipError_t bias_reduce_parts(float* db, const float* bpart, int nparts, int cols, hipStream_t st);
 // Flat copy: xb[i] = bf16(x[i]), n a multiple of 4.
 hipError_t cast_bf16_flat(uint16_t* xb, const float* x, size_t n, hipStream_t st);
 // The LM head's output gradient in bf16: d[r, c] = (exp(z[r, c] - lse[r]) - [c == targets[r]]) * scale for
@@ -167,10 +169,15 @@ struct AttnBf16 {
 hipError_t attention_forward_bf16(float* out, uint16_t* outb, float* lse, const AttnBf16& a, int B, int T, int C,
                                   int NH, hipStream_t st);
 // dqkv (B,T,3C) fp32 (overwritten) from bf16 dO (row-major dob, transposed dot), the fp32
-// output `out`, lse, and q, k, v, qt, kt; delta needs B*NH*T floats.
-hipError_t attention_backward_bf16(float* dqkv, float* delta, const uint16_t* dob, const uint16_t* dot,
-                                   const float* out, const float* lse, const AttnBf16& a, int B, int T, int C, int NH,
-                                   hipStream_t st);
+// output `out`, lse, and q, k, v, qt, kt; delta needs B*NH*T floats.  Optional: dqkvb
+// (4-byte aligned) gets the bf16 rounding of dqkv, same layout; bsum the column sums of
+// dqkv per 64-row tile of each sequence, attn_bias_partial_rows(B, T) rows of 3C floats in
+// (b, tile) order (bias_reduce_parts adds them).
+hipError_t attention_backward_bf16(float* dqkv, uint16_t* dqkvb, float* bsum, float* delta, const uint16_t* dob,
+                                   const uint16_t* dot, const float* out, const float* lse, const AttnBf16& a, int B,
+                                   int T, int C, int NH, hipStream_t st);
+size_t attn_bias_partial_floats(int B, int T, int C);
+int attn_bias_partial_rows(int B, int T);
 
 // ---- rotary positions (rope.hip) ------------------------------------------------------
 // table: rope_table_floats(maxT, hs) floats of (cos, sin) pairs, filled by rope_table.
