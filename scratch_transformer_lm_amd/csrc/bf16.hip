@@ -114,10 +114,10 @@ __global__ __launch_bounds__(CT_THREADS) void cast_tile_kernel(CastArgs a, XentA
     }
 }
 
-// db[c] += sum over row blocks of bpart[rb][c]: 64 columns per block, four threads per
-// column each summing every fourth row block (eight loads in flight), then the four
+// db[c] += sum over row blocks of bpart[rb][c]: 64 columns per block, sixteen threads per
+// column each summing every sixteenth row block (eight loads in flight), then the sixteen
 // partial sums added in a fixed order.
-constexpr int BR_GROUPS = 4, BR_UNROLL = 8;
+constexpr int BR_GROUPS = 16, BR_UNROLL = 8;
 __global__ __launch_bounds__(TILE * BR_GROUPS) void bias_reduce_kernel(float* db, const float* bpart, int nrb, int cols) {
     __shared__ float part[BR_GROUPS][TILE];
     const int cl = threadIdx.x % TILE, q = threadIdx.x / TILE;
@@ -136,7 +136,12 @@ __global__ __launch_bounds__(TILE * BR_GROUPS) void bias_reduce_kernel(float* db
     }
     part[q][cl] = s;
     __syncthreads();
-    if (q == 0 && c < cols) db[c] += ((part[0][cl] + part[1][cl]) + part[2][cl]) + part[3][cl];
+    if (q == 0 && c < cols) {
+        float t = part[0][cl];
+#pragma unroll
+        for (int j = 1; j < BR_GROUPS; j++) t += part[j][cl];
+        db[c] += t;
+    }
 }
 
 __global__ void cast_flat_kernel(uint2* xb, const float4* x, size_t n4) {

@@ -137,8 +137,9 @@ struct Params {
     float xscale;       // dlogits operand: d loss / d loss_row (1 / rows)
     float xlog2s;       // log2(xscale)
     float* lsep;        // EPI_STORE_LSE: partial (max, sum) pairs, [2 * tiles_n][M] float2
-    uint16_t* cb;       // EPI_BIAS_GELU: bf16 rounding of C (nullable)
+    uint16_t* cb;       // EPI_BIAS_GELU, EPI_GELU_BWD: bf16 rounding of C (nullable)
     long ldcb;
+    float* csum;        // EPI_GELU_BWD: column sums of C per 16-row slice, [M/16][N] (nullable)
     int tiles_m, tiles_n, nk;
     int G;              // persistent blocks
     int R;              // whole-tile rounds: block lb takes tiles r*G + lb, r < R
@@ -276,7 +277,7 @@ GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0,
             for (int v = 0; v < 4; v++) in[b][v] = gelu_f(in[b][v]);
     }
     store_row(p.C, p.ldc);
-    if constexpr (EPI == EPI_BIAS_GELU) {
+    if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD) {
         // the bf16 copy the next GEMM multiplies (and the weight gradient reads)
         if (p.cb) {
 #pragma unroll
@@ -286,6 +287,24 @@ GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0,
                     uint16_t* q = p.cb + (long)(r0 + v) * p.ldcb + c0 + 16 * b;
                     bf16_store_rows2(q, q + p.ldcb, in[b][v], in[b][v + 1], inside(b, v), inside(b, v + 1));
                 }
+        }
+    }
+    if constexpr (EPI == EPI_GELU_BWD) {
+        // the bias gradient of the layer whose output gradient C is: this row slice's 16
+        // rows added per column (v, then the four lane groups), one partial row per slice
+        if (p.csum) {
+            const int slice = (m0 + (wave >> 1) * 64 + 16 * a) >> 4;
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                float t = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    if (inside(b, v)) t += in[b][v];
+                t += __shfl_xor(t, 16, 64);
+                t += __shfl_xor(t, 32, 64);
+                if ((lane >> 4) == 0 && 16 * slice < p.M && (!CHECK || c0 + 16 * b < p.N))
+                    p.csum[(long)slice * p.N + c0 + 16 * b] = t;
+            }
         }
     }
 }
@@ -1308,10 +1327,11 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
 
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
                      int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
-                     hipStream_t st, float* lse_part, uint16_t* cb, long ldcb) {
+                     hipStream_t st, float* lse_part, uint16_t* cb, long ldcb, float* csum) {
     if (K % 2 || lda % 8 || ldb % 8 || lda < K || ldb < K || !aligned16(a) || !aligned16(b)) return hipErrorInvalidValue;
-    if (cb && (epi != BF16_BIAS_GELU || N % 2 || ldcb % 2 || ldcb < N || ((uintptr_t)cb & 3)))
+    if (cb && ((epi != BF16_BIAS_GELU && epi != BF16_GELU_BWD) || N % 2 || ldcb % 2 || ldcb < N || ((uintptr_t)cb & 3)))
         return hipErrorInvalidValue;
+    if (csum && epi != BF16_GELU_BWD) return hipErrorInvalidValue;
     Params p{};
     p.M = M;
     p.N = N;
@@ -1330,6 +1350,7 @@ hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, c
     p.partial = partial;
     p.cb = cb;
     p.ldcb = ldcb;
+    p.csum = csum;
     const int bn = bf16_tile_n(M, N);
     auto go = [&](auto epi_c) -> hipError_t {
         constexpr int E = decltype(epi_c)::value;

@@ -16,6 +16,7 @@
 // probabilities in its backward; activation gradients live in a small per-layer
 // scratch that each backward rewrites (the residual stream's gradient is one buffer
 // that every block adds into), so zero_grad only clears the parameter gradients.
+#include <algorithm>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -84,10 +85,12 @@ struct Layout {
     size_t ba[NBA], ba_l[NBA], bs[NBS], bpart;
 };
 
-// floats of one output-gradient kind's bias partial sums: per 128-row block (the casts)
-// or per 64-row tile of each sequence (attention's dqkv)
+// floats of one output-gradient kind's bias partial sums: per 128-row block (the casts),
+// per 64-row tile of each sequence (attention's dqkv) or per 16-row slice (the
+// GELU-backward epilogue's dfch)
 size_t bias_slot_floats(size_t B, size_t T, size_t C) {
-    return std::max(bias_partial_floats((int)(B * T), (int)(4 * C)), attn_bias_partial_floats((int)B, (int)T, (int)C));
+    return std::max({bias_partial_floats((int)(B * T), (int)(4 * C)), attn_bias_partial_floats((int)B, (int)T, (int)C),
+                     (B * T + 15) / 16 * 4 * C});
 }
 
 Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
@@ -507,9 +510,9 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     // dX[BT,N] = dY[BT,K] . W[K,N] (times gelu'(gelu_pre) if given); yb = bf16 dY, wt = bf16
     // W^T (N, K padded)
     auto dgrad = [&](float* dx, const float* dy, const uint16_t* yb, int K, const float* w, const uint16_t* wt, int N,
-                     const float* gelu_pre) {
+                     const float* gelu_pre, uint16_t* xb = nullptr, float* xsum = nullptr) {
         if (bf) return gemm_bf16(gelu_pre ? BF16_GELU_BWD : BF16_STORE, dx, N, yb, K, wt, (long)pad64(K), BT, N, K,
-                                 nullptr, gelu_pre, N, nullptr, part, st);
+                                 nullptr, gelu_pre, N, nullptr, part, st, nullptr, xb, N, xsum);
         return linear_dgrad(dx, dy, K, w, gelu_pre, BT, N, K, part, st);
     };
     uint16_t* dresb = bf ? BS(g, BS_DRES) : nullptr;
@@ -555,13 +558,14 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
                         A(g, GPT2_ACT_FCH_GELU, l), bf ? BA(g, BA_FCHG, l) : nullptr, 4 * C));
         HIPCHK(g, mark(EV_W_FCPROJ, sw));
         if (later) HIPCHK(g, after(st, EV_W_FC));  // the fc wgrad above still reads dfch
+        // (mixed precision: the GELU-backward epilogue also writes dfch's bf16 copy and the
+        // fc bias gradient's column sums per 16-row slice)
         HIPCHK(g, dgrad(dfch, dres, dresb, C, P(g, P_FCPROJW) + (size_t)l * 4 * C * C, BA(g, BWT_P, l), 4 * C,
-                        A(g, GPT2_ACT_FCH, l)));
+                        A(g, GPT2_ACT_FCH, l), dfchb, bf ? bpart(1) : nullptr));
         // MLP expansion: fch = ln2 . Wf^T + bf.
-        if (bf) HIPCHK(g, grad_copies(dfch, 4 * C, dfchb, 1));
         HIPCHK(g, mark(EV_DFCH, st));
         HIPCHK(g, after(sw, EV_DFCH));
-        if (bf) HIPCHK(g, bias_w(G(g, P_FCB) + l * 4 * C, 4 * C, 1));
+        if (bf) HIPCHK(g, bias_reduce_parts(G(g, P_FCB) + l * 4 * C, bpart(1), (BT + 15) / 16, 4 * C, sw));
         HIPCHK(g, wgrad(G(g, P_FCW) + (size_t)l * 4 * C * C, G(g, P_FCB) + l * 4 * C, dfch, dfchb, 4 * C,
                         A(g, GPT2_ACT_LN2, l), bf ? BA(g, BA_LN2, l) : nullptr, C));
         HIPCHK(g, mark(EV_W_FC, sw));

@@ -55,11 +55,13 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
 //   BF16_GELU_BWD: C = . * gelu'(aux).   aux has leading dimension ldaux, pre ldc.
 enum { BF16_STORE = 0, BF16_BIAS, BF16_BIAS_RESID, BF16_BIAS_GELU, BF16_ACCUM, BF16_GELU_BWD };
 // lse_part with BF16_STORE: the log-sum-exp partials as linear_forward's.  cb with
-// BF16_BIAS_GELU: the bf16 rounding of C as well (leading dimension ldcb; N, ldcb even,
-// cb 4-byte aligned).
+// BF16_BIAS_GELU or BF16_GELU_BWD: the bf16 rounding of C as well (leading dimension ldcb;
+// N, ldcb even, cb 4-byte aligned).  csum with BF16_GELU_BWD: the column sums of C per
+// 16-row slice, ceil(M/16) rows of N floats (bias_reduce_parts adds them).
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,
                      int N, int K, const float* bias, const float* aux, long ldaux, float* pre, float* partial,
-                     hipStream_t st, float* lse_part = nullptr, uint16_t* cb = nullptr, long ldcb = 0);
+                     hipStream_t st, float* lse_part = nullptr, uint16_t* cb = nullptr, long ldcb = 0,
+                     float* csum = nullptr);
 // C[M,N] += sum over k of A[k,m] B[k,n] with bfloat16 A, B stored row-contiguous, as
 // [K][lda] and [K][ldb] (the weight gradients dW += dY^T X on the straight copies of dY and
 // X): lda >= M, ldb >= N, both multiples of 8; 16-byte aligned; the elements of a row past
