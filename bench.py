@@ -10,7 +10,10 @@ gpt2_backward followed by gpt2_update; it starts each layer's update as soon as 
 layer's gradients are final).  Prints ONE JSON line.  Besides throughput it reports
 the roofline position of the kernel that takes the most time (measured with HIP events
 around each of its launches, on the stream that launch runs on, over the timed region;
-plus the same kernel in a single-stream step) and the CPU oracle timed on a bounded
+plus the same kernel in a single-stream step), the aggregate matrix-core and HBM
+fractions of the kernel classes, the chip's measured ceilings at its running clock
+(matrix-core and copy probes), the standalone LayerNorm workload (8192 x 768) over
+rotating buffers larger than the last-level cache, and the CPU oracle timed on a bounded
 sample of the same workload.
 """
 from __future__ import annotations
@@ -28,14 +31,42 @@ sys.path.insert(0, ROOT)
 
 from scratch_transformer_lm_amd import synthetic as S  # noqa: E402
 
+
+def progress(msg: str) -> None:
+    """A progress line on stderr (stdout carries only the JSON result)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
 PEAK_FP32_MFMA = 157.3e12
 PEAK_BF16_MFMA = 2.5e15  # dense
 PEAK_HBM = 8.0e12
 
 
 def mfma_peak(name: str) -> float:
-    """Matrix-core peak of a kernel's arithmetic: bf16 for the mixed-precision GEMM."""
-    return PEAK_BF16_MFMA if name.startswith("gemm_bf16_kernel") else PEAK_FP32_MFMA
+    """Matrix-core peak of a kernel's operand type: the mixed-precision kernels (GEMMs and
+    attention, every name with _bf16) multiply bf16, every other kernel fp32."""
+    return PEAK_BF16_MFMA if "_bf16" in name else PEAK_FP32_MFMA
+
+
+def aggregates(kernels):
+    """Aggregate fractions over one step's kernels: the GEMMs' and the attention kernels'
+    summed algorithmic flops over their summed time against the matrix-core peak of their
+    type, and the memory-bound kernels' summed algorithmic bytes over their summed time
+    against HBM."""
+    def frac_mfma(ks):
+        if not ks:
+            return None
+        fl = sum(k["flops"] for k in ks)
+        ms = sum(k["ms"] for k in ks)
+        peak = mfma_peak(ks[0]["name"])
+        return dict(kernels=len(ks), ms=ms, tflops=fl / (ms / 1e3) / 1e12, frac=fl / (ms / 1e3) / peak)
+    gemm = [k for k in kernels if k["flops"] > 0 and k["name"].startswith("gemm")]
+    attn = [k for k in kernels if k["flops"] > 0 and k["name"].startswith("attn")]
+    mem = [k for k in kernels if k["flops"] == 0 and k["bytes"] > 0]
+    ms_mem = sum(k["ms"] for k in mem)
+    by = sum(k["bytes"] for k in mem)
+    return dict(gemm=frac_mfma(gemm), attention=frac_mfma(attn),
+                memory=dict(kernels=len(mem), ms=ms_mem, gbps=by / (ms_mem / 1e3) / 1e9,
+                            frac=by / (ms_mem / 1e3) / PEAK_HBM) if mem else None)
 
 
 def step_flops(m: S.ModelShape, B: int, T: int) -> float:
@@ -112,25 +143,204 @@ def recorded_traffic(kernel: str):
     return float(rec["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w: S.Workload, rows: int = 1):
-    """The oracle (float64, as it stands) on a bounded sample: `rows` sequences of the
-    workload, one full step (forward, zero_grad, backward, AdamW)."""
+def physical_cores() -> int:
+    """Physical cores of the host (distinct core/socket pairs lscpu lists)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu", "-p=CORE,SOCKET"], capture_output=True, text=True, check=True).stdout
+        pairs = {l for l in out.splitlines() if l and not l.startswith("#")}
+        return len(pairs) or (os.cpu_count() or 1)
+    except (OSError, subprocess.CalledProcessError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w: S.Workload, timed: int = 2):
+    """The oracle as it stands, float32, built for this host (-march=native), on a bounded
+    sample of the workload: one of its B sequences (1/B of the batch, T tokens), one
+    warm-up step and `timed` timed full steps (forward, zero_grad, backward, AdamW) with
+    as many threads as the host has physical cores available to this process, then one
+    timed step at 8 threads (the pages' OMP_NUM_THREADS=8)."""
+    from oracle import build as OB
     from oracle import oracle as O
+    OB.build_native("f32")
+    prec = "f32_native"
     params = S.init_params(w.model)
     x, y = S.tokens(w)
-    x, y = x[:rows], y[:rows]
-    m = O.OracleGPT2(w.model, rows, w.T, params)
-    t0 = time.perf_counter()
-    m.forward(x, y)
-    m.zero_grad()
-    m.backward()
-    m.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1)
-    dt = time.perf_counter() - t0
-    threads = O.load().oracle_get_threads()
+    x, y = x[:1], y[:1]
+    phys = physical_cores()
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    env = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(phys, avail, env) if env > 0 else min(phys, avail)
+    m = O.OracleGPT2(w.model, 1, w.T, params, prec)
+
+    def one(t):
+        t0 = time.perf_counter()
+        m.forward(x, y)
+        m.zero_grad()
+        m.backward()
+        m.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
+        return time.perf_counter() - t0
+
+    O.set_threads(threads, prec)
+    warm = one(1)
+    times = [one(2 + i) for i in range(timed)]
+    O.set_threads(8, prec)
+    t8 = one(2 + timed)
+    used = O.load(prec).oracle_get_threads()
+    O.set_threads(threads, prec)
     m.close()
-    return dict(value=rows * w.T / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{rows} sequence(s) of {w.T} tokens of the same workload, one full step "
-                       f"(forward, zero_grad, backward, AdamW) in float64, {dt:.1f} s")
+    med = float(np.median(times))
+    flops = step_flops(w.model, 1, w.T)
+    return dict(value=w.T / med, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"1 of the {w.B} sequences ({w.T} tokens, 1/{w.B} of the batch) of the same workload; "
+                       f"float32 oracle built -march=native; 1 warm-up step ({warm:.1f} s) then {timed} timed "
+                       f"full steps (forward, zero_grad, backward, AdamW), median {med:.2f} s",
+                host_physical_cores=phys, cpus_available=avail, threads=threads,
+                tflops=flops / med / 1e12, step_s=[round(v, 3) for v in times],
+                omp8=dict(threads=used, step_s=round(t8, 3), tokens_per_s=w.T / t8),
+                pages_context="the pages' plain C step on an Apple M3 Max with OMP_NUM_THREADS=8: 1.29-1.45 s "
+                              "per step of 256 tokens (GPT-2 124M, B=4, T=64), about 176-199 tokens/s")
+
+
+def layernorm_standalone(G, torch, rounds: int = 5, sets: int = 8):
+    """The standalone LayerNorm workload (8192 x 768, eps 1e-5) through the C ABI, over
+    `sets` rotating buffer sets (x, dy, y, dx: 100 MB each, 805 MB in all, beyond the
+    last-level cache), each call timed with HIP events on the stream it runs on."""
+    N, C = S.LAYERNORM_ROWS, S.LAYERNORM_C
+    x, gw, gb, dy = S.layernorm_inputs()
+    st = torch.cuda.current_stream()
+    bufs = []
+    for i in range(sets):
+        tx = torch.from_numpy(x).cuda().roll(i, 0).contiguous()
+        bufs.append(dict(x=tx, dy=torch.from_numpy(dy).cuda().roll(i, 0).contiguous(),
+                         y=torch.empty_like(tx), dx=torch.empty_like(tx),
+                         mean=torch.empty(N, device="cuda"), rstd=torch.empty(N, device="cuda")))
+    tw, tb = torch.from_numpy(gw).cuda(), torch.from_numpy(gb).cuda()
+    dw, db = torch.empty_like(tw), torch.empty_like(tb)
+    ws = torch.empty(max(1, G.layernorm_backward_workspace(N, C)), device="cuda")
+    fwd, bwd = [], []
+    for r in range(rounds + 1):
+        for b in bufs:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(st)
+            G.layernorm_forward(b["y"], b["mean"], b["rstd"], b["x"], tw, tb, 1e-5, stream=st)
+            e[1].record(st)
+            G.layernorm_backward(b["dx"], dw, db, b["dy"], b["x"], tw, b["mean"], b["rstd"], ws, stream=st)
+            e[2].record(st)
+            if r:
+                fwd.append(e[:2])
+                bwd.append(e[1:])
+    torch.cuda.synchronize()
+    tf = float(np.median([a.elapsed_time(b) for a, b in fwd])) / 1e3
+    tbw = float(np.median([a.elapsed_time(b) for a, b in bwd])) / 1e3
+    # algorithmic bytes: forward reads x, writes y, mean and rstd (and reads w, b);
+    # backward reads dy, x, mean, rstd (and w), writes dx, dw and db
+    bf = 4.0 * (2 * N * C + 2 * N + 2 * C)
+    bb = 4.0 * (3 * N * C + 2 * N + 3 * C)
+    return dict(shape=[N, C], buffer_sets=sets, bytes_all_sets=sets * 4 * 4 * N * C,
+                forward=dict(us=tf * 1e6, gbps=bf / tf / 1e9, frac_hbm=bf / tf / PEAK_HBM),
+                backward=dict(us=tbw * 1e6, gbps=bb / tbw / 1e9, frac_hbm=bb / tbw / PEAK_HBM,
+                              note="both kernels of the call (per-row pass and the dgamma/dbeta reduction)"))
+
+
+def ceilings(G, torch):
+    """The chip's ceilings at its running clock: matrix-core probes (fp32 16x16x4 and
+    bf16 16x16x32 products in registers, no memory traffic) and a 1 GiB float4 copy."""
+    st = torch.cuda.current_stream()
+    out = torch.empty(G.probe_mfma_out_floats(), device="cuda")
+    res = {}
+    for kind, name, peak, iters in ((0, "fp32_mfma", PEAK_FP32_MFMA, 6000), (1, "bf16_mfma", PEAK_BF16_MFMA, 3000)):
+        best = None
+        for blocks in (512, 1024):  # two or four waves per SIMD
+            G.probe_mfma(kind, 100, out, blocks=blocks, stream=st)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fl = G.probe_mfma(kind, iters * 1024 // blocks, out, blocks=blocks, stream=st)
+            e1.record(st)
+            torch.cuda.synchronize()
+            s = e0.elapsed_time(e1) / 1e3
+            if best is None or fl / s > best[0]:
+                best = (fl / s, blocks)
+        res[name] = dict(tflops=best[0] / 1e12, frac_of_datasheet=best[0] / peak, waves_per_simd=best[1] // 256)
+    n = (1 << 30) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    G.probe_copy(dst, src, stream=st)
+    ts = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        G.probe_copy(dst, src, stream=st)
+        e1.record(st)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    s = min(a.elapsed_time(b) for a, b in ts) / 1e3
+    res["copy_1gib"] = dict(gbps=2.0 * 4 * n / s / 1e9, frac_of_datasheet=2.0 * 4 * n / s / PEAK_HBM)
+    del src, dst
+    res["note"] = "fractions elsewhere in this line use the datasheet peaks (fp32 157.3 TFLOP/s, bf16 2.5 PFLOP/s, HBM 8 TB/s)"
+    return res
+
+
+def variant_leg(G, torch, w, stream, params, tx, ty, variant, steps=5):
+    """A second model of the same shape in another variant, from the same parameters:
+    2 warm-up steps (the second with events on every kernel), `steps` timed steps."""
+    vm = G.GPT2(w.model, w.B, w.T, stream=stream, variant=variant)
+    vm.params.copy_(params)
+    tv = 0
+
+    def vstep():
+        nonlocal tv
+        tv += 1
+        loss = vm.forward(tx, ty)
+        vm.zero_grad()
+        vm.backward_update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, tv)
+        return loss
+
+    vstep()
+    vm.profile_enable(True)
+    vstep()
+    torch.cuda.synchronize()
+    kernels = vm.profile_entries()
+    vm.profile_enable(False)
+    t0 = time.perf_counter()
+    losses = [vstep() for _ in range(steps)]
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    err = vm.last_error()
+    vm.close()
+    if err != 0 or not all(np.isfinite(losses)):
+        print(f"bench: variant {variant} step failed: {G.strerror(err)}, losses {losses}", file=sys.stderr)
+        sys.exit(1)
+    return kernels, dt, losses
+
+
+def generation_leg(model, w, torch):
+    """Forward-only generation with the model's current weights (the pages' sample loop):
+    64 new tokens from the end-of-text token, one fixed coin per token, each step
+    recomputing the whole prefix; the sampling kernel timed with events."""
+    gen_new = 64
+    coins = np.random.default_rng(7).random(gen_new).astype(np.float32)
+    eot = w.model.vocab_size - 1
+    model.profile_enable(True)
+    model.profile_filter("sample_kernel")
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    gen = model.generate([eot], gen_new + 1, coins)
+    torch.cuda.synchronize()
+    dt_gen = time.perf_counter() - t2
+    sk = [e for e in model.profile_entries() if e["name"] == "sample_kernel"]
+    model.profile_enable(False)
+    return {
+        "new_tokens": gen_new, "prompt": [eot], "tokens_per_s": gen_new / dt_gen,
+        "ms_per_token": dt_gen * 1e3 / gen_new, "batch": 1,
+        "method": "forward over the whole prefix per token (no key/value cache), then sample_mult on the "
+                  "last position; coins from numpy default_rng(7)",
+        "sample_kernel_us": sk[0]["ms"] * 1e3 / sk[0]["launches"] if sk else None,
+        "first_tokens": [int(v) for v in gen[:9]],
+    }
 
 
 def main():
@@ -140,6 +350,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=S.GPT2_124M.name)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the training step (for profiler runs): no generation, variants, standalone "
+                         "LayerNorm, ceilings or CPU baseline")
+    ap.add_argument("--variant", choices=("fp32", "bf16"), default="fp32",
+                    help="variant of the timed step (bf16: the mixed-precision model; for profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain device copy of MIB MiB three times "
                          "(a kernel of known traffic for scaling hardware byte counters)")
@@ -153,7 +368,8 @@ def main():
     w = S.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    model = G.GPT2(w.model, w.B, w.T, stream=stream)
+    main_variant = G.VARIANT_BF16 if args.variant == "bf16" else 0
+    model = G.GPT2(w.model, w.B, w.T, stream=stream, variant=main_variant)
     model.params.copy_(torch.from_numpy(S.init_params(w.model)).cuda())
     x, y = S.tokens(w)
     tx = torch.from_numpy(x).cuda()
@@ -170,6 +386,7 @@ def main():
         model.backward_update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
         return loss
 
+    progress(f"{w.name}: warm-up")
     # Warm-up; all but the first warm-up step carry events around every kernel, which
     # gives the per-kernel breakdown and names the kernel that takes the most time.
     step()
@@ -180,14 +397,22 @@ def main():
     all_kernels = model.profile_entries()
     dominant = max(all_kernels, key=lambda e: e["ms"])["name"]
     # The timed region: K steps, with HIP events around each launch of the dominant kernel
-    # only, recorded on the stream that launch runs on.
+    # only, recorded on the stream that launch runs on; one event pair per step on the
+    # model's stream gives each step's time (median and spread).
+    progress(f"timed steps ({args.steps})")
     model.profile_enable(True)
     model.profile_filter(dominant)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    losses = [step() for _ in range(args.steps)]
+    losses = []
+    for i in range(args.steps):
+        step_ev[i].record(stream)
+        losses.append(step())
+    step_ev[-1].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in zip(step_ev[:-1], step_ev[1:])]
     kernels = model.profile_entries()
     model.profile_enable(False)
     # The same K steps without any events, to show what the events cost.
@@ -206,80 +431,6 @@ def main():
     isolated = model.profile_entries()
     model.profile_enable(False)
     model.set_backward_streams(2)
-    # Forward-only generation with the trained-for-K-steps weights (the pages' sample
-    # loop): 64 new tokens from the end-of-text token, one fixed coin per token, each
-    # step recomputing the whole prefix; the sampling kernel timed with events.
-    gen_new = 64
-    coins = np.random.default_rng(7).random(gen_new).astype(np.float32)
-    eot = w.model.vocab_size - 1
-    model.profile_enable(True)
-    model.profile_filter("sample_kernel")
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    gen = model.generate([eot], gen_new + 1, coins)
-    torch.cuda.synchronize()
-    dt_gen = time.perf_counter() - t2
-    sk = [e for e in model.profile_entries() if e["name"] == "sample_kernel"]
-    model.profile_enable(False)
-    # The Llama-style variant (RMSNorm + rotary positions) at the same shape: a second
-    # model, 2 warm-up steps (the second with events on every kernel), 5 timed steps.
-    vm = G.GPT2(w.model, w.B, w.T, stream=stream, variant=G.VARIANT_RMSNORM | G.VARIANT_ROPE)
-    vm.params.copy_(model.params)
-    tv = 0
-
-    def vstep():
-        nonlocal tv
-        tv += 1
-        loss = vm.forward(tx, ty)
-        vm.zero_grad()
-        vm.backward_update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, tv)
-        return loss
-
-    vstep()
-    vm.profile_enable(True)
-    vstep()
-    torch.cuda.synchronize()
-    vkernels = vm.profile_entries()
-    vm.profile_enable(False)
-    t3 = time.perf_counter()
-    vlosses = [vstep() for _ in range(5)]
-    torch.cuda.synchronize()
-    dt_var = (time.perf_counter() - t3) / 5
-    verr = vm.last_error()
-    vm.close()
-    if verr != 0 or not all(np.isfinite(vlosses)):
-        print(f"bench: variant step failed: {G.strerror(verr)}, losses {vlosses}", file=sys.stderr)
-        sys.exit(1)
-    # Mixed precision (bf16 matmul operands; fp32 master weights, AdamW and every other
-    # operation) at the same shape: 2 warm-up steps (the second with events on every
-    # kernel), 5 timed steps.
-    bm = G.GPT2(w.model, w.B, w.T, stream=stream, variant=G.VARIANT_BF16)
-    bm.params.copy_(model.params)
-    tb = 0
-
-    def bstep():
-        nonlocal tb
-        tb += 1
-        loss = bm.forward(tx, ty)
-        bm.zero_grad()
-        bm.backward_update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, tb)
-        return loss
-
-    bstep()
-    bm.profile_enable(True)
-    bstep()
-    torch.cuda.synchronize()
-    bkernels = bm.profile_entries()
-    bm.profile_enable(False)
-    t4 = time.perf_counter()
-    blosses = [bstep() for _ in range(5)]
-    torch.cuda.synchronize()
-    dt_bf = (time.perf_counter() - t4) / 5
-    berr = bm.last_error()
-    bm.close()
-    if berr != 0 or not all(np.isfinite(blosses)):
-        print(f"bench: mixed-precision step failed: {G.strerror(berr)}, losses {blosses}", file=sys.stderr)
-        sys.exit(1)
     if model.last_error() != 0 or not all(np.isfinite(losses)):
         print(f"bench: step failed: {G.strerror(model.last_error())}, losses {losses}", file=sys.stderr)
         sys.exit(1)
@@ -298,7 +449,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if not main_variant else "bf16 matmul operands, f32 otherwise",
         "data": "synthetic (Zipf(1.1) int32 tokens with separator 50256 every 256; N(0,0.02) init)",
         "config": {"workload": w.name, "global_batch": w.B, "seq_len": w.T,
                    "layers": w.model.num_layers, "channels": w.model.channels,
@@ -308,6 +459,9 @@ def main():
         "step_roofline_frac": flops / PEAK_FP32_MFMA / (dt / args.steps),
         "loss_first_last": [losses[0], losses[-1]],
     }
+    out["ms_per_step_median"] = float(np.median(step_ms))
+    out["tokens_per_s_at_median"] = tokens / (out["ms_per_step_median"] / 1e3)
+    out["ms_per_step_min_max"] = [min(step_ms), max(step_ms)]
     out["ms_per_step_without_events"] = dt_plain * 1e3 / args.steps
     out["roofline"] = roofline(kernels)
     # The same kernel measured alone (single-stream step): in the timed schedule its
@@ -319,44 +473,58 @@ def main():
     out["roofline"]["schedule"] = ("timed steps overlap each layer's weight-gradient GEMMs (second stream) "
                                    "with the dgrad/attention/LayerNorm chain; 'isolated' is one "
                                    "single-stream step")
-    out["generation"] = {
-        "new_tokens": gen_new, "prompt": [eot], "tokens_per_s": gen_new / dt_gen,
-        "ms_per_token": dt_gen * 1e3 / gen_new, "batch": 1,
-        "method": "forward over the whole prefix per token (no key/value cache), then sample_mult on the "
-                  "last position; coins from numpy default_rng(7)",
-        "sample_kernel_us": sk[0]["ms"] * 1e3 / sk[0]["launches"] if sk else None,
-        "first_tokens": [int(v) for v in gen[:9]],
-    }
-    vb = {k["name"]: k for k in breakdown(vkernels, 1)}
-    out["variant_rmsnorm_rope"] = {
-        "tokens_per_s": tokens / dt_var, "ms_per_step": dt_var * 1e3, "steps": 5,
-        "what": "every LayerNorm replaced by RMSNorm, rotary q/k positions instead of wpe; same shape and step",
-        "kernels": {n: vb[n] for n in ("rope_kernel<1>", "rope_kernel<-1>", "rms_fwd_kernel", "rms_bwd_kernel")
-                    if n in vb},
-    }
-    bf_gemms = [k for k in bkernels if k["name"].startswith("gemm_bf16_kernel")]
-    out["mixed_precision_bf16"] = {
-        "tokens_per_s": tokens / dt_bf, "ms_per_step": dt_bf * 1e3, "steps": 5,
-        "loss_first_last": [blosses[0], blosses[-1]],
-        "what": "every linear layer and the LM head multiply bf16 roundings of their operands on the bf16 "
-                "matrix cores (fp32 sums); fp32 master weights, AdamW, LayerNorm, attention, softmax/CE",
-        "roofline_bf16_gemm": roofline(bf_gemms) if bf_gemms else None,
-        "kernels": breakdown(bkernels, 1)[:16],
-    }
     out["kernels"] = breakdown(all_kernels, max(1, args.warmup - 1))
     out["kernels_isolated"] = breakdown(isolated, 1)
+    # Aggregate fractions from the single-stream step, where kernel times do not overlap.
+    out["aggregates_isolated"] = aggregates(isolated)
+    out["aggregates_isolated"]["note"] = ("GEMM and attention: summed algorithmic flops over summed kernel "
+                                          "time vs the matrix-core peak of their type; memory: summed "
+                                          "algorithmic bytes of the memory-bound kernels over their summed "
+                                          "time vs 8 TB/s")
     traffic = recorded_traffic(out["roofline"]["kernel"])
     if traffic is not None:
         out["roofline"]["traffic"] = traffic
+    if not args.step_only:
+        progress("generation")
+        out["generation"] = generation_leg(model, w, torch)
+        if not main_variant:
+            progress("RMSNorm + RoPE variant")
+            vkernels, dt_var, _ = variant_leg(G, torch, w, stream, model.params, tx, ty,
+                                              G.VARIANT_RMSNORM | G.VARIANT_ROPE)
+            vb = {k["name"]: k for k in breakdown(vkernels, 1)}
+            out["variant_rmsnorm_rope"] = {
+                "tokens_per_s": tokens / dt_var, "ms_per_step": dt_var * 1e3, "steps": 5,
+                "what": "every LayerNorm replaced by RMSNorm, rotary q/k positions instead of wpe; same shape "
+                        "and step",
+                "kernels": {n: vb[n] for n in ("rope_kernel<1>", "rope_kernel<-1>", "rms_fwd_kernel",
+                                               "rms_bwd_kernel") if n in vb},
+            }
+            progress("mixed-precision variant")
+            bkernels, dt_bf, blosses = variant_leg(G, torch, w, stream, model.params, tx, ty, G.VARIANT_BF16)
+            bf_gemms = [k for k in bkernels if k["name"].startswith("gemm_bf16")]
+            out["mixed_precision_bf16"] = {
+                "tokens_per_s": tokens / dt_bf, "ms_per_step": dt_bf * 1e3, "steps": 5,
+                "loss_first_last": [blosses[0], blosses[-1]],
+                "what": "every linear layer and the LM head multiply bf16 roundings of their operands on the "
+                        "bf16 matrix cores (fp32 sums); fp32 master weights, AdamW, LayerNorm, attention, "
+                        "softmax/CE",
+                "roofline_bf16_gemm": roofline(bf_gemms) if bf_gemms else None,
+                "aggregates": aggregates(bkernels),
+                "kernels": breakdown(bkernels, 1)[:16],
+            }
+        progress("standalone LayerNorm and ceilings")
+        out["layernorm_standalone"] = layernorm_standalone(G, torch)
+        out["ceilings"] = ceilings(G, torch)
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            G.probe_copy(dst, src, stream=stream)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = 2 * 4 * n
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.step_only:
+        progress("CPU baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

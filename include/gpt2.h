@@ -127,7 +127,10 @@ int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const g
 
 /* Forward pass (huxiu page 核心代码解读 item 3: outputs and loss).  inputs and targets
  * are device pointers to B*T int32 token ids, row-major (B,T); ids must lie in
- * [0, vocab_size).  Requires 1 <= T <= max_seq_len and B*T <= the built B*T.
+ * [0, vocab_size).  Requires 1 <= T <= max_seq_len and B*T <= the built B*T; a model
+ * built with GPT2_VARIANT_BF16 also requires B*ceil64(T) <= B0*ceil64(T0), where (B0, T0)
+ * is the built shape and ceil64 rounds up to a multiple of 64 (its per-head attention
+ * copies are sized in whole 64-position tiles).
  * Returns the mean cross-entropy over the B*T positions.  With targets == NULL the
  * logits and each row's log-sum-exp (which gives the softmax) are computed and -1.0f is
  * returned.  Synchronises the
@@ -135,13 +138,16 @@ int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const g
  * device, GPT2_EDEVICE for a HIP failure). */
 float gpt2_forward(gpt2* model, const int32_t* inputs, const int32_t* targets, int B, int T);
 
-/* Zero the parameter gradients (activation gradients are scratch that each backward
- * rewrites, so there is nothing else to clear).  Enqueue only. */
+/* Zero the gradients (huxiu page 核心代码解读 item 3: zero_grad clears the gradients of
+ * the parameters and of the activations).  Here the activation gradients are scratch
+ * that each backward rewrites, so only the parameter gradients need clearing.  Enqueue
+ * only. */
 int gpt2_zero_grad(gpt2* model);
 
-/* Backward pass of the last forward (which must have had targets, else GPT2_ESTATE).
- * ADDS into grads: two calls without gpt2_zero_grad give twice the gradients.
- * Enqueue only. */
+/* Backward pass of the last forward (huxiu page 核心代码解读 item 3: the hand-derived
+ * backward of every layer, from the loss back to the embeddings), which must have had
+ * targets, else GPT2_ESTATE.  ADDS into grads: two calls without gpt2_zero_grad give
+ * twice the gradients.  Enqueue only. */
 int gpt2_backward(gpt2* model);
 
 /* AdamW over the whole flat buffer (huxiu page 核心代码解读 item 3; lr 1e-4 on the
@@ -154,8 +160,9 @@ int gpt2_update(gpt2* model, float lr, float beta1, float beta2, float eps, floa
 /* gpt2_backward followed by gpt2_update(lr, beta1, beta2, eps, weight_decay, t) in one
  * call, bitwise the same result: every parameter gets the same elementwise AdamW.  Each
  * layer's parameters are updated as soon as its gradients are final (after its
- * LayerNorm backward and weight-gradient GEMMs), on the second backward stream, while the
- * gradients of the layers below are still being formed; wte, wpe and the final norm are
+ * LayerNorm backward and weight-gradient GEMMs), on a third stream the handle owns (the
+ * update stream, next to the main and weight-gradient streams), while the gradients of
+ * the layers below are still being formed; wte, wpe and the final norm are
  * updated last.  Gradients are left in `grads` as gpt2_backward leaves them.
  * Returns GPT2_OK, GPT2_EINVAL for a null model, GPT2_ESTATE without a forward with
  * targets or with t < 1, GPT2_EDEVICE on a HIP error. */
@@ -284,6 +291,23 @@ size_t gpt2_layernorm_backward_workspace(int N, int C);
 int gpt2_layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x,
                             const float* w, const float* mean, const float* rstd, int N, int C,
                             float* workspace, size_t workspace_floats, void* stream);
+
+/* Measurement probes, not part of the training step: the chip's ceilings at its running
+ * clock, which the benchmark reports beside the datasheet peaks (the pages only print
+ * whole-step times, so these are aids of the measurement, not of the method).
+ * gpt2_probe_mfma: one launch of `blocks` (1..4096) blocks of 256 threads, each wave
+ * running `iters` rounds of 16 independent matrix-core products held in registers, with
+ * no memory traffic: kind 0 = fp32 16x16x4, kind 1 = bf16 16x16x32 (the shapes the
+ * step's kernels use).  `out` is a device buffer of gpt2_probe_mfma_out_floats() floats
+ * that receives one value per thread (so nothing is optimised away); *flops (host)
+ * receives the flops the launch executes.
+ * gpt2_probe_copy: dst[i] = src[i] for n floats (n a multiple of 4, 16-byte aligned
+ * device buffers that do not overlap), float4 loads and stores.
+ * Both enqueue on `stream` only; GPT2_EINVAL for bad arguments, GPT2_EDEVICE if the
+ * launch fails. */
+size_t gpt2_probe_mfma_out_floats(void);
+int gpt2_probe_mfma(int kind, int iters, int blocks, float* out, double* flops, void* stream);
+int gpt2_probe_copy(float* dst, const float* src, size_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,20 @@ def lib_path(precision: str) -> str:
     return os.path.join(HERE, f"liboracle_{precision}.so")
 
 
+def build_native(precision: str = "f32", verbose: bool = False) -> str:
+    """The same source built for the host it runs on (-march=native instead of the
+    portable x86-64-v3), as liboracle_<precision>_native.so: the benchmark's CPU
+    baseline times this build on the machine that runs the GPU."""
+    out = lib_path(precision + "_native")
+    flags = [f for f in FLAGS if not f.startswith("-march=")] + ["-march=native"]
+    cmd = ["gcc", *flags, *TARGETS[precision], SRC, "-o", out + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(verbose: bool = False) -> None:
     procs = []
     for prec, extra in TARGETS.items():

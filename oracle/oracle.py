@@ -36,9 +36,12 @@ def load(precision: str = "f64") -> ct.CDLL:
         return _LIBS[precision]
     path = _build.lib_path(precision)
     if not os.path.exists(path):
-        _build.build()
+        if precision.endswith("_native"):
+            _build.build_native(precision[:-len("_native")])
+        else:
+            _build.build()
     lib = ct.CDLL(path)
-    real = ct.c_double if precision == "f64" else ct.c_float
+    real = ct.c_double if precision.startswith("f64") else ct.c_float
     P = ct.c_void_p
     sz = ct.c_size_t
     i = ct.c_int
@@ -97,7 +100,8 @@ def load(precision: str = "f64") -> ct.CDLL:
 
 
 def dtype_of(precision: str):
-    return np.float64 if precision == "f64" else np.float32
+    """f64, f32 (portable builds) or f32_native / f64_native (built for the host)."""
+    return np.float64 if precision.startswith("f64") else np.float32
 
 
 def _ptr(a: np.ndarray | None):
@@ -206,7 +210,7 @@ class OracleGPT2:
         p = self.lib.oracle_gpt2_activation(self.h, aid, layer, int(grad), ct.byref(cnt))
         if not p:
             raise ValueError(f"no activation {name}[{layer}]")
-        buf = (ct.c_double if self.precision == "f64" else ct.c_float) * cnt.value
+        buf = (ct.c_double if self.precision.startswith("f64") else ct.c_float) * cnt.value
         return np.frombuffer(buf.from_address(p), dtype=self.dtype).copy()
 
 

@@ -1054,7 +1054,12 @@ const char* splitk_fixup_name() {
 
 // Work distribution over a persistent grid of up to RESIDENT blocks: whole-tile rounds
 // while at least RESIDENT tiles remain, then equal ranges of the rest.
-void schedule(Params& p, long tiles, int split) {
+// The fp32 weight gradients run on their own stream next to the main backward chain; a
+// persistent grid of fewer blocks than the chip holds leaves CU slots to that chain.
+#ifndef GEMM_WGRAD_RESIDENT
+#define GEMM_WGRAD_RESIDENT RESIDENT
+#endif
+void schedule(Params& p, long tiles, int split, int resident = RESIDENT) {
     p.R = 0;
     p.tile0 = 0;
     p.S = 0;
@@ -1077,19 +1082,19 @@ void schedule(Params& p, long tiles, int split) {
         p.nr = 0;
         return;
     }
-    if (tiles >= RESIDENT) {
-        p.G = RESIDENT;
-        p.R = (int)(tiles / RESIDENT);
-        p.tile0 = p.R * RESIDENT;
+    if (tiles >= resident) {
+        p.G = resident;
+        p.R = (int)(tiles / resident);
+        p.tile0 = p.R * resident;
     }
     p.skt = (int)(tiles - p.tile0);
     p.total = (long)p.skt * p.nk;
-    p.nr = (int)std::min<long>(RESIDENT, p.total);
+    p.nr = (int)std::min<long>(resident, p.total);
     if (p.R == 0) p.G = p.nr;
 }
 
 template <bool A_K, bool B_K, int EPI, bool XF, int BN, bool BF = false>
-hipError_t launch(Params& p, hipStream_t st, int split) {
+hipError_t launch(Params& p, hipStream_t st, int split, int resident = RESIDENT) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
     p.nk = (p.K + KTileOf<A_K, BF, BN>::BK - 1) / KTileOf<A_K, BF, BN>::BK;
@@ -1099,7 +1104,7 @@ hipError_t launch(Params& p, hipStream_t st, int split) {
         // empty reduction: every output is the epilogue of 0
         p.nk = 1;
     }
-    schedule(p, tiles, split);
+    schedule(p, tiles, split, resident);
     const double mn = (double)p.M * p.N;
     const double extra = (EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD || EPI == EPI_BIAS_GELU ||
                           EPI == EPI_DLOGITS) ? mn : 0.0;
@@ -1322,7 +1327,7 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
         p.xlog2s = (float)std::log2((double)xent->scale);
         return launch<false, false, EPI_ACCUM, true, 128>(p, st, 0);
     }
-    return launch<false, false, EPI_ACCUM, false, 128>(p, st, 0);
+    return launch<false, false, EPI_ACCUM, false, 128>(p, st, 0, GEMM_WGRAD_RESIDENT);
 }
 
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,

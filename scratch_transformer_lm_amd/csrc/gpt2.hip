@@ -747,6 +747,13 @@ float gpt2_forward(gpt2* g, const int32_t* inputs, const int32_t* targets, int B
         g->last_error = GPT2_EINVAL;
         return NAN;
     }
+    // The mixed-precision variant's per-head attention copies and their bias partial
+    // sums hold B rows of T positions rounded up to whole 64-position tiles, sized at
+    // build: a batch whose rounded size exceeds the built one would not fit.
+    if (bf_on(g) && (long)B * (long)pad64(T) > (long)g->maxB * (long)pad64(g->maxT)) {
+        g->last_error = GPT2_EINVAL;
+        return NAN;
+    }
     float loss = NAN;
     ProfBind bind(g);
     const int rc = forward_impl(g, inputs, targets, B, T, &loss);

@@ -215,8 +215,9 @@ hipError_t adamw(float* p, const float* g, float* m, float* v, size_t n, float l
 constexpr int ADAM_MAX_SEGS = 16;
 struct AdamSegments {
     int n;
-    size_t off4[ADAM_MAX_SEGS];
-    size_t start4[ADAM_MAX_SEGS + 1];
+    size_t off4[ADAM_MAX_SEGS];    // first float4 of each slice
+    size_t len4[ADAM_MAX_SEGS];    // float4s of each slice
+    size_t start4[ADAM_MAX_SEGS + 1];  // first tile of each slice (tiles of the kernel's width)
 };
 hipError_t adamw_segments(float* p, const float* g, float* m, float* v, const size_t* off, const size_t* len, int n,
                           float lr, float b1, float b2, float eps, float wd, float bc1, float bc2, hipStream_t st);

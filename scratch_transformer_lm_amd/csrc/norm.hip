@@ -20,61 +20,80 @@ namespace gpt2k {
 namespace {
 
 constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
-constexpr int LN_MAX_BLOCKS = 512;
+// The backward's grid is capped: each block leaves one partial [dgamma | dbeta] row.
+#ifndef LN_BWD_MAX_BLOCKS
+#define LN_BWD_MAX_BLOCKS 512
+#endif
+constexpr int LN_MAX_BLOCKS = LN_BWD_MAX_BLOCKS;
 
-template <int VPL, bool RMS>
+// Rows per wave of the forward: a wave loads all of its rows before reducing any, so
+// more bytes are in flight per wave and fewer blocks are dispatched.
+#ifndef LN_FWD_ROWS
+#define LN_FWD_ROWS 1
+#endif
+
+template <int VPL, bool RMS, int RPW>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, uint16_t* __restrict__ yb,
                                                      float* __restrict__ mean,
                                                      float* __restrict__ rstd, const float* __restrict__ x,
                                                      const float* __restrict__ w, const float* __restrict__ b,
                                                      int N, int C, float eps) {
-    const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6)) * RPW;
     const int lane = threadIdx.x & 63;
-    if (row >= N) return;
+    if (row0 >= N) return;
     const int C4 = C >> 2;
-    const float4* xr = reinterpret_cast<const float4*>(x + (long)row * C);
-    float4 v[VPL];
-    float s = 0.f;
+    float4 v[RPW][VPL];
 #pragma unroll
-    for (int j = 0; j < VPL; j++) {
-        const int i = lane + 64 * j;
-        v[j] = i < C4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-    }
-    const float m = RMS ? 0.f : wave_sum(s) / (float)C;
-    float ss = 0.f;
+    for (int q = 0; q < RPW; q++) {
+        const float4* xr = reinterpret_cast<const float4*>(x + (long)(row0 + q) * C);
 #pragma unroll
-    for (int j = 0; j < VPL; j++) {
-        const int i = lane + 64 * j;
-        if (i < C4) {
-            const float a = v[j].x - m, bb = v[j].y - m, c = v[j].z - m, d = v[j].w - m;
-            ss += (a * a + bb * bb) + (c * c + d * d);
+        for (int j = 0; j < VPL; j++) {
+            const int i = lane + 64 * j;
+            v[q][j] = (i < C4 && row0 + q < N) ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
-    const float var = wave_sum(ss) / (float)C;
-    const float r = 1.0f / sqrtf(var + eps);
-    float4* yr = reinterpret_cast<float4*>(y + (long)row * C);
     const float4* w4 = reinterpret_cast<const float4*>(w);
     const float4* b4 = reinterpret_cast<const float4*>(b);
 #pragma unroll
-    for (int j = 0; j < VPL; j++) {
-        const int i = lane + 64 * j;
-        if (i < C4) {
-            const float4 ww = w4[i], bv = RMS ? make_float4(0.f, 0.f, 0.f, 0.f) : b4[i];
-            float4 o;
-            o.x = (v[j].x - m) * r * ww.x + bv.x;
-            o.y = (v[j].y - m) * r * ww.y + bv.y;
-            o.z = (v[j].z - m) * r * ww.z + bv.z;
-            o.w = (v[j].w - m) * r * ww.w + bv.w;
-            yr[i] = o;
-            if (yb)
-                reinterpret_cast<uint2*>(yb + (long)row * C)[i] =
-                    make_uint2(bf16_pack2(o.x, o.y), bf16_pack2(o.z, o.w));
+    for (int q = 0; q < RPW; q++) {
+        const int row = row0 + q;
+        if (row >= N) break;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < VPL; j++) s += (v[q][j].x + v[q][j].y) + (v[q][j].z + v[q][j].w);
+        const float m = RMS ? 0.f : wave_sum(s) / (float)C;
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            const int i = lane + 64 * j;
+            if (i < C4) {
+                const float a = v[q][j].x - m, bb = v[q][j].y - m, c = v[q][j].z - m, d = v[q][j].w - m;
+                ss += (a * a + bb * bb) + (c * c + d * d);
+            }
         }
-    }
-    if (lane == 0) {
-        mean[row] = m;
-        rstd[row] = r;
+        const float var = wave_sum(ss) / (float)C;
+        const float r = 1.0f / sqrtf(var + eps);
+        float4* yr = reinterpret_cast<float4*>(y + (long)row * C);
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            const int i = lane + 64 * j;
+            if (i < C4) {
+                const float4 ww = w4[i], bv = RMS ? make_float4(0.f, 0.f, 0.f, 0.f) : b4[i];
+                float4 o;
+                o.x = (v[q][j].x - m) * r * ww.x + bv.x;
+                o.y = (v[q][j].y - m) * r * ww.y + bv.y;
+                o.z = (v[q][j].z - m) * r * ww.z + bv.z;
+                o.w = (v[q][j].w - m) * r * ww.w + bv.w;
+                yr[i] = o;
+                if (yb)
+                    reinterpret_cast<uint2*>(yb + (long)row * C)[i] =
+                        make_uint2(bf16_pack2(o.x, o.y), bf16_pack2(o.z, o.w));
+            }
+        }
+        if (lane == 0) {
+            mean[row] = m;
+            rstd[row] = r;
+        }
     }
 }
 
@@ -167,20 +186,22 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
     }
 }
 
-// out[w] (+)= sum_r part[r*W + w] over R rows (W % 4 == 0).  A block covers 64 columns as
-// 16 float4 columns x 16 row groups; group j adds rows j, j+16, ... in order, then the 16
+// out[w] (+)= sum_r part[r*W + w] over R rows (W % 4 == 0).  A block covers 16 columns as
+// 4 float4 columns x 64 row groups (so the grid has W/16 blocks: 96 for LayerNorm's
+// [dgamma | dbeta] rows at C = 768); group j adds rows j, j+64, ... in order, then the 64
 // group sums are added in group order.  Columns w < W1 go to out_lo[w], the rest to
 // out_hi[w - W1].
+constexpr int RR_GROUPS = 64;
 __global__ __launch_bounds__(256) void reduce_rows_kernel(float* out_lo, float* out_hi, int W1,
                                                           const float* __restrict__ part, int R, int W,
                                                           int accumulate) {
-    __shared__ float4 s[16][16];
-    const int c4 = threadIdx.x & 15, grp = threadIdx.x >> 4;
-    const int w = blockIdx.x * 64 + c4 * 4;
+    __shared__ float4 s[RR_GROUPS][4];
+    const int c4 = threadIdx.x & 3, grp = threadIdx.x >> 2;
+    const int w = blockIdx.x * 16 + c4 * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (w < W) {
 #pragma unroll 8
-        for (int r = grp; r < R; r += 16) {
+        for (int r = grp; r < R; r += RR_GROUPS) {
             const float4 v = *reinterpret_cast<const float4*>(part + (long)r * W + w);
             acc.x += v.x;
             acc.y += v.y;
@@ -192,7 +213,7 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(float* out_lo, float* 
     __syncthreads();
     if (grp == 0 && w < W) {
         float4 tot = s[0][c4];
-        for (int j = 1; j < 16; j++) {
+        for (int j = 1; j < RR_GROUPS; j++) {
             const float4 v = s[j][c4];
             tot.x += v.x;
             tot.y += v.y;
@@ -220,17 +241,19 @@ hipError_t norm_forward(float* y, float* mean, float* rstd, const float* x, cons
     if (C % 4 || C > 4096 || N < 0 || ((uintptr_t)yb & 7)) return hipErrorInvalidValue;
     if (N == 0) return hipSuccess;
     const int vpl = (C / 4 + 63) / 64;
-    dim3 grid((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), block(256);
+    // several rows per wave only where the rows are short enough to keep in registers
+    const int rpw = vpl <= 4 ? LN_FWD_ROWS : 1;
+    dim3 grid((N + ROWS_PER_BLOCK * rpw - 1) / (ROWS_PER_BLOCK * rpw)), block(256);
     ProfScope ps(st, RMS ? "rms_fwd_kernel" : "ln_fwd_kernel", 0.0,
                  4.0 * ((double)N * C * (yb ? 2.5 : 2.0) + 2.0 * N + (RMS ? 1.0 : 2.0) * C));
-#define LN_FWD(V) hipLaunchKernelGGL((ln_fwd_kernel<V, RMS>), grid, block, 0, st, y, yb, mean, rstd, x, w, b, N, C, eps)
+#define LN_FWD(V, R) hipLaunchKernelGGL((ln_fwd_kernel<V, RMS, R>), grid, block, 0, st, y, yb, mean, rstd, x, w, b, N, C, eps)
     switch (vpl) {
-        case 1: LN_FWD(1); break;
-        case 2: LN_FWD(2); break;
-        case 3: LN_FWD(3); break;
-        case 4: LN_FWD(4); break;
-        case 5: case 6: case 7: case 8: LN_FWD(8); break;
-        default: LN_FWD(16); break;
+        case 1: LN_FWD(1, LN_FWD_ROWS); break;
+        case 2: LN_FWD(2, LN_FWD_ROWS); break;
+        case 3: LN_FWD(3, LN_FWD_ROWS); break;
+        case 4: LN_FWD(4, LN_FWD_ROWS); break;
+        case 5: case 6: case 7: case 8: LN_FWD(8, 1); break;
+        default: LN_FWD(16, 1); break;
     }
 #undef LN_FWD
     return hipGetLastError();
@@ -271,7 +294,7 @@ hipError_t norm_backward(float* dx, float* dw, float* db, const float* dy, const
     if (e != hipSuccess) return e;
     ProfScope ps2(st, "reduce_rows_kernel", 0.0,
                   4.0 * ((double)G * PARTS * C + (double)PARTS * C * (accumulate_dwdb ? 2 : 1)));
-    hipLaunchKernelGGL(reduce_rows_kernel, dim3((PARTS * C + 63) / 64), dim3(256), 0, st, dw, db, C,
+    hipLaunchKernelGGL(reduce_rows_kernel, dim3((PARTS * C + 15) / 16), dim3(256), 0, st, dw, db, C,
                        (const float*)partial, G, PARTS * C, (int)accumulate_dwdb);
     return hipGetLastError();
 }

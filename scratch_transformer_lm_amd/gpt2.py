@@ -113,6 +113,12 @@ def load() -> ct.CDLL:
     lib.gpt2_layernorm_backward_workspace.restype = sz
     lib.gpt2_layernorm_backward.argtypes = [P, P, P, P, P, P, P, P, i, i, P, sz, P]
     lib.gpt2_layernorm_backward.restype = i
+    lib.gpt2_probe_mfma_out_floats.argtypes = []
+    lib.gpt2_probe_mfma_out_floats.restype = sz
+    lib.gpt2_probe_mfma.argtypes = [i, i, i, P, ct.POINTER(ct.c_double), P]
+    lib.gpt2_probe_mfma.restype = i
+    lib.gpt2_probe_copy.argtypes = [P, P, sz, P]
+    lib.gpt2_probe_copy.restype = i
     _LIB = lib
     return lib
 
@@ -327,3 +333,24 @@ def layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, workspace, stream=None)
                                         _stream_ptr(stream))
     if rc != GPT2_OK:
         raise GPT2Error(rc, "gpt2_layernorm_backward")
+
+
+def probe_mfma_out_floats() -> int:
+    return load().gpt2_probe_mfma_out_floats()
+
+
+def probe_mfma(kind: int, iters: int, out, blocks: int = 1024, stream=None) -> float:
+    """gpt2_probe_mfma: enqueue one matrix-core probe launch; returns the flops it executes."""
+    fl = ct.c_double()
+    rc = load().gpt2_probe_mfma(kind, iters, blocks, out.data_ptr(), ct.byref(fl), _stream_ptr(stream))
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, "gpt2_probe_mfma")
+    return fl.value
+
+
+def probe_copy(dst, src, stream=None) -> None:
+    """gpt2_probe_copy: dst[:] = src[:] (float32 device tensors of equal size)."""
+    assert dst.numel() == src.numel()
+    rc = load().gpt2_probe_copy(dst.data_ptr(), src.data_ptr(), src.numel(), _stream_ptr(stream))
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, "gpt2_probe_copy")

@@ -13,8 +13,8 @@ import pytest
 from scipy.special import logsumexp
 
 from scratch_transformer_lm_amd import synthetic as S
-from tests.parity import (F32_FACTOR, GRAD_TOL, LN_BWD_TOL, LN_FWD_TOL, LOSS_RTOL, param_bound, per_tensor,
-                          rel_max, run_oracle)
+from tests.parity import (F32_FACTOR, GRAD_TOL, LN_BWD_TOL, LN_FWD_TOL, LOSS_RTOL, PARAM_TOL, oracle_rowwise_gradient,
+                          param_bound, param_p99_bound, per_tensor, per_tensor_p99, rel_max, rel_p99, run_oracle)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -134,12 +134,28 @@ def check_training(G, w, steps, variant=0, B=None, T=None):
             say(f"float32 oracle grad rel err step {t}:", {k: f"{v:.2e}" for k, v in e32g.items()})
             tol = {k: max(GRAD_TOL, F32_FACTOR * e32g[k]) for k in e}
         bad += [(t, k, v, tol[k]) for k, v in e.items() if not v <= tol[k]]
+        if bf:
+            # the bulk of each gradient tensor: its 99th-percentile element error within
+            # the fixed tolerance, or F32_FACTOR x the float32 oracle's own percentile
+            # (after a few steps the bf16 rounding flips of earlier updates spread)
+            q = per_tensor_p99(G.PARAM_NAMES, m.offsets, m.lengths, gr["grads"][t], orc["grads"][t])
+            q32 = per_tensor_p99(G.PARAM_NAMES, m.offsets, m.lengths, o32["grads"][t], orc["grads"][t])
+            say(f"grad p99 rel err step {t}:", {k: f"{v:.2e}" for k, v in q.items()})
+            say(f"float32 oracle grad p99 rel err step {t}:", {k: f"{v:.2e}" for k, v in q32.items()})
+            bad += [(t, "p99", k, v, q32[k]) for k, v in q.items() if not v <= max(GRAD_TOL, F32_FACTOR * q32[k])]
     e = per_tensor(G.PARAM_NAMES, m.offsets, m.lengths, gr["params"], orc["params"])
     e32 = per_tensor(G.PARAM_NAMES, m.offsets, m.lengths, o32["params"], orc["params"])
     say("param rel err:", {k: f"{v:.2e}" for k, v in e.items()})
     say("float32 oracle param rel err:", {k: f"{v:.2e}" for k, v in e32.items()})
     if not bf:
+        q = per_tensor_p99(G.PARAM_NAMES, m.offsets, m.lengths, gr["params"], orc["params"])
+        q32 = per_tensor_p99(G.PARAM_NAMES, m.offsets, m.lengths, o32["params"], orc["params"])
+        say("param p99 rel err:", {k: f"{v:.2e}" for k, v in q.items()})
+        say("float32 oracle param p99 rel err:", {k: f"{v:.2e}" for k, v in q32.items()})
+        say("tensors above the literal 1e-4 (max, p99):",
+            {k: (f"{e[k]:.1e}", f"{q[k]:.1e}") for k in e if e[k] > PARAM_TOL or q[k] > PARAM_TOL})
         bad += [("params", k, v, e32[k]) for k, v in e.items() if not v <= param_bound(e32[k])]
+        bad += [("params p99", k, v, q32[k]) for k, v in q.items() if not v <= param_p99_bound(q32[k])]
     else:
         # AdamW moves every element by about lr per step whatever its gradient's size, so
         # an element whose gradient lies within bf16 rounding noise of zero (many bias
@@ -541,12 +557,140 @@ def full_context_check(G, w, rows, variant=0):
     assert err <= 1e-6
 
 
-def test_gpt2_124m_full_context(G):
-    full_context_check(G, S.GPT2_124M, rows=(0, 7))
+# ------------------------------------------------------------------ full context vs the oracle
+#
+# GPT-2 124M at B=8, T=1024 (the benchmarked shape) and 350M at B=4, T=1024 (weight decay
+# 0.1), compared element by element with the float64 oracle.  The oracle's batch gradient
+# is formed from single-row runs (tests/parity.py, oracle_rowwise_gradient).  Step 1 is
+# compared live: every position's loss and every element of every gradient tensor.  The
+# ten-step trajectory takes the float64 oracle far too long to repeat here, so it comes
+# from tests/golden/full_context_<key>.npz, written by tests/golden/make_full_context.py
+# (oracle only): the loss of every step, and samples of the tenth step's gradients and of
+# the parameters after ten updates, with the float32 oracle's whole-tensor errors.
+
+FULL_CONTEXT = {"124m": S.GPT2_124M, "350m": S.GPT2_350M}
+FULL_STEPS = 10
+_full_gpu = {}
 
 
-def test_gpt2_350m_full_context(G):
-    full_context_check(G, S.GPT2_350M, rows=(3,))
+def full_context_gpu(G, key):
+    """Ten GPU steps of a full-context workload (kept for the two tests of that workload):
+    losses, step-1 per-position losses, gradients of steps 1 and 10, final parameters."""
+    if key in _full_gpu:
+        return _full_gpu[key]
+    _full_gpu.clear()
+    w = FULL_CONTEXT[key]
+    say(f"[full context] {w.name}: {FULL_STEPS} GPU steps")
+    params = S.init_params(w.model)
+    x, y = S.tokens(w)
+    m = G.GPT2(w.model, w.B, w.T)
+    m.params.copy_(dev(params))
+    tx, ty = dev(x, torch.int32), dev(y, torch.int32)
+    out = dict(losses=[], offsets=m.offsets, lengths=m.lengths)
+    for t in range(1, FULL_STEPS + 1):
+        out["losses"].append(m.forward(tx, ty))
+        assert m.last_error() == 0, G.strerror(m.last_error())
+        if t == 1:
+            out["per_pos"] = host(m.activation("losses")).reshape(w.B, w.T).copy()
+        assert m.zero_grad() == 0 and m.backward() == 0
+        if t in (1, FULL_STEPS):
+            out[f"g{t}"] = host(m.grads).copy()
+        assert m.update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t) == 0
+    out["losses"] = np.array(out["losses"])
+    out["params"] = host(m.params).copy()
+    m.close()
+    _full_gpu[key] = out
+    return out
+
+
+def full_context_step1(G, key):
+    """Step 1 against the live float64 oracle: the mean loss, every row's per-position
+    losses (1e-5 relative to the row's largest), every gradient tensor element-wise."""
+    from oracle import oracle as O
+    w = FULL_CONTEXT[key]
+    gpu = full_context_gpu(G, key)
+    params = S.init_params(w.model)
+    x, y = S.tokens(w)
+    say(f"[full context] {w.name}: float64 oracle, {w.B} single-row runs")
+    o = O.OracleGPT2(w.model, 1, w.T, params)
+    loss, per_pos = oracle_rowwise_gradient(o, x, y, progress=lambda r: say(f"  oracle row {r} done"))
+    lerr = abs(gpu["losses"][0] - loss) / loss
+    say(f"loss gpu {gpu['losses'][0]:.9f} oracle {loss:.9f} rel err {lerr:.2e}")
+    row_err = [rel_max(gpu["per_pos"][r], per_pos[r]) for r in range(w.B)]
+    say("per-position loss rel err by row:", [f"{e:.1e}" for e in row_err])
+    e = per_tensor(G.PARAM_NAMES, gpu["offsets"], gpu["lengths"], gpu["g1"], o.grads)
+    q = per_tensor_p99(G.PARAM_NAMES, gpu["offsets"], gpu["lengths"], gpu["g1"], o.grads)
+    say("grad rel err step 1:", {k: f"{v:.2e}" for k, v in e.items()})
+    say("grad p99 rel err step 1:", {k: f"{v:.2e}" for k, v in q.items()})
+    o.close()
+    assert lerr <= LOSS_RTOL
+    assert max(row_err) <= LOSS_RTOL, row_err
+    assert max(e.values()) <= GRAD_TOL, e
+
+
+def full_context_ten_steps(G, key):
+    """Ten steps against the stored float64 trajectory: every step's loss (1e-5); the
+    tenth step's gradients on the stored sample (largest error 1e-3); the parameters on
+    the stored sample (largest error within param_bound of the float32 oracle's largest
+    whole-tensor error, the uniform sample's 99th percentile within param_p99_bound of the
+    float32 oracle's whole-tensor percentile)."""
+    import os
+    w = FULL_CONTEXT[key]
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", f"full_context_{key}.npz")
+    assert os.path.exists(path), f"{path} missing: run python tests/golden/make_full_context.py {key}"
+    gold = np.load(path, allow_pickle=False)
+    assert str(gold["workload"]) == w.name and int(gold["steps"]) == FULL_STEPS
+    gpu = full_context_gpu(G, key)
+    _full_gpu.clear()
+    lerr = np.abs(gpu["losses"] - gold["losses64"]) / gold["losses64"]
+    l32 = np.abs(gold["losses32"] - gold["losses64"]) / gold["losses64"]
+    say("loss gpu", gpu["losses"].tolist())
+    say("loss oracle", gold["losses64"].tolist())
+    say("loss rel err", [f"{v:.1e}" for v in lerr], "float32 oracle", [f"{v:.1e}" for v in l32])
+    bad = []
+    rows = []
+    for i, (k, o, n) in enumerate(zip(G.PARAM_NAMES, gpu["offsets"], gpu["lengths"])):
+        ps, p32max, p32p99 = gold["pstats"][i]
+        gs, g32max, g32p99 = gold["gstats"][i]
+        pu, gu = gpu["params"][o:o + n], gpu["g10"][o:o + n]
+        eu = np.abs(pu[gold[f"{k}.pidx"]] - gold[f"{k}.p"]) / ps
+        et = np.abs(pu[gold[f"{k}.ptop"]] - gold[f"{k}.pt"]) / ps
+        pmax, pp99 = float(max(eu.max(), et.max())), float(np.percentile(eu, 99))
+        gu_e = np.abs(gu[gold[f"{k}.gidx"]] - gold[f"{k}.g"]) / gs
+        gt_e = np.abs(gu[gold[f"{k}.gtop"]] - gold[f"{k}.gt"]) / gs
+        gmax = float(max(gu_e.max(), gt_e.max()))
+        rows.append(f"{k}: params max {pmax:.1e} (f32 {p32max:.1e}) p99 {pp99:.1e} (f32 {p32p99:.1e}); "
+                    f"grads max {gmax:.1e} (f32 {g32max:.1e})")
+        if not pmax <= param_bound(p32max):
+            bad.append(("params max", k, pmax, p32max))
+        if not pp99 <= param_p99_bound(p32p99):
+            bad.append(("params p99", k, pp99, p32p99))
+        if not gmax <= GRAD_TOL:
+            bad.append(("grads step 10", k, gmax, g32max))
+    for r in rows:
+        say(r)
+    assert np.all(lerr <= LOSS_RTOL), lerr
+    assert not bad, bad
+
+
+@pytest.mark.timeout(400)
+def test_gpt2_124m_full_context_step1(G):
+    full_context_step1(G, "124m")
+
+
+@pytest.mark.timeout(400)
+def test_gpt2_124m_full_context_ten_steps(G):
+    full_context_ten_steps(G, "124m")
+
+
+@pytest.mark.timeout(400)
+def test_gpt2_350m_full_context_step1(G):
+    full_context_step1(G, "350m")
+
+
+@pytest.mark.timeout(400)
+def test_gpt2_350m_full_context_ten_steps(G):
+    full_context_ten_steps(G, "350m")
 
 
 def test_bf16_124m_full_context(G):
@@ -588,6 +732,23 @@ def test_errors_accumulation_and_determinism(G):
     l2 = m.forward(tx, ty)
     m.backward()
     assert l1 == l2 and np.array_equal(host(m.grads), g1)
+
+
+def test_bf16_batch_shape_beyond_built_tiles(G):
+    """The mixed-precision variant sizes its per-head attention copies in whole 64-position
+    tiles of the built shape: built at (B=1, T=64), a forward at (B=2, T=32) has the same
+    B*T but needs two tiles, and is refused before any launch; (1, 40) fits."""
+    w = S.TINY
+    say("[bf16 shape bound]")
+    params = S.init_params(w.model)
+    m = G.GPT2(w.model, 1, 64, variant=G.VARIANT_BF16)
+    m.params.copy_(dev(params))
+    x, y = S.tokens(w, B=2, T=32)
+    assert math.isnan(m.forward(dev(x, torch.int32), dev(y, torch.int32)))
+    assert m.last_error() == G.GPT2_EINVAL
+    x1, y1 = S.tokens(w, B=1, T=40)
+    loss = m.forward(dev(x1, torch.int32), dev(y1, torch.int32))
+    assert m.last_error() == 0 and math.isfinite(loss)
 
 
 # ------------------------------------------------------------------ mixed precision

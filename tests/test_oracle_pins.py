@@ -127,6 +127,50 @@ def test_matmul_vs_numpy():
     np.testing.assert_allclose(db, dy.sum(0), atol=1e-12)
 
 
+def test_matmul_blocking_only_partitions_outputs():
+    """The oracle's matmul works on blocks of 8 rows x 256 outputs for speed; every output
+    still sums its terms in the plain order (bias, then k = 0, 1, ...).  So it must equal,
+    bit for bit, a triple loop written from the definition, on a shape with ragged row and
+    column blocks (11 rows, 300 outputs) - run in Python floats, which are IEEE doubles
+    with no fused multiply-add, like the oracle's build."""
+    rng = np.random.default_rng(13)
+    N, IC, OC = 11, 13, 300
+    x = rng.standard_normal((N, IC))
+    w = rng.standard_normal((OC, IC))
+    b = rng.standard_normal(OC)
+    dy = rng.standard_normal((N, OC))
+    xl, wl, bl, dyl = x.tolist(), w.tolist(), b.tolist(), dy.tolist()
+    out = np.empty((N, OC))
+    for r in range(N):
+        for o in range(OC):
+            acc = bl[o]
+            for i in range(IC):
+                acc += xl[r][i] * wl[o][i]
+            out[r, o] = acc
+    assert np.array_equal(O.matmul_forward(x, w, b), out)
+    dx, dw, db = O.matmul_backward(dy, x, w)
+    rdx = np.empty((N, IC))
+    for r in range(N):
+        for i in range(IC):
+            acc = 0.0
+            for o in range(OC):
+                acc += dyl[r][o] * wl[o][i]
+            rdx[r, i] = acc
+    rdw = np.empty((OC, IC))
+    rdb = np.empty(OC)
+    for o in range(OC):
+        for i in range(IC):
+            acc = 0.0
+            for r in range(N):
+                acc += dyl[r][o] * xl[r][i]
+            rdw[o, i] = acc
+        acc = 0.0
+        for r in range(N):
+            acc += dyl[r][o]
+        rdb[o] = acc
+    assert np.array_equal(dx, rdx) and np.array_equal(dw, rdw) and np.array_equal(db, rdb)
+
+
 def brute_attention(qkv, NH):
     """Attention from its definition with dense matrices and an explicit mask."""
     B, T, C3 = qkv.shape
