@@ -49,7 +49,8 @@ enum {
     GPT2_EINVAL = -1,  /* bad argument, shape or token id */
     GPT2_ESTATE = -2,  /* call out of order (backward without a forward with targets, t < 1) */
     GPT2_EDEVICE = -3, /* a HIP call failed */
-    GPT2_ENOMEM = -4   /* host allocation failed */
+    GPT2_ENOMEM = -4,  /* host allocation failed */
+    GPT2_ESCRATCH = -5 /* request larger than the library's fixed device scratch */
 };
 
 #define GPT2_NUM_PARAM_TENSORS 16
@@ -308,6 +309,24 @@ int gpt2_layernorm_backward(float* dx, float* dw, float* db, const float* dy, co
 size_t gpt2_probe_mfma_out_floats(void);
 int gpt2_probe_mfma(int kind, int iters, int blocks, float* out, double* flops, void* stream);
 int gpt2_probe_copy(float* dst, const float* src, size_t n, void* stream);
+
+/* gpt2_layernorm_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and determinism as
+ * gpt2_layernorm_backward (the same kernels run), but the partial rows go to a fixed
+ * device array inside the library: at most gpt2_layernorm_backward_noalloc_max_floats()
+ * floats (16 MiB), held on every device the library runs on until the process ends.  No
+ * call allocates: the array's device address is looked up on a device's first call.
+ * Every call on a device shares that device's array (nothing in it needs to start at
+ * any value; a call leaves its partial rows there), so calls that overlap on one
+ * device, on different streams or from different host threads, race and must not be
+ * issued.  Returns GPT2_OK; GPT2_EINVAL for the argument errors of
+ * gpt2_layernorm_backward; GPT2_ESCRATCH if (N, C) needs more than the fixed array;
+ * GPT2_EDEVICE if the array's address cannot be found or a launch fails. */
+size_t gpt2_layernorm_backward_noalloc_max_floats(void);
+int gpt2_layernorm_backward_noalloc(float* dx, float* dw, float* db, const float* dy, const float* x,
+                                    const float* w, const float* mean, const float* rstd, int N, int C,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

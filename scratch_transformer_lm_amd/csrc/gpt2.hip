@@ -808,6 +808,7 @@ const char* gpt2_strerror(int code) {
         case GPT2_ESTATE: return "call out of order";
         case GPT2_EDEVICE: return "HIP call failed";
         case GPT2_ENOMEM: return "out of host memory";
+        case GPT2_ESCRATCH: return "request larger than the library's fixed device scratch";
         default: return "unknown error";
     }
 }

@@ -11,7 +11,10 @@
 // name those model families): no mean subtraction and no bias, r = 1/sqrt(mean(x^2) +
 // eps), y = x r w; the mean slot is written as 0, so the backward's x_hat = (x - mean) r
 // is the same expression, and dx = r (g - x_hat mean(g x_hat)) with no dbeta.
+#include <mutex>
+
 #include "common.h"
+#include "gpt2.h"
 #include "kernels.h"
 #include "prof.h"
 
@@ -329,3 +332,58 @@ hipError_t rmsnorm_backward(float* dx, float* dw, const float* dy, const float* 
 }
 
 }  // namespace gpt2k
+
+// ---------------------------------------------------------------------------------------
+// gpt2_layernorm_backward_noalloc: the standalone LayerNorm backward for callers that
+// cannot allocate (code under HIP graph capture, tight serving loops).  Its partial rows
+// live in a fixed device array of this library instead of a caller workspace.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the device address
+// is looked up once per device with hipGetSymbolAddress and only that address is used.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_FLOATS = (size_t)4 << 20;  // 16 MiB per device
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+static __device__ __align__(256) float scratch[NOALLOC_SCRATCH_FLOATS];
+
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+
+// Device address of `scratch` on the current device (looked up on its first use there),
+// or nullptr on failure.
+float* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = static_cast<float*>(ptr);
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gpt2_layernorm_backward_noalloc_max_floats(void) { return NOALLOC_SCRATCH_FLOATS; }
+
+int gpt2_layernorm_backward_noalloc(float* dx, float* dw, float* db, const float* dy, const float* x,
+                                    const float* w, const float* mean, const float* rstd, int N, int C,
+                                    void* stream) {
+    auto al = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    if (!dw || !db || N < 0 || C <= 0 || C % 4 || C > 4096) return GPT2_EINVAL;
+    if (N > 0 && (!dx || !dy || !x || !w || !mean || !rstd)) return GPT2_EINVAL;
+    if (N > 0 && (!al(dx) || !al(dy) || !al(x) || !al(w))) return GPT2_EINVAL;
+    if (gpt2k::layernorm_partial_floats(N, C) > NOALLOC_SCRATCH_FLOATS) return GPT2_ESCRATCH;
+    float* ptr = device_scratch();
+    if (!ptr) return GPT2_EDEVICE;
+    return gpt2k::layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, N, C, false, false, ptr,
+                                     (hipStream_t)stream) == hipSuccess
+               ? GPT2_OK
+               : GPT2_EDEVICE;
+}
+
+}  // extern "C"

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgpt2_mi355x.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "gpt2.h")
 
-GPT2_OK, GPT2_EINVAL, GPT2_ESTATE, GPT2_EDEVICE, GPT2_ENOMEM = 0, -1, -2, -3, -4
+GPT2_OK, GPT2_EINVAL, GPT2_ESTATE, GPT2_EDEVICE, GPT2_ENOMEM, GPT2_ESCRATCH = 0, -1, -2, -3, -4, -5
 PARAM_NAMES = ("wte", "wpe", "ln1w", "ln1b", "qkvw", "qkvb", "attprojw", "attprojb",
                "ln2w", "ln2b", "fcw", "fcb", "fcprojw", "fcprojb", "lnfw", "lnfb")
 ACT_NAMES = ("encoded", "ln1", "ln1_mean", "ln1_rstd", "qkv", "atty", "att_lse", "residual2",
@@ -119,6 +119,10 @@ def load() -> ct.CDLL:
     lib.gpt2_probe_mfma.restype = i
     lib.gpt2_probe_copy.argtypes = [P, P, sz, P]
     lib.gpt2_probe_copy.restype = i
+    lib.gpt2_layernorm_backward_noalloc_max_floats.argtypes = []
+    lib.gpt2_layernorm_backward_noalloc_max_floats.restype = sz
+    lib.gpt2_layernorm_backward_noalloc.argtypes = [P, P, P, P, P, P, P, P, i, i, P]
+    lib.gpt2_layernorm_backward_noalloc.restype = i
     _LIB = lib
     return lib
 
@@ -333,6 +337,21 @@ def layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, workspace, stream=None)
                                         _stream_ptr(stream))
     if rc != GPT2_OK:
         raise GPT2Error(rc, "gpt2_layernorm_backward")
+
+
+def layernorm_backward_noalloc_max_floats() -> int:
+    return load().gpt2_layernorm_backward_noalloc_max_floats()
+
+
+def layernorm_backward_noalloc(dx, dw, db, dy, x, w, mean, rstd, stream=None) -> None:
+    """gpt2_layernorm_backward_noalloc: as layernorm_backward, with the library's fixed
+    device scratch instead of a workspace."""
+    N, C = x.shape
+    rc = load().gpt2_layernorm_backward_noalloc(dx.data_ptr(), dw.data_ptr(), db.data_ptr(), dy.data_ptr(),
+                                                x.data_ptr(), w.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
+                                                N, C, _stream_ptr(stream))
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, "gpt2_layernorm_backward_noalloc")
 
 
 def probe_mfma_out_floats() -> int:
