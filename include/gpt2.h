@@ -303,12 +303,13 @@ int gpt2_layernorm_backward(float* dx, float* dw, float* db, const float* dy, co
  * that receives one value per thread (so nothing is optimised away); *flops (host)
  * receives the flops the launch executes.
  * gpt2_probe_copy: dst[i] = src[i] for n floats (n a multiple of 4, 16-byte aligned
- * device buffers that do not overlap), float4 loads and stores.
+ * device buffers that do not overlap), float4 loads and stores, by a grid-stride loop
+ * over `blocks` (1..65536) blocks of 256 threads.
  * Both enqueue on `stream` only; GPT2_EINVAL for bad arguments, GPT2_EDEVICE if the
  * launch fails. */
 size_t gpt2_probe_mfma_out_floats(void);
 int gpt2_probe_mfma(int kind, int iters, int blocks, float* out, double* flops, void* stream);
-int gpt2_probe_copy(float* dst, const float* src, size_t n, void* stream);
+int gpt2_probe_copy(float* dst, const float* src, size_t n, int blocks, void* stream);
 
 /* gpt2_layernorm_backward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses

@@ -1055,9 +1055,24 @@ const char* splitk_fixup_name() {
 // Work distribution over a persistent grid of up to RESIDENT blocks: whole-tile rounds
 // while at least RESIDENT tiles remain, then equal ranges of the rest.
 // The fp32 weight gradients run on their own stream next to the main backward chain; a
-// persistent grid of fewer blocks than the chip holds leaves CU slots to that chain.
+// persistent grid of fewer blocks than the chip holds leaves CU slots to that chain
+// (measured slower: 448, 384 and 256 blocks give 55.6, 56.5 and 57.0 ms per step against
+// 55.0 at 512).
 #ifndef GEMM_WGRAD_RESIDENT
 #define GEMM_WGRAD_RESIDENT RESIDENT
+#endif
+// fp32 weight gradients as split-K rounds ordered k-segment first (as the bf16 ones)
+// instead of stream-K ranges: the 64 blocks of an XCD then work on neighbouring tiles at
+// the same k and share operand panels in that XCD's L2.  Same time (54.90 against
+// 54.84 ms per step), but the kernel's memory-side reads fall from 435 to 80 MB per
+// launch (114.8 MB algorithmic), which leaves the fabric to the concurrent main chain.
+#ifndef GEMM_F32_WGRAD_SPLITK
+#define GEMM_F32_WGRAD_SPLITK 1
+#endif
+// ... launched as one block per split-K unit rather than a persistent grid, so that blocks
+// retire (and free CU slots for the main chain's kernels) every unit.
+#ifndef GEMM_WGRAD_NONPERSISTENT
+#define GEMM_WGRAD_NONPERSISTENT 0
 #endif
 void schedule(Params& p, long tiles, int split, int resident = RESIDENT) {
     p.R = 0;
@@ -1067,12 +1082,14 @@ void schedule(Params& p, long tiles, int split, int resident = RESIDENT) {
     if (split > 1 && p.partial != nullptr && tiles * split <= MAX_UNITS && split <= p.nk) {
         p.S = split;
         p.units = (int)tiles * split;
-        p.G = std::min(RESIDENT, p.units);
+        // resident < 0: one block per unit instead of a persistent grid
+        p.G = resident < 0 ? p.units : std::min(resident, p.units);
         p.nr = 0;
         p.skt = 0;
         p.total = 0;
         return;
     }
+    if (resident < 0) resident = RESIDENT;
     if (p.partial == nullptr) {  // nowhere to put partial tiles: one tile per block
         p.G = (int)tiles;
         p.R = 1;
@@ -1120,12 +1137,28 @@ hipError_t launch(Params& p, hipStream_t st, int split, int resident = RESIDENT)
         else if constexpr (BF) hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BN>), dim3(p.G), dim3(NT), 0, st, p);
         else hipLaunchKernelGGL((gemm_kernel<A_K, B_K, EPI, XF, BN>), dim3(p.G), dim3(NT), 0, st, p);
     }
+    // fix-up algorithmic bytes: the partial tiles it reads, and for each tile it finishes
+    // the output written (and read too where the epilogue reads C or an aux tensor)
     const double slot = (double)BM * BN + BM;
+    const double per_tile = (double)BM * BN * (extra > 0 ? 2.0 : 1.0);
     if (p.S > 1) {
-        ProfScope ps(st, splitk_fixup_name<EPI, BN>(), 0.0, 4.0 * ((double)p.units * slot + extra));
+        const double split_tiles = (double)(p.units / p.S);
+        ProfScope ps(st, splitk_fixup_name<EPI, BN>(), 0.0, 4.0 * ((double)p.units * slot + split_tiles * per_tile));
         hipLaunchKernelGGL((gemm_splitk_fixup_kernel<EPI, BN>), dim3(4 * (p.units / p.S)), dim3(NT), 0, st, p);
     } else if (p.nr > 1 && !(p.total % p.nr == 0 && (p.total / p.nr) % p.nk == 0)) {
-        ProfScope ps(st, fixup_name<EPI, BN>(), 0.0, 4.0 * (2.0 * p.nr * slot + extra));
+        // the (range, tile) pieces that are not whole tiles, and the tiles they split
+        long pieces = 0, split_tiles = 0, last_split = -1;
+        for (int l = 0; l < p.nr; l++) {
+            const long s0 = (long)l * p.total / p.nr, s1 = (long)(l + 1) * p.total / p.nr;
+            for (long t = s0 / p.nk; s1 > s0 && t <= (s1 - 1) / p.nk; t++) {
+                const long a = std::max(s0, t * p.nk), b = std::min(s1, (t + 1) * p.nk);
+                if (b - a < p.nk) {
+                    pieces++;
+                    if (t != last_split) split_tiles++, last_split = t;
+                }
+            }
+        }
+        ProfScope ps(st, fixup_name<EPI, BN>(), 0.0, 4.0 * ((double)pieces * slot + (double)split_tiles * per_tile));
         hipLaunchKernelGGL((gemm_fixup_kernel<EPI, BN>), dim3(4 * (p.nr - 1)), dim3(NT), 0, st, p);
     }
     return hipGetLastError();
@@ -1170,16 +1203,16 @@ int tile_n(int M, int N) {
 #define GEMM_BF_SPLITK 1
 #endif
 template <bool A_K, bool BF, int BN>
-int pick_split_rounds(int M, int N, int K) {
+int pick_split_rounds(int M, int N, int K, int resident = RESIDENT) {
     const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int nk = (K + KTileOf<A_K, BF, BN>::BK - 1) / KTileOf<A_K, BF, BN>::BK;
-    if (tiles == 0 || tiles >= RESIDENT) return 0;
+    if (tiles == 0 || tiles >= resident) return 0;
     int best = 0;
     double best_util = 0.9;
     for (int s = 2; s <= 16; s++) {
         const long units = tiles * s;
         if (units > MAX_UNITS || nk < 8 * s) break;
-        const double util = (double)units / (double)(((units + RESIDENT - 1) / RESIDENT) * RESIDENT);
+        const double util = (double)units / (double)(((units + resident - 1) / resident) * resident);
         if (util > best_util + 1e-9) {
             best_util = util;
             best = s;
@@ -1327,7 +1360,9 @@ hipError_t linear_wgrad(float* dw, float* dbias, const float* dout, long ld_dout
         p.xlog2s = (float)std::log2((double)xent->scale);
         return launch<false, false, EPI_ACCUM, true, 128>(p, st, 0);
     }
-    return launch<false, false, EPI_ACCUM, false, 128>(p, st, 0, GEMM_WGRAD_RESIDENT);
+    const int split = GEMM_F32_WGRAD_SPLITK ? pick_split_rounds<false, false, 128>(M, N, K, GEMM_WGRAD_RESIDENT) : 0;
+    return launch<false, false, EPI_ACCUM, false, 128>(
+        p, st, split, (GEMM_WGRAD_NONPERSISTENT && split > 1) ? -1 : GEMM_WGRAD_RESIDENT);
 }
 
 hipError_t gemm_bf16(int epi, float* c, long ldc, const uint16_t* a, long lda, const uint16_t* b, long ldb, int M,

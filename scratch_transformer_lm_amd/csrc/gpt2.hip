@@ -718,8 +718,8 @@ int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const g
     }
     // the weight-gradient stream (default priority, no implicit sync with the null stream)
     // and the events that order it against the main stream
-    bool ok = hipStreamCreateWithFlags(&g->st_w, hipStreamNonBlocking) == hipSuccess &&
-              hipStreamCreateWithFlags(&g->st_u, hipStreamNonBlocking) == hipSuccess;
+    bool ok = hipStreamCreateWithFlags(&g->st_w, hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipStreamCreateWithFlags(&g->st_u, hipStreamNonBlocking) == hipSuccess;
     int nev = 0;
     for (; ok && nev < 13; nev++) ok = hipEventCreateWithFlags(&g->ev[nev], hipEventDisableTiming) == hipSuccess;
     if (ok) {

@@ -123,9 +123,17 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
     for (int row = blockIdx.x * ROWS_PER_BLOCK + wave; row < N; row += gridDim.x * ROWS_PER_BLOCK) {
         const float4* xr = reinterpret_cast<const float4*>(x + (long)row * C);
         const float4* dr = reinterpret_cast<const float4*>(dy + (long)row * C);
+        float4* o = reinterpret_cast<float4*>(dx + (long)row * C);
         const float m = mean[row], r = rstd[row];
-        float4 xh[VPL], g[VPL];
+        float4 xh[VPL], g[VPL], ov[VPL];
         float sg = 0.f, sgx = 0.f;
+        // the row's x, dy and (when accumulating) old dx are all requested before the
+        // reductions, so a row costs one memory latency
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            const int i = lane + 64 * j;
+            ov[j] = (accumulate && i < C4) ? o[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
         for (int j = 0; j < VPL; j++) {
             const int i = lane + 64 * j;
@@ -150,7 +158,6 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
         }
         const float mg = RMS ? 0.f : wave_sum(sg) / (float)C;
         const float mgx = wave_sum(sgx) / (float)C;
-        float4* o = reinterpret_cast<float4*>(dx + (long)row * C);
 #pragma unroll
         for (int j = 0; j < VPL; j++) {
             const int i = lane + 64 * j;
@@ -161,11 +168,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
                 d.z = r * (g[j].z - mg - xh[j].z * mgx);
                 d.w = r * (g[j].w - mg - xh[j].w * mgx);
                 if (accumulate) {
-                    const float4 old = o[i];
-                    d.x += old.x;
-                    d.y += old.y;
-                    d.z += old.z;
-                    d.w += old.w;
+                    d.x += ov[j].x;
+                    d.y += ov[j].y;
+                    d.z += ov[j].z;
+                    d.w += ov[j].w;
                 }
                 o[i] = d;
             }

@@ -3,8 +3,8 @@
 // training step.
 //   probe_mfma_kernel: independent matrix-core products held in registers (no memory
 //     traffic), fp32 16x16x4 or bf16 16x16x32, the shapes the step's kernels use;
-//   probe_copy_kernel: a plain float4 copy (each block one tile, a thread's loads all
-//     issued before its stores), the bandwidth a streaming kernel can reach.
+//   probe_copy_kernel: a plain float4 copy over a grid of a given size, the bandwidth a
+//     streaming kernel can reach.
 #include "common.h"
 #include "gpt2.h"
 
@@ -16,7 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int PROBE_CHAINS = 16;        // independent accumulators per wave
 constexpr int PROBE_MAX_BLOCKS = 4096;  // 256-thread blocks: 4 per CU = 4 waves per SIMD
 constexpr int PROBE_THREADS = 256;
-constexpr int COPY_UNROLL = 8;          // float4s per thread of the copy, all loaded first
+constexpr int COPY_UNROLL = 4;          // float4s per thread and round of the copy, all loaded first
 
 template <bool BF16>
 __global__ __launch_bounds__(PROBE_THREADS) void probe_mfma_kernel(float* __restrict__ out, int iters) {
@@ -45,16 +45,20 @@ __global__ __launch_bounds__(PROBE_THREADS) void probe_mfma_kernel(float* __rest
     out[(size_t)blockIdx.x * PROBE_THREADS + threadIdx.x] = s;
 }
 
+// grid-stride copy: each thread moves COPY_UNROLL float4s per round, all loaded before
+// any is stored
 __global__ __launch_bounds__(256) void probe_copy_kernel(float4* __restrict__ dst, const float4* __restrict__ src,
                                                          size_t n4) {
-    const size_t base = (size_t)blockIdx.x * (256 * COPY_UNROLL) + threadIdx.x;
-    float4 v[COPY_UNROLL];
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (COPY_UNROLL - 1) * stride < n4; i += COPY_UNROLL * stride) {
+        float4 v[COPY_UNROLL];
 #pragma unroll
-    for (int u = 0; u < COPY_UNROLL; u++)
-        if (base + (size_t)u * 256 < n4) v[u] = src[base + (size_t)u * 256];
+        for (int u = 0; u < COPY_UNROLL; u++) v[u] = src[i + u * stride];
 #pragma unroll
-    for (int u = 0; u < COPY_UNROLL; u++)
-        if (base + (size_t)u * 256 < n4) dst[base + (size_t)u * 256] = v[u];
+        for (int u = 0; u < COPY_UNROLL; u++) dst[i + u * stride] = v[u];
+    }
+    for (; i < n4; i += stride) dst[i] = src[i];
 }
 
 }  // namespace
@@ -77,12 +81,11 @@ int gpt2_probe_mfma(int kind, int iters, int blocks, float* out, double* flops, 
     return hipGetLastError() == hipSuccess ? GPT2_OK : GPT2_EDEVICE;
 }
 
-int gpt2_probe_copy(float* dst, const float* src, size_t n, void* stream) {
-    if (!dst || !src || n % 4 || ((uintptr_t)dst & 15) || ((uintptr_t)src & 15)) return GPT2_EINVAL;
+int gpt2_probe_copy(float* dst, const float* src, size_t n, int blocks, void* stream) {
+    if (!dst || !src || n % 4 || blocks < 1 || blocks > 65536 || ((uintptr_t)dst & 15) || ((uintptr_t)src & 15))
+        return GPT2_EINVAL;
     if (n == 0) return GPT2_OK;
-    const size_t tiles = (n / 4 + 256 * COPY_UNROLL - 1) / (256 * COPY_UNROLL);
-    if (tiles > 0x7fffffff) return GPT2_EINVAL;
-    hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        reinterpret_cast<float4*>(dst), reinterpret_cast<const float4*>(src), n / 4);
     return hipGetLastError() == hipSuccess ? GPT2_OK : GPT2_EDEVICE;
 }

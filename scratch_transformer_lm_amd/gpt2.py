@@ -117,7 +117,7 @@ def load() -> ct.CDLL:
     lib.gpt2_probe_mfma_out_floats.restype = sz
     lib.gpt2_probe_mfma.argtypes = [i, i, i, P, ct.POINTER(ct.c_double), P]
     lib.gpt2_probe_mfma.restype = i
-    lib.gpt2_probe_copy.argtypes = [P, P, sz, P]
+    lib.gpt2_probe_copy.argtypes = [P, P, sz, i, P]
     lib.gpt2_probe_copy.restype = i
     lib.gpt2_layernorm_backward_noalloc_max_floats.argtypes = []
     lib.gpt2_layernorm_backward_noalloc_max_floats.restype = sz
@@ -367,9 +367,9 @@ def probe_mfma(kind: int, iters: int, out, blocks: int = 1024, stream=None) -> f
     return fl.value
 
 
-def probe_copy(dst, src, stream=None) -> None:
+def probe_copy(dst, src, blocks: int = 2048, stream=None) -> None:
     """gpt2_probe_copy: dst[:] = src[:] (float32 device tensors of equal size)."""
     assert dst.numel() == src.numel()
-    rc = load().gpt2_probe_copy(dst.data_ptr(), src.data_ptr(), src.numel(), _stream_ptr(stream))
+    rc = load().gpt2_probe_copy(dst.data_ptr(), src.data_ptr(), src.numel(), blocks, _stream_ptr(stream))
     if rc != GPT2_OK:
         raise GPT2Error(rc, "gpt2_probe_copy")
