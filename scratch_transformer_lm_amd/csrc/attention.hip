@@ -45,6 +45,22 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TILE = 64;
+// Build options: blocks per CU of the forward and dQ kernels (their registers are capped
+// to fit), and whether the next LDS fragments are read while the current ones multiply
+// (two register buffers) or just before use (one).
+#ifndef ATTN_FWD_OCC
+#define ATTN_FWD_OCC 3
+#endif
+#ifndef ATTN_AHEAD
+#define ATTN_AHEAD 1
+#endif
+// forward and dQ: the next K/V tile is loaded into registers while the current one is used
+// (1), or after the current one is done, straight before it is stored to LDS (0)
+#ifndef ATTN_PREFETCH
+#define ATTN_PREFETCH 1
+#endif
+constexpr int NFB = ATTN_AHEAD ? 2 : 1;
+GPT2_DEV constexpr int fb(int a) { return ATTN_AHEAD ? (a & 1) : 0; }
 
 GPT2_DEV f32x4 mfma4(float a, float b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
 
@@ -145,7 +161,7 @@ GPT2_DEV void dot_operand(float (&v)[4][HS / 16], const float* row, bool valid, 
 
 // ---------------------------------------------------------------------------- forward
 template <int HS>
-__global__ __launch_bounds__(256, 3) void attn_fwd_kernel(float* __restrict__ out, float* __restrict__ lse,
+__global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __restrict__ out, float* __restrict__ lse,
                                                        const float* __restrict__ qkv, int B, int T, int C, int NH,
                                                        float scale) {
     constexpr int DG = HS / 16, LD = HS + 4;
@@ -180,7 +196,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(float* __restrict__ ou
     // one key tile; only the diagonal tile (kt == qt) has keys after the query
     auto step = [&](int kt, auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
-        if (kt + 1 < nkt) {
+        if (ATTN_PREFETCH && kt + 1 < nkt) {
             tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
             tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
         }
@@ -191,7 +207,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(float* __restrict__ ou
         f32x4 s[4];
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) s[kb] = zero4();
-        float kf[2][4][DG];
+        float kf[NFB][4][DG];
         auto read_k = [&](int a, float (&dst)[4][DG]) {
 #pragma unroll
             for (int kb = 0; kb < 4; kb++) lds_get<DG>(dst[kb], K + (kb * 16 + i16) * LD + DG * (4 * a + g4));
@@ -199,16 +215,17 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(float* __restrict__ ou
         read_k(0, kf[0]);
 #pragma unroll
         for (int a = 0; a < 4; a++) {
-            if (a + 1 < 4) read_k(a + 1, kf[(a + 1) & 1]);
+            if (ATTN_AHEAD && a + 1 < 4) read_k(a + 1, kf[fb(a + 1)]);
+            if (!ATTN_AHEAD && a > 0) read_k(a, kf[0]);
             sched_fence();
 #pragma unroll
             for (int j = 0; j < DG; j++)
 #pragma unroll
-                for (int kb = 0; kb < 4; kb++) s[kb] = mfma4(kf[a & 1][kb][j], qreg[a][j], s[kb]);
+                for (int kb = 0; kb < 4; kb++) s[kb] = mfma4(kf[fb(a)][kb][j], qreg[a][j], s[kb]);
             sched_fence();
         }
         // the V runs of the first key block, read while the softmax runs
-        float vf[2][4][DG];
+        float vf[NFB][4][DG];
         auto read_v = [&](int kb, float (&dst)[4][DG]) {
 #pragma unroll
             for (int v = 0; v < 4; v++) lds_get<DG>(dst[v], V + (kb * 16 + 4 * g4 + v) * LD + DG * i16);
@@ -259,15 +276,20 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(float* __restrict__ ou
         // which is one interleaved run; block kb+1's runs are read while block kb multiplies
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
-            if (kb + 1 < 4) read_v(kb + 1, vf[(kb + 1) & 1]);
+            if (ATTN_AHEAD && kb + 1 < 4) read_v(kb + 1, vf[fb(kb + 1)]);
+            if (!ATTN_AHEAD && kb > 0) read_v(kb, vf[0]);
             sched_fence();
 #pragma unroll
             for (int v = 0; v < 4; v++)
 #pragma unroll
-                for (int d = 0; d < DG; d++) o[d] = mfma4(s[kb][v], vf[kb & 1][v][d], o[d]);
+                for (int d = 0; d < DG; d++) o[d] = mfma4(s[kb][v], vf[fb(kb)][v][d], o[d]);
             sched_fence();
         }
         if (kt + 1 < nkt) {
+            if (!ATTN_PREFETCH) {
+                tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
+                tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
+            }
             // every wave is done with this tile before the next one overwrites it
             __syncthreads();
             tile_store<HS>(Ks, kreg);
@@ -293,7 +315,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(float* __restrict__ ou
 
 // ---------------------------------------------------------------------------- dq (+ D)
 template <int HS>
-__global__ __launch_bounds__(256, 3) void attn_bwd_dq_kernel(float* __restrict__ dqkv, float* __restrict__ delta,
+__global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_bwd_dq_kernel(float* __restrict__ dqkv, float* __restrict__ delta,
                                                           const float* __restrict__ dout, const float* __restrict__ qkv,
                                                           const float* __restrict__ out, const float* __restrict__ lse,
                                                           int B, int T, int C, int NH, float scale) {
@@ -342,7 +364,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_kernel(float* __restrict__
     // one key tile; only the diagonal tile (kt == qt) has keys after the query
     auto step = [&](int kt, auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
-        if (kt + 1 < nkt) {
+        if (ATTN_PREFETCH && kt + 1 < nkt) {
             tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
             tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
         }
@@ -355,7 +377,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_kernel(float* __restrict__
             float kr[4][DG];
 #pragma unroll
             for (int v = 0; v < 4; v++) lds_get<DG>(kr[v], K + (kb * 16 + 4 * g4 + v) * LD + DG * i16);
-            float kf[2][DG], vf[2][DG];
+            float kf[NFB][DG], vf[NFB][DG];
             auto read_kv = [&](int a, float (&k)[DG], float (&v)[DG]) {
                 lds_get<DG>(k, K + (kb * 16 + i16) * LD + DG * (4 * a + g4));
                 lds_get<DG>(v, V + (kb * 16 + i16) * LD + DG * (4 * a + g4));
@@ -363,12 +385,13 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_kernel(float* __restrict__
             read_kv(0, kf[0], vf[0]);
 #pragma unroll
             for (int a = 0; a < 4; a++) {
-                if (a + 1 < 4) read_kv(a + 1, kf[(a + 1) & 1], vf[(a + 1) & 1]);
+                if (ATTN_AHEAD && a + 1 < 4) read_kv(a + 1, kf[fb(a + 1)], vf[fb(a + 1)]);
+                if (!ATTN_AHEAD && a > 0) read_kv(a, kf[0], vf[0]);
                 sched_fence();
 #pragma unroll
                 for (int j = 0; j < DG; j++) {
-                    s = mfma4(kf[a & 1][j], qreg[a][j], s);
-                    dp = mfma4(vf[a & 1][j], doreg[a][j], dp);
+                    s = mfma4(kf[fb(a)][j], qreg[a][j], s);
+                    dp = mfma4(vf[fb(a)][j], doreg[a][j], dp);
                 }
                 sched_fence();
             }
@@ -386,6 +409,10 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_kernel(float* __restrict__
                 for (int d = 0; d < DG; d++) dq[d] = mfma4(ds[v], kr[v][d], dq[d]);
         }
         if (kt + 1 < nkt) {
+            if (!ATTN_PREFETCH) {
+                tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
+                tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
+            }
             // every wave is done with this tile before the next one overwrites it
             __syncthreads();
             tile_store<HS>(Ks, kreg);

@@ -1070,7 +1070,8 @@ const char* splitk_fixup_name() {
 #define GEMM_F32_WGRAD_SPLITK 1
 #endif
 // ... launched as one block per split-K unit rather than a persistent grid, so that blocks
-// retire (and free CU slots for the main chain's kernels) every unit.
+// retire (and free CU slots for the main chain's kernels) every unit (measured slower:
+// 56.15 against 55.06 ms per step).
 #ifndef GEMM_WGRAD_NONPERSISTENT
 #define GEMM_WGRAD_NONPERSISTENT 0
 #endif
