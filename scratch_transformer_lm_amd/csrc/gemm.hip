@@ -587,6 +587,13 @@ GPT2_DEV void gemm_body(const Params& p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * WN;
     const int li = lane & 15, grp = lane >> 4;
+    // 96-row row-contiguous B fragments: element (k row 16g + 4grp + s, row wn + 16b + li)
+    // sits at rpos<96> = boff96[s] + (b BK + 16g) 16, since wn is a multiple of 16 and
+    // kperm(16g + 4grp + s) = 16g + 4grp + (s ^ grp); the lane-dependent part stays in
+    // four registers and the rest folds into the LDS reads' immediate offsets.
+    int boff96[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) boff96[s] = (((wn >> 4) * BK + 4 * grp + (s ^ grp)) << 4) + li;
     const int kfull = p.K / BK;  // k-tiles that need no bounds check
     // row clamps: k-contiguous rows to the last row; row-contiguous float4 groups to the
     // last whole group inside the row (for the logits operand, inside the padded row)
@@ -786,6 +793,10 @@ GPT2_DEV void gemm_body(const Params& p) {
                         fb[b][1] = v.y;
                         fb[b][2] = v.z;
                         fb[b][3] = v.w;
+                    } else if (BN == 96) {
+                        // rpos<96> split into a per-lane part and an immediate offset
+#pragma unroll
+                        for (int s = 0; s < 4; s++) fb[b][s] = Sb[boff96[s] + (b * BK + 16 * g) * 16];
                     } else {
 #pragma unroll
                         for (int s = 0; s < 4; s++) {
