@@ -289,6 +289,17 @@ def ceilings(G, torch):
             best = (s, blocks)
     s = best[0]
     res["copy_1gib"] = dict(gbps=2.0 * 4 * n / s / 1e9, frac_of_datasheet=2.0 * 4 * n / s / PEAK_HBM, blocks=best[1])
+    # the platform's own device-to-device copy of the same buffers, for comparison
+    ts = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        dst.copy_(src)
+        e1.record(st)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    s = min(a.elapsed_time(b) for a, b in ts) / 1e3
+    res["platform_copy_1gib"] = dict(gbps=2.0 * 4 * n / s / 1e9, frac_of_datasheet=2.0 * 4 * n / s / PEAK_HBM)
     del src, dst
     res["note"] = "fractions elsewhere in this line use the datasheet peaks (fp32 157.3 TFLOP/s, bf16 2.5 PFLOP/s, HBM 8 TB/s)"
     return res
