@@ -12,6 +12,25 @@ namespace gpt2k {
 
 namespace {
 
+// Build option: the optimizer-only streams (g read; m, v read and written) as nontemporal
+// accesses (1), or as ordinary ones (0).  Measured over the 124M buffer: 5.69 against
+// 5.36 TB/s.  p stays ordinary: the next forward reads it.
+#ifndef ADAM_NT
+#define ADAM_NT 1
+#endif
+typedef float nt4 __attribute__((ext_vector_type(4)));
+GPT2_DEV float4 ld_s(const float4* a) {
+    if (ADAM_NT) {
+        const nt4 t = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(a));
+        return make_float4(t.x, t.y, t.z, t.w);
+    }
+    return *a;
+}
+GPT2_DEV void st_s(float4* a, float4 v) {
+    if (ADAM_NT) __builtin_nontemporal_store(nt4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt4*>(a));
+    else *a = v;
+}
+
 // One element.  ibc1, ibc2 are the reciprocals of the bias corrections 1 - b^t.
 GPT2_DEV void adam_one(float& p, float g, float& m, float& v, float lr, float b1, float b2, float eps,
                        float wd, float ibc1, float ibc2) {
@@ -30,8 +49,8 @@ GPT2_DEV void adam_four(float4* __restrict__ p, const float4* __restrict__ g, fl
     adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, ibc1, ibc2);
     adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, ibc1, ibc2);
     p[j] = pp;
-    m[j] = mm;
-    v[j] = vv;
+    st_s(m + j, mm);
+    st_s(v + j, vv);
 }
 
 // A block updates one tile of ADAM_TILE float4s of one contiguous range: ADAM_UNROLL
@@ -51,9 +70,9 @@ GPT2_DEV void adam_tile(float* p_, const float* g_, float* m_, float* v_, size_t
         const size_t j = base4 + (size_t)u * 256 + threadIdx.x;
         if (j < end4) {
             pp[u] = p[j];
-            gg[u] = g[j];
-            mm[u] = m[j];
-            vv[u] = v[j];
+            gg[u] = ld_s(g + j);
+            mm[u] = ld_s(m + j);
+            vv[u] = ld_s(v + j);
         }
     }
 #pragma unroll
