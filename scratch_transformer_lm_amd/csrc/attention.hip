@@ -74,6 +74,25 @@ constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
 GPT2_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 GPT2_DEV float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
+// Max and sum over the four 16-lane rows of a wave (lanes i, i^16, i^32, i^48), on the
+// VALU: v_permlane16_swap exchanges rows 1,3 of its first operand with rows 0,2 of its
+// second, v_permlane32_swap the upper half of the first with the lower half of the second,
+// so with both operands the same value each lane ends up holding its own row's value and
+// its partner's.  The sum is (r0 + r1) + (r2 + r3) in every lane (addition commutes), the
+// same as two shuffle-xor steps.
+GPT2_DEV float xmax4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+GPT2_DEV float xsum4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // DG = HS/16 consecutive floats of an interleaved LDS row (aligned to 4*DG bytes).
 template <int DG>
 GPT2_DEV void lds_get(float (&v)[DG], const float* src) {
@@ -241,14 +260,14 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
                 if (DIAG && kt * TILE + kb * 16 + 4 * g4 + v > tq) s[kb][v] = -INFINITY;
                 mx = fmaxf(mx, s[kb][v]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         // The reference max m (base 2) of each row moves only when the row's new max
         // exceeds it by more than 8, i.e. probabilities relative to m stay below 2^8; the
         // result is the same softmax, and O is rescaled only on the (rare, wave-wide)
-        // occasions when some row's reference moves.
-        const float mnew = fmaxf(m, mx * scale2);
-        if (__any(mnew > m + 8.0f)) {
+        // occasions when some row's reference moves.  A row's max exceeds m + 8 exactly
+        // when one of its four lanes' partial maxima does, so the row max across the lanes
+        // is only formed on those occasions.
+        if (__any(mx * scale2 > m + 8.0f)) {
+            const float mnew = fmaxf(m, xmax4(mx) * scale2);
             const float alpha = exp2_hw(m - mnew);
             l *= alpha;
             m = mnew;
@@ -269,9 +288,7 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
                 s[kb][v] = p;
                 rs += p;
             }
-        rs += __shfl_xor(rs, 16, 64);
-        rs += __shfl_xor(rs, 32, 64);
-        l += rs;
+        l += xsum4(rs);
         // O += P V: for key kb*16 + 4*g4 + v this lane needs V[key][16d + i16], d < DG,
         // which is one interleaved run; block kb+1's runs are read while block kb multiplies
 #pragma unroll
