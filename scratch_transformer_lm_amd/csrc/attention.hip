@@ -74,25 +74,6 @@ constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
 GPT2_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 GPT2_DEV float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
-// Max and sum over the four 16-lane rows of a wave (lanes i, i^16, i^32, i^48), on the
-// VALU: v_permlane16_swap exchanges rows 1,3 of its first operand with rows 0,2 of its
-// second, v_permlane32_swap the upper half of the first with the lower half of the second,
-// so with both operands the same value each lane ends up holding its own row's value and
-// its partner's.  The sum is (r0 + r1) + (r2 + r3) in every lane (addition commutes), the
-// same as two shuffle-xor steps.
-GPT2_DEV float xmax4(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-GPT2_DEV float xsum4(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // DG = HS/16 consecutive floats of an interleaved LDS row (aligned to 4*DG bytes).
 template <int DG>
 GPT2_DEV void lds_get(float (&v)[DG], const float* src) {
@@ -267,7 +248,7 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
         // when one of its four lanes' partial maxima does, so the row max across the lanes
         // is only formed on those occasions.
         if (__any(mx * scale2 > m + 8.0f)) {
-            const float mnew = fmaxf(m, xmax4(mx) * scale2);
+            const float mnew = fmaxf(m, rows4_max(mx) * scale2);
             const float alpha = exp2_hw(m - mnew);
             l *= alpha;
             m = mnew;
@@ -288,7 +269,7 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
                 s[kb][v] = p;
                 rs += p;
             }
-        l += xsum4(rs);
+        l += rows4_sum(rs);
         // O += P V: for key kb*16 + 4*g4 + v this lane needs V[key][16d + i16], d < DG,
         // which is one interleaved run; block kb+1's runs are read while block kb multiplies
 #pragma unroll
@@ -361,8 +342,7 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_bwd_dq_kernel(float* _
     for (int a = 0; a < 4; a++)
 #pragma unroll
         for (int j = 0; j < DG; j++) dd = fmaf(doreg[a][j], oreg[a][j], dd);
-    dd += __shfl_xor(dd, 16, 64);
-    dd += __shfl_xor(dd, 32, 64);
+    dd = rows4_sum(dd);
     const float D = dd;
     const float L = valid ? lse[((long)b * NH + h) * T + tq] : INFINITY;
     const float L2 = L * LOG2E, scale2 = scale * LOG2E;

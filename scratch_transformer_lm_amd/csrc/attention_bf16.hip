@@ -267,12 +267,11 @@ __global__ __launch_bounds__(NTH, 2) void attn_fwd_bf16_kernel(float* __restrict
                 if (DIAG && kt * TILE + k4 * 16 + 4 * g4 + v > tq) s[k4][v] = -INFINITY;
                 mx = fmaxf(mx, s[k4][v]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         // the reference max moves only when a row's max exceeds it by more than 8 (base 2);
-        // the softmax is the same, and O is rescaled only then
-        const float mnew = fmaxf(m, mx * scale2);
-        if (__any(mnew > m + 8.0f)) {
+        // the softmax is the same, and O is rescaled only then.  A row's max does so exactly
+        // when one of its four lanes' partial maxima does, so the row max is formed only then.
+        if (__any(mx * scale2 > m + 8.0f)) {
+            const float mnew = fmaxf(m, rows4_max(mx) * scale2);
             const float alpha = exp2_hw(m - mnew);
             l *= alpha;
             m = mnew;
@@ -292,9 +291,7 @@ __global__ __launch_bounds__(NTH, 2) void attn_fwd_bf16_kernel(float* __restrict
                 s[k4][v] = p;
                 rs += p;
             }
-        rs += __shfl_xor(rs, 16, 64);
-        rs += __shfl_xor(rs, 32, 64);
-        l += rs;
+        l += rows4_sum(rs);
         // O += P V over key pairs (2P, 2P+1): P as hi + lo
 #pragma unroll
         for (int P = 0; P < 2; P++) {
@@ -372,8 +369,7 @@ GPT2_DEV void write_grad(const f32x4 (&x)[DG], float* out, uint16_t* outb, long 
 #pragma unroll
             for (int v = 0; v < 4; v++)
                 if (row0 + 4 * g4 + v < T) sum += x[d][v];
-            sum += __shfl_xor(sum, 16, 64);
-            sum += __shfl_xor(sum, 32, 64);
+            sum = rows4_sum(sum);
             if (g4 == 0) red[wave * 16 * DG + 16 * d + i16] = sum;
         }
         __syncthreads();
@@ -422,8 +418,7 @@ __global__ __launch_bounds__(NTH, 2) void attn_bwd_dq_bf16_kernel(
                 dd = fmaf(bf16_float((w[e / 2] >> (16 * (e & 1))) & 0xffffu), orow[32 * ks + 8 * g4 + e], dd);
         }
     }
-    dd += __shfl_xor(dd, 16, 64);
-    dd += __shfl_xor(dd, 32, 64);
+    dd = rows4_sum(dd);
     const float D = valid ? dd : 0.f;
     const float L2 = (valid ? lse[((long)b * NH + h) * T + tq] : INFINITY) * LOG2E, scale2 = scale * LOG2E;
     if (g4 == 0 && valid) delta[((long)b * NH + h) * T + tq] = D;

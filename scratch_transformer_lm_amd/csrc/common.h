@@ -10,16 +10,73 @@ namespace gpt2k {
 
 constexpr int WAVE = 64;
 
+// Cross-lane reductions on the VALU (DPP and the gfx950 permlane swaps, no LDS round trip),
+// each in the tree of the shuffle-xor steps it stands for, so sums are bitwise the same:
+//  rows4_*: over lanes i, i^16, i^32, i^48.  v_permlane16_swap exchanges rows 1, 3 of its
+//    first operand with rows 0, 2 of its second, v_permlane32_swap the upper half of the
+//    first with the lower half of the second; with both operands the value, each lane holds
+//    its own and its partner's value: (r0 + r1) + (r2 + r3) in every lane.
+//  row16_*: over the 16 lanes of each row, xor 1, 2, 4, 8.  After the two quad steps the
+//    values are equal within each quad, after the half-row mirror within each 8 lanes, so
+//    the mirrors pair the same values as xor 4 and xor 8.
+//  wave_*: xor 32 and 16 as permlane swaps, then 8, 4, 2, 1 as row rotations: after the
+//    xor-8 step the values are equal within each residue class mod 8 of the lane, and
+//    rotating by 4, 2, 1 reaches the class that xor 4, 2, 1 would.
+template <int CTRL>
+GPT2_DEV float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+constexpr int DPP_ROR1 = 0x121, DPP_ROR2 = 0x122, DPP_ROR4 = 0x124, DPP_ROR8 = 0x128;
+GPT2_DEV float xpair16_a(float x, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    b = __uint_as_float(r[1]);
+    return __uint_as_float(r[0]);
+}
+GPT2_DEV float xpair32_a(float x, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    b = __uint_as_float(r[1]);
+    return __uint_as_float(r[0]);
+}
+GPT2_DEV float rows4_sum(float x) {
+    float b;
+    x = xpair16_a(x, b) + b;
+    x = xpair32_a(x, b) + b;
+    return x;
+}
+GPT2_DEV float rows4_max(float x) {
+    float b;
+    x = fmaxf(xpair16_a(x, b), b);
+    x = fmaxf(xpair32_a(x, b), b);
+    return x;
+}
+GPT2_DEV float row16_sum(float x) {
+    x += dpp_f<DPP_XOR1>(x);
+    x += dpp_f<DPP_XOR2>(x);
+    x += dpp_f<DPP_HALF_MIRROR>(x);
+    return x + dpp_f<DPP_MIRROR>(x);
+}
+GPT2_DEV float row16_max(float x) {
+    x = fmaxf(x, dpp_f<DPP_XOR1>(x));
+    x = fmaxf(x, dpp_f<DPP_XOR2>(x));
+    x = fmaxf(x, dpp_f<DPP_HALF_MIRROR>(x));
+    return fmaxf(x, dpp_f<DPP_MIRROR>(x));
+}
+
 GPT2_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-    return v;
+    v = rows4_sum(v);
+    v += dpp_f<DPP_ROR8>(v);
+    v += dpp_f<DPP_ROR4>(v);
+    v += dpp_f<DPP_ROR2>(v);
+    return v + dpp_f<DPP_ROR1>(v);
 }
 
 GPT2_DEV float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-    return v;
+    v = rows4_max(v);
+    v = fmaxf(v, dpp_f<DPP_ROR8>(v));
+    v = fmaxf(v, dpp_f<DPP_ROR4>(v));
+    v = fmaxf(v, dpp_f<DPP_ROR2>(v));
+    return fmaxf(v, dpp_f<DPP_ROR1>(v));
 }
 
 GPT2_DEV double wave_sum_d(double v) {

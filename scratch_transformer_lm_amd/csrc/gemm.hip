@@ -250,16 +250,14 @@ GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0,
 #pragma unroll
             for (int b = 0; b < NB; b++)
                 if (inside(b, v)) m = fmaxf(m, in[b][v] * LOG2E_EPI);
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            m = row16_max(m);
             float sum = 0.f;
             if (m > -INFINITY) {
 #pragma unroll
                 for (int b = 0; b < NB; b++)
                     if (inside(b, v)) sum += __builtin_amdgcn_exp2f(fmaf(in[b][v], LOG2E_EPI, -m));
             }
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+            sum = row16_sum(sum);
             if ((lane & 15) == v) {
                 pm = m;
                 ps = sum;
@@ -300,8 +298,7 @@ GPT2_DEV void epi_store(const Params& p, const f32x4 (&acc)[NB], int m0, int n0,
 #pragma unroll
                 for (int v = 0; v < 4; v++)
                     if (inside(b, v)) t += in[b][v];
-                t += __shfl_xor(t, 16, 64);
-                t += __shfl_xor(t, 32, 64);
+                t = rows4_sum(t);
                 if ((lane >> 4) == 0 && 16 * slice < p.M && (!CHECK || c0 + 16 * b < p.N))
                     p.csum[(long)slice * p.N + c0 + 16 * b] = t;
             }
@@ -893,8 +890,7 @@ GPT2_DEV void gemm_body(const Params& p) {
 #pragma unroll
             for (int a = 0; a < 4; a++) {
                 float s = bsum[a];
-                s += __shfl_xor(s, 16, 64);
-                s += __shfl_xor(s, 32, 64);
+                s = rows4_sum(s);
                 const int row = wm + 16 * a + li;
                 if (grp == 0) {
                     if (full) {
