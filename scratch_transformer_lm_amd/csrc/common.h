@@ -19,9 +19,10 @@ constexpr int WAVE = 64;
 //  row16_*: over the 16 lanes of each row, xor 1, 2, 4, 8.  After the two quad steps the
 //    values are equal within each quad, after the half-row mirror within each 8 lanes, so
 //    the mirrors pair the same values as xor 4 and xor 8.
-//  wave_*: xor 32 and 16 as permlane swaps, then 8, 4, 2, 1 as row rotations: after the
-//    xor-8 step the values are equal within each residue class mod 8 of the lane, and
-//    rotating by 4, 2, 1 reaches the class that xor 4, 2, 1 would.
+//  wave_*: xor 32 then 16 as permlane swaps (v_permlane32_swap pairs lanes i and i^32 the
+//    same way), then 8, 4, 2, 1 as row rotations: after the xor-8 step the values are equal
+//    within each residue class mod 8 of the lane, and rotating by 4, 2, 1 reaches the class
+//    that xor 4, 2, 1 would.
 template <int CTRL>
 GPT2_DEV float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -64,7 +65,9 @@ GPT2_DEV float row16_max(float x) {
 }
 
 GPT2_DEV float wave_sum(float v) {
-    v = rows4_sum(v);
+    float b;
+    v = xpair32_a(v, b) + b;
+    v = xpair16_a(v, b) + b;
     v += dpp_f<DPP_ROR8>(v);
     v += dpp_f<DPP_ROR4>(v);
     v += dpp_f<DPP_ROR2>(v);
@@ -72,7 +75,9 @@ GPT2_DEV float wave_sum(float v) {
 }
 
 GPT2_DEV float wave_max(float v) {
-    v = rows4_max(v);
+    float b;
+    v = fmaxf(xpair32_a(v, b), b);
+    v = fmaxf(xpair16_a(v, b), b);
     v = fmaxf(v, dpp_f<DPP_ROR8>(v));
     v = fmaxf(v, dpp_f<DPP_ROR4>(v));
     v = fmaxf(v, dpp_f<DPP_ROR2>(v));
