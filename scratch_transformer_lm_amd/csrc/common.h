@@ -90,24 +90,27 @@ GPT2_DEV double wave_sum_d(double v) {
     return v;
 }
 
-// Tanh-form GELU and its derivative (same constants as the model definition).
+// Tanh-form GELU and its derivative (same constants as the model definition),
+//   GELU(u) = 0.5 u (1 + tanh z),  z = K0 (u + K1 u^3),
+// evaluated through the logistic form 0.5 (1 + tanh z) = s = 1 / (1 + e^{-2z}):
+// GELU(u) = u s and GELU'(u) = s + u s (1 - s) 2 dz/du, with the factor -2 log2 e folded
+// into the constants of one base-2 exponential, on the hardware transcendental unit
+// (v_exp_f32, v_rcp_f32: a few ulp).  e^{-2z} overflowing to +inf gives s = 0 exactly,
+// underflowing to 0 gives s = 1.
 constexpr float GELU_K0 = 0.7978845608028654f;  // sqrt(2/pi)
 constexpr float GELU_K1 = 0.044715f;
-
-// tanh z = 1 - 2 / (e^{2z} + 1), with e^x and 1/x on the hardware transcendental unit
-// (v_exp_f32, v_rcp_f32: a few ulp; e^{2z} overflowing to +inf still gives exactly 1).
-GPT2_DEV float tanh_fast(float z) { return 1.0f - 2.0f * __builtin_amdgcn_rcpf(__expf(2.0f * z) + 1.0f); }
-
-GPT2_DEV float gelu_f(float u) {
-    float z = GELU_K0 * (u + GELU_K1 * u * u * u);
-    return 0.5f * u * (1.0f + tanh_fast(z));
+constexpr float GELU_C0 = -2.0f * 1.4426950408889634f * GELU_K0;            // u^1 term of -2 z log2 e
+constexpr float GELU_C1 = -2.0f * 1.4426950408889634f * GELU_K0 * GELU_K1;  // u^3 term
+GPT2_DEV float gelu_s(float u, float w) {  // w = u^2
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * fmaf(GELU_C1, w, GELU_C0)));
 }
+GPT2_DEV float gelu_f(float u) { return u * gelu_s(u, u * u); }
 
 GPT2_DEV float gelu_grad_f(float u) {
-    float z = GELU_K0 * (u + GELU_K1 * u * u * u);
-    float th = tanh_fast(z);
-    float dz = GELU_K0 * (1.0f + 3.0f * GELU_K1 * u * u);
-    return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
+    const float w = u * u;
+    const float s = gelu_s(u, w);
+    const float dz2 = fmaf(6.0f * GELU_K0 * GELU_K1, w, 2.0f * GELU_K0);  // 2 dz/du
+    return fmaf(u * s, (1.0f - s) * dz2, s);
 }
 
 // fp32 pair -> packed bfloat16 (low half = lo), round to nearest, ties to even: one
