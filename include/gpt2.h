@@ -163,8 +163,9 @@ int gpt2_update(gpt2* model, float lr, float beta1, float beta2, float eps, floa
  * layer's parameters are updated as soon as its gradients are final (after its
  * LayerNorm backward and weight-gradient GEMMs), on a third stream the handle owns (the
  * update stream, next to the main and weight-gradient streams), while the gradients of
- * the layers below are still being formed; wte, wpe and the final norm are
- * updated last.  Gradients are left in `grads` as gpt2_backward leaves them.
+ * the layers below are still being formed; the layers' LayerNorm weight and bias
+ * gradients are also summed there, just before their update.  wte, wpe and the final
+ * norm are updated last.  Gradients are left in `grads` as gpt2_backward leaves them.
  * Returns GPT2_OK, GPT2_EINVAL for a null model, GPT2_ESTATE without a forward with
  * targets or with t < 1, GPT2_EDEVICE on a HIP error. */
 int gpt2_backward_update(gpt2* model, float lr, float beta1, float beta2, float eps, float weight_decay, int t);

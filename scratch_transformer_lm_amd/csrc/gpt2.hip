@@ -73,14 +73,21 @@ enum { BS_DRES, BS_DFCH, BS_DQKV, BS_DLOG, BS_HDO, BS_HDOT, NBS };
 
 size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
 
+// Build option: with the fused backward + update on two backward streams, each layer's
+// LayerNorm dw/db reductions run on the update stream (which applies them) instead of the
+// main chain, from partial rows of their own (measured at the 124M shape: 54.15-54.28
+// against 54.39-54.50 ms per step; 2 L partial-row buffers, 79 MB there).
+#ifndef GPT2_LN_REDUCE_ASYNC
+#define GPT2_LN_REDUCE_ASYNC 1
+#endif
 struct Layout {
     size_t BT, Vp;
     ActInfo a[GPT2_NUM_ACTS];
     size_t tok_in, tok_tgt;  // int32 arrays inside acts (offset in 4-byte words)
     size_t n_acts;
     // grad_scratch
-    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, sample, rope, lsep,
-        n_scratch;
+    size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, lnpart, sample,
+        rope, lsep, n_scratch;
     // mixed precision: offsets (floats) of the bf16 arrays, per-layer strides (bf16 elements)
     size_t ba[NBA], ba_l[NBA], bs[NBS], bpart;
 };
@@ -164,6 +171,9 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     y.n_partial = np;
     y.partial = take(np);
     y.partial_w = take(gemm_partial_floats());  // split tiles of the weight-gradient stream
+    // each layer's two LayerNorm backwards' partial rows, when their dw/db reductions run on
+    // the update stream
+    y.lnpart = GPT2_LN_REDUCE_ASYNC ? take(2 * L * layernorm_partial_floats((int)BT, (int)C)) : 0;
     y.sample = take(3 * BT);                      // sampling requests: rows, coins, tokens
     y.rope = take(rope_table_floats(c->max_seq_len, (int)(C / NH)));  // rotary variant's (cos, sin) table
     y.lsep = take(lse_partial_floats((int)BT, (int)V));  // the LM head's per-tile log-sum-exp partials
@@ -188,7 +198,7 @@ struct gpt2 {
     // ordered against the main chain by events (see backward_impl).
     hipStream_t st_w;
     hipStream_t st_u;  // per-layer AdamW of gpt2_backward_update
-    hipEvent_t ev[13];
+    hipEvent_t ev[14];  // [13]: a LayerNorm backward's partial rows are written
     int backward_streams;  // 2: weight gradients on st_w; 1: everything on st
     int variant;           // GPT2_VARIANT_* bits (Llama-style layers)
     gpt2_buffers buf;
@@ -284,10 +294,10 @@ hipError_t norm_fwd(gpt2* g, float* y, float* mean, float* rstd, const float* x,
 
 hipError_t norm_bwd(gpt2* g, float* dx, float* dw, float* db, const float* dy, const float* x, const float* w,
                     const float* mean, const float* rstd, int N, int C, bool acc_dx, bool acc_dw, float* part,
-                    hipStream_t st) {
+                    hipStream_t st, hipStream_t st_red = nullptr, hipEvent_t ev = nullptr) {
     if (g->variant & GPT2_VARIANT_RMSNORM)
-        return rmsnorm_backward(dx, dw, dy, x, w, mean, rstd, N, C, acc_dx, acc_dw, part, st);
-    return layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, N, C, acc_dx, acc_dw, part, st);
+        return rmsnorm_backward(dx, dw, dy, x, w, mean, rstd, N, C, acc_dx, acc_dw, part, st, st_red, ev);
+    return layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, N, C, acc_dx, acc_dw, part, st, st_red, ev);
 }
 
 bool rope_on(const gpt2* g) { return (g->variant & GPT2_VARIANT_ROPE) != 0; }
@@ -483,6 +493,12 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     enum { EV_DRES_A, EV_DFCH, EV_DRES_B, EV_DQKV, EV_W_FCPROJ, EV_W_FC, EV_W_ATTPROJ, EV_W_QKV, EV_LM, EV_W_LM, EV_LN1,
            EV_W_END, EV_U_END };
     hipStream_t su = g->backward_streams == 2 ? g->st_u : st;
+    // the layers' LayerNorm dw/db reductions on the update stream, each from its own
+    // partial rows (the update stream applies them after its layer's weight gradients)
+    const bool lnred = GPT2_LN_REDUCE_ASYNC && up != nullptr && su != st;
+    auto lnpart = [&](int i) {
+        return S(g, g->lay.lnpart) + (size_t)i * layernorm_partial_floats((int)BT, (int)C);
+    };
     auto mark = [&](int e, hipStream_t s) { return hipEventRecord(g->ev[e], s); };
     auto after = [&](hipStream_t s, int e) { return hipStreamWaitEvent(s, g->ev[e], 0); };
     // Mixed precision: every GEMM below multiplies bf16 copies.  dlogits is written once
@@ -573,7 +589,7 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         HIPCHK(g, after(st, EV_W_FCPROJ));  // dres is about to change
         HIPCHK(g, norm_bwd(g, dres, G(g, P_LN2W) + l * C, G(g, P_LN2B) + l * C, dln, A(g, GPT2_ACT_RESIDUAL2, l),
                            P(g, P_LN2W) + l * C, A(g, GPT2_ACT_LN2_MEAN, l), A(g, GPT2_ACT_LN2_RSTD, l), BT, C, true,
-                           true, part, st));
+                           true, lnred ? lnpart(2 * l) : part, st, lnred ? su : nullptr, g->ev[13]));
         // Attention projection: residual2 = residual + atty . Wa^T + ba.
         if (bf) HIPCHK(g, grad_copies(dres, C, dresb, 2));
         HIPCHK(g, mark(EV_DRES_B, st));
@@ -613,7 +629,8 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         HIPCHK(g, dgrad(dln, dqkv, dqkvb, 3 * C, P(g, P_QKVW) + (size_t)l * 3 * C * C, BA(g, BWT_Q, l), C, nullptr));
         HIPCHK(g, after(st, EV_W_ATTPROJ));  // dres is about to change
         HIPCHK(g, norm_bwd(g, dres, G(g, P_LN1W) + l * C, G(g, P_LN1B) + l * C, dln, residual, P(g, P_LN1W) + l * C,
-                           A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true, part, st));
+                           A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), BT, C, true, true,
+                           lnred ? lnpart(2 * l + 1) : part, st, lnred ? su : nullptr, g->ev[13]));
         if (up) {
             // layer l's gradients are final once its LayerNorm backwards (main stream, just
             // queued) and its weight gradients (last: the qkv wgrad on the second stream)
@@ -721,7 +738,7 @@ int gpt2_build_variant(gpt2** out, const gpt2_config* cfg, int B, int T, const g
     bool ok = hipStreamCreateWithFlags(&g->st_w, hipStreamNonBlocking) == hipSuccess;
     ok = ok && hipStreamCreateWithFlags(&g->st_u, hipStreamNonBlocking) == hipSuccess;
     int nev = 0;
-    for (; ok && nev < 13; nev++) ok = hipEventCreateWithFlags(&g->ev[nev], hipEventDisableTiming) == hipSuccess;
+    for (; ok && nev < 14; nev++) ok = hipEventCreateWithFlags(&g->ev[nev], hipEventDisableTiming) == hipSuccess;
     if (ok) {
         ok = fill_zero(b.grads, g->nparams, g->st) == hipSuccess && fill_zero(b.m, g->nparams, g->st) == hipSuccess &&
              fill_zero(b.v, g->nparams, g->st) == hipSuccess;

@@ -109,10 +109,13 @@ hipError_t layernorm_forward(float* y, float* mean, float* rstd, const float* x,
 // dx (+)= ..., dw/db (+)= ...; accumulate flags choose += or =.  partial needs
 // layernorm_partial_floats(N, C) floats.
 size_t layernorm_partial_floats(int N, int C);
+// st_red (with ev): the dw/db reduction of the partial rows runs on that stream after ev,
+// recorded on st once the partial rows are written (the caller keeps partial untouched
+// until st_red has run it).
 hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x,
                               const float* w, const float* mean, const float* rstd, int N, int C,
                               bool accumulate_dx, bool accumulate_dwdb, float* partial,
-                              hipStream_t st);
+                              hipStream_t st, hipStream_t st_red = nullptr, hipEvent_t ev = nullptr);
 // RMSNorm (no mean subtraction, no bias): y = x r w, r = 1/sqrt(mean(x^2) + eps); mean[]
 // is written as 0 so the LayerNorm activation layout still holds.  The backward adds
 // only dw (same partial scratch as layernorm_backward, at most that size).
@@ -120,7 +123,8 @@ hipError_t rmsnorm_forward(float* y, float* mean, float* rstd, const float* x, c
                            float eps, hipStream_t st, uint16_t* yb = nullptr);
 hipError_t rmsnorm_backward(float* dx, float* dw, const float* dy, const float* x, const float* w,
                             const float* mean, const float* rstd, int N, int C, bool accumulate_dx,
-                            bool accumulate_dw, float* partial, hipStream_t st);
+                            bool accumulate_dw, float* partial, hipStream_t st, hipStream_t st_red = nullptr,
+                            hipEvent_t ev = nullptr);
 
 // ---- embedding (encoder.hip) --------------------------------------------------------
 // out[b,t] = wte[tok[b,t]] + wpe[t]; wpe may be null (no position rows).

@@ -271,7 +271,8 @@ hipError_t norm_forward(float* y, float* mean, float* rstd, const float* x, cons
 template <bool RMS>
 hipError_t norm_backward(float* dx, float* dw, float* db, const float* dy, const float* x, const float* w,
                          const float* mean, const float* rstd, int N, int C, bool accumulate_dx,
-                         bool accumulate_dwdb, float* partial, hipStream_t st) {
+                         bool accumulate_dwdb, float* partial, hipStream_t st, hipStream_t st_red = nullptr,
+                         hipEvent_t ev = nullptr) {
     if (C % 4 || C > 4096 || N < 0) return hipErrorInvalidValue;
     if (N == 0) {
         if (!accumulate_dwdb) {
@@ -301,9 +302,15 @@ hipError_t norm_backward(float* dx, float* dw, float* db, const float* dy, const
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    ProfScope ps2(st, "reduce_rows_kernel", 0.0,
+    hipStream_t sr = st;
+    if (st_red && ev && st_red != st) {
+        if ((e = hipEventRecord(ev, st)) != hipSuccess || (e = hipStreamWaitEvent(st_red, ev, 0)) != hipSuccess)
+            return e;
+        sr = st_red;
+    }
+    ProfScope ps2(sr, "reduce_rows_kernel", 0.0,
                   4.0 * ((double)G * PARTS * C + (double)PARTS * C * (accumulate_dwdb ? 2 : 1)));
-    hipLaunchKernelGGL(reduce_rows_kernel, dim3((PARTS * C + 15) / 16), dim3(256), 0, st, dw, db, C,
+    hipLaunchKernelGGL(reduce_rows_kernel, dim3((PARTS * C + 15) / 16), dim3(256), 0, sr, dw, db, C,
                        (const float*)partial, G, PARTS * C, (int)accumulate_dwdb);
     return hipGetLastError();
 }
@@ -325,16 +332,16 @@ size_t layernorm_partial_floats(int N, int C) { return (size_t)ln_blocks(N) * 2 
 hipError_t layernorm_backward(float* dx, float* dw, float* db, const float* dy, const float* x,
                               const float* w, const float* mean, const float* rstd, int N, int C,
                               bool accumulate_dx, bool accumulate_dwdb, float* partial,
-                              hipStream_t st) {
+                              hipStream_t st, hipStream_t st_red, hipEvent_t ev) {
     return norm_backward<false>(dx, dw, db, dy, x, w, mean, rstd, N, C, accumulate_dx, accumulate_dwdb, partial,
-                                st);
+                                st, st_red, ev);
 }
 
 hipError_t rmsnorm_backward(float* dx, float* dw, const float* dy, const float* x, const float* w,
                             const float* mean, const float* rstd, int N, int C, bool accumulate_dx,
-                            bool accumulate_dw, float* partial, hipStream_t st) {
+                            bool accumulate_dw, float* partial, hipStream_t st, hipStream_t st_red, hipEvent_t ev) {
     return norm_backward<true>(dx, dw, nullptr, dy, x, w, mean, rstd, N, C, accumulate_dx, accumulate_dw, partial,
-                               st);
+                               st, st_red, ev);
 }
 
 }  // namespace gpt2k
