@@ -171,9 +171,9 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     y.n_partial = np;
     y.partial = take(np);
     y.partial_w = take(gemm_partial_floats());  // split tiles of the weight-gradient stream
-    // each layer's two LayerNorm backwards' partial rows, when their dw/db reductions run on
-    // the update stream
-    y.lnpart = GPT2_LN_REDUCE_ASYNC ? take(2 * L * layernorm_partial_floats((int)BT, (int)C)) : 0;
+    // each LayerNorm backward's partial rows (two per layer, then the final norm's), when
+    // their dw/db reductions run off the main stream
+    y.lnpart = GPT2_LN_REDUCE_ASYNC ? take((2 * L + 1) * layernorm_partial_floats((int)BT, (int)C)) : 0;
     y.sample = take(3 * BT);                      // sampling requests: rows, coins, tokens
     y.rope = take(rope_table_floats(c->max_seq_len, (int)(C / NH)));  // rotary variant's (cos, sin) table
     y.lsep = take(lse_partial_floats((int)BT, (int)V));  // the LM head's per-tile log-sum-exp partials
@@ -475,11 +475,12 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     float* logits = A(g, GPT2_ACT_LOGITS);
 
     // wte receives rows by token twice (targets' lnf rows below, inputs' residual-gradient
-    // rows at the end): both token lists are sorted once, up front
+    // rows at the end): both token lists are sorted once, up front, on the second stream
+    // (the main chain needs neither; that stream's first user is the targets' scatter, and
+    // the main stream's input scatter comes after it waits for that stream's end)
     int* wk_in = reinterpret_cast<int*>(S(g, g->lay.enc_work));
     int* wk_tgt = reinterpret_cast<int*>(S(g, g->lay.enc_work_tgt));
     const bool sorted = embedding_sortable(BT, V);
-    if (sorted) HIPCHK(g, sort_token_lists(wk_in, tok_in(g), wk_tgt, tok_tgt(g), BT, V, st));
 
     // LM head (tied): dlnf = dlogits . wte;  dwte += dlogits^T . lnf, where
     // dlogits = (softmax(logits) - onehot(target)) / (B*T) is formed as the GEMMs load the
@@ -539,6 +540,7 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
                                  st));
         HIPCHK(g, mark(EV_LM, st));
         HIPCHK(g, after(sw, EV_LM));
+        if (sorted) HIPCHK(g, sort_token_lists(wk_in, tok_in(g), wk_tgt, tok_tgt(g), BT, V, sw));
         HIPCHK(g, gemm_bf16_rows(G(g, P_WTE), C, BS(g, BS_DLOG), Vp, BA(g, BA_LNF), C, V, C, BT, part_w, sw));
         HIPCHK(g, mark(EV_W_LM, sw));
         HIPCHK(g, gemm_bf16(BF16_STORE, dln, C, BS(g, BS_DLOG), Vp, BA(g, BWT_WTE), Vp, BT, C, (int)Vp, nullptr, nullptr,
@@ -546,6 +548,7 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
     } else {
         HIPCHK(g, mark(EV_LM, st));
         HIPCHK(g, after(sw, EV_LM));
+        if (sorted) HIPCHK(g, sort_token_lists(wk_in, tok_in(g), wk_tgt, tok_tgt(g), BT, V, sw));
         HIPCHK(g, linear_wgrad(G(g, P_WTE), nullptr, logits, Vp, A(g, GPT2_ACT_LNF), V, C, BT, part_w, sw, &xo));
         // the one-hot part of dlogits: dwte[target] -= lnf / BT
         if (sorted) HIPCHK(g, scatter_sorted(G(g, P_WTE), C, A(g, GPT2_ACT_LNF), C, -xo.scale, wk_tgt, BT, sw));
@@ -553,8 +556,11 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
         HIPCHK(g, mark(EV_W_LM, sw));
         HIPCHK(g, linear_dgrad(dln, logits, Vp, P(g, P_WTE), nullptr, BT, C, V, part, st, &xo));
     }
+    // (the final norm's dw/db are only read by the last update, on the main stream after it
+    // waits for the second stream's end: their reduction goes to the second stream)
     HIPCHK(g, norm_bwd(g, dres, G(g, P_LNFW), G(g, P_LNFB), dln, A(g, GPT2_ACT_RESIDUAL3, L - 1), P(g, P_LNFW),
-                       A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true, part, st));
+                       A(g, GPT2_ACT_LNF_MEAN), A(g, GPT2_ACT_LNF_RSTD), BT, C, false, true,
+                       lnred ? lnpart(2 * L) : part, st, lnred ? sw : nullptr, g->ev[13]));
     // Per layer, the weight gradients (dW += dY^T X, db) need only that layer's output
     // gradient, so they run on the handle's second stream and overlap the main chain
     // (dgrads, attention, LayerNorm).  Events order the two: the second stream waits for
