@@ -28,6 +28,12 @@ constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
 #define LN_BWD_MAX_BLOCKS 512
 #endif
 constexpr int LN_MAX_BLOCKS = LN_BWD_MAX_BLOCKS;
+// Waves (rows in flight) per block of the backward (8 measured no faster at 8192 x 768:
+// 21.0 against 20.8 us per launch).
+#ifndef LN_BWD_WAVES
+#define LN_BWD_WAVES 4
+#endif
+constexpr int BWD_WAVES = LN_BWD_WAVES;
 
 // Rows per wave of the forward: a wave loads all of its rows before reducing any, so
 // more bytes are in flight per wave and fewer blocks are dispatched.
@@ -103,11 +109,11 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ y, uint
 // dx = rstd * (g - mean(g) - xh * mean(g*xh)), g = w*dy, xh = (x-mean)*rstd.
 // Each block also leaves one partial row [dw | db] (2C floats) in `partial`.
 template <int VPL, bool RMS>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, float* __restrict__ partial,
+__global__ __launch_bounds__(64 * BWD_WAVES) void ln_bwd_kernel(float* __restrict__ dx, float* __restrict__ partial,
                                                      const float* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ w, const float* __restrict__ mean,
                                                      const float* __restrict__ rstd, int N, int C, int accumulate) {
-    extern __shared__ float red[];  // [4][C]
+    extern __shared__ float red[];  // [BWD_WAVES][C]
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int C4 = C >> 2;
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
         pdw[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         pdb[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int row = blockIdx.x * ROWS_PER_BLOCK + wave; row < N; row += gridDim.x * ROWS_PER_BLOCK) {
+    for (int row = blockIdx.x * BWD_WAVES + wave; row < N; row += gridDim.x * BWD_WAVES) {
         const float4* xr = reinterpret_cast<const float4*>(x + (long)row * C);
         const float4* dr = reinterpret_cast<const float4*>(dy + (long)row * C);
         float4* o = reinterpret_cast<float4*>(dx + (long)row * C);
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
             }
         }
     }
-    // Combine the 4 waves' partials in wave order, then write the block's partial row
+    // Combine the waves' partials in wave order, then write the block's partial row
     // ([dw | db], or [dw] for RMSNorm).
     constexpr int PARTS = RMS ? 1 : 2;
     for (int part = 0; part < PARTS; part++) {
@@ -188,7 +194,9 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
         }
         __syncthreads();
         for (int c = threadIdx.x; c < C; c += blockDim.x) {
-            const float s = ((red[c] + red[C + c]) + red[2 * C + c]) + red[3 * C + c];
+            float s = red[c];
+#pragma unroll
+            for (int q = 1; q < BWD_WAVES; q++) s += red[q * C + c];
             partial[(long)blockIdx.x * PARTS * C + part * C + c] = s;
         }
         __syncthreads();
@@ -197,15 +205,23 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dx, flo
 
 // out[w] (+)= sum_r part[r*W + w] over R rows (W % 4 == 0).  A block covers 16 columns as
 // 4 float4 columns x 64 row groups (so the grid has W/16 blocks: 96 for LayerNorm's
-// [dgamma | dbeta] rows at C = 768); group j adds rows j, j+64, ... in order, then the 64
-// group sums are added in group order.  Columns w < W1 go to out_lo[w], the rest to
+// [dgamma | dbeta] rows at C = 768); group j adds rows j, j+64, ... in order.  The 64
+// group sums of a column are then added as a fixed tree: within a wave (16 groups: lane
+// bits 2..5) by row rotations of 4 and 8 lanes and the two permlane swaps, then the four
+// waves' sums in wave order through LDS.  Columns w < W1 go to out_lo[w], the rest to
 // out_hi[w - W1].
 constexpr int RR_GROUPS = 64;
+GPT2_DEV float rr_wave_sum(float x) {
+    x += dpp_f<DPP_ROR4>(x);  // lanes i, i+4 of each 16-lane row (same column, bits 0..1)
+    x += dpp_f<DPP_ROR8>(x);  // ... and i+8, i+12
+    return rows4_sum(x);      // ... and the same lane of the other three rows
+}
 __global__ __launch_bounds__(256) void reduce_rows_kernel(float* out_lo, float* out_hi, int W1,
                                                           const float* __restrict__ part, int R, int W,
                                                           int accumulate) {
-    __shared__ float4 s[RR_GROUPS][4];
+    __shared__ float4 s[4][4];
     const int c4 = threadIdx.x & 3, grp = threadIdx.x >> 2;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int w = blockIdx.x * 16 + c4 * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (w < W) {
@@ -218,11 +234,16 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(float* out_lo, float* 
             acc.w += v.w;
         }
     }
-    s[grp][c4] = acc;
+    acc.x = rr_wave_sum(acc.x);
+    acc.y = rr_wave_sum(acc.y);
+    acc.z = rr_wave_sum(acc.z);
+    acc.w = rr_wave_sum(acc.w);
+    if (lane < 4) s[wave][c4] = acc;
     __syncthreads();
-    if (grp == 0 && w < W) {
+    if (threadIdx.x < 4 && w < W) {
         float4 tot = s[0][c4];
-        for (int j = 1; j < RR_GROUPS; j++) {
+#pragma unroll
+        for (int j = 1; j < 4; j++) {
             const float4 v = s[j][c4];
             tot.x += v.x;
             tot.y += v.y;
@@ -238,7 +259,7 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(float* out_lo, float* 
     }
 }
 
-int ln_blocks(int N) { return std::min((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, LN_MAX_BLOCKS); }
+int ln_blocks(int N) { return std::min((N + BWD_WAVES - 1) / BWD_WAVES, LN_MAX_BLOCKS); }
 
 }  // namespace
 
@@ -285,11 +306,11 @@ hipError_t norm_backward(float* dx, float* dw, float* db, const float* dy, const
     constexpr int PARTS = RMS ? 1 : 2;
     const int vpl = (C / 4 + 63) / 64;
     const int G = ln_blocks(N);
-    const size_t lds = (size_t)4 * C * sizeof(float);
+    const size_t lds = (size_t)BWD_WAVES * C * sizeof(float);
     {
         ProfScope ps(st, RMS ? "rms_bwd_kernel" : "ln_bwd_kernel", 0.0,
                      4.0 * ((double)N * C * (accumulate_dx ? 4 : 3) + 2.0 * N + C + (double)PARTS * G * C));
-#define LN_BWD(V) hipLaunchKernelGGL((ln_bwd_kernel<V, RMS>), dim3(G), dim3(256), lds, st, dx, partial, dy, x, w, mean, rstd, N, C, (int)accumulate_dx)
+#define LN_BWD(V) hipLaunchKernelGGL((ln_bwd_kernel<V, RMS>), dim3(G), dim3(64 * BWD_WAVES), lds, st, dx, partial, dy, x, w, mean, rstd, N, C, (int)accumulate_dx)
         switch (vpl) {
             case 1: LN_BWD(1); break;
             case 2: LN_BWD(2); break;
