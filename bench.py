@@ -103,7 +103,8 @@ def breakdown(kernels, steps):
     out = []
     for k in sorted(kernels, key=lambda e: -e["ms"]):
         avg_s = k["ms"] / k["launches"] / 1e3
-        e = dict(name=k["name"], ms_per_step=k["ms"] / steps, launches_per_step=k["launches"] / steps)
+        e = dict(name=k["name"], ms_per_step=k["ms"] / steps, launches_per_step=k["launches"] / steps,
+                 alg_flops_per_launch=k["flops"] / k["launches"], alg_bytes_per_launch=k["bytes"] / k["launches"])
         if k["flops"] > 0:
             e["tflops"] = k["flops"] / k["launches"] / avg_s / 1e12
             e["frac_mfma"] = e["tflops"] * 1e12 / mfma_peak(k["name"])
@@ -305,6 +306,45 @@ def ceilings(G, torch):
     return res
 
 
+def same_size_copies(G, torch, entries, stream):
+    """For each memory-bound kernel of a breakdown (1 MB or more per launch): the time of a
+    plain float4 copy (the library's probe copy) that reads and writes the kernel's
+    algorithmic bytes per launch in equal halves, timed the same way (one event pair
+    around one launch, best grid of several, best of five launches).  Short launches pay
+    their ramp, drain and event cost whatever they compute, so this is the ceiling a
+    kernel of that size can reach here; the ratio says how close each kernel comes."""
+    out = {}
+    for e in entries:
+        if "gbps" not in e or e["gbps"] <= 0:
+            continue
+        us = e["ms_per_step"] * 1e3 / e["launches_per_step"]
+        nbytes = e["gbps"] * 1e9 * us / 1e6
+        if nbytes < 1e6:
+            continue
+        n = max(4096, int(nbytes / 8) // 4 * 4)
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        G.probe_copy(dst, src, blocks=256, stream=stream)
+        best = None
+        for blocks in (256, 512, 1024, 2048, 4096):
+            blocks = min(blocks, max(1, n // (4 * 1024)))
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                G.probe_copy(dst, src, blocks=blocks, stream=stream)
+                e1.record(stream)
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            t = min(a.elapsed_time(b) for a, b in ts) * 1e3
+            if best is None or t < best:
+                best = t
+        del src, dst
+        out[e["name"]] = dict(bytes_per_launch=8 * n, kernel_us=us, copy_us=best,
+                              copy_frac_hbm=8 * n / (best / 1e6) / PEAK_HBM, kernel_vs_copy=best / us)
+    return out
+
+
 def variant_leg(G, torch, w, stream, params, tx, ty, variant, steps=5):
     """A second model of the same shape in another variant, from the same parameters:
     2 warm-up steps (the second with events on every kernel), `steps` timed steps."""
@@ -496,6 +536,10 @@ def main():
                                    "single-stream step")
     out["kernels"] = breakdown(all_kernels, max(1, args.warmup - 1))
     out["kernels_isolated"] = breakdown(isolated, 1)
+    # Each memory-bound kernel against a plain copy of its own bytes per launch (not in
+    # profiler runs, whose only probe copies are the calibration copies).
+    if not args.step_only:
+        out["memory_kernels_vs_same_size_copy"] = same_size_copies(G, torch, out["kernels_isolated"], stream)
     # Aggregate fractions from the single-stream step, where kernel times do not overlap.
     out["aggregates_isolated"] = aggregates(isolated)
     out["aggregates_isolated"]["note"] = ("GEMM and attention: summed algorithmic flops over summed kernel "

@@ -14,11 +14,13 @@
 // from lane j + 16k, C[i][j] in lane j + 16(i/4), register i%4).  The score tile is
 // computed transposed where that puts the probabilities directly into the A-operand
 // layout of the next product, so P never goes through LDS.  The next K/V (or Q/dO) tile
-// is prefetched into registers while the current one is used.  Forward and dQ keep one
-// LDS copy of each tile (two barriers per tile) so that three blocks fit a CU: with the
-// query tiles' very unequal lengths (1 to T/64 key tiles), 768 block slots schedule the
-// 1536 blocks of the 124M shape almost evenly where 512 slots leave a 9% tail.  dK/dV
-// double-buffers its tiles at two blocks per CU (measured faster there).
+// is prefetched into registers while the current one is used.  dQ keeps one LDS copy of
+// each tile (two barriers per tile) so that three blocks fit a CU: with the query tiles'
+// very unequal lengths (1 to T/64 key tiles), 768 block slots schedule the 1536 blocks of
+// the 124M shape almost evenly where 512 slots leave a 9% tail.  The forward and dK/dV
+// double-buffer their tiles (one barrier per tile) at two blocks per CU, measured faster
+// there (the forward 1.60 -> 1.58 ms per step at the 124M shape; dQ double-buffered is
+// slower, 2.24 -> 2.25 ms).
 //
 // LDS rows are stored head-dimension interleaved: dimension d = 16j + i (i < 16,
 // j < HS/16) sits at position (HS/16) i + j.  A tile is read two ways, and both become
@@ -49,7 +51,7 @@ constexpr int TILE = 64;
 // to fit), and whether the next LDS fragments are read while the current ones multiply
 // (two register buffers) or just before use (one).
 #ifndef ATTN_FWD_OCC
-#define ATTN_FWD_OCC 3
+#define ATTN_FWD_OCC 2
 #endif
 #ifndef ATTN_AHEAD
 #define ATTN_AHEAD 1
@@ -58,6 +60,18 @@ constexpr int TILE = 64;
 // (1), or after the current one is done, straight before it is stored to LDS (0)
 #ifndef ATTN_PREFETCH
 #define ATTN_PREFETCH 1
+#endif
+// forward: K/V tiles double-buffered in LDS (one barrier per tile; the LDS then holds two
+// blocks per CU, so ATTN_FWD_OCC is 2) instead of one copy and two barriers (then 3)
+#ifndef ATTN_FWD_DB
+#define ATTN_FWD_DB 1
+#endif
+// the same for the dQ kernel, and its own blocks per CU
+#ifndef ATTN_DQ_DB
+#define ATTN_DQ_DB 0
+#endif
+#ifndef ATTN_DQ_OCC
+#define ATTN_DQ_OCC 3
 #endif
 constexpr int NFB = ATTN_AHEAD ? 2 : 1;
 GPT2_DEV constexpr int fb(int a) { return ATTN_AHEAD ? (a & 1) : 0; }
@@ -165,8 +179,9 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
                                                        const float* __restrict__ qkv, int B, int T, int C, int NH,
                                                        float scale) {
     constexpr int DG = HS / 16, LD = HS + 4;
-    __shared__ __attribute__((aligned(16))) float Ks[TILE * LD];
-    __shared__ __attribute__((aligned(16))) float Vs[TILE * LD];
+    constexpr int NBUF = ATTN_FWD_DB ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) float Ks[NBUF][TILE * LD];
+    __shared__ __attribute__((aligned(16))) float Vs[NBUF][TILE * LD];
     const int nqt = (T + TILE - 1) / TILE;
     const int bh = blockIdx.x % (B * NH);
     const int qt = nqt - 1 - (int)(blockIdx.x / (B * NH));  // longest rows first
@@ -190,8 +205,8 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
     const int nkt = qt + 1;
     tile_load<HS>(kreg, base + C + h * HS, ld, 0, T);
     tile_load<HS>(vreg, base + 2 * C + h * HS, ld, 0, T);
-    tile_store<HS>(Ks, kreg);
-    tile_store<HS>(Vs, vreg);
+    tile_store<HS>(Ks[0], kreg);
+    tile_store<HS>(Vs[0], vreg);
     __syncthreads();
     // one key tile; only the diagonal tile (kt == qt) has keys after the query
     auto step = [&](int kt, auto diag_tag) {
@@ -200,8 +215,9 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
             tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
             tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
         }
-        const float* K = Ks;
-        const float* V = Vs;
+        const int cur = ATTN_FWD_DB ? (kt & 1) : 0;
+        const float* K = Ks[cur];
+        const float* V = Vs[cur];
         // S^T[key][query] = K Q^T for 4 blocks of 16 keys, the four chains interleaved;
         // the K runs of step a+1 are read while step a multiplies
         f32x4 s[4];
@@ -288,11 +304,18 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
                 tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
                 tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
             }
-            // every wave is done with this tile before the next one overwrites it
-            __syncthreads();
-            tile_store<HS>(Ks, kreg);
-            tile_store<HS>(Vs, vreg);
-            __syncthreads();
+            if (ATTN_FWD_DB) {
+                // the other buffer was last read in the previous step, before its barrier
+                tile_store<HS>(Ks[cur ^ 1], kreg);
+                tile_store<HS>(Vs[cur ^ 1], vreg);
+                __syncthreads();
+            } else {
+                // every wave is done with this tile before the next one overwrites it
+                __syncthreads();
+                tile_store<HS>(Ks[0], kreg);
+                tile_store<HS>(Vs[0], vreg);
+                __syncthreads();
+            }
         }
     };
     for (int kt = 0; kt < qt; kt++) step(kt, std::false_type{});
@@ -313,13 +336,14 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
 
 // ---------------------------------------------------------------------------- dq (+ D)
 template <int HS>
-__global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_bwd_dq_kernel(float* __restrict__ dqkv, float* __restrict__ delta,
+__global__ __launch_bounds__(256, ATTN_DQ_OCC) void attn_bwd_dq_kernel(float* __restrict__ dqkv, float* __restrict__ delta,
                                                           const float* __restrict__ dout, const float* __restrict__ qkv,
                                                           const float* __restrict__ out, const float* __restrict__ lse,
                                                           int B, int T, int C, int NH, float scale) {
     constexpr int DG = HS / 16, LD = HS + 4;
-    __shared__ __attribute__((aligned(16))) float Ks[TILE * LD];
-    __shared__ __attribute__((aligned(16))) float Vs[TILE * LD];
+    constexpr int NBUF = ATTN_DQ_DB ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) float Ks[NBUF][TILE * LD];
+    __shared__ __attribute__((aligned(16))) float Vs[NBUF][TILE * LD];
     const int nqt = (T + TILE - 1) / TILE;
     const int bh = blockIdx.x % (B * NH);
     const int qt = nqt - 1 - (int)(blockIdx.x / (B * NH));
@@ -355,8 +379,8 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_bwd_dq_kernel(float* _
     const int nkt = qt + 1;
     tile_load<HS>(kreg, base + C + h * HS, ld, 0, T);
     tile_load<HS>(vreg, base + 2 * C + h * HS, ld, 0, T);
-    tile_store<HS>(Ks, kreg);
-    tile_store<HS>(Vs, vreg);
+    tile_store<HS>(Ks[0], kreg);
+    tile_store<HS>(Vs[0], vreg);
     __syncthreads();
     // one key tile; only the diagonal tile (kt == qt) has keys after the query
     auto step = [&](int kt, auto diag_tag) {
@@ -365,8 +389,9 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_bwd_dq_kernel(float* _
             tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
             tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
         }
-        const float* K = Ks;
-        const float* V = Vs;
+        const int cur = ATTN_DQ_DB ? (kt & 1) : 0;
+        const float* K = Ks[cur];
+        const float* V = Vs[cur];
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
             f32x4 s = zero4(), dp = zero4();
@@ -410,11 +435,18 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_bwd_dq_kernel(float* _
                 tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
                 tile_load<HS>(vreg, base + 2 * C + h * HS, ld, (kt + 1) * TILE, T);
             }
-            // every wave is done with this tile before the next one overwrites it
-            __syncthreads();
-            tile_store<HS>(Ks, kreg);
-            tile_store<HS>(Vs, vreg);
-            __syncthreads();
+            if (ATTN_DQ_DB) {
+                // the other buffer was last read in the previous step, before its barrier
+                tile_store<HS>(Ks[cur ^ 1], kreg);
+                tile_store<HS>(Vs[cur ^ 1], vreg);
+                __syncthreads();
+            } else {
+                // every wave is done with this tile before the next one overwrites it
+                __syncthreads();
+                tile_store<HS>(Ks[0], kreg);
+                tile_store<HS>(Vs[0], vreg);
+                __syncthreads();
+            }
         }
     };
     for (int kt = 0; kt < qt; kt++) step(kt, std::false_type{});

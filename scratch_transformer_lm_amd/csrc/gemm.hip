@@ -55,10 +55,21 @@ constexpr int BM = 128, NT = 256;
 // when A is k-contiguous (forward, dgrad), 16 and 4 for the wgrad, whose row-contiguous
 // fragments and fused bias sums need more registers than a second wave per SIMD leaves
 // with 32-wide k-tiles.  Both rings take 64 KB.
+// Waves raise their issue priority for the k loop and drop it for the epilogue (build
+// option).
+#ifndef GEMM_SETPRIO
+#define GEMM_SETPRIO 0
+#endif
+#ifndef GEMM_WG_BK
+#define GEMM_WG_BK 16
+#endif
+#ifndef GEMM_WG_STAGES
+#define GEMM_WG_STAGES 4
+#endif
 template <bool A_K>
 struct KTile {
-    static constexpr int BK = A_K ? 32 : 16;
-    static constexpr int STAGES = A_K ? 2 : 4;
+    static constexpr int BK = A_K ? 32 : GEMM_WG_BK;
+    static constexpr int STAGES = A_K ? 2 : GEMM_WG_STAGES;
 };
 // bf16 operands (k-tile width in float pairs): a k-tile takes an eighth of the fp32 MFMA
 // time, so more of them must be in flight to cover the global -> LDS latency.
@@ -98,7 +109,10 @@ struct KTileOf<false, true, BN> {
     static constexpr int STAGES = GEMM_BFT_STAGES;
 };
 constexpr int XF_FLOATS = 4 * 64;                // dlogits wgrad: per-wave lse slots
-constexpr int GROUP_M = 8;
+#ifndef GEMM_GROUP_M
+#define GEMM_GROUP_M 8
+#endif
+constexpr int GROUP_M = GEMM_GROUP_M;  // tile rows per group of the tile order
 constexpr int RESIDENT = 512;                    // blocks the chip holds at once (2 per CU)
 constexpr int MAX_UNITS = 1536;                  // split-K units the partial region holds
 // partial slot of a BM x BN tile: the tile (at least BM x 128), then its bias-gradient row sums
@@ -870,6 +884,7 @@ GPT2_DEV void gemm_body(const Params& p) {
         const int n = ke - ks;
         wait_vm<0>();
         __builtin_amdgcn_s_barrier();
+        if (GEMM_SETPRIO) __builtin_amdgcn_s_setprio(1);
         for (int kt = 0; kt < n; kt++) {
             if (kt + STAGES - 1 < n) issue((kt + STAGES - 1) % STAGES, ks + kt + STAGES - 1, m0, n0);
             compute(kt % STAGES, ks + kt);
@@ -879,6 +894,7 @@ GPT2_DEV void gemm_body(const Params& p) {
             __builtin_amdgcn_s_barrier();
         }
 
+        if (GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
         // start the next item's transfers, then finish this one while they fly
         float* slot = cur.slot;
         have = next_item(cur);
