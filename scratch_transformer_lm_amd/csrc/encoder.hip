@@ -228,13 +228,17 @@ __global__ __launch_bounds__(SORT_NT) void sort_tokens_kernel(int* __restrict__ 
 
 // Block r < run count owns run r of the sorted keys: dst[token] += scale * (sum of the
 // run's source rows).  The block's G = blockDim / (C/4) thread groups each add every G-th
-// row of the run (8 rows in flight per thread), and the G partial sums are then added in
-// group order, so the result is the same on every run.
-constexpr int SCATTER_NT = 1024;
+// row of the run in order, and the G partial sums are then added in group order, so the
+// result is the same on every run.  The run's row ids are first copied into LDS (in
+// chunks of SCATTER_CHUNK), so that a group's loads depend on no other load, and each
+// thread keeps SCATTER_AHEAD rows in flight: the longest run (the most frequent token,
+// hundreds of rows) is then a few memory latencies, not one per 8 rows and id fetch.
+constexpr int SCATTER_NT = 1024, SCATTER_CHUNK = 4096, SCATTER_AHEAD = 16;
 __global__ __launch_bounds__(SCATTER_NT) void scatter_rows_kernel(float* __restrict__ dst, const float* __restrict__ src,
                                                                   long ld, int C, float scale,
                                                                   const int* __restrict__ work, int np) {
     __shared__ float4 part[SCATTER_NT];
+    __shared__ int rid[SCATTER_CHUNK];
     const int nrun = work[0];
     const unsigned* keys = reinterpret_cast<const unsigned*>(work + 1);
     const int* runs = work + 1 + np;
@@ -243,31 +247,38 @@ __global__ __launch_bounds__(SCATTER_NT) void scatter_rows_kernel(float* __restr
     for (int r = blockIdx.x; r < nrun; r += gridDim.x) {
         const int j0 = runs[r], j1 = runs[r + 1];
         const int v = (int)(keys[j0] >> 16);
-        if (g < G) {
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            int j = j0 + g;
-            for (; j + 7 * G < j1; j += 8 * G) {
-                float4 d[8];
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int cs = j0; cs < j1; cs += SCATTER_CHUNK) {
+            const int ce = min(cs + SCATTER_CHUNK, j1);
+            __syncthreads();  // the previous chunk's ids (or run) are no longer read
+            for (int i = threadIdx.x; i < ce - cs; i += SCATTER_NT) rid[i] = (int)(keys[cs + i] & 0xFFFFu);
+            __syncthreads();
+            if (g < G) {
+                // this group's rows are j0 + g + kG; the first one in [cs, ce)
+                int j = cs + (g - (cs - j0) % G + G) % G;
+                for (; j + (SCATTER_AHEAD - 1) * G < ce; j += SCATTER_AHEAD * G) {
+                    float4 d[SCATTER_AHEAD];
 #pragma unroll
-                for (int u = 0; u < 8; u++)
-                    d[u] = reinterpret_cast<const float4*>(src + (long)(keys[j + u * G] & 0xFFFFu) * ld)[c4];
+                    for (int u = 0; u < SCATTER_AHEAD; u++)
+                        d[u] = reinterpret_cast<const float4*>(src + (long)rid[j - cs + u * G] * ld)[c4];
 #pragma unroll
-                for (int u = 0; u < 8; u++) {
-                    acc.x += d[u].x;
-                    acc.y += d[u].y;
-                    acc.z += d[u].z;
-                    acc.w += d[u].w;
+                    for (int u = 0; u < SCATTER_AHEAD; u++) {
+                        acc.x += d[u].x;
+                        acc.y += d[u].y;
+                        acc.z += d[u].z;
+                        acc.w += d[u].w;
+                    }
+                }
+                for (; j < ce; j += G) {
+                    const float4 d = reinterpret_cast<const float4*>(src + (long)rid[j - cs] * ld)[c4];
+                    acc.x += d.x;
+                    acc.y += d.y;
+                    acc.z += d.z;
+                    acc.w += d.w;
                 }
             }
-            for (; j < j1; j += G) {
-                const float4 d = reinterpret_cast<const float4*>(src + (long)(keys[j] & 0xFFFFu) * ld)[c4];
-                acc.x += d.x;
-                acc.y += d.y;
-                acc.z += d.z;
-                acc.w += d.w;
-            }
-            part[threadIdx.x] = acc;
         }
+        if (g < G) part[threadIdx.x] = acc;
         __syncthreads();
         if (g == 0) {
             float4 t = part[c4];
@@ -286,7 +297,6 @@ __global__ __launch_bounds__(SCATTER_NT) void scatter_rows_kernel(float* __restr
             w.w += scale * t.w;
             *o = w;
         }
-        __syncthreads();
     }
 }
 

@@ -19,10 +19,12 @@ namespace gpt2k {
 namespace {
 
 // Log-sum-exp from the LM-head forward's partials: (max, sum) pairs in base 2, stored
-// [part][row].  A block takes 64 rows; wave q merges parts q, q+4, ... of each row (a
-// wave's loads cover 64 consecutive rows: 512 contiguous bytes), then the four waves'
-// results are merged in LDS, in order.
-constexpr int LC_ROWS = 64, LC_WAVES = 4;
+// [part][row].  A block takes 64 rows; wave q merges parts q, q+16, ... of each row (a
+// wave's loads cover 64 consecutive rows: 512 contiguous bytes), then the sixteen waves'
+// results are merged in LDS, in order.  With 8192 rows and ~800 parts a row, sixteen
+// waves per block keep each thread's chain of dependent loads short (four waves: 26 us
+// per launch, about 2.5x a copy of the same bytes).
+constexpr int LC_ROWS = 64, LC_WAVES = 16;
 GPT2_DEV void merge2(float& m, float& s, float m2, float s2) {
     const float M = fmaxf(m, m2);
     if (M == -INFINITY) return;
