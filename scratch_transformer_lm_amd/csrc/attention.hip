@@ -32,8 +32,13 @@
 //    holds dimensions 16j + i for lane i, i.e. the run at i.
 // Rows are padded to HS + 4 floats so that 16 lanes reading 16 rows, or 16 runs of one
 // row, hit 16 different bank groups.
-// dq and dk/dv come from two kernels (query-tile and key-tile ownership) so every
-// output element has one writer: no atomics, bitwise reproducible.
+// dq and dk/dv come from separate kernels (query-tile and key-tile ownership) so every
+// output element has one writer: no atomics, bitwise reproducible.  With a score-gradient
+// buffer (the default of the step), D comes from its own small kernel, the dK/dV kernel
+// (the only one that recomputes S and dP) also stores ds for every causal tile pair, and
+// dQ is the plain product ds K: one product per pair instead of three (at the 124M shape
+// 0.89 against 2.25 ms per step for dQ, +0.22 ms of stores in dK/dV: the step 54.3 ->
+// 53.35 ms).  Without the buffer, dQ recomputes S and dP itself.
 #include <type_traits>
 
 #include "common.h"
@@ -463,11 +468,15 @@ __global__ __launch_bounds__(256, ATTN_DQ_OCC) void attn_bwd_dq_kernel(float* __
 }
 
 // ---------------------------------------------------------------------------- dk, dv
-template <int HS>
+// DS: also store dS (unscaled, p (dP - D)) of every causal (query tile, key tile) pair,
+// for the dQ kernel that multiplies it by K instead of recomputing S and dP: tile pair
+// (qt, kt <= qt) of (b, h) is the 64x64 row-major block at ((b NH + h) P + qt(qt+1)/2 +
+// kt) 4096, P = nqt(nqt+1)/2; entries of masked or out-of-range pairs are 0.
+template <int HS, bool DS>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ dqkv, const float* __restrict__ delta,
                                                             const float* __restrict__ dout, const float* __restrict__ qkv,
                                                             const float* __restrict__ lse, int B, int T, int C, int NH,
-                                                            float scale) {
+                                                            float scale, float* __restrict__ dsout) {
     constexpr int DG = HS / 16, LD = HS + 4;
     __shared__ __attribute__((aligned(16))) float Qs[2][TILE * LD];
     __shared__ __attribute__((aligned(16))) float Os[2][TILE * LD];
@@ -566,6 +575,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
                 p[v] = pv;
                 ds[v] = pv * (dp[v] - Ds[cur][qi]);
             }
+            if (DS) {
+                // this lane: queries qb*16 + 4*g4 + v of the tile, key wave*16 + i16
+                float* dst = dsout + (((long)bh * ((long)nqt * (nqt + 1) / 2) + (long)qt * (qt + 1) / 2 + kt) << 12) +
+                             (qb * 16 + 4 * g4) * TILE + wave * 16 + i16;
+#pragma unroll
+                for (int v = 0; v < 4; v++) dst[v * TILE] = ds[v];
+            }
 #pragma unroll
             for (int v = 0; v < 4; v++)
 #pragma unroll
@@ -597,6 +613,105 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
     }
 }
 
+// D_t = dO_t . o_t of every (row, head), one thread each (HS/4 float4s of dO and o, summed
+// in order), for the backward kernels that read it.
+template <int HS>
+__global__ __launch_bounds__(256) void attn_delta_kernel(float* __restrict__ delta, const float* __restrict__ dout,
+                                                         const float* __restrict__ out, int B, int T, int C, int NH) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)B * T * NH) return;
+    const long row = i / NH;
+    const int h = (int)(i - row * NH);
+    const float4* a = reinterpret_cast<const float4*>(dout + row * C + h * HS);
+    const float4* o = reinterpret_cast<const float4*>(out + row * C + h * HS);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < HS / 4; j++) {
+        const float4 x = a[j], y = o[j];
+        s = fmaf(x.x, y.x, s);
+        s = fmaf(x.y, y.y, s);
+        s = fmaf(x.z, y.z, s);
+        s = fmaf(x.w, y.w, s);
+    }
+    const long b = row / T, t = row - b * T;
+    delta[(b * NH + h) * T + t] = s;
+}
+
+// dQ = scale dS K from the dS blocks the dK/dV kernel stored: a block per 64-query tile
+// (longest first), 4 waves x 16 queries.  Per key tile the K tile goes through LDS
+// (double-buffered, one barrier per tile) and each lane takes its query row's 16 dS values
+// at keys 16 g4 .. 16 g4 + 15 straight from memory (the next tile's requested while this
+// one multiplies): MFMA step m (m < 16) has k slot g4 hold key 16 g4 + m, so a lane's A
+// values are its 16 consecutive dS and its B values the interleaved K run of key row
+// 16 g4 + m.  One product per pair instead of the three (S, dP, dS K) of recomputation.
+template <int HS>
+__global__ __launch_bounds__(256, 3) void attn_bwd_dq_ds_kernel(float* __restrict__ dqkv, const float* __restrict__ ds,
+                                                                const float* __restrict__ qkv, int B, int T, int C,
+                                                                int NH, float scale) {
+    constexpr int DG = HS / 16, LD = HS + 4;
+    __shared__ __attribute__((aligned(16))) float Ks[2][TILE * LD];
+    const int nqt = (T + TILE - 1) / TILE;
+    const int bh = blockIdx.x % (B * NH);
+    const int qt = nqt - 1 - (int)(blockIdx.x / (B * NH));  // longest rows first
+    const int b = bh / NH, h = bh % NH;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const long ld = 3L * C;
+    const float* base = qkv + (long)b * T * ld;
+    // this lane's dS row (query wave*16 + i16 of the tile), keys 16*g4 .. 16*g4 + 15, of pair (qt, kt)
+    const float* arow = ds + (((long)bh * ((long)nqt * (nqt + 1) / 2) + (long)qt * (qt + 1) / 2) << 12) +
+                        (wave * 16 + i16) * TILE + 16 * g4;
+    f32x4 dq[DG];
+#pragma unroll
+    for (int d = 0; d < DG; d++) dq[d] = zero4();
+    float4 acur[4], anxt[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) acur[j] = reinterpret_cast<const float4*>(arow)[j];
+    float4 kreg[DG];
+    tile_load<HS>(kreg, base + C + h * HS, ld, 0, T);
+    tile_store<HS>(Ks[0], kreg);
+    __syncthreads();
+    for (int kt = 0; kt <= qt; kt++) {
+        const int cur = kt & 1;
+        if (kt < qt) {
+            tile_load<HS>(kreg, base + C + h * HS, ld, (kt + 1) * TILE, T);
+            const float4* an = reinterpret_cast<const float4*>(arow + ((long)(kt + 1) << 12));
+#pragma unroll
+            for (int j = 0; j < 4; j++) anxt[j] = an[j];
+        }
+        const float* K = Ks[cur];
+        const float av[16] = {acur[0].x, acur[0].y, acur[0].z, acur[0].w, acur[1].x, acur[1].y, acur[1].z, acur[1].w,
+                              acur[2].x, acur[2].y, acur[2].z, acur[2].w, acur[3].x, acur[3].y, acur[3].z, acur[3].w};
+        float kf[2][DG];
+        lds_get<DG>(kf[0], K + (16 * g4) * LD + DG * i16);
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            if (m + 1 < 16) lds_get<DG>(kf[(m + 1) & 1], K + (16 * g4 + m + 1) * LD + DG * i16);
+            sched_fence();
+#pragma unroll
+            for (int d = 0; d < DG; d++) dq[d] = mfma4(av[m], kf[m & 1][d], dq[d]);
+            sched_fence();
+        }
+        if (kt < qt) {
+            // the other buffer was last read in the previous step, before its barrier
+            tile_store<HS>(Ks[cur ^ 1], kreg);
+#pragma unroll
+            for (int j = 0; j < 4; j++) acur[j] = anxt[j];
+            __syncthreads();
+        }
+    }
+    const int q0 = qt * TILE + wave * 16;
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const int q = q0 + 4 * g4 + v;
+        if (q < T) {
+            float* drow = dqkv + ((long)b * T + q) * ld + h * HS + i16;
+#pragma unroll
+            for (int d = 0; d < DG; d++) drow[16 * d] = dq[d][v] * scale;
+        }
+    }
+}
+
 template <int HS>
 const char* fwd_name() {
     return HS == 16 ? "attn_fwd_kernel<16>" : HS == 32 ? "attn_fwd_kernel<32>" : "attn_fwd_kernel<64>";
@@ -621,11 +736,40 @@ void launch_fwd(float* out, float* lse, const float* qkv, int B, int T, int C, i
 }
 
 template <int HS>
+const char* delta_name() {
+    return HS == 16 ? "attn_delta_kernel<16>" : HS == 32 ? "attn_delta_kernel<32>" : "attn_delta_kernel<64>";
+}
+template <int HS>
+const char* dqds_name() {
+    return HS == 16 ? "attn_bwd_dq_ds_kernel<16>" : HS == 32 ? "attn_bwd_dq_ds_kernel<32>" : "attn_bwd_dq_ds_kernel<64>";
+}
+
+template <int HS>
 void launch_bwd(float* dqkv, float* delta, const float* dout, const float* qkv, const float* out, const float* lse,
-                int B, int T, int C, int NH, hipStream_t st) {
+                int B, int T, int C, int NH, hipStream_t st, float* ds) {
     const int nt = (T + TILE - 1) / TILE;
     const float scale = 1.0f / sqrtf((float)HS);
     const double pairs = (double)B * NH * T * (T + 1) / 2;
+    if (ds) {
+        const double rows = (double)B * T, dsbytes = 4.0 * attn_ds_floats(B, T, NH);
+        {
+            ProfScope ps(st, delta_name<HS>(), 0.0, 4.0 * (2.0 * rows * C + rows * NH));
+            const long n = (long)B * T * NH;
+            hipLaunchKernelGGL(attn_delta_kernel<HS>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, delta, dout,
+                               out, B, T, C, NH);
+        }
+        {
+            // products formed: S (recomputed), dP, dV, dK; dS stored
+            ProfScope ps(st, dkdv_name<HS>(), pairs * HS * 2 * 4, 4.0 * rows * (3.0 * C + C + 2.0 * C + 2 * NH) + dsbytes);
+            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS, true>), dim3(nt * B * NH), dim3(256), 0, st, dqkv,
+                               (const float*)delta, dout, qkv, lse, B, T, C, NH, scale, ds);
+        }
+        // products formed: dQ = dS K
+        ProfScope ps(st, dqds_name<HS>(), pairs * HS * 2, 4.0 * rows * (C + C) + dsbytes);
+        hipLaunchKernelGGL(attn_bwd_dq_ds_kernel<HS>, dim3(nt * B * NH), dim3(256), 0, st, dqkv, (const float*)ds, qkv,
+                           B, T, C, NH, scale);
+        return;
+    }
     {
         // products formed: S (recomputed), dP, dQ
         ProfScope ps(st, dq_name<HS>(), pairs * HS * 2 * 3, 4.0 * B * T * (2.0 * C + 3.0 * C + 2 * NH));
@@ -634,8 +778,8 @@ void launch_bwd(float* dqkv, float* delta, const float* dout, const float* qkv, 
     }
     // products formed: S (recomputed), dP, dV, dK
     ProfScope ps(st, dkdv_name<HS>(), pairs * HS * 2 * 4, 4.0 * B * T * (3.0 * C + C + 2.0 * C + 2 * NH));
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<HS>, dim3(nt * B * NH), dim3(256), 0, st, dqkv, (const float*)delta, dout,
-                       qkv, lse, B, T, C, NH, scale);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS, false>), dim3(nt * B * NH), dim3(256), 0, st, dqkv,
+                       (const float*)delta, dout, qkv, lse, B, T, C, NH, scale, (float*)nullptr);
 }
 
 }  // namespace
@@ -653,15 +797,21 @@ hipError_t attention_forward(float* out, float* lse, const float* qkv, int B, in
     return hipGetLastError();
 }
 
+size_t attn_ds_floats(int B, int T, int NH) {
+    const size_t nqt = (size_t)(T + TILE - 1) / TILE;
+    return (size_t)B * NH * (nqt * (nqt + 1) / 2) * TILE * TILE;
+}
+
 hipError_t attention_backward(float* dqkv, float* delta, const float* dout, const float* qkv,
                               const float* out, const float* lse, int B, int T, int C, int NH,
-                              hipStream_t st) {
+                              hipStream_t st, float* ds) {
     if (C % NH || C % 4) return hipErrorInvalidValue;
     if ((long)B * T == 0) return hipSuccess;
+    if (ds && ((uintptr_t)ds & 15)) return hipErrorInvalidValue;
     switch (C / NH) {
-        case 16: launch_bwd<16>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st); break;
-        case 32: launch_bwd<32>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st); break;
-        case 64: launch_bwd<64>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st); break;
+        case 16: launch_bwd<16>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds); break;
+        case 32: launch_bwd<32>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds); break;
+        case 64: launch_bwd<64>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -87,7 +87,7 @@ struct Layout {
     size_t n_acts;
     // grad_scratch
     size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, lnpart, sample,
-        rope, lsep, n_scratch;
+        rope, lsep, attn_ds, n_attn_ds, n_scratch;
     // mixed precision: offsets (floats) of the bf16 arrays, per-layer strides (bf16 elements)
     size_t ba[NBA], ba_l[NBA], bs[NBS], bpart;
 };
@@ -99,6 +99,12 @@ size_t bias_slot_floats(size_t B, size_t T, size_t C) {
     return std::max({bias_partial_floats((int)(B * T), (int)(4 * C)), attn_bias_partial_floats((int)B, (int)T, (int)C),
                      (B * T + 15) / 16 * 4 * C});
 }
+
+// The fp32 attention backward stores the score gradients once (dK/dV kernel) and forms
+// dQ from them, instead of recomputing S and dP for dQ (build option; 0: recompute).
+#ifndef GPT2_ATTN_DS
+#define GPT2_ATTN_DS 1
+#endif
 
 Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     Layout y{};
@@ -177,6 +183,9 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     y.sample = take(3 * BT);                      // sampling requests: rows, coins, tokens
     y.rope = take(rope_table_floats(c->max_seq_len, (int)(C / NH)));  // rotary variant's (cos, sin) table
     y.lsep = take(lse_partial_floats((int)BT, (int)V));  // the LM head's per-tile log-sum-exp partials
+    // fp32 attention backward: the score gradients of every causal tile pair of one layer
+    y.n_attn_ds = (variant & GPT2_VARIANT_BF16) || !GPT2_ATTN_DS ? 0 : attn_ds_floats(B, T, (int)NH);
+    y.attn_ds = y.n_attn_ds ? take(y.n_attn_ds) : 0;
     if (variant & GPT2_VARIANT_BF16) {
         const size_t n[NBS] = {BT * C, BT * 4 * C, BT * 3 * C, BT * y.Vp, BT * C, attn_bf16_head_elems(B, T, (int)C)};
         for (int i = 0; i < NBS; i++) y.bs[i] = take((n[i] + 1) / 2);
@@ -617,8 +626,11 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
                                               BS(g, BS_HDO), BS(g, BS_HDOT), A(g, GPT2_ACT_ATTY, l),
                                               A(g, GPT2_ACT_ATT_LSE, l), attn_copies(g, l), B, T, C, NH, st));
         } else {
+            // the stored-score-gradient path when this batch shape's pairs fit the buffer
+            // sized at build (a call may use another B, T with B*T within the built one)
+            float* ds = g->lay.n_attn_ds && attn_ds_floats(B, T, NH) <= g->lay.n_attn_ds ? S(g, g->lay.attn_ds) : nullptr;
             HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
-                                         A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st));
+                                         A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st, ds));
         }
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
         // rotary variant: attention gave the gradient of the rotated q and k; rotate it back

@@ -152,10 +152,13 @@ hipError_t wpe_backward(float* dwpe, const float* dout, int B, int T, int C, hip
 // qkv (B,T,3C) -> out (B,T,C), lse (B,NH,T).
 hipError_t attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
                              hipStream_t st);
-// dout (B,T,C) -> dqkv (B,T,3C) (overwritten); delta needs B*NH*T floats.
+// dout (B,T,C) -> dqkv (B,T,3C) (overwritten); delta needs B*NH*T floats.  With ds (16-byte
+// aligned, attn_ds_floats(B, T, NH) floats) the dK/dV kernel stores the score gradients
+// and dQ is their product with K; without it dQ recomputes them.
+size_t attn_ds_floats(int B, int T, int NH);
 hipError_t attention_backward(float* dqkv, float* delta, const float* dout, const float* qkv,
                               const float* out, const float* lse, int B, int T, int C, int NH,
-                              hipStream_t st);
+                              hipStream_t st, float* ds = nullptr);
 
 // ---- attention of the mixed-precision variant (attention_bf16.hip) ------------------
 // bf16 copies of each head, per (batch, head): row-major (T, HS) and transposed (HS, Tp)

@@ -127,16 +127,21 @@ def test_build_variant_argument_checks_need_no_gpu():
 def test_bf16_variant_arena_sizes(w, B, T):
     """The mixed-precision arenas hold at least the bf16 copies: weights straight and
     transposed, the four per-layer linear inputs and lnf; the scratch one copy per kind of
-    output gradient (residual stream, fc, qkv) and the logits gradient's."""
+    output gradient (residual stream, fc, qkv) and the logits gradient's.  (The fp32
+    scratch alone holds the attention backward's score gradients of one layer: B heads'
+    worth of 64x64 blocks for every causal pair of 64-row tiles, 256-byte aligned.)"""
     m = w.model
-    L, C, V = m.num_layers, m.channels, m.vocab_size
+    L, C, V, NH = m.num_layers, m.channels, m.vocab_size, m.num_heads
     BT = B * T
     a0, s0 = G.arena_sizes(m, B, T)
     a4, s4 = G.arena_sizes(m, B, T, G.VARIANT_BF16)
     weights = L * 12 * C * C + V * C
     acts = L * 7 * C * BT + C * BT
+    nqt = (T + 63) // 64
+    ds = B * NH * (nqt * (nqt + 1) // 2) * 4096
+    assert s0 >= ds
     assert (a4 - a0) * 2 >= 2 * weights + acts
-    assert (s4 - s0) * 2 >= 8 * C * BT + V * BT
+    assert (s4 - (s0 - ds)) * 2 >= 8 * C * BT + V * BT
     with pytest.raises(G.GPT2Error):
         G.arena_sizes(m, B, T, 8)
 
