@@ -613,28 +613,49 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
     }
 }
 
-// D_t = dO_t . o_t of every (row, head), one thread each (HS/4 float4s of dO and o, summed
-// in order), for the backward kernels that read it.
+// D_t = dO_t . o_t of every (row, head): a wave per row, lane l holding float4 l of each
+// 256-float pass (all passes requested first, up to four at a time); each lane's four
+// products are added in order, then the HS/4 lanes of a head by DPP steps (within quads,
+// then half rows, then rows).
+template <int GL>
+GPT2_DEV float group_sum(float x) {
+    x += dpp_f<DPP_XOR1>(x);
+    x += dpp_f<DPP_XOR2>(x);
+    if (GL >= 8) x += dpp_f<DPP_HALF_MIRROR>(x);
+    if (GL >= 16) x += dpp_f<DPP_MIRROR>(x);
+    return x;
+}
 template <int HS>
 __global__ __launch_bounds__(256) void attn_delta_kernel(float* __restrict__ delta, const float* __restrict__ dout,
                                                          const float* __restrict__ out, int B, int T, int C, int NH) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (long)B * T * NH) return;
-    const long row = i / NH;
-    const int h = (int)(i - row * NH);
-    const float4* a = reinterpret_cast<const float4*>(dout + row * C + h * HS);
-    const float4* o = reinterpret_cast<const float4*>(out + row * C + h * HS);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < HS / 4; j++) {
-        const float4 x = a[j], y = o[j];
-        s = fmaf(x.x, y.x, s);
-        s = fmaf(x.y, y.y, s);
-        s = fmaf(x.z, y.z, s);
-        s = fmaf(x.w, y.w, s);
-    }
+    constexpr int GL = HS / 4;  // lanes per head
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= (long)B * T) return;  // the whole wave: row is uniform over it
+    const int C4 = C / 4;
+    const float4* a = reinterpret_cast<const float4*>(dout + row * C);
+    const float4* o = reinterpret_cast<const float4*>(out + row * C);
     const long b = row / T, t = row - b * T;
-    delta[(b * NH + h) * T + t] = s;
+    for (int p0 = 0; p0 < C4; p0 += 256) {
+        float4 x[4], y[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int i = p0 + 64 * q + lane;
+            x[q] = i < C4 ? a[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            y[q] = i < C4 ? o[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int i = p0 + 64 * q + lane;
+            if (p0 + 64 * q >= C4) break;  // uniform
+            float s = x[q].x * y[q].x;
+            s = fmaf(x[q].y, y[q].y, s);
+            s = fmaf(x[q].z, y[q].z, s);
+            s = fmaf(x[q].w, y[q].w, s);
+            s = group_sum<GL>(s);
+            if (i < C4 && lane % GL == 0) delta[(b * NH + i / GL) * T + t] = s;
+        }
+    }
 }
 
 // dQ = scale dS K from the dS blocks the dK/dV kernel stored: a block per 64-query tile
@@ -754,8 +775,8 @@ void launch_bwd(float* dqkv, float* delta, const float* dout, const float* qkv, 
         const double rows = (double)B * T, dsbytes = 4.0 * attn_ds_floats(B, T, NH);
         {
             ProfScope ps(st, delta_name<HS>(), 0.0, 4.0 * (2.0 * rows * C + rows * NH));
-            const long n = (long)B * T * NH;
-            hipLaunchKernelGGL(attn_delta_kernel<HS>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, delta, dout,
+            const long n = (long)B * T;
+            hipLaunchKernelGGL(attn_delta_kernel<HS>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, delta, dout,
                                out, B, T, C, NH);
         }
         {
