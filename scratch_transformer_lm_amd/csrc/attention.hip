@@ -741,9 +741,13 @@ template <int HS>
 const char* dq_name() {
     return HS == 16 ? "attn_bwd_dq_kernel<16>" : HS == 32 ? "attn_bwd_dq_kernel<32>" : "attn_bwd_dq_kernel<64>";
 }
-template <int HS>
+template <int HS, bool DS = false>
 const char* dkdv_name() {
-    return HS == 16 ? "attn_bwd_dkdv_kernel<16>" : HS == 32 ? "attn_bwd_dkdv_kernel<32>" : "attn_bwd_dkdv_kernel<64>";
+    if (DS)
+        return HS == 16 ? "attn_bwd_dkdv_kernel<16, true>" : HS == 32 ? "attn_bwd_dkdv_kernel<32, true>"
+                                                             : "attn_bwd_dkdv_kernel<64, true>";
+    return HS == 16 ? "attn_bwd_dkdv_kernel<16, false>" : HS == 32 ? "attn_bwd_dkdv_kernel<32, false>"
+                                                          : "attn_bwd_dkdv_kernel<64, false>";
 }
 
 template <int HS>
@@ -781,7 +785,8 @@ void launch_bwd(float* dqkv, float* delta, const float* dout, const float* qkv, 
         }
         {
             // products formed: S (recomputed), dP, dV, dK; dS stored
-            ProfScope ps(st, dkdv_name<HS>(), pairs * HS * 2 * 4, 4.0 * rows * (3.0 * C + C + 2.0 * C + 2 * NH) + dsbytes);
+            ProfScope ps(st, dkdv_name<HS, true>(), pairs * HS * 2 * 4,
+                         4.0 * rows * (3.0 * C + C + 2.0 * C + 2 * NH) + dsbytes);
             hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS, true>), dim3(nt * B * NH), dim3(256), 0, st, dqkv,
                                (const float*)delta, dout, qkv, lse, B, T, C, NH, scale, ds);
         }
