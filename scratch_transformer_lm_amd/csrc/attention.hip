@@ -659,17 +659,21 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(float* __restrict__ del
 }
 
 // dQ = scale dS K from the dS blocks the dK/dV kernel stored: a block per 64-query tile
-// (longest first), 4 waves x 16 queries.  Per key tile the K tile goes through LDS
-// (double-buffered, one barrier per tile) and each lane takes its query row's 16 dS values
-// at keys 16 g4 .. 16 g4 + 15 straight from memory (the next tile's requested while this
-// one multiplies): MFMA step m (m < 16) has k slot g4 hold key 16 g4 + m, so a lane's A
-// values are its 16 consecutive dS and its B values the interleaved K run of key row
-// 16 g4 + m.  One product per pair instead of the three (S, dP, dS K) of recomputation.
+// (longest first), 4 waves x 16 queries.  Per key tile the K tile goes through LDS, stored
+// plainly (row-major, one 16-byte write per float4: the interleaved layout's scalar writes
+// would cost as much as the tile's reads here) and double-buffered (one barrier per tile),
+// and each lane takes its query row's 16 dS values at keys 16 g4 .. 16 g4 + 15 straight
+// from memory (the next tile's requested while this one multiplies).  MFMA step m (m < 16)
+// has k slot g4 hold key 16 g4 + m, so a lane's A values are its 16 consecutive dS; output
+// block db holds dimensions DG j + db in column j, so a lane's B values for all blocks are
+// the DG consecutive floats of key row 16 g4 + m at DG i16 (one LDS read), and its
+// results for query row v are DG consecutive floats (one store).  One product per pair
+// instead of the three (S, dP, dS K) of recomputation.
 template <int HS>
 __global__ __launch_bounds__(256, 3) void attn_bwd_dq_ds_kernel(float* __restrict__ dqkv, const float* __restrict__ ds,
                                                                 const float* __restrict__ qkv, int B, int T, int C,
                                                                 int NH, float scale) {
-    constexpr int DG = HS / 16, LD = HS + 4;
+    constexpr int DG = HS / 16, LD = HS + 4, C4 = HS / 4, RPP = 256 / C4;
     __shared__ __attribute__((aligned(16))) float Ks[2][TILE * LD];
     const int nqt = (T + TILE - 1) / TILE;
     const int bh = blockIdx.x % (B * NH);
@@ -682,6 +686,12 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_ds_kernel(float* __restric
     // this lane's dS row (query wave*16 + i16 of the tile), keys 16*g4 .. 16*g4 + 15, of pair (qt, kt)
     const float* arow = ds + (((long)bh * ((long)nqt * (nqt + 1) / 2) + (long)qt * (qt + 1) / 2) << 12) +
                         (wave * 16 + i16) * TILE + 16 * g4;
+    // plain row-major K tile: thread t's float4 p sits at row t / C4 + RPP p, column 4 (t % C4)
+    auto kstore = [&](float* S, const float4 (&reg)[HS / 16]) {
+#pragma unroll
+        for (int p = 0; p < HS / 16; p++)
+            *reinterpret_cast<float4*>(S + (threadIdx.x / C4 + RPP * p) * LD + 4 * (threadIdx.x % C4)) = reg[p];
+    };
     f32x4 dq[DG];
 #pragma unroll
     for (int d = 0; d < DG; d++) dq[d] = zero4();
@@ -690,7 +700,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_ds_kernel(float* __restric
     for (int j = 0; j < 4; j++) acur[j] = reinterpret_cast<const float4*>(arow)[j];
     float4 kreg[DG];
     tile_load<HS>(kreg, base + C + h * HS, ld, 0, T);
-    tile_store<HS>(Ks[0], kreg);
+    kstore(Ks[0], kreg);
     __syncthreads();
     for (int kt = 0; kt <= qt; kt++) {
         const int cur = kt & 1;
@@ -715,7 +725,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_ds_kernel(float* __restric
         }
         if (kt < qt) {
             // the other buffer was last read in the previous step, before its barrier
-            tile_store<HS>(Ks[cur ^ 1], kreg);
+            kstore(Ks[cur ^ 1], kreg);
 #pragma unroll
             for (int j = 0; j < 4; j++) acur[j] = anxt[j];
             __syncthreads();
@@ -726,9 +736,10 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_ds_kernel(float* __restric
     for (int v = 0; v < 4; v++) {
         const int q = q0 + 4 * g4 + v;
         if (q < T) {
-            float* drow = dqkv + ((long)b * T + q) * ld + h * HS + i16;
+            float o[DG];
 #pragma unroll
-            for (int d = 0; d < DG; d++) drow[16 * d] = dq[d][v] * scale;
+            for (int d = 0; d < DG; d++) o[d] = dq[d][v] * scale;
+            lds_put<DG>(dqkv + ((long)b * T + q) * ld + h * HS + DG * i16, o);
         }
     }
 }
