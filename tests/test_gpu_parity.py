@@ -461,6 +461,35 @@ def test_smaller_batch_than_built(G):
     assert max(e.values()) <= GRAD_TOL, e
 
 
+@pytest.mark.parametrize("heads,C,Tb", [(4, 64, 64), (2, 128, 64)])
+def test_attention_backward_recompute_path(G, heads, C, Tb):
+    """A handle built at one sequence of Tb = 64 tokens sizes its score-gradient buffer for
+    that sequence's one tile pair per head; called with two sequences of 32 tokens (the same
+    token count, two tile pairs per head) the backward takes the path whose dQ kernel
+    recomputes S and dP.  Head sizes 16 and 64, two steps against the oracle."""
+    w = S.Workload(f"gpt2 L2 C{C} H{heads} V512", S.ModelShape(128, 512, 2, heads, C), 2, Tb // 2)
+    say(f"[recompute path] C{C} H{heads}: built B1 T{Tb}, run B2 T{Tb // 2}")
+    params = S.init_params(w.model)
+    x, y = S.tokens(w, B=2, T=Tb // 2, seed=11)
+    gr = gpu_run(G, w, params, x, y, 2, capture=(1, 2), B=1, T=Tb)
+    orc = run_oracle(w, params, x, y, 2, capture_steps=(1, 2))
+    assert np.all(np.abs(gr["losses"] - orc["losses"]) / orc["losses"] <= LOSS_RTOL)
+    m = gr["model"]
+    for t in (1, 2):
+        e = per_tensor(G.PARAM_NAMES, m.offsets, m.lengths, gr["grads"][t], orc["grads"][t])
+        say(f"grad rel err step {t}:", {k: f"{v:.1e}" for k, v in e.items()})
+        assert max(e.values()) <= GRAD_TOL, e
+    # the kernels that ran: the recomputing dQ, not the stored-score-gradient one
+    m.profile_enable(True)
+    m.forward(dev(x, torch.int32), dev(y, torch.int32))
+    assert m.zero_grad() == 0 and m.backward() == 0
+    torch.cuda.synchronize()
+    names = {e["name"] for e in m.profile_entries()}
+    m.profile_enable(False)
+    hs = C // heads
+    assert f"attn_bwd_dq_kernel<{hs}>" in names and f"attn_bwd_dq_ds_kernel<{hs}>" not in names, sorted(names)
+
+
 @pytest.mark.parametrize("B,T", [(520, 64), (512, 64)])
 def test_embedding_backward_paths(G, B, T):
     """B*T = 33280 takes the embedding backward's first-occurrence fallback (more positions
