@@ -179,10 +179,13 @@ GPT2_DEV void dot_operand(float (&v)[4][HS / 16], const float* row, bool valid, 
 }
 
 // ---------------------------------------------------------------------------- forward
-template <int HS>
+// SS: also store the raw scores q.k of every causal (query tile, key tile) pair, laid out
+// as the score gradients are (64x64 row-major block per pair, see the dK/dV kernel), so
+// that the backward need not form them again.
+template <int HS, bool SS>
 __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __restrict__ out, float* __restrict__ lse,
                                                        const float* __restrict__ qkv, int B, int T, int C, int NH,
-                                                       float scale) {
+                                                       float scale, float* __restrict__ sout) {
     constexpr int DG = HS / 16, LD = HS + 4;
     constexpr int NBUF = ATTN_FWD_DB ? 2 : 1;
     __shared__ __attribute__((aligned(16))) float Ks[NBUF][TILE * LD];
@@ -254,6 +257,12 @@ __global__ __launch_bounds__(256, ATTN_FWD_OCC) void attn_fwd_kernel(float* __re
         read_v(0, vf[0]);
         sched_fence();
         // lane holds raw scores of query tq against keys kt*64 + kb*16 + 4*g4 + v
+        if (SS) {
+            float* dst = sout + (((long)bh * ((long)nqt * (nqt + 1) / 2) + (long)qt * (qt + 1) / 2 + kt) << 12) +
+                         (wave * 16 + i16) * TILE + 4 * g4;
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++) *reinterpret_cast<f32x4*>(dst + 16 * kb) = s[kb];
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
@@ -472,11 +481,13 @@ __global__ __launch_bounds__(256, ATTN_DQ_OCC) void attn_bwd_dq_kernel(float* __
 // for the dQ kernel that multiplies it by K instead of recomputing S and dP: tile pair
 // (qt, kt <= qt) of (b, h) is the 64x64 row-major block at ((b NH + h) P + qt(qt+1)/2 +
 // kt) 4096, P = nqt(nqt+1)/2; entries of masked or out-of-range pairs are 0.
-template <int HS, bool DS>
+// SL: the raw scores come from the forward's store (sin, same layout) instead of Q K^T.
+template <int HS, bool DS, bool SL = false>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ dqkv, const float* __restrict__ delta,
                                                             const float* __restrict__ dout, const float* __restrict__ qkv,
                                                             const float* __restrict__ lse, int B, int T, int C, int NH,
-                                                            float scale, float* __restrict__ dsout) {
+                                                            float scale, float* __restrict__ dsout,
+                                                            const float* __restrict__ sin = nullptr) {
     constexpr int DG = HS / 16, LD = HS + 4;
     __shared__ __attribute__((aligned(16))) float Qs[2][TILE * LD];
     __shared__ __attribute__((aligned(16))) float Os[2][TILE * LD];
@@ -525,6 +536,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
     tile_store<HS>(Os[0], oreg);
     store_side(0);
     __syncthreads();
+    // SL: this lane's 16 stored scores of a pair: queries qb*16 + 4*g4 + v (qb, v < 4),
+    // key wave*16 + i16; the next pair's requested while this one is used
+    float scur[16], snext[16];
+    auto load_s = [&](float (&dst)[16], int qt) {
+        const float* src = sin + (((long)bh * ((long)nqt * (nqt + 1) / 2) + (long)qt * (qt + 1) / 2 + kt) << 12) +
+                           (4 * g4) * TILE + wave * 16 + i16;
+#pragma unroll
+        for (int qb = 0; qb < 4; qb++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) dst[4 * qb + v] = src[(qb * 16 + v) * TILE];
+    };
+    if (SL) load_s(scur, kt);
     // one query tile; only the diagonal tile (qt == kt) has queries before the key
     auto step = [&](int qt, auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
@@ -533,6 +556,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
             tile_load<HS>(qreg, base + h * HS, ld, (qt + 1) * TILE, T);
             tile_load<HS>(oreg, dbase + h * HS, C, (qt + 1) * TILE, T);
             load_side(qt + 1);
+            if (SL) load_s(snext, qt + 1);
         }
         const float* Q = Qs[cur];
         const float* O = Os[cur];
@@ -550,7 +574,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
             }
             float qf[2][DG], of[2][DG];
             auto read_qo = [&](int a, float (&q)[DG], float (&o)[DG]) {
-                lds_get<DG>(q, Q + (qb * 16 + i16) * LD + DG * (4 * a + g4));
+                if (!SL) lds_get<DG>(q, Q + (qb * 16 + i16) * LD + DG * (4 * a + g4));
                 lds_get<DG>(o, O + (qb * 16 + i16) * LD + DG * (4 * a + g4));
             };
             read_qo(0, qf[0], of[0]);
@@ -560,10 +584,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
                 sched_fence();
 #pragma unroll
                 for (int j = 0; j < DG; j++) {
-                    s = mfma4(qf[a & 1][j], kreg[a][j], s);
+                    if (!SL) s = mfma4(qf[a & 1][j], kreg[a][j], s);
                     dp = mfma4(of[a & 1][j], vreg[a][j], dp);
                 }
                 sched_fence();
+            }
+            if (SL) {
+#pragma unroll
+                for (int v = 0; v < 4; v++) s[v] = scur[4 * qb + v];
             }
             // lane: query qt*64 + qb*16 + 4*g4 + v, key tu
             float p[4], ds[4];
@@ -594,6 +622,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(float* __restrict__ 
             tile_store<HS>(Qs[cur ^ 1], qreg);
             tile_store<HS>(Os[cur ^ 1], oreg);
             store_side(cur ^ 1);
+            if (SL) {
+#pragma unroll
+                for (int e = 0; e < 16; e++) scur[e] = snext[e];
+            }
         }
         __syncthreads();
     };
@@ -762,13 +794,21 @@ const char* dkdv_name() {
 }
 
 template <int HS>
-void launch_fwd(float* out, float* lse, const float* qkv, int B, int T, int C, int NH, hipStream_t st) {
+void launch_fwd(float* out, float* lse, const float* qkv, int B, int T, int C, int NH, hipStream_t st, float* sbuf) {
     const int nqt = (T + TILE - 1) / TILE;
     const float scale = 1.0f / sqrtf((float)HS);
     // causal half: T(T+1)/2 (query, key) pairs per (b, h), two products of HS MACs each
     const double pairs = (double)B * NH * T * (T + 1) / 2;
+    if (sbuf) {
+        ProfScope ps(st, fwd_name<HS>(), pairs * HS * 2 * 2,
+                     4.0 * B * T * (3.0 * C + C + NH) + 4.0 * attn_ds_floats(B, T, NH));
+        hipLaunchKernelGGL((attn_fwd_kernel<HS, true>), dim3(nqt * B * NH), dim3(256), 0, st, out, lse, qkv, B, T, C,
+                           NH, scale, sbuf);
+        return;
+    }
     ProfScope ps(st, fwd_name<HS>(), pairs * HS * 2 * 2, 4.0 * B * T * (3.0 * C + C + NH));
-    hipLaunchKernelGGL(attn_fwd_kernel<HS>, dim3(nqt * B * NH), dim3(256), 0, st, out, lse, qkv, B, T, C, NH, scale);
+    hipLaunchKernelGGL((attn_fwd_kernel<HS, false>), dim3(nqt * B * NH), dim3(256), 0, st, out, lse, qkv, B, T, C, NH,
+                       scale, (float*)nullptr);
 }
 
 template <int HS>
@@ -782,7 +822,7 @@ const char* dqds_name() {
 
 template <int HS>
 void launch_bwd(float* dqkv, float* delta, const float* dout, const float* qkv, const float* out, const float* lse,
-                int B, int T, int C, int NH, hipStream_t st, float* ds) {
+                int B, int T, int C, int NH, hipStream_t st, float* ds, const float* sbuf) {
     const int nt = (T + TILE - 1) / TILE;
     const float scale = 1.0f / sqrtf((float)HS);
     const double pairs = (double)B * NH * T * (T + 1) / 2;
@@ -794,7 +834,13 @@ void launch_bwd(float* dqkv, float* delta, const float* dout, const float* qkv, 
             hipLaunchKernelGGL(attn_delta_kernel<HS>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, delta, dout,
                                out, B, T, C, NH);
         }
-        {
+        if (sbuf) {
+            // products formed: dP, dV, dK (S from the forward's store); dS stored
+            ProfScope ps(st, dkdv_name<HS, true>(), pairs * HS * 2 * 3,
+                         4.0 * rows * (3.0 * C + C + 2.0 * C + 2 * NH) + 2.0 * dsbytes);
+            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS, true, true>), dim3(nt * B * NH), dim3(256), 0, st, dqkv,
+                               (const float*)delta, dout, qkv, lse, B, T, C, NH, scale, ds, sbuf);
+        } else {
             // products formed: S (recomputed), dP, dV, dK; dS stored
             ProfScope ps(st, dkdv_name<HS, true>(), pairs * HS * 2 * 4,
                          4.0 * rows * (3.0 * C + C + 2.0 * C + 2 * NH) + dsbytes);
@@ -822,13 +868,13 @@ void launch_bwd(float* dqkv, float* delta, const float* dout, const float* qkv, 
 }  // namespace
 
 hipError_t attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
-                             hipStream_t st) {
+                             hipStream_t st, float* sbuf) {
     if (C % NH || C % 4) return hipErrorInvalidValue;
     if ((long)B * T == 0) return hipSuccess;
     switch (C / NH) {
-        case 16: launch_fwd<16>(out, lse, qkv, B, T, C, NH, st); break;
-        case 32: launch_fwd<32>(out, lse, qkv, B, T, C, NH, st); break;
-        case 64: launch_fwd<64>(out, lse, qkv, B, T, C, NH, st); break;
+        case 16: launch_fwd<16>(out, lse, qkv, B, T, C, NH, st, sbuf); break;
+        case 32: launch_fwd<32>(out, lse, qkv, B, T, C, NH, st, sbuf); break;
+        case 64: launch_fwd<64>(out, lse, qkv, B, T, C, NH, st, sbuf); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -841,14 +887,14 @@ size_t attn_ds_floats(int B, int T, int NH) {
 
 hipError_t attention_backward(float* dqkv, float* delta, const float* dout, const float* qkv,
                               const float* out, const float* lse, int B, int T, int C, int NH,
-                              hipStream_t st, float* ds) {
+                              hipStream_t st, float* ds, const float* sbuf) {
     if (C % NH || C % 4) return hipErrorInvalidValue;
     if ((long)B * T == 0) return hipSuccess;
-    if (ds && ((uintptr_t)ds & 15)) return hipErrorInvalidValue;
+    if ((ds && ((uintptr_t)ds & 15)) || (sbuf && ((uintptr_t)sbuf & 15))) return hipErrorInvalidValue;
     switch (C / NH) {
-        case 16: launch_bwd<16>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds); break;
-        case 32: launch_bwd<32>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds); break;
-        case 64: launch_bwd<64>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds); break;
+        case 16: launch_bwd<16>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds, ds ? sbuf : nullptr); break;
+        case 32: launch_bwd<32>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds, ds ? sbuf : nullptr); break;
+        case 64: launch_bwd<64>(dqkv, delta, dout, qkv, out, lse, B, T, C, NH, st, ds, ds ? sbuf : nullptr); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -87,7 +87,7 @@ struct Layout {
     size_t n_acts;
     // grad_scratch
     size_t dres, dln, datty, dqkv, dfch, delta, enc_work, enc_work_tgt, partial, n_partial, partial_w, lnpart, sample,
-        rope, lsep, attn_ds, n_attn_ds, n_scratch;
+        rope, lsep, attn_ds, n_attn_ds, attn_s, n_scratch;
     // mixed precision: offsets (floats) of the bf16 arrays, per-layer strides (bf16 elements)
     size_t ba[NBA], ba_l[NBA], bs[NBS], bpart;
 };
@@ -104,6 +104,11 @@ size_t bias_slot_floats(size_t B, size_t T, size_t C) {
 // dQ from them, instead of recomputing S and dP for dQ (build option; 0: recompute).
 #ifndef GPT2_ATTN_DS
 #define GPT2_ATTN_DS 1
+#endif
+// With it, the forward also stores the raw scores of every layer and the dK/dV kernel
+// reads them instead of forming Q K^T again (build option; 0: recompute).
+#ifndef GPT2_ATTN_S
+#define GPT2_ATTN_S 1
 #endif
 
 Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
@@ -186,6 +191,8 @@ Layout make_layout(const gpt2_config* c, int B, int T, int variant = 0) {
     // fp32 attention backward: the score gradients of every causal tile pair of one layer
     y.n_attn_ds = (variant & GPT2_VARIANT_BF16) || !GPT2_ATTN_DS ? 0 : attn_ds_floats(B, T, (int)NH);
     y.attn_ds = y.n_attn_ds ? take(y.n_attn_ds) : 0;
+    // ... and the raw scores the forward stores for it, one such buffer per layer
+    y.attn_s = y.n_attn_ds && GPT2_ATTN_S ? take(L * y.n_attn_ds) : 0;
     if (variant & GPT2_VARIANT_BF16) {
         const size_t n[NBS] = {BT * C, BT * 4 * C, BT * 3 * C, BT * y.Vp, BT * C, attn_bf16_head_elems(B, T, (int)C)};
         for (int i = 0; i < NBS; i++) y.bs[i] = take((n[i] + 1) / 2);
@@ -216,6 +223,7 @@ struct gpt2 {
     int* host_ret;  // pinned: [loss bits, flags]
     int last_error;
     bool have_forward, have_targets;
+    bool scores_stored;  // the last forward stored every layer's raw attention scores
     Profiler* prof;  // non-null while per-kernel timing is enabled
 };
 
@@ -346,6 +354,10 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
         if (bf) return gemm_bf16(epi, out, ldo, xb, K, wb, K, BT, N, K, bias, resid, ldo, pre, part, st, nullptr, yb, N);
         return linear_forward(out, ldo, x, w, bias, resid, pre, BT, N, K, part, st);
     };
+    // the raw attention scores for the backward (which needs targets), when this batch
+    // shape's tile pairs fit
+    const bool store_s = targets && !bf && g->lay.attn_s && attn_ds_floats(B, T, NH) <= g->lay.n_attn_ds;
+    g->scores_stored = false;
     for (int l = 0; l < L; l++) {
         float* residual = l == 0 ? A(g, GPT2_ACT_ENCODED) : A(g, GPT2_ACT_RESIDUAL3, l - 1);
         HIPCHK(g, norm_fwd(g, A(g, GPT2_ACT_LN1, l), A(g, GPT2_ACT_LN1_MEAN, l), A(g, GPT2_ACT_LN1_RSTD, l), residual,
@@ -364,7 +376,7 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
                                              attn_copies(g, l), B, T, C, NH, st));
         } else {
             HIPCHK(g, attention_forward(A(g, GPT2_ACT_ATTY, l), A(g, GPT2_ACT_ATT_LSE, l), A(g, GPT2_ACT_QKV, l), B, T,
-                                        C, NH, st));
+                                        C, NH, st, store_s ? S(g, g->lay.attn_s) + (size_t)l * g->lay.n_attn_ds : nullptr));
         }
         HIPCHK(g, linear(BF16_BIAS_RESID, A(g, GPT2_ACT_RESIDUAL2, l), C, A(g, GPT2_ACT_ATTY, l), BA(g, BA_ATTY, l),
                          P(g, P_ATTPROJW) + (size_t)l * C * C, BA(g, BW_A, l), P(g, P_ATTPROJB) + l * C, residual,
@@ -403,6 +415,7 @@ int forward_impl(gpt2* g, const int32_t* inputs, const int32_t* targets, int B, 
     *loss_out = targets ? loss : -1.0f;
     g->have_forward = true;
     g->have_targets = targets != nullptr;
+    g->scores_stored = store_s;
     return GPT2_OK;
 }
 
@@ -629,8 +642,9 @@ int backward_impl(gpt2* g, const UpdateArgs* up) {
             // the stored-score-gradient path when this batch shape's pairs fit the buffer
             // sized at build (a call may use another B, T with B*T within the built one)
             float* ds = g->lay.n_attn_ds && attn_ds_floats(B, T, NH) <= g->lay.n_attn_ds ? S(g, g->lay.attn_ds) : nullptr;
+            const float* sb = ds && g->scores_stored ? S(g, g->lay.attn_s) + (size_t)l * g->lay.n_attn_ds : nullptr;
             HIPCHK(g, attention_backward(dqkv, S(g, g->lay.delta), datty, A(g, GPT2_ACT_QKV, l), A(g, GPT2_ACT_ATTY, l),
-                                         A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st, ds));
+                                         A(g, GPT2_ACT_ATT_LSE, l), B, T, C, NH, st, ds, sb));
         }
         // QKV projection: qkv = ln1 . Wqkv^T + bqkv.
         // rotary variant: attention gave the gradient of the rotated q and k; rotate it back

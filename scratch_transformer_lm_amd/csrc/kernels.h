@@ -150,15 +150,18 @@ hipError_t wpe_backward(float* dwpe, const float* dout, int B, int T, int C, hip
 
 // ---- attention (attention.hip) ------------------------------------------------------
 // qkv (B,T,3C) -> out (B,T,C), lse (B,NH,T).
+// sbuf (nullable, 16-byte aligned, attn_ds_floats(B, T, NH) floats): also store the raw
+// scores q.k of every causal tile pair for the backward.
 hipError_t attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
-                             hipStream_t st);
+                             hipStream_t st, float* sbuf = nullptr);
 // dout (B,T,C) -> dqkv (B,T,3C) (overwritten); delta needs B*NH*T floats.  With ds (16-byte
 // aligned, attn_ds_floats(B, T, NH) floats) the dK/dV kernel stores the score gradients
-// and dQ is their product with K; without it dQ recomputes them.
+// and dQ is their product with K; without it dQ recomputes them.  With ds and sbuf (the
+// raw scores the forward stored) the dK/dV kernel reads S instead of forming Q K^T.
 size_t attn_ds_floats(int B, int T, int NH);
 hipError_t attention_backward(float* dqkv, float* delta, const float* dout, const float* qkv,
                               const float* out, const float* lse, int B, int T, int C, int NH,
-                              hipStream_t st, float* ds = nullptr);
+                              hipStream_t st, float* ds = nullptr, const float* sbuf = nullptr);
 
 // ---- attention of the mixed-precision variant (attention_bf16.hip) ------------------
 // bf16 copies of each head, per (batch, head): row-major (T, HS) and transposed (HS, Tp)

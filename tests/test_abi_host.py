@@ -128,8 +128,9 @@ def test_bf16_variant_arena_sizes(w, B, T):
     """The mixed-precision arenas hold at least the bf16 copies: weights straight and
     transposed, the four per-layer linear inputs and lnf; the scratch one copy per kind of
     output gradient (residual stream, fc, qkv) and the logits gradient's.  (The fp32
-    scratch alone holds the attention backward's score gradients of one layer: B heads'
-    worth of 64x64 blocks for every causal pair of 64-row tiles, 256-byte aligned.)"""
+    scratch alone holds the attention backward's score gradients of one layer and the
+    forward's raw scores of every layer: B heads' worth of 64x64 blocks for every causal
+    pair of 64-row tiles each.)"""
     m = w.model
     L, C, V, NH = m.num_layers, m.channels, m.vocab_size, m.num_heads
     BT = B * T
@@ -138,7 +139,7 @@ def test_bf16_variant_arena_sizes(w, B, T):
     weights = L * 12 * C * C + V * C
     acts = L * 7 * C * BT + C * BT
     nqt = (T + 63) // 64
-    ds = B * NH * (nqt * (nqt + 1) // 2) * 4096
+    ds = (L + 1) * B * NH * (nqt * (nqt + 1) // 2) * 4096
     assert s0 >= ds
     assert (a4 - a0) * 2 >= 2 * weights + acts
     assert (s4 - (s0 - ds)) * 2 >= 8 * C * BT + V * BT
