@@ -39,6 +39,7 @@
 // dQ is the plain product ds K: one product per pair instead of three (at the 124M shape
 // 0.89 against 2.25 ms per step for dQ, +0.22 ms of stores in dK/dV: the step 54.3 ->
 // 53.35 ms).  Without the buffer, dQ recomputes S and dP itself.
+#include <string>
 #include <type_traits>
 
 #include "common.h"
@@ -784,13 +785,12 @@ template <int HS>
 const char* dq_name() {
     return HS == 16 ? "attn_bwd_dq_kernel<16>" : HS == 32 ? "attn_bwd_dq_kernel<32>" : "attn_bwd_dq_kernel<64>";
 }
-template <int HS, bool DS = false>
+// as the profiler prints the instantiation
+template <int HS, bool DS = false, bool SL = false>
 const char* dkdv_name() {
-    if (DS)
-        return HS == 16 ? "attn_bwd_dkdv_kernel<16, true>" : HS == 32 ? "attn_bwd_dkdv_kernel<32, true>"
-                                                             : "attn_bwd_dkdv_kernel<64, true>";
-    return HS == 16 ? "attn_bwd_dkdv_kernel<16, false>" : HS == 32 ? "attn_bwd_dkdv_kernel<32, false>"
-                                                          : "attn_bwd_dkdv_kernel<64, false>";
+    static const std::string n = "attn_bwd_dkdv_kernel<" + std::to_string(HS) + (DS ? ", true" : ", false") +
+                                 (SL ? ", true>" : ", false>");
+    return n.c_str();
 }
 
 template <int HS>
@@ -836,7 +836,7 @@ void launch_bwd(float* dqkv, float* delta, const float* dout, const float* qkv, 
         }
         if (sbuf) {
             // products formed: dP, dV, dK (S from the forward's store); dS stored
-            ProfScope ps(st, dkdv_name<HS, true>(), pairs * HS * 2 * 3,
+            ProfScope ps(st, dkdv_name<HS, true, true>(), pairs * HS * 2 * 3,
                          4.0 * rows * (3.0 * C + C + 2.0 * C + 2 * NH) + 2.0 * dsbytes);
             hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS, true, true>), dim3(nt * B * NH), dim3(256), 0, st, dqkv,
                                (const float*)delta, dout, qkv, lse, B, T, C, NH, scale, ds, sbuf);
