@@ -777,9 +777,10 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_ds_kernel(float* __restric
     }
 }
 
-template <int HS>
+template <int HS, bool SS>
 const char* fwd_name() {
-    return HS == 16 ? "attn_fwd_kernel<16>" : HS == 32 ? "attn_fwd_kernel<32>" : "attn_fwd_kernel<64>";
+    static const std::string n = "attn_fwd_kernel<" + std::to_string(HS) + (SS ? ", true>" : ", false>");
+    return n.c_str();
 }
 template <int HS>
 const char* dq_name() {
@@ -800,13 +801,13 @@ void launch_fwd(float* out, float* lse, const float* qkv, int B, int T, int C, i
     // causal half: T(T+1)/2 (query, key) pairs per (b, h), two products of HS MACs each
     const double pairs = (double)B * NH * T * (T + 1) / 2;
     if (sbuf) {
-        ProfScope ps(st, fwd_name<HS>(), pairs * HS * 2 * 2,
+        ProfScope ps(st, fwd_name<HS, true>(), pairs * HS * 2 * 2,
                      4.0 * B * T * (3.0 * C + C + NH) + 4.0 * attn_ds_floats(B, T, NH));
         hipLaunchKernelGGL((attn_fwd_kernel<HS, true>), dim3(nqt * B * NH), dim3(256), 0, st, out, lse, qkv, B, T, C,
                            NH, scale, sbuf);
         return;
     }
-    ProfScope ps(st, fwd_name<HS>(), pairs * HS * 2 * 2, 4.0 * B * T * (3.0 * C + C + NH));
+    ProfScope ps(st, fwd_name<HS, false>(), pairs * HS * 2 * 2, 4.0 * B * T * (3.0 * C + C + NH));
     hipLaunchKernelGGL((attn_fwd_kernel<HS, false>), dim3(nqt * B * NH), dim3(256), 0, st, out, lse, qkv, B, T, C, NH,
                        scale, (float*)nullptr);
 }
