@@ -70,7 +70,11 @@ int gpt2_param_layout(const gpt2_config* cfg, size_t off[GPT2_NUM_PARAM_TENSORS]
                       size_t len[GPT2_NUM_PARAM_TENSORS]);
 
 /* Sizes (in floats) of the two arenas a model of batch shape (B, T) needs: the
- * activation arena and the gradient scratch arena.  Host-only. */
+ * activation arena and the gradient scratch arena.  Host-only.  In the fp32 variants the
+ * scratch also holds the attention's raw scores of every layer and one layer's score
+ * gradients (B x heads 64x64 blocks per causal pair of 64-position tiles each: about
+ * 2.8 GB in all for GPT-2 124M at B=8, T=1024); the backward falls back to recomputing
+ * them for batch shapes whose pairs do not fit. */
 int gpt2_arena_sizes(const gpt2_config* cfg, int B, int T, size_t* n_acts, size_t* n_grad_scratch);
 /* The same for a model built with gpt2_build_variant(..., variant): GPT2_VARIANT_BF16
  * adds the bfloat16 operand copies (weights, their transposes and the linear layers'
